@@ -1,0 +1,330 @@
+"""NVFP4 W4A4 quantized linear layer for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI in include/fql.h (libfql.so, built
+in-tree by fp8_quantized_linear_amd.build). This module only marshals
+arguments: every step of the layer runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream.
+
+Typical use (weights quantized and packed once, activations per call):
+
+    w = NVFP4Weight.from_float(w_fp32_cuda, input_global_scale=g_x)
+    y = linear_nvfp4(x_bf16_cuda, w, bias=b)
+
+The layer follows the vLLM write-ups' NVFP4 linear path ("TorchNvFp4LinearKernel",
+"B12X CuTe-DSL linear backends"): quantize x with the layer's input global
+scale, block-scaled GEMM with the packed weight, multiply by alpha (the
+product of the two global dequant scales), add the bias, keep the input dtype
+and the shape [*x.shape[:-1], N].
+"""
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "FQLError",
+    "lib",
+    "is_supported",
+    "can_implement",
+    "amax",
+    "global_scale_from_amax",
+    "quant_nvfp4",
+    "quant_nvfp4_weight",
+    "packed_nvfp4_bytes",
+    "pack_weight_nvfp4",
+    "unpack_weight_nvfp4",
+    "linear_workspace_bytes",
+    "linear_nvfp4",
+    "NVFP4Weight",
+    "HADAMARD_BLOCKS",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfql.so")
+HADAMARD_BLOCKS = (0, 16, 32, 64, 128)
+FMT_NVFP4 = 1
+
+_c_int, _c_i64, _c_f32, _c_vp, _c_sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                                         ctypes.c_void_p, ctypes.c_size_t)
+
+# name -> (restype, argtypes); must match include/fql.h
+SIGNATURES = {
+    "fql_version": (_c_int, []),
+    "fql_last_error": (ctypes.c_char_p, []),
+    "fql_is_supported": (_c_int, [_c_int, ctypes.c_char_p, _c_sz]),
+    "fql_can_implement": (_c_int, [_c_int, _c_i64, _c_i64, _c_int, ctypes.c_char_p, _c_sz]),
+    "fql_amax_bf16": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_vp]),
+    "fql_amax_f32": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_int, _c_vp, _c_vp]),
+    "fql_quant_nvfp4": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_int, _c_vp, _c_vp, _c_vp]),
+    "fql_quant_nvfp4_f32": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_int, _c_vp, _c_vp, _c_vp]),
+    "fql_packed_nvfp4_bytes": (_c_int, [_c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+    "fql_pack_weight_nvfp4": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fql_unpack_weight_nvfp4": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "fql_linear_nvfp4_workspace_bytes": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+    "fql_linear_nvfp4": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_int, _c_vp, _c_i64,
+                                  _c_f32, _c_vp, _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+}
+
+
+class FQLError(RuntimeError):
+    """An error status returned by the library (message from fql_last_error)."""
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def lib():
+    """The loaded libfql.so (built in-tree on first use if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                from . import build as _build
+
+                _build.build()
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = handle
+    return _lib
+
+
+def _check(status):
+    if status < 0:
+        raise FQLError(f"fql error {status}: {lib().fql_last_error().decode()}")
+    return status
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _require_cuda(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise FQLError(f"{name} must be a CUDA (HIP) tensor")
+
+
+def _rows_view(x, name):
+    """(2-D view [M, K], row stride) of x [..., K] without copying."""
+    if x.dim() < 1:
+        raise FQLError(f"{name} must have at least one dimension")
+    if x.stride(-1) != 1:
+        raise FQLError(f"{name} must have unit stride in its last dimension")
+    K = x.shape[-1]
+    if x.dim() == 1:
+        return x.view(1, K), K
+    try:
+        x2 = x.view(-1, K) if x.dim() > 2 else x
+    except RuntimeError as e:
+        raise FQLError(f"{name}: leading dimensions cannot be flattened without a copy") from e
+    ld = x2.stride(0) if x2.shape[0] > 1 else max(K, x2.stride(0))
+    return x2, ld
+
+
+# ---------------------------------------------------------------------------
+# availability
+# ---------------------------------------------------------------------------
+
+def is_supported(device=0):
+    buf = ctypes.create_string_buffer(256)
+    r = _check(lib().fql_is_supported(int(device), buf, 256))
+    return bool(r), buf.value.decode()
+
+
+def can_implement(N, K, hadamard_block=0):
+    buf = ctypes.create_string_buffer(256)
+    r = _check(lib().fql_can_implement(FMT_NVFP4, int(N), int(K), int(hadamard_block), buf, 256))
+    return bool(r), buf.value.decode()
+
+
+# ---------------------------------------------------------------------------
+# quantizer
+# ---------------------------------------------------------------------------
+
+def amax(x, hadamard_block=0):
+    """max |v| of x (bf16 or float32, [..., K]) after the optional rotation; 0-d float32 tensor."""
+    _require_cuda(x, "x")
+    x2, ld = _rows_view(x, "x")
+    M, K = x2.shape
+    out = torch.empty((), dtype=torch.float32, device=x.device)
+    if x.dtype == torch.bfloat16:
+        fn = lib().fql_amax_bf16
+    elif x.dtype == torch.float32:
+        fn = lib().fql_amax_f32
+    else:
+        raise FQLError("amax supports bfloat16 and float32 inputs")
+    _check(fn(_ptr(x2), M, K, ld, int(hadamard_block), _ptr(out), _stream(x.device)))
+    return out
+
+
+def global_scale_from_amax(amax_value):
+    """g = 448 * 6 / amax rounded to float32 (1 when amax is 0), on the host."""
+    import numpy as np
+
+    a = np.float32(amax_value)
+    if a == 0:
+        return float(np.float32(1.0))
+    return float(np.float32(2688.0) / a)
+
+
+def quant_nvfp4(x, global_scale, hadamard_block=0, codes=None, scales=None):
+    """Quantize bf16 x [..., K] to NVFP4: (codes uint8 [..., K/2], scales uint8 [..., K/16])."""
+    _require_cuda(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise FQLError("quant_nvfp4 takes bfloat16 activations")
+    x2, ld = _rows_view(x, "x")
+    M, K = x2.shape
+    lead = tuple(x.shape[:-1])
+    if codes is None:
+        codes = torch.empty(lead + (K // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(lead + (K // 16,), dtype=torch.uint8, device=x.device)
+    _check(lib().fql_quant_nvfp4(_ptr(x2), M, K, ld, float(global_scale), int(hadamard_block),
+                                 _ptr(codes), _ptr(scales), _stream(x.device)))
+    return codes, scales
+
+
+def quant_nvfp4_weight(w, global_scale, hadamard_block=0):
+    """Quantize float32 weights w [N, K] (rows rotated if hadamard_block > 0)."""
+    _require_cuda(w, "w")
+    if w.dtype != torch.float32:
+        raise FQLError("quant_nvfp4_weight takes float32 weights")
+    w2, ld = _rows_view(w, "w")
+    N, K = w2.shape
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, K // 16), dtype=torch.uint8, device=w.device)
+    _check(lib().fql_quant_nvfp4_f32(_ptr(w2), N, K, ld, float(global_scale), int(hadamard_block),
+                                     _ptr(codes), _ptr(scales), _stream(w.device)))
+    return codes, scales
+
+
+# ---------------------------------------------------------------------------
+# packer
+# ---------------------------------------------------------------------------
+
+def packed_nvfp4_bytes(N, K):
+    n = ctypes.c_size_t()
+    _check(lib().fql_packed_nvfp4_bytes(int(N), int(K), ctypes.byref(n)))
+    return n.value
+
+
+def pack_weight_nvfp4(codes, scales, out=None):
+    """Re-lay canonical NVFP4 weight (codes [N, K/2], scales [N, K/16]) for the GEMM."""
+    _require_cuda(codes, "codes")
+    N, K = codes.shape[0], codes.shape[1] * 2
+    if not (codes.is_contiguous() and scales.is_contiguous()):
+        raise FQLError("codes and scales must be contiguous")
+    if tuple(scales.shape) != (N, K // 16):
+        raise FQLError("scales must be [N, K/16]")
+    nbytes = packed_nvfp4_bytes(N, K)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    _check(lib().fql_pack_weight_nvfp4(_ptr(codes), _ptr(scales), N, K, _ptr(out), out.numel(),
+                                       _stream(codes.device)))
+    return out
+
+
+def unpack_weight_nvfp4(packed, N, K):
+    codes = torch.empty((N, K // 2), dtype=torch.uint8, device=packed.device)
+    scales = torch.empty((N, K // 16), dtype=torch.uint8, device=packed.device)
+    _check(lib().fql_unpack_weight_nvfp4(_ptr(packed), int(N), int(K), _ptr(codes), _ptr(scales),
+                                         _stream(packed.device)))
+    return codes, scales
+
+
+class NVFP4Weight:
+    """A packed NVFP4 weight and the layer constants the linear call needs.
+
+    packed: uint8 device buffer from pack_weight_nvfp4; N, K: logical shape;
+    input_global_scale: the activation encode scale g_x (static calibration);
+    weight_global_scale: g_w; hadamard_block: rotation block (0 = none).
+    alpha = 1 / (g_x * g_w) rounded once to float32.
+    """
+
+    def __init__(self, packed, N, K, input_global_scale, weight_global_scale, hadamard_block=0):
+        self.packed = packed
+        self.N, self.K = int(N), int(K)
+        self.input_global_scale = float(input_global_scale)
+        self.weight_global_scale = float(weight_global_scale)
+        self.hadamard_block = int(hadamard_block)
+        import numpy as np
+
+        self.alpha = float(np.float32((1.0 / np.float64(np.float32(input_global_scale))) *
+                                      (1.0 / np.float64(np.float32(weight_global_scale)))))
+
+    @classmethod
+    def from_float(cls, w, input_global_scale, hadamard_block=0, weight_global_scale=None):
+        """Quantize and pack a float32 weight [N, K] on the GPU."""
+        if weight_global_scale is None:
+            weight_global_scale = global_scale_from_amax(amax(w, hadamard_block).item())
+        codes, scales = quant_nvfp4_weight(w, weight_global_scale, hadamard_block)
+        packed = pack_weight_nvfp4(codes, scales)
+        return cls(packed, w.shape[0], w.shape[1], input_global_scale, weight_global_scale,
+                   hadamard_block)
+
+    def repack_(self, codes, scales):
+        """Re-pack new canonical weights into the same storage (address kept)."""
+        pack_weight_nvfp4(codes, scales, out=self.packed)
+        return self
+
+
+# ---------------------------------------------------------------------------
+# linear
+# ---------------------------------------------------------------------------
+
+def linear_workspace_bytes(M, N, K):
+    n = ctypes.c_size_t()
+    _check(lib().fql_linear_nvfp4_workspace_bytes(int(M), int(N), int(K), ctypes.byref(n)))
+    return n.value
+
+
+_workspaces = {}
+
+
+def _workspace(device, nbytes):
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def linear_nvfp4(x, weight, alpha=None, bias=None, out=None, workspace=None):
+    """y = bf16(alpha * quant(x) @ W^T + bias) for bf16 x [..., K]; returns [..., N]."""
+    _require_cuda(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise FQLError("linear_nvfp4 takes bfloat16 activations")
+    if x.shape[-1] != weight.K:
+        raise FQLError(f"x has K={x.shape[-1]}, weight has K={weight.K}")
+    x2, ld = _rows_view(x, "x")
+    M, K = x2.shape
+    N = weight.N
+    if alpha is None:
+        alpha = weight.alpha
+    if bias is not None:
+        _require_cuda(bias, "bias")
+        if bias.dtype != torch.bfloat16 or bias.numel() != N or not bias.is_contiguous():
+            raise FQLError("bias must be a contiguous bf16 tensor of N elements")
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=torch.bfloat16, device=x.device)
+    y2, ldy = _rows_view(out, "out")
+    need = linear_workspace_bytes(M, N, K)
+    if workspace is None:
+        workspace = _workspace(x.device, need)
+    _check(lib().fql_linear_nvfp4(_ptr(x2), M, K, ld, weight.input_global_scale,
+                                  weight.hadamard_block, _ptr(weight.packed), N, float(alpha),
+                                  _ptr(bias), _ptr(y2), ldy, _ptr(workspace), workspace.numel(),
+                                  _stream(x.device)))
+    return out

@@ -1,0 +1,237 @@
+// C ABI of the gfx950 NVFP4 linear library: argument validation, dispatch,
+// error reporting. Every entry point validates on the host (cheap checks
+// only), enqueues kernels on the caller's stream and returns a status code.
+// The availability / format-constraint split follows the write-ups' kernel
+// lifecycle: is_supported decides availability with a reason string,
+// can_implement checks format constraints, and the hot call only asserts.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/fql.h"
+#include "fql_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return FQL_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FQL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+void write_reason(char* reason, size_t len, const std::string& s) {
+  if (reason && len > 0) {
+    std::snprintf(reason, len, "%s", s.c_str());
+  }
+}
+
+bool valid_hadamard(int hb) { return hb == 0 || hb == 16 || hb == 32 || hb == 64 || hb == 128; }
+
+// Shared NVFP4 shape checks; returns FQL_OK or an error with a message.
+int check_nvfp4_shape(int64_t rows, int64_t K, int64_t ld, int hb, const char* rows_name) {
+  if (rows < 1) return fail(FQL_ERR_INVALID, "%s must be >= 1 (got %lld)", rows_name, (long long)rows);
+  if (K < 16 || K % 16 != 0)
+    return fail(FQL_ERR_INVALID, "K must be a positive multiple of 16 (got %lld)", (long long)K);
+  if (ld < K) return fail(FQL_ERR_INVALID, "row stride %lld is smaller than K %lld", (long long)ld, (long long)K);
+  if (!valid_hadamard(hb))
+    return fail(FQL_ERR_INVALID, "hadamard_block must be 0, 16, 32, 64 or 128 (got %d)", hb);
+  if (hb > 0 && K % hb != 0)
+    return fail(FQL_ERR_INVALID, "K %lld is not a multiple of hadamard_block %d", (long long)K, hb);
+  if (K > (int64_t)1 << 24 || rows > (int64_t)1 << 24)
+    return fail(FQL_ERR_INVALID, "dimension too large");
+  return FQL_OK;
+}
+
+bool aligned16(const void* p, int64_t ld, int64_t elem_bytes) {
+  return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((ld * elem_bytes) % 16 == 0);
+}
+
+int check_scale(float g, const char* name) {
+  if (!std::isfinite(g) || !(g > 0.0f))
+    return fail(FQL_ERR_INVALID, "%s must be finite and > 0 (got %g)", name, (double)g);
+  return FQL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fql_version(void) { return 100; }
+
+const char* fql_last_error(void) { return g_last_error.c_str(); }
+
+int fql_is_supported(int device, char* reason, size_t reason_len) {
+  int count = 0;
+  hipError_t e = hipGetDeviceCount(&count);
+  if (e != hipSuccess || count == 0) {
+    write_reason(reason, reason_len, "no HIP device available");
+    ok();
+    return 0;
+  }
+  if (device < 0 || device >= count) {
+    write_reason(reason, reason_len, "device index out of range");
+    ok();
+    return 0;
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return hip_status(e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    write_reason(reason, reason_len,
+                 std::string("requires a gfx950 (MI355X) device, found ") + prop.gcnArchName);
+    ok();
+    return 0;
+  }
+  write_reason(reason, reason_len, "");
+  ok();
+  return 1;
+}
+
+int fql_can_implement(int format, int64_t N, int64_t K, int hadamard_block, char* reason,
+                      size_t reason_len) {
+  std::string why;
+  if (format != FQL_FMT_NVFP4) why = "unknown format";
+  else if (N < 1) why = "N must be >= 1";
+  else if (K < 16 || K % 16 != 0) why = "K must be a positive multiple of 16 (the NVFP4 block)";
+  else if (!valid_hadamard(hadamard_block)) why = "hadamard_block must be 0, 16, 32, 64 or 128";
+  else if (hadamard_block > 0 && K % hadamard_block != 0) why = "K must be a multiple of hadamard_block";
+  write_reason(reason, reason_len, why);
+  ok();
+  return why.empty() ? 1 : 0;
+}
+
+int fql_amax_bf16(const void* x, int64_t M, int64_t K, int64_t ldx, int hadamard_block,
+                  float* amax_out, void* stream) {
+  if (int r = check_nvfp4_shape(M, K, ldx, hadamard_block, "M")) return r;
+  if (!x || !amax_out) return fail(FQL_ERR_INVALID, "null pointer");
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  return hip_status(fql::launch_amax_bf16(xp, M, K, ldx, hadamard_block, aligned16(x, ldx, 2),
+                                          amax_out, static_cast<hipStream_t>(stream)),
+                    "amax_bf16 launch");
+}
+
+int fql_amax_f32(const float* w, int64_t N, int64_t K, int64_t ldw, int hadamard_block,
+                 float* amax_out, void* stream) {
+  if (int r = check_nvfp4_shape(N, K, ldw, hadamard_block, "N")) return r;
+  if (!w || !amax_out) return fail(FQL_ERR_INVALID, "null pointer");
+  return hip_status(fql::launch_amax_f32(w, N, K, ldw, hadamard_block, aligned16(w, ldw, 4),
+                                         amax_out, static_cast<hipStream_t>(stream)),
+                    "amax_f32 launch");
+}
+
+int fql_quant_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float global_scale,
+                    int hadamard_block, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (int r = check_nvfp4_shape(M, K, ldx, hadamard_block, "M")) return r;
+  if (int r = check_scale(global_scale, "global_scale")) return r;
+  if (!x || !codes || !scales) return fail(FQL_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(codes) % 8 != 0)
+    return fail(FQL_ERR_INVALID, "codes must be 8-byte aligned");
+  return hip_status(
+      fql::launch_quant_nvfp4_bf16(static_cast<const uint16_t*>(x), M, K, ldx, global_scale,
+                                   hadamard_block, aligned16(x, ldx, 2), codes, scales,
+                                   static_cast<hipStream_t>(stream)),
+      "quant_nvfp4 launch");
+}
+
+int fql_quant_nvfp4_f32(const float* w, int64_t N, int64_t K, int64_t ldw, float global_scale,
+                        int hadamard_block, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (int r = check_nvfp4_shape(N, K, ldw, hadamard_block, "N")) return r;
+  if (int r = check_scale(global_scale, "global_scale")) return r;
+  if (!w || !codes || !scales) return fail(FQL_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(codes) % 8 != 0)
+    return fail(FQL_ERR_INVALID, "codes must be 8-byte aligned");
+  return hip_status(fql::launch_quant_nvfp4_f32(w, N, K, ldw, global_scale, hadamard_block,
+                                                aligned16(w, ldw, 4), codes, scales,
+                                                static_cast<hipStream_t>(stream)),
+                    "quant_nvfp4_f32 launch");
+}
+
+int fql_packed_nvfp4_bytes(int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(FQL_ERR_INVALID, "null pointer");
+  if (N < 1 || K < 16 || K % 16 != 0)
+    return fail(FQL_ERR_INVALID, "need N >= 1 and K a positive multiple of 16");
+  *bytes = (size_t)fql::packed_dims(N, K).total_bytes();
+  return ok();
+}
+
+int fql_pack_weight_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                          void* packed, size_t packed_bytes, void* stream) {
+  if (int r = check_nvfp4_shape(N, K, K, 0, "N")) return r;
+  if (!codes || !scales || !packed) return fail(FQL_ERR_INVALID, "null pointer");
+  const size_t need = (size_t)fql::packed_dims(N, K).total_bytes();
+  if (packed_bytes < need)
+    return fail(FQL_ERR_INVALID, "packed buffer holds %zu bytes, %zu needed", packed_bytes, need);
+  if (reinterpret_cast<uintptr_t>(packed) % 16 != 0)
+    return fail(FQL_ERR_INVALID, "packed buffer must be 16-byte aligned");
+  return hip_status(fql::launch_pack_nvfp4(codes, scales, N, K, static_cast<uint8_t*>(packed),
+                                           static_cast<hipStream_t>(stream)),
+                    "pack launch");
+}
+
+int fql_unpack_weight_nvfp4(const void* packed, int64_t N, int64_t K, uint8_t* codes,
+                            uint8_t* scales, void* stream) {
+  if (int r = check_nvfp4_shape(N, K, K, 0, "N")) return r;
+  if (!codes || !scales || !packed) return fail(FQL_ERR_INVALID, "null pointer");
+  return hip_status(fql::launch_unpack_nvfp4(static_cast<const uint8_t*>(packed), N, K, codes,
+                                             scales, static_cast<hipStream_t>(stream)),
+                    "unpack launch");
+}
+
+int fql_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(FQL_ERR_INVALID, "null pointer");
+  if (M < 1 || N < 1 || K < 16 || K % 16 != 0)
+    return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 16");
+  *bytes = (size_t)fql::plan_gemm_nvfp4(M, N, K).total_bytes;
+  return ok();
+}
+
+int fql_linear_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float input_global_scale,
+                     int hadamard_block, const void* w_packed, int64_t N, float alpha,
+                     const void* bias, void* y, int64_t ldy, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (int r = check_nvfp4_shape(M, K, ldx, hadamard_block, "M")) return r;
+  if (int r = check_scale(input_global_scale, "input_global_scale")) return r;
+  if (!std::isfinite(alpha)) return fail(FQL_ERR_INVALID, "alpha must be finite");
+  if (N < 1 || N > (int64_t)1 << 24) return fail(FQL_ERR_INVALID, "N out of range");
+  if (ldy < N) return fail(FQL_ERR_INVALID, "ldy %lld is smaller than N %lld", (long long)ldy, (long long)N);
+  if (!x || !w_packed || !y || !workspace) return fail(FQL_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(w_packed) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(FQL_ERR_INVALID, "packed weight must be 16-byte and workspace 256-byte aligned");
+  const fql::GemmPlan plan = fql::plan_gemm_nvfp4(M, N, K);
+  if (workspace_bytes < (size_t)plan.total_bytes)
+    return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
+                (long long)plan.total_bytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  _Float16* xhat = reinterpret_cast<_Float16*>(ws);
+  float* partial = reinterpret_cast<float*>(ws + plan.xhat_bytes);
+  hipError_t e = fql::launch_quant_nvfp4_xhat(static_cast<const uint16_t*>(x), M, K, ldx,
+                                              input_global_scale, hadamard_block,
+                                              aligned16(x, ldx, 2), plan.Mp, plan.Kp, xhat, st);
+  if (e != hipSuccess) return hip_status(e, "quant launch");
+  e = fql::launch_gemm_nvfp4(plan, xhat, static_cast<const uint8_t*>(w_packed), M, N, alpha,
+                             static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), ldy,
+                             partial, st);
+  return hip_status(e, "gemm launch");
+}
+
+}  // extern "C"

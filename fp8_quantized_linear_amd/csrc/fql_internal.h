@@ -1,0 +1,65 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fql {
+
+// ---- packed NVFP4 weight layout -------------------------------------------
+// N is padded to a multiple of 16 (one MFMA tile of output columns) and K to
+// a multiple of 128 (four 32-deep MFMA steps). The blob holds the code region
+// followed by the scale region:
+//   codes  [Np/16][Kp/128][lane 64][16 bytes]   lane = kq*16 + n  (n < 16, kq < 4)
+//          dword j of a lane = the eight codes of row n at k = 128c + 32j + 8kq + 0..7,
+//          element i in nibble i (canonical nibble order).
+//   scales [Np/16][Kp/128][n 16][8 bytes]        byte h*4 + j = scale of block 8c + 2j + h
+// One 16-byte load per lane gives the B operand codes of four MFMA steps, and
+// one 4-byte load the matching four scales.
+struct PackedDims {
+  int64_t Np, Kp;
+  int64_t code_bytes() const { return Np * Kp / 2; }
+  int64_t scale_bytes() const { return Np * Kp / 16; }
+  int64_t total_bytes() const { return code_bytes() + scale_bytes(); }
+};
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+inline PackedDims packed_dims(int64_t N, int64_t K) { return PackedDims{round_up(N, 16), round_up(K, 128)}; }
+
+// ---- launchers (stream-ordered, return the launch status) -----------------
+hipError_t launch_quant_nvfp4_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
+                                   int hb, bool aligned, uint8_t* codes, uint8_t* scales,
+                                   hipStream_t st);
+hipError_t launch_quant_nvfp4_f32(const float* w, int64_t N, int64_t K, int64_t ldw, float g,
+                                  int hb, bool aligned, uint8_t* codes, uint8_t* scales,
+                                  hipStream_t st);
+hipError_t launch_quant_nvfp4_xhat(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
+                                   int hb, bool aligned, int64_t Mp, int64_t Kp, _Float16* xhat,
+                                   hipStream_t st);
+hipError_t launch_amax_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int hb,
+                            bool aligned, float* out, hipStream_t st);
+hipError_t launch_amax_f32(const float* w, int64_t N, int64_t K, int64_t ldw, int hb, bool aligned,
+                           float* out, hipStream_t st);
+
+hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                             uint8_t* packed, hipStream_t st);
+hipError_t launch_unpack_nvfp4(const uint8_t* packed, int64_t N, int64_t K, uint8_t* codes,
+                               uint8_t* scales, hipStream_t st);
+
+// GEMM launch plan for one (M, N, K): tile shape, split-K, workspace carve-up.
+struct GemmPlan {
+  int mt;            // 16-row M tiles per workgroup
+  int nt;            // 16-column N tiles per wave (4 waves per workgroup)
+  int64_t Mp;        // M padded to mt*16
+  int64_t Np, Kp;    // packed weight dims
+  int splits;        // K splits (1 = epilogue fused in the GEMM)
+  int kc_per_split;  // 128-wide K chunks per split
+  int64_t xhat_bytes, partial_bytes, total_bytes;
+};
+GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K);
+
+hipError_t launch_gemm_nvfp4(const GemmPlan& p, const _Float16* xhat, const uint8_t* packed,
+                             int64_t M, int64_t N, float alpha, const uint16_t* bias, uint16_t* y,
+                             int64_t ldy, float* partial, hipStream_t st);
+
+}  // namespace fql

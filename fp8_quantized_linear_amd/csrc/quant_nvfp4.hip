@@ -1,0 +1,306 @@
+// NVFP4 quantizer kernels for gfx950: fused block-diagonal Hadamard (FWHT),
+// per-16 amax, E4M3 block scale, E2M1 encode, nibble packing.
+//
+// What is computed (vLLM write-ups: "TorchNvFp4LinearKernel" quantizes the
+// activation with the layer's input global scale into packed FP4 bytes plus
+// block scales; "QUTLASS NVFP4 online transforms" fuses the block-diagonal
+// Hadamard rotation, normalised by 1/sqrt(n) with n in {16,32,64,128}, into
+// that quantizer):
+//   v   = x (float32), rotated per b-chunk if b > 0
+//   a   = max |v| over each 16-element block
+//   s   = E4M3_RNE_satfinite(fl32(fl32(a / 6) * g))
+//   r   = fl32(g / s), or 0 when s == 0
+//   q_i = E2M1_RNE_satfinite(fl32(v_i * r)), sign of v_i kept
+//
+// Work mapping: one thread per 16-element block. Consecutive threads take
+// consecutive blocks of a row, so a wave reads 64 * 32 contiguous bytes of
+// bf16 (two 16-byte loads per lane) and writes 64 * 8 contiguous code bytes.
+// The FWHT's first four butterfly strides (1, 2, 4, 8) stay inside a thread;
+// strides 16, 32, 64 pair a lane with lane ^ 1, ^ 2, ^ 4 through cross-lane
+// shuffles (a b-chunk is b/16 <= 8 adjacent lanes of one wave).
+//
+// No FMA contraction anywhere in this file: every float operation must be
+// the single IEEE operation the definition names.
+#pragma clang fp contract(off)
+
+#include "fql_device.h"
+#include "fql_internal.h"
+
+namespace fql {
+
+template <typename TIn>
+struct Loader;
+
+// bf16 rows: 16 elements = 32 bytes.
+template <>
+struct Loader<uint16_t> {
+  static __device__ __forceinline__ void load16(const uint16_t* p, bool aligned16, float v[16]) {
+    if (aligned16) {
+      const uint4v* q = reinterpret_cast<const uint4v*>(p);
+      uint4v a = q[0], b = q[1];
+      uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = bf16_bits_to_f32(p[i]);
+    }
+  }
+};
+
+// float32 rows: 16 elements = 64 bytes.
+template <>
+struct Loader<float> {
+  static __device__ __forceinline__ void load16(const float* p, bool aligned16, float v[16]) {
+    if (aligned16) {
+      const float4v* q = reinterpret_cast<const float4v*>(p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4v t = q[i];
+        v[4 * i] = t.x;
+        v[4 * i + 1] = t.y;
+        v[4 * i + 2] = t.z;
+        v[4 * i + 3] = t.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = p[i];
+    }
+  }
+};
+
+// Rotate the thread's 16 values as part of its b-chunk: in-thread butterfly
+// strides 1, 2, 4, 8 (those below b), then cross-lane strides 16 .. b/2, then
+// the 1/sqrt(b) multiply. `blk` is the block index within the row; its low
+// bits give this thread's position inside the chunk.
+template <int HB>
+__device__ __forceinline__ void fwht_block(float v[16], int64_t blk) {
+#pragma unroll
+  for (int h = 1; h < 16 && h < HB; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if ((e & h) == 0) {
+        float a = v[e], b = v[e + h];
+        v[e] = a + b;
+        v[e + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int hs = 1; hs < HB / 16; hs <<= 1) {
+    const bool upper = (blk & hs) != 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float other = __shfl_xor(v[e], hs);
+      // lower lane holds a, upper lane holds b: lower gets a + b, upper a - b
+      v[e] = upper ? (other - v[e]) : (v[e] + other);
+    }
+  }
+  // fl32(1/sqrt(b)): 0x3E800000, 0x3E3504F3, 0x3E000000, 0x3DB504F3
+  const float cb = HB == 16 ? 0x1p-2f : HB == 32 ? 0x1.6a09e6p-3f : HB == 64 ? 0x1p-3f : 0x1.6a09e6p-4f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = v[e] * cb;
+}
+
+// Quantize one 16-block: codes (16 nibbles as two words) and the scale byte.
+__device__ __forceinline__ void quant_block(const float v[16], float g, uint32_t& lo, uint32_t& hi,
+                                            uint32_t& sbyte) {
+  float a = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(v[e]));
+  const float sf = (a / 6.0f) * g;
+  const uint32_t s = e4m3_encode_nonneg(sf);
+  const float sd = e4m3_decode_nonneg(s);
+  const float r = sd == 0.0f ? 0.0f : g / sd;
+  lo = 0u;
+  hi = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) lo |= e2m1_encode(v[e] * r) << (4 * e);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) hi |= e2m1_encode(v[8 + e] * r) << (4 * e);
+  sbyte = s;
+}
+
+// Canonical output: codes [rows][K/2], scales [rows][K/16].
+template <typename TIn, int HB>
+__global__ __launch_bounds__(256) void quant_nvfp4_canonical_kernel(
+    const TIn* __restrict__ x, int64_t rows, int64_t K, int64_t ldx, float g, int aligned16,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t nblk = K / 16;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool active = i < rows * nblk;
+  const int64_t m = active ? i / nblk : 0;
+  const int64_t kb = active ? i - m * nblk : 0;
+  float v[16];
+  if (active) {
+    Loader<TIn>::load16(x + m * ldx + kb * 16, aligned16 != 0, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = 0.0f;
+  }
+  if constexpr (HB > 0) fwht_block<HB>(v, kb);
+  if (!active) return;
+  uint32_t lo, hi, s;
+  quant_block(v, g, lo, hi, s);
+  *reinterpret_cast<uint2*>(codes + m * (K / 2) + kb * 8) = make_uint2(lo, hi);
+  scales[m * nblk + kb] = (uint8_t)s;
+}
+
+// GEMM operand output: the exactly dequantized activation x_hat = e2m1(q)*s
+// in float16, in the MFMA A-fragment order the GEMM reads (see gemm_nvfp4):
+//   [Mp/16][Kp/32][lane 0..63][8 halves], lane = kq*16 + (m%16), k = 32*ks + 8*kq + i.
+// Rows >= M and columns >= K are written as zeros.
+template <int HB>
+__global__ __launch_bounds__(256) void quant_nvfp4_xhat_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, float g, int aligned16,
+    int64_t Mp, int64_t Kp, _Float16* __restrict__ xhat) {
+  const int64_t nblk = Kp / 16;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= Mp * nblk) return;  // whole waves only: Mp * nblk is a multiple of 64
+  const int64_t m = i / nblk;
+  const int64_t kb = i - m * nblk;
+  const bool real = (m < M) && (kb * 16 < K);
+  float v[16];
+  if (real) {
+    Loader<uint16_t>::load16(x + m * ldx + kb * 16, aligned16 != 0, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = 0.0f;
+  }
+  if constexpr (HB > 0) fwht_block<HB>(v, kb);
+  uint32_t lo, hi, s;
+  quant_block(v, g, lo, hi, s);
+  const float sd = e4m3_decode_nonneg(s);
+  uint32_t hw[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint32_t w = p < 4 ? lo : hi;
+    const uint32_t c0 = (w >> (8 * (p & 3))) & 15u, c1 = (w >> (8 * (p & 3) + 4)) & 15u;
+    _Float16 h0 = (_Float16)(e2m1_decode(c0) * sd);  // exact: <= 6 significant bits
+    _Float16 h1 = (_Float16)(e2m1_decode(c1) * sd);
+    hw[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+            ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+  }
+  const int64_t k0 = kb * 16;
+  const int64_t ks = k0 / 32;
+  const int kq0 = (int)((k0 % 32) / 8);  // 0 or 2
+  const int ml = (int)(m % 16);
+  _Float16* base = xhat + (((m / 16) * (Kp / 32) + ks) * 64) * 8;
+  uint4v* d0 = reinterpret_cast<uint4v*>(base + (kq0 * 16 + ml) * 8);
+  uint4v* d1 = reinterpret_cast<uint4v*>(base + ((kq0 + 1) * 16 + ml) * 8);
+  *d0 = uint4v{hw[0], hw[1], hw[2], hw[3]};
+  *d1 = uint4v{hw[4], hw[5], hw[6], hw[7]};
+}
+
+// max |v| (after the optional rotation) into *amax (as ordered uint bits;
+// non-negative floats compare like their bit patterns). *amax must be 0 first.
+template <typename TIn, int HB>
+__global__ __launch_bounds__(256) void amax_kernel(const TIn* __restrict__ x, int64_t rows,
+                                                   int64_t K, int64_t ldx, int aligned16,
+                                                   uint32_t* __restrict__ amax) {
+  const int64_t nblk = K / 16;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool active = i < rows * nblk;
+  const int64_t m = active ? i / nblk : 0;
+  const int64_t kb = active ? i - m * nblk : 0;
+  float v[16];
+  if (active) {
+    Loader<TIn>::load16(x + m * ldx + kb * 16, aligned16 != 0, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = 0.0f;
+  }
+  if constexpr (HB > 0) fwht_block<HB>(v, kb);
+  float a = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(v[e]));
+  for (int off = 32; off > 0; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off));
+  if ((threadIdx.x & 63) == 0) atomicMax(amax, __float_as_uint(a));
+}
+
+__global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+template <typename TIn>
+static hipError_t launch_canonical(const TIn* x, int64_t rows, int64_t K, int64_t ldx, float g,
+                                   int hb, bool aligned, uint8_t* codes, uint8_t* scales,
+                                   hipStream_t st) {
+  const int64_t total = rows * (K / 16);
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  const int al = aligned ? 1 : 0;
+  switch (hb) {
+    case 0: quant_nvfp4_canonical_kernel<TIn, 0><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales); break;
+    case 16: quant_nvfp4_canonical_kernel<TIn, 16><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales); break;
+    case 32: quant_nvfp4_canonical_kernel<TIn, 32><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales); break;
+    case 64: quant_nvfp4_canonical_kernel<TIn, 64><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales); break;
+    case 128: quant_nvfp4_canonical_kernel<TIn, 128><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nvfp4_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
+                                   int hb, bool aligned, uint8_t* codes, uint8_t* scales,
+                                   hipStream_t st) {
+  return launch_canonical<uint16_t>(x, M, K, ldx, g, hb, aligned, codes, scales, st);
+}
+
+hipError_t launch_quant_nvfp4_f32(const float* w, int64_t N, int64_t K, int64_t ldw, float g,
+                                  int hb, bool aligned, uint8_t* codes, uint8_t* scales,
+                                  hipStream_t st) {
+  return launch_canonical<float>(w, N, K, ldw, g, hb, aligned, codes, scales, st);
+}
+
+hipError_t launch_quant_nvfp4_xhat(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
+                                   int hb, bool aligned, int64_t Mp, int64_t Kp, _Float16* xhat,
+                                   hipStream_t st) {
+  const int64_t total = Mp * (Kp / 16);
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  const int al = aligned ? 1 : 0;
+  switch (hb) {
+    case 0: quant_nvfp4_xhat_kernel<0><<<grid, block, 0, st>>>(x, M, K, ldx, g, al, Mp, Kp, xhat); break;
+    case 16: quant_nvfp4_xhat_kernel<16><<<grid, block, 0, st>>>(x, M, K, ldx, g, al, Mp, Kp, xhat); break;
+    case 32: quant_nvfp4_xhat_kernel<32><<<grid, block, 0, st>>>(x, M, K, ldx, g, al, Mp, Kp, xhat); break;
+    case 64: quant_nvfp4_xhat_kernel<64><<<grid, block, 0, st>>>(x, M, K, ldx, g, al, Mp, Kp, xhat); break;
+    case 128: quant_nvfp4_xhat_kernel<128><<<grid, block, 0, st>>>(x, M, K, ldx, g, al, Mp, Kp, xhat); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename TIn>
+static hipError_t launch_amax(const TIn* x, int64_t rows, int64_t K, int64_t ldx, int hb,
+                              bool aligned, float* out, hipStream_t st) {
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);
+  zero_u32_kernel<<<1, 1, 0, st>>>(o);
+  const int64_t total = rows * (K / 16);
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  const int al = aligned ? 1 : 0;
+  switch (hb) {
+    case 0: amax_kernel<TIn, 0><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o); break;
+    case 16: amax_kernel<TIn, 16><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o); break;
+    case 32: amax_kernel<TIn, 32><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o); break;
+    case 64: amax_kernel<TIn, 64><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o); break;
+    case 128: amax_kernel<TIn, 128><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int hb,
+                            bool aligned, float* out, hipStream_t st) {
+  return launch_amax<uint16_t>(x, M, K, ldx, hb, aligned, out, st);
+}
+
+hipError_t launch_amax_f32(const float* w, int64_t N, int64_t K, int64_t ldw, int hb, bool aligned,
+                           float* out, hipStream_t st) {
+  return launch_amax<float>(w, N, K, ldw, hb, aligned, out, st);
+}
+
+}  // namespace fql

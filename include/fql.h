@@ -1,0 +1,167 @@
+/*
+ * fql.h - C ABI of the MI355X (gfx950) NVFP4 W4A4 quantized linear library.
+ *
+ * The layer (vLLM write-ups "TorchNvFp4LinearKernel", "QUTLASS NVFP4 online
+ * transforms", "B12X CuTe-DSL linear backends"): bf16 activations are
+ * quantized on the fly to NVFP4 (E2M1 codes, one E4M3 scale per 16 elements
+ * along K, one float32 global scale), optionally after a block-diagonal
+ * Hadamard rotation; a block-scaled GEMM multiplies them with a pre-packed
+ * NVFP4 weight; alpha (the product of the two global dequant scales) and an
+ * optional bias are applied and the result is cast to bf16.
+ *
+ * Conventions shared by every call:
+ *  - All tensor pointers are DEVICE pointers unless stated otherwise, owned by
+ *    the caller. Outputs are caller-allocated and written in place; no call
+ *    allocates device memory (the write-ups' in-place quantize op takes
+ *    preallocated outputs for the same reason).
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream). Every
+ *    call is stream-ordered and asynchronous: it only enqueues kernels.
+ *  - Sizes are element counts; leading dimensions (ld*) are in elements.
+ *  - Return value: FQL_OK (0) or a negative FQL_ERR_* code. On error nothing
+ *    is launched and fql_last_error() returns a message for the calling
+ *    thread. Validation is cheap and host-side only.
+ *  - Layouts: activations x [M][ldx] bf16 row-major (ldx >= K, any row
+ *    stride: a non-contiguous row slice is consumed without a copy, as the
+ *    B12X NVFP4 path requires); codes [rows][K/2] bytes with the even-index
+ *    element in the low nibble; scales [rows][K/16] E4M3 bytes, row-major
+ *    (the canonical layout; the GEMM's own layout is internal to the packed
+ *    weight); y [M][ldy] bf16 row-major, exactly N columns written.
+ *  - Numerics of the quantizer: a = max|v| over the 16-block,
+ *    s = E4M3_RNE_satfinite(fl32(fl32(a/6)*g)), r = fl32(g/s) (0 if s == 0),
+ *    q = E2M1_RNE_satfinite(fl32(v*r)) with the sign of v kept. Codes and
+ *    scales are bit-identical to the CPU oracle.
+ */
+#ifndef FQL_H
+#define FQL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FQL_OK 0
+#define FQL_ERR_INVALID -1     /* bad argument: shape, stride, pointer, value */
+#define FQL_ERR_UNSUPPORTED -2 /* device or configuration not supported */
+#define FQL_ERR_HIP -3         /* a HIP runtime call failed */
+#define FQL_ERR_WORKSPACE -4   /* workspace too small */
+
+/* Weight/activation formats (fql_can_implement). */
+#define FQL_FMT_NVFP4 1
+
+/* Library version (major*10000 + minor*100 + patch). */
+int fql_version(void);
+
+/* Message for the last error returned on the calling thread ("" if none). */
+const char* fql_last_error(void);
+
+/*
+ * Availability check, in the spirit of the write-ups' is_supported(): returns
+ * 1 if `device` is a gfx950 GPU this library was built for, else 0, and
+ * writes the reason into `reason` (may be NULL) when it is not. Negative on
+ * a HIP error.
+ */
+int fql_is_supported(int device, char* reason, size_t reason_len);
+
+/*
+ * Format-level constraints, in the spirit of can_implement(): returns 1 if a
+ * layer with these sizes can run, else 0 with the reason. NVFP4 needs
+ * K % 16 == 0, N >= 1, K >= 16, and hadamard_block in {0, 16, 32, 64, 128}
+ * with K % hadamard_block == 0.
+ */
+int fql_can_implement(int format, int64_t N, int64_t K, int hadamard_block, char* reason,
+                      size_t reason_len);
+
+/*
+ * max |v| over x [M][K] (bf16, row stride ldx) after the optional
+ * block-diagonal Hadamard rotation (hadamard_block 0 = none), written as one
+ * float to `amax_out` (device). The calibration value for the global scale
+ * g = 448*6/amax (QUTLASS write-up: the rotation is applied before
+ * quantization, so the calibration sees rotated values).
+ */
+int fql_amax_bf16(const void* x, int64_t M, int64_t K, int64_t ldx, int hadamard_block,
+                  float* amax_out, void* stream);
+
+/* Same for float32 input (weights before packing). */
+int fql_amax_f32(const float* w, int64_t N, int64_t K, int64_t ldw, int hadamard_block,
+                 float* amax_out, void* stream);
+
+/*
+ * Activation quantizer (TorchNvFp4LinearKernel apply_weights: the activation
+ * is quantized with the layer's input global scale into packed FP4 bytes and
+ * block scales; QUTLASS write-up: fused block-diagonal Hadamard + NVFP4
+ * quantize into caller-provided code and scale tensors).
+ *   x       [M][ldx] bf16, ldx >= K; 16-byte aligned rows are fastest but not
+ *           required.
+ *   global_scale  g > 0 and finite (the reciprocal of the global dequant scale).
+ *   hadamard_block 0 (none) or 16/32/64/128: per b-element chunk of each row,
+ *           v = H_b v / sqrt(b) with Sylvester H_b, as a float32 FWHT with
+ *           strides 1, 2, ..., b/2 and one multiply by fl32(1/sqrt(b)).
+ *   codes   [M][K/2] bytes out; scales [M][K/16] E4M3 bytes out.
+ */
+int fql_quant_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float global_scale,
+                    int hadamard_block, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * Weight quantizer: as fql_quant_nvfp4 but for float32 input w [N][ldw]. With
+ * hadamard_block > 0 the weight rows are rotated by the same transform, so
+ * x' w'^T = x w^T (the rotation is orthogonal).
+ */
+int fql_quant_nvfp4_f32(const float* w, int64_t N, int64_t K, int64_t ldw, float global_scale,
+                        int hadamard_block, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * Size in bytes of the packed weight for an [N][K] NVFP4 weight (host-side,
+ * no device work). The packed blob pads N to a multiple of 16 and K to a
+ * multiple of 128 with zeros.
+ */
+int fql_packed_nvfp4_bytes(int64_t N, int64_t K, size_t* bytes);
+
+/*
+ * Weight packer (process_weights_after_loading in the write-ups, which
+ * re-lays block scales and pads the weight for their GEMM): re-lays canonical
+ * codes [N][K/2] and scales [N][K/16] into the GEMM's operand order. Writes
+ * into the caller's buffer `packed` (packed_bytes from
+ * fql_packed_nvfp4_bytes), so re-packing a reloaded weight keeps its address
+ * (the B12X write-up reuses packed storage so captured graphs stay valid).
+ */
+int fql_pack_weight_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                          void* packed, size_t packed_bytes, void* stream);
+
+/* Inverse of fql_pack_weight_nvfp4 (packed -> canonical codes and scales). */
+int fql_unpack_weight_nvfp4(const void* packed, int64_t N, int64_t K, uint8_t* codes,
+                            uint8_t* scales, void* stream);
+
+/*
+ * Workspace bytes fql_linear_nvfp4 needs for this shape (host-side). The
+ * workspace holds the dequantized activation tile operand and, for split-K
+ * launches, float32 partial sums.
+ */
+int fql_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
+
+/*
+ * The NVFP4 W4A4 linear layer (TorchNvFp4LinearKernel / B12X NVFP4
+ * apply_weights): y = bf16(alpha * (x_q @ w_q^T) + bias), where x_q is x
+ * quantized exactly as fql_quant_nvfp4 does with (input_global_scale,
+ * hadamard_block), w_q the packed weight, and the sum is accumulated in
+ * float32 over exactly dequantized products.
+ *   x        [M][ldx] bf16, M >= 1 (M = product of the leading dims).
+ *   w_packed from fql_pack_weight_nvfp4 for an [N][K] weight (rotated with
+ *            the same hadamard_block if it is > 0).
+ *   alpha    float32 scalar: 1 / (g_x * g_w).
+ *   bias     [N] bf16 or NULL.
+ *   y        [M][ldy] bf16 out, ldy >= N.
+ *   workspace/workspace_bytes  device scratch of at least
+ *            fql_linear_nvfp4_workspace_bytes(M, N, K).
+ */
+int fql_linear_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float input_global_scale,
+                     int hadamard_block, const void* w_packed, int64_t N, float alpha,
+                     const void* bias, void* y, int64_t ldy, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FQL_H */

@@ -1,0 +1,92 @@
+"""The C-ABI library loads and exports every symbol include/fql.h declares (CPU).
+
+No compute calls: only host-side entry points (version, size queries,
+format checks, argument validation that fails before any launch).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_quantized_linear_amd as fql
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "fql.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fql_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = fql.lib()
+    names = _declared()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_covers_every_declared_symbol():
+    assert set(_declared()) == set(fql.SIGNATURES)
+
+
+def test_version_and_sizes():
+    lib = fql.lib()
+    assert lib.fql_version() >= 100
+    # packed blob: N padded to 16, K to 128; codes K/2 + scales K/16 bytes per row
+    assert fql.packed_nvfp4_bytes(512, 256) == 512 * 256 // 2 + 512 * 256 // 16
+    assert fql.packed_nvfp4_bytes(100, 272) == 112 * 384 // 2 + 112 * 384 // 16
+    assert fql.linear_workspace_bytes(1, 6144, 4096) > 0
+
+
+def test_can_implement_rules():
+    assert fql.can_implement(4096, 4096, 0) == (True, "")
+    assert fql.can_implement(5120, 25600, 128)[0]
+    ok, why = fql.can_implement(4096, 4100, 0)
+    assert not ok and "16" in why
+    ok, why = fql.can_implement(4096, 4096, 24)
+    assert not ok and "hadamard" in why
+    ok, why = fql.can_implement(4096, 4112, 32)
+    assert not ok and "multiple" in why
+
+
+def test_is_supported_without_gpu_reports_reason():
+    try:
+        import torch
+
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except Exception:
+        pass
+    ok, why = fql.is_supported(0)
+    assert not ok and why
+
+
+@pytest.mark.parametrize("K,hb", [(4100, 0), (4096, 24), (48, 32), (0, 0)])
+def test_invalid_shapes_rejected_before_launch(K, hb):
+    lib = fql.lib()
+    null = ctypes.c_void_p(0)
+    st = lib.fql_quant_nvfp4(ctypes.c_void_p(16), 4, K, max(K, 16), 1.0, hb, ctypes.c_void_p(16),
+                             ctypes.c_void_p(16), null)
+    assert st == -1
+    assert lib.fql_last_error().decode()
+
+
+def test_invalid_scalars_rejected():
+    lib = fql.lib()
+    p = ctypes.c_void_p(256)
+    null = ctypes.c_void_p(0)
+    for g in (0.0, -1.0, float("inf"), float("nan")):
+        assert lib.fql_quant_nvfp4(p, 4, 64, 64, g, 0, p, p, null) == -1
+    # null pointers
+    assert lib.fql_quant_nvfp4(null, 4, 64, 64, 1.0, 0, p, p, null) == -1
+    # ldx < K
+    assert lib.fql_quant_nvfp4(p, 4, 64, 32, 1.0, 0, p, p, null) == -1
+    # linear: ldy < N, tiny workspace
+    assert lib.fql_linear_nvfp4(p, 1, 64, 64, 1.0, 0, p, 64, 1.0, null, p, 32, p, 1 << 20, null) == -1
+    assert lib.fql_linear_nvfp4(p, 1, 64, 64, 1.0, 0, p, 64, 1.0, null, p, 64, p, 16, null) == -4
+    # pack into a buffer that is too small
+    assert lib.fql_pack_weight_nvfp4(p, p, 64, 64, p, 10, null) == -1

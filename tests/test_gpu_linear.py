@@ -1,0 +1,176 @@
+"""GPU parity of the NVFP4 W4A4 linear layer against the oracle.
+
+The HIP path quantizes the activation, runs the block-scaled GEMM and the
+fused epilogue; the oracle quantizes independently and evaluates the float64
+product of the decoded operands, rounded to bf16. Outputs must agree within a
+relative Frobenius error of 1e-3 (bf16 vs bf16). Large configurations compare
+a seeded sample of rows and columns, each computed in full by the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_quantized_linear_amd as fql
+import synthetic
+from oracle import formats as F
+from oracle import nvfp4 as Q
+from oracle.hadamard import fwht_fp32
+
+from gpu_helpers import (DEV, REL_FROB_TOL, alpha_of, announce, bf16_bits_to_dev,
+                         cached_activations, dev_bf16_to_bits, f32_to_dev, rel_frob, weight_case)
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_weight(W, gw, hb, gx):
+    """Quantize + pack on the GPU with the oracle's g_w; check codes bit-exactly."""
+    codes, scales = fql.quant_nvfp4_weight(f32_to_dev(W), float(gw), hb)
+    packed = fql.pack_weight_nvfp4(codes, scales)
+    return fql.NVFP4Weight(packed, W.shape[0], W.shape[1], float(gx), float(gw), hb), codes, scales
+
+
+def _run_case(config, M, K, N, hb, with_bias, rows=None, cols=None, xkind=None, label=""):
+    xkind = xkind or synthetic.WORKLOADS[config]["x"]
+    xb = cached_activations(xkind, M, K, config)
+    x32 = synthetic.bf16_bits_to_f32(xb)
+    r_sel = np.arange(M) if rows is None else np.asarray(rows)
+    c_sel = None if cols is None else tuple(int(c) for c in cols)
+    gx = Q.global_scale_from_amax(Q.amax_for_calibration(x32[r_sel], hb))
+    W, gw, wc_ref, ws_ref = weight_case(config, N, K, hb, c_sel)
+    bias_bits = synthetic.bias(N, config=config) if with_bias else None
+    alpha = alpha_of(gx, gw)
+
+    announce(f"linear {label} {config} M={M} K={K} N={N} hb={hb} bias={with_bias}")
+    wobj, wcodes, wscales = _gpu_weight(W, gw, hb, gx)
+    if c_sel is None:
+        assert np.array_equal(wcodes.cpu().numpy(), wc_ref)
+        assert np.array_equal(wscales.cpu().numpy(), ws_ref)
+    else:
+        assert np.array_equal(wcodes.cpu().numpy()[list(c_sel)], wc_ref)
+        assert np.array_equal(wscales.cpu().numpy()[list(c_sel)], ws_ref)
+    xd = bf16_bits_to_dev(xb)
+    bd = bf16_bits_to_dev(bias_bits) if with_bias else None
+    y = fql.linear_nvfp4(xd, wobj, alpha=float(alpha), bias=bd)
+    torch.cuda.synchronize()
+    yb = dev_bf16_to_bits(y)
+
+    xc, xs = Q.quant_nvfp4(x32[r_sel], gx, hb)
+    bias64 = None
+    if with_bias:
+        bias64 = F.bf16_bits_to_f64(bias_bits if c_sel is None else bias_bits[list(c_sel)])
+    ref = Q.linear_nvfp4(xc, xs, wc_ref, ws_ref, alpha, bias64)
+    got = yb[r_sel] if c_sel is None else yb[np.ix_(r_sel, list(c_sel))]
+    err = rel_frob(got, ref)
+    assert err <= REL_FROB_TOL, f"rel Frobenius {err:.3e}"
+    return err
+
+
+def test_linear_tiny():
+    _run_case("tiny", 16, 256, 512, 0, False, label="tiny")
+
+
+@pytest.mark.parametrize("M", [1, 8, 32, 128])
+@pytest.mark.parametrize("shape", ["qkv", "gate_up", "down"])
+def test_linear_decode(M, shape):
+    K, N = synthetic.LLAMA_SHAPES[shape]
+    _run_case("decode", M, K, N, 0, True, label=shape)
+
+
+@pytest.mark.parametrize("M", [2048, 8192])
+@pytest.mark.parametrize("shape", ["qkv", "gate_up", "down"])
+def test_linear_prefill_sampled(M, shape):
+    K, N = synthetic.LLAMA_SHAPES[shape]
+    r = np.random.default_rng(M + K + N)
+    rows = np.sort(r.choice(M, 48, replace=False))
+    rows[-1] = M - 1
+    cols = np.sort(r.choice(N, 96, replace=False))
+    cols[-1] = N - 1
+    _run_case("prefill", M, K, N, 0, False, rows=rows, cols=cols, label=shape)
+
+
+@pytest.mark.parametrize("hb", [16, 32, 64, 128])
+@pytest.mark.parametrize("shape", ["gate_up", "down"])
+@pytest.mark.parametrize("M", [1, 256, 4096])
+def test_linear_hadamard_sampled(hb, shape, M):
+    K, N = synthetic.QWEN_SHAPES[shape]
+    r = np.random.default_rng(hb + M + K)
+    rows = None if M <= 256 else np.sort(r.choice(M, 24, replace=False))
+    if M == 256:
+        rows = np.sort(r.choice(M, 64, replace=False))
+    cols = np.sort(r.choice(N, 64, replace=False))
+    _run_case("hadamard", M, K, N, hb, False, rows=rows, cols=cols, label=f"qwen-{shape}")
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 272, 100), (3, 144, 520), (17, 400, 33), (33, 2064, 200),
+                                   (100, 1040, 130), (65, 128, 16), (130, 4096, 48)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_linear_ragged(M, K, N, with_bias):
+    _run_case("decode", M, K, N, 0, with_bias, label="ragged")
+
+
+def test_linear_strided_3d_input_and_output_stride():
+    M, K, N = 24, 1024, 320
+    xb = synthetic.activations("normal", M, K, config="decode", seed=4)
+    x32 = synthetic.bf16_bits_to_f32(xb)
+    gx = Q.global_scale_from_amax(Q.amax_for_calibration(x32))
+    W, gw, wc, ws = weight_case("decode", N, K, 0)
+    alpha = alpha_of(gx, gw)
+    announce("linear strided/3-D")
+    wobj, _, _ = _gpu_weight(W, gw, 0, gx)
+    big = np.zeros((M, K + 64), np.uint16)
+    big[:, 32:32 + K] = xb
+    xd = bf16_bits_to_dev(big)[:, 32:32 + K]                      # non-contiguous rows
+    ybig = torch.zeros((M, N + 8), dtype=torch.bfloat16, device=DEV)
+    y = ybig[:, :N]
+    fql.linear_nvfp4(xd, wobj, alpha=float(alpha), out=y)
+    ref = Q.linear_nvfp4(*Q.quant_nvfp4(x32, gx), wc, ws, alpha)
+    assert rel_frob(dev_bf16_to_bits(y), ref) <= REL_FROB_TOL
+    assert torch.all(ybig[:, N:] == 0)                              # nothing past N written
+    x3 = bf16_bits_to_dev(xb).view(2, 12, K)
+    y3 = fql.linear_nvfp4(x3, wobj, alpha=float(alpha))
+    assert tuple(y3.shape) == (2, 12, N) and y3.dtype == torch.bfloat16
+    assert rel_frob(dev_bf16_to_bits(y3).reshape(M, N), ref) <= REL_FROB_TOL
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 6144, 4096), (128, 4096, 14336), (300, 256, 512)])
+def test_linear_deterministic(M, N, K):
+    xb = synthetic.activations("normal", M, K, config="decode", seed=11)
+    W, gw, _, _ = weight_case("decode", N, K, 0)
+    announce(f"determinism M={M} N={N} K={K}")
+    wobj, _, _ = _gpu_weight(W, gw, 0, 1.0)
+    xd = bf16_bits_to_dev(xb)
+    y1 = fql.linear_nvfp4(xd, wobj).clone()
+    y2 = fql.linear_nvfp4(xd, wobj).clone()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_linear_identity_weight_closed_form():
+    # identity weight: codes 2 (1.0) on the diagonal with E4M3 scale 1.0
+    K = 256
+    xb = synthetic.activations("normal", 8, K, config="tiny", seed=3)
+    x32 = synthetic.bf16_bits_to_f32(xb)
+    gx = Q.global_scale_from_amax(Q.amax_for_calibration(x32))
+    q = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(q, 2)
+    wc = Q.pack_nibbles(q)
+    ws = np.full((K, K // 16), 0x38, np.uint8)
+    bias_bits = synthetic.bias(K, config="tiny")
+    announce("identity weight")
+    packed = fql.pack_weight_nvfp4(torch.from_numpy(wc).to(DEV), torch.from_numpy(ws).to(DEV))
+    wobj = fql.NVFP4Weight(packed, K, K, float(gx), 1.0, 0)
+    xd = bf16_bits_to_dev(xb)
+    xc, xs = Q.quant_nvfp4(x32, gx)
+    xhat = Q.dequant_nvfp4(xc, xs)
+    # no bias: one exact product per output and a power-of-two alpha -> exact
+    y0 = fql.linear_nvfp4(xd, wobj, alpha=0.125)
+    expect0 = F.bf16_round_bits(0.125 * xhat)
+    assert np.array_equal(F.bf16_bits_to_f64(dev_bf16_to_bits(y0)), F.bf16_bits_to_f64(expect0))
+    # with bias: the float32 sum may round once before the bf16 cast -> 1 ulp
+    y = fql.linear_nvfp4(xd, wobj, alpha=0.125, bias=bf16_bits_to_dev(bias_bits))
+    expect = F.bf16_round_bits(0.125 * xhat + F.bf16_bits_to_f64(bias_bits)[None, :])
+    got = F.bf16_bits_to_f64(dev_bf16_to_bits(y))
+    ref = F.bf16_bits_to_f64(expect)
+    ulp = np.abs(ref) * 2.0 ** -7 + 1e-30
+    assert np.all(np.abs(got - ref) <= ulp)
+    assert np.mean(got == ref) > 0.999
