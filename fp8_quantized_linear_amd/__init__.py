@@ -36,6 +36,7 @@ __all__ = [
     "pack_weight_nvfp4",
     "unpack_weight_nvfp4",
     "linear_workspace_bytes",
+    "new_workspace",
     "linear_nvfp4",
     "NVFP4Weight",
     "HADAMARD_BLOCKS",
@@ -292,11 +293,17 @@ def linear_workspace_bytes(M, N, K):
 _workspaces = {}
 
 
+def new_workspace(nbytes, device):
+    """A zero-filled workspace buffer (its leading arrival counters must start at zero;
+    every linear call leaves them zero again). One workspace per stream at a time."""
+    return torch.zeros(max(int(nbytes), 1 << 20), dtype=torch.uint8, device=device)
+
+
 def _workspace(device, nbytes):
-    key = (device.type, device.index)
+    key = (device.type, device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        ws = new_workspace(nbytes, device)
         _workspaces[key] = ws
     return ws
 

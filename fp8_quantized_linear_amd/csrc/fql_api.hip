@@ -221,17 +221,12 @@ int fql_linear_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float inp
     return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
                 (long long)plan.total_bytes);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  _Float16* xhat = reinterpret_cast<_Float16*>(ws);
-  float* partial = reinterpret_cast<float*>(ws + plan.xhat_bytes);
-  hipError_t e = fql::launch_quant_nvfp4_xhat(static_cast<const uint16_t*>(x), M, K, ldx,
-                                              input_global_scale, hadamard_block,
-                                              aligned16(x, ldx, 2), plan.Mp, plan.Kp, xhat, st);
-  if (e != hipSuccess) return hip_status(e, "quant launch");
-  e = fql::launch_gemm_nvfp4(plan, xhat, static_cast<const uint8_t*>(w_packed), M, N, alpha,
-                             static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), ldy,
-                             partial, st);
-  return hip_status(e, "gemm launch");
+  hipError_t e = fql::launch_linear_nvfp4(
+      plan, static_cast<const uint16_t*>(x), M, K, ldx, input_global_scale, hadamard_block,
+      aligned16(x, ldx, 2), static_cast<const uint8_t*>(w_packed), N, alpha,
+      static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), ldy,
+      static_cast<uint8_t*>(workspace), st);
+  return hip_status(e, "linear launch");
 }
 
 }  // extern "C"

@@ -46,20 +46,31 @@ hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_
 hipError_t launch_unpack_nvfp4(const uint8_t* packed, int64_t N, int64_t K, uint8_t* codes,
                                uint8_t* scales, hipStream_t st);
 
-// GEMM launch plan for one (M, N, K): tile shape, split-K, workspace carve-up.
+// Launch plan of one linear call for (M, N, K).
+//   kind 0: M <= 32, one fused launch (quantize into LDS + GEMM + split-K
+//           reduction by the last workgroup to arrive).
+//   kind 1: quantizer kernel (x_hat in A-fragment order) + tiled GEMM.
+// Workspace layout: [arrival counters | x_hat | split-K partial slabs]. The
+// counters must be zero before the first call on a workspace; every call
+// leaves them zero again.
 struct GemmPlan {
-  int mt;            // 16-row M tiles per workgroup
-  int nt;            // 16-column N tiles per wave (4 waves per workgroup)
-  int64_t Mp;        // M padded to mt*16
-  int64_t Np, Kp;    // packed weight dims
-  int splits;        // K splits (1 = epilogue fused in the GEMM)
-  int kc_per_split;  // 128-wide K chunks per split
-  int64_t xhat_bytes, partial_bytes, total_bytes;
+  int kind;
+  int mt;             // 16-row M tiles per workgroup
+  int nt;             // 16-column N tiles per wave (4 waves per workgroup)
+  int64_t Mp;         // M padded to a whole number of M tiles
+  int64_t Np, Kp;     // packed weight dims
+  int64_t groups;     // output tiles (workgroups per split)
+  int64_t ngroups;    // column groups (kind 1)
+  int splits;         // K splits (1 = epilogue directly in the GEMM)
+  int kc_per_split;   // 128-deep K chunks per split
+  int kcmax;          // kind 0: chunk capacity of the kernel instantiation (4, 8, 16)
+  int64_t counter_bytes, xhat_bytes, partial_bytes, total_bytes;
 };
 GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K);
 
-hipError_t launch_gemm_nvfp4(const GemmPlan& p, const _Float16* xhat, const uint8_t* packed,
-                             int64_t M, int64_t N, float alpha, const uint16_t* bias, uint16_t* y,
-                             int64_t ldy, float* partial, hipStream_t st);
+hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K,
+                               int64_t ldx, float g, int hb, bool aligned, const uint8_t* packed,
+                               int64_t N, float alpha, const uint16_t* bias, uint16_t* y,
+                               int64_t ldy, uint8_t* workspace, hipStream_t st);
 
 }  // namespace fql

@@ -19,110 +19,13 @@
 // strides 16, 32, 64 pair a lane with lane ^ 1, ^ 2, ^ 4 through cross-lane
 // shuffles (a b-chunk is b/16 <= 8 adjacent lanes of one wave).
 //
-// No FMA contraction anywhere in this file: every float operation must be
-// the single IEEE operation the definition names.
-#pragma clang fp contract(off)
-
+// The block arithmetic (fql_quant.h) runs with FMA contraction off: every
+// float operation is the single IEEE operation the definition names.
 #include "fql_device.h"
 #include "fql_internal.h"
+#include "fql_quant.h"
 
 namespace fql {
-
-template <typename TIn>
-struct Loader;
-
-// bf16 rows: 16 elements = 32 bytes.
-template <>
-struct Loader<uint16_t> {
-  static __device__ __forceinline__ void load16(const uint16_t* p, bool aligned16, float v[16]) {
-    if (aligned16) {
-      const uint4v* q = reinterpret_cast<const uint4v*>(p);
-      uint4v a = q[0], b = q[1];
-      uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        v[2 * i] = __uint_as_float(w[i] << 16);
-        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = bf16_bits_to_f32(p[i]);
-    }
-  }
-};
-
-// float32 rows: 16 elements = 64 bytes.
-template <>
-struct Loader<float> {
-  static __device__ __forceinline__ void load16(const float* p, bool aligned16, float v[16]) {
-    if (aligned16) {
-      const float4v* q = reinterpret_cast<const float4v*>(p);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float4v t = q[i];
-        v[4 * i] = t.x;
-        v[4 * i + 1] = t.y;
-        v[4 * i + 2] = t.z;
-        v[4 * i + 3] = t.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = p[i];
-    }
-  }
-};
-
-// Rotate the thread's 16 values as part of its b-chunk: in-thread butterfly
-// strides 1, 2, 4, 8 (those below b), then cross-lane strides 16 .. b/2, then
-// the 1/sqrt(b) multiply. `blk` is the block index within the row; its low
-// bits give this thread's position inside the chunk.
-template <int HB>
-__device__ __forceinline__ void fwht_block(float v[16], int64_t blk) {
-#pragma unroll
-  for (int h = 1; h < 16 && h < HB; h <<= 1) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if ((e & h) == 0) {
-        float a = v[e], b = v[e + h];
-        v[e] = a + b;
-        v[e + h] = a - b;
-      }
-    }
-  }
-#pragma unroll
-  for (int hs = 1; hs < HB / 16; hs <<= 1) {
-    const bool upper = (blk & hs) != 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float other = __shfl_xor(v[e], hs);
-      // lower lane holds a, upper lane holds b: lower gets a + b, upper a - b
-      v[e] = upper ? (other - v[e]) : (v[e] + other);
-    }
-  }
-  // fl32(1/sqrt(b)): 0x3E800000, 0x3E3504F3, 0x3E000000, 0x3DB504F3
-  const float cb = HB == 16 ? 0x1p-2f : HB == 32 ? 0x1.6a09e6p-3f : HB == 64 ? 0x1p-3f : 0x1.6a09e6p-4f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) v[e] = v[e] * cb;
-}
-
-// Quantize one 16-block: codes (16 nibbles as two words) and the scale byte.
-__device__ __forceinline__ void quant_block(const float v[16], float g, uint32_t& lo, uint32_t& hi,
-                                            uint32_t& sbyte) {
-  float a = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 16; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(v[e]));
-  const float sf = (a / 6.0f) * g;
-  const uint32_t s = e4m3_encode_nonneg(sf);
-  const float sd = e4m3_decode_nonneg(s);
-  const float r = sd == 0.0f ? 0.0f : g / sd;
-  lo = 0u;
-  hi = 0u;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) lo |= e2m1_encode(v[e] * r) << (4 * e);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) hi |= e2m1_encode(v[8 + e] * r) << (4 * e);
-  sbyte = s;
-}
 
 // Canonical output: codes [rows][K/2], scales [rows][K/16].
 template <typename TIn, int HB>
@@ -173,17 +76,11 @@ __global__ __launch_bounds__(256) void quant_nvfp4_xhat_kernel(
   if constexpr (HB > 0) fwht_block<HB>(v, kb);
   uint32_t lo, hi, s;
   quant_block(v, g, lo, hi, s);
-  const float sd = e4m3_decode_nonneg(s);
+  const _Float16 sh = e4m3_to_f16(s);
+  const half2v s2 = {sh, sh};
   uint32_t hw[8];
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const uint32_t w = p < 4 ? lo : hi;
-    const uint32_t c0 = (w >> (8 * (p & 3))) & 15u, c1 = (w >> (8 * (p & 3) + 4)) & 15u;
-    _Float16 h0 = (_Float16)(e2m1_decode(c0) * sd);  // exact: <= 6 significant bits
-    _Float16 h1 = (_Float16)(e2m1_decode(c1) * sd);
-    hw[p] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
-            ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-  }
+  dequant8_f16(lo, s2, hw);
+  dequant8_f16(hi, s2, hw + 4);
   const int64_t k0 = kb * 16;
   const int64_t ks = k0 / 32;
   const int kq0 = (int)((k0 % 32) / 8);  // 0 or 2

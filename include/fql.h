@@ -135,8 +135,11 @@ int fql_unpack_weight_nvfp4(const void* packed, int64_t N, int64_t K, uint8_t* c
 
 /*
  * Workspace bytes fql_linear_nvfp4 needs for this shape (host-side). The
- * workspace holds the dequantized activation tile operand and, for split-K
- * launches, float32 partial sums.
+ * workspace holds arrival counters (its first 64 KiB), the dequantized
+ * activation operand (M > 32) and, for split-K launches, float32 partial
+ * sums. The counters must be zero before a workspace's first use (allocate it
+ * zero-filled); every call leaves them zero again. Calls that run at the same
+ * time (other streams) must not share a workspace.
  */
 int fql_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
 
