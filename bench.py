@@ -55,13 +55,11 @@ def _cases(workload, hb_override=None):
     return out
 
 
-def _kernel_of(M, hb):
-    """Name of the kernel that carries one linear call of M rows."""
-    if M <= 32:
-        return f"linear_small_kernel<{1 if M <= 16 else 2},1,{hb}>"
-    mt = 4 if M <= 64 else 8
-    nt = 1 if M <= 128 else 4
-    return f"gemm_tiled_kernel<{mt},{nt}> (+quant_nvfp4_xhat_kernel<{hb}>)"
+def _kernel_of(M, N, K):
+    """The kernel that carries one linear call of this shape (the library's own plan)."""
+    import fp8_quantized_linear_amd as fql
+
+    return fql.linear_plan(M, N, K).split(" grid=")[0]
 
 
 def gpu_bench(workload, steps, warmup, hb, per_case_reps=3):
@@ -100,7 +98,7 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3):
         ws = fql.new_workspace(fql.linear_workspace_bytes(M, N, K), dev)
         setups.append(dict(M=M, N=N, K=K, name=name, hb=hbk, x=x, objs=objs, bias=bias, y=y,
                            ws=ws, flops=2.0 * M * N * K, bytes=_alg_bytes(M, N, K, with_bias),
-                           kernel=_kernel_of(M, hbk)))
+                           kernel=_kernel_of(M, N, K)))
     torch.cuda.synchronize()
     n = len(setups)
 

@@ -36,6 +36,7 @@ __all__ = [
     "pack_weight_nvfp4",
     "unpack_weight_nvfp4",
     "linear_workspace_bytes",
+    "linear_plan",
     "new_workspace",
     "linear_nvfp4",
     "NVFP4Weight",
@@ -64,6 +65,7 @@ SIGNATURES = {
     "fql_pack_weight_nvfp4": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_sz, _c_vp]),
     "fql_unpack_weight_nvfp4": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
     "fql_linear_nvfp4_workspace_bytes": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+    "fql_linear_nvfp4_describe": (_c_int, [_c_i64, _c_i64, _c_i64, _c_int, ctypes.c_char_p, _c_sz]),
     "fql_linear_nvfp4": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_int, _c_vp, _c_i64,
                                   _c_f32, _c_vp, _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
 }
@@ -288,6 +290,13 @@ def linear_workspace_bytes(M, N, K):
     n = ctypes.c_size_t()
     _check(lib().fql_linear_nvfp4_workspace_bytes(int(M), int(N), int(K), ctypes.byref(n)))
     return n.value
+
+
+def linear_plan(M, N, K, aligned=True):
+    """One-line description of the kernel/launch plan a linear call of this shape uses."""
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().fql_linear_nvfp4_describe(int(M), int(N), int(K), int(bool(aligned)), buf, 256))
+    return buf.value.decode()
 
 
 _workspaces = {}

@@ -199,7 +199,17 @@ int fql_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* by
   if (!bytes) return fail(FQL_ERR_INVALID, "null pointer");
   if (M < 1 || N < 1 || K < 16 || K % 16 != 0)
     return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 16");
-  *bytes = (size_t)fql::plan_gemm_nvfp4(M, N, K).total_bytes;
+  const int64_t a = fql::plan_gemm_nvfp4(M, N, K, true).total_bytes;
+  const int64_t u = fql::plan_gemm_nvfp4(M, N, K, false).total_bytes;
+  *bytes = (size_t)(a > u ? a : u);
+  return ok();
+}
+
+int fql_linear_nvfp4_describe(int64_t M, int64_t N, int64_t K, int aligned, char* buf,
+                              size_t buf_len) {
+  if (M < 1 || N < 1 || K < 16 || K % 16 != 0)
+    return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 16");
+  write_reason(buf, buf_len, fql::describe_plan(fql::plan_gemm_nvfp4(M, N, K, aligned != 0)));
   return ok();
 }
 
@@ -216,14 +226,15 @@ int fql_linear_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float inp
   if (reinterpret_cast<uintptr_t>(w_packed) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(FQL_ERR_INVALID, "packed weight must be 16-byte and workspace 256-byte aligned");
-  const fql::GemmPlan plan = fql::plan_gemm_nvfp4(M, N, K);
+  const bool xal = aligned16(x, ldx, 2);
+  const fql::GemmPlan plan = fql::plan_gemm_nvfp4(M, N, K, xal);
   if (workspace_bytes < (size_t)plan.total_bytes)
     return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
                 (long long)plan.total_bytes);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = fql::launch_linear_nvfp4(
       plan, static_cast<const uint16_t*>(x), M, K, ldx, input_global_scale, hadamard_block,
-      aligned16(x, ldx, 2), static_cast<const uint8_t*>(w_packed), N, alpha,
+      xal, static_cast<const uint8_t*>(w_packed), N, alpha,
       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), ldy,
       static_cast<uint8_t*>(workspace), st);
   return hip_status(e, "linear launch");

@@ -4,22 +4,30 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace fql {
 
 // ---- packed NVFP4 weight layout -------------------------------------------
 // N is padded to a multiple of 16 (one MFMA tile of output columns) and K to
-// a multiple of 128 (four 32-deep MFMA steps). The blob holds the code region
-// followed by the scale region:
-//   codes  [Np/16][Kp/128][lane 64][16 bytes]   lane = kq*16 + n  (n < 16, kq < 4)
+// a multiple of 128 (four 32-deep MFMA steps, "a chunk"). The blob holds the
+// code region followed by the scale region:
+//   codes  [Np/16][KC][lane 64][16 bytes]        KC = Kp/128, lane = kq*16 + n
 //          dword j of a lane = the eight codes of row n at k = 128c + 32j + 8kq + 0..7,
 //          element i in nibble i (canonical nibble order).
-//   scales [Np/16][Kp/128][n 16][8 bytes]        byte h*4 + j = scale of block 8c + 2j + h
-// One 16-byte load per lane gives the B operand codes of four MFMA steps, and
-// one 4-byte load the matching four scales.
+//   scales [Np/16][KC4][slot 32][16 bytes]       KC4 = ceil(KC/4), slot = n*2 + h
+//          byte 4q + j = scale of row n, block 8c + 2j + h, for chunk c = 4*group + q
+//          (zero for chunks past KC).
+// One 16-byte load per lane gives the B-operand codes of four MFMA steps of
+// one chunk, and one 16-byte load per lane the scales of four chunks
+// (lane = kq*16 + n reads slot n*2 + kq/2), so a wave issues a few large
+// requests instead of many small ones.
 struct PackedDims {
   int64_t Np, Kp;
+  int64_t kc() const { return Kp / 128; }
+  int64_t kc4() const { return (Kp / 128 + 3) / 4; }
   int64_t code_bytes() const { return Np * Kp / 2; }
-  int64_t scale_bytes() const { return Np * Kp / 16; }
+  int64_t scale_bytes() const { return (Np / 16) * kc4() * 512; }
   int64_t total_bytes() const { return code_bytes() + scale_bytes(); }
 };
 
@@ -47,8 +55,9 @@ hipError_t launch_unpack_nvfp4(const uint8_t* packed, int64_t N, int64_t K, uint
                                uint8_t* scales, hipStream_t st);
 
 // Launch plan of one linear call for (M, N, K).
-//   kind 0: M <= 32, one fused launch (quantize into LDS + GEMM + split-K
-//           reduction by the last workgroup to arrive).
+//   kind 0: small M (M <= 16 and M*Kp*2 <= 64 KiB): one launch; each
+//           workgroup quantizes the activation into LDS and computes one
+//           16-column tile over the full K, its waves splitting K.
 //   kind 1: quantizer kernel (x_hat in A-fragment order) + tiled GEMM.
 // Workspace layout: [arrival counters | x_hat | split-K partial slabs]. The
 // counters must be zero before the first call on a workspace; every call
@@ -63,10 +72,20 @@ struct GemmPlan {
   int64_t ngroups;    // column groups (kind 1)
   int splits;         // K splits (1 = epilogue directly in the GEMM)
   int kc_per_split;   // 128-deep K chunks per split
-  int kcmax;          // kind 0: chunk capacity of the kernel instantiation (4, 8, 16)
+  int kcmax;          // kind 0: weight register ring depth in chunks (4 or 8)
+  int waves;          // kind 0: waves per workgroup (split of K inside the workgroup)
+  int qpre;           // kind 0: activation blocks per thread loaded ahead of the weights
+  int ntw;            // kind 0: 16-column tiles per workgroup
+  int64_t lds_bytes;  // kind 0: dynamic LDS (compact activation copy / reduction)
   int64_t counter_bytes, xhat_bytes, partial_bytes, total_bytes;
 };
-GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K);
+// `aligned`: x rows are 16-byte aligned (pointer and row stride); the
+// fused small-M kernel needs it. Workspace sizes of both kinds are covered by
+// the aligned=false plan, which never needs less.
+GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned);
+
+// Kernel name and parameters of a plan (diagnostics).
+std::string describe_plan(const GemmPlan& p);
 
 hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K,
                                int64_t ldx, float g, int hb, bool aligned, const uint8_t* packed,

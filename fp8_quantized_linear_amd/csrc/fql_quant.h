@@ -128,6 +128,14 @@ __device__ __forceinline__ void quant_block(const float v[16], float g, uint32_t
 // E4M3 byte -> float16 value (exact: E4M3 values are float16 values).
 __device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t c) { return (_Float16)e4m3_decode_nonneg(c); }
 
+// Four E4M3 bytes -> four float16 values with two v_cvt_scalef32_pk_f16_fp8
+// (scale 1.0; checked exact against the E4M3 definition for all 256 bytes):
+// lo = (byte0, byte1), hi = (byte2, byte3).
+__device__ __forceinline__ void e4m3x4_to_f16(uint32_t w, half2v& lo, half2v& hi) {
+  lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
+}
+
 // Eight E2M1 codes (element i in nibble i) times a float16 scale -> eight
 // float16 values in four words (element 2p in the low half of word p).
 // Each product has at most 6 significant bits, so it is exact.

@@ -36,6 +36,9 @@
 //    reduction.
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
 
 #include "fql_device.h"
 #include "fql_internal.h"
@@ -47,14 +50,23 @@ namespace fql {
 // shared pieces
 // ---------------------------------------------------------------------------
 
-// B fragments for one 32-deep K step of one 16-column tile.
-__device__ __forceinline__ half8 b_fragment(uint32_t codes, uint32_t scale_byte) {
-  const _Float16 sh = e4m3_to_f16(scale_byte);
+// B fragment for one 32-deep K step of one 16-column tile: eight codes times
+// their block scale (already float16).
+__device__ __forceinline__ half8 b_fragment(uint32_t codes, _Float16 sh) {
   const half2v s2 = {sh, sh};
   uint32_t hw[4];
   dequant8_f16(codes, s2, hw);
   return __builtin_bit_cast(half8, uint4v{hw[0], hw[1], hw[2], hw[3]});
 }
+
+// The four K steps' scales of one chunk (one dword, byte j = step j) as float16.
+struct ChunkScales {
+  half2v lo, hi;
+  __device__ __forceinline__ explicit ChunkScales(uint32_t w) { e4m3x4_to_f16(w, lo, hi); }
+  __device__ __forceinline__ _Float16 operator[](int ks) const {
+    return ks == 0 ? lo[0] : ks == 1 ? lo[1] : ks == 2 ? hi[0] : hi[1];
+  }
+};
 
 __device__ __forceinline__ uint32_t dword_of(const uint4v& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -151,122 +163,199 @@ __device__ __forceinline__ void finish_tile(float4v (&acc)[MT][NT], int M, int N
 }
 
 // ---------------------------------------------------------------------------
-// small-M fused kernel
+// full-K matrix-vector kernel (small M): no cross-workgroup reduction
 // ---------------------------------------------------------------------------
-
-template <int MT, int NT, int HB, int KCMAX>
-__global__ __launch_bounds__(256) void linear_small_kernel(
-    const uint16_t* __restrict__ x, int M, int K, int64_t ldx, float g, int aligned16,
+//
+// One workgroup owns NTW 16-column tiles and the whole K range; its W waves
+// split K into W contiguous parts and their partial sums are added in wave
+// order through LDS at the end (deterministic, no global atomics: a
+// device-scope arrival counter costs about a microsecond per round trip and
+// serialises under contention, which is the whole budget of a decode call).
+// The activation's M rows are quantized once per workgroup straight into a
+// compact LDS copy x_hat[M][Kp] (float16, 16-byte groups XOR-swizzled by
+// row so the 16 fragment rows of a read hit distinct banks); fragment lanes
+// for rows >= M read nothing and supply zeros. Weight loads are issued in
+// rounds of RC chunks per tile before the round's MFMAs.
+// (x is deliberately not __restrict__: the compiler barriers below must pin
+//  its loads ahead of the weight loads, which they cannot do for memory the
+//  compiler knows no asm statement can touch.)
+template <int W, int NTW, int HB, int RC, int QPRE>
+__global__ __launch_bounds__(64 * W) void linear_gemv_kernel(
+    const uint16_t* x, int M, int K, int64_t ldx, float g, int aligned16,
     const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales, int N, int64_t Kp,
-    int ntiles, int kc_per_split, int splits, float alpha, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ y, int64_t ldy, float* __restrict__ partial,
-    uint32_t* __restrict__ counters) {
-  // KCMAX: chunks per split this instantiation holds (A in LDS = MT*KCMAX*4 KB,
-  // weight registers = 5*KCMAX per tile); the plan picks the smallest that fits
-  constexpr int WGC = 64 * NT;
-  __shared__ uint4v a_lds[MT][KCMAX * 4][64];
-  __shared__ uint32_t s_flag;
-
+    int ntiles, float alpha, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
+    int64_t ldy) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint4v* xs = reinterpret_cast<uint4v*>(smem);  // [M][Kp/8] 16-byte groups, swizzled
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t KC = Kp / 128;
-  const int group = blockIdx.x / splits;
-  const int split = blockIdx.x - group * splits;
-  const int64_t c0 = (int64_t)split * kc_per_split;
-  const int nck = (int)(KC - c0 < kc_per_split ? KC - c0 : kc_per_split);
-  const int tile0 = (group * 4 + wave) * NT;
+  const int64_t G8 = Kp / 8;  // 16-byte groups per row
+  const int tile0 = blockIdx.x * NTW;
+  const int64_t KC4 = (KC + 3) / 4;
+  // per-wave K part in whole 4-chunk scale groups
+  const int64_t cpw = ((KC + W - 1) / W + 3) / 4 * 4;
+  const int64_t cw0 = wave * cpw < KC ? wave * cpw : KC;
+  const int64_t cw1 = cw0 + cpw < KC ? cw0 + cpw : KC;
 
-  // 1. all weight loads of this workgroup's K range, issued first
-  uint4v bq[NT][KCMAX];
-  uint32_t bs[NT][KCMAX];
+  // weight pointers of this workgroup's tiles (invalid tiles read tile 0)
+  const uint4v* qp[NTW];
+  const uint4v* sp[NTW];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const bool tv = (tile0 + nt) < ntiles;
-    const int64_t t = tv ? tile0 + nt : 0;
-    const uint4v* qp = reinterpret_cast<const uint4v*>(wcodes) + (t * KC + c0) * 64 + lane;
-    const uint32_t* sp = reinterpret_cast<const uint32_t*>(wscales) + (t * KC + c0) * 32 +
-                         (lane & 15) * 2 + (lane >> 5);
-    // unconditional loads (chunks past the range re-read the last one, a cache
-    // hit) keep the outstanding-load count static, so each chunk's compute
-    // waits only for its own data
-#pragma unroll
-    for (int c = 0; c < KCMAX; ++c) {
-      const int cc = c < nck ? c : nck - 1;
-      bq[nt][c] = qp[cc * 64];
-      bs[nt][c] = sp[cc * 32];
-    }
+  for (int j = 0; j < NTW; ++j) {
+    const int64_t t = (tile0 + j) < ntiles ? tile0 + j : 0;
+    qp[j] = reinterpret_cast<const uint4v*>(wcodes) + (t * KC) * 64 + lane;
+    sp[j] = reinterpret_cast<const uint4v*>(wscales) + (t * KC4) * 32 + (lane & 15) * 2 + (lane >> 5);
   }
-
-  // 2. quantize x[0:M, c0*128 : (c0+nck)*128] into LDS A fragments
-  //    slot (mt, ks, lane') holds x_hat[mt*16 + lane'%16][k = 32 ks + 8 (lane'/16) + 0..7]
-  {
-    // zero the fragment rows >= M
-    const int nslots = MT * nck * 4 * 64;
-    for (int s = tid; s < nslots; s += 256) {
-      const int l2 = s & 63, ks = (s >> 6) % (nck * 4), mt = (s >> 6) / (nck * 4);
-      if (mt * 16 + (l2 & 15) >= M) a_lds[mt][ks][l2] = uint4v{0u, 0u, 0u, 0u};
-    }
-    const int nblk = nck * 8;  // 16-blocks per row in range
-    const int total = M * nblk;
-    const uint16_t* xk = x + c0 * 128;
-    for (int b0 = 0; b0 < total; b0 += 256) {
-      const int b = b0 + tid;
-      const bool act = b < total;
-      const int m = act ? b / nblk : 0;
-      const int kb = act ? b - m * nblk : 0;
-      float v[16];
-      if (act && (c0 * 128 + kb * 16) < K) {
-        Loader<uint16_t>::load16(xk + (int64_t)m * ldx + kb * 16, aligned16 != 0, v);
-      } else {
+  // register ring of RC chunks per tile (RC a multiple of 4): slot i holds
+  // chunk cr + i of the current round; sg holds the matching scale groups
+  uint4v bq[NTW][RC];
+  uint4v sg[NTW][RC / 4];
+  const int64_t c_last = cw1 > cw0 ? cw1 - 1 : 0;  // clamp target: a valid chunk of this tile
+  // codes of chunk c into slot i; the scale group of slots 4q..4q+3 is
+  // (re)loaded with the first slot of the group at start-up and after the
+  // group's last slot has been consumed in the loop
+  auto load_codes = [&](int i, int64_t c) {
+    c = c < c_last ? c : c_last;  // unconditional, clamped: static outstanding-load count
 #pragma unroll
-        for (int e = 0; e < 16; ++e) v[e] = 0.0f;
-      }
-      if constexpr (HB > 0) fwht_block<HB>(v, kb);
-      if (act) {
-        uint32_t lo, hi, s;
-        quant_block(v, g, lo, hi, s);
-        const _Float16 sh = e4m3_to_f16(s);
-        const half2v s2 = {sh, sh};
-        uint32_t hw[8];
-        dequant8_f16(lo, s2, hw);
-        dequant8_f16(hi, s2, hw + 4);
-        const int ks = kb >> 1, kq0 = (kb & 1) * 2, ml = m & 15, mt = m >> 4;
-        a_lds[mt][ks][kq0 * 16 + ml] = uint4v{hw[0], hw[1], hw[2], hw[3]};
-        a_lds[mt][ks][(kq0 + 1) * 16 + ml] = uint4v{hw[4], hw[5], hw[6], hw[7]};
-      }
+    for (int j = 0; j < NTW; ++j) bq[j][i] = qp[j][c * 64];
+  };
+  auto load_group = [&](int q, int64_t c_first) {
+    const int64_t c = c_first < c_last ? c_first : c_last;
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) sg[j][q] = sp[j][(c / 4) * 32];
+  };
+  auto load_slot = [&](int i, int64_t c) {
+    load_codes(i, c);
+    if ((i & 3) == 0) load_group(i / 4, c);
+  };
+  // Activation loads go out first: the load counter retires in order, so
+  // waiting for x must not have to wait for the (slower) weight stream too.
+  // QPRE blocks per thread are prefetched (the plan sizes it to cover all
+  // rows when it can); the weight ring follows.
+  const int64_t nblk = Kp / 16;
+  const int64_t qtotal = (int64_t)M * nblk;
+  uint4v xq[QPRE][2];
+  bool xact[QPRE];
+  int64_t xm[QPRE], xkb[QPRE];
+#pragma unroll
+  for (int q = 0; q < QPRE; ++q) {
+    // branch-free: inactive lanes read block 0 of row 0 (in bounds) and zero it
+    const int64_t b = (int64_t)q * 64 * W + tid;
+    xact[q] = b < qtotal;
+    xm[q] = xact[q] ? b / nblk : 0;
+    xkb[q] = xact[q] ? b - xm[q] * nblk : 0;
+    const bool real = xact[q] && xkb[q] * 16 < K;
+    const uint4v* px = reinterpret_cast<const uint4v*>(x + (real ? xm[q] * ldx + xkb[q] * 16 : 0));
+    const uint4v z = uint4v{0u, 0u, 0u, 0u};
+    const uint4v l0 = px[0], l1 = px[1];
+    xq[q][0] = real ? l0 : z;
+    xq[q][1] = real ? l1 : z;
+  }
+  __asm__ volatile("" ::: "memory");  // keep every x load ahead of the weight loads
+#pragma unroll
+  for (int i = 0; i < RC; ++i) load_slot(i, cw0 + i);
+  __asm__ volatile("" ::: "memory");
+
+  // quantize x rows [0, M) over the full K into the compact LDS copy
+  auto quant_store = [&](const float (&v)[16], int64_t m, int64_t kb) {
+    uint32_t lo, hi, sc;
+    quant_block(v, g, lo, hi, sc);
+    const _Float16 sh = e4m3_to_f16(sc);
+    const half2v s2 = {sh, sh};
+    uint32_t hw[8];
+    dequant8_f16(lo, s2, hw);
+    dequant8_f16(hi, s2, hw + 4);
+    const int64_t gi = kb * 2;  // first 16-byte group of the block
+    const int sw = (int)(m & 15);
+    xs[m * G8 + ((gi & ~15) | ((gi & 15) ^ sw))] = uint4v{hw[0], hw[1], hw[2], hw[3]};
+    xs[m * G8 + (((gi + 1) & ~15) | (((gi + 1) & 15) ^ sw))] = uint4v{hw[4], hw[5], hw[6], hw[7]};
+  };
+#pragma unroll
+  for (int q = 0; q < QPRE; ++q) {  // static trip count: the loads cannot be sunk
+    float v[16];
+    const uint32_t w[8] = {xq[q][0].x, xq[q][0].y, xq[q][0].z, xq[q][0].w,
+                           xq[q][1].x, xq[q][1].y, xq[q][1].z, xq[q][1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
     }
+    if constexpr (HB > 0) fwht_block<HB>(v, xkb[q]);
+    if (xact[q]) quant_store(v, xm[q], xkb[q]);
+  }
+  for (int64_t b0 = (int64_t)QPRE * 64 * W; b0 < qtotal; b0 += 64 * W) {  // rows beyond the prefetch
+    const int64_t b = b0 + tid;
+    const bool act = b < qtotal;
+    const int64_t m = act ? b / nblk : 0;
+    const int64_t kb = act ? b - m * nblk : 0;
+    float v[16];
+    if (act && kb * 16 < K) {
+      Loader<uint16_t>::load16(x + m * ldx + kb * 16, aligned16 != 0, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = 0.0f;
+    }
+    if constexpr (HB > 0) fwht_block<HB>(v, kb);
+    if (act) quant_store(v, m, kb);
   }
   __syncthreads();
 
-  // 3. MFMA over the K range
-  float4v acc[MT][NT];
+  // MFMA over this wave's K part
+  const int r = lane & 15, kq = lane >> 4;
+  const bool row_real = r < M;
+  float4v acc[NTW];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int j = 0; j < NTW; ++j) acc[j] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (int64_t cr = cw0; cr < cw1; cr += RC) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < RC; ++i) {
+      const int64_t c = cr + i;
+      if (c < cw1) {
 #pragma unroll
-  for (int c = 0; c < KCMAX; ++c) {
-    if (c < nck) {
+        for (int ks = 0; ks < 4; ++ks) {
+          const int64_t gi = c * 16 + ks * 4 + kq;  // 16-byte group of this lane's 8 k values
+          uint4v av = uint4v{0u, 0u, 0u, 0u};
+          if (row_real) av = xs[r * G8 + ((gi & ~15) | ((gi & 15) ^ r))];
+          const half8 a = __builtin_bit_cast(half8, av);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        half8 bf[NT];
+          for (int j = 0; j < NTW; ++j) {
+            const ChunkScales cs(dword_of(sg[j][i / 4], i & 3));
+            const half8 bf = b_fragment(dword_of(bq[j][i], ks), cs[ks]);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf, acc[j], 0, 0, 0);
+          }
+        }
+      }
+      load_codes(i, c + RC);  // refill this slot with the chunk RC ahead
+      if ((i & 3) == 3) load_group(i / 4, c - 3 + RC);  // group fully consumed
+    }
+  }
+
+  // reduce the W partial tiles in wave order through LDS (reusing x_hat space)
+  __syncthreads();
+  float4v* red = reinterpret_cast<float4v*>(smem);  // [W][NTW][64]
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          bf[nt] = b_fragment(dword_of(bq[nt][c], ks), (bs[nt][c] >> (8 * ks)) & 0xFFu);
+  for (int j = 0; j < NTW; ++j) red[(wave * NTW + j) * 64 + lane] = acc[j];
+  __syncthreads();
+  if (wave == 0) {
+    const int col = lane & 15, row0 = 4 * (lane >> 4);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const half8 a = __builtin_bit_cast(half8, a_lds[mt][c * 4 + ks][lane]);
+    for (int j = 0; j < NTW; ++j) {
+      float4v s4 = red[j * 64 + lane];
+      for (int w = 1; w < W; ++w) {
+        const float4v t = red[(w * NTW + j) * 64 + lane];
+        s4 = s4 + t;
+      }
+      const int n = (tile0 + j) * 16 + col;
+      if (n < N) {
+        const float bv = bias ? bf16_bits_to_f32(bias[n]) : 0.0f;
 #pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[nt], acc[mt][nt], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          const int m = row0 + i;
+          if (m < M) y[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16_bits(alpha * s4[i] + bv);
         }
       }
     }
   }
-
-  // 4. output (direct, or split-K partials + last-arriver reduction)
-  float* slab = partial + (int64_t)group * splits * (MT * 16) * WGC;
-  finish_tile<MT, NT>(acc, M, N, 0, group * WGC, split, splits, alpha, bias, y, ldy, slab,
-                      counters + group, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -304,15 +393,18 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
   auto a_src = [&](int mt, int64_t c) -> const uint4v* {
     return xsrc + ((((int64_t)mgroup * MT + mt) * KS + c * 4 + (tid >> 6)) * 64 + (tid & 63));
   };
+  const int64_t KC4 = (KC + 3) / 4;
   const uint4v* bq_base[NT];
   const uint32_t* bs_base[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int64_t t = tvalid[nt] ? tile0 + nt : 0;
     bq_base[nt] = reinterpret_cast<const uint4v*>(wcodes) + (t * KC) * 64 + lane;
-    bs_base[nt] = reinterpret_cast<const uint32_t*>(wscales) + (t * KC) * 32 + (lane & 15) * 2 +
-                  (lane >> 5);
+    bs_base[nt] = reinterpret_cast<const uint32_t*>(wscales) +
+                  ((t * KC4) * 32 + (lane & 15) * 2 + (lane >> 5)) * 4;
   }
+  // scale dword of chunk c in the 4-chunk group layout
+  auto bs_at = [&](int nt, int64_t c) -> uint32_t { return bs_base[nt][(c >> 2) * 128 + (c & 3)]; };
 
   float4v acc[MT][NT];
 #pragma unroll
@@ -338,9 +430,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {  // invalid tiles read tile 0 (in bounds, never stored)
     bq0[nt] = bq_base[nt][c_begin * 64];
-    bs0[nt] = bs_base[nt][c_begin * 32];
+    bs0[nt] = bs_at(nt, c_begin);
     bq1[nt] = bq_base[nt][clampc(c_begin + 1) * 64];
-    bs1[nt] = bs_base[nt][clampc(c_begin + 1) * 32];
+    bs1[nt] = bs_at(nt, clampc(c_begin + 1));
   }
   __syncthreads();
 
@@ -349,7 +441,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
     for (int ks = 0; ks < 4; ++ks) {
       half8 bf[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) bf[nt] = b_fragment(dword_of(bq[nt], ks), (bs[nt] >> (8 * ks)) & 0xFFu);
+      for (int nt = 0; nt < NT; ++nt) bf[nt] = b_fragment(dword_of(bq[nt], ks), ChunkScales(bs[nt])[ks]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const half8 a = __builtin_bit_cast(half8, a_lds[buf][mt * 4 + ks][lane]);
@@ -369,7 +461,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       bq[nt] = bq_base[nt][c2 * 64];
-      bs[nt] = bs_base[nt][c2 * 32];
+      bs[nt] = bs_at(nt, c2);
     }
     __syncthreads();
   };
@@ -399,69 +491,92 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 // ---------------------------------------------------------------------------
 
 static constexpr int kCUs = 256;
-static constexpr int64_t kCounterBytes = 64 * 1024;  // arrival counters at the workspace start
 
-// Pick a split count in [s_lo, s_hi]: the estimated cost is the bytes moved
-// (weight, plus split-K partials written and read back, which mostly stay in
-// the last-level cache and are weighted by one half) divided by how evenly
-// and how fully the workgroups occupy the CUs.
-static int pick_splits(int64_t groups, int64_t s_lo, int64_t s_hi, int64_t min_wgs,
-                       double w_bytes, double partial_bytes_per_split) {
-  if (s_lo < 1) s_lo = 1;
-  if (s_hi < s_lo) s_hi = s_lo;
-  int best = (int)s_lo;
-  double best_cost = 1e300;
-  for (int64_t s = s_lo; s <= s_hi; ++s) {
-    const int64_t wgs = groups * s;
-    const double waves = (double)wgs / kCUs;
-    const double balance = waves / std::ceil(waves);
-    const double fill = wgs >= min_wgs ? 1.0 : (double)wgs / (double)min_wgs;
-    const double traffic = w_bytes + (s > 1 ? (double)s * partial_bytes_per_split : 0.0);
-    const double cost = traffic / (balance * fill);
-    if (cost < best_cost * (1.0 - 1e-6)) {
-      best_cost = cost;
-      best = (int)s;
+// Benchmarking aid: FQL_PLAN="kind=0,waves=8,ntw=2,rc=4" or "kind=1,mt=4,nt=1,splits=2"
+// overrides the launch-plan heuristics (no effect on results, only on speed).
+struct GemmOverride {
+  int kind = -1, waves = 0, ntw = 0, rc = 0, mt = 0, nt = 0, splits = 0;
+};
+static GemmOverride gemm_override() {
+  GemmOverride o;
+  const char* e = std::getenv("FQL_PLAN");
+  if (!e) return o;
+  std::string s(e);
+  size_t pos = 0;
+  while (pos < s.size()) {
+    size_t end = s.find(',', pos);
+    if (end == std::string::npos) end = s.size();
+    const std::string kv = s.substr(pos, end - pos);
+    const size_t eq = kv.find('=');
+    if (eq != std::string::npos) {
+      const std::string k = kv.substr(0, eq);
+      const int v = std::atoi(kv.c_str() + eq + 1);
+      if (k == "kind") o.kind = v;
+      else if (k == "waves" && (v == 4 || v == 8)) o.waves = v;
+      else if (k == "ntw" && (v == 1 || v == 2 || v == 4)) o.ntw = v;
+      else if (k == "rc" && (v == 4 || v == 8)) o.rc = v;
+      else if (k == "mt" && (v == 1 || v == 2 || v == 4 || v == 8)) o.mt = v;
+      else if (k == "nt" && (v == 1 || v == 4)) o.nt = v;
+      else if (k == "splits" && v >= 1 && v <= 64) o.splits = v;
     }
+    pos = end + 1;
   }
-  return best;
+  return o;
 }
+static constexpr int64_t kCounterBytes = 64 * 1024;  // arrival counters at the workspace start
+static constexpr int64_t kGemvMaxLds = 64 * 1024;    // compact activation copy in LDS
+static constexpr int64_t kGemvMaxRedundantBlocks = 1 << 20;  // workgroups x 16-blocks quantized
 
-GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K) {
+GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
   GemmPlan p{};
   const PackedDims d = packed_dims(N, K);
   p.Np = d.Np;
   p.Kp = d.Kp;
   const int64_t KC = p.Kp / 128;
   const int64_t ntiles = p.Np / 16;
-  if (M <= 32) {
+  const GemmOverride ov = gemm_override();
+  // The fused kernel re-quantizes the activation in every workgroup; keep it
+  // while that redundant work stays small (measured: gate_up at M = 8 is
+  // faster through the quantizer kernel + tiled GEMM).
+  const int64_t quant_blocks = (int64_t)M * (p.Kp / 16);
+  const bool gemv_ok = aligned && M <= 16 && M * p.Kp * 2 <= kGemvMaxLds &&
+                       (ov.kind == 0 || ntiles * quant_blocks <= kGemvMaxRedundantBlocks);
+  if (gemv_ok && ov.kind != 1) {
+    // one workgroup per NTW 16-column tiles over the full K (no cross-workgroup reduction)
     p.kind = 0;
-    p.mt = M <= 16 ? 1 : 2;
+    p.mt = 1;
     p.nt = 1;
-    p.Mp = 16 * p.mt;
-    const int64_t kcmax = 16 / p.mt;  // LDS cap: MT * 16 chunks * 4 KB / MT = 64 KB
-    const int64_t groups = (ntiles + 4 * p.nt - 1) / (4 * p.nt);
-    const int64_t s_lo = (KC + kcmax - 1) / kcmax;
-    const double wb = 0.5625 * (double)p.Np * (double)p.Kp;
-    const double pb = 4.0 * (double)M * (double)p.Np;
-    int64_t s = pick_splits(groups, s_lo, std::max<int64_t>(s_lo, std::min<int64_t>(KC, 4 * s_lo + 8)),
-                            3 * kCUs, wb, pb);
-    p.kc_per_split = (int)((KC + s - 1) / s);
-    p.splits = (int)((KC + p.kc_per_split - 1) / p.kc_per_split);
-    p.kcmax = p.kc_per_split <= 4 ? 4 : p.kc_per_split <= 8 ? 8 : 16;
-    p.groups = groups;
+    p.Mp = M;
+    p.waves = ntiles < 1024 ? 8 : 4;
+    p.ntw = 1;
+    if (ov.waves) p.waves = ov.waves;
+    if (ov.ntw) p.ntw = ov.ntw;
+    const int64_t cpw = (KC + p.waves - 1) / p.waves;
+    p.kcmax = cpw <= 4 ? 4 : 8;  // register ring depth (chunks)
+    if (ov.rc) p.kcmax = ov.rc;
+    const int64_t qblk = (M * p.Kp / 16 + 64 * p.waves - 1) / (64 * p.waves);  // blocks per thread
+    p.qpre = qblk <= 1 ? 1 : qblk <= 2 ? 2 : 4;
+    p.groups = (ntiles + p.ntw - 1) / p.ntw;
+    p.splits = 1;
+    p.kc_per_split = (int)KC;
     p.xhat_bytes = 0;
+    p.lds_bytes = std::max<int64_t>(M * p.Kp * 2, (int64_t)p.waves * p.ntw * 1024);
   } else {
     p.kind = 1;
-    p.mt = M <= 64 ? 4 : 8;
+    p.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
     p.nt = M <= 128 ? 1 : 4;
+    if (ov.mt && ov.mt * 16 >= std::min<int64_t>(M, 128)) p.mt = ov.mt;
+    if (ov.nt) p.nt = ov.nt;
     p.Mp = round_up(M, 16 * p.mt);
     const int64_t ngroups = (ntiles + 4 * p.nt - 1) / (4 * p.nt);
     const int64_t mgroups = p.Mp / (16 * p.mt);
     const int64_t groups = ngroups * mgroups;
+    // Split K across workgroups only when there are too few output tiles to
+    // occupy the GPU: the arrival counter of the split-K reduction costs
+    // about a microsecond plus ~0.35 us per split contending on it.
     int64_t s = 1;
-    const double wb = 0.5625 * (double)p.Np * (double)p.Kp * (double)mgroups;
-    const double pb = 4.0 * (double)M * (double)p.Np;
-    if (groups < 2 * kCUs) s = pick_splits(groups, 1, std::min<int64_t>(KC, 16), 3 * kCUs, wb, pb);
+    if (groups < 192) s = std::min<int64_t>(std::min<int64_t>(4, KC), (256 + groups - 1) / groups);
+    if (ov.splits) s = std::min<int64_t>(ov.splits, KC);
     p.kc_per_split = (int)((KC + s - 1) / s);
     p.splits = (int)((KC + p.kc_per_split - 1) / p.kc_per_split);
     p.groups = groups;
@@ -475,46 +590,60 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
-template <int MT, int NT, int HB, int KCMAX>
-static void launch_small_t(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                           float g, bool aligned, const uint8_t* packed, int64_t N, float alpha,
-                           const uint16_t* bias, uint16_t* y, int64_t ldy, float* partial,
-                           uint32_t* counters, hipStream_t st) {
+std::string describe_plan(const GemmPlan& p) {
+  char b[256];
+  if (p.kind == 0) {
+    std::snprintf(b, sizeof(b), "linear_gemv_kernel<W=%d,NTW=%d,RC=%d,QPRE=%d> grid=%lld lds=%lld",
+                  p.waves, p.ntw, p.kcmax, p.qpre, (long long)p.groups, (long long)p.lds_bytes);
+  } else {
+    std::snprintf(b, sizeof(b),
+                  "quant_nvfp4_xhat_kernel + gemm_tiled_kernel<MT=%d,NT=%d> grid=%lld splits=%d",
+                  p.mt, p.nt, (long long)(p.groups * p.splits), p.splits);
+  }
+  return std::string(b);
+}
+
+template <int W, int NTW, int HB, int RC, int QPRE>
+static void launch_gemv_t(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                          float g, bool aligned, const uint8_t* packed, int64_t N, float alpha,
+                          const uint16_t* bias, uint16_t* y, int64_t ldy, hipStream_t st) {
   const uint8_t* wcodes = packed;
   const uint8_t* wscales = packed + p.Np * p.Kp / 2;
-  linear_small_kernel<MT, NT, HB, KCMAX><<<(unsigned)(p.groups * p.splits), 256, 0, st>>>(
-      x, (int)M, (int)K, ldx, g, aligned ? 1 : 0, wcodes, wscales, (int)N, p.Kp, (int)(p.Np / 16),
-      p.kc_per_split, p.splits, alpha, bias, y, ldy, partial, counters);
+  linear_gemv_kernel<W, NTW, HB, RC, QPRE><<<(unsigned)p.groups, 64 * W, (size_t)p.lds_bytes, st>>>(
+      x, (int)M, (int)K, ldx, g, aligned ? 1 : 0, wcodes, wscales, (int)N, p.Kp,
+      (int)(p.Np / 16), alpha, bias, y, ldy);
 }
 
-template <int MT, int NT, int HB>
-static void launch_small_k(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                           float g, bool aligned, const uint8_t* packed, int64_t N, float alpha,
-                           const uint16_t* bias, uint16_t* y, int64_t ldy, float* partial,
-                           uint32_t* counters, hipStream_t st) {
-  if (p.kcmax == 4)
-    launch_small_t<MT, NT, HB, 4>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, partial, counters, st);
-  else if (p.kcmax == 8 || MT == 2)
-    launch_small_t<MT, NT, HB, 8>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, partial, counters, st);
-  else
-    launch_small_t<MT, NT, HB, 16 / MT>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, partial, counters, st);
-}
-
-template <int MT, int NT>
-static hipError_t launch_small_hb(const GemmPlan& p, int hb, const uint16_t* x, int64_t M,
-                                  int64_t K, int64_t ldx, float g, bool aligned,
-                                  const uint8_t* packed, int64_t N, float alpha,
-                                  const uint16_t* bias, uint16_t* y, int64_t ldy, float* partial,
-                                  uint32_t* counters, hipStream_t st) {
-  switch (hb) {
-    case 0: launch_small_k<MT, NT, 0>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, partial, counters, st); break;
-    case 16: launch_small_k<MT, NT, 16>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, partial, counters, st); break;
-    case 32: launch_small_k<MT, NT, 32>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, partial, counters, st); break;
-    case 64: launch_small_k<MT, NT, 64>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, partial, counters, st); break;
-    case 128: launch_small_k<MT, NT, 128>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, partial, counters, st); break;
-    default: return hipErrorInvalidValue;
+template <int W, int NTW, int HB>
+static void launch_gemv_q(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                          float g, bool aligned, const uint8_t* packed, int64_t N, float alpha,
+                          const uint16_t* bias, uint16_t* y, int64_t ldy, hipStream_t st) {
+#define FQL_GEMV_ARGS p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st
+  if (p.kcmax == 4) {
+    if (p.qpre == 1) launch_gemv_t<W, NTW, HB, 4, 1>(FQL_GEMV_ARGS);
+    else if (p.qpre == 2) launch_gemv_t<W, NTW, HB, 4, 2>(FQL_GEMV_ARGS);
+    else launch_gemv_t<W, NTW, HB, 4, 4>(FQL_GEMV_ARGS);
+  } else {
+    if (p.qpre == 1) launch_gemv_t<W, NTW, HB, 8, 1>(FQL_GEMV_ARGS);
+    else if (p.qpre == 2) launch_gemv_t<W, NTW, HB, 8, 2>(FQL_GEMV_ARGS);
+    else launch_gemv_t<W, NTW, HB, 8, 4>(FQL_GEMV_ARGS);
   }
-  return hipGetLastError();
+}
+
+template <int HB>
+static void launch_gemv_hb(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                           float g, bool aligned, const uint8_t* packed, int64_t N, float alpha,
+                           const uint16_t* bias, uint16_t* y, int64_t ldy, hipStream_t st) {
+  if (p.waves == 8) {
+    if (p.ntw == 1) launch_gemv_q<8, 1, HB>(FQL_GEMV_ARGS);
+    else if (p.ntw == 2) launch_gemv_q<8, 2, HB>(FQL_GEMV_ARGS);
+    else launch_gemv_q<8, 4, HB>(FQL_GEMV_ARGS);
+  } else {
+    if (p.ntw == 1) launch_gemv_q<4, 1, HB>(FQL_GEMV_ARGS);
+    else if (p.ntw == 2) launch_gemv_q<4, 2, HB>(FQL_GEMV_ARGS);
+    else launch_gemv_q<4, 4, HB>(FQL_GEMV_ARGS);
+  }
+#undef FQL_GEMV_ARGS
 }
 
 template <int MT, int NT>
@@ -538,13 +667,22 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
   _Float16* xhat = reinterpret_cast<_Float16*>(workspace + p.counter_bytes);
   float* partial = reinterpret_cast<float*>(workspace + p.counter_bytes + p.xhat_bytes);
   if (p.groups > p.counter_bytes / 4) return hipErrorInvalidValue;
-  if (p.kind == 0) {
-    if (p.mt == 1) return launch_small_hb<1, 1>(p, hb, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, partial, counters, st);
-    if (p.mt == 2) return launch_small_hb<2, 1>(p, hb, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, partial, counters, st);
-    return hipErrorInvalidValue;
+  if (p.kind == 0 && aligned) {  // the fused path reads x rows with 16-byte loads
+    switch (hb) {
+      case 0: launch_gemv_hb<0>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st); break;
+      case 16: launch_gemv_hb<16>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st); break;
+      case 32: launch_gemv_hb<32>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st); break;
+      case 64: launch_gemv_hb<64>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st); break;
+      case 128: launch_gemv_hb<128>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
   }
+  if (p.kind == 0) return hipErrorInvalidValue;  // caller re-plans unaligned inputs as kind 1
   hipError_t e = launch_quant_nvfp4_xhat(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp, xhat, st);
   if (e != hipSuccess) return e;
+  if (p.mt == 1 && p.nt == 1) return launch_tiled_t<1, 1>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial, counters, st);
+  if (p.mt == 2 && p.nt == 1) return launch_tiled_t<2, 1>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial, counters, st);
   if (p.mt == 4 && p.nt == 1) return launch_tiled_t<4, 1>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial, counters, st);
   if (p.mt == 8 && p.nt == 1) return launch_tiled_t<8, 1>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial, counters, st);
   if (p.mt == 4 && p.nt == 4) return launch_tiled_t<4, 4>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial, counters, st);

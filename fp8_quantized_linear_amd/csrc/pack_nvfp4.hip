@@ -38,21 +38,20 @@ __global__ __launch_bounds__(256) void pack_nvfp4_kernel(const uint8_t* __restri
     w[j] = v;
   }
   *reinterpret_cast<uint4v*>(packed + slot * 16) = uint4v{w[0], w[1], w[2], w[3]};
-  if (kq == 0) {
-    // scale bytes for row n, chunk c: byte h*4 + j = block 8c + 2j + h
-    uint32_t s[2] = {0u, 0u};
+  if (kq < 2) {
+    // scale dword of (row n, chunk c, h = kq): byte j = block 8c + 2j + h
+    const int h = kq;
+    uint32_t sw = 0u;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t b = c * 8 + 2 * j + h;
-        uint32_t v = 0u;
-        if (n < N && b * 16 < K) v = scales[n * (K / 16) + b];
-        s[h] |= v << (8 * j);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int64_t b = c * 8 + 2 * j + h;
+      uint32_t v = 0u;
+      if (n < N && b * 16 < K) v = scales[n * (K / 16) + b];
+      sw |= v << (8 * j);
     }
-    uint8_t* sdst = packed + Np * Kp / 2 + (tc * 16 + n_in) * 8;
-    *reinterpret_cast<uint2*>(sdst) = make_uint2(s[0], s[1]);
+    const int64_t KC4 = (KC + 3) / 4;
+    uint8_t* sdst = packed + Np * Kp / 2 + ((t * KC4 + c / 4) * 32 + n_in * 2 + h) * 16 + (c % 4) * 4;
+    *reinterpret_cast<uint32_t*>(sdst) = sw;
   }
 }
 
@@ -82,12 +81,30 @@ __global__ __launch_bounds__(256) void unpack_nvfp4_kernel(const uint8_t* __rest
     for (int q = 0; q < 4; ++q) dst[q] = src[q];
   }
   const int jb = (int)((b % 8) / 2), h = (int)(b % 2);
-  scales[i] = packed[Np * Kp / 2 + (tc * 16 + n_in) * 8 + h * 4 + jb];
+  const int64_t KC4 = (KC + 3) / 4;
+  scales[i] = packed[Np * Kp / 2 + ((t * KC4 + c / 4) * 32 + n_in * 2 + h) * 16 + (c % 4) * 4 + jb];
+}
+
+// Zero the scale dwords of chunks past KC in the last group of each tile
+// (their codes are never read, but the group is loaded as a whole).
+__global__ void pack_zero_tail_kernel(uint8_t* __restrict__ packed, int64_t Np, int64_t Kp) {
+  const int64_t KC = Kp / 128, KC4 = (KC + 3) / 4;
+  const int64_t tail = KC4 * 4 - KC;  // 0..3 chunks
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (tile, slot, q)
+  if (i >= (Np / 16) * 32 * tail) return;
+  const int64_t t = i / (32 * tail), r = i - t * 32 * tail;
+  const int64_t slot = r / tail, q = KC % 4 + r % tail;
+  *reinterpret_cast<uint32_t*>(packed + Np * Kp / 2 + ((t * KC4 + KC4 - 1) * 32 + slot) * 16 + q * 4) = 0u;
 }
 
 hipError_t launch_pack_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
                              uint8_t* packed, hipStream_t st) {
   const PackedDims d = packed_dims(N, K);
+  const int64_t tail = d.kc4() * 4 - d.kc();
+  if (tail > 0) {
+    const int64_t n = (d.Np / 16) * 32 * tail;
+    pack_zero_tail_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(packed, d.Np, d.Kp);
+  }
   const int64_t slots = (d.Np / 16) * (d.Kp / 128) * 64;
   pack_nvfp4_kernel<<<(unsigned)((slots + 255) / 256), 256, 0, st>>>(codes, scales, N, K, d.Np,
                                                                      d.Kp, packed);

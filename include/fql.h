@@ -144,6 +144,15 @@ int fql_unpack_weight_nvfp4(const void* packed, int64_t N, int64_t K, uint8_t* c
 int fql_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
 
 /*
+ * Diagnostics: writes a one-line description of the launch plan
+ * fql_linear_nvfp4 uses for this shape into `buf` (kernel name, template
+ * parameters, grid, splits), e.g. for attributing profiler time. `aligned`
+ * says whether x rows will be 16-byte aligned. Host-side only.
+ */
+int fql_linear_nvfp4_describe(int64_t M, int64_t N, int64_t K, int aligned, char* buf,
+                              size_t buf_len);
+
+/*
  * The NVFP4 W4A4 linear layer (TorchNvFp4LinearKernel / B12X NVFP4
  * apply_weights): y = bf16(alpha * (x_q @ w_q^T) + bias), where x_q is x
  * quantized exactly as fql_quant_nvfp4 does with (input_global_scale,

@@ -36,9 +36,15 @@ def test_binding_covers_every_declared_symbol():
 def test_version_and_sizes():
     lib = fql.lib()
     assert lib.fql_version() >= 100
-    # packed blob: N padded to 16, K to 128; codes K/2 + scales K/16 bytes per row
-    assert fql.packed_nvfp4_bytes(512, 256) == 512 * 256 // 2 + 512 * 256 // 16
-    assert fql.packed_nvfp4_bytes(100, 272) == 112 * 384 // 2 + 112 * 384 // 16
+    # packed blob: N padded to 16, K to 128; codes Np*Kp/2 bytes, then scales in
+    # 512-byte groups of four 128-deep chunks per 16-row tile
+    def expect(N, K):
+        Np, Kp = -(-N // 16) * 16, -(-K // 128) * 128
+        kc4 = -(-(Kp // 128) // 4)
+        return Np * Kp // 2 + (Np // 16) * kc4 * 512
+    assert fql.packed_nvfp4_bytes(512, 256) == expect(512, 256) == 512 * 128 + 32 * 512
+    assert fql.packed_nvfp4_bytes(100, 272) == expect(100, 272)
+    assert fql.packed_nvfp4_bytes(4096, 4096) == 4096 * 4096 // 2 + 4096 * 4096 // 16
     assert fql.linear_workspace_bytes(1, 6144, 4096) > 0
 
 
