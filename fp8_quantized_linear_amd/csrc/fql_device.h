@@ -16,16 +16,18 @@ namespace fql {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// float32 -> bfloat16 bits, round to nearest even (finite inputs; NaN kept as NaN).
+// float32 -> bfloat16 bits, round to nearest even (NaN stays NaN): gfx950's
+// v_cvt_pk_bf16_f32, which was checked equal to the integer rounding
+// (b + 0x7FFF + lsb) >> 16 on every non-NaN float32 bit pattern and to give a
+// NaN for every NaN input.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7F800000u) == 0x7F800000u) return (b >> 16) | ((b & 0xFFFFu) ? 0x40u : 0u);
-  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // E4M3 encode of a non-negative float32 (block scales are >= 0).

@@ -59,13 +59,16 @@ hipError_t launch_unpack_nvfp4(const uint8_t* packed, int64_t N, int64_t K, uint
 //           workgroup quantizes the activation into LDS and computes one
 //           16-column tile over the full K, its waves splitting K.
 //   kind 1: quantizer kernel (x_hat in A-fragment order) + tiled GEMM.
+//   kind 2: quantizer kernel + LDS-ring tiled GEMM (direct global->LDS loads).
 // Workspace layout: [arrival counters | x_hat | split-K partial slabs]. The
 // counters must be zero before the first call on a workspace; every call
 // leaves them zero again.
 struct GemmPlan {
   int kind;
-  int mt;             // 16-row M tiles per workgroup
-  int nt;             // 16-column N tiles per wave (4 waves per workgroup)
+  int mt;             // kind 1: 16-row M tiles per wave
+  int nt;             // kind 1: 16-column N tiles per wave
+  int wm;             // kind 1: wave rows (the 4 waves form a wm x 4/wm grid)
+  int st;             // kind 2: LDS ring depth (chunks)
   int64_t Mp;         // M padded to a whole number of M tiles
   int64_t Np, Kp;     // packed weight dims
   int64_t groups;     // output tiles (workgroups per split)
@@ -83,6 +86,11 @@ struct GemmPlan {
 // fused small-M kernel needs it. Workspace sizes of both kinds are covered by
 // the aligned=false plan, which never needs less.
 GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned);
+
+// Whether gemm_tiled_kernel<mt, nt, wm> / gemm_lds_kernel<mt, nt, st> is built
+// into the library.
+bool tiled_config_built(int mt, int nt, int wm);
+bool lds_config_built(int mt, int nt, int st);
 
 // Kernel name and parameters of a plan (diagnostics).
 std::string describe_plan(const GemmPlan& p);

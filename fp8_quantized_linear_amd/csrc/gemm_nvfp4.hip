@@ -24,16 +24,17 @@
 // workgroup, which own different 16-column tiles.
 //
 // Two kernels:
-//  * linear_small_kernel (M <= 32): ONE launch per layer call. Each
-//    workgroup quantizes the activation rows for its K range straight into
-//    LDS (the quantizer's arithmetic, fql_quant.h), issues all of its weight
-//    loads up front (one HBM round trip), and reduces split-K partials
-//    itself: the last workgroup of a column group to arrive sums the float32
-//    partials in split order (deterministic) and applies the epilogue.
-//  * gemm_tiled_kernel (M > 32): x_hat comes pre-quantized from the
+//  * linear_gemv_kernel (small M, x rows 16-byte aligned): ONE launch per
+//    layer call. Each workgroup quantizes the activation rows straight into
+//    LDS (the quantizer's arithmetic, fql_quant.h) and computes its 16-column
+//    tiles over the full K, its waves splitting K and adding their partial
+//    tiles through LDS in wave order.
+//  * gemm_tiled_kernel (larger M): x_hat comes pre-quantized from the
 //    quantizer kernel; A chunks are double-buffered through LDS and B is
-//    prefetched one chunk ahead; split-K (if any) uses the same last-arriver
-//    reduction.
+//    prefetched one chunk ahead. When there are too few output tiles to
+//    occupy the GPU, K is split across workgroups: the last workgroup of a
+//    tile to arrive sums the float32 partials in split order
+//    (deterministic) and applies the epilogue.
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
@@ -72,58 +73,65 @@ __device__ __forceinline__ uint32_t dword_of(const uint4v& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// Split-K partials are exchanged between workgroups that may sit on different
+// XCDs (each with its own L2), so they are written and read with agent-scope
+// relaxed atomics, which on gfx950 write through / read past the L2s to the
+// device coherence point. Waiting for the stores to complete before the
+// arrival increment orders them without any whole-cache write-back or
+// invalidate. Each lane moves its accumulator fragment as two 8-byte words.
+__device__ __forceinline__ void store_partial(float4v* p, const float4v& v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  __hip_atomic_store(q, __builtin_bit_cast(uint64_t, float2v{v[0], v[1]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, __builtin_bit_cast(uint64_t, float2v{v[2], v[3]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4v load_partial(const float4v* p) {
+  uint64_t* q = const_cast<uint64_t*>(reinterpret_cast<const uint64_t*>(p));
+  const float2v a = __builtin_bit_cast(float2v, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const float2v b = __builtin_bit_cast(float2v, __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return float4v{a[0], a[1], b[0], b[1]};
+}
+
 // Write the workgroup's output tile: directly (one split) or through the
 // split-K slab and the last-arriver reduction.
-//   rows: MT*16 rows starting at m0; cols: 64*NT columns starting at n0.
-//   slab: [splits][MT*16][64*NT] float32 for this workgroup's tile.
-template <int MT, int NT>
+//   The 4 waves form a WM x (4/WM) grid; wave (wm, wn) holds MT x NT 16x16
+//   accumulator tiles: rows m0 + (wm*MT + mt)*16 + .., cols n0 + (wn*NT + nt)*16 + ..
+//   slab: [splits][4 waves][MT*NT][64 lanes] float4 for this workgroup's tile,
+//   so every lane writes and later sums exactly its own fragments.
+template <int MT, int NT, int WM>
 __device__ __forceinline__ void finish_tile(float4v (&acc)[MT][NT], int M, int N, int m0, int n0,
                                             int split, int splits, float alpha,
                                             const uint16_t* __restrict__ bias,
                                             uint16_t* __restrict__ y, int64_t ldy,
-                                            float* __restrict__ slab, uint32_t* counter,
+                                            float4v* __restrict__ slab, uint32_t* counter,
                                             uint32_t* s_flag) {
-  constexpr int WGC = 64 * NT;
-  constexpr int ROWS = MT * 16;
+  constexpr int WN = 4 / WM;
+  constexpr int FR = MT * NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
   const int col = lane & 15, row0 = 4 * (lane >> 4);
+  auto emit = [&](int mt, int nt, const float4v& s) {
+    const int n = n0 + (wn * NT + nt) * 16 + col;
+    if (n >= N) return;
+    const float bv = bias ? bf16_bits_to_f32(bias[n]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + (wm * MT + mt) * 16 + row0 + i;
+      if (m < M) y[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16_bits(alpha * s[i] + bv);
+    }
+  };
   if (splits == 1) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = n0 + (wave * NT + nt) * 16 + col;
-      if (n >= N) continue;
-      const float bv = bias ? bf16_bits_to_f32(bias[n]) : 0.0f;
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = m0 + mt * 16 + row0 + i;
-          if (m < M) y[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16_bits(alpha * acc[mt][nt][i] + bv);
-        }
-      }
-    }
+      for (int nt = 0; nt < NT; ++nt) emit(mt, nt, acc[mt][nt]);
     return;
   }
-  // Split-K: publish this split's float32 partial tile, count arrivals, and
-  // let the last workgroup to arrive sum the splits in order. The partials
-  // are written and read with agent-scope relaxed atomics, which on gfx950
-  // write through / read past the per-XCD L2s to the device coherence point;
-  // waiting for the stores to complete before the arrival increment orders
-  // them without any whole-cache write-back or invalidate.
+  float4v* mine = slab + wave * FR * 64 + lane;
+  const int64_t zstride = 4 * FR * 64;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int c = (wave * NT + nt) * 16 + col;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = mt * 16 + row0 + i;
-        if (m0 + r < M)
-          __hip_atomic_store(slab + ((int64_t)split * ROWS + r) * WGC + c, acc[mt][nt][i],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
+  for (int f = 0; f < FR; ++f) store_partial(mine + split * zstride + f * 64, acc[f / NT][f % NT]);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // partial stores have completed
   __syncthreads();
   if (tid == 0) {
@@ -133,31 +141,32 @@ __device__ __forceinline__ void finish_tile(float4v (&acc)[MT][NT], int M, int N
   }
   __syncthreads();
   if (*s_flag == 0u) return;
-  // Sum in split order. Loads are issued in unconditional batches of 8 (a
-  // clamped split index) so they overlap instead of costing one memory
-  // round trip each.
-  const int rows = min(ROWS, M - m0);
-  for (int e = tid; e < rows * WGC; e += 256) {
-    const int r = e / WGC, c = e - r * WGC;
-    const int n = n0 + c;
-    const float* base = slab + (int64_t)r * WGC + c;
-    float s = 0.0f;
-    for (int z0 = 0; z0 < splits; z0 += 8) {
-      float v[8];
+  // Sum in split order, FG fragments at a time. ZB splits' fragments are
+  // loaded per round, all issued before any is used (clamped split index: a
+  // static number of loads), so a round costs one memory round trip.
+  constexpr int FG = FR < 8 ? FR : 8;
+  constexpr int ZB = 16 / FG < 8 ? 16 / FG : 8;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+  for (int f0 = 0; f0 < FR; f0 += FG) {
+    float4v sum[FG];
+#pragma unroll
+    for (int f = 0; f < FG; ++f) sum[f] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int z0 = 0; z0 < splits; z0 += ZB) {
+      float4v v[ZB][FG];
+#pragma unroll
+      for (int j = 0; j < ZB; ++j) {
         const int z = z0 + j < splits ? z0 + j : splits - 1;
-        v[j] = __hip_atomic_load(base + (int64_t)z * ROWS * WGC, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int f = 0; f < FG; ++f) v[j][f] = load_partial(mine + z * zstride + (f0 + f) * 64);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (z0 + j < splits) s += v[j];
+      for (int j = 0; j < ZB; ++j)
+        if (z0 + j < splits)
+#pragma unroll
+          for (int f = 0; f < FG; ++f) sum[f] += v[j][f];
     }
-    if (n < N) {
-      const float bv = bias ? bf16_bits_to_f32(bias[n]) : 0.0f;
-      y[(int64_t)(m0 + r) * ldy + n] = (uint16_t)f32_to_bf16_bits(alpha * s + bv);
-    }
+#pragma unroll
+    for (int f = 0; f < FG; ++f) emit((f0 + f) / NT, (f0 + f) % NT, sum[f]);
   }
   if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -362,18 +371,26 @@ __global__ __launch_bounds__(64 * W) void linear_gemv_kernel(
 // tiled kernel (x_hat from the quantizer kernel)
 // ---------------------------------------------------------------------------
 
-template <int MT, int NT>
+// The 4 waves form a WM x (4/WM) grid over the workgroup tile: wave (wm, wn)
+// owns MT 16-row tiles and NT 16-column tiles. A (x_hat) chunks for all WM*MT
+// row tiles are staged through LDS and read by the 4/WM waves of a row; each
+// wave dequantizes only its own NT weight tiles (WM > 1 dequantizes a tile in
+// WM waves, trading VALU work for fewer LDS reads: a wave reads MT A fragments
+// per NT*MT MFMAs).
+template <int MT, int NT, int WM>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(
     const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
     const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, int ngroups,
     int kc_per_split, int splits, float alpha, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ y, int64_t ldy, float* __restrict__ partial,
+    uint16_t* __restrict__ y, int64_t ldy, float4v* __restrict__ partial,
     uint32_t* __restrict__ counters) {
-  constexpr int WGC = 64 * NT;
-  __shared__ uint4v a_lds[2][MT * 4][64];
+  constexpr int WN = 4 / WM;
+  constexpr int AM = WM * MT;  // 16-row A tiles per workgroup
+  __shared__ uint4v a_lds[2][AM * 4][64];
   __shared__ uint32_t s_flag;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
   const int64_t KC = Kp / 128;
   const int64_t KS = Kp / 32;
   // blockIdx.x = (mgroup * ngroups + ngroup) * splits + split
@@ -383,15 +400,16 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
   const int mgroup = tilegrp / ngroups;
   const int64_t c_begin = (int64_t)split * kc_per_split;
   const int64_t c_end = c_begin + kc_per_split < KC ? c_begin + kc_per_split : KC;
-  const int tile0 = (ngroup * 4 + wave) * NT;
+  const int tile0 = (ngroup * WN + wn) * NT;
 
   bool tvalid[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) tvalid[nt] = (tile0 + nt) < ntiles;
 
+  // thread tid stages fragment (f, ks = tid / 64) of every A row tile f
   const uint4v* xsrc = reinterpret_cast<const uint4v*>(xhat);
-  auto a_src = [&](int mt, int64_t c) -> const uint4v* {
-    return xsrc + ((((int64_t)mgroup * MT + mt) * KS + c * 4 + (tid >> 6)) * 64 + (tid & 63));
+  auto a_src = [&](int f, int64_t c) -> const uint4v* {
+    return xsrc + ((((int64_t)mgroup * AM + f) * KS + c * 4 + wave) * 64 + lane);
   };
   const int64_t KC4 = (KC + 3) / 4;
   const uint4v* bq_base[NT];
@@ -422,11 +440,11 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
   auto clampc = [&](int64_t c) -> int64_t { return c < c_end ? c : c_end - 1; };
   uint4v bq0[NT], bq1[NT];
   uint32_t bs0[NT], bs1[NT];
-  uint4v ar0[MT], ar1[MT];
+  uint4v ar0[AM], ar1[AM];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) a_lds[0][mt * 4 + (tid >> 6)][tid & 63] = *a_src(mt, c_begin);
+  for (int f = 0; f < AM; ++f) a_lds[0][f * 4 + wave][lane] = *a_src(f, c_begin);
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) ar1[mt] = *a_src(mt, clampc(c_begin + 1));
+  for (int f = 0; f < AM; ++f) ar1[f] = *a_src(f, clampc(c_begin + 1));
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {  // invalid tiles read tile 0 (in bounds, never stored)
     bq0[nt] = bq_base[nt][c_begin * 64];
@@ -444,20 +462,20 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
       for (int nt = 0; nt < NT; ++nt) bf[nt] = b_fragment(dword_of(bq[nt], ks), ChunkScales(bs[nt])[ks]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const half8 a = __builtin_bit_cast(half8, a_lds[buf][mt * 4 + ks][lane]);
+        const half8 a = __builtin_bit_cast(half8, a_lds[buf][(wm * MT + mt) * 4 + ks][lane]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[nt], acc[mt][nt], 0, 0, 0);
       }
     }
   };
-  auto advance = [&](int buf, int64_t c, uint4v (&ar_store)[MT], uint4v (&ar_load)[MT],
+  auto advance = [&](int buf, int64_t c, uint4v (&ar_store)[AM], uint4v (&ar_load)[AM],
                      uint4v (&bq)[NT], uint32_t (&bs)[NT]) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) a_lds[buf ^ 1][mt * 4 + (tid >> 6)][tid & 63] = ar_store[mt];
+    for (int f = 0; f < AM; ++f) a_lds[buf ^ 1][f * 4 + wave][lane] = ar_store[f];
     const int64_t c2 = clampc(c + 2);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) ar_load[mt] = *a_src(mt, c2);
+    for (int f = 0; f < AM; ++f) ar_load[f] = *a_src(f, c2);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       bq[nt] = bq_base[nt][c2 * 64];
@@ -481,9 +499,216 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
   }
   if (c < c_end) compute(0, bq0, bs0);  // odd chunk count: last chunk
 
-  float* slab = partial + (int64_t)tilegrp * splits * (MT * 16) * WGC;
-  finish_tile<MT, NT>(acc, M, N, mgroup * MT * 16, ngroup * WGC, split, splits, alpha, bias, y,
-                      ldy, slab, counters + tilegrp, &s_flag);
+  float4v* slab = partial + (int64_t)tilegrp * splits * (4 * MT * NT * 64);
+  finish_tile<MT, NT, WM>(acc, M, N, mgroup * AM * 16, ngroup * WN * NT * 16, split, splits,
+                          alpha, bias, y, ldy, slab, counters + tilegrp, &s_flag);
+}
+
+// ---------------------------------------------------------------------------
+// LDS-ring tiled kernel (x_hat from the quantizer kernel)
+// ---------------------------------------------------------------------------
+//
+// Workgroup: 4 waves; tile (MT*16) rows x (4*NT*16) columns; wave w owns
+// columns [w*NT*16, (w+1)*NT*16) of the tile and all of its rows, so every
+// weight tile is dequantized by exactly one wave and the activation
+// fragments (read by all four waves) come from LDS.
+// Every global -> LDS transfer is a direct LDS load (global_load_lds_*), so
+// the data in flight holds no registers and an ST-deep ring of per-chunk
+// stages runs ST-1 chunks (128-deep K slices) ahead of the MFMAs:
+//   A  [MT][4 ks][64 lanes] x 16 B   x_hat fragments (wave w loads ks = w)
+//   Bq [4 waves][NT][64 lanes] x 16 B  weight code slots
+//   Bs [4 waves][NT][64 lanes] x 4 B   the lane's scale dword of the chunk
+// The loads are issued with inline assembly and waited for with explicit
+// s_waitcnt vmcnt(n): the compiler does not track LDS-DMA completion per
+// stage and would otherwise wait for the whole ring before every LDS read.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_t*)(p);
+}
+// 16 (or 4) bytes per lane from sbase + voff into LDS at lds + lane * 16 (or 4).
+// sbase and lds must be wave-uniform.
+__device__ __forceinline__ void lds_load16(const void* sbase, uint32_t voff, uint32_t lds) {
+  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+                   : "memory");
+}
+__device__ __forceinline__ void lds_load4(const void* sbase, uint32_t voff, uint32_t lds) {
+  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+                   : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier without the compiler's release fence (which would wait
+// for every outstanding load, including the ring's prefetches); LDS reads of
+// the finished stage have completed (lgkmcnt) before any wave passes it.
+__device__ __forceinline__ void stage_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+template <int MT, int NT>
+struct LdsStage {
+  uint4v a[MT * 4][64];
+  uint4v bq[4 * NT][64];
+  uint32_t bs[4 * NT][64];
+};
+
+template <int MT, int NT, int ST, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(
+    const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
+    const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, int ngroups,
+    int kc_per_split, int splits, float alpha, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ y, int64_t ldy, float4v* __restrict__ partial,
+    uint32_t* __restrict__ counters) {
+  static_assert(ST >= 2 && ST <= 4, "ring depth");
+  constexpr int L = MT + 2 * NT;  // LDS loads per chunk per wave
+  static_assert(L * (ST - 2) <= 63, "vmcnt range");
+  __shared__ LdsStage<MT, NT> stage[ST];
+  __shared__ uint32_t s_flag;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t KC = Kp / 128;
+  const int64_t KC4 = (KC + 3) / 4;
+  const int split = blockIdx.x % splits;
+  const int tilegrp = blockIdx.x / splits;
+  const int ngroup = tilegrp % ngroups;
+  const int mgroup = tilegrp / ngroups;
+  const int64_t c_begin = (int64_t)split * kc_per_split;
+  const int64_t c_end = c_begin + kc_per_split < KC ? c_begin + kc_per_split : KC;
+  const int nch = (int)(c_end - c_begin);
+  const int tile0 = (ngroup * 4 + wave) * NT;
+
+  // wave-uniform global bases; per-lane byte offsets
+  const uint8_t* a_base = reinterpret_cast<const uint8_t*>(xhat) +
+                          ((int64_t)mgroup * MT * (Kp / 32) + wave) * 1024;  // + f*KS*1024 + c*4096
+  const uint32_t a_voff = lane * 16;
+  const uint8_t* q_base[NT];
+  const uint8_t* s_base[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int64_t t = tile0 + nt < ntiles ? tile0 + nt : 0;  // invalid tiles read tile 0, never stored
+    q_base[nt] = wcodes + t * KC * 1024;                       // + c*1024
+    s_base[nt] = wscales + t * KC4 * 512;                      // + (c/4)*512 + (c%4)*4
+  }
+  const uint32_t q_voff = lane * 16;
+  const uint32_t s_voff = ((lane & 15) * 2 + (lane >> 5)) * 16;
+
+  auto issue = [&](LdsStage<MT, NT>& sg, int64_t c) {
+    c = c < c_end ? c : c_end - 1;  // clamped: a static number of loads per chunk
+#pragma unroll
+    for (int f = 0; f < MT; ++f)
+      lds_load16(a_base + ((int64_t)f * (Kp / 32) + c * 4) * 1024, a_voff, lds_offset(&sg.a[f * 4 + wave][0]));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      lds_load16(q_base[nt] + c * 1024, q_voff, lds_offset(&sg.bq[wave * NT + nt][0]));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      lds_load4(s_base[nt] + (c >> 2) * 512 + (c & 3) * 4, s_voff, lds_offset(&sg.bs[wave * NT + nt][0]));
+  };
+
+  float4v acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // Software pipeline. A chunk is four 32-deep K steps; step ks issues the
+  // LDS reads of step ks+1's activation fragments, then its own MFMAs
+  // interleaved with the dequantization of step ks+1's weight fragments (one
+  // wave per SIMD: VALU work only overlaps the matrix pipe when it is issued
+  // between the MFMAs, in program order). Between steps 2 and 3 the wave
+  // waits for the next chunk's stage, passes the workgroup barrier, refills
+  // the stage it has finished reading, and reads the next chunk's weight
+  // codes and first activation fragments, which step 3's MFMAs then hide.
+  constexpr int MFMAS = MT * NT;                    // per K step
+  constexpr int VPM = (8 * NT + MFMAS - 1) / MFMAS;  // dequantization VALU ops per MFMA
+  uint4v bq[NT];
+  uint32_t bsw[NT];
+  half8 bf[2][NT];
+  uint4v af[2][MT];
+  auto read_head = [&](const LdsStage<MT, NT>& sg) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      bq[nt] = sg.bq[wave * NT + nt][lane];
+      bsw[nt] = sg.bs[wave * NT + nt][lane];
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) af[0][mt] = sg.a[mt * 4][lane];
+  };
+  auto dequant = [&](int buf, int ks) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bf[buf][nt] = b_fragment(dword_of(bq[nt], ks), ChunkScales(bsw[nt])[ks]);
+  };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const half8 a = __builtin_bit_cast(half8, af[buf][mt]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[buf][nt], acc[mt][nt], 0, 0, 0);
+    }
+  };
+  // steps 0..2 of a chunk held in stage sg
+  auto steps012 = [&](const LdsStage<MT, NT>& sg) {
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+      const int cur = ks & 1, nxt = cur ^ 1;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) af[nxt][mt] = sg.a[mt * 4 + ks + 1][lane];
+      __builtin_amdgcn_sched_barrier(0);
+      dequant(nxt, ks + 1);
+      mfmas(cur);
+#pragma unroll
+      for (int i = 0; i < MFMAS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // prologue: every stage filled, chunk 0's head in registers
+#pragma unroll
+  for (int p = 0; p < ST; ++p) issue(stage[p], c_begin + p);
+  wait_vmcnt<L * (ST - 1)>();
+  stage_barrier();
+  read_head(stage[0]);
+  dequant(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // chunk i lives in stage i % ST; the loop is unrolled by ST so that every
+  // stage index is a compile-time constant
+  for (int i0 = 0; i0 < nch; i0 += ST) {
+#pragma unroll
+    for (int j = 0; j < ST; ++j) {
+      if (i0 + j < nch) {
+        steps012(stage[j]);
+        const bool more = i0 + j + 1 < nch;
+        wait_vmcnt<L * (ST - 2)>();  // this wave's loads of chunk i+1 have landed
+        stage_barrier();             // everyone's have, and stage j has been read by all
+        issue(stage[j], c_begin + i0 + j + ST);
+        if (more) read_head(stage[(j + 1) % ST]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) dequant(0, 0);
+        mfmas(1);
+        // the head reads need time: the first MFMAs go out alone
+#pragma unroll
+        for (int i = 0; i < MFMAS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i >= MFMAS / 4) __builtin_amdgcn_sched_group_barrier(0x002, VPM + 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  wait_vmcnt<0>();  // no LDS load may still be in flight when the workgroup ends
+
+  float4v* slab = partial + (int64_t)tilegrp * splits * (4 * MT * NT * 64);
+  finish_tile<MT, NT, 1>(acc, M, N, mgroup * MT * 16, ngroup * 4 * NT * 16, split, splits, alpha,
+                         bias, y, ldy, slab, counters + tilegrp, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -495,7 +720,7 @@ static constexpr int kCUs = 256;
 // Benchmarking aid: FQL_PLAN="kind=0,waves=8,ntw=2,rc=4" or "kind=1,mt=4,nt=1,splits=2"
 // overrides the launch-plan heuristics (no effect on results, only on speed).
 struct GemmOverride {
-  int kind = -1, waves = 0, ntw = 0, rc = 0, mt = 0, nt = 0, splits = 0;
+  int kind = -1, waves = 0, ntw = 0, rc = 0, mt = 0, nt = 0, wm = 0, st = 0, splits = 0;
 };
 static GemmOverride gemm_override() {
   GemmOverride o;
@@ -516,7 +741,9 @@ static GemmOverride gemm_override() {
       else if (k == "ntw" && (v == 1 || v == 2 || v == 4)) o.ntw = v;
       else if (k == "rc" && (v == 4 || v == 8)) o.rc = v;
       else if (k == "mt" && (v == 1 || v == 2 || v == 4 || v == 8)) o.mt = v;
-      else if (k == "nt" && (v == 1 || v == 4)) o.nt = v;
+      else if (k == "nt" && (v == 1 || v == 2 || v == 4)) o.nt = v;
+      else if (k == "wm" && (v == 1 || v == 2 || v == 4)) o.wm = v;
+      else if (k == "st" && v >= 2 && v <= 4) o.st = v;
       else if (k == "splits" && v >= 1 && v <= 64) o.splits = v;
     }
     pos = end + 1;
@@ -546,6 +773,7 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     p.kind = 0;
     p.mt = 1;
     p.nt = 1;
+    p.wm = 1;
     p.Mp = M;
     p.waves = ntiles < 1024 ? 8 : 4;
     p.ntw = 1;
@@ -562,28 +790,54 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     p.xhat_bytes = 0;
     p.lds_bytes = std::max<int64_t>(M * p.Kp * 2, (int64_t)p.waves * p.ntw * 1024);
   } else {
-    p.kind = 1;
-    p.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-    p.nt = M <= 128 ? 1 : 4;
-    if (ov.mt && ov.mt * 16 >= std::min<int64_t>(M, 128)) p.mt = ov.mt;
-    if (ov.nt) p.nt = ov.nt;
-    p.Mp = round_up(M, 16 * p.mt);
-    const int64_t ngroups = (ntiles + 4 * p.nt - 1) / (4 * p.nt);
-    const int64_t mgroups = p.Mp / (16 * p.mt);
+    // Workgroup tile (WM*MT*16) x ((4/WM)*NT*16); kind 2 always has WM = 1.
+    // Defaults (measured on the decode and prefill layer shapes): small M
+    // keeps the register-staged tiled kernel; from 33 rows on the LDS-ring
+    // kernel with 64 x 128 tiles (up to 128 rows) or 64 x 256 tiles.
+    p.kind = M <= 32 ? 1 : 2;
+    if (ov.kind == 1 || ov.kind == 2) p.kind = ov.kind;
+    const bool lds_ring = p.kind == 2;
+    p.wm = 1;
+    p.st = 2;
+    if (!lds_ring) {
+      if (M <= 16) { p.mt = 1; p.nt = 1; }
+      else if (M <= 32) { p.mt = 2; p.nt = 1; }
+      else if (M <= 64) { p.mt = 2; p.nt = 2; p.wm = 2; }
+      else if (M <= 128) { p.mt = 4; p.nt = 2; p.wm = 2; }
+      else { p.mt = 8; p.nt = 4; }
+    } else if (M <= 128) {
+      p.mt = 4; p.nt = 2;
+    } else {
+      p.mt = 4; p.nt = 4;
+    }
+    if (ov.mt || ov.nt || ov.wm || ov.st) {
+      if (ov.mt) p.mt = ov.mt;
+      if (ov.nt) p.nt = ov.nt;
+      if (ov.wm && !lds_ring) p.wm = ov.wm;
+      if (ov.st) p.st = ov.st;
+    }
+    if (lds_ring ? !lds_config_built(p.mt, p.nt, p.st) : !tiled_config_built(p.mt, p.nt, p.wm)) {
+      p.kind = 1; p.mt = 1; p.nt = 1; p.wm = 1;
+    }
+    p.Mp = round_up(M, 16 * p.mt * p.wm);
+    const int64_t ngroups = (ntiles + (4 / p.wm) * p.nt - 1) / ((4 / p.wm) * p.nt);
+    const int64_t mgroups = p.Mp / (16 * p.mt * p.wm);
     const int64_t groups = ngroups * mgroups;
     // Split K across workgroups only when there are too few output tiles to
     // occupy the GPU: the arrival counter of the split-K reduction costs
     // about a microsecond plus ~0.35 us per split contending on it.
     int64_t s = 1;
-    if (groups < 192) s = std::min<int64_t>(std::min<int64_t>(4, KC), (256 + groups - 1) / groups);
+    if (groups < 192) s = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(4, KC), 256 / groups));
     if (ov.splits) s = std::min<int64_t>(ov.splits, KC);
+    // the LDS ring runs deeper when a split-K tile has few chunks to hide latency in
+    if (p.kind == 2 && !ov.st && s > 1 && lds_config_built(p.mt, p.nt, 4)) p.st = 4;
     p.kc_per_split = (int)((KC + s - 1) / s);
     p.splits = (int)((KC + p.kc_per_split - 1) / p.kc_per_split);
     p.groups = groups;
     p.ngroups = ngroups;
     p.xhat_bytes = round_up(p.Mp * p.Kp * 2, 256);
   }
-  const int64_t slab = (int64_t)p.splits * (16 * p.mt) * (64 * p.nt) * 4;
+  const int64_t slab = (int64_t)p.splits * 4 * p.mt * p.nt * 64 * 16;  // [splits][4 waves][MT*NT][64] float4
   p.partial_bytes = p.splits > 1 ? round_up(p.groups * slab, 256) : 0;
   p.counter_bytes = kCounterBytes;
   p.total_bytes = p.counter_bytes + p.xhat_bytes + p.partial_bytes;
@@ -592,13 +846,17 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
 
 std::string describe_plan(const GemmPlan& p) {
   char b[256];
-  if (p.kind == 0) {
+  if (p.kind == 2) {
+    std::snprintf(b, sizeof(b),
+                  "quant_nvfp4_xhat_kernel + gemm_lds_kernel<MT=%d,NT=%d,ST=%d> grid=%lld splits=%d",
+                  p.mt, p.nt, p.st, (long long)(p.groups * p.splits), p.splits);
+  } else if (p.kind == 0) {
     std::snprintf(b, sizeof(b), "linear_gemv_kernel<W=%d,NTW=%d,RC=%d,QPRE=%d> grid=%lld lds=%lld",
                   p.waves, p.ntw, p.kcmax, p.qpre, (long long)p.groups, (long long)p.lds_bytes);
   } else {
     std::snprintf(b, sizeof(b),
-                  "quant_nvfp4_xhat_kernel + gemm_tiled_kernel<MT=%d,NT=%d> grid=%lld splits=%d",
-                  p.mt, p.nt, (long long)(p.groups * p.splits), p.splits);
+                  "quant_nvfp4_xhat_kernel + gemm_tiled_kernel<MT=%d,NT=%d,WM=%d> grid=%lld splits=%d",
+                  p.mt, p.nt, p.wm, (long long)(p.groups * p.splits), p.splits);
   }
   return std::string(b);
 }
@@ -646,17 +904,55 @@ static void launch_gemv_hb(const GemmPlan& p, const uint16_t* x, int64_t M, int6
 #undef FQL_GEMV_ARGS
 }
 
-template <int MT, int NT>
+template <int MT, int NT, int WM>
 static hipError_t launch_tiled_t(const GemmPlan& p, const _Float16* xhat, const uint8_t* packed,
                                  int64_t M, int64_t N, float alpha, const uint16_t* bias,
-                                 uint16_t* y, int64_t ldy, float* partial, uint32_t* counters,
+                                 uint16_t* y, int64_t ldy, float4v* partial, uint32_t* counters,
                                  hipStream_t st) {
   const uint8_t* wcodes = packed;
   const uint8_t* wscales = packed + p.Np * p.Kp / 2;
-  gemm_tiled_kernel<MT, NT><<<(unsigned)(p.groups * p.splits), 256, 0, st>>>(
+  gemm_tiled_kernel<MT, NT, WM><<<(unsigned)(p.groups * p.splits), 256, 0, st>>>(
       xhat, wcodes, wscales, (int)M, (int)N, p.Kp, (int)(p.Np / 16), (int)p.ngroups,
       p.kc_per_split, p.splits, alpha, bias, y, ldy, partial, counters);
   return hipGetLastError();
+}
+
+// The (MT, NT, WM) tiled configurations built into the library.
+#define FQL_TILED_CONFIGS(X) \
+  X(1, 1, 1) X(2, 1, 1) X(4, 1, 1) X(8, 1, 1) X(8, 2, 1) X(4, 4, 1) X(8, 4, 1) \
+  X(2, 2, 2) X(4, 2, 2) X(2, 4, 2) X(4, 4, 2) X(1, 4, 4) X(2, 4, 4) X(2, 2, 4)
+
+template <int MT, int NT, int ST, int OCC>
+static hipError_t launch_lds_t(const GemmPlan& p, const _Float16* xhat, const uint8_t* packed,
+                               int64_t M, int64_t N, float alpha, const uint16_t* bias,
+                               uint16_t* y, int64_t ldy, float4v* partial, uint32_t* counters,
+                               hipStream_t st) {
+  const uint8_t* wcodes = packed;
+  const uint8_t* wscales = packed + p.Np * p.Kp / 2;
+  gemm_lds_kernel<MT, NT, ST, OCC><<<(unsigned)(p.groups * p.splits), 256, 0, st>>>(
+      xhat, wcodes, wscales, (int)M, (int)N, p.Kp, (int)(p.Np / 16), (int)p.ngroups,
+      p.kc_per_split, p.splits, alpha, bias, y, ldy, partial, counters);
+  return hipGetLastError();
+}
+
+// The (MT, NT, ST, OCC) LDS-ring configurations built into the library
+// (OCC: workgroups per CU the register and LDS budgets are sized for).
+#define FQL_LDS_CONFIGS(X) \
+  X(1, 4, 4, 1) X(2, 4, 4, 1) X(4, 4, 3, 1) X(4, 4, 4, 1) X(8, 4, 2, 1) X(8, 4, 3, 1) X(4, 2, 4, 1) \
+  X(8, 2, 3, 1) X(2, 2, 4, 1) X(4, 4, 2, 2) X(2, 4, 2, 2) X(4, 2, 2, 2) X(2, 2, 2, 2)
+
+bool lds_config_built(int mt, int nt, int st) {
+#define FQL_X(A, B, C, D) if (mt == A && nt == B && st == C) return true;
+  FQL_LDS_CONFIGS(FQL_X)
+#undef FQL_X
+  return false;
+}
+
+bool tiled_config_built(int mt, int nt, int wm) {
+#define FQL_X(A, B, C) if (mt == A && nt == B && wm == C) return true;
+  FQL_TILED_CONFIGS(FQL_X)
+#undef FQL_X
+  return false;
 }
 
 hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K,
@@ -681,12 +977,20 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
   if (p.kind == 0) return hipErrorInvalidValue;  // caller re-plans unaligned inputs as kind 1
   hipError_t e = launch_quant_nvfp4_xhat(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp, xhat, st);
   if (e != hipSuccess) return e;
-  if (p.mt == 1 && p.nt == 1) return launch_tiled_t<1, 1>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial, counters, st);
-  if (p.mt == 2 && p.nt == 1) return launch_tiled_t<2, 1>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial, counters, st);
-  if (p.mt == 4 && p.nt == 1) return launch_tiled_t<4, 1>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial, counters, st);
-  if (p.mt == 8 && p.nt == 1) return launch_tiled_t<8, 1>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial, counters, st);
-  if (p.mt == 4 && p.nt == 4) return launch_tiled_t<4, 4>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial, counters, st);
-  if (p.mt == 8 && p.nt == 4) return launch_tiled_t<8, 4>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial, counters, st);
+  float4v* partial4 = reinterpret_cast<float4v*>(partial);
+  if (p.kind == 2) {
+#define FQL_X(A, B, C, D)                                                                        \
+  if (p.mt == A && p.nt == B && p.st == C)                                                       \
+    return launch_lds_t<A, B, C, D>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial4, counters, st);
+    FQL_LDS_CONFIGS(FQL_X)
+#undef FQL_X
+    return hipErrorInvalidValue;
+  }
+#define FQL_X(A, B, C)                                                                           \
+  if (p.mt == A && p.nt == B && p.wm == C)                                                       \
+    return launch_tiled_t<A, B, C>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial4, counters, st);
+  FQL_TILED_CONFIGS(FQL_X)
+#undef FQL_X
   return hipErrorInvalidValue;
 }
 

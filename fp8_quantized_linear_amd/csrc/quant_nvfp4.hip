@@ -21,6 +21,8 @@
 //
 // The block arithmetic (fql_quant.h) runs with FMA contraction off: every
 // float operation is the single IEEE operation the definition names.
+#include <algorithm>
+
 #include "fql_device.h"
 #include "fql_internal.h"
 #include "fql_quant.h"
@@ -58,17 +60,18 @@ __global__ __launch_bounds__(256) void quant_nvfp4_canonical_kernel(
 // Rows >= M and columns >= K are written as zeros.
 template <int HB>
 __global__ __launch_bounds__(256) void quant_nvfp4_xhat_kernel(
-    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, float g, int aligned16,
-    int64_t Mp, int64_t Kp, _Float16* __restrict__ xhat) {
-  const int64_t nblk = Kp / 16;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= Mp * nblk) return;  // whole waves only: Mp * nblk is a multiple of 64
-  const int64_t m = i / nblk;
-  const int64_t kb = i - m * nblk;
-  const bool real = (m < M) && (kb * 16 < K);
+    const uint16_t* __restrict__ x, int M, int K, int64_t ldx, float g, int aligned16, int Mp,
+    int Kp, _Float16* __restrict__ xhat) {
+  // 32-bit index arithmetic: the launcher checks Mp * Kp / 16 < 2^31
+  const uint32_t nblk = (uint32_t)Kp / 16u;
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i >= (uint32_t)Mp * nblk) return;  // whole waves only: Mp * nblk is a multiple of 64
+  const uint32_t m = i / nblk;
+  const uint32_t kb = i - m * nblk;
+  const bool real = (m < (uint32_t)M) && (kb * 16u < (uint32_t)K);
   float v[16];
   if (real) {
-    Loader<uint16_t>::load16(x + m * ldx + kb * 16, aligned16 != 0, v);
+    Loader<uint16_t>::load16(x + (int64_t)m * ldx + kb * 16u, aligned16 != 0, v);
   } else {
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = 0.0f;
@@ -81,41 +84,50 @@ __global__ __launch_bounds__(256) void quant_nvfp4_xhat_kernel(
   uint32_t hw[8];
   dequant8_f16(lo, s2, hw);
   dequant8_f16(hi, s2, hw + 4);
-  const int64_t k0 = kb * 16;
-  const int64_t ks = k0 / 32;
-  const int kq0 = (int)((k0 % 32) / 8);  // 0 or 2
-  const int ml = (int)(m % 16);
-  _Float16* base = xhat + (((m / 16) * (Kp / 32) + ks) * 64) * 8;
-  uint4v* d0 = reinterpret_cast<uint4v*>(base + (kq0 * 16 + ml) * 8);
-  uint4v* d1 = reinterpret_cast<uint4v*>(base + ((kq0 + 1) * 16 + ml) * 8);
-  *d0 = uint4v{hw[0], hw[1], hw[2], hw[3]};
-  *d1 = uint4v{hw[4], hw[5], hw[6], hw[7]};
+  const uint32_t ks = kb >> 1;           // 32-deep K step of the block
+  const uint32_t kq0 = (kb & 1u) * 2u;   // first of its two 8-deep quarters
+  const uint32_t ml = m & 15u;
+  uint4v* base = reinterpret_cast<uint4v*>(xhat) + ((m >> 4) * ((uint32_t)Kp / 32u) + ks) * 64u;
+  base[kq0 * 16u + ml] = uint4v{hw[0], hw[1], hw[2], hw[3]};
+  base[(kq0 + 1u) * 16u + ml] = uint4v{hw[4], hw[5], hw[6], hw[7]};
 }
 
 // max |v| (after the optional rotation) into *amax (as ordered uint bits;
 // non-negative floats compare like their bit patterns). *amax must be 0 first.
+// Grid-stride over 16-blocks (the stride is a multiple of 64, so the lanes of
+// a Hadamard chunk stay adjacent in one wave); one atomic per workgroup.
 template <typename TIn, int HB>
 __global__ __launch_bounds__(256) void amax_kernel(const TIn* __restrict__ x, int64_t rows,
                                                    int64_t K, int64_t ldx, int aligned16,
                                                    uint32_t* __restrict__ amax) {
+  __shared__ float wmax[4];
   const int64_t nblk = K / 16;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const bool active = i < rows * nblk;
-  const int64_t m = active ? i / nblk : 0;
-  const int64_t kb = active ? i - m * nblk : 0;
-  float v[16];
-  if (active) {
-    Loader<TIn>::load16(x + m * ldx + kb * 16, aligned16 != 0, v);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = 0.0f;
-  }
-  if constexpr (HB > 0) fwht_block<HB>(v, kb);
+  const int64_t total = rows * nblk;
+  const int64_t stride = (int64_t)gridDim.x * 256;
   float a = 0.0f;
+  for (int64_t base = (int64_t)blockIdx.x * 256; base < total; base += stride) {
+    const int64_t i = base + threadIdx.x;
+    const bool active = i < total;
+    const int64_t m = active ? i / nblk : 0;
+    const int64_t kb = active ? i - m * nblk : 0;
+    float v[16];
+    if (active) {
+      Loader<TIn>::load16(x + m * ldx + kb * 16, aligned16 != 0, v);
+    } else {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(v[e]));
+      for (int e = 0; e < 16; ++e) v[e] = 0.0f;
+    }
+    if constexpr (HB > 0) fwht_block<HB>(v, kb);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) a = __builtin_fmaxf(a, __builtin_fabsf(v[e]));
+  }
   for (int off = 32; off > 0; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off));
-  if ((threadIdx.x & 63) == 0) atomicMax(amax, __float_as_uint(a));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float b = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
+    atomicMax(amax, __float_as_uint(b));
+  }
 }
 
 __global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
@@ -158,14 +170,16 @@ hipError_t launch_quant_nvfp4_xhat(const uint16_t* x, int64_t M, int64_t K, int6
                                    int hb, bool aligned, int64_t Mp, int64_t Kp, _Float16* xhat,
                                    hipStream_t st) {
   const int64_t total = Mp * (Kp / 16);
+  if (total >= ((int64_t)1 << 31) || Kp >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
   const int al = aligned ? 1 : 0;
+  const int m = (int)M, k = (int)K, mp = (int)Mp, kp = (int)Kp;
   switch (hb) {
-    case 0: quant_nvfp4_xhat_kernel<0><<<grid, block, 0, st>>>(x, M, K, ldx, g, al, Mp, Kp, xhat); break;
-    case 16: quant_nvfp4_xhat_kernel<16><<<grid, block, 0, st>>>(x, M, K, ldx, g, al, Mp, Kp, xhat); break;
-    case 32: quant_nvfp4_xhat_kernel<32><<<grid, block, 0, st>>>(x, M, K, ldx, g, al, Mp, Kp, xhat); break;
-    case 64: quant_nvfp4_xhat_kernel<64><<<grid, block, 0, st>>>(x, M, K, ldx, g, al, Mp, Kp, xhat); break;
-    case 128: quant_nvfp4_xhat_kernel<128><<<grid, block, 0, st>>>(x, M, K, ldx, g, al, Mp, Kp, xhat); break;
+    case 0: quant_nvfp4_xhat_kernel<0><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat); break;
+    case 16: quant_nvfp4_xhat_kernel<16><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat); break;
+    case 32: quant_nvfp4_xhat_kernel<32><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat); break;
+    case 64: quant_nvfp4_xhat_kernel<64><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat); break;
+    case 128: quant_nvfp4_xhat_kernel<128><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -177,7 +191,7 @@ static hipError_t launch_amax(const TIn* x, int64_t rows, int64_t K, int64_t ldx
   uint32_t* o = reinterpret_cast<uint32_t*>(out);
   zero_u32_kernel<<<1, 1, 0, st>>>(o);
   const int64_t total = rows * (K / 16);
-  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  const dim3 grid((unsigned)std::min<int64_t>((total + 255) / 256, 2048)), block(256);
   const int al = aligned ? 1 : 0;
   switch (hb) {
     case 0: amax_kernel<TIn, 0><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o); break;

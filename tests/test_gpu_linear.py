@@ -174,3 +174,36 @@ def test_linear_identity_weight_closed_form():
     ulp = np.abs(ref) * 2.0 ** -7 + 1e-30
     assert np.all(np.abs(got - ref) <= ulp)
     assert np.mean(got == ref) > 0.999
+
+
+# Every tiled GEMM configuration built into the library (workgroup tile of
+# (WM*MT*16) rows x ((4/WM)*NT*16) columns), with and without split K, on a
+# ragged shape: several row groups, an odd chunk count, a partial column tile.
+TILED_CONFIGS = [(1, 1, 1), (2, 1, 1), (4, 1, 1), (8, 1, 1), (8, 2, 1), (4, 4, 1), (8, 4, 1),
+                 (2, 2, 2), (4, 2, 2), (2, 4, 2), (4, 4, 2), (1, 4, 4), (2, 4, 4), (2, 2, 4)]
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("mt,nt,wm", TILED_CONFIGS)
+def test_linear_every_tiled_config(mt, nt, wm, splits, monkeypatch):
+    M, K, N = 150, 1152, 400
+    monkeypatch.setenv("FQL_PLAN", f"kind=1,mt={mt},nt={nt},wm={wm},splits={splits}")
+    plan = fql.linear_plan(M, N, K)
+    assert f"MT={mt},NT={nt},WM={wm}>" in plan and f"splits={splits}" in plan, plan
+    _run_case("tiny", M, K, N, 0, True, label=f"tiled<{mt},{nt},{wm}> splits={splits}")
+
+
+# Every LDS-ring GEMM configuration built into the library (workgroup tile of
+# (MT*16) rows x (4*NT*16) columns, ring depth ST), same ragged shape.
+LDS_CONFIGS = [(1, 4, 4), (2, 4, 4), (4, 4, 3), (4, 4, 4), (8, 4, 2), (8, 4, 3), (4, 2, 4),
+               (8, 2, 3), (2, 2, 4), (4, 4, 2), (2, 4, 2), (4, 2, 2), (2, 2, 2)]
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("mt,nt,st", LDS_CONFIGS)
+def test_linear_every_lds_config(mt, nt, st, splits, monkeypatch):
+    M, K, N = 150, 1152, 400
+    monkeypatch.setenv("FQL_PLAN", f"kind=2,mt={mt},nt={nt},st={st},splits={splits}")
+    plan = fql.linear_plan(M, N, K)
+    assert f"gemm_lds_kernel<MT={mt},NT={nt},ST={st}>" in plan and f"splits={splits}" in plan, plan
+    _run_case("tiny", M, K, N, 0, True, label=f"lds<{mt},{nt},{st}> splits={splits}")
