@@ -60,6 +60,7 @@ hipError_t launch_unpack_nvfp4(const uint8_t* packed, int64_t N, int64_t K, uint
 //           16-column tile over the full K, its waves splitting K.
 //   kind 1: quantizer kernel (x_hat in A-fragment order) + tiled GEMM.
 //   kind 2: quantizer kernel + LDS-ring tiled GEMM (direct global->LDS loads).
+//   kind 3: as kind 2 on 32x32x16 MFMAs (mt, nt count 32-row / 32-column tiles).
 // Workspace layout: [arrival counters | x_hat | split-K partial slabs]. The
 // counters must be zero before the first call on a workspace; every call
 // leaves them zero again.
@@ -91,6 +92,7 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned);
 // into the library.
 bool tiled_config_built(int mt, int nt, int wm);
 bool lds_config_built(int mt, int nt, int st);
+bool lds32_config_built(int mt, int nt, int st);
 
 // Kernel name and parameters of a plan (diagnostics).
 std::string describe_plan(const GemmPlan& p);

@@ -94,44 +94,38 @@ __device__ __forceinline__ float4v load_partial(const float4v* p) {
 }
 
 // Write the workgroup's output tile: directly (one split) or through the
-// split-K slab and the last-arriver reduction.
-//   The 4 waves form a WM x (4/WM) grid; wave (wm, wn) holds MT x NT 16x16
-//   accumulator tiles: rows m0 + (wm*MT + mt)*16 + .., cols n0 + (wn*NT + nt)*16 + ..
-//   slab: [splits][4 waves][MT*NT][64 lanes] float4 for this workgroup's tile,
+// split-K slab and the last-arriver reduction. The lane's accumulators come
+// as FR float4 fragments; fragment f element i is the output element at
+// (m0 + row_of(f, i), n0 + col_of(f)).
+//   slab: [splits][4 waves][FR][64 lanes] float4 for this workgroup's tile,
 //   so every lane writes and later sums exactly its own fragments.
-template <int MT, int NT, int WM>
-__device__ __forceinline__ void finish_tile(float4v (&acc)[MT][NT], int M, int N, int m0, int n0,
-                                            int split, int splits, float alpha,
-                                            const uint16_t* __restrict__ bias,
-                                            uint16_t* __restrict__ y, int64_t ldy,
-                                            float4v* __restrict__ slab, uint32_t* counter,
-                                            uint32_t* s_flag) {
-  constexpr int WN = 4 / WM;
-  constexpr int FR = MT * NT;
+template <int FR, typename RowOf, typename ColOf>
+__device__ __forceinline__ void finish_frags(float4v (&frag)[FR], RowOf row_of, ColOf col_of, int M,
+                                             int N, int m0, int n0, int split, int splits,
+                                             float alpha, const uint16_t* __restrict__ bias,
+                                             uint16_t* __restrict__ y, int64_t ldy,
+                                             float4v* __restrict__ slab, uint32_t* counter,
+                                             uint32_t* s_flag) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int col = lane & 15, row0 = 4 * (lane >> 4);
-  auto emit = [&](int mt, int nt, const float4v& s) {
-    const int n = n0 + (wn * NT + nt) * 16 + col;
+  auto emit = [&](int f, const float4v& s) {
+    const int n = n0 + col_of(f);
     if (n >= N) return;
     const float bv = bias ? bf16_bits_to_f32(bias[n]) : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + (wm * MT + mt) * 16 + row0 + i;
+      const int m = m0 + row_of(f, i);
       if (m < M) y[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16_bits(alpha * s[i] + bv);
     }
   };
   if (splits == 1) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) emit(mt, nt, acc[mt][nt]);
+    for (int f = 0; f < FR; ++f) emit(f, frag[f]);
     return;
   }
   float4v* mine = slab + wave * FR * 64 + lane;
   const int64_t zstride = 4 * FR * 64;
 #pragma unroll
-  for (int f = 0; f < FR; ++f) store_partial(mine + split * zstride + f * 64, acc[f / NT][f % NT]);
+  for (int f = 0; f < FR; ++f) store_partial(mine + split * zstride + f * 64, frag[f]);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // partial stores have completed
   __syncthreads();
   if (tid == 0) {
@@ -166,9 +160,59 @@ __device__ __forceinline__ void finish_tile(float4v (&acc)[MT][NT], int M, int N
           for (int f = 0; f < FG; ++f) sum[f] += v[j][f];
     }
 #pragma unroll
-    for (int f = 0; f < FG; ++f) emit((f0 + f) / NT, (f0 + f) % NT, sum[f]);
+    for (int f = 0; f < FG; ++f) emit(f0 + f, sum[f]);
   }
   if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16x16 accumulator tiles: the 4 waves form a WM x (4/WM) grid; wave (wm, wn)
+// holds MT x NT tiles, rows m0 + (wm*MT + mt)*16 + 4*(lane/16) + i, columns
+// n0 + (wn*NT + nt)*16 + lane%16.
+template <int MT, int NT, int WM>
+__device__ __forceinline__ void finish_tile(float4v (&acc)[MT][NT], int M, int N, int m0, int n0,
+                                            int split, int splits, float alpha,
+                                            const uint16_t* __restrict__ bias,
+                                            uint16_t* __restrict__ y, int64_t ldy,
+                                            float4v* __restrict__ slab, uint32_t* counter,
+                                            uint32_t* s_flag) {
+  constexpr int WN = 4 / WM;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  float4v frag[MT * NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) frag[mt * NT + nt] = acc[mt][nt];
+  auto row_of = [&](int f, int i) { return (wm * MT + f / NT) * 16 + 4 * (lane >> 4) + i; };
+  auto col_of = [&](int f) { return (wn * NT + f % NT) * 16 + (lane & 15); };
+  finish_frags<MT * NT>(frag, row_of, col_of, M, N, m0, n0, split, splits, alpha, bias, y, ldy,
+                        slab, counter, s_flag);
+}
+
+// 32x32 accumulator tiles (v_mfma_f32_32x32x16_f16 layout): wave w holds MT x
+// NT tiles; register r of tile (a, b) is row m0 + a*32 + 8*(r/4) + 4*(lane/32)
+// + r%4, column n0 + (w*NT + b)*32 + lane%32.
+template <int MT, int NT>
+__device__ __forceinline__ void finish_tile32(float16v (&acc)[MT][NT], int M, int N, int m0, int n0,
+                                              int split, int splits, float alpha,
+                                              const uint16_t* __restrict__ bias,
+                                              uint16_t* __restrict__ y, int64_t ldy,
+                                              float4v* __restrict__ slab, uint32_t* counter,
+                                              uint32_t* s_flag) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float4v frag[MT * NT * 4];
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        frag[(a * NT + b) * 4 + r4] = float4v{acc[a][b][4 * r4], acc[a][b][4 * r4 + 1],
+                                              acc[a][b][4 * r4 + 2], acc[a][b][4 * r4 + 3]};
+  auto row_of = [&](int f, int i) { return (f / (NT * 4)) * 32 + 8 * (f % 4) + 4 * (lane >> 5) + i; };
+  auto col_of = [&](int f) { return (wave * NT + (f / 4) % NT) * 32 + (lane & 31); };
+  finish_frags<MT * NT * 4>(frag, row_of, col_of, M, N, m0, n0, split, splits, alpha, bias, y, ldy,
+                            slab, counter, s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -562,7 +606,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(
     int kc_per_split, int splits, float alpha, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ y, int64_t ldy, float4v* __restrict__ partial,
     uint32_t* __restrict__ counters) {
-  static_assert(ST >= 2 && ST <= 4, "ring depth");
+  static_assert(ST >= 3 && ST <= 4, "ring depth (chunk i+1 must be issued a whole chunk ahead)");
   constexpr int L = MT + 2 * NT;  // LDS loads per chunk per wave
   static_assert(L * (ST - 2) <= 63, "vmcnt range");
   __shared__ LdsStage<MT, NT> stage[ST];
@@ -596,17 +640,23 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(
   const uint32_t q_voff = lane * 16;
   const uint32_t s_voff = ((lane & 15) * 2 + (lane >> 5)) * 16;
 
-  auto issue = [&](LdsStage<MT, NT>& sg, int64_t c) {
-    c = c < c_end ? c : c_end - 1;  // clamped: a static number of loads per chunk
-#pragma unroll
-    for (int f = 0; f < MT; ++f)
-      lds_load16(a_base + ((int64_t)f * (Kp / 32) + c * 4) * 1024, a_voff, lds_offset(&sg.a[f * 4 + wave][0]));
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+  // LDS load number e (0 <= e < L) of chunk c into stage sg; chunks past the
+  // range are clamped (a static number of loads per chunk)
+  auto issue_one = [&](LdsStage<MT, NT>& sg, int64_t c, int e) {
+    c = c < c_end ? c : c_end - 1;
+    if (e < MT) {
+      lds_load16(a_base + ((int64_t)e * (Kp / 32) + c * 4) * 1024, a_voff, lds_offset(&sg.a[e * 4 + wave][0]));
+    } else if (e < MT + NT) {
+      const int nt = e - MT;
       lds_load16(q_base[nt] + c * 1024, q_voff, lds_offset(&sg.bq[wave * NT + nt][0]));
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    } else {
+      const int nt = e - MT - NT;
       lds_load4(s_base[nt] + (c >> 2) * 512 + (c & 3) * 4, s_voff, lds_offset(&sg.bs[wave * NT + nt][0]));
+    }
+  };
+  auto issue = [&](LdsStage<MT, NT>& sg, int64_t c) {
+#pragma unroll
+    for (int e = 0; e < L; ++e) issue_one(sg, c, e);
   };
 
   float4v acc[MT][NT];
@@ -629,14 +679,22 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(
   uint32_t bsw[NT];
   half8 bf[2][NT];
   uint4v af[2][MT];
-  auto read_head = [&](const LdsStage<MT, NT>& sg) {
+  // the wave's own codes and scales (only its own loads must have landed)
+  auto read_head_b = [&](const LdsStage<MT, NT>& sg) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       bq[nt] = sg.bq[wave * NT + nt][lane];
       bsw[nt] = sg.bs[wave * NT + nt][lane];
     }
+  };
+  // the first step's activation fragments (loaded by all waves)
+  auto read_head_a = [&](const LdsStage<MT, NT>& sg) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) af[0][mt] = sg.a[mt * 4][lane];
+  };
+  auto read_head = [&](const LdsStage<MT, NT>& sg) {
+    read_head_b(sg);
+    read_head_a(sg);
   };
   auto dequant = [&](int buf, int ks) {
 #pragma unroll
@@ -651,13 +709,16 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(
         acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[buf][nt], acc[mt][nt], 0, 0, 0);
     }
   };
-  // steps 0..2 of a chunk held in stage sg
-  auto steps012 = [&](const LdsStage<MT, NT>& sg) {
+  // steps 0..2 of a chunk held in stage sg; refill receives chunk rc's loads,
+  // spread over the steps so that the address unit works while the MFMAs run
+  auto steps012 = [&](const LdsStage<MT, NT>& sg, LdsStage<MT, NT>& refill, int64_t rc) {
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
       const int cur = ks & 1, nxt = cur ^ 1;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) af[nxt][mt] = sg.a[mt * 4 + ks + 1][lane];
+#pragma unroll
+      for (int e = ks * L / 3; e < (ks + 1) * L / 3; ++e) issue_one(refill, rc, e);
       __builtin_amdgcn_sched_barrier(0);
       dequant(nxt, ks + 1);
       mfmas(cur);
@@ -670,27 +731,31 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(
     }
   };
 
-  // prologue: every stage filled, chunk 0's head in registers
+  // prologue: chunks 0 .. ST-2 in flight, chunk 0's head in registers
 #pragma unroll
-  for (int p = 0; p < ST; ++p) issue(stage[p], c_begin + p);
-  wait_vmcnt<L * (ST - 1)>();
+  for (int p = 0; p < ST - 1; ++p) issue(stage[p], c_begin + p);
+  wait_vmcnt<L * (ST - 2)>();
   stage_barrier();
   read_head(stage[0]);
   dequant(0, 0);
   __builtin_amdgcn_sched_barrier(0);
 
-  // chunk i lives in stage i % ST; the loop is unrolled by ST so that every
-  // stage index is a compile-time constant
+  // Ring protocol: chunk i lives in stage i % ST (the loop is unrolled by ST
+  // so that every stage index is a compile-time constant). While chunk i is
+  // computed, stage (i-1) % ST (chunk i-1's, freed by the previous mid-chunk
+  // barrier; for i = 0 the one stage the prologue left empty) receives chunk
+  // i+ST-1. At the mid-chunk barrier of chunk i, chunk i+1 has landed and
+  // everyone has finished reading chunk i's activation fragments.
   for (int i0 = 0; i0 < nch; i0 += ST) {
 #pragma unroll
     for (int j = 0; j < ST; ++j) {
       if (i0 + j < nch) {
-        steps012(stage[j]);
+        steps012(stage[j], stage[(j + ST - 1) % ST], c_begin + i0 + j + ST - 1);
         const bool more = i0 + j + 1 < nch;
         wait_vmcnt<L * (ST - 2)>();  // this wave's loads of chunk i+1 have landed
+        if (more) read_head_b(stage[(j + 1) % ST]);
         stage_barrier();             // everyone's have, and stage j has been read by all
-        issue(stage[j], c_begin + i0 + j + ST);
-        if (more) read_head(stage[(j + 1) % ST]);
+        if (more) read_head_a(stage[(j + 1) % ST]);
         __builtin_amdgcn_sched_barrier(0);
         if (more) dequant(0, 0);
         mfmas(1);
@@ -709,6 +774,217 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(
   float4v* slab = partial + (int64_t)tilegrp * splits * (4 * MT * NT * 64);
   finish_tile<MT, NT, 1>(acc, M, N, mgroup * MT * 16, ngroup * 4 * NT * 16, split, splits, alpha,
                          bias, y, ldy, slab, counters + tilegrp, &s_flag);
+}
+
+// ---------------------------------------------------------------------------
+// LDS-ring tiled kernel on 32x32x16 MFMAs
+// ---------------------------------------------------------------------------
+//
+// Same ring and pipeline as gemm_lds_kernel, with v_mfma_f32_32x32x16_f16:
+// each MFMA is twice the work of a 16x16x32 one for the same operand bytes,
+// so a wave spends half as many issue slots on MFMAs and the dequantization,
+// LDS reads and loads fit between them. One 16-deep K step is exactly one
+// NVFP4 block, so a weight fragment carries a single scale per lane.
+//   Workgroup tile (MT*32) rows x (4*NT*32) columns; wave w owns columns
+//   [w*NT*32, (w+1)*NT*32) and all rows.
+//   A fragment (32 rows x 16 k) of step s: lane l takes row l%32 and
+//   k = 16s + 8*(l/32) + 0..7, i.e. 16-row tile 2a + (l%32)/16, 32-deep step
+//   s/2, quarter kq = 2*(s%2) + l/32 of the x_hat fragment layout.
+//   B fragment (16 k x 32 columns) of step s: lane l takes column l%32 of
+//   the 32-column tile (16-column packed tile 2b + (l%32)/16) and the same k;
+//   its codes are dword s/2 of the packed slot kq*16 + l%16, its scale byte
+//   s/2 of the slot's scale dword (l%16)*2 + s%2 for the chunk.
+// Per chunk and 32-column tile a lane therefore loads two code slots (even
+// and odd steps) and two scale dwords.
+template <int MT, int NT>
+struct LdsStage32 {
+  uint4v a[MT * 2 * 4][64];     // [16-row tile][32-deep step][lane] x_hat fragments
+  uint4v bq[4 * NT * 2][64];    // [wave][32-col tile][even/odd steps][lane] codes
+  uint32_t bs[4 * NT * 2][64];  // [wave][32-col tile][even/odd steps][lane] scales
+};
+
+template <int MT, int NT, int ST, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
+    const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
+    const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, int ngroups,
+    int kc_per_split, int splits, float alpha, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ y, int64_t ldy, float4v* __restrict__ partial,
+    uint32_t* __restrict__ counters) {
+  static_assert(ST >= 3 && ST <= 4, "ring depth (chunk i+1 must be issued a whole chunk ahead)");
+  constexpr int L = 2 * MT + 4 * NT;  // LDS loads per chunk per wave
+  static_assert(L * (ST - 2) <= 63, "vmcnt range");
+  __shared__ LdsStage32<MT, NT> stage[ST];
+  __shared__ uint32_t s_flag;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t KC = Kp / 128;
+  const int64_t KC4 = (KC + 3) / 4;
+  const int split = blockIdx.x % splits;
+  const int tilegrp = blockIdx.x / splits;
+  const int ngroup = tilegrp % ngroups;
+  const int mgroup = tilegrp / ngroups;
+  const int64_t c_begin = (int64_t)split * kc_per_split;
+  const int64_t c_end = c_begin + kc_per_split < KC ? c_begin + kc_per_split : KC;
+  const int nch = (int)(c_end - c_begin);
+  const int tile16_0 = (ngroup * 4 + wave) * NT * 2;  // first packed 16-column tile of the wave
+
+  // wave-uniform global bases; per-lane byte offsets
+  const uint8_t* a_base = reinterpret_cast<const uint8_t*>(xhat) +
+                          ((int64_t)mgroup * MT * 2 * (Kp / 32) + wave) * 1024;
+  const uint32_t a_voff = lane * 16;
+  const int jc = lane & 31, hh = lane >> 5;  // column in the 32-column tile, k half
+  // per-lane offsets of the lane's 16-column packed tile (a tile past the end
+  // is clamped to the last one: read, never stored); the host keeps the
+  // packed blob below 4 GiB so that these 32-bit offsets cannot wrap
+  uint32_t q_voff[NT][2], s_voff[NT][2];
+#pragma unroll
+  for (int b = 0; b < NT; ++b) {
+    int64_t tl = tile16_0 + 2 * b + (jc >> 4);
+    tl = tl < ntiles ? tl : ntiles - 1;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      q_voff[b][e] = (uint32_t)(tl * KC * 1024 + ((2 * e + hh) * 16 + (jc & 15)) * 16);
+      s_voff[b][e] = (uint32_t)(tl * KC4 * 512 + ((jc & 15) * 2 + e) * 16);
+    }
+  }
+
+  // LDS load number e (0 <= e < L) of chunk c into stage sg; chunks past the
+  // range are clamped (a static number of loads per chunk)
+  auto issue_one = [&](LdsStage32<MT, NT>& sg, int64_t c, int e) {
+    c = c < c_end ? c : c_end - 1;
+    if (e < 2 * MT) {
+      lds_load16(a_base + ((int64_t)e * (Kp / 32) + c * 4) * 1024, a_voff, lds_offset(&sg.a[e * 4 + wave][0]));
+    } else if (e < 2 * MT + 2 * NT) {
+      const int b = (e - 2 * MT) / 2, h = (e - 2 * MT) % 2;
+      lds_load16(wcodes + c * 1024, q_voff[b][h], lds_offset(&sg.bq[(wave * NT + b) * 2 + h][0]));
+    } else {
+      const int b = (e - 2 * MT - 2 * NT) / 2, h = (e - 2 * MT - 2 * NT) % 2;
+      lds_load4(wscales + (c >> 2) * 512 + (c & 3) * 4, s_voff[b][h],
+                lds_offset(&sg.bs[(wave * NT + b) * 2 + h][0]));
+    }
+  };
+  auto issue = [&](LdsStage32<MT, NT>& sg, int64_t c) {
+#pragma unroll
+    for (int e = 0; e < L; ++e) issue_one(sg, c, e);
+  };
+
+  float16v acc[MT][NT];
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[a][b] = float16v{};
+
+  // Software pipeline over the eight 16-deep steps of a chunk (see
+  // gemm_lds_kernel): step s issues the LDS reads of step s+1's activation
+  // fragments, then its MFMAs interleaved with step s+1's dequantization;
+  // between steps 6 and 7 the wave moves to the next chunk's stage.
+  constexpr int MFMAS = MT * NT;                              // per step
+  constexpr int VPM = (8 * NT + MFMAS - 1) / MFMAS;           // dequantization VALU per MFMA
+  const int a_lane = ((lane & 31) >> 4) * 4 * 64 + hh * 16 + (lane & 15);  // within a[][] of stage
+  uint4v bq[NT][2];
+  uint32_t bsw[NT][2];
+  half8 bf[2][NT];
+  uint4v af[2][MT];
+  auto a_frag = [&](const LdsStage32<MT, NT>& sg, int a, int s) -> uint4v {
+    return (&sg.a[0][0])[a_lane + ((2 * a) * 4 + (s >> 1)) * 64 + 2 * (s & 1) * 16];
+  };
+  // the wave's own codes and scales (only its own loads must have landed)
+  auto read_head_b = [&](const LdsStage32<MT, NT>& sg) {
+#pragma unroll
+    for (int b = 0; b < NT; ++b)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        bq[b][e] = sg.bq[(wave * NT + b) * 2 + e][lane];
+        bsw[b][e] = sg.bs[(wave * NT + b) * 2 + e][lane];
+      }
+  };
+  // the first step's activation fragments (loaded by all waves)
+  auto read_head_a = [&](const LdsStage32<MT, NT>& sg) {
+#pragma unroll
+    for (int a = 0; a < MT; ++a) af[0][a] = a_frag(sg, a, 0);
+  };
+  auto read_head = [&](const LdsStage32<MT, NT>& sg) {
+    read_head_b(sg);
+    read_head_a(sg);
+  };
+  auto dequant = [&](int buf, int s) {
+#pragma unroll
+    for (int b = 0; b < NT; ++b)
+      bf[buf][b] = b_fragment(dword_of(bq[b][s & 1], s >> 1), ChunkScales(bsw[b][s & 1])[s >> 1]);
+  };
+  auto mfmas = [&](int buf) {
+#pragma unroll
+    for (int a = 0; a < MT; ++a) {
+      const half8 av = __builtin_bit_cast(half8, af[buf][a]);
+#pragma unroll
+      for (int b = 0; b < NT; ++b)
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bf[buf][b], acc[a][b], 0, 0, 0);
+    }
+  };
+  // refill (when given) receives chunk rc's loads, spread over the seven steps
+  // so that the address unit works while the MFMAs run
+  auto steps0to6 = [&](const LdsStage32<MT, NT>& sg, LdsStage32<MT, NT>& refill, int64_t rc) {
+#pragma unroll
+    for (int s = 0; s < 7; ++s) {
+      const int cur = s & 1, nxt = cur ^ 1;
+#pragma unroll
+      for (int a = 0; a < MT; ++a) af[nxt][a] = a_frag(sg, a, s + 1);
+#pragma unroll
+      for (int e = s * L / 7; e < (s + 1) * L / 7; ++e) issue_one(refill, rc, e);
+      __builtin_amdgcn_sched_barrier(0);
+      dequant(nxt, s + 1);
+      mfmas(cur);
+#pragma unroll
+      for (int i = 0; i < MFMAS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // prologue: chunks 0 .. ST-2 in flight, chunk 0's head in registers
+#pragma unroll
+  for (int p = 0; p < ST - 1; ++p) issue(stage[p], c_begin + p);
+  wait_vmcnt<L * (ST - 2)>();
+  stage_barrier();
+  read_head(stage[0]);
+  dequant(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Ring protocol: chunk i lives in stage i % ST. While chunk i is computed,
+  // stage (i-1) % ST (chunk i-1's, freed by the previous mid-chunk barrier;
+  // for i = 0 the one stage the prologue left empty) receives chunk i+ST-1.
+  // At the mid-chunk barrier of chunk i, chunk i+1 has landed and everyone
+  // has finished reading chunk i's activation fragments.
+  for (int i0 = 0; i0 < nch; i0 += ST) {
+#pragma unroll
+    for (int j = 0; j < ST; ++j) {
+      if (i0 + j < nch) {
+        steps0to6(stage[j], stage[(j + ST - 1) % ST], c_begin + i0 + j + ST - 1);
+        const bool more = i0 + j + 1 < nch;
+        wait_vmcnt<L * (ST - 2)>();  // this wave's loads of chunk i+1 have landed
+        if (more) read_head_b(stage[(j + 1) % ST]);
+        stage_barrier();             // everyone's have, and stage j has been read by all
+        if (more) read_head_a(stage[(j + 1) % ST]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) dequant(0, 0);
+        mfmas(1);
+#pragma unroll
+        for (int i = 0; i < MFMAS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i >= MFMAS / 4) __builtin_amdgcn_sched_group_barrier(0x002, VPM + 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+  wait_vmcnt<0>();  // no LDS load may still be in flight when the workgroup ends
+
+  float4v* slab = partial + (int64_t)tilegrp * splits * (4 * MT * NT * 4 * 64);
+  finish_tile32<MT, NT>(acc, M, N, mgroup * MT * 32, ngroup * 4 * NT * 32, split, splits, alpha,
+                        bias, y, ldy, slab, counters + tilegrp, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -793,18 +1069,29 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     // Workgroup tile (WM*MT*16) x ((4/WM)*NT*16); kind 2 always has WM = 1.
     // Defaults (measured on the decode and prefill layer shapes): small M
     // keeps the register-staged tiled kernel; from 33 rows on the LDS-ring
-    // kernel with 64 x 128 tiles (up to 128 rows) or 64 x 256 tiles.
-    p.kind = M <= 32 ? 1 : 2;
-    if (ov.kind == 1 || ov.kind == 2) p.kind = ov.kind;
-    const bool lds_ring = p.kind == 2;
+    // kernel on 32x32 MFMAs.
+    p.kind = M <= 32 ? 1 : 3;
+    if (ov.kind >= 1 && ov.kind <= 3) p.kind = ov.kind;
+    // kind 3 addresses the packed blob with 32-bit per-lane offsets
+    if (p.kind == 3 && d.total_bytes() >= ((int64_t)1 << 32)) p.kind = 2;
+    const bool lds_ring = p.kind >= 2;
     p.wm = 1;
-    p.st = 2;
+    p.st = 3;
     if (!lds_ring) {
       if (M <= 16) { p.mt = 1; p.nt = 1; }
       else if (M <= 32) { p.mt = 2; p.nt = 1; }
       else if (M <= 64) { p.mt = 2; p.nt = 2; p.wm = 2; }
       else if (M <= 128) { p.mt = 4; p.nt = 2; p.wm = 2; }
       else { p.mt = 8; p.nt = 4; }
+    } else if (p.kind == 3) {  // 32x32 tiles: MT x 32 rows, 4 x NT x 32 columns
+      if (M <= 128) {
+        // 128 x 128 tiles when they alone fill the GPU, else 64 x 128 tiles
+        // with a deeper ring and split K
+        p.mt = 4; p.nt = 1; p.st = 3;
+        if ((M + 127) / 128 * ((ntiles + 7) / 8) < 192) { p.mt = 2; p.st = 4; }
+      } else {
+        p.mt = 4; p.nt = 2; p.st = 3;
+      }
     } else if (M <= 128) {
       p.mt = 4; p.nt = 2;
     } else {
@@ -816,12 +1103,16 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
       if (ov.wm && !lds_ring) p.wm = ov.wm;
       if (ov.st) p.st = ov.st;
     }
-    if (lds_ring ? !lds_config_built(p.mt, p.nt, p.st) : !tiled_config_built(p.mt, p.nt, p.wm)) {
-      p.kind = 1; p.mt = 1; p.nt = 1; p.wm = 1;
-    }
-    p.Mp = round_up(M, 16 * p.mt * p.wm);
-    const int64_t ngroups = (ntiles + (4 / p.wm) * p.nt - 1) / ((4 / p.wm) * p.nt);
-    const int64_t mgroups = p.Mp / (16 * p.mt * p.wm);
+    const bool built = p.kind == 3   ? lds32_config_built(p.mt, p.nt, p.st)
+                       : p.kind == 2 ? lds_config_built(p.mt, p.nt, p.st)
+                                     : tiled_config_built(p.mt, p.nt, p.wm);
+    if (!built) { p.kind = 1; p.mt = 1; p.nt = 1; p.wm = 1; }
+    // rows and 16-column tiles per workgroup
+    const int tile_rows = p.kind == 3 ? 32 * p.mt : 16 * p.mt * p.wm;
+    const int tile_cols16 = p.kind == 3 ? 8 * p.nt : (4 / p.wm) * p.nt;
+    p.Mp = round_up(M, tile_rows);
+    const int64_t ngroups = (ntiles + tile_cols16 - 1) / tile_cols16;
+    const int64_t mgroups = p.Mp / tile_rows;
     const int64_t groups = ngroups * mgroups;
     // Split K across workgroups only when there are too few output tiles to
     // occupy the GPU: the arrival counter of the split-K reduction costs
@@ -837,7 +1128,9 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     p.ngroups = ngroups;
     p.xhat_bytes = round_up(p.Mp * p.Kp * 2, 256);
   }
-  const int64_t slab = (int64_t)p.splits * 4 * p.mt * p.nt * 64 * 16;  // [splits][4 waves][MT*NT][64] float4
+  // [splits][4 waves][fragments][64 lanes] float4 per output tile
+  const int64_t frags = (int64_t)p.mt * p.nt * (p.kind == 3 ? 4 : 1);
+  const int64_t slab = (int64_t)p.splits * 4 * frags * 64 * 16;
   p.partial_bytes = p.splits > 1 ? round_up(p.groups * slab, 256) : 0;
   p.counter_bytes = kCounterBytes;
   p.total_bytes = p.counter_bytes + p.xhat_bytes + p.partial_bytes;
@@ -846,7 +1139,11 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
 
 std::string describe_plan(const GemmPlan& p) {
   char b[256];
-  if (p.kind == 2) {
+  if (p.kind == 3) {
+    std::snprintf(b, sizeof(b),
+                  "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d> grid=%lld splits=%d",
+                  p.mt, p.nt, p.st, (long long)(p.groups * p.splits), p.splits);
+  } else if (p.kind == 2) {
     std::snprintf(b, sizeof(b),
                   "quant_nvfp4_xhat_kernel + gemm_lds_kernel<MT=%d,NT=%d,ST=%d> grid=%lld splits=%d",
                   p.mt, p.nt, p.st, (long long)(p.groups * p.splits), p.splits);
@@ -938,12 +1235,37 @@ static hipError_t launch_lds_t(const GemmPlan& p, const _Float16* xhat, const ui
 // The (MT, NT, ST, OCC) LDS-ring configurations built into the library
 // (OCC: workgroups per CU the register and LDS budgets are sized for).
 #define FQL_LDS_CONFIGS(X) \
-  X(1, 4, 4, 1) X(2, 4, 4, 1) X(4, 4, 3, 1) X(4, 4, 4, 1) X(8, 4, 2, 1) X(8, 4, 3, 1) X(4, 2, 4, 1) \
-  X(8, 2, 3, 1) X(2, 2, 4, 1) X(4, 4, 2, 2) X(2, 4, 2, 2) X(4, 2, 2, 2) X(2, 2, 2, 2)
+  X(1, 4, 4, 1) X(2, 4, 4, 1) X(4, 4, 3, 1) X(4, 4, 4, 1) X(8, 4, 3, 1) X(4, 2, 4, 1) X(8, 2, 3, 1) \
+  X(2, 2, 4, 1) X(4, 2, 3, 2) X(2, 4, 3, 1) X(2, 2, 3, 2)
 
 bool lds_config_built(int mt, int nt, int st) {
 #define FQL_X(A, B, C, D) if (mt == A && nt == B && st == C) return true;
   FQL_LDS_CONFIGS(FQL_X)
+#undef FQL_X
+  return false;
+}
+
+template <int MT, int NT, int ST, int OCC>
+static hipError_t launch_lds32_t(const GemmPlan& p, const _Float16* xhat, const uint8_t* packed,
+                                 int64_t M, int64_t N, float alpha, const uint16_t* bias,
+                                 uint16_t* y, int64_t ldy, float4v* partial, uint32_t* counters,
+                                 hipStream_t st) {
+  const uint8_t* wcodes = packed;
+  const uint8_t* wscales = packed + p.Np * p.Kp / 2;
+  gemm_lds32_kernel<MT, NT, ST, OCC><<<(unsigned)(p.groups * p.splits), 256, 0, st>>>(
+      xhat, wcodes, wscales, (int)M, (int)N, p.Kp, (int)(p.Np / 16), (int)p.ngroups,
+      p.kc_per_split, p.splits, alpha, bias, y, ldy, partial, counters);
+  return hipGetLastError();
+}
+
+// The (MT, NT, ST, OCC) 32x32 LDS-ring configurations built into the library.
+#define FQL_LDS32_CONFIGS(X) \
+  X(4, 2, 3, 1) X(4, 1, 3, 1) X(2, 2, 4, 1) X(2, 2, 3, 2) X(2, 1, 4, 2) X(2, 1, 3, 2) X(1, 2, 4, 2) \
+  X(1, 2, 3, 2)
+
+bool lds32_config_built(int mt, int nt, int st) {
+#define FQL_X(A, B, C, D) if (mt == A && nt == B && st == C) return true;
+  FQL_LDS32_CONFIGS(FQL_X)
 #undef FQL_X
   return false;
 }
@@ -978,6 +1300,14 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
   hipError_t e = launch_quant_nvfp4_xhat(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp, xhat, st);
   if (e != hipSuccess) return e;
   float4v* partial4 = reinterpret_cast<float4v*>(partial);
+  if (p.kind == 3) {
+#define FQL_X(A, B, C, D)                                                                        \
+  if (p.mt == A && p.nt == B && p.st == C)                                                       \
+    return launch_lds32_t<A, B, C, D>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial4, counters, st);
+    FQL_LDS32_CONFIGS(FQL_X)
+#undef FQL_X
+    return hipErrorInvalidValue;
+  }
   if (p.kind == 2) {
 #define FQL_X(A, B, C, D)                                                                        \
   if (p.mt == A && p.nt == B && p.st == C)                                                       \

@@ -195,8 +195,8 @@ def test_linear_every_tiled_config(mt, nt, wm, splits, monkeypatch):
 
 # Every LDS-ring GEMM configuration built into the library (workgroup tile of
 # (MT*16) rows x (4*NT*16) columns, ring depth ST), same ragged shape.
-LDS_CONFIGS = [(1, 4, 4), (2, 4, 4), (4, 4, 3), (4, 4, 4), (8, 4, 2), (8, 4, 3), (4, 2, 4),
-               (8, 2, 3), (2, 2, 4), (4, 4, 2), (2, 4, 2), (4, 2, 2), (2, 2, 2)]
+LDS_CONFIGS = [(1, 4, 4), (2, 4, 4), (4, 4, 3), (4, 4, 4), (8, 4, 3), (4, 2, 4), (8, 2, 3),
+               (2, 2, 4), (4, 2, 3), (2, 4, 3), (2, 2, 3)]
 
 
 @pytest.mark.parametrize("splits", [1, 3])
@@ -207,3 +207,18 @@ def test_linear_every_lds_config(mt, nt, st, splits, monkeypatch):
     plan = fql.linear_plan(M, N, K)
     assert f"gemm_lds_kernel<MT={mt},NT={nt},ST={st}>" in plan and f"splits={splits}" in plan, plan
     _run_case("tiny", M, K, N, 0, True, label=f"lds<{mt},{nt},{st}> splits={splits}")
+
+
+# Every 32x32-MFMA LDS-ring configuration (workgroup tile (MT*32) rows x
+# (4*NT*32) columns), same ragged shape (N = 400 leaves half a 32-column tile).
+LDS32_CONFIGS = [(4, 2, 3), (4, 1, 3), (2, 2, 4), (2, 2, 3), (2, 1, 4), (2, 1, 3), (1, 2, 4), (1, 2, 3)]
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("mt,nt,st", LDS32_CONFIGS)
+def test_linear_every_lds32_config(mt, nt, st, splits, monkeypatch):
+    M, K, N = 150, 1152, 400
+    monkeypatch.setenv("FQL_PLAN", f"kind=3,mt={mt},nt={nt},st={st},splits={splits}")
+    plan = fql.linear_plan(M, N, K)
+    assert f"gemm_lds32_kernel<MT={mt},NT={nt},ST={st}>" in plan and f"splits={splits}" in plan, plan
+    _run_case("tiny", M, K, N, 0, True, label=f"lds32<{mt},{nt},{st}> splits={splits}")
