@@ -41,12 +41,21 @@ __all__ = [
     "linear_nvfp4",
     "NVFP4Weight",
     "HADAMARD_BLOCKS",
+    "quant_mxfp4",
+    "quant_mxfp4_weight",
+    "packed_mxfp4_bytes",
+    "pack_weight_mxfp4",
+    "linear_mxfp4_workspace_bytes",
+    "linear_mxfp4_plan",
+    "linear_mxfp4",
+    "MXFP4Weight",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfql.so")
 HADAMARD_BLOCKS = (0, 16, 32, 64, 128)
 FMT_NVFP4 = 1
+FMT_MXFP4 = 2
 
 _c_int, _c_i64, _c_f32, _c_vp, _c_sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_float,
                                          ctypes.c_void_p, ctypes.c_size_t)
@@ -68,6 +77,14 @@ SIGNATURES = {
     "fql_linear_nvfp4_describe": (_c_int, [_c_i64, _c_i64, _c_i64, _c_int, ctypes.c_char_p, _c_sz]),
     "fql_linear_nvfp4": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_int, _c_vp, _c_i64,
                                   _c_f32, _c_vp, _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fql_quant_mxfp4": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "fql_quant_mxfp4_f32": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "fql_packed_mxfp4_bytes": (_c_int, [_c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+    "fql_pack_weight_mxfp4": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fql_linear_mxfp4_workspace_bytes": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+    "fql_linear_mxfp4_describe": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_char_p, _c_sz]),
+    "fql_linear_mxfp4": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_f32, _c_vp,
+                                  _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
 }
 
 
@@ -145,9 +162,9 @@ def is_supported(device=0):
     return bool(r), buf.value.decode()
 
 
-def can_implement(N, K, hadamard_block=0):
+def can_implement(N, K, hadamard_block=0, fmt=FMT_NVFP4):
     buf = ctypes.create_string_buffer(256)
-    r = _check(lib().fql_can_implement(FMT_NVFP4, int(N), int(K), int(hadamard_block), buf, 256))
+    r = _check(lib().fql_can_implement(int(fmt), int(N), int(K), int(hadamard_block), buf, 256))
     return bool(r), buf.value.decode()
 
 
@@ -341,6 +358,113 @@ def linear_nvfp4(x, weight, alpha=None, bias=None, out=None, workspace=None):
         workspace = _workspace(x.device, need)
     _check(lib().fql_linear_nvfp4(_ptr(x2), M, K, ld, weight.input_global_scale,
                                   weight.hadamard_block, _ptr(weight.packed), N, float(alpha),
+                                  _ptr(bias), _ptr(y2), ldy, _ptr(workspace), workspace.numel(),
+                                  _stream(x.device)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 (E2M1 + one E8M0 scale per 32, no global scale)
+# ---------------------------------------------------------------------------
+
+def _quant_mx(x, name, dtype, fn):
+    _require_cuda(x, name)
+    if x.dtype != dtype:
+        raise FQLError(f"{name} must be {dtype}")
+    x2, ld = _rows_view(x, name)
+    M, K = x2.shape
+    lead = tuple(x.shape[:-1])
+    codes = torch.empty(lead + (K // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(lead + (K // 32,), dtype=torch.uint8, device=x.device)
+    _check(fn(_ptr(x2), M, K, ld, _ptr(codes), _ptr(scales), _stream(x.device)))
+    return codes, scales
+
+
+def quant_mxfp4(x):
+    """Quantize bf16 x [..., K] to MXFP4: (codes uint8 [..., K/2], scales uint8 [..., K/32])."""
+    return _quant_mx(x, "x", torch.bfloat16, lib().fql_quant_mxfp4)
+
+
+def quant_mxfp4_weight(w):
+    """Quantize float32 weights w [N, K] to MXFP4 (codes, scales)."""
+    return _quant_mx(w, "w", torch.float32, lib().fql_quant_mxfp4_f32)
+
+
+def packed_mxfp4_bytes(N, K):
+    n = ctypes.c_size_t()
+    _check(lib().fql_packed_mxfp4_bytes(int(N), int(K), ctypes.byref(n)))
+    return n.value
+
+
+def pack_weight_mxfp4(codes, scales, out=None):
+    """Re-lay canonical MXFP4 weight (codes [N, K/2], scales [N, K/32]) for the GEMM."""
+    _require_cuda(codes, "codes")
+    N, K = codes.shape[0], codes.shape[1] * 2
+    if not (codes.is_contiguous() and scales.is_contiguous()):
+        raise FQLError("codes and scales must be contiguous")
+    if tuple(scales.shape) != (N, K // 32):
+        raise FQLError("scales must be [N, K/32]")
+    nbytes = packed_mxfp4_bytes(N, K)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    _check(lib().fql_pack_weight_mxfp4(_ptr(codes), _ptr(scales), N, K, _ptr(out), out.numel(),
+                                       _stream(codes.device)))
+    return out
+
+
+class MXFP4Weight:
+    """A packed MXFP4 weight [N, K] (uint8 device buffer from pack_weight_mxfp4)."""
+
+    def __init__(self, packed, N, K):
+        self.packed = packed
+        self.N, self.K = int(N), int(K)
+
+    @classmethod
+    def from_float(cls, w):
+        """Quantize and pack a float32 weight [N, K] on the GPU."""
+        codes, scales = quant_mxfp4_weight(w)
+        return cls(pack_weight_mxfp4(codes, scales), w.shape[0], w.shape[1])
+
+    def repack_(self, codes, scales):
+        """Re-pack new canonical weights into the same storage (address kept)."""
+        pack_weight_mxfp4(codes, scales, out=self.packed)
+        return self
+
+
+def linear_mxfp4_workspace_bytes(M, N, K):
+    n = ctypes.c_size_t()
+    _check(lib().fql_linear_mxfp4_workspace_bytes(int(M), int(N), int(K), ctypes.byref(n)))
+    return n.value
+
+
+def linear_mxfp4_plan(M, N, K):
+    """One-line description of the MXFP4 launch plan for this shape."""
+    buf = ctypes.create_string_buffer(256)
+    _check(lib().fql_linear_mxfp4_describe(int(M), int(N), int(K), buf, 256))
+    return buf.value.decode()
+
+
+def linear_mxfp4(x, weight, alpha=1.0, bias=None, out=None, workspace=None):
+    """y = bf16(alpha * mxfp4(x) @ W^T + bias) for bf16 x [..., K]; returns [..., N]."""
+    _require_cuda(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise FQLError("linear_mxfp4 takes bfloat16 activations")
+    if x.shape[-1] != weight.K:
+        raise FQLError(f"x has K={x.shape[-1]}, weight has K={weight.K}")
+    x2, ld = _rows_view(x, "x")
+    M, K = x2.shape
+    N = weight.N
+    if bias is not None:
+        _require_cuda(bias, "bias")
+        if bias.dtype != torch.bfloat16 or bias.numel() != N or not bias.is_contiguous():
+            raise FQLError("bias must be a contiguous bf16 tensor of N elements")
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=torch.bfloat16, device=x.device)
+    y2, ldy = _rows_view(out, "out")
+    need = linear_mxfp4_workspace_bytes(M, N, K)
+    if workspace is None:
+        workspace = _workspace(x.device, need)
+    _check(lib().fql_linear_mxfp4(_ptr(x2), M, K, ld, _ptr(weight.packed), N, float(alpha),
                                   _ptr(bias), _ptr(y2), ldy, _ptr(workspace), workspace.numel(),
                                   _stream(x.device)))
     return out

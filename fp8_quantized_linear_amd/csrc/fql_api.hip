@@ -60,6 +60,17 @@ int check_nvfp4_shape(int64_t rows, int64_t K, int64_t ld, int hb, const char* r
   return FQL_OK;
 }
 
+// MXFP4 shape checks (32-element blocks, no rotation).
+int check_mx_shape(int64_t rows, int64_t K, int64_t ld, const char* rows_name) {
+  if (rows < 1) return fail(FQL_ERR_INVALID, "%s must be >= 1 (got %lld)", rows_name, (long long)rows);
+  if (K < 32 || K % 32 != 0)
+    return fail(FQL_ERR_INVALID, "K must be a positive multiple of 32 (got %lld)", (long long)K);
+  if (ld < K) return fail(FQL_ERR_INVALID, "row stride %lld is smaller than K %lld", (long long)ld, (long long)K);
+  if (K > (int64_t)1 << 24 || rows > (int64_t)1 << 24)
+    return fail(FQL_ERR_INVALID, "dimension too large");
+  return FQL_OK;
+}
+
 bool aligned16(const void* p, int64_t ld, int64_t elem_bytes) {
   return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((ld * elem_bytes) % 16 == 0);
 }
@@ -108,11 +119,19 @@ int fql_is_supported(int device, char* reason, size_t reason_len) {
 int fql_can_implement(int format, int64_t N, int64_t K, int hadamard_block, char* reason,
                       size_t reason_len) {
   std::string why;
-  if (format != FQL_FMT_NVFP4) why = "unknown format";
-  else if (N < 1) why = "N must be >= 1";
-  else if (K < 16 || K % 16 != 0) why = "K must be a positive multiple of 16 (the NVFP4 block)";
-  else if (!valid_hadamard(hadamard_block)) why = "hadamard_block must be 0, 16, 32, 64 or 128";
-  else if (hadamard_block > 0 && K % hadamard_block != 0) why = "K must be a multiple of hadamard_block";
+  if (format == FQL_FMT_NVFP4) {
+    if (N < 1) why = "N must be >= 1";
+    else if (K < 16 || K % 16 != 0) why = "K must be a positive multiple of 16 (the NVFP4 block)";
+    else if (!valid_hadamard(hadamard_block)) why = "hadamard_block must be 0, 16, 32, 64 or 128";
+    else if (hadamard_block > 0 && K % hadamard_block != 0) why = "K must be a multiple of hadamard_block";
+  } else if (format == FQL_FMT_MXFP4) {
+    if (N < 1) why = "N must be >= 1";
+    else if (K < 32 || K % 32 != 0) why = "K must be a positive multiple of 32 (the MX block)";
+    else if (hadamard_block != 0) why = "MXFP4 layers take no rotation (hadamard_block must be 0)";
+  } else {
+    why = "unknown format";
+  }
+  if (why.empty() && (N > (int64_t)1 << 24 || K > (int64_t)1 << 24)) why = "dimension too large";
   write_reason(reason, reason_len, why);
   ok();
   return why.empty() ? 1 : 0;
@@ -238,6 +257,97 @@ int fql_linear_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float inp
       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), ldy,
       static_cast<uint8_t*>(workspace), st);
   return hip_status(e, "linear launch");
+}
+
+// ---- MXFP4 ----------------------------------------------------------------
+
+int fql_quant_mxfp4(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
+                    uint8_t* scales, void* stream) {
+  if (int r = check_mx_shape(M, K, ldx, "M")) return r;
+  if (!x || !codes || !scales) return fail(FQL_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(codes) % 4 != 0)
+    return fail(FQL_ERR_INVALID, "codes must be 4-byte aligned");
+  if (M * (K / 32) > ((int64_t)1 << 31) - 256) return fail(FQL_ERR_INVALID, "too many blocks");
+  return hip_status(fql::launch_quant_mxfp4_bf16(static_cast<const uint16_t*>(x), M, K, ldx, codes,
+                                                 scales, static_cast<hipStream_t>(stream)),
+                    "quant_mxfp4 launch");
+}
+
+int fql_quant_mxfp4_f32(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* codes,
+                        uint8_t* scales, void* stream) {
+  if (int r = check_mx_shape(N, K, ldw, "N")) return r;
+  if (!w || !codes || !scales) return fail(FQL_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(codes) % 4 != 0)
+    return fail(FQL_ERR_INVALID, "codes must be 4-byte aligned");
+  if (N * (K / 32) > ((int64_t)1 << 31) - 256) return fail(FQL_ERR_INVALID, "too many blocks");
+  return hip_status(fql::launch_quant_mxfp4_f32(w, N, K, ldw, codes, scales,
+                                                static_cast<hipStream_t>(stream)),
+                    "quant_mxfp4_f32 launch");
+}
+
+int fql_packed_mxfp4_bytes(int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(FQL_ERR_INVALID, "null pointer");
+  if (int r = check_mx_shape(N, K, K, "N")) return r;
+  *bytes = (size_t)fql::mx_dims(N, K).total_bytes();
+  return ok();
+}
+
+int fql_pack_weight_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                          void* packed, size_t packed_bytes, void* stream) {
+  if (int r = check_mx_shape(N, K, K, "N")) return r;
+  if (!codes || !scales || !packed) return fail(FQL_ERR_INVALID, "null pointer");
+  const size_t need = (size_t)fql::mx_dims(N, K).total_bytes();
+  if (packed_bytes < need)
+    return fail(FQL_ERR_INVALID, "packed buffer holds %zu bytes, %zu needed", packed_bytes, need);
+  if (reinterpret_cast<uintptr_t>(packed) % 16 != 0 || reinterpret_cast<uintptr_t>(codes) % 16 != 0)
+    return fail(FQL_ERR_INVALID, "codes and the packed buffer must be 16-byte aligned");
+  if (need >= ((size_t)1 << 32)) return fail(FQL_ERR_INVALID, "packed weight above 4 GiB");
+  return hip_status(fql::launch_pack_mxfp4(codes, scales, N, K, static_cast<uint8_t*>(packed),
+                                           static_cast<hipStream_t>(stream)),
+                    "pack_mxfp4 launch");
+}
+
+int fql_linear_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(FQL_ERR_INVALID, "null pointer");
+  if (M < 1 || N < 1 || K < 32 || K % 32 != 0)
+    return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 32");
+  *bytes = (size_t)fql::plan_gemm_mxfp4(M, N, K).total_bytes;
+  return ok();
+}
+
+int fql_linear_mxfp4_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t buf_len) {
+  if (M < 1 || N < 1 || K < 32 || K % 32 != 0)
+    return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 32");
+  write_reason(buf, buf_len, fql::describe_mx_plan(fql::plan_gemm_mxfp4(M, N, K)));
+  return ok();
+}
+
+int fql_linear_mxfp4(const void* x, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
+                     int64_t N, float alpha, const void* bias, void* y, int64_t ldy,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (int r = check_mx_shape(M, K, ldx, "M")) return r;
+  if (!std::isfinite(alpha)) return fail(FQL_ERR_INVALID, "alpha must be finite");
+  if (N < 1 || N > (int64_t)1 << 24) return fail(FQL_ERR_INVALID, "N out of range");
+  if (ldy < N) return fail(FQL_ERR_INVALID, "ldy %lld is smaller than N %lld", (long long)ldy, (long long)N);
+  if (!x || !w_packed || !y || !workspace) return fail(FQL_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(w_packed) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(FQL_ERR_INVALID, "packed weight must be 16-byte and workspace 256-byte aligned");
+  if (fql::mx_dims(N, K).total_bytes() >= ((int64_t)1 << 32))
+    return fail(FQL_ERR_INVALID, "packed weight above 4 GiB");
+  const fql::MxPlan plan = fql::plan_gemm_mxfp4(M, N, K);
+  if (plan.Mp * (fql::mx_dims(N, K).Kp / 32) > ((int64_t)1 << 31) - 256)
+    return fail(FQL_ERR_INVALID, "activation too large (M * K / 32 blocks)");
+  if (workspace_bytes < (size_t)plan.total_bytes)
+    return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
+                (long long)plan.total_bytes);
+  if (plan.groups > plan.counter_bytes / 4)
+    return fail(FQL_ERR_INVALID, "too many output tiles for the arrival counters");
+  hipError_t e = fql::launch_linear_mxfp4(
+      plan, static_cast<const uint16_t*>(x), M, K, ldx, static_cast<const uint8_t*>(w_packed), N,
+      alpha, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), ldy,
+      static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream));
+  return hip_status(e, "linear_mxfp4 launch");
 }
 
 }  // extern "C"

@@ -1,0 +1,208 @@
+// Pieces shared by the GEMM kernels: weight-fragment dequantization, direct
+// global->LDS loads with explicit completion waits, the workgroup barrier
+// used by the LDS rings, and the split-K epilogue.
+#pragma once
+
+#include "fql_device.h"
+#include "fql_quant.h"
+
+namespace fql {
+
+// B fragment for one 32-deep K step of one 16-column tile: eight codes times
+// their block scale (already float16).
+__device__ __forceinline__ half8 b_fragment(uint32_t codes, _Float16 sh) {
+  const half2v s2 = {sh, sh};
+  uint32_t hw[4];
+  dequant8_f16(codes, s2, hw);
+  return __builtin_bit_cast(half8, uint4v{hw[0], hw[1], hw[2], hw[3]});
+}
+
+// The four K steps' scales of one chunk (one dword, byte j = step j) as float16.
+struct ChunkScales {
+  half2v lo, hi;
+  __device__ __forceinline__ explicit ChunkScales(uint32_t w) { e4m3x4_to_f16(w, lo, hi); }
+  __device__ __forceinline__ _Float16 operator[](int ks) const {
+    return ks == 0 ? lo[0] : ks == 1 ? lo[1] : ks == 2 ? hi[0] : hi[1];
+  }
+};
+
+__device__ __forceinline__ uint32_t dword_of(const uint4v& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Split-K partials are exchanged between workgroups that may sit on different
+// XCDs (each with its own L2), so they are written and read with agent-scope
+// relaxed atomics, which on gfx950 write through / read past the L2s to the
+// device coherence point. Waiting for the stores to complete before the
+// arrival increment orders them without any whole-cache write-back or
+// invalidate. Each lane moves its accumulator fragment as two 8-byte words.
+__device__ __forceinline__ void store_partial(float4v* p, const float4v& v) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(p);
+  __hip_atomic_store(q, __builtin_bit_cast(uint64_t, float2v{v[0], v[1]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, __builtin_bit_cast(uint64_t, float2v{v[2], v[3]}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float4v load_partial(const float4v* p) {
+  uint64_t* q = const_cast<uint64_t*>(reinterpret_cast<const uint64_t*>(p));
+  const float2v a = __builtin_bit_cast(float2v, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const float2v b = __builtin_bit_cast(float2v, __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return float4v{a[0], a[1], b[0], b[1]};
+}
+
+// Write the workgroup's output tile: directly (one split) or through the
+// split-K slab and the last-arriver reduction. The lane's accumulators come
+// as FR float4 fragments; fragment f element i is the output element at
+// (m0 + row_of(f, i), n0 + col_of(f)).
+//   slab: [splits][4 waves][FR][64 lanes] float4 for this workgroup's tile,
+//   so every lane writes and later sums exactly its own fragments.
+template <int FR, typename RowOf, typename ColOf>
+__device__ __forceinline__ void finish_frags(float4v (&frag)[FR], RowOf row_of, ColOf col_of, int M,
+                                             int N, int m0, int n0, int split, int splits,
+                                             float alpha, const uint16_t* __restrict__ bias,
+                                             uint16_t* __restrict__ y, int64_t ldy,
+                                             float4v* __restrict__ slab, uint32_t* counter,
+                                             uint32_t* s_flag) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto emit = [&](int f, const float4v& s) {
+    const int n = n0 + col_of(f);
+    if (n >= N) return;
+    const float bv = bias ? bf16_bits_to_f32(bias[n]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + row_of(f, i);
+      if (m < M) y[(int64_t)m * ldy + n] = (uint16_t)f32_to_bf16_bits(alpha * s[i] + bv);
+    }
+  };
+  if (splits == 1) {
+#pragma unroll
+    for (int f = 0; f < FR; ++f) emit(f, frag[f]);
+    return;
+  }
+  float4v* mine = slab + wave * FR * 64 + lane;
+  const int64_t zstride = 4 * FR * 64;
+#pragma unroll
+  for (int f = 0; f < FR; ++f) store_partial(mine + split * zstride + f * 64, frag[f]);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // partial stores have completed
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t arrived =
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = arrived == (uint32_t)(splits - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (*s_flag == 0u) return;
+  // Sum in split order, FG fragments at a time. ZB splits' fragments are
+  // loaded per round, all issued before any is used (clamped split index: a
+  // static number of loads), so a round costs one memory round trip.
+  constexpr int FG = FR < 8 ? FR : 8;
+  constexpr int ZB = 16 / FG < 8 ? 16 / FG : 8;
+#pragma unroll
+  for (int f0 = 0; f0 < FR; f0 += FG) {
+    float4v sum[FG];
+#pragma unroll
+    for (int f = 0; f < FG; ++f) sum[f] = float4v{0.f, 0.f, 0.f, 0.f};
+    for (int z0 = 0; z0 < splits; z0 += ZB) {
+      float4v v[ZB][FG];
+#pragma unroll
+      for (int j = 0; j < ZB; ++j) {
+        const int z = z0 + j < splits ? z0 + j : splits - 1;
+#pragma unroll
+        for (int f = 0; f < FG; ++f) v[j][f] = load_partial(mine + z * zstride + (f0 + f) * 64);
+      }
+#pragma unroll
+      for (int j = 0; j < ZB; ++j)
+        if (z0 + j < splits)
+#pragma unroll
+          for (int f = 0; f < FG; ++f) sum[f] += v[j][f];
+    }
+#pragma unroll
+    for (int f = 0; f < FG; ++f) emit(f0 + f, sum[f]);
+  }
+  if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16x16 accumulator tiles: the 4 waves form a WM x (4/WM) grid; wave (wm, wn)
+// holds MT x NT tiles, rows m0 + (wm*MT + mt)*16 + 4*(lane/16) + i, columns
+// n0 + (wn*NT + nt)*16 + lane%16.
+template <int MT, int NT, int WM>
+__device__ __forceinline__ void finish_tile(float4v (&acc)[MT][NT], int M, int N, int m0, int n0,
+                                            int split, int splits, float alpha,
+                                            const uint16_t* __restrict__ bias,
+                                            uint16_t* __restrict__ y, int64_t ldy,
+                                            float4v* __restrict__ slab, uint32_t* counter,
+                                            uint32_t* s_flag) {
+  constexpr int WN = 4 / WM;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  float4v frag[MT * NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) frag[mt * NT + nt] = acc[mt][nt];
+  auto row_of = [&](int f, int i) { return (wm * MT + f / NT) * 16 + 4 * (lane >> 4) + i; };
+  auto col_of = [&](int f) { return (wn * NT + f % NT) * 16 + (lane & 15); };
+  finish_frags<MT * NT>(frag, row_of, col_of, M, N, m0, n0, split, splits, alpha, bias, y, ldy,
+                        slab, counter, s_flag);
+}
+
+// 32x32 accumulator tiles (v_mfma_f32_32x32x16_f16 layout): wave w holds MT x
+// NT tiles; register r of tile (a, b) is row m0 + a*32 + 8*(r/4) + 4*(lane/32)
+// + r%4, column n0 + (w*NT + b)*32 + lane%32.
+template <int MT, int NT>
+__device__ __forceinline__ void finish_tile32(float16v (&acc)[MT][NT], int M, int N, int m0, int n0,
+                                              int split, int splits, float alpha,
+                                              const uint16_t* __restrict__ bias,
+                                              uint16_t* __restrict__ y, int64_t ldy,
+                                              float4v* __restrict__ slab, uint32_t* counter,
+                                              uint32_t* s_flag) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float4v frag[MT * NT * 4];
+#pragma unroll
+  for (int a = 0; a < MT; ++a)
+#pragma unroll
+    for (int b = 0; b < NT; ++b)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        frag[(a * NT + b) * 4 + r4] = float4v{acc[a][b][4 * r4], acc[a][b][4 * r4 + 1],
+                                              acc[a][b][4 * r4 + 2], acc[a][b][4 * r4 + 3]};
+  auto row_of = [&](int f, int i) { return (f / (NT * 4)) * 32 + 8 * (f % 4) + 4 * (lane >> 5) + i; };
+  auto col_of = [&](int f) { return (wave * NT + (f / 4) % NT) * 32 + (lane & 31); };
+  finish_frags<MT * NT * 4>(frag, row_of, col_of, M, N, m0, n0, split, splits, alpha, bias, y, ldy,
+                            slab, counter, s_flag);
+}
+
+// Direct global -> LDS loads. The loads are issued with inline assembly and
+// waited for with explicit s_waitcnt vmcnt(n): the compiler does not track
+// LDS-DMA completion per ring stage and would otherwise wait for the whole
+// ring before every LDS read.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void_t*)(p);
+}
+// 16 (or 4) bytes per lane from sbase + voff into LDS at lds + lane * 16 (or 4).
+// sbase and lds must be wave-uniform.
+__device__ __forceinline__ void lds_load16(const void* sbase, uint32_t voff, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);  // uniform by contract; keeps it in an SGPR
+  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+                   : "memory");
+}
+__device__ __forceinline__ void lds_load4(const void* sbase, uint32_t voff, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
+  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+                   : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier without the compiler's release fence (which would wait
+// for every outstanding load, including the ring's prefetches); LDS reads of
+// the finished stage have completed (lgkmcnt) before any wave passes it.
+__device__ __forceinline__ void stage_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+}  // namespace fql

@@ -102,4 +102,37 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
                                int64_t N, float alpha, const uint16_t* bias, uint16_t* y,
                                int64_t ldy, uint8_t* workspace, hipStream_t st);
 
+// ---- MXFP4 (E2M1 + E8M0 per 32) ------------------------------------------
+// Operand layout (activation and packed weight): rows padded to 16, K to 128:
+//   codes  [rows/16][KC][lane 64][16 B]   lane = kg*16 + r, 32 codes of
+//          k = 128c + 32kg + 0..31 of row r
+//   scales [rows/16][ceil(KC/4)][lane 64][4 B]  byte q = chunk 4*group + q
+struct MxDims {
+  int64_t rows_p, Kp, code_bytes, scale_bytes;
+  int64_t total_bytes() const { return code_bytes + scale_bytes; }
+};
+MxDims mx_dims(int64_t rows, int64_t K);
+
+// Workspace: [64 KiB arrival counters | x codes | x scales | split-K slabs].
+struct MxPlan {
+  int mt, nt, st;        // 16-row tiles per workgroup, 16-column tiles per wave, ring depth
+  int splits_override;   // benchmarking override of the K split (0 = heuristic)
+  int64_t Mp, groups, ngroups;
+  int splits, kc_per_split;
+  int64_t counter_bytes, xcode_bytes, xscale_bytes, partial_bytes, total_bytes;
+};
+MxPlan plan_gemm_mxfp4(int64_t M, int64_t N, int64_t K);
+std::string describe_mx_plan(const MxPlan& p);
+
+hipError_t launch_quant_mxfp4_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                   uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_quant_mxfp4_f32(const float* w, int64_t N, int64_t K, int64_t ldw,
+                                  uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                             uint8_t* packed, hipStream_t st);
+hipError_t launch_linear_mxfp4(const MxPlan& p, const uint16_t* x, int64_t M, int64_t K,
+                               int64_t ldx, const uint8_t* packed, int64_t N, float alpha,
+                               const uint16_t* bias, uint16_t* y, int64_t ldy, uint8_t* workspace,
+                               hipStream_t st);
+
 }  // namespace fql

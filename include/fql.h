@@ -49,6 +49,7 @@ extern "C" {
 
 /* Weight/activation formats (fql_can_implement). */
 #define FQL_FMT_NVFP4 1
+#define FQL_FMT_MXFP4 2
 
 /* Library version (major*10000 + minor*100 + patch). */
 int fql_version(void);
@@ -68,7 +69,8 @@ int fql_is_supported(int device, char* reason, size_t reason_len);
  * Format-level constraints, in the spirit of can_implement(): returns 1 if a
  * layer with these sizes can run, else 0 with the reason. NVFP4 needs
  * K % 16 == 0, N >= 1, K >= 16, and hadamard_block in {0, 16, 32, 64, 128}
- * with K % hadamard_block == 0.
+ * with K % hadamard_block == 0. MXFP4 needs K % 32 == 0, N >= 1, K >= 32 and
+ * hadamard_block == 0. N and K are at most 2^24.
  */
 int fql_can_implement(int format, int64_t N, int64_t K, int hadamard_block, char* reason,
                       size_t reason_len);
@@ -171,6 +173,63 @@ int fql_linear_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float inp
                      int hadamard_block, const void* w_packed, int64_t N, float alpha,
                      const void* bias, void* y, int64_t ldy, void* workspace,
                      size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * MXFP4 (B12X write-up, Implementation: the MXFP4 linear kernel accepts only a
+ * dynamically quantized activation; element and scale formats per OCP
+ * Microscaling v1.0): E2M1 codes with one E8M0 scale byte per 32 consecutive
+ * elements along K, no global scale, no rotation.
+ * Quantizer numerics, per 32-block: a = max|v|; E = floor(log2 a) - 2
+ * clamped to [-127, 127] (a = 0 gives -127); scale byte E + 127;
+ * q = E2M1_RNE_satfinite(fl32(v * 2^-E)) with the sign of v kept. The block
+ * maximum lands in [4, 8), so values in (6, 8) * 2^E saturate to 6 * 2^E.
+ * Codes [rows][K/2] (even element in the low nibble) and scales [rows][K/32]
+ * are bit-identical to the CPU oracle.
+ * ------------------------------------------------------------------------- */
+
+/* Activation quantizer: bf16 x [M][ldx] (ldx >= K, K % 32 == 0) -> codes
+ * [M][K/2] (4-byte aligned) and scales [M][K/32]. */
+int fql_quant_mxfp4(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
+                    uint8_t* scales, void* stream);
+
+/* Same for float32 input (weights before packing). */
+int fql_quant_mxfp4_f32(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* codes,
+                        uint8_t* scales, void* stream);
+
+/* Size in bytes of the packed MXFP4 weight for [N][K] (host-side). The blob
+ * pads N to a multiple of 16 and K to a multiple of 128 with zero codes and
+ * zero scale bytes. */
+int fql_packed_mxfp4_bytes(int64_t N, int64_t K, size_t* bytes);
+
+/* Weight packer (process_weights_after_loading): canonical codes [N][K/2]
+ * (16-byte aligned) and scales [N][K/32] -> the scaled-MFMA operand order, in
+ * the caller's 16-byte aligned buffer of at least fql_packed_mxfp4_bytes. */
+int fql_pack_weight_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                          void* packed, size_t packed_bytes, void* stream);
+
+/* Workspace bytes fql_linear_mxfp4 needs (host-side): arrival counters (first
+ * 64 KiB, zero before first use and left zero by every call), the quantized
+ * activation operand and split-K partial sums. */
+int fql_linear_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
+
+/* One-line description of the launch plan of fql_linear_mxfp4 (host-side). */
+int fql_linear_mxfp4_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t buf_len);
+
+/*
+ * The MXFP4 W4A4 linear layer (B12X MXFP4 apply_weights: dynamic activation
+ * quantize, then the block-scaled GEMM): y = bf16(alpha * (x_q @ w_q^T) + bias)
+ * with x_q quantized exactly as fql_quant_mxfp4 does and the products of
+ * dequantized values accumulated in float32 by the scaled matrix cores.
+ *   x        [M][ldx] bf16 (any alignment), K % 32 == 0.
+ *   w_packed from fql_pack_weight_mxfp4 for [N][K].
+ *   alpha    float32 output scale (1 for a plain MXFP4 layer).
+ *   bias     [N] bf16 or NULL.   y [M][ldy] bf16 out, ldy >= N.
+ *   workspace  at least fql_linear_mxfp4_workspace_bytes(M, N, K), 256-byte
+ *            aligned; one workspace per stream at a time.
+ */
+int fql_linear_mxfp4(const void* x, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
+                     int64_t N, float alpha, const void* bias, void* y, int64_t ldy,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

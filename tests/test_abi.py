@@ -96,3 +96,39 @@ def test_invalid_scalars_rejected():
     assert lib.fql_linear_nvfp4(p, 1, 64, 64, 1.0, 0, p, 64, 1.0, null, p, 64, p, 16, null) == -4
     # pack into a buffer that is too small
     assert lib.fql_pack_weight_nvfp4(p, p, 64, 64, p, 10, null) == -1
+
+
+def test_mxfp4_sizes_and_rules():
+    # packed MXFP4: N padded to 16, K to 128; codes Np*Kp/2, then 256-byte scale
+    # groups (64 lanes x 4 chunks) per 16-row tile and 4-chunk group
+    def expect(N, K):
+        Np, Kp = -(-N // 16) * 16, -(-K // 128) * 128
+        kc4 = -(-(Kp // 128) // 4)
+        return Np * Kp // 2 + (Np // 16) * kc4 * 256
+    assert fql.packed_mxfp4_bytes(4096, 4096) == expect(4096, 4096) == 4096 * 2048 + 4096 * 128
+    assert fql.packed_mxfp4_bytes(100, 96) == expect(100, 96)
+    assert fql.linear_mxfp4_workspace_bytes(1, 6144, 4096) > 0
+    assert "gemm_mx4_kernel" in fql.linear_mxfp4_plan(8192, 4096, 4096)
+    assert fql.can_implement(4096, 4096, 0, fmt=fql.FMT_MXFP4) == (True, "")
+    ok, why = fql.can_implement(4096, 4112, 0, fmt=fql.FMT_MXFP4)
+    assert not ok and "32" in why
+    ok, why = fql.can_implement(4096, 4096, 32, fmt=fql.FMT_MXFP4)
+    assert not ok and "rotation" in why
+    ok, why = fql.can_implement(4096, 4096, 0, fmt=7)
+    assert not ok and "unknown" in why
+
+
+def test_mxfp4_invalid_arguments_rejected():
+    lib = fql.lib()
+    p = ctypes.c_void_p(256)
+    null = ctypes.c_void_p(0)
+    assert lib.fql_quant_mxfp4(p, 4, 48, 48, p, p, null) == -1        # K % 32
+    assert lib.fql_quant_mxfp4(p, 4, 64, 32, p, p, null) == -1        # ldx < K
+    assert lib.fql_quant_mxfp4(null, 4, 64, 64, p, p, null) == -1     # null x
+    assert lib.fql_quant_mxfp4(p, 0, 64, 64, p, p, null) == -1        # M = 0
+    assert lib.fql_quant_mxfp4(p, 4, 64, 64, ctypes.c_void_p(258), p, null) == -1  # codes alignment
+    assert lib.fql_pack_weight_mxfp4(p, p, 64, 64, p, 10, null) == -1  # buffer too small
+    assert lib.fql_linear_mxfp4(p, 1, 64, 64, p, 64, 1.0, null, p, 32, p, 1 << 20, null) == -1
+    assert lib.fql_linear_mxfp4(p, 1, 64, 64, p, 64, 1.0, null, p, 64, p, 16, null) == -4
+    assert lib.fql_linear_mxfp4(p, 1, 64, 64, p, 64, float("nan"), null, p, 64, p, 1 << 20, null) == -1
+    assert lib.fql_last_error().decode()
