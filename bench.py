@@ -1,6 +1,6 @@
 """Benchmark of the NVFP4 W4A4 linear layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode] [--format nvfp4]
 
 A step is one pass of the whole hot path (activation quantize -> block-scaled
 GEMM -> alpha/bias/bf16 epilogue, i.e. one linear call) over every case of the
@@ -16,6 +16,10 @@ step / step time). `roofline` describes the GEMM calls against HBM bandwidth
 (algorithmic bytes: 0.5625 B per weight element + 2 B per activation and
 output element + bias), timed per call with HIP events on the launch stream.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+
+`--format mxfp4` runs the MXFP4 sibling layer (E2M1 + E8M0 per 32, scaled FP4
+MFMA) instead; its natural workload is `siblings` (K=4096, N=14336, M=1 and
+4096), and its algorithmic weight bytes are 0.53125 B per element.
 """
 
 import argparse
@@ -32,12 +36,16 @@ FP4_PEAK_TFLOPS = 10100.0
 F16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 512 << 20
 
-WORKLOAD_KEYS = ("decode", "prefill", "hadamard", "tiny")
+WORKLOAD_KEYS = ("decode", "prefill", "hadamard", "tiny", "siblings")
+FORMAT_KEYS = ("nvfp4", "mxfp4")
+# algorithmic weight bytes per element: 4-bit code + one scale byte per block
+WEIGHT_BYTES = {"nvfp4": 0.5 + 1.0 / 16, "mxfp4": 0.5 + 1.0 / 32}
 WORKLOAD_NAMES = {
     "decode": "decode: Llama-3.1-8B qkv/gate_up/down at M=1,8,32,128, bias",
     "prefill": "prefill: Llama-3.1-8B qkv/gate_up/down at M=2048,8192, 1% outlier channels",
     "hadamard": "hadamard: Qwen3-32B gate_up/down at M=1,256,4096, block-diagonal Hadamard",
     "tiny": "tiny: M=16, K=256, N=512",
+    "siblings": "siblings: K=4096, N=14336 at M=1,4096",
 }
 
 
@@ -77,8 +85,9 @@ def measured_traffic(workload, kernel):
     return None
 
 
-def _alg_bytes(M, N, K, with_bias):
-    return 0.5625 * N * K + 2.0 * M * K + 2.0 * M * N + (2.0 * N if with_bias else 0.0)
+def _alg_bytes(M, N, K, with_bias, fmt="nvfp4"):
+    return (WEIGHT_BYTES[fmt] * N * K + 2.0 * M * K + 2.0 * M * N
+            + (2.0 * N if with_bias else 0.0))
 
 
 def _cases(workload, hb_override=None):
@@ -92,14 +101,16 @@ def _cases(workload, hb_override=None):
     return out
 
 
-def _kernel_of(M, N, K):
+def _kernel_of(M, N, K, fmt="nvfp4"):
     """The kernel that carries one linear call of this shape (the library's own plan)."""
     import fp8_quantized_linear_amd as fql
 
+    if fmt == "mxfp4":
+        return fql.linear_mxfp4_plan(M, N, K).split(" grid=")[0].split(" + ")[-1]
     return fql.linear_plan(M, N, K).split(" grid=")[0]
 
 
-def gpu_bench(workload, steps, warmup, hb, per_case_reps=3):
+def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4"):
     import torch
 
     import fp8_quantized_linear_amd as fql
@@ -116,7 +127,10 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3):
         key = (name, K, N, hbk)
         if key not in weights:
             W = torch.from_numpy(synthetic.weight(N, K, config=workload)).to(dev)
-            w0 = fql.NVFP4Weight.from_float(W, input_global_scale=1.0, hadamard_block=hbk)
+            if fmt == "mxfp4":
+                w0 = fql.MXFP4Weight.from_float(W)
+            else:
+                w0 = fql.NVFP4Weight.from_float(W, input_global_scale=1.0, hadamard_block=hbk)
             del W
             nbytes = w0.packed.numel()
             ncopies = max(1, -(-ROTATE_BYTES // nbytes))
@@ -125,23 +139,30 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3):
         w0, copies = weights[key]
         xb = synthetic.activations(synthetic.WORKLOADS[workload]["x"], M, K, config=workload)
         x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
-        gx = fql.global_scale_from_amax(fql.amax(x, hbk).item())
-        objs = [fql.NVFP4Weight(p, N, K, gx, w0.weight_global_scale, hbk) for p in copies]
+        if fmt == "mxfp4":
+            objs = [fql.MXFP4Weight(p, N, K) for p in copies]
+        else:
+            gx = fql.global_scale_from_amax(fql.amax(x, hbk).item())
+            objs = [fql.NVFP4Weight(p, N, K, gx, w0.weight_global_scale, hbk) for p in copies]
         bias = None
         if with_bias:
             bias = torch.from_numpy(synthetic.bias(N, config=workload).view(np.int16)).view(
                 torch.bfloat16).to(dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        ws = fql.new_workspace(fql.linear_workspace_bytes(M, N, K), dev)
+        wsb = (fql.linear_mxfp4_workspace_bytes(M, N, K) if fmt == "mxfp4"
+               else fql.linear_workspace_bytes(M, N, K))
+        ws = fql.new_workspace(wsb, dev)
         setups.append(dict(M=M, N=N, K=K, name=name, hb=hbk, x=x, objs=objs, bias=bias, y=y,
-                           ws=ws, flops=2.0 * M * N * K, bytes=_alg_bytes(M, N, K, with_bias),
-                           kernel=_kernel_of(M, N, K)))
+                           ws=ws, flops=2.0 * M * N * K, bytes=_alg_bytes(M, N, K, with_bias, fmt),
+                           kernel=_kernel_of(M, N, K, fmt)))
     torch.cuda.synchronize()
     n = len(setups)
 
+    linear = fql.linear_mxfp4 if fmt == "mxfp4" else fql.linear_nvfp4
+
     def call(s, copy_index):
         w = s["objs"][copy_index % len(s["objs"])]
-        fql.linear_nvfp4(s["x"], w, bias=s["bias"], out=s["y"], workspace=s["ws"])
+        linear(s["x"], w, bias=s["bias"], out=s["y"], workspace=s["ws"])
 
     # One HIP graph per step position: call j of step i uses weight copy i*n + j, so
     # consecutive calls on one weight shape never reuse a copy (cold last-level cache).
@@ -218,6 +239,42 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3):
                 alg_bytes=alg_bytes, detail=detail, dominant=(dom_name, dom))
 
 
+def cpu_baseline_mx(workload, budget_s=12.0, n_rows=2048):
+    """The MXFP4 oracle on a bounded sample of the workload (as cpu_baseline)."""
+    import oracle.mx as X
+    import synthetic
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    cases = _cases(workload)
+    wcache = {}
+    flops = t_total = 0.0
+    passes = 0
+    while t_total < budget_s and passes < 20:
+        for (M, name, K, N, hb, with_bias) in cases:
+            ns = min(N, n_rows)
+            if name not in wcache:
+                wcache[name] = X.quant_mxfp4(synthetic.weight(N, K, config=workload)[:ns])
+            wc, wsc = wcache[name]
+            Mr = min(M, 512)
+            xb = synthetic.activations(synthetic.WORKLOADS[workload]["x"], Mr, K, config=workload)
+            x = synthetic.bf16_bits_to_f32(xb)
+            t0 = time.perf_counter()
+            X.linear_mxfp4(*X.quant_mxfp4(x), wc, wsc)
+            t_total += time.perf_counter() - t0
+            flops += 2.0 * Mr * ns * K
+        passes += 1
+    return dict(value=round(flops / t_total / 1e12, 6), unit="TFLOP/s", cores=int(threads),
+                kind="oracle",
+                sample=f"{passes} pass(es) over the {len(cases)} {workload} cases with the first "
+                       f"{n_rows} weight rows and at most 512 activation rows each "
+                       f"(x quantize + float64 GEMM + epilogue), {t_total:.1f} s of oracle time")
+
+
 def cpu_baseline(workload, budget_s=12.0, n_rows=2048):
     """The oracle, as it stands, on a bounded sample of the workload.
 
@@ -275,6 +332,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=WORKLOAD_KEYS)
+    ap.add_argument("--format", default="nvfp4", choices=FORMAT_KEYS)
     ap.add_argument("--hadamard-block", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", action="store_true", help="print per-case timings to stderr")
@@ -298,29 +356,33 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
         return
-    r = gpu_bench(args.workload, args.steps, args.warmup, args.hadamard_block)
+    r = gpu_bench(args.workload, args.steps, args.warmup, args.hadamard_block, fmt=args.format)
     value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
     dom_name, dom = r["dominant"]
     # binding bound of the dominant kernel: HBM bytes vs f16-MFMA flops (the exact
     # NVFP4 path multiplies dequantized float16 operands), whichever needs more time
+    # (MXFP4 runs on the scaled FP4 MFMA itself, so its compute peak is the FP4 one)
+    mfma_peak = FP4_PEAK_TFLOPS if args.format == "mxfp4" else F16_PEAK_TFLOPS
     t_hbm = dom["bytes"] / (HBM_PEAK_GBS * 1e9)
-    t_mfma = dom["flops"] / (F16_PEAK_TFLOPS * 1e12)
+    t_mfma = dom["flops"] / (mfma_peak * 1e12)
     if t_hbm >= t_mfma:
         ach = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4)}
     else:
         ach = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": F16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / F16_PEAK_TFLOPS, 4),
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": round(ach / mfma_peak, 4),
                 "frac_of_fp4_peak": round(ach / FP4_PEAK_TFLOPS, 4)}
     roof.update({"kernel": dom_name, "launches_per_step": dom["launches"],
                  "alg_bytes_per_step": dom["bytes"], "flops_per_step": dom["flops"],
                  "avg_launch_us": round(dom["ms"] * 1e3 / dom["launches"], 2),
                  "alg_bytes_per_launch": round(dom["bytes"] / dom["launches"]),
-                 "traffic": measured_traffic(args.workload, dom_name)})
+                 "traffic": measured_traffic(args.workload, dom_name)
+                 if args.format == "nvfp4" else None})
     out = {
         "metric": "NVFP4 W4A4 linear TFLOP/s (quant+GEMM), M=1..8192; % of HBM/FP4-MFMA roofline",
+        "format": args.format,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -330,14 +392,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 (e2m1 x e4m3/16) -> f16 MFMA, f32 accumulate, bf16 out",
+        "dtype": ("mxfp4 (e2m1 x e8m0/32) -> scaled fp4 MFMA, f32 accumulate, bf16 out"
+                  if args.format == "mxfp4"
+                  else "nvfp4 (e2m1 x e4m3/16) -> f16 MFMA, f32 accumulate, bf16 out"),
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.workload], "cases": len(r["detail"]),
                    "timing": "HIP graph replay per step, weights rotated over >= 512 MB"},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.workload)
+        out["cpu_baseline"] = (cpu_baseline_mx(args.workload) if args.format == "mxfp4"
+                               else cpu_baseline(args.workload))
     if args.detail:
         for d in r["detail"]:
             print(json.dumps(d), file=sys.stderr)

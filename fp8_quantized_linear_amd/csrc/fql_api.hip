@@ -341,7 +341,7 @@ int fql_linear_mxfp4(const void* x, int64_t M, int64_t K, int64_t ldx, const voi
   if (workspace_bytes < (size_t)plan.total_bytes)
     return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
                 (long long)plan.total_bytes);
-  if (plan.groups > plan.counter_bytes / 4)
+  if (plan.splits > 1 && plan.groups > plan.counter_bytes / 4)
     return fail(FQL_ERR_INVALID, "too many output tiles for the arrival counters");
   hipError_t e = fql::launch_linear_mxfp4(
       plan, static_cast<const uint16_t*>(x), M, K, ldx, static_cast<const uint8_t*>(w_packed), N,

@@ -1090,7 +1090,7 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
   uint32_t* counters = reinterpret_cast<uint32_t*>(workspace);
   _Float16* xhat = reinterpret_cast<_Float16*>(workspace + p.counter_bytes);
   float* partial = reinterpret_cast<float*>(workspace + p.counter_bytes + p.xhat_bytes);
-  if (p.groups > p.counter_bytes / 4) return hipErrorInvalidValue;
+  if (p.splits > 1 && p.groups > p.counter_bytes / 4) return hipErrorInvalidValue;
   if (p.kind == 0 && aligned) {  // the fused path reads x rows with 16-byte loads
     switch (hb) {
       case 0: launch_gemv_hb<0>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st); break;

@@ -309,8 +309,12 @@ MxPlan plan_gemm_mxfp4(int64_t M, int64_t N, int64_t K) {
   MxPlan p{};
   const MxDims w = mx_dims(N, K);
   const int64_t KC = w.Kp / 128, ntiles = w.rows_p / 16;
-  p.mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-  p.nt = 4;
+  // Measured on the K=4096 shapes (N = 6144 .. 28672): one row tile with four
+  // column tiles per wave for M <= 32; above that a 64 x 128 workgroup tile,
+  // except for large M and N, where the 128 x 256 tile's reuse wins.
+  if (M <= 32) { p.mt = 1; p.nt = 4; }
+  else if (M >= 2048 && N >= 16384) { p.mt = 8; p.nt = 4; }
+  else { p.mt = 4; p.nt = 2; }
   p.st = 4;
   if (const char* e = std::getenv("FQL_MX_PLAN")) {  // benchmarking aid: "mt,nt,st,splits"
     int a = 0, b = 0, c = 0, s = 0;
@@ -322,8 +326,8 @@ MxPlan plan_gemm_mxfp4(int64_t M, int64_t N, int64_t K) {
   p.Mp = x.rows_p;
   p.ngroups = (ntiles + 4 * p.nt - 1) / (4 * p.nt);
   const int64_t groups = p.ngroups * (p.Mp / (16 * p.mt));
-  int64_t s = 1;
-  if (groups < 192) s = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(8, KC), 256 / groups));
+  // split K until about 160 workgroups are in flight (at most 4 ways)
+  int64_t s = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(4, KC), (160 + groups / 2) / groups));
   if (p.splits_override > 0) s = std::min<int64_t>(p.splits_override, KC);
   p.kc_per_split = (int)((KC + s - 1) / s);
   p.splits = (int)((KC + p.kc_per_split - 1) / p.kc_per_split);
@@ -389,7 +393,7 @@ hipError_t launch_linear_mxfp4(const MxPlan& p, const uint16_t* x, int64_t M, in
   uint8_t* xc = workspace + p.counter_bytes;
   uint8_t* xs = xc + p.xcode_bytes;
   float4v* partial = reinterpret_cast<float4v*>(xs + p.xscale_bytes);
-  if (p.groups > p.counter_bytes / 4) return hipErrorInvalidValue;
+  if (p.splits > 1 && p.groups > p.counter_bytes / 4) return hipErrorInvalidValue;
   const int64_t total = p.Mp * (w.Kp / 32);
   quant_mxfp4_operand_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(x, M, K, ldx, p.Mp,
                                                                               w.Kp, xc, xs);
