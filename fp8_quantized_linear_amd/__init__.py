@@ -49,6 +49,24 @@ __all__ = [
     "linear_mxfp4_plan",
     "linear_mxfp4",
     "MXFP4Weight",
+    "quant_mxfp8",
+    "quant_mxfp8_weight",
+    "pack_weight_mxfp8",
+    "linear_mxfp8",
+    "MXFP8Weight",
+    "quant_fp8",
+    "quant_fp8_weight",
+    "pack_weight_fp8",
+    "linear_fp8",
+    "FP8Weight",
+    "quant_fp8_block",
+    "quant_fp8_block_weight",
+    "pack_weight_fp8_block",
+    "linear_fp8_block",
+    "FP8BlockWeight",
+    "fp8_scale_from_amax",
+    "linear_sc_plan",
+    "linear_sc_workspace_bytes",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +74,9 @@ LIB_PATH = os.path.join(HERE, "libfql.so")
 HADAMARD_BLOCKS = (0, 16, 32, 64, 128)
 FMT_NVFP4 = 1
 FMT_MXFP4 = 2
+FMT_MXFP8 = 3
+FMT_FP8 = 4
+FMT_FP8_BLOCK = 5
 
 _c_int, _c_i64, _c_f32, _c_vp, _c_sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_float,
                                          ctypes.c_void_p, ctypes.c_size_t)
@@ -77,6 +98,30 @@ SIGNATURES = {
     "fql_linear_nvfp4_describe": (_c_int, [_c_i64, _c_i64, _c_i64, _c_int, ctypes.c_char_p, _c_sz]),
     "fql_linear_nvfp4": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_int, _c_vp, _c_i64,
                                   _c_f32, _c_vp, _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fql_quant_mxfp8": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "fql_quant_mxfp8_f32": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "fql_packed_mxfp8_bytes": (_c_int, [_c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+    "fql_pack_weight_mxfp8": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fql_linear_mxfp8_workspace_bytes": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+    "fql_linear_mxfp8_describe": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_char_p, _c_sz]),
+    "fql_linear_mxfp8": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_f32, _c_vp,
+                                  _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fql_quant_fp8": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_vp, _c_vp]),
+    "fql_quant_fp8_f32": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_vp, _c_vp]),
+    "fql_packed_fp8_bytes": (_c_int, [_c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+    "fql_pack_weight_fp8": (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fql_linear_fp8_workspace_bytes": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+    "fql_linear_fp8_describe": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_char_p, _c_sz]),
+    "fql_linear_fp8": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_vp, _c_i64, _c_f32,
+                                _c_vp, _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fql_quant_fp8_block": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "fql_quant_fp8_block_weight_f32": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "fql_packed_fp8_block_bytes": (_c_int, [_c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+    "fql_pack_weight_fp8_block": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fql_linear_fp8_block_workspace_bytes": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
+    "fql_linear_fp8_block_describe": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_char_p, _c_sz]),
+    "fql_linear_fp8_block": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_f32, _c_vp,
+                                      _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
     "fql_quant_mxfp4": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
     "fql_quant_mxfp4_f32": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
     "fql_packed_mxfp4_bytes": (_c_int, [_c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
@@ -364,91 +409,230 @@ def linear_nvfp4(x, weight, alpha=None, bias=None, out=None, workspace=None):
 
 
 # ---------------------------------------------------------------------------
-# MXFP4 (E2M1 + one E8M0 scale per 32, no global scale)
+# scaled-MFMA formats: MXFP4, MXFP8 (E8M0 per 32), per-tensor FP8, block FP8
 # ---------------------------------------------------------------------------
 
-def _quant_mx(x, name, dtype, fn):
+_SC = {"mxfp4": "mxfp4", "mxfp8": "mxfp8", "fp8": "fp8", "fp8_block": "fp8_block"}
+
+
+def _fn(name):
+    return getattr(lib(), name)
+
+
+def _size_query(name, *args):
+    n = ctypes.c_size_t()
+    _check(_fn(name)(*[int(a) for a in args], ctypes.byref(n)))
+    return n.value
+
+
+def _sc_codes_shape(fmt, lead, K):
+    return lead + ((K // 2,) if fmt == "mxfp4" else (K,))
+
+
+def _quant_sc(fmt, x, name, dtype, fn, scale=None, weight_tiles=False):
     _require_cuda(x, name)
     if x.dtype != dtype:
         raise FQLError(f"{name} must be {dtype}")
     x2, ld = _rows_view(x, name)
     M, K = x2.shape
     lead = tuple(x.shape[:-1])
-    codes = torch.empty(lead + (K // 2,), dtype=torch.uint8, device=x.device)
-    scales = torch.empty(lead + (K // 32,), dtype=torch.uint8, device=x.device)
+    codes = torch.empty(_sc_codes_shape(fmt, lead, K), dtype=torch.uint8, device=x.device)
+    if fmt in ("mxfp4", "mxfp8"):
+        scales = torch.empty(lead + (K // 32,), dtype=torch.uint8, device=x.device)
+    elif fmt == "fp8_block":
+        shape = (M // 128, K // 128) if weight_tiles else lead + (K // 128,)
+        scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    else:
+        scales = None
+    if fmt == "fp8":
+        _check(fn(_ptr(x2), M, K, ld, float(scale), _ptr(codes), _stream(x.device)))
+        return codes
     _check(fn(_ptr(x2), M, K, ld, _ptr(codes), _ptr(scales), _stream(x.device)))
     return codes, scales
 
 
 def quant_mxfp4(x):
     """Quantize bf16 x [..., K] to MXFP4: (codes uint8 [..., K/2], scales uint8 [..., K/32])."""
-    return _quant_mx(x, "x", torch.bfloat16, lib().fql_quant_mxfp4)
+    return _quant_sc("mxfp4", x, "x", torch.bfloat16, _fn("fql_quant_mxfp4"))
 
 
 def quant_mxfp4_weight(w):
     """Quantize float32 weights w [N, K] to MXFP4 (codes, scales)."""
-    return _quant_mx(w, "w", torch.float32, lib().fql_quant_mxfp4_f32)
+    return _quant_sc("mxfp4", w, "w", torch.float32, _fn("fql_quant_mxfp4_f32"))
+
+
+def quant_mxfp8(x):
+    """Quantize bf16 x [..., K] to MXFP8: (codes uint8 [..., K], scales uint8 [..., K/32])."""
+    return _quant_sc("mxfp8", x, "x", torch.bfloat16, _fn("fql_quant_mxfp8"))
+
+
+def quant_mxfp8_weight(w):
+    return _quant_sc("mxfp8", w, "w", torch.float32, _fn("fql_quant_mxfp8_f32"))
+
+
+def quant_fp8(x, scale):
+    """Per-tensor FP8 codes uint8 [..., K] of bf16 x with the float32 scale s (q = E4M3(x * fl32(1/s)))."""
+    return _quant_sc("fp8", x, "x", torch.bfloat16, _fn("fql_quant_fp8"), scale=scale)
+
+
+def quant_fp8_weight(w, scale):
+    return _quant_sc("fp8", w, "w", torch.float32, _fn("fql_quant_fp8_f32"), scale=scale)
+
+
+def quant_fp8_block(x):
+    """Block FP8 of bf16 x [..., K]: (codes uint8 [..., K], scales float32 [..., K/128])."""
+    return _quant_sc("fp8_block", x, "x", torch.bfloat16, _fn("fql_quant_fp8_block"))
+
+
+def quant_fp8_block_weight(w):
+    """Block FP8 of float32 w [N, K] over 128 x 128 tiles: (codes [N, K], scales [N/128, K/128])."""
+    return _quant_sc("fp8_block", w, "w", torch.float32, _fn("fql_quant_fp8_block_weight_f32"),
+                     weight_tiles=True)
+
+
+def fp8_scale_from_amax(amax_value):
+    """s = fl32(amax / 448) on the host (the FP8 calibration scale; 1 when amax is 0)."""
+    import numpy as np
+
+    a = np.float32(amax_value)
+    return float(np.float32(a / np.float32(448.0))) if a > 0 else 1.0
 
 
 def packed_mxfp4_bytes(N, K):
-    n = ctypes.c_size_t()
-    _check(lib().fql_packed_mxfp4_bytes(int(N), int(K), ctypes.byref(n)))
-    return n.value
+    return _size_query("fql_packed_mxfp4_bytes", N, K)
+
+
+def _pack_sc(fmt, codes, scales, out):
+    _require_cuda(codes, "codes")
+    N = codes.shape[0]
+    K = codes.shape[1] * (2 if fmt == "mxfp4" else 1)
+    if not codes.is_contiguous() or (scales is not None and not scales.is_contiguous()):
+        raise FQLError("codes and scales must be contiguous")
+    if fmt in ("mxfp4", "mxfp8") and tuple(scales.shape) != (N, K // 32):
+        raise FQLError("scales must be [N, K/32]")
+    if fmt == "fp8_block" and (tuple(scales.shape) != (N // 128, K // 128) or scales.dtype != torch.float32):
+        raise FQLError("scales must be float32 [N/128, K/128]")
+    nbytes = _size_query(f"fql_packed_{fmt}_bytes", N, K)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    if fmt == "fp8":
+        _check(_fn("fql_pack_weight_fp8")(_ptr(codes), N, K, _ptr(out), out.numel(),
+                                          _stream(codes.device)))
+    else:
+        _check(_fn(f"fql_pack_weight_{fmt}")(_ptr(codes), _ptr(scales), N, K, _ptr(out), out.numel(),
+                                             _stream(codes.device)))
+    return out, N, K
 
 
 def pack_weight_mxfp4(codes, scales, out=None):
     """Re-lay canonical MXFP4 weight (codes [N, K/2], scales [N, K/32]) for the GEMM."""
-    _require_cuda(codes, "codes")
-    N, K = codes.shape[0], codes.shape[1] * 2
-    if not (codes.is_contiguous() and scales.is_contiguous()):
-        raise FQLError("codes and scales must be contiguous")
-    if tuple(scales.shape) != (N, K // 32):
-        raise FQLError("scales must be [N, K/32]")
-    nbytes = packed_mxfp4_bytes(N, K)
-    if out is None:
-        out = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
-    _check(lib().fql_pack_weight_mxfp4(_ptr(codes), _ptr(scales), N, K, _ptr(out), out.numel(),
-                                       _stream(codes.device)))
-    return out
+    return _pack_sc("mxfp4", codes, scales, out)[0]
 
 
-class MXFP4Weight:
-    """A packed MXFP4 weight [N, K] (uint8 device buffer from pack_weight_mxfp4)."""
+def pack_weight_mxfp8(codes, scales, out=None):
+    """Re-lay canonical MXFP8 weight (codes [N, K], scales [N, K/32]) for the GEMM."""
+    return _pack_sc("mxfp8", codes, scales, out)[0]
+
+
+def pack_weight_fp8(codes, out=None):
+    """Re-lay per-tensor FP8 weight codes [N, K] for the GEMM."""
+    return _pack_sc("fp8", codes, None, out)[0]
+
+
+def pack_weight_fp8_block(codes, scales, out=None):
+    """Re-lay block FP8 weight (codes [N, K], float32 scales [N/128, K/128]) for the GEMM."""
+    return _pack_sc("fp8_block", codes, scales, out)[0]
+
+
+class _ScWeight:
+    fmt = None
 
     def __init__(self, packed, N, K):
         self.packed = packed
         self.N, self.K = int(N), int(K)
 
-    @classmethod
-    def from_float(cls, w):
-        """Quantize and pack a float32 weight [N, K] on the GPU."""
-        codes, scales = quant_mxfp4_weight(w)
-        return cls(pack_weight_mxfp4(codes, scales), w.shape[0], w.shape[1])
-
-    def repack_(self, codes, scales):
+    def repack_(self, codes, scales=None):
         """Re-pack new canonical weights into the same storage (address kept)."""
-        pack_weight_mxfp4(codes, scales, out=self.packed)
+        _pack_sc(self.fmt, codes, scales, self.packed)
         return self
 
 
+class MXFP4Weight(_ScWeight):
+    """A packed MXFP4 weight [N, K] (uint8 device buffer from pack_weight_mxfp4)."""
+    fmt = "mxfp4"
+
+    @classmethod
+    def from_float(cls, w):
+        codes, scales = quant_mxfp4_weight(w)
+        return cls(pack_weight_mxfp4(codes, scales), w.shape[0], w.shape[1])
+
+
+class MXFP8Weight(_ScWeight):
+    """A packed MXFP8 weight [N, K]."""
+    fmt = "mxfp8"
+
+    @classmethod
+    def from_float(cls, w):
+        codes, scales = quant_mxfp8_weight(w)
+        return cls(pack_weight_mxfp8(codes, scales), w.shape[0], w.shape[1])
+
+
+class FP8BlockWeight(_ScWeight):
+    """A packed block-FP8 weight [N, K] (scales of 128 x 128 tiles inside the blob)."""
+    fmt = "fp8_block"
+
+    @classmethod
+    def from_float(cls, w):
+        codes, scales = quant_fp8_block_weight(w)
+        return cls(pack_weight_fp8_block(codes, scales), w.shape[0], w.shape[1])
+
+
+class FP8Weight(_ScWeight):
+    """A packed per-tensor FP8 weight [N, K] with its weight scale and the layer's
+    static input scale; alpha = fl32(input_scale * weight_scale)."""
+    fmt = "fp8"
+
+    def __init__(self, packed, N, K, weight_scale, input_scale):
+        super().__init__(packed, N, K)
+        import numpy as np
+
+        self.weight_scale = float(np.float32(weight_scale))
+        self.input_scale = float(np.float32(input_scale))
+        self.alpha = float(np.float32(np.float64(self.input_scale) * np.float64(self.weight_scale)))
+
+    @classmethod
+    def from_float(cls, w, input_scale, weight_scale=None):
+        if weight_scale is None:
+            weight_scale = fp8_scale_from_amax(amax(w).item())
+        return cls(pack_weight_fp8(quant_fp8_weight(w, weight_scale)), w.shape[0], w.shape[1],
+                   weight_scale, input_scale)
+
+
+def linear_sc_workspace_bytes(fmt, M, N, K):
+    return _size_query(f"fql_linear_{_SC[fmt]}_workspace_bytes", M, N, K)
+
+
+def linear_sc_plan(fmt, M, N, K):
+    buf = ctypes.create_string_buffer(256)
+    _check(_fn(f"fql_linear_{_SC[fmt]}_describe")(int(M), int(N), int(K), buf, 256))
+    return buf.value.decode()
+
+
 def linear_mxfp4_workspace_bytes(M, N, K):
-    n = ctypes.c_size_t()
-    _check(lib().fql_linear_mxfp4_workspace_bytes(int(M), int(N), int(K), ctypes.byref(n)))
-    return n.value
+    return linear_sc_workspace_bytes("mxfp4", M, N, K)
 
 
 def linear_mxfp4_plan(M, N, K):
     """One-line description of the MXFP4 launch plan for this shape."""
-    buf = ctypes.create_string_buffer(256)
-    _check(lib().fql_linear_mxfp4_describe(int(M), int(N), int(K), buf, 256))
-    return buf.value.decode()
+    return linear_sc_plan("mxfp4", M, N, K)
 
 
-def linear_mxfp4(x, weight, alpha=1.0, bias=None, out=None, workspace=None):
-    """y = bf16(alpha * mxfp4(x) @ W^T + bias) for bf16 x [..., K]; returns [..., N]."""
+def _linear_sc(fmt, x, weight, alpha, bias, out, workspace):
     _require_cuda(x, "x")
     if x.dtype != torch.bfloat16:
-        raise FQLError("linear_mxfp4 takes bfloat16 activations")
+        raise FQLError(f"linear_{fmt} takes bfloat16 activations")
+    if weight.fmt != fmt:
+        raise FQLError(f"weight is {weight.fmt}, not {fmt}")
     if x.shape[-1] != weight.K:
         raise FQLError(f"x has K={x.shape[-1]}, weight has K={weight.K}")
     x2, ld = _rows_view(x, "x")
@@ -461,10 +645,37 @@ def linear_mxfp4(x, weight, alpha=1.0, bias=None, out=None, workspace=None):
     if out is None:
         out = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=torch.bfloat16, device=x.device)
     y2, ldy = _rows_view(out, "out")
-    need = linear_mxfp4_workspace_bytes(M, N, K)
     if workspace is None:
-        workspace = _workspace(x.device, need)
-    _check(lib().fql_linear_mxfp4(_ptr(x2), M, K, ld, _ptr(weight.packed), N, float(alpha),
-                                  _ptr(bias), _ptr(y2), ldy, _ptr(workspace), workspace.numel(),
-                                  _stream(x.device)))
+        workspace = _workspace(x.device, linear_sc_workspace_bytes(fmt, M, N, K))
+    st = _stream(x.device)
+    if fmt == "fp8":
+        a = weight.alpha if alpha is None else alpha
+        _check(_fn("fql_linear_fp8")(_ptr(x2), M, K, ld, weight.input_scale, _ptr(weight.packed), N,
+                                     float(a), _ptr(bias), _ptr(y2), ldy, _ptr(workspace),
+                                     workspace.numel(), st))
+    else:
+        a = 1.0 if alpha is None else alpha
+        _check(_fn(f"fql_linear_{fmt}")(_ptr(x2), M, K, ld, _ptr(weight.packed), N, float(a),
+                                        _ptr(bias), _ptr(y2), ldy, _ptr(workspace), workspace.numel(),
+                                        st))
     return out
+
+
+def linear_mxfp4(x, weight, alpha=1.0, bias=None, out=None, workspace=None):
+    """y = bf16(alpha * mxfp4(x) @ W^T + bias) for bf16 x [..., K]; returns [..., N]."""
+    return _linear_sc("mxfp4", x, weight, alpha, bias, out, workspace)
+
+
+def linear_mxfp8(x, weight, alpha=1.0, bias=None, out=None, workspace=None):
+    """y = bf16(alpha * mxfp8(x) @ W^T + bias)."""
+    return _linear_sc("mxfp8", x, weight, alpha, bias, out, workspace)
+
+
+def linear_fp8(x, weight, alpha=None, bias=None, out=None, workspace=None):
+    """y = bf16(alpha * fp8(x; input_scale) @ W_q^T + bias), alpha = input_scale * weight_scale."""
+    return _linear_sc("fp8", x, weight, alpha, bias, out, workspace)
+
+
+def linear_fp8_block(x, weight, alpha=1.0, bias=None, out=None, workspace=None):
+    """y = bf16(sum over 128-groups of s_x s_w (x_q @ W_q^T) + bias)."""
+    return _linear_sc("fp8_block", x, weight, alpha, bias, out, workspace)

@@ -20,7 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfql.so")
 
-SOURCES = ["fql_api.hip", "quant_nvfp4.hip", "pack_nvfp4.hip", "gemm_nvfp4.hip", "mx_fp4.hip"]
+SOURCES = ["fql_api.hip", "quant_nvfp4.hip", "pack_nvfp4.hip", "gemm_nvfp4.hip", "sc_quant.hip",
+           "sc_gemm.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -60,17 +60,6 @@ int check_nvfp4_shape(int64_t rows, int64_t K, int64_t ld, int hb, const char* r
   return FQL_OK;
 }
 
-// MXFP4 shape checks (32-element blocks, no rotation).
-int check_mx_shape(int64_t rows, int64_t K, int64_t ld, const char* rows_name) {
-  if (rows < 1) return fail(FQL_ERR_INVALID, "%s must be >= 1 (got %lld)", rows_name, (long long)rows);
-  if (K < 32 || K % 32 != 0)
-    return fail(FQL_ERR_INVALID, "K must be a positive multiple of 32 (got %lld)", (long long)K);
-  if (ld < K) return fail(FQL_ERR_INVALID, "row stride %lld is smaller than K %lld", (long long)ld, (long long)K);
-  if (K > (int64_t)1 << 24 || rows > (int64_t)1 << 24)
-    return fail(FQL_ERR_INVALID, "dimension too large");
-  return FQL_OK;
-}
-
 bool aligned16(const void* p, int64_t ld, int64_t elem_bytes) {
   return (reinterpret_cast<uintptr_t>(p) % 16 == 0) && ((ld * elem_bytes) % 16 == 0);
 }
@@ -124,10 +113,14 @@ int fql_can_implement(int format, int64_t N, int64_t K, int hadamard_block, char
     else if (K < 16 || K % 16 != 0) why = "K must be a positive multiple of 16 (the NVFP4 block)";
     else if (!valid_hadamard(hadamard_block)) why = "hadamard_block must be 0, 16, 32, 64 or 128";
     else if (hadamard_block > 0 && K % hadamard_block != 0) why = "K must be a multiple of hadamard_block";
-  } else if (format == FQL_FMT_MXFP4) {
+  } else if (format == FQL_FMT_MXFP4 || format == FQL_FMT_MXFP8 || format == FQL_FMT_FP8) {
     if (N < 1) why = "N must be >= 1";
     else if (K < 32 || K % 32 != 0) why = "K must be a positive multiple of 32 (the MX block)";
-    else if (hadamard_block != 0) why = "MXFP4 layers take no rotation (hadamard_block must be 0)";
+    else if (hadamard_block != 0) why = "this format takes no rotation (hadamard_block must be 0)";
+  } else if (format == FQL_FMT_FP8_BLOCK) {
+    if (N < 128 || N % 128 != 0) why = "N must be a positive multiple of 128 (weight group 128 x 128)";
+    else if (K < 128 || K % 128 != 0) why = "K must be a positive multiple of 128 (activation group 1 x 128)";
+    else if (hadamard_block != 0) why = "this format takes no rotation (hadamard_block must be 0)";
   } else {
     why = "unknown format";
   }
@@ -259,95 +252,239 @@ int fql_linear_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float inp
   return hip_status(e, "linear launch");
 }
 
-// ---- MXFP4 ----------------------------------------------------------------
+// ---- scaled-MFMA formats: MXFP4, MXFP8, per-tensor FP8, block FP8 -------------
 
-int fql_quant_mxfp4(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
-                    uint8_t* scales, void* stream) {
-  if (int r = check_mx_shape(M, K, ldx, "M")) return r;
-  if (!x || !codes || !scales) return fail(FQL_ERR_INVALID, "null pointer");
-  if (reinterpret_cast<uintptr_t>(codes) % 4 != 0)
-    return fail(FQL_ERR_INVALID, "codes must be 4-byte aligned");
-  if (M * (K / 32) > ((int64_t)1 << 31) - 256) return fail(FQL_ERR_INVALID, "too many blocks");
-  return hip_status(fql::launch_quant_mxfp4_bf16(static_cast<const uint16_t*>(x), M, K, ldx, codes,
-                                                 scales, static_cast<hipStream_t>(stream)),
-                    "quant_mxfp4 launch");
+}  // extern "C"
+
+namespace {
+
+const char* sc_name(int fmt) {
+  return fmt == fql::SC_MXFP4 ? "MXFP4" : fmt == fql::SC_MXFP8 ? "MXFP8" : fmt == fql::SC_FP8 ? "FP8" : "block FP8";
 }
 
-int fql_quant_mxfp4_f32(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* codes,
-                        uint8_t* scales, void* stream) {
-  if (int r = check_mx_shape(N, K, ldw, "N")) return r;
-  if (!w || !codes || !scales) return fail(FQL_ERR_INVALID, "null pointer");
-  if (reinterpret_cast<uintptr_t>(codes) % 4 != 0)
-    return fail(FQL_ERR_INVALID, "codes must be 4-byte aligned");
-  if (N * (K / 32) > ((int64_t)1 << 31) - 256) return fail(FQL_ERR_INVALID, "too many blocks");
-  return hip_status(fql::launch_quant_mxfp4_f32(w, N, K, ldw, codes, scales,
-                                                static_cast<hipStream_t>(stream)),
-                    "quant_mxfp4_f32 launch");
+// K granularity: 32 (MX block; per-tensor FP8 follows the same operand
+// granularity) or 128 (block FP8 group).
+int64_t sc_kmult(int fmt) { return fmt == fql::SC_FP8_BLOCK ? 128 : 32; }
+
+int check_sc_shape(int fmt, int64_t rows, int64_t K, int64_t ld, const char* rows_name, bool weight) {
+  if (rows < 1) return fail(FQL_ERR_INVALID, "%s must be >= 1 (got %lld)", rows_name, (long long)rows);
+  const int64_t km = sc_kmult(fmt);
+  if (K < km || K % km != 0)
+    return fail(FQL_ERR_INVALID, "%s needs K a positive multiple of %lld (got %lld)", sc_name(fmt),
+                (long long)km, (long long)K);
+  if (weight && fmt == fql::SC_FP8_BLOCK && rows % 128 != 0)
+    return fail(FQL_ERR_INVALID, "block FP8 needs N a multiple of 128 (got %lld)", (long long)rows);
+  if (ld < K) return fail(FQL_ERR_INVALID, "row stride %lld is smaller than K %lld", (long long)ld, (long long)K);
+  if (K > (int64_t)1 << 24 || rows > (int64_t)1 << 24) return fail(FQL_ERR_INVALID, "dimension too large");
+  if (rows * (fql::round_up(K, 128) / 32) > ((int64_t)1 << 31) - 4096)
+    return fail(FQL_ERR_INVALID, "too many 32-element blocks");
+  return FQL_OK;
 }
 
-int fql_packed_mxfp4_bytes(int64_t N, int64_t K, size_t* bytes) {
+int sc_quant(int fmt, bool f32_input, bool weight_tiles, const void* x, int64_t rows, int64_t K,
+             int64_t ld, float scale, uint8_t* codes, void* scales, void* stream) {
+  if (int r = check_sc_shape(fmt, rows, K, ld, weight_tiles ? "N" : "M", weight_tiles)) return r;
+  if (!x || !codes || (fmt != fql::SC_FP8 && !scales)) return fail(FQL_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(codes) % 4 != 0 ||
+      (fmt == fql::SC_FP8_BLOCK && reinterpret_cast<uintptr_t>(scales) % 4 != 0))
+    return fail(FQL_ERR_INVALID, "codes (and float scales) must be 4-byte aligned");
+  float inv = 0.0f;
+  if (fmt == fql::SC_FP8) {
+    if (int r = check_scale(scale, "scale")) return r;
+    inv = std::fmin(1.0f / scale, 3.4028234663852886e38f);  // fl32(1/s), finite
+  }
+  return hip_status(fql::launch_sc_quant(fmt, f32_input, weight_tiles, x, rows, K, ld, inv, codes,
+                                         scales, static_cast<hipStream_t>(stream)),
+                    "quant launch");
+}
+
+int sc_packed_bytes(int fmt, int64_t N, int64_t K, size_t* bytes) {
   if (!bytes) return fail(FQL_ERR_INVALID, "null pointer");
-  if (int r = check_mx_shape(N, K, K, "N")) return r;
-  *bytes = (size_t)fql::mx_dims(N, K).total_bytes();
+  if (int r = check_sc_shape(fmt, N, K, K, "N", true)) return r;
+  *bytes = (size_t)fql::sc_dims(fmt, N, K, true).total_bytes();
   return ok();
 }
 
-int fql_pack_weight_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
-                          void* packed, size_t packed_bytes, void* stream) {
-  if (int r = check_mx_shape(N, K, K, "N")) return r;
-  if (!codes || !scales || !packed) return fail(FQL_ERR_INVALID, "null pointer");
-  const size_t need = (size_t)fql::mx_dims(N, K).total_bytes();
+int sc_pack(int fmt, const uint8_t* codes, const void* scales, int64_t N, int64_t K, void* packed,
+            size_t packed_bytes, void* stream) {
+  if (int r = check_sc_shape(fmt, N, K, K, "N", true)) return r;
+  if (!codes || !packed || (fmt != fql::SC_FP8 && !scales)) return fail(FQL_ERR_INVALID, "null pointer");
+  const size_t need = (size_t)fql::sc_dims(fmt, N, K, true).total_bytes();
   if (packed_bytes < need)
     return fail(FQL_ERR_INVALID, "packed buffer holds %zu bytes, %zu needed", packed_bytes, need);
   if (reinterpret_cast<uintptr_t>(packed) % 16 != 0 || reinterpret_cast<uintptr_t>(codes) % 16 != 0)
     return fail(FQL_ERR_INVALID, "codes and the packed buffer must be 16-byte aligned");
-  if (need >= ((size_t)1 << 32)) return fail(FQL_ERR_INVALID, "packed weight above 4 GiB");
-  return hip_status(fql::launch_pack_mxfp4(codes, scales, N, K, static_cast<uint8_t*>(packed),
-                                           static_cast<hipStream_t>(stream)),
-                    "pack_mxfp4 launch");
+  if (fmt == fql::SC_FP8_BLOCK && reinterpret_cast<uintptr_t>(scales) % 4 != 0)
+    return fail(FQL_ERR_INVALID, "scales must be 4-byte aligned");
+  return hip_status(fql::launch_sc_pack(fmt, codes, scales, N, K, static_cast<uint8_t*>(packed),
+                                        static_cast<hipStream_t>(stream)),
+                    "pack launch");
 }
 
-int fql_linear_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+int sc_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes) {
   if (!bytes) return fail(FQL_ERR_INVALID, "null pointer");
-  if (M < 1 || N < 1 || K < 32 || K % 32 != 0)
-    return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 32");
-  *bytes = (size_t)fql::plan_gemm_mxfp4(M, N, K).total_bytes;
+  if (int r = check_sc_shape(fmt, N, K, K, "N", true)) return r;
+  if (M < 1) return fail(FQL_ERR_INVALID, "M must be >= 1");
+  *bytes = (size_t)fql::plan_sc_gemm(fmt, M, N, K).total_bytes;
   return ok();
 }
 
-int fql_linear_mxfp4_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t buf_len) {
-  if (M < 1 || N < 1 || K < 32 || K % 32 != 0)
-    return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 32");
-  write_reason(buf, buf_len, fql::describe_mx_plan(fql::plan_gemm_mxfp4(M, N, K)));
+int sc_describe(int fmt, int64_t M, int64_t N, int64_t K, char* buf, size_t len) {
+  if (int r = check_sc_shape(fmt, N, K, K, "N", true)) return r;
+  if (M < 1) return fail(FQL_ERR_INVALID, "M must be >= 1");
+  write_reason(buf, len, fql::describe_sc_plan(fql::plan_sc_gemm(fmt, M, N, K)));
   return ok();
 }
 
-int fql_linear_mxfp4(const void* x, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
-                     int64_t N, float alpha, const void* bias, void* y, int64_t ldy,
-                     void* workspace, size_t workspace_bytes, void* stream) {
-  if (int r = check_mx_shape(M, K, ldx, "M")) return r;
+int sc_linear(int fmt, const void* x, int64_t M, int64_t K, int64_t ldx, float input_scale,
+              const void* w_packed, int64_t N, float alpha, const void* bias, void* y, int64_t ldy,
+              void* workspace, size_t workspace_bytes, void* stream) {
+  if (int r = check_sc_shape(fmt, M, K, ldx, "M", false)) return r;
+  if (int r = check_sc_shape(fmt, N, K, K, "N", true)) return r;
   if (!std::isfinite(alpha)) return fail(FQL_ERR_INVALID, "alpha must be finite");
-  if (N < 1 || N > (int64_t)1 << 24) return fail(FQL_ERR_INVALID, "N out of range");
+  float inv = 0.0f;
+  if (fmt == fql::SC_FP8) {
+    if (int r = check_scale(input_scale, "input_scale")) return r;
+    inv = std::fmin(1.0f / input_scale, 3.4028234663852886e38f);
+  }
   if (ldy < N) return fail(FQL_ERR_INVALID, "ldy %lld is smaller than N %lld", (long long)ldy, (long long)N);
   if (!x || !w_packed || !y || !workspace) return fail(FQL_ERR_INVALID, "null pointer");
   if (reinterpret_cast<uintptr_t>(w_packed) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(FQL_ERR_INVALID, "packed weight must be 16-byte and workspace 256-byte aligned");
-  if (fql::mx_dims(N, K).total_bytes() >= ((int64_t)1 << 32))
-    return fail(FQL_ERR_INVALID, "packed weight above 4 GiB");
-  const fql::MxPlan plan = fql::plan_gemm_mxfp4(M, N, K);
-  if (plan.Mp * (fql::mx_dims(N, K).Kp / 32) > ((int64_t)1 << 31) - 256)
-    return fail(FQL_ERR_INVALID, "activation too large (M * K / 32 blocks)");
+  const fql::ScPlan plan = fql::plan_sc_gemm(fmt, M, N, K);
   if (workspace_bytes < (size_t)plan.total_bytes)
     return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
                 (long long)plan.total_bytes);
   if (plan.splits > 1 && plan.groups > plan.counter_bytes / 4)
     return fail(FQL_ERR_INVALID, "too many output tiles for the arrival counters");
-  hipError_t e = fql::launch_linear_mxfp4(
-      plan, static_cast<const uint16_t*>(x), M, K, ldx, static_cast<const uint8_t*>(w_packed), N,
-      alpha, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), ldy,
-      static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream));
-  return hip_status(e, "linear_mxfp4 launch");
+  if (plan.Mp * (plan.groups > 0 ? fql::round_up(K, 128) / 32 : 0) > ((int64_t)1 << 31) - 4096)
+    return fail(FQL_ERR_INVALID, "activation too large");
+  hipError_t e = fql::launch_sc_linear(
+      plan, static_cast<const uint16_t*>(x), M, K, ldx, aligned16(x, ldx, 2), inv,
+      static_cast<const uint8_t*>(w_packed), N, alpha, static_cast<const uint16_t*>(bias),
+      static_cast<uint16_t*>(y), ldy, static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream));
+  return hip_status(e, "linear launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+// MXFP4
+int fql_quant_mxfp4(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
+                    uint8_t* scales, void* stream) {
+  return sc_quant(fql::SC_MXFP4, false, false, x, M, K, ldx, 0.0f, codes, scales, stream);
+}
+int fql_quant_mxfp4_f32(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* codes,
+                        uint8_t* scales, void* stream) {
+  return sc_quant(fql::SC_MXFP4, true, false, w, N, K, ldw, 0.0f, codes, scales, stream);
+}
+int fql_packed_mxfp4_bytes(int64_t N, int64_t K, size_t* bytes) {
+  return sc_packed_bytes(fql::SC_MXFP4, N, K, bytes);
+}
+int fql_pack_weight_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                          void* packed, size_t packed_bytes, void* stream) {
+  return sc_pack(fql::SC_MXFP4, codes, scales, N, K, packed, packed_bytes, stream);
+}
+int fql_linear_mxfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  return sc_workspace_bytes(fql::SC_MXFP4, M, N, K, bytes);
+}
+int fql_linear_mxfp4_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t buf_len) {
+  return sc_describe(fql::SC_MXFP4, M, N, K, buf, buf_len);
+}
+int fql_linear_mxfp4(const void* x, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
+                     int64_t N, float alpha, const void* bias, void* y, int64_t ldy,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return sc_linear(fql::SC_MXFP4, x, M, K, ldx, 1.0f, w_packed, N, alpha, bias, y, ldy, workspace,
+                   workspace_bytes, stream);
+}
+
+// MXFP8
+int fql_quant_mxfp8(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
+                    uint8_t* scales, void* stream) {
+  return sc_quant(fql::SC_MXFP8, false, false, x, M, K, ldx, 0.0f, codes, scales, stream);
+}
+int fql_quant_mxfp8_f32(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* codes,
+                        uint8_t* scales, void* stream) {
+  return sc_quant(fql::SC_MXFP8, true, false, w, N, K, ldw, 0.0f, codes, scales, stream);
+}
+int fql_packed_mxfp8_bytes(int64_t N, int64_t K, size_t* bytes) {
+  return sc_packed_bytes(fql::SC_MXFP8, N, K, bytes);
+}
+int fql_pack_weight_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                          void* packed, size_t packed_bytes, void* stream) {
+  return sc_pack(fql::SC_MXFP8, codes, scales, N, K, packed, packed_bytes, stream);
+}
+int fql_linear_mxfp8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  return sc_workspace_bytes(fql::SC_MXFP8, M, N, K, bytes);
+}
+int fql_linear_mxfp8_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t buf_len) {
+  return sc_describe(fql::SC_MXFP8, M, N, K, buf, buf_len);
+}
+int fql_linear_mxfp8(const void* x, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
+                     int64_t N, float alpha, const void* bias, void* y, int64_t ldy,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return sc_linear(fql::SC_MXFP8, x, M, K, ldx, 1.0f, w_packed, N, alpha, bias, y, ldy, workspace,
+                   workspace_bytes, stream);
+}
+
+// per-tensor FP8
+int fql_quant_fp8(const void* x, int64_t M, int64_t K, int64_t ldx, float scale, uint8_t* codes,
+                  void* stream) {
+  return sc_quant(fql::SC_FP8, false, false, x, M, K, ldx, scale, codes, nullptr, stream);
+}
+int fql_quant_fp8_f32(const float* w, int64_t N, int64_t K, int64_t ldw, float scale,
+                      uint8_t* codes, void* stream) {
+  return sc_quant(fql::SC_FP8, true, false, w, N, K, ldw, scale, codes, nullptr, stream);
+}
+int fql_packed_fp8_bytes(int64_t N, int64_t K, size_t* bytes) {
+  return sc_packed_bytes(fql::SC_FP8, N, K, bytes);
+}
+int fql_pack_weight_fp8(const uint8_t* codes, int64_t N, int64_t K, void* packed,
+                        size_t packed_bytes, void* stream) {
+  return sc_pack(fql::SC_FP8, codes, nullptr, N, K, packed, packed_bytes, stream);
+}
+int fql_linear_fp8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  return sc_workspace_bytes(fql::SC_FP8, M, N, K, bytes);
+}
+int fql_linear_fp8_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t buf_len) {
+  return sc_describe(fql::SC_FP8, M, N, K, buf, buf_len);
+}
+int fql_linear_fp8(const void* x, int64_t M, int64_t K, int64_t ldx, float input_scale,
+                   const void* w_packed, int64_t N, float alpha, const void* bias, void* y,
+                   int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+  return sc_linear(fql::SC_FP8, x, M, K, ldx, input_scale, w_packed, N, alpha, bias, y, ldy,
+                   workspace, workspace_bytes, stream);
+}
+
+// block FP8
+int fql_quant_fp8_block(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
+                        float* scales, void* stream) {
+  return sc_quant(fql::SC_FP8_BLOCK, false, false, x, M, K, ldx, 0.0f, codes, scales, stream);
+}
+int fql_quant_fp8_block_weight_f32(const float* w, int64_t N, int64_t K, int64_t ldw,
+                                   uint8_t* codes, float* scales, void* stream) {
+  return sc_quant(fql::SC_FP8_BLOCK, true, true, w, N, K, ldw, 0.0f, codes, scales, stream);
+}
+int fql_packed_fp8_block_bytes(int64_t N, int64_t K, size_t* bytes) {
+  return sc_packed_bytes(fql::SC_FP8_BLOCK, N, K, bytes);
+}
+int fql_pack_weight_fp8_block(const uint8_t* codes, const float* scales, int64_t N, int64_t K,
+                              void* packed, size_t packed_bytes, void* stream) {
+  return sc_pack(fql::SC_FP8_BLOCK, codes, scales, N, K, packed, packed_bytes, stream);
+}
+int fql_linear_fp8_block_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  return sc_workspace_bytes(fql::SC_FP8_BLOCK, M, N, K, bytes);
+}
+int fql_linear_fp8_block_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t buf_len) {
+  return sc_describe(fql::SC_FP8_BLOCK, M, N, K, buf, buf_len);
+}
+int fql_linear_fp8_block(const void* x, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
+                         int64_t N, float alpha, const void* bias, void* y, int64_t ldy,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return sc_linear(fql::SC_FP8_BLOCK, x, M, K, ldx, 1.0f, w_packed, N, alpha, bias, y, ldy,
+                   workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

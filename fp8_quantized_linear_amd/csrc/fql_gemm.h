@@ -54,9 +54,9 @@ __device__ __forceinline__ float4v load_partial(const float4v* p) {
 // split-K slab and the last-arriver reduction. The lane's accumulators come
 // as FR float4 fragments; fragment f element i is the output element at
 // (m0 + row_of(f, i), n0 + col_of(f)).
-//   slab: [splits][4 waves][FR][64 lanes] float4 for this workgroup's tile,
+//   slab: [splits][NW waves][FR][64 lanes] float4 for this workgroup's tile,
 //   so every lane writes and later sums exactly its own fragments.
-template <int FR, typename RowOf, typename ColOf>
+template <int FR, typename RowOf, typename ColOf, int NW = 4>
 __device__ __forceinline__ void finish_frags(float4v (&frag)[FR], RowOf row_of, ColOf col_of, int M,
                                              int N, int m0, int n0, int split, int splits,
                                              float alpha, const uint16_t* __restrict__ bias,
@@ -80,7 +80,7 @@ __device__ __forceinline__ void finish_frags(float4v (&frag)[FR], RowOf row_of, 
     return;
   }
   float4v* mine = slab + wave * FR * 64 + lane;
-  const int64_t zstride = 4 * FR * 64;
+  const int64_t zstride = (int64_t)NW * FR * 64;
 #pragma unroll
   for (int f = 0; f < FR; ++f) store_partial(mine + split * zstride + f * 64, frag[f]);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // partial stores have completed

@@ -102,37 +102,58 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
                                int64_t N, float alpha, const uint16_t* bias, uint16_t* y,
                                int64_t ldy, uint8_t* workspace, hipStream_t st);
 
-// ---- MXFP4 (E2M1 + E8M0 per 32) ------------------------------------------
-// Operand layout (activation and packed weight): rows padded to 16, K to 128:
-//   codes  [rows/16][KC][lane 64][16 B]   lane = kg*16 + r, 32 codes of
-//          k = 128c + 32kg + 0..31 of row r
-//   scales [rows/16][ceil(KC/4)][lane 64][4 B]  byte q = chunk 4*group + q
-struct MxDims {
-  int64_t rows_p, Kp, code_bytes, scale_bytes;
+// ---- scaled-MFMA formats: MXFP4, MXFP8, per-tensor FP8, block FP8 ---------
+// All four run on v_mfma_scale_f32_16x16x128_f8f6f4 (one instruction per
+// 16x16 output tile and 128-deep "chunk" of K). Operand layout, shared by the
+// quantized activation (workspace) and the packed weight; rows padded to 16,
+// K to 128:
+//   codes [rows_p/16][KC][H halves][lane 64][16 B]   H = 1 (FP4) or 2 (FP8)
+//     FP4: lane l holds row l%16, k = 128c + 32(l/16) + i in nibble i.
+//     FP8: half h of lane l holds row l%16, k = 128c + 64h + 16(l/16) + i in byte i.
+//   MX scales (E8M0) [quads][KC][lane 64][4 B], quads = ceil(rows_p/64):
+//     byte q of lane l = scale of row 64*quad + 16q + l%16, 32-block 4c + l/16
+//     (the MFMA takes the scale of row r, block j from lane 16j + r).
+//   block-FP8 activation row scales (float32) [quads][KC][row 64].
+//   block-FP8 weight scales (float32) [N/128][KC], after the weight codes.
+enum ScFmt { SC_MXFP4 = 0, SC_MXFP8 = 1, SC_FP8 = 2, SC_FP8_BLOCK = 3 };
+
+struct ScDims {
+  int64_t rows_p, Kp, KC, quads, code_bytes, scale_bytes;
   int64_t total_bytes() const { return code_bytes + scale_bytes; }
 };
-MxDims mx_dims(int64_t rows, int64_t K);
+// Layout sizes of an operand of `rows` x K; `weight` selects the packed-weight
+// scale region (block FP8: [N/128][KC] floats) over the activation one.
+ScDims sc_dims(int fmt, int64_t rows, int64_t K, bool weight);
 
-// Workspace: [64 KiB arrival counters | x codes | x scales | split-K slabs].
-struct MxPlan {
-  int mt, nt, st;        // 16-row tiles per workgroup, 16-column tiles per wave, ring depth
-  int splits_override;   // benchmarking override of the K split (0 = heuristic)
+// Workspace: [64 KiB arrival counters | activation codes | activation scales | split-K slabs].
+struct ScPlan {
+  int fmt;
+  int wm, wn, mtw, ntw, st;  // wave grid, 16x16 tiles per wave, LDS ring depth
   int64_t Mp, groups, ngroups;
   int splits, kc_per_split;
   int64_t counter_bytes, xcode_bytes, xscale_bytes, partial_bytes, total_bytes;
 };
-MxPlan plan_gemm_mxfp4(int64_t M, int64_t N, int64_t K);
-std::string describe_mx_plan(const MxPlan& p);
+ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K);
+std::string describe_sc_plan(const ScPlan& p);
 
-hipError_t launch_quant_mxfp4_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                                   uint8_t* codes, uint8_t* scales, hipStream_t st);
-hipError_t launch_quant_mxfp4_f32(const float* w, int64_t N, int64_t K, int64_t ldw,
-                                  uint8_t* codes, uint8_t* scales, hipStream_t st);
-hipError_t launch_pack_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
-                             uint8_t* packed, hipStream_t st);
-hipError_t launch_linear_mxfp4(const MxPlan& p, const uint16_t* x, int64_t M, int64_t K,
-                               int64_t ldx, const uint8_t* packed, int64_t N, float alpha,
-                               const uint16_t* bias, uint16_t* y, int64_t ldy, uint8_t* workspace,
-                               hipStream_t st);
+// Canonical quantizers: codes [rows][K/2] (FP4) or [rows][K] (FP8);
+// scales: MX [rows][K/32] bytes, block FP8 [rows][K/128] floats (activation)
+// or [rows/128][K/128] floats (weight, f32 input only), per-tensor none
+// (`inv_scale` = fl32(1/s) is applied instead).
+hipError_t launch_sc_quant(int fmt, bool f32_input, bool weight_tiles, const void* x, int64_t rows,
+                           int64_t K, int64_t ld, float inv_scale, uint8_t* codes, void* scales,
+                           hipStream_t st);
+// Canonical weight -> packed operand layout.
+hipError_t launch_sc_pack(int fmt, const uint8_t* codes, const void* scales, int64_t N, int64_t K,
+                          uint8_t* packed, hipStream_t st);
+// Activation quantize (straight into the operand layout) + GEMM + epilogue.
+hipError_t launch_sc_linear(const ScPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                            bool aligned, float inv_scale, const uint8_t* packed, int64_t N,
+                            float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
+                            uint8_t* workspace, hipStream_t st);
+// Activation operand quantizer used by launch_sc_linear.
+hipError_t launch_sc_quant_operand(int fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                   bool aligned, float inv_scale, int64_t Mp, uint8_t* codes,
+                                   void* scales, hipStream_t st);
 
 }  // namespace fql

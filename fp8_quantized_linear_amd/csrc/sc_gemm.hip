@@ -1,0 +1,366 @@
+// GEMM of the scaled-MFMA formats (MXFP4, MXFP8, per-tensor FP8, block FP8)
+// on gfx950, plus the launch planner and the linear-layer launcher.
+//
+// One v_mfma_scale_f32_16x16x128_f8f6f4 computes a 16x16 output tile over a
+// 128-deep chunk of K from the operands exactly as they sit in memory: E2M1 or
+// E4M3 codes and, for the MX formats, one E8M0 byte per row and 32-block
+// (lane 16j + r carries the scale of row r, block j). Nothing is
+// dequantized. Per-tensor FP8 passes the unit scale and applies alpha in the
+// epilogue; block FP8 computes each chunk into a fresh accumulator and adds
+// it with the product of the row's and the column block's float32 scales
+// (the per-128-group promotion).
+//
+// Workgroup: NW = WM x WN waves; wave (wm, wn) owns MTW x NTW output tiles of
+// 16x16, so the workgroup tile is (WM*MTW*16) x (WN*NTW*16). The activation
+// and weight tiles of one chunk go through an LDS ring of ST stages, filled by
+// direct global->LDS loads that every wave issues for its share of the stage
+// (item e of the stage is loaded by wave e % NW), spread between its MFMAs.
+// The per-CU vector-memory path (about 64 B/clk) and LDS reads set the tile
+// sizes: bytes per flop fall as 1/tile_rows + 1/tile_cols.
+#include <algorithm>
+#include <cstddef>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "fql_device.h"
+#include "fql_gemm.h"
+#include "fql_internal.h"
+
+namespace fql {
+
+typedef int int8v __attribute__((ext_vector_type(8)));
+
+ScDims sc_dims(int fmt, int64_t rows, int64_t K, bool weight) {
+  ScDims d;
+  d.rows_p = round_up(rows, 16);
+  d.Kp = round_up(K, 128);
+  d.KC = d.Kp / 128;
+  d.quads = (d.rows_p + 63) / 64;
+  d.code_bytes = fmt == SC_MXFP4 ? d.rows_p * d.Kp / 2 : d.rows_p * d.Kp;
+  if (fmt == SC_MXFP4 || fmt == SC_MXFP8) d.scale_bytes = d.quads * d.KC * 256;
+  else if (fmt == SC_FP8_BLOCK) d.scale_bytes = weight ? round_up((rows / 128) * d.KC * 4, 256) : d.quads * d.KC * 256;
+  else d.scale_bytes = 0;
+  return d;
+}
+
+template <int F>
+struct ScTraits {
+  static constexpr int H = F == SC_MXFP4 ? 1 : 2;            // 1 KiB halves per tile-chunk
+  static constexpr int FMT = F == SC_MXFP4 ? 4 : 0;          // MFMA operand format (E2M1 / E4M3)
+  static constexpr bool MX = F == SC_MXFP4 || F == SC_MXFP8;  // E8M0 scales in the operands
+  static constexpr bool BLOCK = F == SC_FP8_BLOCK;
+};
+
+template <int F, int WM, int WN, int MTW, int NTW>
+struct ScStage {
+  static constexpr int H = ScTraits<F>::H;
+  static constexpr int TA = WM * MTW, TB = WN * NTW;
+  static_assert(TA == 1 || TA == 2 || TA % 4 == 0, "activation tiles within whole scale quads");
+  static constexpr int QA = (TA + 3) / 4;
+  static constexpr int QB = TB / 4;
+  // block FP8: one float per 128-column block of the workgroup
+  static constexpr int NBS = (TB * 16 + 127) / 128;
+  static constexpr int SA = ScTraits<F>::MX || ScTraits<F>::BLOCK ? QA : 0;
+  static constexpr int SB = ScTraits<F>::MX ? QB : (ScTraits<F>::BLOCK ? NBS : 0);
+  uint4v a[TA][H][64];
+  uint4v b[TB][H][64];
+  uint32_t as[SA > 0 ? SA : 1][64];
+  uint32_t bs[SB > 0 ? SB : 1][64];
+};
+
+template <int F, int WM, int WN, int MTW, int NTW, int ST>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
+    const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
+    const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales, int M, int N,
+    int64_t KC, int ntiles_w, int64_t quads_w, int ngroups, int kc_per_split, int splits,
+    float alpha, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t ldy,
+    float4v* __restrict__ partial, uint32_t* __restrict__ counters) {
+  typedef ScTraits<F> T;
+  typedef ScStage<F, WM, WN, MTW, NTW> Stage;
+  constexpr int NW = WM * WN, H = T::H, TA = Stage::TA, TB = Stage::TB;
+  constexpr int NA = TA * H, NB = TB * H, SA = Stage::SA, SB = Stage::SB;
+  constexpr int ITEMS = NA + NB + SA + SB;
+  constexpr int L = (ITEMS + NW - 1) / NW;  // loads per wave per chunk
+  constexpr int P = MTW * NTW;              // MFMAs per wave per chunk
+  constexpr int CHUNK = 64 * 16 * H;        // bytes of one tile-chunk
+  static_assert(ST >= 3 && ST <= 4, "ring depth");
+  static_assert(L * (ST - 2) <= 63, "vmcnt range");
+  static_assert(TB % 4 == 0, "weight tiles come in quads");
+  static_assert(!T::BLOCK || (NTW * 16 <= 128 && 128 % (NTW * 16) == 0), "a wave's columns in one block");
+  __shared__ Stage stage[ST];
+  __shared__ uint32_t s_flag;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int split = blockIdx.x % splits;
+  const int tilegrp = blockIdx.x / splits;
+  const int ngroup = tilegrp % ngroups;
+  const int mgroup = tilegrp / ngroups;
+  const int64_t c_begin = (int64_t)split * kc_per_split;
+  const int64_t c_end = c_begin + kc_per_split < KC ? c_begin + kc_per_split : KC;
+  const int nch = (int)(c_end - c_begin);
+  const int64_t a_tile0 = (int64_t)mgroup * TA;
+  const int64_t a_quad0 = a_tile0 / 4;
+  const int a_qoff = (int)(a_tile0 % 4);  // nonzero only when TA < 4
+  const int64_t b_tile0 = (int64_t)ngroup * TB;
+
+  // item j of this wave's share of a stage
+  auto issue_item = [&](Stage& sg, int64_t c, int j) {
+    int e = wave + NW * j;
+    e = e < ITEMS ? e : 0;  // waves past the last item repeat item 0 (same bytes, same place)
+    const uint32_t base = lds_offset(&sg);
+    if (e < NA) {
+      const int t = e / H, h = e % H;
+      lds_load16(xcodes + ((a_tile0 + t) * KC + c) * CHUNK + h * 1024, lane * 16,
+                 base + (uint32_t)offsetof(Stage, a) + (t * H + h) * 1024);
+    } else if (e < NA + NB) {
+      const int t = (e - NA) / H, h = (e - NA) % H;
+      const int64_t gt = b_tile0 + t < ntiles_w ? b_tile0 + t : 0;  // past N: tile 0, never stored
+      lds_load16(wcodes + (gt * KC + c) * CHUNK + h * 1024, lane * 16,
+                 base + (uint32_t)offsetof(Stage, b) + (t * H + h) * 1024);
+    } else if (e < NA + NB + SA) {
+      const int q = e - NA - NB;
+      lds_load4(xscales + ((a_quad0 + q) * KC + c) * 256, lane * 4,
+                base + (uint32_t)offsetof(Stage, as) + q * 256);
+    } else {
+      const int q = e - NA - NB - SA;
+      if (T::MX) {
+        const int64_t gq = b_tile0 / 4 + q < quads_w ? b_tile0 / 4 + q : 0;
+        lds_load4(wscales + (gq * KC + c) * 256, lane * 4, base + (uint32_t)offsetof(Stage, bs) + q * 256);
+      } else {  // block FP8: the column block's scale, broadcast to all 64 slots
+        int64_t nb = (b_tile0 * 16) / 128 + q;
+        const int64_t nbs = ((int64_t)ntiles_w * 16) / 128;
+        nb = nb < nbs ? nb : 0;
+        lds_load4(wscales + (nb * KC + c) * 4, 0u, base + (uint32_t)offsetof(Stage, bs) + q * 256);
+      }
+    }
+  };
+
+  float4v acc[MTW][NTW];
+#pragma unroll
+  for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // one chunk: fragments from stage sg, MFMAs, and the refill loads of the
+  // stage `refill` (chunk rc) spread between the MFMAs
+  auto compute = [&](const Stage& sg, Stage& refill, int64_t rc) {
+    int8v b[NTW];
+    int sb[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const int t = wn * NTW + nt;
+      const uint4v q0 = sg.b[t][0][lane];
+      if (H == 1) {
+        b[nt] = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, 0, 0, 0, 0};
+      } else {
+        const uint4v q1 = sg.b[t][H - 1][lane];
+        b[nt] = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+      }
+      sb[nt] = T::MX ? (int)((sg.bs[t / 4][lane] >> (8 * (t % 4))) & 0xFFu) : 127;
+    }
+    float swv = 0.0f;
+    if (T::BLOCK) swv = __uint_as_float(sg.bs[(wn * NTW * 16) / 128][0]);
+    int p = 0;
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) {
+      const int t = wm * MTW + mt;
+      const uint4v q0 = sg.a[t][0][lane];
+      int8v a;
+      if (H == 1) {
+        a = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, 0, 0, 0, 0};
+      } else {
+        const uint4v q1 = sg.a[t][H - 1][lane];
+        a = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+      }
+      const int at = a_qoff + t;  // tile index within the loaded scale quads
+      int sa = 127;
+      if (T::MX) sa = (int)((sg.as[at / 4][lane] >> (8 * (at % 4))) & 0xFFu);
+      float4v s4 = float4v{0.f, 0.f, 0.f, 0.f};
+      if (T::BLOCK) {
+        // row scales of the lane's four accumulator rows 16*at + 4*(lane/16) + i
+        const float* rs = reinterpret_cast<const float*>(&sg.as[at / 4][0]) + 16 * (at % 4) + 4 * (lane >> 4);
+        s4 = float4v{rs[0] * swv, rs[1] * swv, rs[2] * swv, rs[3] * swv};
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+        for (int j = 0; j < L; ++j)
+          if ((j * P) / L == p) issue_item(refill, rc, j);
+        if (T::BLOCK) {
+          const float4v z = float4v{0.f, 0.f, 0.f, 0.f};
+          const float4v part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[nt], z, 0, 0, 0, 127, 0, 127);
+          acc[mt][nt] += part * s4;
+        } else {
+          acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[nt], acc[mt][nt], T::FMT,
+                                                                         T::FMT, 0, sa, 0, sb[nt]);
+        }
+        ++p;
+      }
+    }
+  };
+
+  // Ring: chunk i lives in stage i % ST. Before computing chunk i a wave
+  // waits for its own loads of chunk i, passes the barrier (everyone's have
+  // landed and everyone has finished chunk i-1), then refills stage
+  // (i-1) % ST with chunk i+ST-1 while computing (clamped chunk index past
+  // the end: a static number of loads per chunk).
+#pragma unroll
+  for (int p0 = 0; p0 < ST - 1; ++p0) {
+    const int64_t c = c_begin + p0 < c_end ? c_begin + p0 : c_end - 1;
+#pragma unroll
+    for (int j = 0; j < L; ++j) issue_item(stage[p0], c, j);
+  }
+  for (int i0 = 0; i0 < nch; i0 += ST) {
+#pragma unroll
+    for (int j = 0; j < ST; ++j) {
+      if (i0 + j < nch) {
+        wait_vmcnt<L * (ST - 2)>();
+        stage_barrier();
+        int64_t rc = c_begin + i0 + j + ST - 1;
+        rc = rc < c_end ? rc : c_end - 1;
+        compute(stage[j], stage[(j + ST - 1) % ST], rc);
+      }
+    }
+  }
+  wait_vmcnt<0>();  // no LDS load may still be in flight when the workgroup ends
+
+  float4v frag[P];
+#pragma unroll
+  for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) frag[mt * NTW + nt] = acc[mt][nt];
+  auto row_of = [&](int f, int i) { return (wm * MTW + f / NTW) * 16 + 4 * (lane >> 4) + i; };
+  auto col_of = [&](int f) { return (wn * NTW + f % NTW) * 16 + (lane & 15); };
+  float4v* slab = partial + (int64_t)tilegrp * splits * (NW * P * 64);
+  finish_frags<P, decltype(row_of), decltype(col_of), NW>(
+      frag, row_of, col_of, M, N, mgroup * TA * 16, ngroup * TB * 16, split, splits, alpha, bias, y,
+      ldy, slab, counters + tilegrp, &s_flag);
+}
+
+// ---------------------------------------------------------------------------
+// configurations, plan, launcher
+// ---------------------------------------------------------------------------
+
+// (WM, WN, MTW, NTW, ST) built for every format; FP8 formats skip the ones
+// whose ring does not fit in LDS (see sc_config_fits).
+#define FQL_SC_CONFIGS(X, F)                                                                    \
+  X(F, 1, 4, 1, 4, 4) X(F, 1, 4, 2, 4, 4) X(F, 1, 4, 4, 2, 4) X(F, 2, 2, 4, 4, 3)              \
+  X(F, 2, 4, 4, 4, 3) X(F, 2, 4, 8, 4, 4) X(F, 4, 2, 4, 4, 3) X(F, 1, 4, 1, 2, 4)
+
+static constexpr size_t kLdsLimit = 160 * 1024;
+
+template <int F, int WM, int WN, int MTW, int NTW, int ST>
+static constexpr bool sc_config_fits() {
+  return sizeof(ScStage<F, WM, WN, MTW, NTW>) * ST + 16 <= kLdsLimit;
+}
+
+static bool sc_config_built(int fmt, int wm, int wn, int mtw, int ntw, int st) {
+#define FQL_X(F0, A, B, C, D, E)                                                                 \
+  if (fmt == F0 && wm == A && wn == B && mtw == C && ntw == D && st == E)                        \
+    return sc_config_fits<F0, A, B, C, D, E>();
+  FQL_SC_CONFIGS(FQL_X, SC_MXFP4) FQL_SC_CONFIGS(FQL_X, SC_MXFP8) FQL_SC_CONFIGS(FQL_X, SC_FP8)
+  FQL_SC_CONFIGS(FQL_X, SC_FP8_BLOCK)
+#undef FQL_X
+  return false;
+}
+
+static const char* sc_fmt_name(int f) {
+  return f == SC_MXFP4 ? "mxfp4" : f == SC_MXFP8 ? "mxfp8" : f == SC_FP8 ? "fp8" : "fp8_block";
+}
+
+ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
+  ScPlan p{};
+  p.fmt = fmt;
+  const ScDims w = sc_dims(fmt, N, K, true);
+  const int64_t KC = w.KC, ntiles = w.rows_p / 16;
+  const bool fp4 = fmt == SC_MXFP4;
+  // defaults (MI355X measurements on K = 4096 shapes): one row tile and four
+  // column tiles per wave for decode sizes; 64 x 128 workgroup tiles for
+  // mid-size M; the big 8-wave tiles for large M.
+  int wm = 1, wn = 4, mtw = 1, ntw = 4, st = 4;
+  if (M <= 16) { wm = 1; wn = 4; mtw = 1; ntw = fp4 ? 4 : 2; st = 4; }
+  else if (M <= 32) { wm = 1; wn = 4; mtw = 2; ntw = 4; st = 4; }
+  else if (M <= 512) { wm = 1; wn = 4; mtw = 4; ntw = 2; st = 4; }
+  else if (fp4) { wm = 2; wn = 4; mtw = 8; ntw = 4; st = 4; }
+  else { wm = 4; wn = 2; mtw = 4; ntw = 4; st = 3; }
+  int splits_override = 0;
+  if (const char* e = std::getenv("FQL_SC_PLAN")) {  // benchmarking aid: "wm,wn,mtw,ntw,st,splits"
+    int a = 0, b = 0, c = 0, d = 0, f = 0, s = 0;
+    if (std::sscanf(e, "%d,%d,%d,%d,%d,%d", &a, &b, &c, &d, &f, &s) >= 5 &&
+        sc_config_built(fmt, a, b, c, d, f)) {
+      wm = a; wn = b; mtw = c; ntw = d; st = f; splits_override = s;
+    }
+  }
+  if (!sc_config_built(fmt, wm, wn, mtw, ntw, st)) { wm = 1; wn = 4; mtw = 1; ntw = 4; st = fp4 ? 4 : 3; }
+  if (!sc_config_built(fmt, wm, wn, mtw, ntw, st)) { ntw = 2; st = 4; }
+  p.wm = wm; p.wn = wn; p.mtw = mtw; p.ntw = ntw; p.st = st;
+  const int tile_rows = 16 * wm * mtw, tile_cols = 16 * wn * ntw;
+  p.Mp = round_up(M, std::max(tile_rows, 16));
+  p.ngroups = (ntiles * 16 + tile_cols - 1) / tile_cols;
+  const int64_t groups = p.ngroups * (p.Mp / tile_rows);
+  // split K until about 160 workgroups are in flight (at most 4 ways)
+  int64_t s = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(4, KC), (160 + groups / 2) / groups));
+  if (splits_override > 0) s = std::min<int64_t>(splits_override, KC);
+  p.kc_per_split = (int)((KC + s - 1) / s);
+  p.splits = (int)((KC + p.kc_per_split - 1) / p.kc_per_split);
+  p.groups = groups;
+  const ScDims x = sc_dims(fmt, p.Mp, K, false);
+  p.xcode_bytes = round_up(x.code_bytes, 256);
+  p.xscale_bytes = round_up(std::max<int64_t>(x.scale_bytes, 0), 256);
+  const int64_t slab = (int64_t)p.splits * wm * wn * mtw * ntw * 64 * 16;
+  p.partial_bytes = p.splits > 1 ? round_up(groups * slab, 256) : 0;
+  p.counter_bytes = 64 * 1024;
+  p.total_bytes = p.counter_bytes + p.xcode_bytes + p.xscale_bytes + p.partial_bytes;
+  return p;
+}
+
+std::string describe_sc_plan(const ScPlan& p) {
+  char b[240];
+  std::snprintf(b, sizeof(b),
+                "sc_quant_operand_kernel<%s> + gemm_sc_kernel<%s,WM=%d,WN=%d,MTW=%d,NTW=%d,ST=%d> grid=%lld splits=%d",
+                sc_fmt_name(p.fmt), sc_fmt_name(p.fmt), p.wm, p.wn, p.mtw, p.ntw, p.st,
+                (long long)(p.groups * p.splits), p.splits);
+  return std::string(b);
+}
+
+template <int F, int WM, int WN, int MTW, int NTW, int ST>
+static hipError_t launch_sc_t(const ScPlan& p, const uint8_t* xc, const uint8_t* xs,
+                              const uint8_t* packed, const ScDims& w, int64_t M, int64_t N,
+                              float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
+                              float4v* partial, uint32_t* counters, hipStream_t st) {
+  if constexpr (!sc_config_fits<F, WM, WN, MTW, NTW, ST>()) {
+    return hipErrorInvalidValue;
+  } else {
+    gemm_sc_kernel<F, WM, WN, MTW, NTW, ST><<<(unsigned)(p.groups * p.splits), 64 * WM * WN, 0, st>>>(
+        xc, xs, packed, packed + w.code_bytes, (int)M, (int)N, w.KC, (int)(w.rows_p / 16), w.quads,
+        (int)p.ngroups, p.kc_per_split, p.splits, alpha, bias, y, ldy, partial, counters);
+    return hipGetLastError();
+  }
+}
+
+hipError_t launch_sc_linear(const ScPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                            bool aligned, float inv_scale, const uint8_t* packed, int64_t N,
+                            float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
+                            uint8_t* workspace, hipStream_t st) {
+  const ScDims w = sc_dims(p.fmt, N, K, true);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(workspace);
+  uint8_t* xc = workspace + p.counter_bytes;
+  uint8_t* xs = xc + p.xcode_bytes;
+  float4v* partial = reinterpret_cast<float4v*>(xs + p.xscale_bytes);
+  if (p.splits > 1 && p.groups > p.counter_bytes / 4) return hipErrorInvalidValue;
+  hipError_t e = launch_sc_quant_operand(p.fmt, x, M, K, ldx, aligned, inv_scale, p.Mp, xc, xs, st);
+  if (e != hipSuccess) return e;
+#define FQL_X(F0, A, B, C, D, E)                                                                  \
+  if (p.fmt == F0 && p.wm == A && p.wn == B && p.mtw == C && p.ntw == D && p.st == E)             \
+    return launch_sc_t<F0, A, B, C, D, E>(p, xc, xs, packed, w, M, N, alpha, bias, y, ldy, partial, \
+                                          counters, st);
+  FQL_SC_CONFIGS(FQL_X, SC_MXFP4) FQL_SC_CONFIGS(FQL_X, SC_MXFP8) FQL_SC_CONFIGS(FQL_X, SC_FP8)
+  FQL_SC_CONFIGS(FQL_X, SC_FP8_BLOCK)
+#undef FQL_X
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fql

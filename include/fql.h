@@ -50,6 +50,9 @@ extern "C" {
 /* Weight/activation formats (fql_can_implement). */
 #define FQL_FMT_NVFP4 1
 #define FQL_FMT_MXFP4 2
+#define FQL_FMT_MXFP8 3
+#define FQL_FMT_FP8 4       /* per-tensor FP8 */
+#define FQL_FMT_FP8_BLOCK 5 /* block FP8: 1 x 128 activation, 128 x 128 weight groups */
 
 /* Library version (major*10000 + minor*100 + patch). */
 int fql_version(void);
@@ -69,7 +72,10 @@ int fql_is_supported(int device, char* reason, size_t reason_len);
  * Format-level constraints, in the spirit of can_implement(): returns 1 if a
  * layer with these sizes can run, else 0 with the reason. NVFP4 needs
  * K % 16 == 0, N >= 1, K >= 16, and hadamard_block in {0, 16, 32, 64, 128}
- * with K % hadamard_block == 0. MXFP4 needs K % 32 == 0, N >= 1, K >= 32 and
+ * with K % hadamard_block == 0. MXFP4, MXFP8 and per-tensor FP8 need
+ * K % 32 == 0, N >= 1, K >= 32 and hadamard_block == 0. Block FP8 needs N and
+ * K multiples of 128 (the B12X write-up's can_implement: activation group
+ * (1, 128), weight group (128, 128), 128-aligned features) and
  * hadamard_block == 0. N and K are at most 2^24.
  */
 int fql_can_implement(int format, int64_t N, int64_t K, int hadamard_block, char* reason,
@@ -230,6 +236,76 @@ int fql_linear_mxfp4_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t
 int fql_linear_mxfp4(const void* x, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
                      int64_t N, float alpha, const void* bias, void* y, int64_t ldy,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * MXFP8 (B12X write-up, Implementation: the MXFP8 linear kernel; OCP
+ * Microscaling v1.0): E4M3 codes with one E8M0 scale byte per 32 elements
+ * along K. Quantizer per 32-block: E = floor(log2 max|v|) - 8 clamped to
+ * [-127, 127] (all-zero block: -127), scale byte E + 127,
+ * q = E4M3_RNE_satfinite(fl32(v * 2^-E)). Codes [rows][K] (one byte per
+ * element), scales [rows][K/32]. Same conventions as the MXFP4 calls.
+ * ------------------------------------------------------------------------- */
+int fql_quant_mxfp8(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
+                    uint8_t* scales, void* stream);
+int fql_quant_mxfp8_f32(const float* w, int64_t N, int64_t K, int64_t ldw, uint8_t* codes,
+                        uint8_t* scales, void* stream);
+int fql_packed_mxfp8_bytes(int64_t N, int64_t K, size_t* bytes);
+int fql_pack_weight_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K,
+                          void* packed, size_t packed_bytes, void* stream);
+int fql_linear_mxfp8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
+int fql_linear_mxfp8_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t buf_len);
+/* y = bf16(alpha * (x_q @ w_q^T) + bias) with x quantized as fql_quant_mxfp8;
+ * arguments as fql_linear_mxfp4. */
+int fql_linear_mxfp8(const void* x, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
+                     int64_t N, float alpha, const void* bias, void* y, int64_t ldy,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Per-tensor FP8 (B12X write-up, Implementation: the per-tensor FP8 kernel
+ * quantizes the activation with a static per-tensor scale, packs the weight
+ * ahead of time and merges the input and weight scales into one output
+ * scale). q = E4M3_RNE_satfinite(fl32(v * fl32(1 / scale))), scale > 0
+ * (calibration: fl32(amax / 448), amax from fql_amax_bf16 / fql_amax_f32).
+ * Codes [rows][K], K % 32 == 0.
+ * ------------------------------------------------------------------------- */
+int fql_quant_fp8(const void* x, int64_t M, int64_t K, int64_t ldx, float scale, uint8_t* codes,
+                  void* stream);
+int fql_quant_fp8_f32(const float* w, int64_t N, int64_t K, int64_t ldw, float scale,
+                      uint8_t* codes, void* stream);
+int fql_packed_fp8_bytes(int64_t N, int64_t K, size_t* bytes);
+/* codes [N][K] (16-byte aligned) -> packed operand order. */
+int fql_pack_weight_fp8(const uint8_t* codes, int64_t N, int64_t K, void* packed,
+                        size_t packed_bytes, void* stream);
+int fql_linear_fp8_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
+int fql_linear_fp8_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t buf_len);
+/* y = bf16(alpha * (x_q @ w_q^T) + bias): x_q = fql_quant_fp8(x, input_scale),
+ * alpha = fl32(input_scale * weight_scale) (the merged output scale). */
+int fql_linear_fp8(const void* x, int64_t M, int64_t K, int64_t ldx, float input_scale,
+                   const void* w_packed, int64_t N, float alpha, const void* bias, void* y,
+                   int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Block FP8 (B12X write-up, Implementation: the block FP8 kernel: activation
+ * group (1, 128), weight group (128, 128), 128-aligned features, float32
+ * scales; UE8M0 weight scales are widened to float32 by the caller).
+ * Per group: s = fl32(max|v| / 448), q = E4M3_RNE_satfinite(fl32(v * fl32(1/s)))
+ * (s = 0: q = 0). Activation: codes [M][K], scales float [M][K/128].
+ * Weight: codes [N][K], scales float [N/128][K/128]. The GEMM adds every
+ * 128-deep partial product times s_x[m][kb] * s_w[nb][kb] in float32.
+ * ------------------------------------------------------------------------- */
+int fql_quant_fp8_block(const void* x, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
+                        float* scales, void* stream);
+int fql_quant_fp8_block_weight_f32(const float* w, int64_t N, int64_t K, int64_t ldw,
+                                   uint8_t* codes, float* scales, void* stream);
+int fql_packed_fp8_block_bytes(int64_t N, int64_t K, size_t* bytes);
+int fql_pack_weight_fp8_block(const uint8_t* codes, const float* scales, int64_t N, int64_t K,
+                              void* packed, size_t packed_bytes, void* stream);
+int fql_linear_fp8_block_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
+int fql_linear_fp8_block_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t buf_len);
+/* y = bf16(alpha * sum_kb s_x s_w (x_q @ w_q^T)_kb + bias), alpha normally 1. */
+int fql_linear_fp8_block(const void* x, int64_t M, int64_t K, int64_t ldx, const void* w_packed,
+                         int64_t N, float alpha, const void* bias, void* y, int64_t ldy,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,12 +23,16 @@ Block FP8 (write-up: activation groups of 1 x 128, weight groups of
 stored as UE8M0 are widened to float32 before the GEMM), per group:
   B1  a = max |v| over the group.
   B2  s = fl32(a / 448) (float32 scale; a = 0 gives s = 0).
-  B3  r = fl32(1 / s) (r = 0 when s = 0).
+  B3  r = fl32(1 / s) (r = 0 when s = 0; the largest finite float32 when
+      1 / s overflows, i.e. a group whose maximum is a float32 subnormal
+      below 448 * 2^-128: its products v * r then stay finite).
   B4  q = E4M3_RNE_satfinite(fl32(v * r)), sign kept.
   Scales: activation [M][K/128], weight [N/128][K/128], float32.
   Reading: the pages give the group shapes and the float32 scale type but no
   scale rule; amax / 448 (the largest element maps onto the largest E4M3
   value) and the multiply by the rounded reciprocal are the plainest choice.
+  The overflow rule of B3 is ours (the pages are silent; without it a
+  subnormal group would multiply by infinity).
 
 Per-tensor FP8 (write-up: the activation is quantized with a static
 per-tensor scale and the two scales are merged into one output scale):
@@ -106,12 +110,16 @@ def scale_from_amax(amax):
     return _f32(np.asarray(amax, dtype=np.float32).astype(np.float64) / 448.0)
 
 
+FLT_MAX = float(np.finfo(np.float32).max)
+
+
 def reciprocal(s):
-    """B3: r = fl32(1 / s), 0 where s == 0."""
+    """B3: r = fl32(1 / s), 0 where s == 0, and the largest finite float32
+    where 1/s overflows (s below 2^-128, a group of float32 subnormals)."""
     s = np.asarray(s, dtype=np.float32)
     with np.errstate(divide="ignore"):
         r = np.where(s > 0, 1.0 / np.where(s > 0, s.astype(np.float64), 1.0), 0.0)
-    return _f32(r)
+    return _f32(np.minimum(r, FLT_MAX))
 
 
 def encode_with_scale(v, r):

@@ -99,16 +99,15 @@ def test_invalid_scalars_rejected():
 
 
 def test_mxfp4_sizes_and_rules():
-    # packed MXFP4: N padded to 16, K to 128; codes Np*Kp/2, then 256-byte scale
-    # groups (64 lanes x 4 chunks) per 16-row tile and 4-chunk group
+    # packed MXFP4: N padded to 16, K to 128; codes Np*Kp/2, then one 256-byte
+    # scale block (64 lanes x 4 row tiles) per 64-row quad and 128-deep chunk
     def expect(N, K):
         Np, Kp = -(-N // 16) * 16, -(-K // 128) * 128
-        kc4 = -(-(Kp // 128) // 4)
-        return Np * Kp // 2 + (Np // 16) * kc4 * 256
+        return Np * Kp // 2 + (-(-Np // 64)) * (Kp // 128) * 256
     assert fql.packed_mxfp4_bytes(4096, 4096) == expect(4096, 4096) == 4096 * 2048 + 4096 * 128
     assert fql.packed_mxfp4_bytes(100, 96) == expect(100, 96)
     assert fql.linear_mxfp4_workspace_bytes(1, 6144, 4096) > 0
-    assert "gemm_mx4_kernel" in fql.linear_mxfp4_plan(8192, 4096, 4096)
+    assert "gemm_sc_kernel<mxfp4," in fql.linear_mxfp4_plan(8192, 4096, 4096)
     assert fql.can_implement(4096, 4096, 0, fmt=fql.FMT_MXFP4) == (True, "")
     ok, why = fql.can_implement(4096, 4112, 0, fmt=fql.FMT_MXFP4)
     assert not ok and "32" in why
@@ -131,4 +130,47 @@ def test_mxfp4_invalid_arguments_rejected():
     assert lib.fql_linear_mxfp4(p, 1, 64, 64, p, 64, 1.0, null, p, 32, p, 1 << 20, null) == -1
     assert lib.fql_linear_mxfp4(p, 1, 64, 64, p, 64, 1.0, null, p, 64, p, 16, null) == -4
     assert lib.fql_linear_mxfp4(p, 1, 64, 64, p, 64, float("nan"), null, p, 64, p, 1 << 20, null) == -1
+    assert lib.fql_last_error().decode()
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "fp8", "fp8_block"])
+def test_fp8_family_sizes(fmt):
+    N, K = 14336, 4096
+    Np, KC = N, K // 128
+    code = N * K
+    scale = {"mxfp8": (-(-Np // 64)) * KC * 256, "fp8": 0,
+             "fp8_block": -(-((N // 128) * KC * 4) // 256) * 256}[fmt]
+    assert fql._size_query(f"fql_packed_{fmt}_bytes", N, K) == code + scale
+    assert fql.linear_sc_workspace_bytes(fmt, 4096, N, K) >= 64 * 1024 + 4096 * K
+    assert f"gemm_sc_kernel<{fmt}," in fql.linear_sc_plan(fmt, 1, N, K)
+
+
+def test_fp8_family_can_implement():
+    assert fql.can_implement(14336, 4096, 0, fmt=fql.FMT_MXFP8)[0]
+    assert fql.can_implement(14336, 4096, 0, fmt=fql.FMT_FP8)[0]
+    assert fql.can_implement(14336, 4096, 0, fmt=fql.FMT_FP8_BLOCK)[0]
+    ok, why = fql.can_implement(14336 + 64, 4096, 0, fmt=fql.FMT_FP8_BLOCK)
+    assert not ok and "128" in why
+    ok, why = fql.can_implement(14336, 4096 + 32, 0, fmt=fql.FMT_FP8_BLOCK)
+    assert not ok and "128" in why
+    assert fql.can_implement(100, 4096 + 32, 0, fmt=fql.FMT_FP8)[0]
+
+
+def test_fp8_family_invalid_arguments_rejected():
+    lib = fql.lib()
+    p = ctypes.c_void_p(256)
+    null = ctypes.c_void_p(0)
+    # per-tensor: bad scales, K % 32
+    for s in (0.0, -2.0, float("inf"), float("nan")):
+        assert lib.fql_quant_fp8(p, 4, 64, 64, s, p, null) == -1
+    assert lib.fql_quant_fp8(p, 4, 48, 48, 1.0, p, null) == -1
+    assert lib.fql_linear_fp8(p, 1, 64, 64, 0.0, p, 64, 1.0, null, p, 64, p, 1 << 20, null) == -1
+    # block: K and N multiples of 128
+    assert lib.fql_quant_fp8_block(p, 4, 96, 96, p, p, null) == -1
+    assert lib.fql_quant_fp8_block_weight_f32(p, 100, 128, 128, p, p, null) == -1
+    assert lib.fql_pack_weight_fp8_block(p, p, 64, 128, p, 1 << 20, null) == -1
+    assert lib.fql_linear_fp8_block(p, 1, 128, 128, p, 128, 1.0, null, p, 128, p, 16, null) == -4
+    # MXFP8: workspace too small, ldy < N
+    assert lib.fql_linear_mxfp8(p, 1, 64, 64, p, 64, 1.0, null, p, 64, p, 16, null) == -4
+    assert lib.fql_linear_mxfp8(p, 1, 64, 64, p, 64, 1.0, null, p, 32, p, 1 << 20, null) == -1
     assert lib.fql_last_error().decode()

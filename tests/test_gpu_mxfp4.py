@@ -189,19 +189,5 @@ def test_mx_linear_identity_weight_exact():
     got = F.bf16_bits_to_f64(dev_bf16_to_bits(y))
     assert np.array_equal(got, F.bf16_bits_to_f64(F.bf16_round_bits(0.25 * xhat)))
 
-
-# Every MXFP4 GEMM configuration built into the library (workgroup tile of
-# (MT*16) rows x (4*NT*16) columns, ring depth ST), with and without split K,
-# on a ragged shape: several row groups, 9 chunks of 128 (a partial scale
-# group), a partial column tile.
-MX4_CONFIGS = [(1, 4, 4), (2, 4, 4), (4, 4, 4), (8, 4, 4), (4, 2, 4), (8, 2, 4)]
-
-
-@pytest.mark.parametrize("splits", [1, 3])
-@pytest.mark.parametrize("mt,nt,st", MX4_CONFIGS)
-def test_mx_linear_every_config(mt, nt, st, splits, monkeypatch):
-    M, K, N = 150, 1152, 400
-    monkeypatch.setenv("FQL_MX_PLAN", f"{mt},{nt},{st},{splits}")
-    plan = fql.linear_mxfp4_plan(M, N, K)
-    assert f"gemm_mx4_kernel<MT={mt},NT={nt},ST={st}>" in plan and f"splits={splits}" in plan, plan
-    _run_linear("tiny", M, K, N, True, alpha=1.5, label=f"mx4<{mt},{nt},{st}> splits={splits}")
+# Every GEMM configuration of the scaled formats (MXFP4 included) is covered
+# by tests/test_gpu_fp8.py::test_every_sc_config.

@@ -249,3 +249,17 @@ def test_tensor_linear_matches_fsum_and_alpha():
     # and the quantized product approximates the float product (FP8 error level)
     yf = x.astype(np.float64) @ w.T.astype(np.float64)
     assert np.linalg.norm(y - yf) / np.linalg.norm(yf) < 0.05
+
+
+def test_block_subnormal_group_uses_largest_finite_reciprocal():
+    # a group of float32 subnormals: 1/s overflows, r is the largest finite float32
+    x = np.zeros((1, 128), np.float32)
+    x[0, :] = np.float32(1e-39)
+    x[0, 7] = np.float32(-3e-39)
+    x[0, 9] = 0.0
+    c, s = P.quant_fp8_block_act(x)
+    assert 0 < float(s[0, 0]) < 2.0 ** -126
+    r = float(np.finfo(np.float32).max)
+    for k in (0, 7, 9):
+        assert c[0, k] == _e4m3_nearest(_f32(float(x[0, k]) * r))
+    assert c[0, 9] == 0 and np.all(c & 0x7F != 0x7F)
