@@ -17,9 +17,10 @@ step / step time). `roofline` describes the GEMM calls against HBM bandwidth
 output element + bias), timed per call with HIP events on the launch stream.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
-`--format mxfp4` runs the MXFP4 sibling layer (E2M1 + E8M0 per 32, scaled FP4
-MFMA) instead; its natural workload is `siblings` (K=4096, N=14336, M=1 and
-4096), and its algorithmic weight bytes are 0.53125 B per element.
+`--format mxfp4|mxfp8|fp8|fp8_block` runs one of the sibling layers (scaled
+FP4/FP8 MFMA) instead; their natural workload is `siblings` (K=4096,
+N=14336, M=1 and 4096). Algorithmic weight bytes per element: MXFP4 0.53125,
+MXFP8 1.03125, per-tensor FP8 1, block FP8 1 + 4/128^2.
 """
 
 import argparse
@@ -37,9 +38,20 @@ F16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 512 << 20
 
 WORKLOAD_KEYS = ("decode", "prefill", "hadamard", "tiny", "siblings")
-FORMAT_KEYS = ("nvfp4", "mxfp4")
-# algorithmic weight bytes per element: 4-bit code + one scale byte per block
-WEIGHT_BYTES = {"nvfp4": 0.5 + 1.0 / 16, "mxfp4": 0.5 + 1.0 / 32}
+FORMAT_KEYS = ("nvfp4", "mxfp4", "mxfp8", "fp8", "fp8_block")
+# algorithmic weight bytes per element: code + scale bytes per element
+WEIGHT_BYTES = {"nvfp4": 0.5 + 1.0 / 16, "mxfp4": 0.5 + 1.0 / 32, "mxfp8": 1.0 + 1.0 / 32,
+                "fp8": 1.0, "fp8_block": 1.0 + 4.0 / (128 * 128)}
+# dense MFMA peak the format runs on (TFLOP/s): NVFP4 multiplies exactly
+# dequantized float16 operands; the others run on the scaled FP4 / FP8 MFMA
+MFMA_PEAK = {"nvfp4": 2500.0, "mxfp4": 10100.0, "mxfp8": 5000.0, "fp8": 5000.0, "fp8_block": 5000.0}
+FORMAT_DTYPE = {
+    "nvfp4": "nvfp4 (e2m1 x e4m3/16) -> f16 MFMA, f32 accumulate, bf16 out",
+    "mxfp4": "mxfp4 (e2m1 x e8m0/32) -> scaled fp4 MFMA, f32 accumulate, bf16 out",
+    "mxfp8": "mxfp8 (e4m3 x e8m0/32) -> scaled fp8 MFMA, f32 accumulate, bf16 out",
+    "fp8": "fp8 e4m3, per-tensor scales -> fp8 MFMA, f32 accumulate, bf16 out",
+    "fp8_block": "fp8 e4m3, 1x128 / 128x128 f32 scales -> fp8 MFMA + f32 promotion, bf16 out",
+}
 WORKLOAD_NAMES = {
     "decode": "decode: Llama-3.1-8B qkv/gate_up/down at M=1,8,32,128, bias",
     "prefill": "prefill: Llama-3.1-8B qkv/gate_up/down at M=2048,8192, 1% outlier channels",
@@ -105,8 +117,8 @@ def _kernel_of(M, N, K, fmt="nvfp4"):
     """The kernel that carries one linear call of this shape (the library's own plan)."""
     import fp8_quantized_linear_amd as fql
 
-    if fmt == "mxfp4":
-        return fql.linear_mxfp4_plan(M, N, K).split(" grid=")[0].split(" + ")[-1]
+    if fmt != "nvfp4":
+        return fql.linear_sc_plan(fmt, M, N, K).split(" grid=")[0].split(" + ")[-1]
     return fql.linear_plan(M, N, K).split(" grid=")[0]
 
 
@@ -127,10 +139,13 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4"):
         key = (name, K, N, hbk)
         if key not in weights:
             W = torch.from_numpy(synthetic.weight(N, K, config=workload)).to(dev)
-            if fmt == "mxfp4":
-                w0 = fql.MXFP4Weight.from_float(W)
-            else:
+            if fmt == "nvfp4":
                 w0 = fql.NVFP4Weight.from_float(W, input_global_scale=1.0, hadamard_block=hbk)
+            elif fmt == "fp8":
+                w0 = fql.FP8Weight.from_float(W, input_scale=1.0)
+            else:
+                w0 = {"mxfp4": fql.MXFP4Weight, "mxfp8": fql.MXFP8Weight,
+                      "fp8_block": fql.FP8BlockWeight}[fmt].from_float(W)
             del W
             nbytes = w0.packed.numel()
             ncopies = max(1, -(-ROTATE_BYTES // nbytes))
@@ -139,18 +154,21 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4"):
         w0, copies = weights[key]
         xb = synthetic.activations(synthetic.WORKLOADS[workload]["x"], M, K, config=workload)
         x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
-        if fmt == "mxfp4":
-            objs = [fql.MXFP4Weight(p, N, K) for p in copies]
-        else:
+        if fmt == "nvfp4":
             gx = fql.global_scale_from_amax(fql.amax(x, hbk).item())
             objs = [fql.NVFP4Weight(p, N, K, gx, w0.weight_global_scale, hbk) for p in copies]
+        elif fmt == "fp8":
+            sx = fql.fp8_scale_from_amax(fql.amax(x).item())
+            objs = [fql.FP8Weight(p, N, K, w0.weight_scale, sx) for p in copies]
+        else:
+            objs = [type(w0)(p, N, K) for p in copies]
         bias = None
         if with_bias:
             bias = torch.from_numpy(synthetic.bias(N, config=workload).view(np.int16)).view(
                 torch.bfloat16).to(dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        wsb = (fql.linear_mxfp4_workspace_bytes(M, N, K) if fmt == "mxfp4"
-               else fql.linear_workspace_bytes(M, N, K))
+        wsb = (fql.linear_workspace_bytes(M, N, K) if fmt == "nvfp4"
+               else fql.linear_sc_workspace_bytes(fmt, M, N, K))
         ws = fql.new_workspace(wsb, dev)
         setups.append(dict(M=M, N=N, K=K, name=name, hb=hbk, x=x, objs=objs, bias=bias, y=y,
                            ws=ws, flops=2.0 * M * N * K, bytes=_alg_bytes(M, N, K, with_bias, fmt),
@@ -158,7 +176,8 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4"):
     torch.cuda.synchronize()
     n = len(setups)
 
-    linear = fql.linear_mxfp4 if fmt == "mxfp4" else fql.linear_nvfp4
+    linear = {"nvfp4": fql.linear_nvfp4, "mxfp4": fql.linear_mxfp4, "mxfp8": fql.linear_mxfp8,
+              "fp8": fql.linear_fp8, "fp8_block": fql.linear_fp8_block}[fmt]
 
     def call(s, copy_index):
         w = s["objs"][copy_index % len(s["objs"])]
@@ -239,8 +258,9 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4"):
                 alg_bytes=alg_bytes, detail=detail, dominant=(dom_name, dom))
 
 
-def cpu_baseline_mx(workload, budget_s=12.0, n_rows=2048):
-    """The MXFP4 oracle on a bounded sample of the workload (as cpu_baseline)."""
+def cpu_baseline_sc(workload, fmt, budget_s=12.0, n_rows=2048):
+    """The sibling format's oracle on a bounded sample of the workload (as cpu_baseline)."""
+    import oracle.fp8 as P
     import oracle.mx as X
     import synthetic
 
@@ -250,6 +270,27 @@ def cpu_baseline_mx(workload, budget_s=12.0, n_rows=2048):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+
+    def quant_w(W):
+        if fmt == "mxfp4":
+            return X.quant_mxfp4(W)
+        if fmt == "mxfp8":
+            return P.quant_mxfp8(W)
+        if fmt == "fp8_block":
+            return P.quant_fp8_block_weight(W)
+        s = P.scale_from_amax(np.abs(W).max())
+        return P.quant_fp8_tensor(W, s), s
+
+    def layer(x, wq):
+        if fmt == "mxfp4":
+            return X.linear_mxfp4(*X.quant_mxfp4(x), *wq)
+        if fmt == "mxfp8":
+            return P.linear_mxfp8(*P.quant_mxfp8(x), *wq)
+        if fmt == "fp8_block":
+            return P.linear_fp8_block(*P.quant_fp8_block_act(x), *wq)
+        sx = P.scale_from_amax(np.abs(x).max())
+        return P.linear_fp8_tensor(P.quant_fp8_tensor(x, sx), wq[0], P.output_scale(sx, wq[1]))
+
     cases = _cases(workload)
     wcache = {}
     flops = t_total = 0.0
@@ -258,13 +299,12 @@ def cpu_baseline_mx(workload, budget_s=12.0, n_rows=2048):
         for (M, name, K, N, hb, with_bias) in cases:
             ns = min(N, n_rows)
             if name not in wcache:
-                wcache[name] = X.quant_mxfp4(synthetic.weight(N, K, config=workload)[:ns])
-            wc, wsc = wcache[name]
+                wcache[name] = quant_w(synthetic.weight(N, K, config=workload)[:ns])
             Mr = min(M, 512)
             xb = synthetic.activations(synthetic.WORKLOADS[workload]["x"], Mr, K, config=workload)
             x = synthetic.bf16_bits_to_f32(xb)
             t0 = time.perf_counter()
-            X.linear_mxfp4(*X.quant_mxfp4(x), wc, wsc)
+            layer(x, wcache[name])
             t_total += time.perf_counter() - t0
             flops += 2.0 * Mr * ns * K
         passes += 1
@@ -361,8 +401,7 @@ def main():
     dom_name, dom = r["dominant"]
     # binding bound of the dominant kernel: HBM bytes vs f16-MFMA flops (the exact
     # NVFP4 path multiplies dequantized float16 operands), whichever needs more time
-    # (MXFP4 runs on the scaled FP4 MFMA itself, so its compute peak is the FP4 one)
-    mfma_peak = FP4_PEAK_TFLOPS if args.format == "mxfp4" else F16_PEAK_TFLOPS
+    mfma_peak = MFMA_PEAK[args.format]
     t_hbm = dom["bytes"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = dom["flops"] / (mfma_peak * 1e12)
     if t_hbm >= t_mfma:
@@ -392,17 +431,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("mxfp4 (e2m1 x e8m0/32) -> scaled fp4 MFMA, f32 accumulate, bf16 out"
-                  if args.format == "mxfp4"
-                  else "nvfp4 (e2m1 x e4m3/16) -> f16 MFMA, f32 accumulate, bf16 out"),
+        "dtype": FORMAT_DTYPE[args.format],
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.workload], "cases": len(r["detail"]),
                    "timing": "HIP graph replay per step, weights rotated over >= 512 MB"},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = (cpu_baseline_mx(args.workload) if args.format == "mxfp4"
-                               else cpu_baseline(args.workload))
+        out["cpu_baseline"] = (cpu_baseline(args.workload) if args.format == "nvfp4"
+                               else cpu_baseline_sc(args.workload, args.format))
     if args.detail:
         for d in r["detail"]:
             print(json.dumps(d), file=sys.stderr)

@@ -128,7 +128,10 @@ ScDims sc_dims(int fmt, int64_t rows, int64_t K, bool weight);
 // Workspace: [64 KiB arrival counters | activation codes | activation scales | split-K slabs].
 struct ScPlan {
   int fmt;
-  int wm, wn, mtw, ntw, st;  // wave grid, 16x16 tiles per wave, LDS ring depth
+  int kind;                  // 0: LDS-ring GEMM, 1: register-streaming GEMV (small M)
+  int wm, wn, mtw, ntw, st;  // GEMM: wave grid, 16x16 tiles per wave, LDS ring depth;
+                             // GEMV: wn = waves splitting K, mtw = row tiles,
+                             //       ntw = column tiles per workgroup, st = chunks in flight
   int64_t Mp, groups, ngroups;
   int splits, kc_per_split;
   int64_t counter_bytes, xcode_bytes, xscale_bytes, partial_bytes, total_bytes;

@@ -103,12 +103,12 @@ __global__ __launch_bounds__(64 * W) void linear_gemv_kernel(
   auto load_codes = [&](int i, int64_t c) {
     c = c < c_last ? c : c_last;  // unconditional, clamped: static outstanding-load count
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) bq[j][i] = qp[j][c * 64];
+    for (int j = 0; j < NTW; ++j) bq[j][i] = __builtin_nontemporal_load(&qp[j][c * 64]);
   };
   auto load_group = [&](int q, int64_t c_first) {
     const int64_t c = c_first < c_last ? c_first : c_last;
 #pragma unroll
-    for (int j = 0; j < NTW; ++j) sg[j][q] = sp[j][(c / 4) * 32];
+    for (int j = 0; j < NTW; ++j) sg[j][q] = __builtin_nontemporal_load(&sp[j][(c / 4) * 32]);
   };
   auto load_slot = [&](int i, int64_t c) {
     load_codes(i, c);
@@ -299,7 +299,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
                   ((t * KC4) * 32 + (lane & 15) * 2 + (lane >> 5)) * 4;
   }
   // scale dword of chunk c in the 4-chunk group layout
-  auto bs_at = [&](int nt, int64_t c) -> uint32_t { return bs_base[nt][(c >> 2) * 128 + (c & 3)]; };
+  auto bs_at = [&](int nt, int64_t c) -> uint32_t {
+    return __builtin_nontemporal_load(&bs_base[nt][(c >> 2) * 128 + (c & 3)]);
+  };
 
   float4v acc[MT][NT];
 #pragma unroll
@@ -324,9 +326,9 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
   for (int f = 0; f < AM; ++f) ar1[f] = *a_src(f, clampc(c_begin + 1));
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {  // invalid tiles read tile 0 (in bounds, never stored)
-    bq0[nt] = bq_base[nt][c_begin * 64];
+    bq0[nt] = __builtin_nontemporal_load(&bq_base[nt][c_begin * 64]);
     bs0[nt] = bs_at(nt, c_begin);
-    bq1[nt] = bq_base[nt][clampc(c_begin + 1) * 64];
+    bq1[nt] = __builtin_nontemporal_load(&bq_base[nt][clampc(c_begin + 1) * 64]);
     bs1[nt] = bs_at(nt, clampc(c_begin + 1));
   }
   __syncthreads();
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
     for (int f = 0; f < AM; ++f) ar_load[f] = *a_src(f, c2);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      bq[nt] = bq_base[nt][c2 * 64];
+      bq[nt] = __builtin_nontemporal_load(&bq_base[nt][c2 * 64]);
       bs[nt] = bs_at(nt, c2);
     }
     __syncthreads();

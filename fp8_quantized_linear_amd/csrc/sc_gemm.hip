@@ -84,7 +84,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
   constexpr int L = (ITEMS + NW - 1) / NW;  // loads per wave per chunk
   constexpr int P = MTW * NTW;              // MFMAs per wave per chunk
   constexpr int CHUNK = 64 * 16 * H;        // bytes of one tile-chunk
-  static_assert(ST >= 3 && ST <= 4, "ring depth");
+  static_assert(ST >= 3 && ST <= 8, "ring depth");
   static_assert(L * (ST - 2) <= 63, "vmcnt range");
   static_assert(TB % 4 == 0, "weight tiles come in quads");
   static_assert(!T::BLOCK || (NTW * 16 <= 128 && 128 % (NTW * 16) == 0), "a wave's columns in one block");
@@ -241,6 +241,196 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// small-M GEMV: per-wave LDS rings, no workgroup barrier in the loop
+// ---------------------------------------------------------------------------
+//
+// For M <= 32 the call is a stream over the weight: every weight byte is used
+// once. W waves of a workgroup share NT 16-column tiles and split the K range;
+// each wave streams its own chunks (activation tiles, weight tiles, scales)
+// into a private LDS ring of D stages with direct global->LDS loads and waits
+// only for its own loads (explicit vmcnt; no barrier until the end), so D
+// chunks per wave are always in flight. The W partial sums are added in wave
+// order through LDS at the end (deterministic, no global atomics).
+
+// Wait until at most k chunks of L loads each are still in flight (k <= K).
+template <int L, int K>
+struct WaitChunks {
+  static __device__ __forceinline__ void run(int k) {
+    if (k >= K) wait_vmcnt<L * K>();
+    else WaitChunks<L, K - 1>::run(k);
+  }
+};
+template <int L>
+struct WaitChunks<L, 0> {
+  static __device__ __forceinline__ void run(int) { wait_vmcnt<0>(); }
+};
+
+template <int F, int MT, int NT>
+struct ScvStage {
+  static constexpr int H = ScTraits<F>::H;
+  uint4v a[MT][H][64];
+  uint4v b[NT][H][64];
+  uint32_t sa[64];  // MX: A scale quad dword; block FP8: A row scales (float bits)
+  uint32_t sb[64];  // MX: B scale quad dword; block FP8: the column block's scale (broadcast)
+};
+
+template <int F, int W, int MT, int NT, int D>
+__global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
+    const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
+    const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales, int M, int N,
+    int64_t KC, int ntiles_w, int64_t quads_w, float alpha, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ y, int64_t ldy) {
+  typedef ScTraits<F> T;
+  typedef ScvStage<F, MT, NT> Stage;
+  constexpr int H = T::H;
+  constexpr int64_t CHUNK = 1024 * H;
+  constexpr int L = MT * H + NT * H + (T::MX || T::BLOCK ? 2 : 0);  // loads per chunk
+  static_assert(MT >= 1 && MT <= 4 && (NT == 1 || NT == 2 || NT == 4), "tiles within one scale quad");
+  static_assert(L * (D - 1) <= 63, "vmcnt range");
+  __shared__ Stage ring[W][D];
+  static_assert(sizeof(ring) >= sizeof(float4v) * W * MT * NT * 64, "reduction buffer aliases the ring");
+  float4v(*red)[MT * NT][64] = reinterpret_cast<float4v(*)[MT * NT][64]>(&ring[0][0]);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tile0 = (int64_t)blockIdx.x * NT;
+  const int64_t cpw = (KC + W - 1) / W;
+  const int64_t c0 = (int64_t)wave * cpw < KC ? (int64_t)wave * cpw : KC;
+  const int64_t c1 = c0 + cpw < KC ? c0 + cpw : KC;
+  const int n = (int)(c1 - c0);
+
+  int64_t bt[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) bt[nt] = tile0 + nt < ntiles_w ? tile0 + nt : ntiles_w - 1;  // past N: never stored
+  const int64_t bquad = tile0 / 4 < quads_w ? tile0 / 4 : quads_w - 1;
+  const int64_t nbs = ((int64_t)ntiles_w * 16) / 128;
+  const int64_t nb = (tile0 * 16) / 128 < nbs ? (tile0 * 16) / 128 : (nbs > 0 ? nbs - 1 : 0);
+
+  auto issue = [&](Stage& sg, int64_t c) {
+    const uint32_t base = lds_offset(&sg);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+        lds_load16(xcodes + (mt * KC + c) * CHUNK + h * 1024, lane * 16,
+                   base + (uint32_t)offsetof(Stage, a) + (mt * H + h) * 1024);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int h = 0; h < H; ++h)
+        lds_load16(wcodes + (bt[nt] * KC + c) * CHUNK + h * 1024, lane * 16,
+                   base + (uint32_t)offsetof(Stage, b) + (nt * H + h) * 1024);
+    if (T::MX) {
+      lds_load4(xscales + c * 256, lane * 4, base + (uint32_t)offsetof(Stage, sa));
+      lds_load4(wscales + (bquad * KC + c) * 256, lane * 4, base + (uint32_t)offsetof(Stage, sb));
+    } else if (T::BLOCK) {
+      lds_load4(xscales + c * 256, lane * 4, base + (uint32_t)offsetof(Stage, sa));
+      lds_load4(wscales + (nb * KC + c) * 4, 0u, base + (uint32_t)offsetof(Stage, sb));
+    }
+  };
+
+  float4v acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Stage& sg) {
+    int8v b[NT];
+    int sb[NT];
+    const uint32_t sbw = sg.sb[lane];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint4v q0 = sg.b[nt][0][lane];
+      if (H == 1) {
+        b[nt] = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, 0, 0, 0, 0};
+      } else {
+        const uint4v q1 = sg.b[nt][H - 1][lane];
+        b[nt] = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+      }
+      sb[nt] = T::MX ? (int)((sbw >> (8 * ((tile0 + nt) % 4))) & 0xFFu) : 127;
+    }
+    const float swv = T::BLOCK ? __uint_as_float(sbw) : 0.0f;
+    const uint32_t saw = sg.sa[lane];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint4v q0 = sg.a[mt][0][lane];
+      int8v a;
+      if (H == 1) {
+        a = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, 0, 0, 0, 0};
+      } else {
+        const uint4v q1 = sg.a[mt][H - 1][lane];
+        a = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+      }
+      const int sa = T::MX ? (int)((saw >> (8 * mt)) & 0xFFu) : 127;
+      float4v s4 = float4v{0.f, 0.f, 0.f, 0.f};
+      if (T::BLOCK) {
+        const float* rs = reinterpret_cast<const float*>(&sg.sa[0]) + 16 * mt + 4 * (lane >> 4);
+        s4 = float4v{rs[0] * swv, rs[1] * swv, rs[2] * swv, rs[3] * swv};
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (T::BLOCK) {
+          const float4v z = float4v{0.f, 0.f, 0.f, 0.f};
+          const float4v part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[nt], z, 0, 0, 0, 127, 0, 127);
+          acc[mt][nt] += part * s4;
+        } else {
+          acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[nt], acc[mt][nt], T::FMT,
+                                                                         T::FMT, 0, sa, 0, sb[nt]);
+        }
+      }
+    }
+  };
+
+  // chunk idx of this wave lives in stage idx % D; before computing it the
+  // wave waits until at most min(D-1, n-1-idx) later chunks are in flight
+  Stage* mine = ring[wave];
+  const int pre = n < D ? n : D;
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < pre) issue(mine[j], c0 + j);
+  for (int i0 = 0; i0 < n; i0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int idx = i0 + j;
+      if (idx < n) {
+        const int later = n - 1 - idx;
+        WaitChunks<L, D - 1>::run(later < D - 1 ? later : D - 1);
+        compute(mine[j]);
+        if (idx + D < n) {
+          __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage reads done before the refill
+          issue(mine[j], c0 + idx + D);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // every wave is done with the ring, which now holds the partial sums
+
+  // wave-order reduction of the W partial sums, then the epilogue: fragment
+  // f (row tile f / NT, column tile f % NT) is finished by wave f % W
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) red[wave][mt * NT + nt][lane] = acc[mt][nt];
+  __syncthreads();
+#pragma unroll
+  for (int f = 0; f < MT * NT; ++f) {
+    if (f % W != wave) continue;
+    float4v sum = red[0][f][lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) sum += red[w][f][lane];
+    const int n_col = (int)((tile0 + f % NT) * 16) + (lane & 15);
+    if (n_col >= N) continue;
+    const float bv = bias ? bf16_bits_to_f32(bias[n_col]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = (f / NT) * 16 + 4 * (lane >> 4) + i;
+      if (m < M) y[(int64_t)m * ldy + n_col] = (uint16_t)f32_to_bf16_bits(alpha * sum[i] + bv);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // configurations, plan, launcher
 // ---------------------------------------------------------------------------
 
@@ -248,7 +438,27 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
 // whose ring does not fit in LDS (see sc_config_fits).
 #define FQL_SC_CONFIGS(X, F)                                                                    \
   X(F, 1, 4, 1, 4, 4) X(F, 1, 4, 2, 4, 4) X(F, 1, 4, 4, 2, 4) X(F, 2, 2, 4, 4, 3)              \
-  X(F, 2, 4, 4, 4, 3) X(F, 2, 4, 8, 4, 4) X(F, 4, 2, 4, 4, 3) X(F, 1, 4, 1, 2, 4)
+  X(F, 2, 4, 4, 4, 3) X(F, 2, 4, 8, 4, 4) X(F, 4, 2, 4, 4, 3) X(F, 1, 4, 1, 2, 4)              \
+  X(F, 1, 4, 1, 2, 8) X(F, 1, 4, 4, 2, 6)
+
+// (W, MT, NT, D) GEMV configurations built for every format.
+#define FQL_SCV_CONFIGS(X, F)                                                                   \
+  X(F, 4, 1, 2, 4) X(F, 4, 1, 2, 6) X(F, 8, 1, 2, 3) X(F, 4, 1, 4, 3) X(F, 8, 1, 1, 4)          \
+  X(F, 4, 2, 2, 3) X(F, 8, 2, 1, 3) X(F, 4, 1, 2, 3) X(F, 8, 1, 1, 3)
+
+template <int F, int W, int MT, int NT, int D>
+static constexpr bool scv_config_fits() {
+  return sizeof(ScvStage<F, MT, NT>) * W * D <= 160 * 1024;
+}
+
+static bool scv_config_built(int fmt, int w, int mt, int nt, int d) {
+#define FQL_X(F0, A, B, C, E) \
+  if (fmt == F0 && w == A && mt == B && nt == C && d == E) return scv_config_fits<F0, A, B, C, E>();
+  FQL_SCV_CONFIGS(FQL_X, SC_MXFP4) FQL_SCV_CONFIGS(FQL_X, SC_MXFP8) FQL_SCV_CONFIGS(FQL_X, SC_FP8)
+  FQL_SCV_CONFIGS(FQL_X, SC_FP8_BLOCK)
+#undef FQL_X
+  return false;
+}
 
 static constexpr size_t kLdsLimit = 160 * 1024;
 
@@ -277,15 +487,49 @@ ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
   const ScDims w = sc_dims(fmt, N, K, true);
   const int64_t KC = w.KC, ntiles = w.rows_p / 16;
   const bool fp4 = fmt == SC_MXFP4;
-  // defaults (MI355X measurements on K = 4096 shapes): one row tile and four
-  // column tiles per wave for decode sizes; 64 x 128 workgroup tiles for
-  // mid-size M; the big 8-wave tiles for large M.
-  int wm = 1, wn = 4, mtw = 1, ntw = 4, st = 4;
-  if (M <= 16) { wm = 1; wn = 4; mtw = 1; ntw = fp4 ? 4 : 2; st = 4; }
-  else if (M <= 32) { wm = 1; wn = 4; mtw = 2; ntw = 4; st = 4; }
-  else if (M <= 512) { wm = 1; wn = 4; mtw = 4; ntw = 2; st = 4; }
+  // defaults (MI355X sweeps at K = 4096, N = 14336, M = 1 .. 4096): one row
+  // tile and two column tiles per wave for decode sizes (more workgroups in
+  // flight), 64 x 128 workgroup tiles up to M = 128, 128 x 128 for 8-bit
+  // formats up to M = 512, then the 8-wave tiles (256 x 256 for FP4, whose
+  // ring fits in LDS; 256 x 128 for FP8).
+  int wm = 1, wn = 4, mtw = 1, ntw = 2, st = 4;
+  if (M <= 32) { wm = 1; wn = 4; mtw = 1; ntw = 2; st = 4; }
+  else if (M <= 128 || (fp4 && M <= 512)) { wm = 1; wn = 4; mtw = 4; ntw = 2; st = 4; }
+  else if (M <= 512) { wm = 2; wn = 2; mtw = 4; ntw = 4; st = 3; }
   else if (fp4) { wm = 2; wn = 4; mtw = 8; ntw = 4; st = 4; }
   else { wm = 4; wn = 2; mtw = 4; ntw = 4; st = 3; }
+  // register-streaming GEMV for small M: W waves split K, NT tiles per workgroup
+  {
+    int gw = 0, gnt = 0, gd = 0;
+    const int mt = (int)((M + 15) / 16);
+    bool gemv = M <= 32;
+    if (M <= 16) { gw = 4; gnt = 2; gd = 4; }
+    else { gw = 4; gnt = 2; gd = 3; }
+    bool forced = false;
+    if (const char* e = std::getenv("FQL_SC_GEMV")) {  // benchmarking aid: "W,NT,D" (0 = off)
+      int a = 0, b = 0, c = 0;
+      const int k = std::sscanf(e, "%d,%d,%d", &a, &b, &c);
+      if (k >= 1 && a == 0) gemv = false;
+      else if (k == 3 && M <= 64 && scv_config_built(fmt, a, mt, b, c)) { gemv = true; gw = a; gnt = b; gd = c; forced = true; }
+    }
+    if (std::getenv("FQL_SC_PLAN")) gemv = forced;
+    if (gemv && scv_config_built(fmt, gw, mt, gnt, gd)) {
+      p.kind = 1;
+      p.wm = 1; p.wn = gw; p.mtw = mt; p.ntw = gnt; p.st = gd;
+      p.Mp = 16 * mt;
+      p.ngroups = (ntiles + gnt - 1) / gnt;
+      p.groups = p.ngroups;
+      p.splits = 1;
+      p.kc_per_split = (int)KC;
+      const ScDims x = sc_dims(fmt, p.Mp, K, false);
+      p.xcode_bytes = round_up(x.code_bytes, 256);
+      p.xscale_bytes = round_up(x.scale_bytes, 256);
+      p.partial_bytes = 0;
+      p.counter_bytes = 64 * 1024;
+      p.total_bytes = p.counter_bytes + p.xcode_bytes + p.xscale_bytes;
+      return p;
+    }
+  }
   int splits_override = 0;
   if (const char* e = std::getenv("FQL_SC_PLAN")) {  // benchmarking aid: "wm,wn,mtw,ntw,st,splits"
     int a = 0, b = 0, c = 0, d = 0, f = 0, s = 0;
@@ -301,8 +545,8 @@ ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
   p.Mp = round_up(M, std::max(tile_rows, 16));
   p.ngroups = (ntiles * 16 + tile_cols - 1) / tile_cols;
   const int64_t groups = p.ngroups * (p.Mp / tile_rows);
-  // split K until about 160 workgroups are in flight (at most 4 ways)
-  int64_t s = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(4, KC), (160 + groups / 2) / groups));
+  // split K until about 256 workgroups are in flight (at most 4 ways)
+  int64_t s = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(4, KC), (256 + groups / 2) / groups));
   if (splits_override > 0) s = std::min<int64_t>(splits_override, KC);
   p.kc_per_split = (int)((KC + s - 1) / s);
   p.splits = (int)((KC + p.kc_per_split - 1) / p.kc_per_split);
@@ -319,6 +563,11 @@ ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
 
 std::string describe_sc_plan(const ScPlan& p) {
   char b[240];
+  if (p.kind == 1) {
+    std::snprintf(b, sizeof(b), "sc_quant_operand_kernel<%s> + gemv_sc_kernel<%s,W=%d,MT=%d,NT=%d,D=%d> grid=%lld splits=1",
+                  sc_fmt_name(p.fmt), sc_fmt_name(p.fmt), p.wn, p.mtw, p.ntw, p.st, (long long)p.groups);
+    return std::string(b);
+  }
   std::snprintf(b, sizeof(b),
                 "sc_quant_operand_kernel<%s> + gemm_sc_kernel<%s,WM=%d,WN=%d,MTW=%d,NTW=%d,ST=%d> grid=%lld splits=%d",
                 sc_fmt_name(p.fmt), sc_fmt_name(p.fmt), p.wm, p.wn, p.mtw, p.ntw, p.st,
@@ -341,6 +590,21 @@ static hipError_t launch_sc_t(const ScPlan& p, const uint8_t* xc, const uint8_t*
   }
 }
 
+template <int F, int W, int MT, int NT, int D>
+static hipError_t launch_scv_t(const ScPlan& p, const uint8_t* xc, const uint8_t* xs,
+                               const uint8_t* packed, const ScDims& w, int64_t M, int64_t N,
+                               float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
+                               hipStream_t st) {
+  if constexpr (!scv_config_fits<F, W, MT, NT, D>()) {
+    return hipErrorInvalidValue;
+  } else {
+    gemv_sc_kernel<F, W, MT, NT, D><<<(unsigned)p.groups, 64 * W, 0, st>>>(
+        xc, xs, packed, packed + w.code_bytes, (int)M, (int)N, w.KC, (int)(w.rows_p / 16), w.quads,
+        alpha, bias, y, ldy);
+    return hipGetLastError();
+  }
+}
+
 hipError_t launch_sc_linear(const ScPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                             bool aligned, float inv_scale, const uint8_t* packed, int64_t N,
                             float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
@@ -353,6 +617,15 @@ hipError_t launch_sc_linear(const ScPlan& p, const uint16_t* x, int64_t M, int64
   if (p.splits > 1 && p.groups > p.counter_bytes / 4) return hipErrorInvalidValue;
   hipError_t e = launch_sc_quant_operand(p.fmt, x, M, K, ldx, aligned, inv_scale, p.Mp, xc, xs, st);
   if (e != hipSuccess) return e;
+  if (p.kind == 1) {
+#define FQL_X(F0, A, B, C, E)                                                                      \
+  if (p.fmt == F0 && p.wn == A && p.mtw == B && p.ntw == C && p.st == E)                           \
+    return launch_scv_t<F0, A, B, C, E>(p, xc, xs, packed, w, M, N, alpha, bias, y, ldy, st);
+    FQL_SCV_CONFIGS(FQL_X, SC_MXFP4) FQL_SCV_CONFIGS(FQL_X, SC_MXFP8) FQL_SCV_CONFIGS(FQL_X, SC_FP8)
+    FQL_SCV_CONFIGS(FQL_X, SC_FP8_BLOCK)
+#undef FQL_X
+    return hipErrorInvalidValue;
+  }
 #define FQL_X(F0, A, B, C, D, E)                                                                  \
   if (p.fmt == F0 && p.wm == A && p.wn == B && p.mtw == C && p.ntw == D && p.st == E)             \
     return launch_sc_t<F0, A, B, C, D, E>(p, xc, xs, packed, w, M, N, alpha, bias, y, ldy, partial, \

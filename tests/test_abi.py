@@ -142,7 +142,8 @@ def test_fp8_family_sizes(fmt):
              "fp8_block": -(-((N // 128) * KC * 4) // 256) * 256}[fmt]
     assert fql._size_query(f"fql_packed_{fmt}_bytes", N, K) == code + scale
     assert fql.linear_sc_workspace_bytes(fmt, 4096, N, K) >= 64 * 1024 + 4096 * K
-    assert f"gemm_sc_kernel<{fmt}," in fql.linear_sc_plan(fmt, 1, N, K)
+    assert f"gemv_sc_kernel<{fmt}," in fql.linear_sc_plan(fmt, 1, N, K)
+    assert f"gemm_sc_kernel<{fmt}," in fql.linear_sc_plan(fmt, 4096, N, K)
 
 
 def test_fp8_family_can_implement():

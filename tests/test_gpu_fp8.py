@@ -273,3 +273,23 @@ def test_every_sc_config(fmt, cfg, splits, monkeypatch):
     want = f"gemm_sc_kernel<{fmt},WM={wm},WN={wn},MTW={mtw},NTW={ntw},ST={st}>"
     assert want in plan and f"splits={splits}" in plan, plan
     _run(fmt, "tiny", M, K, N, True, alpha=None if fmt == "fp8" else 1.5, label=f"{cfg} splits={splits}")
+
+
+# Every small-M GEMV configuration (W waves splitting K, NT column tiles per
+# workgroup, D chunks in flight per wave) at M = 1, 16 (one row tile) and
+# 17, 32 (two), on a ragged shape: 9 chunks of 128, a partial column tile.
+SCV_CONFIGS = [(4, 2, 4), (4, 2, 6), (8, 2, 3), (4, 4, 3), (8, 1, 4), (4, 2, 3), (8, 1, 3)]
+
+
+@pytest.mark.parametrize("M", [1, 16, 17, 32])
+@pytest.mark.parametrize("cfg", SCV_CONFIGS)
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8", "fp8", "fp8_block"])
+def test_every_gemv_config(fmt, cfg, M, monkeypatch):
+    K = 1152
+    N = 384 if fmt == "fp8_block" else 400
+    w, nt, d = cfg
+    monkeypatch.setenv("FQL_SC_GEMV", f"{w},{nt},{d}")
+    plan = fql.linear_sc_plan(fmt, M, N, K)
+    if f"gemv_sc_kernel<{fmt},W={w},MT={(M + 15) // 16},NT={nt},D={d}>" not in plan:
+        pytest.skip(f"GEMV {cfg} not built for {fmt} at M={M}: {plan}")
+    _run(fmt, "tiny", M, K, N, True, alpha=None if fmt == "fp8" else 1.5, label=f"gemv {cfg}")
