@@ -503,7 +503,7 @@ ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
     int gw = 0, gnt = 0, gd = 0;
     const int mt = (int)((M + 15) / 16);
     bool gemv = M <= 32;
-    if (M <= 16) { gw = 4; gnt = 2; gd = 4; }
+    if (M <= 16) { gw = 4; gnt = fmt == SC_MXFP4 ? 4 : 2; gd = 3; }
     else { gw = 4; gnt = 2; gd = 3; }
     bool forced = false;
     if (const char* e = std::getenv("FQL_SC_GEMV")) {  // benchmarking aid: "W,NT,D" (0 = off)
