@@ -93,6 +93,7 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned);
 bool tiled_config_built(int mt, int nt, int wm);
 bool lds_config_built(int mt, int nt, int st);
 bool lds32_config_built(int mt, int nt, int st);
+bool gemv_ring_config_built(int w, int mt, int nt, int d);
 
 // Kernel name and parameters of a plan (diagnostics).
 std::string describe_plan(const GemmPlan& p);

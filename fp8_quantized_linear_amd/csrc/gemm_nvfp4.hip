@@ -49,6 +49,156 @@
 namespace fql {
 
 // ---------------------------------------------------------------------------
+// small-M kernel with per-wave LDS rings (kind 4)
+// ---------------------------------------------------------------------------
+//
+// A linear call with M <= 32 is a stream over the weight. W waves of a
+// workgroup share NT 16-column tiles and split the K range; each wave
+// streams its own chunks (x_hat tiles, weight codes, scale dwords) into a
+// private D-stage LDS ring with direct global->LDS loads and waits only for
+// its own loads (explicit vmcnt, no workgroup barrier in the loop), so D
+// chunks per wave stay in flight. Weight fragments are dequantized to fp16
+// exactly as in the other kinds; the W partial sums are added in wave order
+// through LDS at the end (deterministic, no atomics).
+template <int MT, int NT>
+struct GemvStage {
+  uint4v a[MT][4][64];  // x_hat fragments of the chunk's four 32-deep steps
+  uint4v b[NT][64];     // weight codes (one 16-byte slot per lane and tile)
+  uint32_t s[NT][64];   // the lane's scale dword of this chunk, per tile
+};
+
+template <int L, int K>
+struct GemvWait {
+  static __device__ __forceinline__ void run(int k) {
+    if (k >= K) wait_vmcnt<L * K>();
+    else GemvWait<L, K - 1>::run(k);
+  }
+};
+template <int L>
+struct GemvWait<L, 0> {
+  static __device__ __forceinline__ void run(int) { wait_vmcnt<0>(); }
+};
+
+template <int W, int MT, int NT, int D>
+__global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
+    const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
+    const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, float alpha,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t ldy) {
+  typedef GemvStage<MT, NT> Stage;
+  constexpr int L = MT * 4 + NT * 2;  // loads per chunk
+  static_assert(L * (D - 1) <= 63, "vmcnt range");
+  __shared__ Stage ring[W][D];
+  static_assert(sizeof(ring) >= sizeof(float4v) * W * MT * NT * 64, "reduction buffer aliases the ring");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t KC = Kp / 128, KC4 = (KC + 3) / 4, KS = Kp / 32;
+  const int64_t tile0 = (int64_t)blockIdx.x * NT;
+  const int64_t cpw = (KC + W - 1) / W;
+  const int64_t c0 = (int64_t)wave * cpw < KC ? (int64_t)wave * cpw : KC;
+  const int64_t c1 = c0 + cpw < KC ? c0 + cpw : KC;
+  const int n = (int)(c1 - c0);
+  int64_t bt[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) bt[nt] = tile0 + nt < ntiles ? tile0 + nt : ntiles - 1;  // never stored
+  const uint8_t* xh = reinterpret_cast<const uint8_t*>(xhat);
+  // this lane's scale dword within a tile's 512-byte group of four chunks
+  const uint32_t s_voff_lane = (uint32_t)(((lane & 15) * 2 + (lane >> 5)) * 16);
+
+  auto issue = [&](Stage& sg, int64_t c) {
+    const uint32_t base = lds_offset(&sg);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        lds_load16(xh + ((mt * KS + 4 * c + ks) * 64) * 16, lane * 16,
+                   base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      lds_load16(wcodes + (bt[nt] * KC + c) * 1024, lane * 16,
+                 base + (uint32_t)offsetof(Stage, b) + nt * 1024);
+      lds_load4(wscales + (bt[nt] * KC4 + c / 4) * 512, s_voff_lane + (uint32_t)(c & 3) * 4,
+                base + (uint32_t)offsetof(Stage, s) + nt * 256);
+    }
+  };
+
+  float4v acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Stage& sg) {
+    uint4v codes[NT];
+    uint32_t sw[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      codes[nt] = sg.b[nt][lane];
+      sw[nt] = sg.s[nt][lane];
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      half8 bf[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) bf[nt] = b_fragment(dword_of(codes[nt], ks), ChunkScales(sw[nt])[ks]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const half8 a = __builtin_bit_cast(half8, sg.a[mt][ks][lane]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[nt], acc[mt][nt], 0, 0, 0);
+      }
+    }
+  };
+
+  // chunk idx of this wave lives in stage idx % D; before computing it the
+  // wave waits until at most min(D-1, n-1-idx) later chunks are in flight
+  Stage* mine = ring[wave];
+  const int pre = n < D ? n : D;
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < pre) issue(mine[j], c0 + j);
+  for (int i0 = 0; i0 < n; i0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int idx = i0 + j;
+      if (idx < n) {
+        const int later = n - 1 - idx;
+        GemvWait<L, D - 1>::run(later < D - 1 ? later : D - 1);
+        compute(mine[j]);
+        if (idx + D < n) {
+          __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage reads done before the refill
+          issue(mine[j], c0 + idx + D);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // every wave is done with the ring, which now holds the partial sums
+
+  float4v(*red)[MT * NT][64] = reinterpret_cast<float4v(*)[MT * NT][64]>(&ring[0][0]);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) red[wave][mt * NT + nt][lane] = acc[mt][nt];
+  __syncthreads();
+#pragma unroll
+  for (int f = 0; f < MT * NT; ++f) {
+    if (f % W != wave) continue;
+    float4v sum = red[0][f][lane];
+#pragma unroll
+    for (int w = 1; w < W; ++w) sum += red[w][f][lane];
+    const int n_col = (int)((tile0 + f % NT) * 16) + (lane & 15);
+    if (n_col >= N) continue;
+    const float bv = bias ? bf16_bits_to_f32(bias[n_col]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = (f / NT) * 16 + 4 * (lane >> 4) + i;
+      if (m < M) y[(int64_t)m * ldy + n_col] = (uint16_t)f32_to_bf16_bits(alpha * sum[i] + bv);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // full-K matrix-vector kernel (small M): no cross-workgroup reduction
 // ---------------------------------------------------------------------------
 //
@@ -827,7 +977,7 @@ static GemmOverride gemm_override() {
       else if (k == "mt" && (v == 1 || v == 2 || v == 4 || v == 8)) o.mt = v;
       else if (k == "nt" && (v == 1 || v == 2 || v == 4)) o.nt = v;
       else if (k == "wm" && (v == 1 || v == 2 || v == 4)) o.wm = v;
-      else if (k == "st" && v >= 2 && v <= 4) o.st = v;
+      else if (k == "st" && v >= 2 && v <= 8) o.st = v;
       else if (k == "splits" && v >= 1 && v <= 64) o.splits = v;
     }
     pos = end + 1;
@@ -850,9 +1000,13 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
   // while that redundant work stays small (measured: gate_up at M = 8 is
   // faster through the quantizer kernel + tiled GEMM).
   const int64_t quant_blocks = (int64_t)M * (p.Kp / 16);
-  const bool gemv_ok = aligned && M <= 16 && M * p.Kp * 2 <= kGemvMaxLds &&
-                       (ov.kind == 0 || ntiles * quant_blocks <= kGemvMaxRedundantBlocks);
-  if (gemv_ok && ov.kind != 1) {
+  bool gemv_ok = aligned && M <= 16 && M * p.Kp * 2 <= kGemvMaxLds &&
+                 (ov.kind == 0 || ntiles * quant_blocks <= kGemvMaxRedundantBlocks);
+  // Measured on the decode shapes: the fused kernel wins at M = 1 and, for
+  // narrow layers with K = 4096 (N < 16384), up to M = 16; long K (K = 14336)
+  // and wide layers stream better through kinds 4 and 1 once M > 1.
+  if (ov.kind < 0 && gemv_ok && M > 1 && (p.Kp >= 8192 || N >= 16384)) gemv_ok = false;
+  if (gemv_ok && ov.kind != 1 && ov.kind != 4) {
     // one workgroup per NTW 16-column tiles over the full K (no cross-workgroup reduction)
     p.kind = 0;
     p.mt = 1;
@@ -860,11 +1014,11 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     p.wm = 1;
     p.Mp = M;
     p.waves = ntiles < 1024 ? 8 : 4;
-    p.ntw = 1;
+    p.ntw = M > 1 && ntiles < 1024 ? 2 : 1;
     if (ov.waves) p.waves = ov.waves;
     if (ov.ntw) p.ntw = ov.ntw;
     const int64_t cpw = (KC + p.waves - 1) / p.waves;
-    p.kcmax = cpw <= 4 ? 4 : 8;  // register ring depth (chunks)
+    p.kcmax = cpw <= 8 ? 4 : 8;  // register ring depth (chunks)
     if (ov.rc) p.kcmax = ov.rc;
     const int64_t qblk = (M * p.Kp / 16 + 64 * p.waves - 1) / (64 * p.waves);  // blocks per thread
     p.qpre = qblk <= 1 ? 1 : qblk <= 2 ? 2 : 4;
@@ -878,8 +1032,33 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     // Defaults (measured on the decode and prefill layer shapes): small M
     // keeps the register-staged tiled kernel; from 33 rows on the LDS-ring
     // kernel on 32x32 MFMAs.
-    p.kind = M <= 32 ? 1 : 3;
-    if (ov.kind >= 1 && ov.kind <= 3) p.kind = ov.kind;
+    p.kind = M <= 32 ? ((N >= 16384 && p.Kp < 8192) ? 1 : 4) : 3;
+    if (ov.kind >= 1 && ov.kind <= 4) p.kind = ov.kind;
+    if (p.kind == 4) {
+      // per-wave rings: W waves split K, NT tiles per workgroup, D chunks in flight
+      p.mt = (int)((M + 15) / 16);
+      p.waves = p.Kp >= 8192 ? 8 : 4;
+      p.nt = p.Kp >= 8192 ? 1 : 2;
+      p.st = 3;
+      if (M <= 16 && N >= 16384) { p.waves = 4; p.nt = 1; p.st = 4; }
+      if (ov.waves) p.waves = ov.waves;
+      if (ov.nt) p.nt = ov.nt;
+      if (ov.st) p.st = ov.st;
+      if (p.mt <= 2 && gemv_ring_config_built(p.waves, p.mt, p.nt, p.st)) {
+        p.wm = 1;
+        p.Mp = 16 * p.mt;
+        p.groups = (ntiles + p.nt - 1) / p.nt;
+        p.ngroups = p.groups;
+        p.splits = 1;
+        p.kc_per_split = (int)KC;
+        p.xhat_bytes = round_up(p.Mp * p.Kp * 2, 256);
+        p.partial_bytes = 0;
+        p.counter_bytes = kCounterBytes;
+        p.total_bytes = p.counter_bytes + p.xhat_bytes;
+        return p;
+      }
+      p.kind = 1;
+    }
     // kind 3 addresses the packed blob with 32-bit per-lane offsets
     if (p.kind == 3 && d.total_bytes() >= ((int64_t)1 << 32)) p.kind = 2;
     const bool lds_ring = p.kind >= 2;
@@ -947,7 +1126,11 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
 
 std::string describe_plan(const GemmPlan& p) {
   char b[256];
-  if (p.kind == 3) {
+  if (p.kind == 4) {
+    std::snprintf(b, sizeof(b),
+                  "quant_nvfp4_xhat_kernel + gemv_ring_kernel<W=%d,MT=%d,NT=%d,D=%d> grid=%lld splits=1",
+                  p.waves, p.mt, p.nt, p.st, (long long)p.groups);
+  } else if (p.kind == 3) {
     std::snprintf(b, sizeof(b),
                   "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d> grid=%lld splits=%d",
                   p.mt, p.nt, p.st, (long long)(p.groups * p.splits), p.splits);
@@ -1078,6 +1261,17 @@ bool lds32_config_built(int mt, int nt, int st) {
   return false;
 }
 
+// The (W, MT, NT, D) per-wave-ring configurations built into the library.
+#define FQL_GEMV_RING_CONFIGS(X) \
+  X(4, 1, 2, 3) X(4, 1, 2, 4) X(4, 1, 4, 3) X(8, 1, 1, 3) X(8, 1, 2, 3) X(4, 2, 2, 3) X(4, 2, 1, 4)
+
+bool gemv_ring_config_built(int w, int mt, int nt, int d) {
+#define FQL_X(A, B, C, E) if (w == A && mt == B && nt == C && d == E) return true;
+  FQL_GEMV_RING_CONFIGS(FQL_X)
+#undef FQL_X
+  return false;
+}
+
 bool tiled_config_built(int mt, int nt, int wm) {
 #define FQL_X(A, B, C) if (mt == A && nt == B && wm == C) return true;
   FQL_TILED_CONFIGS(FQL_X)
@@ -1108,6 +1302,18 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
   hipError_t e = launch_quant_nvfp4_xhat(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp, xhat, st);
   if (e != hipSuccess) return e;
   float4v* partial4 = reinterpret_cast<float4v*>(partial);
+  if (p.kind == 4) {
+#define FQL_X(A, B, C, E)                                                                           \
+  if (p.waves == A && p.mt == B && p.nt == C && p.st == E) {                                        \
+    gemv_ring_kernel<A, B, C, E><<<(unsigned)p.groups, 64 * A, 0, st>>>(                            \
+        xhat, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16), alpha, bias, \
+        y, ldy);                                                                                     \
+    return hipGetLastError();                                                                        \
+  }
+    FQL_GEMV_RING_CONFIGS(FQL_X)
+#undef FQL_X
+    return hipErrorInvalidValue;
+  }
   if (p.kind == 3) {
 #define FQL_X(A, B, C, D)                                                                        \
   if (p.mt == A && p.nt == B && p.st == C)                                                       \

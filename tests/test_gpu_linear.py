@@ -222,3 +222,21 @@ def test_linear_every_lds32_config(mt, nt, st, splits, monkeypatch):
     plan = fql.linear_plan(M, N, K)
     assert f"gemm_lds32_kernel<MT={mt},NT={nt},ST={st}>" in plan and f"splits={splits}" in plan, plan
     _run_case("tiny", M, K, N, 0, True, label=f"lds32<{mt},{nt},{st}> splits={splits}")
+
+
+# Every per-wave-ring small-M configuration (W waves splitting K, MT row
+# tiles, NT column tiles per workgroup, D chunks in flight per wave), same
+# ragged shape at M = 1, 16 (one row tile), 17 and 32 (two).
+GEMV_RING_CONFIGS = [(4, 2, 3), (4, 2, 4), (4, 4, 3), (8, 1, 3), (8, 2, 3), (4, 1, 4)]
+
+
+@pytest.mark.parametrize("M", [1, 16, 17, 32])
+@pytest.mark.parametrize("w,nt,d", GEMV_RING_CONFIGS)
+def test_linear_every_gemv_ring_config(w, nt, d, M, monkeypatch):
+    K, N = 1152, 400
+    monkeypatch.setenv("FQL_PLAN", f"kind=4,waves={w},nt={nt},st={d}")
+    plan = fql.linear_plan(M, N, K)
+    want = f"gemv_ring_kernel<W={w},MT={(M + 15) // 16},NT={nt},D={d}>"
+    if want not in plan:
+        pytest.skip(f"{want} not built: {plan}")
+    _run_case("tiny", M, K, N, 0, True, label=f"gemv_ring<{w},{nt},{d}>")
