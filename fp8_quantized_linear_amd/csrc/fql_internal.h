@@ -81,6 +81,7 @@ struct GemmPlan {
   int qpre;           // kind 0: activation blocks per thread loaded ahead of the weights
   int ntw;            // kind 0: 16-column tiles per workgroup
   int64_t lds_bytes;  // kind 0: dynamic LDS (compact activation copy / reduction)
+  int fq;             // kind 4: activation quantized inside the kernel (no x_hat pass)
   int64_t counter_bytes, xhat_bytes, partial_bytes, total_bytes;
 };
 // `aligned`: x rows are 16-byte aligned (pointer and row stride); the

@@ -79,9 +79,16 @@ struct GemvWait<L, 0> {
   static __device__ __forceinline__ void run(int) { wait_vmcnt<0>(); }
 };
 
-template <int W, int MT, int NT, int D>
+// FQ = 1 fuses the activation quantizer: the ring carries bf16 x rows (16-byte
+// columns XOR-swizzled by row, so a fragment read hits 16 distinct bank groups)
+// instead of x_hat, and each lane quantizes its own A fragment (8 elements;
+// the partner lane l^16 holds the other half of the 16-block, so one shuffle
+// gives the block maximum). Needs 16-byte aligned rows, K % 128 == 0 and no
+// rotation; rows >= M are read from row M-1 (in bounds) and zeroed.
+template <int W, int MT, int NT, int D, int FQ>
 __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
-    const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
+    const _Float16* __restrict__ xhat, const uint16_t* __restrict__ x, int64_t ldx, float g,
+    const uint8_t* __restrict__ wcodes,
     const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, float alpha,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t ldy) {
   typedef GemvStage<MT, NT> Stage;
@@ -101,17 +108,35 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) bt[nt] = tile0 + nt < ntiles ? tile0 + nt : ntiles - 1;  // never stored
   const uint8_t* xh = reinterpret_cast<const uint8_t*>(xhat);
+  const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
   // this lane's scale dword within a tile's 512-byte group of four chunks
   const uint32_t s_voff_lane = (uint32_t)(((lane & 15) * 2 + (lane >> 5)) * 16);
+  // fused: load j of row tile mt brings rows 16mt + 4j + lane/16, 16-byte
+  // column (lane%16) ^ (row%16) of the chunk
+  uint32_t x_voff[FQ ? MT : 1][4];
+  if (FQ) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * mt + 4 * j + (lane >> 4);
+        const int rc = row < M ? row : M - 1;
+        x_voff[mt][j] = (uint32_t)((int64_t)rc * ldx * 2 + (((lane & 15) ^ (row & 15)) * 16));
+      }
+  }
 
   auto issue = [&](Stage& sg, int64_t c) {
     const uint32_t base = lds_offset(&sg);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        lds_load16(xh + ((mt * KS + 4 * c + ks) * 64) * 16, lane * 16,
-                   base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
+      for (int ks = 0; ks < 4; ++ks) {
+        if (FQ)
+          lds_load16(xb + c * 256, x_voff[mt][ks], base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
+        else
+          lds_load16(xh + ((mt * KS + 4 * c + ks) * 64) * 16, lane * 16,
+                     base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
+      }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       lds_load16(wcodes + (bt[nt] * KC + c) * 1024, lane * 16,
@@ -126,6 +151,41 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = float4v{0.f, 0.f, 0.f, 0.f};
+
+  // fused quantizer: this lane's A fragment (row 16mt + lane%16, k = 32ks +
+  // 8(lane/16) + 0..7) as exactly dequantized NVFP4 in fp16, with the same
+  // operations and rounding as the standalone quantizer
+  auto quant_fragment = [&](const Stage& sg, int mt, int ks) -> half8 {
+#pragma clang fp contract(off)
+    const int r = lane & 15;
+    const int c16 = 4 * ks + (lane >> 4);
+    const uint4v raw = *reinterpret_cast<const uint4v*>(
+        reinterpret_cast<const uint8_t*>(&sg.a[0][0][0]) + (mt * 16 + r) * 256 + ((c16 ^ r) * 16));
+    const bool live = 16 * mt + r < M;
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = live ? __uint_as_float(w[j] << 16) : 0.0f;
+      v[2 * j + 1] = live ? __uint_as_float(w[j] & 0xFFFF0000u) : 0.0f;
+    }
+    float a8 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a8 = __builtin_fmaxf(a8, __builtin_fabsf(v[e]));
+    const float a16 = __builtin_fmaxf(a8, __shfl_xor(a8, 16));
+    const float sf = (a16 / 6.0f) * g;
+    const uint32_t sc = e4m3_encode_nonneg(sf);
+    const float sd = e4m3_decode_nonneg(sc);
+    const float rr = sd == 0.0f ? 0.0f : g / sd;
+    uint32_t q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0] * rr, v[1] * rr, 1.0f, 0);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, v[2] * rr, v[3] * rr, 1.0f, 1);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, v[4] * rr, v[5] * rr, 1.0f, 2);
+    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, v[6] * rr, v[7] * rr, 1.0f, 3);
+    const _Float16 sh = (_Float16)sd;
+    uint32_t hw[4];
+    dequant8_f16(q, half2v{sh, sh}, hw);
+    return __builtin_bit_cast(half8, uint4v{hw[0], hw[1], hw[2], hw[3]});
+  };
 
   auto compute = [&](const Stage& sg) {
     uint4v codes[NT];
@@ -142,7 +202,9 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
       for (int nt = 0; nt < NT; ++nt) bf[nt] = b_fragment(dword_of(codes[nt], ks), ChunkScales(sw[nt])[ks]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const half8 a = __builtin_bit_cast(half8, sg.a[mt][ks][lane]);
+        half8 a;
+        if (FQ) a = quant_fragment(sg, mt, ks);
+        else a = __builtin_bit_cast(half8, sg.a[mt][ks][lane]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[nt], acc[mt][nt], 0, 0, 0);
@@ -954,7 +1016,7 @@ static constexpr int kCUs = 256;
 // Benchmarking aid: FQL_PLAN="kind=0,waves=8,ntw=2,rc=4" or "kind=1,mt=4,nt=1,splits=2"
 // overrides the launch-plan heuristics (no effect on results, only on speed).
 struct GemmOverride {
-  int kind = -1, waves = 0, ntw = 0, rc = 0, mt = 0, nt = 0, wm = 0, st = 0, splits = 0;
+  int kind = -1, waves = 0, ntw = 0, rc = 0, mt = 0, nt = 0, wm = 0, st = 0, splits = 0, fq = -1;
 };
 static GemmOverride gemm_override() {
   GemmOverride o;
@@ -979,6 +1041,7 @@ static GemmOverride gemm_override() {
       else if (k == "wm" && (v == 1 || v == 2 || v == 4)) o.wm = v;
       else if (k == "st" && v >= 2 && v <= 8) o.st = v;
       else if (k == "splits" && v >= 1 && v <= 64) o.splits = v;
+      else if (k == "fq" && (v == 0 || v == 1)) o.fq = v;
     }
     pos = end + 1;
   }
@@ -1046,6 +1109,10 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
       if (ov.st) p.st = ov.st;
       if (p.mt <= 2 && gemv_ring_config_built(p.waves, p.mt, p.nt, p.st)) {
         p.wm = 1;
+        // The fused quantizer repeats the activation's quantization in every
+        // workgroup; measured slower than the separate x_hat pass on the decode
+        // shapes (e.g. qkv M = 32: 15.9 vs 12.5 us), so it is opt-in.
+        p.fq = aligned && K % 128 == 0 && ov.fq == 1 ? 1 : 0;
         p.Mp = 16 * p.mt;
         p.groups = (ntiles + p.nt - 1) / p.nt;
         p.ngroups = p.groups;
@@ -1127,9 +1194,9 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
 std::string describe_plan(const GemmPlan& p) {
   char b[256];
   if (p.kind == 4) {
-    std::snprintf(b, sizeof(b),
-                  "quant_nvfp4_xhat_kernel + gemv_ring_kernel<W=%d,MT=%d,NT=%d,D=%d> grid=%lld splits=1",
-                  p.waves, p.mt, p.nt, p.st, (long long)p.groups);
+    std::snprintf(b, sizeof(b), "%sgemv_ring_kernel<W=%d,MT=%d,NT=%d,D=%d,FQ=%d> grid=%lld splits=1",
+                  p.fq ? "" : "quant_nvfp4_xhat_kernel + ", p.waves, p.mt, p.nt, p.st, p.fq,
+                  (long long)p.groups);
   } else if (p.kind == 3) {
     std::snprintf(b, sizeof(b),
                   "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d> grid=%lld splits=%d",
@@ -1299,16 +1366,24 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
     return hipGetLastError();
   }
   if (p.kind == 0) return hipErrorInvalidValue;  // caller re-plans unaligned inputs as kind 1
-  hipError_t e = launch_quant_nvfp4_xhat(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp, xhat, st);
-  if (e != hipSuccess) return e;
+  const bool fused = p.kind == 4 && p.fq && hb == 0 && aligned && K % 128 == 0;
+  if (!fused) {
+    hipError_t e = launch_quant_nvfp4_xhat(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp, xhat, st);
+    if (e != hipSuccess) return e;
+  }
   float4v* partial4 = reinterpret_cast<float4v*>(partial);
   if (p.kind == 4) {
-#define FQL_X(A, B, C, E)                                                                           \
-  if (p.waves == A && p.mt == B && p.nt == C && p.st == E) {                                        \
-    gemv_ring_kernel<A, B, C, E><<<(unsigned)p.groups, 64 * A, 0, st>>>(                            \
-        xhat, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16), alpha, bias, \
-        y, ldy);                                                                                     \
-    return hipGetLastError();                                                                        \
+#define FQL_X(A, B, C, E)                                                                             \
+  if (p.waves == A && p.mt == B && p.nt == C && p.st == E) {                                          \
+    if (fused)                                                                                        \
+      gemv_ring_kernel<A, B, C, E, 1><<<(unsigned)p.groups, 64 * A, 0, st>>>(                         \
+          xhat, x, ldx, g, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16),   \
+          alpha, bias, y, ldy);                                                                        \
+    else                                                                                              \
+      gemv_ring_kernel<A, B, C, E, 0><<<(unsigned)p.groups, 64 * A, 0, st>>>(                         \
+          xhat, x, ldx, g, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16),   \
+          alpha, bias, y, ldy);                                                                        \
+    return hipGetLastError();                                                                          \
   }
     FQL_GEMV_RING_CONFIGS(FQL_X)
 #undef FQL_X

@@ -230,13 +230,36 @@ def test_linear_every_lds32_config(mt, nt, st, splits, monkeypatch):
 GEMV_RING_CONFIGS = [(4, 2, 3), (4, 2, 4), (4, 4, 3), (8, 1, 3), (8, 2, 3), (4, 1, 4)]
 
 
+@pytest.mark.parametrize("fq", [0, 1])
 @pytest.mark.parametrize("M", [1, 16, 17, 32])
 @pytest.mark.parametrize("w,nt,d", GEMV_RING_CONFIGS)
-def test_linear_every_gemv_ring_config(w, nt, d, M, monkeypatch):
+def test_linear_every_gemv_ring_config(w, nt, d, M, fq, monkeypatch):
+    # fq = 1: the activation is quantized inside the kernel (x rows through the ring)
     K, N = 1152, 400
-    monkeypatch.setenv("FQL_PLAN", f"kind=4,waves={w},nt={nt},st={d}")
+    monkeypatch.setenv("FQL_PLAN", f"kind=4,waves={w},nt={nt},st={d},fq={fq}")
     plan = fql.linear_plan(M, N, K)
-    want = f"gemv_ring_kernel<W={w},MT={(M + 15) // 16},NT={nt},D={d}>"
+    want = f"gemv_ring_kernel<W={w},MT={(M + 15) // 16},NT={nt},D={d},FQ={fq}>"
     if want not in plan:
         pytest.skip(f"{want} not built: {plan}")
-    _run_case("tiny", M, K, N, 0, True, label=f"gemv_ring<{w},{nt},{d}>")
+    _run_case("tiny", M, K, N, 0, True, label=f"gemv_ring<{w},{nt},{d},fq={fq}>")
+
+
+@pytest.mark.parametrize("M", [3, 24])
+def test_linear_fused_ring_strided_rows(M, monkeypatch):
+    # fused quantization reads x rows with the caller's stride (rows >= M clamped)
+    K, N = 2048, 272
+    monkeypatch.setenv("FQL_PLAN", "kind=4,waves=4,nt=2,st=3,fq=1")
+    xb = synthetic.activations("normal", M, K, config="decode", seed=9)
+    x32 = synthetic.bf16_bits_to_f32(xb)
+    gx = Q.global_scale_from_amax(Q.amax_for_calibration(x32))
+    W, gw, wc, ws = weight_case("decode", N, K, 0)
+    alpha = alpha_of(gx, gw)
+    announce(f"fused ring strided M={M}")
+    wobj, _, _ = _gpu_weight(W, gw, 0, gx)
+    big = np.zeros((M, K + 64), np.uint16)
+    big[:, 64:] = xb
+    xd = bf16_bits_to_dev(big)[:, 64:]
+    assert "FQ=1" in fql.linear_plan(M, N, K)
+    y = fql.linear_nvfp4(xd, wobj, alpha=float(alpha))
+    ref = Q.linear_nvfp4(*Q.quant_nvfp4(x32, gx), wc, ws, alpha)
+    assert rel_frob(dev_bf16_to_bits(y), ref) <= REL_FROB_TOL
