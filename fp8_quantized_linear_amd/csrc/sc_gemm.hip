@@ -106,35 +106,69 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
   const int a_qoff = (int)(a_tile0 % 4);  // nonzero only when TA < 4
   const int64_t b_tile0 = (int64_t)ngroup * TB;
 
-  // item j of this wave's share of a stage
-  auto issue_item = [&](Stage& sg, int64_t c, int j) {
+  // This wave's share of a stage: item e = wave + NW*j (waves past the last
+  // item repeat the last item: same bytes, same place, and the same kind as
+  // the other items of that slot). The item table is built once
+  // (scalar registers: source base and per-chunk stride, LDS offset within
+  // the stage, load width), so issuing a load in the loop costs a few scalar
+  // instructions instead of re-deriving the item's address.
+  const uint8_t* it_src[L];
+  uint32_t it_stride[L], it_lds[L], it_voff[L];
+  bool it_wide[L];
+#pragma unroll
+  for (int j = 0; j < L; ++j) {
     int e = wave + NW * j;
-    e = e < ITEMS ? e : 0;  // waves past the last item repeat item 0 (same bytes, same place)
-    const uint32_t base = lds_offset(&sg);
+    e = e < ITEMS ? e : ITEMS - 1;
     if (e < NA) {
       const int t = e / H, h = e % H;
-      lds_load16(xcodes + ((a_tile0 + t) * KC + c) * CHUNK + h * 1024, lane * 16,
-                 base + (uint32_t)offsetof(Stage, a) + (t * H + h) * 1024);
+      it_src[j] = xcodes + (a_tile0 + t) * KC * CHUNK + h * 1024;
+      it_stride[j] = CHUNK;
+      it_lds[j] = (uint32_t)offsetof(Stage, a) + (t * H + h) * 1024;
+      it_wide[j] = true;
     } else if (e < NA + NB) {
       const int t = (e - NA) / H, h = (e - NA) % H;
       const int64_t gt = b_tile0 + t < ntiles_w ? b_tile0 + t : 0;  // past N: tile 0, never stored
-      lds_load16(wcodes + (gt * KC + c) * CHUNK + h * 1024, lane * 16,
-                 base + (uint32_t)offsetof(Stage, b) + (t * H + h) * 1024);
+      it_src[j] = wcodes + gt * KC * CHUNK + h * 1024;
+      it_stride[j] = CHUNK;
+      it_lds[j] = (uint32_t)offsetof(Stage, b) + (t * H + h) * 1024;
+      it_wide[j] = true;
     } else if (e < NA + NB + SA) {
       const int q = e - NA - NB;
-      lds_load4(xscales + ((a_quad0 + q) * KC + c) * 256, lane * 4,
-                base + (uint32_t)offsetof(Stage, as) + q * 256);
+      it_src[j] = xscales + (a_quad0 + q) * KC * 256;
+      it_stride[j] = 256;
+      it_lds[j] = (uint32_t)offsetof(Stage, as) + q * 256;
+      it_wide[j] = false;
     } else {
       const int q = e - NA - NB - SA;
+      it_lds[j] = (uint32_t)offsetof(Stage, bs) + q * 256;
+      it_wide[j] = false;
       if (T::MX) {
         const int64_t gq = b_tile0 / 4 + q < quads_w ? b_tile0 / 4 + q : 0;
-        lds_load4(wscales + (gq * KC + c) * 256, lane * 4, base + (uint32_t)offsetof(Stage, bs) + q * 256);
+        it_src[j] = wscales + gq * KC * 256;
+        it_stride[j] = 256;
       } else {  // block FP8: the column block's scale, broadcast to all 64 slots
         int64_t nb = (b_tile0 * 16) / 128 + q;
         const int64_t nbs = ((int64_t)ntiles_w * 16) / 128;
         nb = nb < nbs ? nb : 0;
-        lds_load4(wscales + (nb * KC + c) * 4, 0u, base + (uint32_t)offsetof(Stage, bs) + q * 256);
+        it_src[j] = wscales + nb * KC * 4;
+        it_stride[j] = 4;
       }
+    }
+    it_voff[j] = it_wide[j] ? (uint32_t)lane * 16 : (T::BLOCK && e >= NA + NB + SA ? 0u : (uint32_t)lane * 4);
+  }
+  // Which kind of item slot j holds is known at compile time once the loops
+  // are unrolled whenever all waves' item j are code tiles (or all MX scale
+  // quads): then width and stride are constants and no branch is emitted.
+  auto issue_item = [&](Stage& sg, int64_t c, int j) {
+    const uint32_t lds = lds_offset(&sg) + it_lds[j];
+    if (NW * j + NW <= NA + NB) {
+      lds_load16(it_src[j] + (uint32_t)c * (uint32_t)CHUNK, lane * 16, lds);
+    } else if (NW * j >= NA + NB && T::MX) {
+      lds_load4(it_src[j] + (uint32_t)c * 256u, lane * 4, lds);
+    } else {
+      const uint8_t* src = it_src[j] + (uint32_t)c * it_stride[j];
+      if (it_wide[j]) lds_load16(src, it_voff[j], lds);
+      else lds_load4(src, it_voff[j], lds);
     }
   };
 
