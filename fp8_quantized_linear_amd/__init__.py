@@ -67,6 +67,8 @@ __all__ = [
     "fp8_scale_from_amax",
     "linear_sc_plan",
     "linear_sc_workspace_bytes",
+    "warmup",
+    "token_counts_for_warmup",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -679,3 +681,42 @@ def linear_fp8(x, weight, alpha=None, bias=None, out=None, workspace=None):
 def linear_fp8_block(x, weight, alpha=1.0, bias=None, out=None, workspace=None):
     """y = bf16(sum over 128-groups of s_x s_w (x_q @ W_q^T) + bias)."""
     return _linear_sc("fp8_block", x, weight, alpha, bias, out, workspace)
+
+
+# ---------------------------------------------------------------------------
+# warmup
+# ---------------------------------------------------------------------------
+
+def token_counts_for_warmup(max_tokens, graph_sizes=()):
+    """The row counts M a serving engine warms each layer at: 1 (a decode
+    step), every positive graph-capture size, and the largest batch
+    (B12X write-up, Implementation: the warmup token set)."""
+    return sorted({1, int(max_tokens), *[int(g) for g in graph_sizes if int(g) > 0]})
+
+
+def warmup(layers, token_counts, device=None):
+    """Run every distinct (format, N, K, M) linear call once on zeros.
+
+    `layers` holds packed weights (NVFP4Weight, MXFP4Weight, MXFP8Weight,
+    FP8Weight, FP8BlockWeight); layers with the same format and shape are
+    warmed once (the B12X write-up dedupes warmup layers by signature). This loads
+    the kernels' code objects and leaves the per-stream workspace sized for
+    the largest call, so later calls (and graph captures) allocate nothing.
+    Returns the number of calls made.
+    """
+    seen = set()
+    calls = 0
+    for w in layers:
+        fmt = "nvfp4" if isinstance(w, NVFP4Weight) else w.fmt
+        for M in token_counts:
+            key = (fmt, w.N, w.K, int(M))
+            if key in seen:
+                continue
+            seen.add(key)
+            dev = device or w.packed.device
+            x = torch.zeros((int(M), w.K), dtype=torch.bfloat16, device=dev)
+            fn = {"nvfp4": linear_nvfp4, "mxfp4": linear_mxfp4, "mxfp8": linear_mxfp8,
+                  "fp8": linear_fp8, "fp8_block": linear_fp8_block}[fmt]
+            fn(x, w)
+            calls += 1
+    return calls
