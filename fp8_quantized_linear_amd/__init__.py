@@ -236,13 +236,16 @@ def amax(x, hadamard_block=0):
 
 
 def global_scale_from_amax(amax_value):
-    """g = 448 * 6 / amax rounded to float32 (1 when amax is 0), on the host."""
+    """g = 448 * 6 / amax rounded to float32 (1 when amax is 0, at most
+    2^118), on the host."""
     import numpy as np
 
     a = np.float32(amax_value)
     if a == 0:
         return float(np.float32(1.0))
-    return float(np.float32(2688.0) / a)
+    with np.errstate(over="ignore"):
+        g = np.float32(2688.0) / a
+    return float(min(g, np.float32(2.0 ** 118)))  # keeps g / (smallest E4M3 scale) finite
 
 
 def quant_nvfp4(x, global_scale, hadamard_block=0, codes=None, scales=None):

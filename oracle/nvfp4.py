@@ -55,6 +55,7 @@ from .hadamard import fwht_fp32
 NVFP4_BLOCK = 16
 E2M1_MAX = 6.0
 E4M3_MAX = 448.0
+GLOBAL_SCALE_MAX = 2.0 ** 118
 
 
 def amax_for_calibration(x, hadamard_block=0):
@@ -66,11 +67,19 @@ def amax_for_calibration(x, hadamard_block=0):
 
 
 def global_scale_from_amax(amax):
-    """g = fl32(448 * 6 / amax); g = 1 when amax is zero."""
+    """g = fl32(448 * 6 / amax); g = 1 when amax is zero; at most 2^118.
+
+    The cap (ours; the pages give only 448 * 6 / amax) binds only for amax
+    below 2688 * 2^-118, a tensor of values near the float32 subnormal range.
+    It keeps Q4's r = g / s_d finite for every nonzero E4M3 scale (the
+    smallest is 2^-9), so no product in Q5 meets an infinity.
+    """
     amax = np.float32(amax)
     if amax == 0:
         return np.float32(1.0)
-    return np.float32(np.float32(E4M3_MAX * E2M1_MAX) / amax)
+    with np.errstate(over="ignore"):
+        g = np.float32(np.float32(E4M3_MAX * E2M1_MAX) / amax)
+    return np.float32(min(float(g), GLOBAL_SCALE_MAX))
 
 
 def pack_nibbles(q):

@@ -20,13 +20,18 @@ perplexity runs need trained checkpoints and are not reproduced):
                Hadamard block in {16, 32, 64, 128}.
 * ``siblings``: K = 4096, N = 14336, M in {1, 4096}; x ~ N(0, 1);
                W ~ N(0, 0.02^2).
+* ``transform``: the ``hadamard`` shapes and activations with a general
+               b x b transform matrix (b in {16, 32, 64, 128}) drawn by
+               ``transform_matrix``: a random orthogonal matrix (QR of a
+               Gaussian draw, signs fixed by R's diagonal) or a Gaussian one
+               with entries N(0, 1/b), cast to bfloat16.
 """
 
 import numpy as np
 
-STREAM_X, STREAM_W, STREAM_BIAS, STREAM_OUTLIER = 0, 1, 2, 3
+STREAM_X, STREAM_W, STREAM_BIAS, STREAM_OUTLIER, STREAM_T = 0, 1, 2, 3, 4
 
-CONFIG_IDS = {"tiny": 0, "decode": 1, "prefill": 2, "hadamard": 3, "siblings": 4}
+CONFIG_IDS = {"tiny": 0, "decode": 1, "prefill": 2, "hadamard": 3, "siblings": 4, "transform": 5}
 
 LLAMA_SHAPES = {"qkv": (4096, 6144), "gate_up": (4096, 28672), "down": (14336, 4096)}
 QWEN_SHAPES = {"gate_up": (5120, 51200), "down": (25600, 5120)}
@@ -42,6 +47,8 @@ WORKLOADS = {
                  "x": "student_t3", "hadamard": (16, 32, 64, 128)},
     "siblings": {"M": (1, 4096), "shapes": {"sib": (4096, 14336)}, "bias": False,
                  "x": "normal", "hadamard": (0,)},
+    "transform": {"M": (1, 256, 4096), "shapes": QWEN_SHAPES, "bias": False,
+                  "x": "student_t3", "hadamard": (16, 32, 64, 128)},
 }
 
 
@@ -95,6 +102,20 @@ def bias(N, config="decode", seed=0, std=0.01):
     """bias [N] as bfloat16 bit patterns ~ N(0, std^2)."""
     g = rng(STREAM_BIAS, CONFIG_IDS[config], seed, N)
     return f32_to_bf16_bits(g.standard_normal(N, dtype=np.float32) * np.float32(std))
+
+
+def transform_matrix(b, kind="orthogonal", seed=0):
+    """A b x b transform matrix as bfloat16 bit patterns (uint16) [b, b]."""
+    g = rng(STREAM_T, CONFIG_IDS["transform"], seed, b, 0 if kind == "orthogonal" else 1)
+    a = g.standard_normal((b, b))
+    if kind == "orthogonal":
+        q, r = np.linalg.qr(a)
+        a = q * np.sign(np.diag(r))[None, :]
+    elif kind == "gaussian":
+        a = a / np.sqrt(b)
+    else:
+        raise ValueError(kind)
+    return f32_to_bf16_bits(a.astype(np.float32))
 
 
 def cases(config):
