@@ -69,6 +69,9 @@ __all__ = [
     "linear_sc_workspace_bytes",
     "warmup",
     "token_counts_for_warmup",
+    "transform_bf16",
+    "quant_nvfp4_transform",
+    "quant_nvfp4_dynamic",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -124,6 +127,18 @@ SIGNATURES = {
     "fql_linear_fp8_block_describe": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_char_p, _c_sz]),
     "fql_linear_fp8_block": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_f32, _c_vp,
                                       _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fql_transform_bf16": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_int, _c_vp, _c_i64,
+                                    _c_vp]),
+    "fql_quant_nvfp4_transform": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_vp, _c_int,
+                                           _c_vp, _c_vp, _c_vp]),
+    "fql_quant_nvfp4_dynamic": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_int, _c_vp,
+                                         _c_vp, _c_vp, _c_vp]),
+    "fql_linear_nvfp4_transform": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_vp, _c_int,
+                                            _c_vp, _c_i64, _c_f32, _c_vp, _c_vp, _c_i64, _c_vp,
+                                            _c_sz, _c_vp]),
+    "fql_linear_nvfp4_dynamic": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_int, _c_vp,
+                                          _c_i64, _c_f32, _c_vp, _c_vp, _c_i64, _c_vp, _c_sz,
+                                          _c_vp]),
     "fql_quant_mxfp4": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
     "fql_quant_mxfp4_f32": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
     "fql_packed_mxfp4_bytes": (_c_int, [_c_i64, _c_i64, ctypes.POINTER(_c_sz)]),
@@ -320,28 +335,42 @@ class NVFP4Weight:
     input_global_scale: the activation encode scale g_x (static calibration);
     weight_global_scale: g_w; hadamard_block: rotation block (0 = none).
     alpha = 1 / (g_x * g_w) rounded once to float32.
+    transform: optional bf16 [b, b] device matrix T (b in {16, 32, 64, 128}),
+    a general block-diagonal transform applied to the activation in place of
+    the Hadamard rotation (the weight must have been transformed alike
+    offline). dynamic_input_scale: g_x is computed from each call's
+    activation (448 * 6 / amax) on the device instead of the static scale.
     """
 
-    def __init__(self, packed, N, K, input_global_scale, weight_global_scale, hadamard_block=0):
+    def __init__(self, packed, N, K, input_global_scale, weight_global_scale, hadamard_block=0,
+                 transform=None, dynamic_input_scale=False):
         self.packed = packed
         self.N, self.K = int(N), int(K)
         self.input_global_scale = float(input_global_scale)
         self.weight_global_scale = float(weight_global_scale)
         self.hadamard_block = int(hadamard_block)
+        if transform is not None:
+            _transform_matrix(transform)
+            if self.hadamard_block:
+                raise FQLError("a weight takes either a Hadamard block or a transform matrix")
+        self.transform = transform
+        self.dynamic_input_scale = bool(dynamic_input_scale)
         import numpy as np
 
         self.alpha = float(np.float32((1.0 / np.float64(np.float32(input_global_scale))) *
                                       (1.0 / np.float64(np.float32(weight_global_scale)))))
 
     @classmethod
-    def from_float(cls, w, input_global_scale, hadamard_block=0, weight_global_scale=None):
-        """Quantize and pack a float32 weight [N, K] on the GPU."""
+    def from_float(cls, w, input_global_scale, hadamard_block=0, weight_global_scale=None,
+                   transform=None, dynamic_input_scale=False):
+        """Quantize and pack a float32 weight [N, K] on the GPU (already
+        transformed when `transform` is given)."""
         if weight_global_scale is None:
             weight_global_scale = global_scale_from_amax(amax(w, hadamard_block).item())
         codes, scales = quant_nvfp4_weight(w, weight_global_scale, hadamard_block)
         packed = pack_weight_nvfp4(codes, scales)
         return cls(packed, w.shape[0], w.shape[1], input_global_scale, weight_global_scale,
-                   hadamard_block)
+                   hadamard_block, transform=transform, dynamic_input_scale=dynamic_input_scale)
 
     def repack_(self, codes, scales):
         """Re-pack new canonical weights into the same storage (address kept)."""
@@ -406,11 +435,90 @@ def linear_nvfp4(x, weight, alpha=None, bias=None, out=None, workspace=None):
     need = linear_workspace_bytes(M, N, K)
     if workspace is None:
         workspace = _workspace(x.device, need)
-    _check(lib().fql_linear_nvfp4(_ptr(x2), M, K, ld, weight.input_global_scale,
-                                  weight.hadamard_block, _ptr(weight.packed), N, float(alpha),
-                                  _ptr(bias), _ptr(y2), ldy, _ptr(workspace), workspace.numel(),
-                                  _stream(x.device)))
+    T = getattr(weight, "transform", None)
+    if getattr(weight, "dynamic_input_scale", False):
+        b = T.shape[0] if T is not None else weight.hadamard_block
+        _check(lib().fql_linear_nvfp4_dynamic(_ptr(x2), M, K, ld, _ptr(T), b, _ptr(weight.packed), N,
+                                              weight.weight_global_scale, _ptr(bias), _ptr(y2), ldy,
+                                              _ptr(workspace), workspace.numel(), _stream(x.device)))
+    elif T is not None:
+        _check(lib().fql_linear_nvfp4_transform(_ptr(x2), M, K, ld, weight.input_global_scale,
+                                                _ptr(T), T.shape[0], _ptr(weight.packed), N,
+                                                float(alpha), _ptr(bias), _ptr(y2), ldy,
+                                                _ptr(workspace), workspace.numel(),
+                                                _stream(x.device)))
+    else:
+        _check(lib().fql_linear_nvfp4(_ptr(x2), M, K, ld, weight.input_global_scale,
+                                      weight.hadamard_block, _ptr(weight.packed), N, float(alpha),
+                                      _ptr(bias), _ptr(y2), ldy, _ptr(workspace), workspace.numel(),
+                                      _stream(x.device)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# general block-diagonal transform, dynamic global scale
+# ---------------------------------------------------------------------------
+
+def _transform_matrix(T):
+    _require_cuda(T, "transform")
+    if (T.dtype != torch.bfloat16 or T.dim() != 2 or T.shape[0] != T.shape[1]
+            or T.shape[0] not in (16, 32, 64, 128) or not T.is_contiguous()
+            or T.data_ptr() % 16 != 0):
+        raise FQLError("transform must be a contiguous, 16-byte aligned bf16 [b, b] matrix, "
+                       "b in {16, 32, 64, 128}")
+    return T.shape[0]
+
+
+def transform_bf16(x, T):
+    """v = per-chunk T @ x (float32 [..., K]) for bf16 x [..., K]: the block-diagonal
+    transform alone, as the quantizer applies it."""
+    _require_cuda(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise FQLError("transform_bf16 takes bfloat16 activations")
+    b = _transform_matrix(T)
+    x2, ld = _rows_view(x, "x")
+    M, K = x2.shape
+    v = torch.empty(tuple(x.shape[:-1]) + (K,), dtype=torch.float32, device=x.device)
+    _check(lib().fql_transform_bf16(_ptr(x2), M, K, ld, _ptr(T), b, _ptr(v), K, _stream(x.device)))
+    return v
+
+
+def quant_nvfp4_transform(x, T, global_scale, codes=None, scales=None):
+    """NVFP4-quantize per-chunk T @ x: (codes uint8 [..., K/2], scales uint8 [..., K/16])."""
+    _require_cuda(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise FQLError("quant_nvfp4_transform takes bfloat16 activations")
+    b = _transform_matrix(T)
+    x2, ld = _rows_view(x, "x")
+    M, K = x2.shape
+    lead = tuple(x.shape[:-1])
+    if codes is None:
+        codes = torch.empty(lead + (K // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(lead + (K // 16,), dtype=torch.uint8, device=x.device)
+    _check(lib().fql_quant_nvfp4_transform(_ptr(x2), M, K, ld, float(global_scale), _ptr(T), b,
+                                           _ptr(codes), _ptr(scales), _stream(x.device)))
+    return codes, scales
+
+
+def quant_nvfp4_dynamic(x, T=None, hadamard_block=0):
+    """NVFP4-quantize x with g = 448 * 6 / amax computed on the device from this
+    activation (after the transform T, or the Hadamard rotation, if any).
+    Returns (codes, scales, scalars): scalars float32 [4] on the device,
+    [0] = amax, [1] = g."""
+    _require_cuda(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise FQLError("quant_nvfp4_dynamic takes bfloat16 activations")
+    b = _transform_matrix(T) if T is not None else int(hadamard_block)
+    x2, ld = _rows_view(x, "x")
+    M, K = x2.shape
+    lead = tuple(x.shape[:-1])
+    codes = torch.empty(lead + (K // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(lead + (K // 16,), dtype=torch.uint8, device=x.device)
+    scalars = torch.empty(4, dtype=torch.float32, device=x.device)
+    _check(lib().fql_quant_nvfp4_dynamic(_ptr(x2), M, K, ld, _ptr(T), b, _ptr(scalars), _ptr(codes),
+                                         _ptr(scales), _stream(x.device)))
+    return codes, scales, scalars
 
 
 # ---------------------------------------------------------------------------

@@ -21,7 +21,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfql.so")
 
 SOURCES = ["fql_api.hip", "quant_nvfp4.hip", "pack_nvfp4.hip", "gemm_nvfp4.hip", "sc_quant.hip",
-           "sc_gemm.hip"]
+           "sc_gemm.hip", "transform_nvfp4.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -252,6 +252,183 @@ int fql_linear_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float inp
   return hip_status(e, "linear launch");
 }
 
+// ---- general block-diagonal transform, dynamic global scale ------------------
+
+}  // extern "C"
+
+namespace {
+
+int check_transform(const void* T, int b, int64_t K) {
+  if (b != 16 && b != 32 && b != 64 && b != 128)
+    return fail(FQL_ERR_INVALID, "transform block must be 16, 32, 64 or 128 (got %d)", b);
+  if (K % b != 0)
+    return fail(FQL_ERR_INVALID, "K %lld is not a multiple of the transform block %d", (long long)K, b);
+  if (!T) return fail(FQL_ERR_INVALID, "null transform matrix");
+  if (reinterpret_cast<uintptr_t>(T) % 16 != 0)
+    return fail(FQL_ERR_INVALID, "transform matrix must be 16-byte aligned");
+  return FQL_OK;
+}
+
+// amax of the (optionally transformed or rotated) activation into amax_slot,
+// then g (and alpha when g_w > 0) on the device.
+hipError_t launch_dynamic_prologue(const void* x, int64_t M, int64_t K, int64_t ldx,
+                                   const void* T, int b, uint32_t* amax_slot, float g_w,
+                                   float* g_out, float* alpha_out, hipStream_t st) {
+  hipError_t e;
+  if (T) {
+    fql::TransformArgs a{};
+    a.mode = 2;
+    a.x = static_cast<const uint16_t*>(x); a.M = M; a.K = K; a.ldx = ldx;
+    a.aligned = fql::transform_aligned(x, ldx, b);
+    a.T = static_cast<const uint16_t*>(T); a.b = b;
+    a.rows_out = M; a.amax = amax_slot;
+    e = fql::launch_transform_nvfp4(a, st);
+  } else {
+    e = fql::launch_amax_bf16(static_cast<const uint16_t*>(x), M, K, ldx, b, aligned16(x, ldx, 2),
+                              reinterpret_cast<float*>(amax_slot), st);
+  }
+  if (e != hipSuccess) return e;
+  return fql::launch_dynamic_scale(amax_slot, g_w, g_out, alpha_out, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fql_transform_bf16(const void* x, int64_t M, int64_t K, int64_t ldx, const void* T, int b,
+                       float* v, int64_t ldv, void* stream) {
+  if (int r = check_nvfp4_shape(M, K, ldx, 0, "M")) return r;
+  if (int r = check_transform(T, b, K)) return r;
+  if (!x || !v) return fail(FQL_ERR_INVALID, "null pointer");
+  if (ldv < K || ldv % 4 != 0 || reinterpret_cast<uintptr_t>(v) % 16 != 0)
+    return fail(FQL_ERR_INVALID, "v must be 16-byte aligned with ldv >= K, ldv % 4 == 0");
+  fql::TransformArgs a{};
+  a.mode = 3;
+  a.x = static_cast<const uint16_t*>(x); a.M = M; a.K = K; a.ldx = ldx;
+  a.aligned = fql::transform_aligned(x, ldx, b);
+  a.T = static_cast<const uint16_t*>(T); a.b = b;
+  a.rows_out = M; a.v = v; a.ldv = ldv;
+  return hip_status(fql::launch_transform_nvfp4(a, static_cast<hipStream_t>(stream)), "transform launch");
+}
+
+int fql_quant_nvfp4_transform(const void* x, int64_t M, int64_t K, int64_t ldx, float global_scale,
+                              const void* T, int b, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (int r = check_nvfp4_shape(M, K, ldx, 0, "M")) return r;
+  if (int r = check_transform(T, b, K)) return r;
+  if (int r = check_scale(global_scale, "global_scale")) return r;
+  if (!x || !codes || !scales) return fail(FQL_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(codes) % 8 != 0)
+    return fail(FQL_ERR_INVALID, "codes must be 8-byte aligned");
+  fql::TransformArgs a{};
+  a.mode = 0;
+  a.x = static_cast<const uint16_t*>(x); a.M = M; a.K = K; a.ldx = ldx;
+  a.aligned = fql::transform_aligned(x, ldx, b);
+  a.T = static_cast<const uint16_t*>(T); a.b = b; a.g = global_scale;
+  a.codes = codes; a.scales = scales; a.rows_out = M;
+  return hip_status(fql::launch_transform_nvfp4(a, static_cast<hipStream_t>(stream)), "transform quant launch");
+}
+
+int fql_quant_nvfp4_dynamic(const void* x, int64_t M, int64_t K, int64_t ldx, const void* T, int b,
+                            float* scalars, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (int r = check_nvfp4_shape(M, K, ldx, T ? 0 : b, "M")) return r;
+  if (T) {
+    if (int r = check_transform(T, b, K)) return r;
+  }
+  if (!x || !codes || !scales || !scalars) return fail(FQL_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(codes) % 8 != 0 || reinterpret_cast<uintptr_t>(scalars) % 4 != 0)
+    return fail(FQL_ERR_INVALID, "codes must be 8-byte and scalars 4-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t* amax_slot = reinterpret_cast<uint32_t*>(scalars);
+  hipError_t e = launch_dynamic_prologue(x, M, K, ldx, T, b, amax_slot, 0.0f, scalars + 1, nullptr, st);
+  if (e != hipSuccess) return hip_status(e, "dynamic scale launch");
+  if (T) {
+    fql::TransformArgs a{};
+    a.mode = 0;
+    a.x = static_cast<const uint16_t*>(x); a.M = M; a.K = K; a.ldx = ldx;
+    a.aligned = fql::transform_aligned(x, ldx, b);
+    a.T = static_cast<const uint16_t*>(T); a.b = b; a.g = 1.0f; a.g_dev = scalars + 1;
+    a.codes = codes; a.scales = scales; a.rows_out = M;
+    e = fql::launch_transform_nvfp4(a, st);
+  } else {
+    e = fql::launch_quant_nvfp4_bf16(static_cast<const uint16_t*>(x), M, K, ldx, 1.0f, b,
+                                     aligned16(x, ldx, 2), codes, scales, st, scalars + 1);
+  }
+  return hip_status(e, "dynamic quant launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+int linear_nvfp4_extras(const void* x, int64_t M, int64_t K, int64_t ldx, float g, const void* T,
+                        int b, const void* w_packed, int64_t N, float alpha, float g_w,
+                        bool dynamic, const void* bias, void* y, int64_t ldy, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (int r = check_nvfp4_shape(M, K, ldx, T ? 0 : b, "M")) return r;
+  if (T) {
+    if (int r = check_transform(T, b, K)) return r;
+  }
+  if (dynamic) {
+    if (int r = check_scale(g_w, "weight_global_scale")) return r;
+  } else {
+    if (int r = check_scale(g, "input_global_scale")) return r;
+    if (!std::isfinite(alpha)) return fail(FQL_ERR_INVALID, "alpha must be finite");
+  }
+  if (N < 1 || N > (int64_t)1 << 24) return fail(FQL_ERR_INVALID, "N out of range");
+  if (ldy < N) return fail(FQL_ERR_INVALID, "ldy %lld is smaller than N %lld", (long long)ldy, (long long)N);
+  if (!x || !w_packed || !y || !workspace) return fail(FQL_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(w_packed) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(FQL_ERR_INVALID, "packed weight must be 16-byte and workspace 256-byte aligned");
+  // a plan that writes x_hat (the fused small-M kernel quantizes with a host-side scale)
+  const fql::GemmPlan plan = fql::plan_gemm_nvfp4(M, N, K, false);
+  if (workspace_bytes < (size_t)plan.total_bytes)
+    return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
+                (long long)plan.total_bytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* scal = reinterpret_cast<float*>(ws + fql::kWorkspaceScalarOffset);
+  fql::LinearExtras ex{};
+  ex.T = static_cast<const uint16_t*>(T);
+  ex.t_aligned = T ? fql::transform_aligned(x, ldx, b) : false;
+  if (dynamic) {
+    hipError_t e = launch_dynamic_prologue(x, M, K, ldx, T, b, reinterpret_cast<uint32_t*>(scal), g_w,
+                                           scal + 1, scal + 2, st);
+    if (e != hipSuccess) return hip_status(e, "dynamic scale launch");
+    ex.g_dev = scal + 1;
+    ex.alpha_dev = scal + 2;
+    g = 1.0f;
+    alpha = 1.0f;
+  }
+  hipError_t e = fql::launch_linear_nvfp4(
+      plan, static_cast<const uint16_t*>(x), M, K, ldx, g, b, aligned16(x, ldx, 2),
+      static_cast<const uint8_t*>(w_packed), N, alpha, static_cast<const uint16_t*>(bias),
+      static_cast<uint16_t*>(y), ldy, ws, st, &ex);
+  return hip_status(e, "linear launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fql_linear_nvfp4_transform(const void* x, int64_t M, int64_t K, int64_t ldx,
+                               float input_global_scale, const void* T, int b,
+                               const void* w_packed, int64_t N, float alpha, const void* bias,
+                               void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!T) return fail(FQL_ERR_INVALID, "null transform matrix");
+  return linear_nvfp4_extras(x, M, K, ldx, input_global_scale, T, b, w_packed, N, alpha, 0.0f,
+                             false, bias, y, ldy, workspace, workspace_bytes, stream);
+}
+
+int fql_linear_nvfp4_dynamic(const void* x, int64_t M, int64_t K, int64_t ldx, const void* T,
+                             int b, const void* w_packed, int64_t N, float weight_global_scale,
+                             const void* bias, void* y, int64_t ldy, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return linear_nvfp4_extras(x, M, K, ldx, 0.0f, T, b, w_packed, N, 0.0f, weight_global_scale,
+                             true, bias, y, ldy, workspace, workspace_bytes, stream);
+}
+
 // ---- scaled-MFMA formats: MXFP4, MXFP8, per-tensor FP8, block FP8 -------------
 
 }  // extern "C"

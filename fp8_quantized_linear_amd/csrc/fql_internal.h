@@ -37,13 +37,13 @@ inline PackedDims packed_dims(int64_t N, int64_t K) { return PackedDims{round_up
 // ---- launchers (stream-ordered, return the launch status) -----------------
 hipError_t launch_quant_nvfp4_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
                                    int hb, bool aligned, uint8_t* codes, uint8_t* scales,
-                                   hipStream_t st);
+                                   hipStream_t st, const float* g_dev = nullptr);
 hipError_t launch_quant_nvfp4_f32(const float* w, int64_t N, int64_t K, int64_t ldw, float g,
                                   int hb, bool aligned, uint8_t* codes, uint8_t* scales,
                                   hipStream_t st);
 hipError_t launch_quant_nvfp4_xhat(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
                                    int hb, bool aligned, int64_t Mp, int64_t Kp, _Float16* xhat,
-                                   hipStream_t st);
+                                   const float* g_dev, hipStream_t st);
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int hb,
                             bool aligned, float* out, hipStream_t st);
 hipError_t launch_amax_f32(const float* w, int64_t N, int64_t K, int64_t ldw, int hb, bool aligned,
@@ -99,10 +99,59 @@ bool gemv_ring_config_built(int w, int mt, int nt, int d);
 // Kernel name and parameters of a plan (diagnostics).
 std::string describe_plan(const GemmPlan& p);
 
+// ---- general block-diagonal transform + dynamic global scale ---------------
+// Workspace of the NVFP4 linear call: the first kWorkspaceCounterBytes hold
+// split-K arrival counters, except the last kWorkspaceScalarBytes, which hold
+// the per-call device scalars of the dynamic-scale path:
+//   word 0 tensor amax (float bits), word 1 g_x, word 2 alpha.
+constexpr int64_t kWorkspaceCounterBytes = 64 * 1024;
+constexpr int64_t kWorkspaceScalarBytes = 256;
+constexpr int64_t kWorkspaceScalarOffset = kWorkspaceCounterBytes - kWorkspaceScalarBytes;
+
+// One launch of the transform kernel. mode 0: canonical codes [M][K/2] and
+// scales [M][K/16]; 1: x_hat (float16, GEMM A-fragment order, rows_out = Mp
+// rows and Kp columns, zero padded); 2: max |v| into *amax (zeroed first);
+// 3: float32 values v [M][ldv].
+struct TransformArgs {
+  int mode;
+  const uint16_t* x;
+  int64_t M, K, ldx;
+  bool aligned;         // transform_aligned(x, ldx, b)
+  const uint16_t* T;    // bf16 [b][b], 16-byte aligned
+  int b;
+  float g;
+  const float* g_dev;   // non-null: g read from device memory
+  uint8_t* codes;
+  uint8_t* scales;
+  _Float16* xhat;
+  int64_t rows_out, Kp;
+  float* v;
+  int64_t ldv;
+  uint32_t* amax;
+};
+bool transform_aligned(const void* x, int64_t ldx, int b);
+hipError_t launch_transform_nvfp4(const TransformArgs& a, hipStream_t st);
+// g = fl32(2688 / amax) (1 when amax = 0, at most 2^118) into *g_out;
+// alpha = fl32((1/g) * (1/g_w)) into *alpha_out when it is non-null.
+hipError_t launch_dynamic_scale(const uint32_t* amax_bits, float g_w, float* g_out,
+                                float* alpha_out, hipStream_t st);
+hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st);
+
+// Optional parts of a linear call: a general transform T (b = hb) in place
+// of the Hadamard rotation, and device-resident g / alpha. Needs a plan that
+// writes x_hat (the aligned = false plan).
+struct LinearExtras {
+  const uint16_t* T;
+  bool t_aligned;
+  const float* g_dev;
+  const float* alpha_dev;
+};
+
 hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K,
                                int64_t ldx, float g, int hb, bool aligned, const uint8_t* packed,
                                int64_t N, float alpha, const uint16_t* bias, uint16_t* y,
-                               int64_t ldy, uint8_t* workspace, hipStream_t st);
+                               int64_t ldy, uint8_t* workspace, hipStream_t st,
+                               const LinearExtras* ex = nullptr);
 
 // ---- scaled-MFMA formats: MXFP4, MXFP8, per-tensor FP8, block FP8 ---------
 // All four run on v_mfma_scale_f32_16x16x128_f8f6f4 (one instruction per

@@ -90,7 +90,9 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
     const _Float16* __restrict__ xhat, const uint16_t* __restrict__ x, int64_t ldx, float g,
     const uint8_t* __restrict__ wcodes,
     const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, float alpha,
+    const float* __restrict__ alpha_dev,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t ldy) {
+  if (alpha_dev != nullptr) alpha = *alpha_dev;  // per-call scale computed on the device
   typedef GemvStage<MT, NT> Stage;
   constexpr int L = MT * 4 + NT * 2;  // loads per chunk
   static_assert(L * (D - 1) <= 63, "vmcnt range");
@@ -470,9 +472,11 @@ template <int MT, int NT, int WM>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(
     const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
     const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, int ngroups,
-    int kc_per_split, int splits, float alpha, const uint16_t* __restrict__ bias,
+    int kc_per_split, int splits, float alpha,
+    const float* __restrict__ alpha_dev, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ y, int64_t ldy, float4v* __restrict__ partial,
     uint32_t* __restrict__ counters) {
+  if (alpha_dev != nullptr) alpha = *alpha_dev;  // per-call scale computed on the device
   constexpr int WN = 4 / WM;
   constexpr int AM = WM * MT;  // 16-row A tiles per workgroup
   __shared__ uint4v a_lds[2][AM * 4][64];
@@ -623,9 +627,11 @@ template <int MT, int NT, int ST, int OCC>
 __global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(
     const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
     const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, int ngroups,
-    int kc_per_split, int splits, float alpha, const uint16_t* __restrict__ bias,
+    int kc_per_split, int splits, float alpha,
+    const float* __restrict__ alpha_dev, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ y, int64_t ldy, float4v* __restrict__ partial,
     uint32_t* __restrict__ counters) {
+  if (alpha_dev != nullptr) alpha = *alpha_dev;  // per-call scale computed on the device
   static_assert(ST >= 3 && ST <= 4, "ring depth (chunk i+1 must be issued a whole chunk ahead)");
   constexpr int L = MT + 2 * NT;  // LDS loads per chunk per wave
   static_assert(L * (ST - 2) <= 63, "vmcnt range");
@@ -827,9 +833,11 @@ template <int MT, int NT, int ST, int OCC>
 __global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
     const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
     const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, int ngroups,
-    int kc_per_split, int splits, float alpha, const uint16_t* __restrict__ bias,
+    int kc_per_split, int splits, float alpha,
+    const float* __restrict__ alpha_dev, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ y, int64_t ldy, float4v* __restrict__ partial,
     uint32_t* __restrict__ counters) {
+  if (alpha_dev != nullptr) alpha = *alpha_dev;  // per-call scale computed on the device
   static_assert(ST >= 3 && ST <= 4, "ring depth (chunk i+1 must be issued a whole chunk ahead)");
   constexpr int L = 2 * MT + 4 * NT;  // LDS loads per chunk per wave
   static_assert(L * (ST - 2) <= 63, "vmcnt range");
@@ -1047,7 +1055,7 @@ static GemmOverride gemm_override() {
   }
   return o;
 }
-static constexpr int64_t kCounterBytes = 64 * 1024;  // arrival counters at the workspace start
+static constexpr int64_t kCounterBytes = kWorkspaceCounterBytes;
 static constexpr int64_t kGemvMaxLds = 64 * 1024;    // compact activation copy in LDS
 static constexpr int64_t kGemvMaxRedundantBlocks = 1 << 20;  // workgroups x 16-blocks quantized
 
@@ -1261,14 +1269,15 @@ static void launch_gemv_hb(const GemmPlan& p, const uint16_t* x, int64_t M, int6
 
 template <int MT, int NT, int WM>
 static hipError_t launch_tiled_t(const GemmPlan& p, const _Float16* xhat, const uint8_t* packed,
-                                 int64_t M, int64_t N, float alpha, const uint16_t* bias,
+                                 int64_t M, int64_t N, float alpha, const float* alpha_dev,
+                                 const uint16_t* bias,
                                  uint16_t* y, int64_t ldy, float4v* partial, uint32_t* counters,
                                  hipStream_t st) {
   const uint8_t* wcodes = packed;
   const uint8_t* wscales = packed + p.Np * p.Kp / 2;
   gemm_tiled_kernel<MT, NT, WM><<<(unsigned)(p.groups * p.splits), 256, 0, st>>>(
       xhat, wcodes, wscales, (int)M, (int)N, p.Kp, (int)(p.Np / 16), (int)p.ngroups,
-      p.kc_per_split, p.splits, alpha, bias, y, ldy, partial, counters);
+      p.kc_per_split, p.splits, alpha, alpha_dev, bias, y, ldy, partial, counters);
   return hipGetLastError();
 }
 
@@ -1279,14 +1288,15 @@ static hipError_t launch_tiled_t(const GemmPlan& p, const _Float16* xhat, const 
 
 template <int MT, int NT, int ST, int OCC>
 static hipError_t launch_lds_t(const GemmPlan& p, const _Float16* xhat, const uint8_t* packed,
-                               int64_t M, int64_t N, float alpha, const uint16_t* bias,
+                               int64_t M, int64_t N, float alpha, const float* alpha_dev,
+                                 const uint16_t* bias,
                                uint16_t* y, int64_t ldy, float4v* partial, uint32_t* counters,
                                hipStream_t st) {
   const uint8_t* wcodes = packed;
   const uint8_t* wscales = packed + p.Np * p.Kp / 2;
   gemm_lds_kernel<MT, NT, ST, OCC><<<(unsigned)(p.groups * p.splits), 256, 0, st>>>(
       xhat, wcodes, wscales, (int)M, (int)N, p.Kp, (int)(p.Np / 16), (int)p.ngroups,
-      p.kc_per_split, p.splits, alpha, bias, y, ldy, partial, counters);
+      p.kc_per_split, p.splits, alpha, alpha_dev, bias, y, ldy, partial, counters);
   return hipGetLastError();
 }
 
@@ -1305,14 +1315,15 @@ bool lds_config_built(int mt, int nt, int st) {
 
 template <int MT, int NT, int ST, int OCC>
 static hipError_t launch_lds32_t(const GemmPlan& p, const _Float16* xhat, const uint8_t* packed,
-                                 int64_t M, int64_t N, float alpha, const uint16_t* bias,
+                                 int64_t M, int64_t N, float alpha, const float* alpha_dev,
+                                 const uint16_t* bias,
                                  uint16_t* y, int64_t ldy, float4v* partial, uint32_t* counters,
                                  hipStream_t st) {
   const uint8_t* wcodes = packed;
   const uint8_t* wscales = packed + p.Np * p.Kp / 2;
   gemm_lds32_kernel<MT, NT, ST, OCC><<<(unsigned)(p.groups * p.splits), 256, 0, st>>>(
       xhat, wcodes, wscales, (int)M, (int)N, p.Kp, (int)(p.Np / 16), (int)p.ngroups,
-      p.kc_per_split, p.splits, alpha, bias, y, ldy, partial, counters);
+      p.kc_per_split, p.splits, alpha, alpha_dev, bias, y, ldy, partial, counters);
   return hipGetLastError();
 }
 
@@ -1349,11 +1360,14 @@ bool tiled_config_built(int mt, int nt, int wm) {
 hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K,
                                int64_t ldx, float g, int hb, bool aligned, const uint8_t* packed,
                                int64_t N, float alpha, const uint16_t* bias, uint16_t* y,
-                               int64_t ldy, uint8_t* workspace, hipStream_t st) {
+                               int64_t ldy, uint8_t* workspace, hipStream_t st,
+                               const LinearExtras* ex) {
   uint32_t* counters = reinterpret_cast<uint32_t*>(workspace);
   _Float16* xhat = reinterpret_cast<_Float16*>(workspace + p.counter_bytes);
   float* partial = reinterpret_cast<float*>(workspace + p.counter_bytes + p.xhat_bytes);
-  if (p.splits > 1 && p.groups > p.counter_bytes / 4) return hipErrorInvalidValue;
+  const float* alpha_dev = ex != nullptr ? ex->alpha_dev : nullptr;
+  if (p.splits > 1 && p.groups > (p.counter_bytes - kWorkspaceScalarBytes) / 4) return hipErrorInvalidValue;
+  if (p.kind == 0 && ex != nullptr) return hipErrorInvalidValue;  // needs a plan that writes x_hat
   if (p.kind == 0 && aligned) {  // the fused path reads x rows with 16-byte loads
     switch (hb) {
       case 0: launch_gemv_hb<0>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st); break;
@@ -1366,9 +1380,20 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
     return hipGetLastError();
   }
   if (p.kind == 0) return hipErrorInvalidValue;  // caller re-plans unaligned inputs as kind 1
-  const bool fused = p.kind == 4 && p.fq && hb == 0 && aligned && K % 128 == 0;
+  const bool fused = ex == nullptr && p.kind == 4 && p.fq && hb == 0 && aligned && K % 128 == 0;
   if (!fused) {
-    hipError_t e = launch_quant_nvfp4_xhat(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp, xhat, st);
+    hipError_t e;
+    if (ex != nullptr && ex->T != nullptr) {
+      TransformArgs ta{};
+      ta.mode = 1;  // x_hat
+      ta.x = x; ta.M = M; ta.K = K; ta.ldx = ldx; ta.aligned = ex->t_aligned;
+      ta.T = ex->T; ta.b = hb; ta.g = g; ta.g_dev = ex->g_dev;
+      ta.xhat = xhat; ta.rows_out = p.Mp; ta.Kp = p.Kp;
+      e = launch_transform_nvfp4(ta, st);
+    } else {
+      e = launch_quant_nvfp4_xhat(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp, xhat,
+                                  ex != nullptr ? ex->g_dev : nullptr, st);
+    }
     if (e != hipSuccess) return e;
   }
   float4v* partial4 = reinterpret_cast<float4v*>(partial);
@@ -1378,11 +1403,11 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
     if (fused)                                                                                        \
       gemv_ring_kernel<A, B, C, E, 1><<<(unsigned)p.groups, 64 * A, 0, st>>>(                         \
           xhat, x, ldx, g, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16),   \
-          alpha, bias, y, ldy);                                                                        \
+          alpha, alpha_dev, bias, y, ldy);                                                             \
     else                                                                                              \
       gemv_ring_kernel<A, B, C, E, 0><<<(unsigned)p.groups, 64 * A, 0, st>>>(                         \
           xhat, x, ldx, g, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16),   \
-          alpha, bias, y, ldy);                                                                        \
+          alpha, alpha_dev, bias, y, ldy);                                                             \
     return hipGetLastError();                                                                          \
   }
     FQL_GEMV_RING_CONFIGS(FQL_X)
@@ -1392,7 +1417,7 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
   if (p.kind == 3) {
 #define FQL_X(A, B, C, D)                                                                        \
   if (p.mt == A && p.nt == B && p.st == C)                                                       \
-    return launch_lds32_t<A, B, C, D>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial4, counters, st);
+    return launch_lds32_t<A, B, C, D>(p, xhat, packed, M, N, alpha, alpha_dev, bias, y, ldy, partial4, counters, st);
     FQL_LDS32_CONFIGS(FQL_X)
 #undef FQL_X
     return hipErrorInvalidValue;
@@ -1400,14 +1425,14 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
   if (p.kind == 2) {
 #define FQL_X(A, B, C, D)                                                                        \
   if (p.mt == A && p.nt == B && p.st == C)                                                       \
-    return launch_lds_t<A, B, C, D>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial4, counters, st);
+    return launch_lds_t<A, B, C, D>(p, xhat, packed, M, N, alpha, alpha_dev, bias, y, ldy, partial4, counters, st);
     FQL_LDS_CONFIGS(FQL_X)
 #undef FQL_X
     return hipErrorInvalidValue;
   }
 #define FQL_X(A, B, C)                                                                           \
   if (p.mt == A && p.nt == B && p.wm == C)                                                       \
-    return launch_tiled_t<A, B, C>(p, xhat, packed, M, N, alpha, bias, y, ldy, partial4, counters, st);
+    return launch_tiled_t<A, B, C>(p, xhat, packed, M, N, alpha, alpha_dev, bias, y, ldy, partial4, counters, st);
   FQL_TILED_CONFIGS(FQL_X)
 #undef FQL_X
   return hipErrorInvalidValue;

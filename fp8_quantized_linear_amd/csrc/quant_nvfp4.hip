@@ -33,7 +33,8 @@ namespace fql {
 template <typename TIn, int HB>
 __global__ __launch_bounds__(256) void quant_nvfp4_canonical_kernel(
     const TIn* __restrict__ x, int64_t rows, int64_t K, int64_t ldx, float g, int aligned16,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ g_dev) {
+  if (g_dev != nullptr) g = *g_dev;  // per-call global scale computed on the device
   const int64_t nblk = K / 16;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const bool active = i < rows * nblk;
@@ -61,11 +62,12 @@ __global__ __launch_bounds__(256) void quant_nvfp4_canonical_kernel(
 template <int HB>
 __global__ __launch_bounds__(256) void quant_nvfp4_xhat_kernel(
     const uint16_t* __restrict__ x, int M, int K, int64_t ldx, float g, int aligned16, int Mp,
-    int Kp, _Float16* __restrict__ xhat) {
+    int Kp, _Float16* __restrict__ xhat, const float* __restrict__ g_dev) {
   // 32-bit index arithmetic: the launcher checks Mp * Kp / 16 < 2^31
   const uint32_t nblk = (uint32_t)Kp / 16u;
   const uint32_t i = blockIdx.x * 256u + threadIdx.x;
   if (i >= (uint32_t)Mp * nblk) return;  // whole waves only: Mp * nblk is a multiple of 64
+  if (g_dev != nullptr) g = *g_dev;      // per-call global scale computed on the device
   const uint32_t m = i / nblk;
   const uint32_t kb = i - m * nblk;
   const bool real = (m < (uint32_t)M) && (kb * 16u < (uint32_t)K);
@@ -139,16 +141,16 @@ __global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
 template <typename TIn>
 static hipError_t launch_canonical(const TIn* x, int64_t rows, int64_t K, int64_t ldx, float g,
                                    int hb, bool aligned, uint8_t* codes, uint8_t* scales,
-                                   hipStream_t st) {
+                                   const float* g_dev, hipStream_t st) {
   const int64_t total = rows * (K / 16);
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
   const int al = aligned ? 1 : 0;
   switch (hb) {
-    case 0: quant_nvfp4_canonical_kernel<TIn, 0><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales); break;
-    case 16: quant_nvfp4_canonical_kernel<TIn, 16><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales); break;
-    case 32: quant_nvfp4_canonical_kernel<TIn, 32><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales); break;
-    case 64: quant_nvfp4_canonical_kernel<TIn, 64><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales); break;
-    case 128: quant_nvfp4_canonical_kernel<TIn, 128><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales); break;
+    case 0: quant_nvfp4_canonical_kernel<TIn, 0><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales, g_dev); break;
+    case 16: quant_nvfp4_canonical_kernel<TIn, 16><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales, g_dev); break;
+    case 32: quant_nvfp4_canonical_kernel<TIn, 32><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales, g_dev); break;
+    case 64: quant_nvfp4_canonical_kernel<TIn, 64><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales, g_dev); break;
+    case 128: quant_nvfp4_canonical_kernel<TIn, 128><<<grid, block, 0, st>>>(x, rows, K, ldx, g, al, codes, scales, g_dev); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -156,30 +158,30 @@ static hipError_t launch_canonical(const TIn* x, int64_t rows, int64_t K, int64_
 
 hipError_t launch_quant_nvfp4_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
                                    int hb, bool aligned, uint8_t* codes, uint8_t* scales,
-                                   hipStream_t st) {
-  return launch_canonical<uint16_t>(x, M, K, ldx, g, hb, aligned, codes, scales, st);
+                                   hipStream_t st, const float* g_dev) {
+  return launch_canonical<uint16_t>(x, M, K, ldx, g, hb, aligned, codes, scales, g_dev, st);
 }
 
 hipError_t launch_quant_nvfp4_f32(const float* w, int64_t N, int64_t K, int64_t ldw, float g,
                                   int hb, bool aligned, uint8_t* codes, uint8_t* scales,
                                   hipStream_t st) {
-  return launch_canonical<float>(w, N, K, ldw, g, hb, aligned, codes, scales, st);
+  return launch_canonical<float>(w, N, K, ldw, g, hb, aligned, codes, scales, nullptr, st);
 }
 
 hipError_t launch_quant_nvfp4_xhat(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
                                    int hb, bool aligned, int64_t Mp, int64_t Kp, _Float16* xhat,
-                                   hipStream_t st) {
+                                   const float* g_dev, hipStream_t st) {
   const int64_t total = Mp * (Kp / 16);
   if (total >= ((int64_t)1 << 31) || Kp >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
   const int al = aligned ? 1 : 0;
   const int m = (int)M, k = (int)K, mp = (int)Mp, kp = (int)Kp;
   switch (hb) {
-    case 0: quant_nvfp4_xhat_kernel<0><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat); break;
-    case 16: quant_nvfp4_xhat_kernel<16><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat); break;
-    case 32: quant_nvfp4_xhat_kernel<32><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat); break;
-    case 64: quant_nvfp4_xhat_kernel<64><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat); break;
-    case 128: quant_nvfp4_xhat_kernel<128><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat); break;
+    case 0: quant_nvfp4_xhat_kernel<0><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
+    case 16: quant_nvfp4_xhat_kernel<16><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
+    case 32: quant_nvfp4_xhat_kernel<32><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
+    case 64: quant_nvfp4_xhat_kernel<64><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
+    case 128: quant_nvfp4_xhat_kernel<128><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

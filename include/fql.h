@@ -181,6 +181,63 @@ int fql_linear_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float inp
                      size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * General block-diagonal transform and dynamic global scale ("QUTLASS NVFP4
+ * online transforms" write-up: the fused quantizer accepts any
+ * block-diagonal transform, not only a fixed Hadamard matrix; the matrix is
+ * one b x b partition of the layer's input-transform weight with the
+ * 1/sqrt(n) normalisation already folded in, b in {16, 32, 64, 128}; its
+ * dense branch applies it as a linear layer, v = x @ T^T per chunk).
+ *   T   bf16 [b][b] row-major device matrix, 16-byte aligned; K % b == 0.
+ *   v[c*b + i] = sum_j T[i][j] * x[c*b + j]  per row, per b-chunk c,
+ *       accumulated in float32 on the matrix cores (the products are exact;
+ *       the sum's rounding order is the hardware's, so v may differ from the
+ *       exactly rounded sum in the last bits, and codes or scales from an
+ *       exact evaluation only at near-ties). An exactly zero sum is +0.
+ * Then the NVFP4 quantizer of fql_quant_nvfp4 on v. The dynamic variants
+ * compute g = fl32(2688 / amax) over the whole transformed activation on
+ * the device (1 when amax = 0, at most 2^118, which keeps g / s finite for
+ * every nonzero E4M3 scale s), so no host synchronisation is needed.
+ * ------------------------------------------------------------------------- */
+
+/* The transform alone: bf16 x [M][ldx] -> float32 v [M][ldv] (16-byte
+ * aligned, ldv >= K, ldv % 4 == 0). */
+int fql_transform_bf16(const void* x, int64_t M, int64_t K, int64_t ldx, const void* T, int b,
+                       float* v, int64_t ldv, void* stream);
+
+/* Transform + NVFP4 quantize with a static global scale: codes [M][K/2]
+ * (8-byte aligned), scales [M][K/16] E4M3, as fql_quant_nvfp4. */
+int fql_quant_nvfp4_transform(const void* x, int64_t M, int64_t K, int64_t ldx,
+                              float global_scale, const void* T, int b, uint8_t* codes,
+                              uint8_t* scales, void* stream);
+
+/* NVFP4 quantize with the dynamic global scale. T may be NULL: then b is a
+ * Hadamard block (0 = no rotation) as in fql_quant_nvfp4. scalars: device
+ * float32 [2] (4-byte aligned) receiving [0] = amax, [1] = g; later calls
+ * may overwrite it, so read it before reusing the buffer. Four kernels on
+ * the stream (amax, scale, quantize). */
+int fql_quant_nvfp4_dynamic(const void* x, int64_t M, int64_t K, int64_t ldx, const void* T, int b,
+                            float* scalars, uint8_t* codes, uint8_t* scales, void* stream);
+
+/* fql_linear_nvfp4 with the transform T (b x b) in place of the Hadamard
+ * rotation; the packed weight must come from a weight transformed alike.
+ * Same arguments, layouts and workspace as fql_linear_nvfp4. */
+int fql_linear_nvfp4_transform(const void* x, int64_t M, int64_t K, int64_t ldx,
+                               float input_global_scale, const void* T, int b,
+                               const void* w_packed, int64_t N, float alpha, const void* bias,
+                               void* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* fql_linear_nvfp4 with the dynamic activation global scale: g_x from this
+ * call's activation (after T, or the Hadamard block b when T is NULL) and
+ * alpha = fl32((1/g_x) * (1/weight_global_scale)) in float64, both on the
+ * device (kept in the workspace's reserved scalar slots, so concurrent calls
+ * need separate workspaces, as for every linear call). */
+int fql_linear_nvfp4_dynamic(const void* x, int64_t M, int64_t K, int64_t ldx, const void* T,
+                             int b, const void* w_packed, int64_t N, float weight_global_scale,
+                             const void* bias, void* y, int64_t ldy, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * MXFP4 (B12X write-up, Implementation: the MXFP4 linear kernel accepts only a
  * dynamically quantized activation; element and scale formats per OCP
  * Microscaling v1.0): E2M1 codes with one E8M0 scale byte per 32 consecutive
