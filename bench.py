@@ -37,7 +37,7 @@ FP4_PEAK_TFLOPS = 10100.0
 F16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 512 << 20
 
-WORKLOAD_KEYS = ("decode", "prefill", "hadamard", "tiny", "siblings")
+WORKLOAD_KEYS = ("decode", "prefill", "hadamard", "tiny", "siblings", "transform")
 FORMAT_KEYS = ("nvfp4", "mxfp4", "mxfp8", "fp8", "fp8_block")
 # algorithmic weight bytes per element: code + scale bytes per element
 WEIGHT_BYTES = {"nvfp4": 0.5 + 1.0 / 16, "mxfp4": 0.5 + 1.0 / 32, "mxfp8": 1.0 + 1.0 / 32,
@@ -58,6 +58,8 @@ WORKLOAD_NAMES = {
     "hadamard": "hadamard: Qwen3-32B gate_up/down at M=1,256,4096, block-diagonal Hadamard",
     "tiny": "tiny: M=16, K=256, N=512",
     "siblings": "siblings: K=4096, N=14336 at M=1,4096",
+    "transform": "transform: Qwen3-32B gate_up/down at M=1,256,4096, general b x b transform "
+                 "(random orthogonal bf16, b=16..128)",
 }
 
 
@@ -113,20 +115,30 @@ def _cases(workload, hb_override=None):
     return out
 
 
-def _kernel_of(M, N, K, fmt="nvfp4"):
-    """The kernel that carries one linear call of this shape (the library's own plan)."""
+def _kernel_of(M, N, K, fmt="nvfp4", xhat_only=False):
+    """The kernel that carries one linear call of this shape (the library's own plan;
+    the transform and dynamic-scale paths take the plan that writes x_hat)."""
     import fp8_quantized_linear_amd as fql
 
     if fmt != "nvfp4":
         return fql.linear_sc_plan(fmt, M, N, K).split(" grid=")[0].split(" + ")[-1]
-    return fql.linear_plan(M, N, K).split(" grid=")[0]
+    return fql.linear_plan(M, N, K, aligned=not xhat_only).split(" grid=")[0].split(" + ")[-1]
 
 
-def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4"):
+def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic=False):
     import torch
 
     import fp8_quantized_linear_amd as fql
     import synthetic
+
+    general = workload == "transform"  # the block size is a general transform's, not a rotation's
+    tmats = {}
+
+    def tmat(b):
+        if b not in tmats:
+            tmats[b] = torch.from_numpy(synthetic.transform_matrix(b).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return tmats[b]
 
     ok, why = fql.is_supported(0)
     if not ok:
@@ -139,7 +151,9 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4"):
         key = (name, K, N, hbk)
         if key not in weights:
             W = torch.from_numpy(synthetic.weight(N, K, config=workload)).to(dev)
-            if fmt == "nvfp4":
+            if fmt == "nvfp4" and general:
+                w0 = fql.NVFP4Weight.from_float(W, input_global_scale=1.0, transform=tmat(hbk))
+            elif fmt == "nvfp4":
                 w0 = fql.NVFP4Weight.from_float(W, input_global_scale=1.0, hadamard_block=hbk)
             elif fmt == "fp8":
                 w0 = fql.FP8Weight.from_float(W, input_scale=1.0)
@@ -155,8 +169,13 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4"):
         xb = synthetic.activations(synthetic.WORKLOADS[workload]["x"], M, K, config=workload)
         x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
         if fmt == "nvfp4":
-            gx = fql.global_scale_from_amax(fql.amax(x, hbk).item())
-            objs = [fql.NVFP4Weight(p, N, K, gx, w0.weight_global_scale, hbk) for p in copies]
+            T = tmat(hbk) if general else None
+            if general:  # calibration on the transformed activation (the library's amax kernel)
+                gx = fql.global_scale_from_amax(fql.quant_nvfp4_dynamic(x, T=T)[2][0].item())
+            else:
+                gx = fql.global_scale_from_amax(fql.amax(x, hbk).item())
+            objs = [fql.NVFP4Weight(p, N, K, gx, w0.weight_global_scale, 0 if general else hbk,
+                                    transform=T, dynamic_input_scale=dynamic) for p in copies]
         elif fmt == "fp8":
             sx = fql.fp8_scale_from_amax(fql.amax(x).item())
             objs = [fql.FP8Weight(p, N, K, w0.weight_scale, sx) for p in copies]
@@ -172,7 +191,7 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4"):
         ws = fql.new_workspace(wsb, dev)
         setups.append(dict(M=M, N=N, K=K, name=name, hb=hbk, x=x, objs=objs, bias=bias, y=y,
                            ws=ws, flops=2.0 * M * N * K, bytes=_alg_bytes(M, N, K, with_bias, fmt),
-                           kernel=_kernel_of(M, N, K, fmt)))
+                           kernel=_kernel_of(M, N, K, fmt, xhat_only=general or dynamic)))
     torch.cuda.synchronize()
     n = len(setups)
 
@@ -237,7 +256,8 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4"):
             b.synchronize()
             ms = a.elapsed_time(b) / (per_case_reps * R)
             per_case_ms.append(ms)
-            detail.append(dict(case=f"{s['name']}/M={s['M']}" + (f"/hb={s['hb']}" if s["hb"] else ""),
+            tag = "b" if general else "hb"
+            detail.append(dict(case=f"{s['name']}/M={s['M']}" + (f"/{tag}={s['hb']}" if s["hb"] else ""),
                                kernel=s["kernel"], us=round(ms * 1e3, 2),
                                tflops=round(s["flops"] / (ms * 1e-3) / 1e12, 2),
                                gbs=round(s["bytes"] / (ms * 1e-3) / 1e9, 1),
@@ -324,8 +344,12 @@ def cpu_baseline(workload, budget_s=12.0, n_rows=2048):
     `budget_s` seconds of oracle time have accumulated.
     """
     import oracle.nvfp4 as Q
+    import oracle.transform as TR
     import synthetic
+    from oracle.formats import bf16_bits_to_f64
     from oracle.hadamard import fwht_fp32
+
+    general = workload == "transform"
 
     try:
         from threadpoolctl import threadpool_info
@@ -344,16 +368,23 @@ def cpu_baseline(workload, budget_s=12.0, n_rows=2048):
             ns = min(N, n_rows)
             if (name, hb) not in wcache:
                 W = synthetic.weight(N, K, config=workload)[:ns]
-                Wr = fwht_fp32(W, hb) if hb else W
+                Wr = fwht_fp32(W, hb) if hb and not general else W
                 gw = Q.global_scale_from_amax(Q.amax_for_calibration(Wr))
                 wcache[(name, hb)] = (gw,) + Q.quant_nvfp4(Wr, gw)
             gw, wc, wsc = wcache[(name, hb)]
             Mr = min(M, 512)  # rows of x in the sample
             xb = synthetic.activations(synthetic.WORKLOADS[workload]["x"], Mr, K, config=workload)
             x = synthetic.bf16_bits_to_f32(xb)
-            gx = Q.global_scale_from_amax(Q.amax_for_calibration(x, hb))
+            if general:
+                T64 = bf16_bits_to_f64(synthetic.transform_matrix(hb))
+                gx = Q.global_scale_from_amax(TR.tensor_amax(TR.block_transform(x, T64)))
+            else:
+                gx = Q.global_scale_from_amax(Q.amax_for_calibration(x, hb))
             t0 = time.perf_counter()
-            xc, xs = Q.quant_nvfp4(x, gx, hb)
+            if general:
+                xc, xs = TR.quant_nvfp4_transform(x, T64, gx)
+            else:
+                xc, xs = Q.quant_nvfp4(x, gx, hb)
             Q.linear_nvfp4(xc, xs, wc, wsc, np.float32(1.0 / (float(gx) * float(gw))))
             t_total += time.perf_counter() - t0
             flops += 2.0 * Mr * ns * K
@@ -373,7 +404,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=WORKLOAD_KEYS)
     ap.add_argument("--format", default="nvfp4", choices=FORMAT_KEYS)
-    ap.add_argument("--hadamard-block", type=int, default=None)
+    ap.add_argument("--hadamard-block", type=int, default=None,
+                    help="restrict the hadamard/transform workloads to one block size")
+    ap.add_argument("--dynamic-scale", action="store_true",
+                    help="NVFP4: compute the activation global scale per call on the device")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--detail", action="store_true", help="print per-case timings to stderr")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -396,7 +430,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
         return
-    r = gpu_bench(args.workload, args.steps, args.warmup, args.hadamard_block, fmt=args.format)
+    if args.format != "nvfp4" and (args.dynamic_scale or args.workload == "transform"):
+        raise SystemExit("--dynamic-scale and the transform workload are NVFP4 options")
+    r = gpu_bench(args.workload, args.steps, args.warmup, args.hadamard_block, fmt=args.format,
+                  dynamic=args.dynamic_scale)
     value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
     dom_name, dom = r["dominant"]
     # binding bound of the dominant kernel: HBM bytes vs f16-MFMA flops (the exact
@@ -433,7 +470,9 @@ def main():
         "vs_baseline": None,
         "dtype": FORMAT_DTYPE[args.format],
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[args.workload], "cases": len(r["detail"]),
+        "config": {"workload": WORKLOAD_NAMES[args.workload]
+                   + (", dynamic activation global scale" if args.dynamic_scale else ""),
+                   "cases": len(r["detail"]),
                    "timing": "HIP graph replay per step, weights rotated over >= 512 MB"},
         "roofline": roof,
     }

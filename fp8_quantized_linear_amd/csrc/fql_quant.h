@@ -67,11 +67,11 @@ struct Loader<float> {
 
 // Rotate the thread's 16 values as part of its b-chunk (Sylvester H_b in
 // natural order, scaled by fl32(1/sqrt(b))): in-thread butterfly strides 1,
-// 2, 4, 8 (those below b), then cross-lane strides 16 .. b/2 with lane ^ 1,
-// ^ 2, ^ 4, then one multiply. `blk` is the block index within the row; the
-// b/16 blocks of a chunk must sit in adjacent lanes of one wave, in order.
-// Every lane of those groups must execute this call.
-template <int HB>
+// 2, 4, 8 (those below b), then cross-lane strides 16 .. b/2 with lane ^ LS,
+// ^ 2LS, ^ 4LS, then one multiply. `blk` is the block index within the row;
+// the b/16 blocks of a chunk must sit in lanes LS apart of one wave, in
+// order. Every lane of those groups must execute this call.
+template <int HB, int LS = 1>
 __device__ __forceinline__ void fwht_block(float v[16], int64_t blk) {
 #pragma clang fp contract(off)
 #pragma unroll
@@ -90,7 +90,7 @@ __device__ __forceinline__ void fwht_block(float v[16], int64_t blk) {
     const bool upper = (blk & hs) != 0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float other = __shfl_xor(v[e], hs);
+      float other = __shfl_xor(v[e], hs * LS);
       // lower lane holds a, upper lane holds b: lower gets a + b, upper a - b
       v[e] = upper ? (other - v[e]) : (v[e] + other);
     }

@@ -59,17 +59,26 @@ __global__ __launch_bounds__(256) void quant_nvfp4_canonical_kernel(
 // in float16, in the MFMA A-fragment order the GEMM reads (see gemm_nvfp4):
 //   [Mp/16][Kp/32][lane 0..63][8 halves], lane = kq*16 + (m%16), k = 32*ks + 8*kq + i.
 // Rows >= M and columns >= K are written as zeros.
+// Work mapping: a wave takes R rows x J = 64/R consecutive 16-blocks, lane =
+// r + R*j, so every 16-byte store of a block's halves lands next to the
+// same block's stores for the wave's other rows: R * 16 contiguous bytes
+// per store instruction group (a wave writes 2 * J runs of 16 * R bytes).
+// R = 16 (J = 4) unless the rotation needs 8 blocks per chunk (b = 128: R = 8).
 template <int HB>
 __global__ __launch_bounds__(256) void quant_nvfp4_xhat_kernel(
     const uint16_t* __restrict__ x, int M, int K, int64_t ldx, float g, int aligned16, int Mp,
     int Kp, _Float16* __restrict__ xhat, const float* __restrict__ g_dev) {
+  constexpr uint32_t R = HB == 128 ? 8u : 16u;
+  constexpr uint32_t J = 64u / R;
   // 32-bit index arithmetic: the launcher checks Mp * Kp / 16 < 2^31
-  const uint32_t nblk = (uint32_t)Kp / 16u;
-  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
-  if (i >= (uint32_t)Mp * nblk) return;  // whole waves only: Mp * nblk is a multiple of 64
-  if (g_dev != nullptr) g = *g_dev;      // per-call global scale computed on the device
-  const uint32_t m = i / nblk;
-  const uint32_t kb = i - m * nblk;
+  const uint32_t ncg = (uint32_t)Kp / (16u * J);    // block groups per row
+  const uint32_t w = blockIdx.x * 4u + (threadIdx.x >> 6);
+  if (w >= ((uint32_t)Mp / R) * ncg) return;         // whole waves only
+  if (g_dev != nullptr) g = *g_dev;                  // per-call global scale computed on the device
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t rg = w / ncg, cg = w - rg * ncg;
+  const uint32_t m = rg * R + lane % R;
+  const uint32_t kb = cg * J + lane / R;
   const bool real = (m < (uint32_t)M) && (kb * 16u < (uint32_t)K);
   float v[16];
   if (real) {
@@ -78,7 +87,7 @@ __global__ __launch_bounds__(256) void quant_nvfp4_xhat_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = 0.0f;
   }
-  if constexpr (HB > 0) fwht_block<HB>(v, kb);
+  if constexpr (HB > 0) fwht_block<HB, (int)R>(v, kb);
   uint32_t lo, hi, s;
   quant_block(v, g, lo, hi, s);
   const _Float16 sh = e4m3_to_f16(s);

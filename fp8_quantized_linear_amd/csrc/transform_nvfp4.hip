@@ -256,9 +256,9 @@ hipError_t launch_transform_nvfp4(const TransformArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
   const int mtiles = (int)((a.rows_out + 15) / 16);
   const int nchunks = (int)(a.K / a.b);
-  // about 2048 waves (8 per CU), each wave at least 4 chunks when there are enough
-  int cwc = (int)std::min<int64_t>(nchunks, std::max<int64_t>(1, (2048 + mtiles - 1) / mtiles));
-  if (nchunks >= 16) cwc = std::min(cwc, std::max(1, nchunks / 4));
+  // about 2048 waves (8 per CU); with few row tiles every wave takes a single
+  // chunk (the T fragments come from L2, so reloading them per wave is cheap)
+  const int cwc = (int)std::min<int64_t>(nchunks, std::max<int64_t>(1, (2048 + mtiles - 1) / mtiles));
   const int64_t waves = (int64_t)mtiles * cwc;
   if (waves >= ((int64_t)1 << 31) - 4) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((waves + 3) / 4));
