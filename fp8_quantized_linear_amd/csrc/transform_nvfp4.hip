@@ -95,8 +95,17 @@ __device__ __forceinline__ void load_frag(const uint16_t* p, bool valid, Frag<B>
   }
 }
 
+// Chunks in flight per wave (register ring): DEPTH - 1 chunks are loading
+// while one is computed. The T fragments take 128 VGPRs at b = 128, which
+// leaves room for a 3-deep ring at two waves per SIMD.
+template <int B>
+constexpr int ring_depth() { return B == 128 ? 3 : 4; }
+
 // One launch: waves = mtiles * cw_count; wave (mt, cw) takes chunks cw,
-// cw + cw_count, ... of its 16-row tile.
+// cw + cw_count, ... of its 16-row tile. Rows >= M are loaded from row M - 1
+// (in bounds) and masked at the output, so every load is unconditional and
+// the loop is wave-uniform: the compiler then waits for exactly the ring
+// slot a chunk needs.
 template <int B, int MODE, int AL>
 __global__ __launch_bounds__(256) void transform_quant_kernel(
     const uint16_t* __restrict__ x, int M, int K, int64_t ldx, const uint16_t* __restrict__ T,
@@ -105,8 +114,9 @@ __global__ __launch_bounds__(256) void transform_quant_kernel(
     int64_t ldv, uint32_t* __restrict__ amax) {
 #pragma clang fp contract(off)
   using S = TrShape<B>;
+  constexpr int D = ring_depth<B>();
   const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   if (wid >= mtiles * cw_count) return;  // whole waves only
   const int mt = wid / cw_count;
   const int cw = wid - mt * cw_count;
@@ -125,71 +135,75 @@ __global__ __launch_bounds__(256) void transform_quant_kernel(
       load_frag<B, 1>(T + (int64_t)(16 * it + ml) * B + S::KD * js + q * (S::KD / 4), true, ta[it][js]);
 
   const int nchunks = K / B;
-  const uint16_t* xrow = x + (int64_t)(row_ok ? m : 0) * ldx + q * (S::KD / 4);
+  const uint16_t* xrow = x + (int64_t)(row_ok ? m : M - 1) * ldx + q * (S::KD / 4);
   float wave_max = 0.0f;
 
-  Frag<B> xb[S::JS], xn[S::JS];
-  int c = cw;
-  if (c < nchunks) {
+  // ring slot n % D holds the chunk cw + n * cw_count (loads past the last
+  // chunk re-read the last one; they are never used)
+  Frag<B> xr[D][S::JS];
+  auto load_chunk = [&](int c, Frag<B>* dst) {
+    const int cc = c < nchunks ? c : nchunks - 1;
 #pragma unroll
-    for (int js = 0; js < S::JS; ++js) load_frag<B, AL>(xrow + (int64_t)c * B + S::KD * js, row_ok, xb[js]);
-  }
-  for (; c < nchunks; c += cw_count) {
-    const int cn = c + cw_count;
-    if (cn < nchunks) {  // next chunk's activation loads in flight during this chunk's work
+    for (int js = 0; js < S::JS; ++js) load_frag<B, AL>(xrow + (int64_t)cc * B + S::KD * js, true, dst[js]);
+  };
 #pragma unroll
-      for (int js = 0; js < S::JS; ++js) load_frag<B, AL>(xrow + (int64_t)cn * B + S::KD * js, row_ok, xn[js]);
-    }
+  for (int d = 0; d < D - 1; ++d) load_chunk(cw + d * cw_count, xr[d]);
+
+  for (int c = cw; c < nchunks;) {
 #pragma unroll
-    for (int it = 0; it < S::IT; ++it) {
-      float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int u = 0; u < D; ++u) {
+      if (c >= nchunks) break;
+      load_chunk(c + (D - 1) * cw_count, xr[(u + D - 1) % D]);
 #pragma unroll
-      for (int js = 0; js < S::JS; ++js) acc = mfma_step<B>(ta[it][js], xb[js], acc);
-      float v[4];
+      for (int it = 0; it < S::IT; ++it) {
+        float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = acc[r] + 0.0f;  // an exactly zero sum is +0
-      const int k0 = c * B + 16 * it + 4 * q;             // first of this lane's four elements
-      float a = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
-                                __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])));
-      if constexpr (MODE == TR_VALUES) {
-        if (row_ok) *reinterpret_cast<float4v*>(vout + (int64_t)m * ldv + k0) = float4v{v[0], v[1], v[2], v[3]};
-        continue;
-      }
-      if constexpr (MODE == TR_AMAX) {
-        wave_max = __builtin_fmaxf(wave_max, a);
-        continue;
-      }
-      // block maximum over the four lanes holding this row's 16 elements
-      a = __builtin_fmaxf(a, __shfl_xor(a, 16));
-      a = __builtin_fmaxf(a, __shfl_xor(a, 32));
-      const float sf = (a / 6.0f) * g;
-      const uint32_t s = e4m3_encode_nonneg(sf);
-      const float sd = e4m3_decode_nonneg(s);
-      const float rcp = sd == 0.0f ? 0.0f : g / sd;
-      uint32_t c16 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0] * rcp, v[1] * rcp, 1.0f, 0);
-      c16 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c16, v[2] * rcp, v[3] * rcp, 1.0f, 1);
-      if constexpr (MODE == TR_CANON) {
-        // gather the block's 8 code bytes into lane q == 0: words (q0 | q1 << 16), (q2 | q3 << 16)
-        const uint32_t mine = c16 & 0xFFFFu;
-        const uint32_t nb = __shfl_xor(mine, 16);
-        const uint32_t lo = (q & 1) == 0 ? (mine | (nb << 16)) : 0u;
-        const uint32_t hi = __shfl_xor(lo, 32);
-        if (q == 0 && row_ok) {
-          *reinterpret_cast<uint2v*>(codes + (int64_t)m * (K / 2) + (c * B + 16 * it) / 2) = uint2v{lo, hi};
-          scales[(int64_t)m * (K / 16) + c * (B / 16) + it] = (uint8_t)s;
+        for (int js = 0; js < S::JS; ++js) acc = mfma_step<B>(ta[it][js], xr[u][js], acc);
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = row_ok ? acc[r] + 0.0f : 0.0f;  // an exactly zero sum is +0
+        const int k0 = c * B + 16 * it + 4 * q;  // first of this lane's four elements
+        float a = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                                  __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])));
+        if constexpr (MODE == TR_VALUES) {
+          if (row_ok) *reinterpret_cast<float4v*>(vout + (int64_t)m * ldv + k0) = float4v{v[0], v[1], v[2], v[3]};
+          continue;
         }
-      } else {  // TR_XHAT: e2m1(q) * s_d in float16 (exact), GEMM A-fragment order
-        const _Float16 sh = (_Float16)sd;
-        const half2v s2 = {sh, sh};
-        const uint32_t h0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c16, 1.0f, 0) * s2);
-        const uint32_t h1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c16, 1.0f, 1) * s2);
-        const int ks = k0 >> 5, kq = (k0 >> 3) & 3, e0 = k0 & 7;
-        const int64_t idx = (((int64_t)mt * (Kp / 32) + ks) * 64 + kq * 16 + ml) * 8 + e0;
-        *reinterpret_cast<uint2v*>(xhat + idx) = uint2v{h0, h1};
+        if constexpr (MODE == TR_AMAX) {
+          wave_max = __builtin_fmaxf(wave_max, a);
+          continue;
+        }
+        // block maximum over the four lanes holding this row's 16 elements
+        a = __builtin_fmaxf(a, __shfl_xor(a, 16));
+        a = __builtin_fmaxf(a, __shfl_xor(a, 32));
+        const float sf = (a / 6.0f) * g;
+        const uint32_t s = e4m3_encode_nonneg(sf);
+        const float sd = e4m3_decode_nonneg(s);
+        const float rcp = sd == 0.0f ? 0.0f : g / sd;
+        uint32_t c16 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0] * rcp, v[1] * rcp, 1.0f, 0);
+        c16 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c16, v[2] * rcp, v[3] * rcp, 1.0f, 1);
+        if constexpr (MODE == TR_CANON) {
+          // gather the block's 8 code bytes into lane q == 0: words (q0 | q1 << 16), (q2 | q3 << 16)
+          const uint32_t mine = c16 & 0xFFFFu;
+          const uint32_t nb = __shfl_xor(mine, 16);
+          const uint32_t lo = (q & 1) == 0 ? (mine | (nb << 16)) : 0u;
+          const uint32_t hi = __shfl_xor(lo, 32);
+          if (q == 0 && row_ok) {
+            *reinterpret_cast<uint2v*>(codes + (int64_t)m * (K / 2) + (c * B + 16 * it) / 2) = uint2v{lo, hi};
+            scales[(int64_t)m * (K / 16) + c * (B / 16) + it] = (uint8_t)s;
+          }
+        } else {  // TR_XHAT: e2m1(q) * s_d in float16 (exact), GEMM A-fragment order
+          const _Float16 sh = (_Float16)sd;
+          const half2v s2 = {sh, sh};
+          const uint32_t h0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c16, 1.0f, 0) * s2);
+          const uint32_t h1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c16, 1.0f, 1) * s2);
+          const int ks = k0 >> 5, kq = (k0 >> 3) & 3, e0 = k0 & 7;
+          const int64_t idx = (((int64_t)mt * (Kp / 32) + ks) * 64 + kq * 16 + ml) * 8 + e0;
+          *reinterpret_cast<uint2v*>(xhat + idx) = uint2v{h0, h1};
+        }
       }
+      c += cw_count;
     }
-#pragma unroll
-    for (int js = 0; js < S::JS; ++js) xb[js] = xn[js];
   }
 
   if constexpr (MODE == TR_AMAX) {
@@ -256,9 +270,11 @@ hipError_t launch_transform_nvfp4(const TransformArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
   const int mtiles = (int)((a.rows_out + 15) / 16);
   const int nchunks = (int)(a.K / a.b);
-  // about 2048 waves (8 per CU); with few row tiles every wave takes a single
-  // chunk (the T fragments come from L2, so reloading them per wave is cheap)
-  const int cwc = (int)std::min<int64_t>(nchunks, std::max<int64_t>(1, (2048 + mtiles - 1) / mtiles));
+  // as many waves as the chip keeps resident (8 per SIMD, 2 at b = 128 where T
+  // takes 128 registers); with few row tiles every wave takes a single chunk
+  // (the T fragments come from L2, so reloading them per wave is cheap)
+  const int64_t target = a.b == 128 ? 2048 : 8192;
+  const int cwc = (int)std::min<int64_t>(nchunks, std::max<int64_t>(1, (target + mtiles - 1) / mtiles));
   const int64_t waves = (int64_t)mtiles * cwc;
   if (waves >= ((int64_t)1 << 31) - 4) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((waves + 3) / 4));
