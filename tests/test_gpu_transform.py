@@ -357,3 +357,52 @@ def test_graph_replay(mode):
         assert torch.equal(y.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
         fql.linear_nvfp4(other, w, workspace=ws)  # eager call on the same workspace in between
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("K,b,M", [(208, 16, 1), (208, 16, 40), (96, 32, 17), (64, 64, 3),
+                                   (128, 128, 1), (384, 128, 33)])
+def test_linear_transform_ragged_k(K, b, M):
+    # K not a multiple of 128 (x_hat columns K..Kp are zero padded; K = 208 leaves
+    # half of a 32-column step), a single chunk (K = b), and ragged row counts
+    N = 80
+    xb = _x(M, K, seed=K + M)
+    Tb = _T_bits(b, "gaussian", seed=7)
+    x32 = synthetic.bf16_bits_to_f32(xb)
+    T64 = F.bf16_bits_to_f64(Tb)
+    W = synthetic.weight(N, K, config="transform", seed=1)
+    gw = Q.global_scale_from_amax(Q.amax_for_calibration(W))
+    wc, ws = Q.quant_nvfp4(W, gw)
+    gx = Q.global_scale_from_amax(TR.tensor_amax(TR.block_transform(x32, T64)))
+    xc, xs = TR.quant_nvfp4_transform(x32, T64, gx)
+    ref = Q.linear_nvfp4(xc, xs, wc, ws, alpha_of(gx, gw))
+    Td = _T_dev(Tb)
+    xd = bf16_bits_to_dev(xb)
+    announce(f"linear transform ragged K={K} b={b} M={M}")
+    codes, scales = fql.quant_nvfp4_transform(xd, Td, float(gx))
+    w = fql.NVFP4Weight.from_float(f32_to_dev(W), float(gx), weight_global_scale=float(gw), transform=Td)
+    y = fql.linear_nvfp4(xd, w)
+    wd = fql.NVFP4Weight.from_float(f32_to_dev(W), 1.0, weight_global_scale=float(gw), transform=Td,
+                                    dynamic_input_scale=True)
+    yd = fql.linear_nvfp4(xd, wd)
+    torch.cuda.synchronize()
+    _check_rule(x32, T64, gx, codes.cpu().numpy(), scales.cpu().numpy(), f"ragged K={K} b={b} M={M}")
+    assert rel_frob(dev_bf16_to_bits(y), ref) <= REL_FROB_TOL
+    gxd = TR.dynamic_global_scale(TR.tensor_amax(TR.block_transform(x32, T64)))
+    xcd, xsd = TR.quant_nvfp4_transform(x32, T64, gxd)
+    refd = Q.linear_nvfp4(xcd, xsd, wc, ws, TR.dynamic_alpha(gxd, gw))
+    assert rel_frob(dev_bf16_to_bits(yd), refd) <= REL_FROB_TOL
+
+
+def test_transform_values_3d_input_and_row_stride():
+    # [B, S, K] input flattened without a copy, and a padded row stride for the values
+    b, K = 32, 256
+    xb = _x(6, K, seed=30)
+    Tb = _T_bits(b, seed=8)
+    x3 = bf16_bits_to_dev(xb).view(2, 3, K)
+    announce("transform values 3-d")
+    v = fql.transform_bf16(x3, _T_dev(Tb))
+    torch.cuda.synchronize()
+    assert v.shape == (2, 3, K)
+    x32 = synthetic.bf16_bits_to_f32(xb)
+    v64, err = _bound(x32, F.bf16_bits_to_f64(Tb))
+    assert np.all(np.abs(v.reshape(6, K).cpu().numpy().astype(np.float64) - v64) <= err)
