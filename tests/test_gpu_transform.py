@@ -406,3 +406,68 @@ def test_transform_values_3d_input_and_row_stride():
     x32 = synthetic.bf16_bits_to_f32(xb)
     v64, err = _bound(x32, F.bf16_bits_to_f64(Tb))
     assert np.all(np.abs(v.reshape(6, K).cpu().numpy().astype(np.float64) - v64) <= err)
+
+
+@pytest.mark.parametrize("b", [16, 128])
+@pytest.mark.parametrize("shape", ["gate_up", "down"])
+@pytest.mark.parametrize("M", [1, 256, 4096])
+def test_linear_transform_full_size_sampled(b, shape, M):
+    # the general-transform workload at its full sizes (Qwen3-32B gate_up /
+    # down), the launch configuration the bench times; the oracle computes a
+    # seeded sample of rows and columns in full
+    from gpu_helpers import cached_activations, cached_weight
+
+    K, N = synthetic.QWEN_SHAPES[shape]
+    r = np.random.default_rng(b + M + K)
+    rows = np.arange(M) if M == 1 else np.sort(r.choice(M, 24, replace=False))
+    cols = np.sort(r.choice(N, 48, replace=False))
+    cols[-1] = N - 1
+    xb = cached_activations("student_t3", M, K, "transform")
+    Tb = _T_bits(b)
+    T64 = F.bf16_bits_to_f64(Tb)
+    x32s = synthetic.bf16_bits_to_f32(xb[rows])
+    W = cached_weight("transform", N, K)
+    gw = Q.global_scale_from_amax(Q.amax_for_calibration(W[cols]))
+    wc, ws = Q.quant_nvfp4(W[cols], gw)
+    gx = Q.global_scale_from_amax(TR.tensor_amax(TR.block_transform(x32s, T64)))
+    xc, xs = TR.quant_nvfp4_transform(x32s, T64, gx)
+    ref = Q.linear_nvfp4(xc, xs, wc, ws, alpha_of(gx, gw))
+    announce(f"linear transform full size {shape} M={M} b={b} plan={fql.linear_plan(M, N, K, aligned=False)}")
+    w = fql.NVFP4Weight.from_float(f32_to_dev(W), float(gx), weight_global_scale=float(gw),
+                                   transform=_T_dev(Tb))
+    y = fql.linear_nvfp4(bf16_bits_to_dev(xb), w)
+    torch.cuda.synchronize()
+    got = dev_bf16_to_bits(y)[np.ix_(rows, cols)]
+    err = rel_frob(got, ref)
+    assert err <= REL_FROB_TOL, err
+
+
+def test_linear_dynamic_full_size_sampled():
+    # dynamic scale over the whole 4096 x 25600 transformed activation
+    from gpu_helpers import cached_activations, cached_weight
+
+    M, b = 4096, 128
+    K, N = synthetic.QWEN_SHAPES["down"]
+    r = np.random.default_rng(7)
+    rows = np.sort(r.choice(M, 24, replace=False))
+    cols = np.sort(r.choice(N, 48, replace=False))
+    xb = cached_activations("student_t3", M, K, "transform")
+    Tb = _T_bits(b)
+    T64 = F.bf16_bits_to_f64(Tb)
+    x32 = synthetic.bf16_bits_to_f32(xb)
+    amax = np.float32(0)
+    for r0 in range(0, M, 512):  # the tensor amax in row blocks (bounded host memory)
+        amax = max(amax, TR.tensor_amax(TR.block_transform(x32[r0:r0 + 512], T64)))
+    gx = TR.dynamic_global_scale(amax)
+    W = cached_weight("transform", N, K)
+    gw = Q.global_scale_from_amax(Q.amax_for_calibration(W[cols]))
+    wc, ws = Q.quant_nvfp4(W[cols], gw)
+    xc, xs = TR.quant_nvfp4_transform(x32[rows], T64, gx)
+    ref = Q.linear_nvfp4(xc, xs, wc, ws, TR.dynamic_alpha(gx, gw))
+    announce("linear dynamic full size down M=4096 b=128")
+    w = fql.NVFP4Weight.from_float(f32_to_dev(W), 1.0, weight_global_scale=float(gw),
+                                   transform=_T_dev(Tb), dynamic_input_scale=True)
+    y = fql.linear_nvfp4(bf16_bits_to_dev(xb), w)
+    torch.cuda.synchronize()
+    err = rel_frob(dev_bf16_to_bits(y)[np.ix_(rows, cols)], ref)
+    assert err <= REL_FROB_TOL, err
