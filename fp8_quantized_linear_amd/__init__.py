@@ -501,10 +501,13 @@ def quant_nvfp4_transform(x, T, global_scale, codes=None, scales=None):
     return codes, scales
 
 
+DYNAMIC_SCALARS = 68  # FQL_DYNAMIC_SCALARS: 64 partial maxima, amax, g
+
+
 def quant_nvfp4_dynamic(x, T=None, hadamard_block=0):
     """NVFP4-quantize x with g = 448 * 6 / amax computed on the device from this
     activation (after the transform T, or the Hadamard rotation, if any).
-    Returns (codes, scales, scalars): scalars float32 [4] on the device,
+    Returns (codes, scales, scalars): scalars float32 [2] on the device,
     [0] = amax, [1] = g."""
     _require_cuda(x, "x")
     if x.dtype != torch.bfloat16:
@@ -515,10 +518,10 @@ def quant_nvfp4_dynamic(x, T=None, hadamard_block=0):
     lead = tuple(x.shape[:-1])
     codes = torch.empty(lead + (K // 2,), dtype=torch.uint8, device=x.device)
     scales = torch.empty(lead + (K // 16,), dtype=torch.uint8, device=x.device)
-    scalars = torch.empty(4, dtype=torch.float32, device=x.device)
-    _check(lib().fql_quant_nvfp4_dynamic(_ptr(x2), M, K, ld, _ptr(T), b, _ptr(scalars), _ptr(codes),
+    buf = torch.empty(DYNAMIC_SCALARS, dtype=torch.float32, device=x.device)
+    _check(lib().fql_quant_nvfp4_dynamic(_ptr(x2), M, K, ld, _ptr(T), b, _ptr(buf), _ptr(codes),
                                          _ptr(scales), _stream(x.device)))
-    return codes, scales, scalars
+    return codes, scales, buf[64:66]
 
 
 # ---------------------------------------------------------------------------

@@ -269,11 +269,12 @@ int check_transform(const void* T, int b, int64_t K) {
   return FQL_OK;
 }
 
-// amax of the (optionally transformed or rotated) activation into amax_slot,
-// then g (and alpha when g_w > 0) on the device.
+// amax of the (optionally transformed or rotated) activation into the
+// partial-maximum slots of scal, then amax, g (and alpha when with_alpha) on
+// the device (layout: fql::kAmaxSlots partial maxima, amax, g, alpha).
 hipError_t launch_dynamic_prologue(const void* x, int64_t M, int64_t K, int64_t ldx,
-                                   const void* T, int b, uint32_t* amax_slot, float g_w,
-                                   float* g_out, float* alpha_out, hipStream_t st) {
+                                   const void* T, int b, float* scal, float g_w, bool with_alpha,
+                                   hipStream_t st) {
   hipError_t e;
   if (T) {
     fql::TransformArgs a{};
@@ -281,14 +282,14 @@ hipError_t launch_dynamic_prologue(const void* x, int64_t M, int64_t K, int64_t 
     a.x = static_cast<const uint16_t*>(x); a.M = M; a.K = K; a.ldx = ldx;
     a.aligned = fql::transform_aligned(x, ldx, b);
     a.T = static_cast<const uint16_t*>(T); a.b = b;
-    a.rows_out = M; a.amax = amax_slot;
+    a.rows_out = M; a.amax = reinterpret_cast<uint32_t*>(scal);
     e = fql::launch_transform_nvfp4(a, st);
   } else {
     e = fql::launch_amax_bf16(static_cast<const uint16_t*>(x), M, K, ldx, b, aligned16(x, ldx, 2),
-                              reinterpret_cast<float*>(amax_slot), st);
+                              scal, st, fql::kAmaxSlots);
   }
   if (e != hipSuccess) return e;
-  return fql::launch_dynamic_scale(amax_slot, g_w, g_out, alpha_out, st);
+  return fql::launch_dynamic_scale(scal, g_w, with_alpha, st);
 }
 
 }  // namespace
@@ -337,21 +338,22 @@ int fql_quant_nvfp4_dynamic(const void* x, int64_t M, int64_t K, int64_t ldx, co
   if (!x || !codes || !scales || !scalars) return fail(FQL_ERR_INVALID, "null pointer");
   if (reinterpret_cast<uintptr_t>(codes) % 8 != 0 || reinterpret_cast<uintptr_t>(scalars) % 4 != 0)
     return fail(FQL_ERR_INVALID, "codes must be 8-byte and scalars 4-byte aligned");
+  static_assert(FQL_DYNAMIC_SCALARS >= fql::kDynScalarWords, "scalar buffer size");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  uint32_t* amax_slot = reinterpret_cast<uint32_t*>(scalars);
-  hipError_t e = launch_dynamic_prologue(x, M, K, ldx, T, b, amax_slot, 0.0f, scalars + 1, nullptr, st);
+  float* g_dev = scalars + fql::kAmaxSlots + 1;
+  hipError_t e = launch_dynamic_prologue(x, M, K, ldx, T, b, scalars, 0.0f, false, st);
   if (e != hipSuccess) return hip_status(e, "dynamic scale launch");
   if (T) {
     fql::TransformArgs a{};
     a.mode = 0;
     a.x = static_cast<const uint16_t*>(x); a.M = M; a.K = K; a.ldx = ldx;
     a.aligned = fql::transform_aligned(x, ldx, b);
-    a.T = static_cast<const uint16_t*>(T); a.b = b; a.g = 1.0f; a.g_dev = scalars + 1;
+    a.T = static_cast<const uint16_t*>(T); a.b = b; a.g = 1.0f; a.g_dev = g_dev;
     a.codes = codes; a.scales = scales; a.rows_out = M;
     e = fql::launch_transform_nvfp4(a, st);
   } else {
     e = fql::launch_quant_nvfp4_bf16(static_cast<const uint16_t*>(x), M, K, ldx, 1.0f, b,
-                                     aligned16(x, ldx, 2), codes, scales, st, scalars + 1);
+                                     aligned16(x, ldx, 2), codes, scales, st, g_dev);
   }
   return hip_status(e, "dynamic quant launch");
 }
@@ -392,11 +394,11 @@ int linear_nvfp4_extras(const void* x, int64_t M, int64_t K, int64_t ldx, float 
   ex.T = static_cast<const uint16_t*>(T);
   ex.t_aligned = T ? fql::transform_aligned(x, ldx, b) : false;
   if (dynamic) {
-    hipError_t e = launch_dynamic_prologue(x, M, K, ldx, T, b, reinterpret_cast<uint32_t*>(scal), g_w,
-                                           scal + 1, scal + 2, st);
+    static_assert(fql::kDynScalarWords * 4 <= fql::kWorkspaceScalarBytes, "workspace scalar region");
+    hipError_t e = launch_dynamic_prologue(x, M, K, ldx, T, b, scal, g_w, true, st);
     if (e != hipSuccess) return hip_status(e, "dynamic scale launch");
-    ex.g_dev = scal + 1;
-    ex.alpha_dev = scal + 2;
+    ex.g_dev = scal + fql::kAmaxSlots + 1;
+    ex.alpha_dev = scal + fql::kAmaxSlots + 2;
     g = 1.0f;
     alpha = 1.0f;
   }

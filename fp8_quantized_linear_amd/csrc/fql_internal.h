@@ -44,8 +44,9 @@ hipError_t launch_quant_nvfp4_f32(const float* w, int64_t N, int64_t K, int64_t 
 hipError_t launch_quant_nvfp4_xhat(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
                                    int hb, bool aligned, int64_t Mp, int64_t Kp, _Float16* xhat,
                                    const float* g_dev, hipStream_t st);
+// max |v| into out (one float, or nslots partial maxima that launch_dynamic_scale folds)
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int hb,
-                            bool aligned, float* out, hipStream_t st);
+                            bool aligned, float* out, hipStream_t st, int nslots = 1);
 hipError_t launch_amax_f32(const float* w, int64_t N, int64_t K, int64_t ldw, int hb, bool aligned,
                            float* out, hipStream_t st);
 
@@ -100,18 +101,21 @@ bool gemv_ring_config_built(int w, int mt, int nt, int d);
 std::string describe_plan(const GemmPlan& p);
 
 // ---- general block-diagonal transform + dynamic global scale ---------------
-// Workspace of the NVFP4 linear call: the first kWorkspaceCounterBytes hold
-// split-K arrival counters, except the last kWorkspaceScalarBytes, which hold
-// the per-call device scalars of the dynamic-scale path:
-//   word 0 tensor amax (float bits), word 1 g_x, word 2 alpha.
+// Device scalars of the dynamic-scale path (float words):
+//   [0, kAmaxSlots)  partial maxima (uint bits), one per group of workgroups
+//   kAmaxSlots       the tensor amax, then g_x, then alpha.
+// The linear call keeps them in the last kWorkspaceScalarBytes of the
+// workspace's kWorkspaceCounterBytes of split-K arrival counters.
+constexpr int kAmaxSlots = 64;
+constexpr int kDynScalarWords = kAmaxSlots + 3;
 constexpr int64_t kWorkspaceCounterBytes = 64 * 1024;
-constexpr int64_t kWorkspaceScalarBytes = 256;
+constexpr int64_t kWorkspaceScalarBytes = 512;
 constexpr int64_t kWorkspaceScalarOffset = kWorkspaceCounterBytes - kWorkspaceScalarBytes;
 
 // One launch of the transform kernel. mode 0: canonical codes [M][K/2] and
 // scales [M][K/16]; 1: x_hat (float16, GEMM A-fragment order, rows_out = Mp
-// rows and Kp columns, zero padded); 2: max |v| into *amax (zeroed first);
-// 3: float32 values v [M][ldv].
+// rows and Kp columns, zero padded); 2: max |v| into the kAmaxSlots partial
+// maxima at amax (zeroed first); 3: float32 values v [M][ldv].
 struct TransformArgs {
   int mode;
   const uint16_t* x;
@@ -131,10 +135,10 @@ struct TransformArgs {
 };
 bool transform_aligned(const void* x, int64_t ldx, int b);
 hipError_t launch_transform_nvfp4(const TransformArgs& a, hipStream_t st);
-// g = fl32(2688 / amax) (1 when amax = 0, at most 2^118) into *g_out;
-// alpha = fl32((1/g) * (1/g_w)) into *alpha_out when it is non-null.
-hipError_t launch_dynamic_scale(const uint32_t* amax_bits, float g_w, float* g_out,
-                                float* alpha_out, hipStream_t st);
+// scal[kAmaxSlots] = max of the partial maxima, scal[kAmaxSlots + 1] =
+// g = fl32(2688 / amax) (1 when amax = 0, at most 2^118), and, when
+// with_alpha, scal[kAmaxSlots + 2] = alpha = fl32((1/g) * (1/g_w)).
+hipError_t launch_dynamic_scale(float* scal, float g_w, bool with_alpha, hipStream_t st);
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st);
 
 // Optional parts of a linear call: a general transform T (b = hb) in place

@@ -103,14 +103,16 @@ __global__ __launch_bounds__(256) void quant_nvfp4_xhat_kernel(
   base[(kq0 + 1u) * 16u + ml] = uint4v{hw[4], hw[5], hw[6], hw[7]};
 }
 
-// max |v| (after the optional rotation) into *amax (as ordered uint bits;
-// non-negative floats compare like their bit patterns). *amax must be 0 first.
+// max |v| (after the optional rotation) into amax[0 .. nslots) (as ordered
+// uint bits; non-negative floats compare like their bit patterns): workgroup w
+// folds its maximum into slot w % nslots, so the atomics of many workgroups
+// spread over several addresses. The slots must be 0 first.
 // Grid-stride over 16-blocks (the stride is a multiple of 64, so the lanes of
 // a Hadamard chunk stay adjacent in one wave); one atomic per workgroup.
 template <typename TIn, int HB>
 __global__ __launch_bounds__(256) void amax_kernel(const TIn* __restrict__ x, int64_t rows,
                                                    int64_t K, int64_t ldx, int aligned16,
-                                                   uint32_t* __restrict__ amax) {
+                                                   uint32_t* __restrict__ amax, int nslots) {
   __shared__ float wmax[4];
   const int64_t nblk = K / 16;
   const int64_t total = rows * nblk;
@@ -137,11 +139,13 @@ __global__ __launch_bounds__(256) void amax_kernel(const TIn* __restrict__ x, in
   __syncthreads();
   if (threadIdx.x == 0) {
     const float b = __builtin_fmaxf(__builtin_fmaxf(wmax[0], wmax[1]), __builtin_fmaxf(wmax[2], wmax[3]));
-    atomicMax(amax, __float_as_uint(b));
+    atomicMax(amax + blockIdx.x % nslots, __float_as_uint(b));
   }
 }
 
-__global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
+__global__ void zero_u32_kernel(uint32_t* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
 
 // ---------------------------------------------------------------------------
 // launchers
@@ -198,31 +202,32 @@ hipError_t launch_quant_nvfp4_xhat(const uint16_t* x, int64_t M, int64_t K, int6
 
 template <typename TIn>
 static hipError_t launch_amax(const TIn* x, int64_t rows, int64_t K, int64_t ldx, int hb,
-                              bool aligned, float* out, hipStream_t st) {
+                              bool aligned, float* out, int nslots, hipStream_t st) {
+  if (nslots < 1 || nslots > 64) return hipErrorInvalidValue;
   uint32_t* o = reinterpret_cast<uint32_t*>(out);
-  zero_u32_kernel<<<1, 1, 0, st>>>(o);
+  zero_u32_kernel<<<1, 64, 0, st>>>(o, nslots);
   const int64_t total = rows * (K / 16);
   const dim3 grid((unsigned)std::min<int64_t>((total + 255) / 256, 2048)), block(256);
   const int al = aligned ? 1 : 0;
   switch (hb) {
-    case 0: amax_kernel<TIn, 0><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o); break;
-    case 16: amax_kernel<TIn, 16><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o); break;
-    case 32: amax_kernel<TIn, 32><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o); break;
-    case 64: amax_kernel<TIn, 64><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o); break;
-    case 128: amax_kernel<TIn, 128><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o); break;
+    case 0: amax_kernel<TIn, 0><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o, nslots); break;
+    case 16: amax_kernel<TIn, 16><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o, nslots); break;
+    case 32: amax_kernel<TIn, 32><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o, nslots); break;
+    case 64: amax_kernel<TIn, 64><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o, nslots); break;
+    case 128: amax_kernel<TIn, 128><<<grid, block, 0, st>>>(x, rows, K, ldx, al, o, nslots); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int hb,
-                            bool aligned, float* out, hipStream_t st) {
-  return launch_amax<uint16_t>(x, M, K, ldx, hb, aligned, out, st);
+                            bool aligned, float* out, hipStream_t st, int nslots) {
+  return launch_amax<uint16_t>(x, M, K, ldx, hb, aligned, out, nslots, st);
 }
 
 hipError_t launch_amax_f32(const float* w, int64_t N, int64_t K, int64_t ldw, int hb, bool aligned,
                            float* out, hipStream_t st) {
-  return launch_amax<float>(w, N, K, ldw, hb, aligned, out, st);
+  return launch_amax<float>(w, N, K, ldw, hb, aligned, out, 1, st);
 }
 
 }  // namespace fql

@@ -117,7 +117,10 @@ __global__ __launch_bounds__(256) void transform_quant_kernel(
   constexpr int D = ring_depth<B>();
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
-  if (wid >= mtiles * cw_count) return;  // whole waves only
+  // whole waves only; in the amax mode the surplus waves of the last workgroup
+  // stay for its barrier (their maximum is not read)
+  if (MODE != TR_AMAX && wid >= mtiles * cw_count) return;
+  const bool wave_live = wid < mtiles * cw_count;
   const int mt = wid / cw_count;
   const int cw = wid - mt * cw_count;
   const int ml = lane & 15;   // activation row within the tile (D column)
@@ -146,10 +149,12 @@ __global__ __launch_bounds__(256) void transform_quant_kernel(
 #pragma unroll
     for (int js = 0; js < S::JS; ++js) load_frag<B, AL>(xrow + (int64_t)cc * B + S::KD * js, true, dst[js]);
   };
+  if (wave_live) {
 #pragma unroll
-  for (int d = 0; d < D - 1; ++d) load_chunk(cw + d * cw_count, xr[d]);
+    for (int d = 0; d < D - 1; ++d) load_chunk(cw + d * cw_count, xr[d]);
+  }
 
-  for (int c = cw; c < nchunks;) {
+  for (int c = wave_live ? cw : nchunks; c < nchunks;) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       if (c >= nchunks) break;
@@ -208,11 +213,21 @@ __global__ __launch_bounds__(256) void transform_quant_kernel(
 
   if constexpr (MODE == TR_AMAX) {
     for (int off = 32; off > 0; off >>= 1) wave_max = __builtin_fmaxf(wave_max, __shfl_xor(wave_max, off));
-    if (lane == 0) atomicMax(amax, __float_as_uint(wave_max));  // non-negative floats order like their bits
+    // one atomic per workgroup, spread over kAmaxSlots addresses (non-negative
+    // floats order like their bits)
+    __shared__ float wg_max[4];
+    if (lane == 0) wg_max[threadIdx.x >> 6] = wave_max;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float b = wg_max[0];
+      const int nw = min(4, mtiles * cw_count - (int)blockIdx.x * 4);  // waves of this workgroup
+      for (int w = 1; w < nw; ++w) b = __builtin_fmaxf(b, wg_max[w]);
+      atomicMax(amax + blockIdx.x % kAmaxSlots, __float_as_uint(b));
+    }
   }
   if constexpr (MODE == TR_XHAT) {
     // columns K .. Kp of the tile are zero (8 halves per lane per step)
-    if (cw == 0) {
+    if (wave_live && cw == 0) {
       for (int k8 = K / 8 + q; k8 < Kp / 8; k8 += 4) {
         const int64_t idx = ((int64_t)mt * (Kp / 32) + (k8 >> 2)) * 64 + (k8 & 3) * 16 + ml;
         reinterpret_cast<uint4v*>(xhat)[idx] = uint4v{0u, 0u, 0u, 0u};
@@ -225,17 +240,20 @@ __global__ void zero_words_kernel(uint32_t* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
 }
 
-// D2/D3 on the device: g = fl32(2688 / amax) (1 when amax = 0, at most 2^118),
+// D1-D3 on the device (one wave): amax = max of the kAmaxSlots partial
+// maxima, g = fl32(2688 / amax) (1 when amax = 0, at most 2^118),
 // alpha = fl32((1 / g) * (1 / g_w)) in float64.
-__global__ void dynamic_scale_kernel(const uint32_t* __restrict__ amax_bits, float g_w,
-                                     float* __restrict__ g_out, float* __restrict__ alpha_out) {
+__global__ void dynamic_scale_kernel(float* __restrict__ scal, float g_w, int with_alpha) {
 #pragma clang fp contract(off)
-  if (threadIdx.x != 0) return;
-  const float a = __uint_as_float(*amax_bits);
+  const int lane = threadIdx.x;
+  float a = __uint_as_float(reinterpret_cast<const uint32_t*>(scal)[lane]);
+  for (int off = 32; off > 0; off >>= 1) a = __builtin_fmaxf(a, __shfl_xor(a, off));
+  if (lane != 0) return;
   float g = 1.0f;
   if (a > 0.0f) g = __builtin_fminf(2688.0f / a, 0x1p118f);
-  *g_out = g;
-  if (alpha_out != nullptr) *alpha_out = (float)((1.0 / (double)g) * (1.0 / (double)g_w));
+  scal[kAmaxSlots] = a;
+  scal[kAmaxSlots + 1] = g;
+  if (with_alpha) scal[kAmaxSlots + 2] = (float)((1.0 / (double)g) * (1.0 / (double)g_w));
 }
 
 template <int MODE, int AL>
@@ -280,7 +298,7 @@ hipError_t launch_transform_nvfp4(const TransformArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((waves + 3) / 4));
   const int M = (int)a.M, K = (int)a.K, Kp = (int)a.Kp;
   if (a.mode == TR_AMAX) {
-    zero_words_kernel<<<1, 64, 0, st>>>(a.amax, 1);
+    zero_words_kernel<<<1, 64, 0, st>>>(a.amax, kAmaxSlots);
   }
 #define FQL_TRM(MODE)                                                                              \
   return a.aligned ? launch_tr_mode<MODE, 1>(a.b, grid, st, a.x, M, K, a.ldx, a.T, a.g, a.g_dev,  \
@@ -299,9 +317,9 @@ hipError_t launch_transform_nvfp4(const TransformArgs& a, hipStream_t st) {
 #undef FQL_TRM
 }
 
-hipError_t launch_dynamic_scale(const uint32_t* amax_bits, float g_w, float* g_out,
-                                float* alpha_out, hipStream_t st) {
-  dynamic_scale_kernel<<<1, 64, 0, st>>>(amax_bits, g_w, g_out, alpha_out);
+hipError_t launch_dynamic_scale(float* scal, float g_w, bool with_alpha, hipStream_t st) {
+  static_assert(kAmaxSlots == 64, "one wave folds the partial maxima");
+  dynamic_scale_kernel<<<1, 64, 0, st>>>(scal, g_w, with_alpha ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -212,9 +212,11 @@ int fql_quant_nvfp4_transform(const void* x, int64_t M, int64_t K, int64_t ldx,
 
 /* NVFP4 quantize with the dynamic global scale. T may be NULL: then b is a
  * Hadamard block (0 = no rotation) as in fql_quant_nvfp4. scalars: device
- * float32 [2] (4-byte aligned) receiving [0] = amax, [1] = g; later calls
- * may overwrite it, so read it before reusing the buffer. Four kernels on
- * the stream (amax, scale, quantize). */
+ * float32 [FQL_DYNAMIC_SCALARS] (4-byte aligned); words 0..63 are partial
+ * maxima (scratch), word 64 receives amax and word 65 g. Four kernels on the
+ * stream (clear, amax, scale, quantize); a call on the same buffer before
+ * the previous one has finished races. */
+#define FQL_DYNAMIC_SCALARS 68
 int fql_quant_nvfp4_dynamic(const void* x, int64_t M, int64_t K, int64_t ldx, const void* T, int b,
                             float* scalars, uint8_t* codes, uint8_t* scales, void* stream);
 
