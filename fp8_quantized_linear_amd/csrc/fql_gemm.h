@@ -36,17 +36,21 @@ __device__ __forceinline__ uint32_t dword_of(const uint4v& v, int i) {
 // device coherence point. Waiting for the stores to complete before the
 // arrival increment orders them without any whole-cache write-back or
 // invalidate. Each lane moves its accumulator fragment as two 8-byte words.
-__device__ __forceinline__ void store_partial(float4v* p, const float4v& v) {
-  uint64_t* q = reinterpret_cast<uint64_t*>(p);
-  __hip_atomic_store(q, __builtin_bit_cast(uint64_t, float2v{v[0], v[1]}), __ATOMIC_RELAXED,
+__device__ __forceinline__ void store_partial(float4v* frag, int lane, const float4v& v) {
+  // A fragment's 64 float4 are stored as two 512-byte halves (words 0-1 of
+  // every lane, then words 2-3), so each 8-byte store instruction writes whole
+  // cache lines; interleaving the halves per lane would fill every other 8
+  // bytes of the fragment and write each line to HBM twice.
+  uint64_t* q = reinterpret_cast<uint64_t*>(frag);
+  __hip_atomic_store(q + lane, __builtin_bit_cast(uint64_t, float2v{v[0], v[1]}), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, __builtin_bit_cast(uint64_t, float2v{v[2], v[3]}), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 64 + lane, __builtin_bit_cast(uint64_t, float2v{v[2], v[3]}),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float4v load_partial(const float4v* p) {
-  uint64_t* q = const_cast<uint64_t*>(reinterpret_cast<const uint64_t*>(p));
-  const float2v a = __builtin_bit_cast(float2v, __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  const float2v b = __builtin_bit_cast(float2v, __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+__device__ __forceinline__ float4v load_partial(const float4v* frag, int lane) {
+  uint64_t* q = const_cast<uint64_t*>(reinterpret_cast<const uint64_t*>(frag));
+  const float2v a = __builtin_bit_cast(float2v, __hip_atomic_load(q + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const float2v b = __builtin_bit_cast(float2v, __hip_atomic_load(q + 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   return float4v{a[0], a[1], b[0], b[1]};
 }
 
@@ -79,10 +83,10 @@ __device__ __forceinline__ void finish_frags(float4v (&frag)[FR], RowOf row_of, 
     for (int f = 0; f < FR; ++f) emit(f, frag[f]);
     return;
   }
-  float4v* mine = slab + wave * FR * 64 + lane;
+  float4v* mine = slab + wave * FR * 64;  // this wave's fragments (64 float4 each)
   const int64_t zstride = (int64_t)NW * FR * 64;
 #pragma unroll
-  for (int f = 0; f < FR; ++f) store_partial(mine + split * zstride + f * 64, frag[f]);
+  for (int f = 0; f < FR; ++f) store_partial(mine + split * zstride + f * 64, lane, frag[f]);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");  // partial stores have completed
   __syncthreads();
   if (tid == 0) {
@@ -108,7 +112,7 @@ __device__ __forceinline__ void finish_frags(float4v (&frag)[FR], RowOf row_of, 
       for (int j = 0; j < ZB; ++j) {
         const int z = z0 + j < splits ? z0 + j : splits - 1;
 #pragma unroll
-        for (int f = 0; f < FG; ++f) v[j][f] = load_partial(mine + z * zstride + (f0 + f) * 64);
+        for (int f = 0; f < FG; ++f) v[j][f] = load_partial(mine + z * zstride + (f0 + f) * 64, lane);
       }
 #pragma unroll
       for (int j = 0; j < ZB; ++j)
