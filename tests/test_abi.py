@@ -175,3 +175,20 @@ def test_fp8_family_invalid_arguments_rejected():
     assert lib.fql_linear_mxfp8(p, 1, 64, 64, p, 64, 1.0, null, p, 64, p, 16, null) == -4
     assert lib.fql_linear_mxfp8(p, 1, 64, 64, p, 64, 1.0, null, p, 32, p, 1 << 20, null) == -1
     assert lib.fql_last_error().decode()
+
+
+def test_warmup_token_counts():
+    # 1 (a decode step), every positive graph-capture size, and the largest batch,
+    # each once (B12X write-up, Implementation: the warmup token set)
+    import fp8_quantized_linear_amd as fql
+
+    assert fql.token_counts_for_warmup(8192) == [1, 8192]
+    assert fql.token_counts_for_warmup(512, graph_sizes=(4, 1, 0, -2, 256, 4)) == [1, 4, 256, 512]
+
+
+def test_dynamic_scalar_buffer_size_matches_header():
+    import fp8_quantized_linear_amd as fql
+
+    text = open(os.path.join(ROOT, "include", "fql.h")).read()
+    m = re.search(r"#define FQL_DYNAMIC_SCALARS (\d+)", text)
+    assert m and int(m.group(1)) == fql.DYNAMIC_SCALARS
