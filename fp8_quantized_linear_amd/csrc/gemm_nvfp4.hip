@@ -57,7 +57,10 @@ namespace fql {
 // streams its own chunks (x_hat tiles, weight codes, scale dwords) into a
 // private D-stage LDS ring with direct global->LDS loads and waits only for
 // its own loads (explicit vmcnt, no workgroup barrier in the loop), so D
-// chunks per wave stay in flight. Weight fragments are dequantized to fp16
+// chunks per wave stay in flight. Lanes of x_hat rows >= M skip their loads
+// (an output row depends only on its own A row and rows >= M are never
+// stored; every row tile has a valid row, so each load instruction still
+// issues and the vmcnt counts hold). Weight fragments are dequantized to fp16
 // exactly as in the other kinds; the W partial sums are added in wave order
 // through LDS at the end (deterministic, no atomics).
 template <int MT, int NT>
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
       for (int ks = 0; ks < 4; ++ks) {
         if (FQ)
           lds_load16(xb + c * 256, x_voff[mt][ks], base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
-        else
+        else if (16 * mt + (lane & 15) < M)  // rows >= M are never stored: skip their bytes
           lds_load16(xh + ((mt * KS + 4 * c + ks) * 64) * 16, lane * 16,
                      base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
       }
@@ -504,6 +507,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
   auto a_src = [&](int f, int64_t c) -> const uint4v* {
     return xsrc + ((((int64_t)mgroup * AM + f) * KS + c * 4 + wave) * 64 + lane);
   };
+
   const int64_t KC4 = (KC + 3) / 4;
   const uint4v* bq_base[NT];
   const uint32_t* bs_base[NT];
