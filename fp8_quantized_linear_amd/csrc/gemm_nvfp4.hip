@@ -59,8 +59,8 @@ namespace fql {
 // its own loads (explicit vmcnt, no workgroup barrier in the loop), so D
 // chunks per wave stay in flight. Lanes of x_hat rows >= M skip their loads
 // (an output row depends only on its own A row and rows >= M are never
-// stored; every row tile has a valid row, so each load instruction still
-// issues and the vmcnt counts hold). Weight fragments are dequantized to fp16
+// stored); a row tile with no row below M loads whole, so every load
+// instruction issues and the vmcnt counts hold. Weight fragments are dequantized to fp16
 // exactly as in the other kinds; the W partial sums are added in wave order
 // through LDS at the end (deterministic, no atomics).
 template <int MT, int NT>
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
       for (int ks = 0; ks < 4; ++ks) {
         if (FQ)
           lds_load16(xb + c * 256, x_voff[mt][ks], base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
-        else if (16 * mt + (lane & 15) < M)  // rows >= M are never stored: skip their bytes
+        else if (16 * mt + (lane & 15) < M || 16 * mt >= M)  // rows >= M are never stored: skip their bytes
           lds_load16(xh + ((mt * KS + 4 * c + ks) * 64) * 16, lane * 16,
                      base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
       }
