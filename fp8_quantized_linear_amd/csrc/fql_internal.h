@@ -190,6 +190,8 @@ struct ScPlan {
   int64_t Mp, groups, ngroups;
   int splits, kc_per_split;
   int64_t counter_bytes, xcode_bytes, xscale_bytes, partial_bytes, total_bytes;
+  int fq;           // GEMV: activation quantized inside the workgroups (one launch)
+  int64_t dyn_lds;  // GEMV with fq: dynamic LDS bytes (the activation operand)
 };
 ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K);
 std::string describe_sc_plan(const ScPlan& p);

@@ -26,6 +26,7 @@
 #include "fql_device.h"
 #include "fql_gemm.h"
 #include "fql_internal.h"
+#include "sc_quant.h"
 
 namespace fql {
 
@@ -299,7 +300,7 @@ struct WaitChunks<L, 0> {
   static __device__ __forceinline__ void run(int) { wait_vmcnt<0>(); }
 };
 
-template <int F, int MT, int NT>
+template <int F, int MT, int NT, int FQ = 0>
 struct ScvStage {
   static constexpr int H = ScTraits<F>::H;
   uint4v a[MT][H][64];
@@ -307,18 +308,35 @@ struct ScvStage {
   uint32_t sa[64];  // MX: A scale quad dword; block FP8: A row scales (float bits)
   uint32_t sb[64];  // MX: B scale quad dword; block FP8: the column block's scale (broadcast)
 };
+// With the activation quantized inside the workgroup (FQ = 1) the ring
+// carries only the weight.
+template <int F, int MT, int NT>
+struct ScvStage<F, MT, NT, 1> {
+  static constexpr int H = ScTraits<F>::H;
+  uint4v b[NT][H][64];
+  uint32_t sb[64];
+};
 
-template <int F, int W, int MT, int NT, int D>
+// FQ = 1: the workgroup first quantizes rows 0 .. M-1 of x itself, with the
+// standalone quantizer's block arithmetic, into an LDS copy of the activation
+// operand for the whole K range (dynamic LDS: codes [MT][KC][H][64] x 16 B,
+// then the scales [KC][64] dwords or floats); rows >= M are left unwritten
+// (an output row depends only on its own activation row and rows >= M are
+// never stored), blocks past K are zero. The ring then carries only the
+// weight. This removes the separate quantizer launch for decode sizes.
+template <int F, int W, int MT, int NT, int D, int FQ>
 __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
     const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
     const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales, int M, int N,
     int64_t KC, int ntiles_w, int64_t quads_w, float alpha, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ y, int64_t ldy) {
+    uint16_t* __restrict__ y, int64_t ldy, const uint16_t* __restrict__ x, int64_t ldx,
+    int aligned, float inv_scale, int64_t K) {
   typedef ScTraits<F> T;
-  typedef ScvStage<F, MT, NT> Stage;
+  typedef ScvStage<F, MT, NT, FQ> Stage;
   constexpr int H = T::H;
   constexpr int64_t CHUNK = 1024 * H;
-  constexpr int L = MT * H + NT * H + (T::MX || T::BLOCK ? 2 : 0);  // loads per chunk
+  // loads per chunk
+  constexpr int L = (FQ ? 0 : MT * H) + NT * H + (T::MX || T::BLOCK ? (FQ ? 1 : 2) : 0);
   static_assert(MT >= 1 && MT <= 4 && (NT == 1 || NT == 2 || NT == 4), "tiles within one scale quad");
   static_assert(L * (D - 1) <= 63, "vmcnt range");
   __shared__ Stage ring[W][D];
@@ -339,27 +357,78 @@ __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
   const int64_t nbs = ((int64_t)ntiles_w * 16) / 128;
   const int64_t nb = (tile0 * 16) / 128 < nbs ? (tile0 * 16) / 128 : (nbs > 0 ? nbs - 1 : 0);
 
+  extern __shared__ __attribute__((aligned(16))) uint8_t sc_xop[];
+  const uint4v* xa = reinterpret_cast<const uint4v*>(sc_xop);
+  const uint32_t* xsd = reinterpret_cast<const uint32_t*>(sc_xop + MT * KC * H * 1024);
+
+  // (called after the first weight chunks are issued, so they load meanwhile)
+  auto quantize_activation = [&]() {
+    const int64_t nblk = KC * 4;              // 32-blocks per row of the padded operand
+    const int64_t total = (int64_t)M * nblk;  // rows >= M are never stored: not quantized
+    for (int64_t base = 0; base < total; base += 64 * W) {
+      // consecutive lanes take consecutive blocks of a row, so the four blocks
+      // of a 128-group (block FP8) sit in lanes l, l^1, l^2, l^3
+      const int64_t i = base + tid;
+      const bool inside = i < total;
+      const int64_t m = inside ? i / nblk : 0, b = inside ? i - m * nblk : 0;
+      const bool valid = inside && b * 32 < K;
+      float v[32];
+      if (valid) load32(x + m * ldx + b * 32, aligned != 0, v);
+      else
+#pragma unroll
+        for (int j = 0; j < 32; ++j) v[j] = 0.0f;
+      uint32_t w[8], sbyte = 0;
+      float gs = 0.0f;
+      quant_block32<F>(v, valid, inv_scale, w, sbyte, gs);
+      if (inside) {
+        if (!valid) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) w[j] = 0u;
+          sbyte = 0;
+          gs = 0.0f;
+        }
+        const int64_t tile = m / 16, c = b / 4;
+        const int r = (int)(m % 16), kg = (int)(b % 4);
+        uint8_t* tb = sc_xop + (tile * KC + c) * (int64_t)(H * 1024);
+        if (F == SC_MXFP4) {
+          *reinterpret_cast<uint4v*>(tb + (kg * 16 + r) * 16) = uint4v{w[0], w[1], w[2], w[3]};
+        } else {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int h16 = 2 * kg + j;
+            *reinterpret_cast<uint4v*>(tb + (h16 / 4) * 1024 + ((h16 % 4) * 16 + r) * 16) =
+                uint4v{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+          }
+        }
+        uint8_t* sbase = sc_xop + MT * KC * H * 1024;
+        if (T::MX) sbase[((c * 64 + kg * 16 + r) * 4) + (int)tile] = (uint8_t)sbyte;
+        if (T::BLOCK && kg == 0) reinterpret_cast<float*>(sbase)[c * 64 + m % 64] = gs;
+      }
+    }
+    __syncthreads();
+  };
+
   auto issue = [&](Stage& sg, int64_t c) {
     const uint32_t base = lds_offset(&sg);
+    if constexpr (!FQ) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int h = 0; h < H; ++h)
-        lds_load16(xcodes + (mt * KC + c) * CHUNK + h * 1024, lane * 16,
-                   base + (uint32_t)offsetof(Stage, a) + (mt * H + h) * 1024);
+        for (int h = 0; h < H; ++h)
+          lds_load16(xcodes + (mt * KC + c) * CHUNK + h * 1024, lane * 16,
+                     base + (uint32_t)offsetof(Stage, a) + (mt * H + h) * 1024);
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int h = 0; h < H; ++h)
         lds_load16(wcodes + (bt[nt] * KC + c) * CHUNK + h * 1024, lane * 16,
                    base + (uint32_t)offsetof(Stage, b) + (nt * H + h) * 1024);
-    if (T::MX) {
-      lds_load4(xscales + c * 256, lane * 4, base + (uint32_t)offsetof(Stage, sa));
-      lds_load4(wscales + (bquad * KC + c) * 256, lane * 4, base + (uint32_t)offsetof(Stage, sb));
-    } else if (T::BLOCK) {
-      lds_load4(xscales + c * 256, lane * 4, base + (uint32_t)offsetof(Stage, sa));
-      lds_load4(wscales + (nb * KC + c) * 4, 0u, base + (uint32_t)offsetof(Stage, sb));
+    if constexpr (!FQ) {
+      if (T::MX || T::BLOCK) lds_load4(xscales + c * 256, lane * 4, base + (uint32_t)offsetof(Stage, sa));
     }
+    if (T::MX) lds_load4(wscales + (bquad * KC + c) * 256, lane * 4, base + (uint32_t)offsetof(Stage, sb));
+    else if (T::BLOCK) lds_load4(wscales + (nb * KC + c) * 4, 0u, base + (uint32_t)offsetof(Stage, sb));
   };
 
   float4v acc[MT][NT];
@@ -368,7 +437,16 @@ __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Stage& sg) {
+  // the activation's code words and scale dword of row tile mt, chunk c
+  auto a_word = [&](const Stage& sg, int mt, int h, int64_t c) -> uint4v {
+    if constexpr (FQ) return xa[((mt * KC + c) * H + h) * 64 + lane];
+    else return sg.a[mt][h][lane];
+  };
+  auto a_scales = [&](const Stage& sg, int64_t c) -> const uint32_t* {
+    if constexpr (FQ) return xsd + c * 64;
+    else return &sg.sa[0];
+  };
+  auto compute = [&](const Stage& sg, int64_t c) {
     int8v b[NT];
     int sb[NT];
     const uint32_t sbw = sg.sb[lane];
@@ -384,21 +462,22 @@ __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
       sb[nt] = T::MX ? (int)((sbw >> (8 * ((tile0 + nt) % 4))) & 0xFFu) : 127;
     }
     const float swv = T::BLOCK ? __uint_as_float(sbw) : 0.0f;
-    const uint32_t saw = sg.sa[lane];
+    const uint32_t* asc = a_scales(sg, c);
+    const uint32_t saw = asc[lane];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const uint4v q0 = sg.a[mt][0][lane];
+      const uint4v q0 = a_word(sg, mt, 0, c);
       int8v a;
       if (H == 1) {
         a = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, 0, 0, 0, 0};
       } else {
-        const uint4v q1 = sg.a[mt][H - 1][lane];
+        const uint4v q1 = a_word(sg, mt, H - 1, c);
         a = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
       }
       const int sa = T::MX ? (int)((saw >> (8 * mt)) & 0xFFu) : 127;
       float4v s4 = float4v{0.f, 0.f, 0.f, 0.f};
       if (T::BLOCK) {
-        const float* rs = reinterpret_cast<const float*>(&sg.sa[0]) + 16 * mt + 4 * (lane >> 4);
+        const float* rs = reinterpret_cast<const float*>(asc) + 16 * mt + 4 * (lane >> 4);
         s4 = float4v{rs[0] * swv, rs[1] * swv, rs[2] * swv, rs[3] * swv};
       }
 #pragma unroll
@@ -422,6 +501,7 @@ __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
 #pragma unroll
   for (int j = 0; j < D; ++j)
     if (j < pre) issue(mine[j], c0 + j);
+  if constexpr (FQ) quantize_activation();
   for (int i0 = 0; i0 < n; i0 += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
@@ -429,7 +509,7 @@ __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
       if (idx < n) {
         const int later = n - 1 - idx;
         WaitChunks<L, D - 1>::run(later < D - 1 ? later : D - 1);
-        compute(mine[j]);
+        compute(mine[j], c0 + idx);
         if (idx + D < n) {
           __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // stage reads done before the refill
           issue(mine[j], c0 + idx + D);
@@ -480,6 +560,10 @@ __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
   X(F, 4, 1, 2, 4) X(F, 4, 1, 2, 6) X(F, 8, 1, 2, 3) X(F, 4, 1, 4, 3) X(F, 8, 1, 1, 4)          \
   X(F, 4, 2, 2, 3) X(F, 8, 2, 1, 3) X(F, 4, 1, 2, 3) X(F, 8, 1, 1, 3)
 
+// The (W, MT, NT, D) GEMV configurations also built with the activation
+// quantized in the workgroup (FQ = 1): the decode defaults.
+#define FQL_SCV_FUSED_CONFIGS(X, F) X(F, 4, 1, 4, 3) X(F, 4, 1, 2, 3)
+
 template <int F, int W, int MT, int NT, int D>
 static constexpr bool scv_config_fits() {
   return sizeof(ScvStage<F, MT, NT>) * W * D <= 160 * 1024;
@@ -492,6 +576,21 @@ static bool scv_config_built(int fmt, int w, int mt, int nt, int d) {
   FQL_SCV_CONFIGS(FQL_X, SC_FP8_BLOCK)
 #undef FQL_X
   return false;
+}
+
+// Dynamic LDS of the fused GEMV (the whole activation operand of MT row
+// tiles), or 0 when the fused kernel is not built for this configuration or
+// the operand and the weight ring do not fit in 160 KiB together.
+static int64_t scv_fused_lds(int fmt, int w, int mt, int nt, int d, int64_t KC) {
+  const int H = fmt == SC_MXFP4 ? 1 : 2;
+  const int64_t dyn = (int64_t)mt * KC * H * 1024 + KC * 256;
+#define FQL_X(F0, A, B, C, E)                                                                     \
+  if (fmt == F0 && w == A && mt == B && nt == C && d == E)                                         \
+    return (int64_t)sizeof(ScvStage<F0, B, C, 1>) * A * E + dyn <= 160 * 1024 ? dyn : 0;
+  FQL_SCV_FUSED_CONFIGS(FQL_X, SC_MXFP4) FQL_SCV_FUSED_CONFIGS(FQL_X, SC_MXFP8)
+  FQL_SCV_FUSED_CONFIGS(FQL_X, SC_FP8) FQL_SCV_FUSED_CONFIGS(FQL_X, SC_FP8_BLOCK)
+#undef FQL_X
+  return 0;
 }
 
 static constexpr size_t kLdsLimit = 160 * 1024;
@@ -540,16 +639,24 @@ ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
     if (M <= 16) { gw = 4; gnt = fmt == SC_MXFP4 ? 4 : 2; gd = 3; }
     else { gw = 4; gnt = 2; gd = 3; }
     bool forced = false;
-    if (const char* e = std::getenv("FQL_SC_GEMV")) {  // benchmarking aid: "W,NT,D" (0 = off)
-      int a = 0, b = 0, c = 0;
-      const int k = std::sscanf(e, "%d,%d,%d", &a, &b, &c);
+    int fq = -1;  // -1: fused when built and it fits
+    if (const char* e = std::getenv("FQL_SC_GEMV")) {  // benchmarking aid: "W,NT,D[,FQ]" (0 = off)
+      int a = 0, b = 0, c = 0, f = -1;
+      const int k = std::sscanf(e, "%d,%d,%d,%d", &a, &b, &c, &f);
       if (k >= 1 && a == 0) gemv = false;
-      else if (k == 3 && M <= 64 && scv_config_built(fmt, a, mt, b, c)) { gemv = true; gw = a; gnt = b; gd = c; forced = true; }
+      else if (k >= 3 && M <= 64 && scv_config_built(fmt, a, mt, b, c)) {
+        gemv = true; gw = a; gnt = b; gd = c; forced = true;
+        if (k == 4) fq = f;
+      }
     }
     if (std::getenv("FQL_SC_PLAN")) gemv = forced;
     if (gemv && scv_config_built(fmt, gw, mt, gnt, gd)) {
       p.kind = 1;
       p.wm = 1; p.wn = gw; p.mtw = mt; p.ntw = gnt; p.st = gd;
+      // decode sizes quantize the activation inside the workgroups (one launch)
+      const int64_t dyn = M <= 16 && fq != 0 ? scv_fused_lds(fmt, gw, mt, gnt, gd, KC) : 0;
+      p.fq = dyn > 0 ? 1 : 0;
+      p.dyn_lds = dyn;
       p.Mp = 16 * mt;
       p.ngroups = (ntiles + gnt - 1) / gnt;
       p.groups = p.ngroups;
@@ -597,6 +704,11 @@ ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
 
 std::string describe_sc_plan(const ScPlan& p) {
   char b[240];
+  if (p.kind == 1 && p.fq) {
+    std::snprintf(b, sizeof(b), "gemv_sc_kernel<%s,W=%d,MT=%d,NT=%d,D=%d,FQ=1> grid=%lld splits=1",
+                  sc_fmt_name(p.fmt), p.wn, p.mtw, p.ntw, p.st, (long long)p.groups);
+    return std::string(b);
+  }
   if (p.kind == 1) {
     std::snprintf(b, sizeof(b), "sc_quant_operand_kernel<%s> + gemv_sc_kernel<%s,W=%d,MT=%d,NT=%d,D=%d> grid=%lld splits=1",
                   sc_fmt_name(p.fmt), sc_fmt_name(p.fmt), p.wn, p.mtw, p.ntw, p.st, (long long)p.groups);
@@ -632,11 +744,23 @@ static hipError_t launch_scv_t(const ScPlan& p, const uint8_t* xc, const uint8_t
   if constexpr (!scv_config_fits<F, W, MT, NT, D>()) {
     return hipErrorInvalidValue;
   } else {
-    gemv_sc_kernel<F, W, MT, NT, D><<<(unsigned)p.groups, 64 * W, 0, st>>>(
+    gemv_sc_kernel<F, W, MT, NT, D, 0><<<(unsigned)p.groups, 64 * W, 0, st>>>(
         xc, xs, packed, packed + w.code_bytes, (int)M, (int)N, w.KC, (int)(w.rows_p / 16), w.quads,
-        alpha, bias, y, ldy);
+        alpha, bias, y, ldy, nullptr, 0, 0, 0.0f, 0);
     return hipGetLastError();
   }
+}
+
+template <int F, int W, int MT, int NT, int D>
+static hipError_t launch_scv_fused_t(const ScPlan& p, const uint16_t* x, int64_t ldx, bool aligned,
+                                     float inv_scale, int64_t K, const uint8_t* packed,
+                                     const ScDims& w, int64_t M, int64_t N, float alpha,
+                                     const uint16_t* bias, uint16_t* y, int64_t ldy, hipStream_t st) {
+  if (p.dyn_lds <= 0 || M > 16 * MT) return hipErrorInvalidValue;
+  gemv_sc_kernel<F, W, MT, NT, D, 1><<<(unsigned)p.groups, 64 * W, (size_t)p.dyn_lds, st>>>(
+      nullptr, nullptr, packed, packed + w.code_bytes, (int)M, (int)N, w.KC, (int)(w.rows_p / 16),
+      w.quads, alpha, bias, y, ldy, x, ldx, aligned ? 1 : 0, inv_scale, K);
+  return hipGetLastError();
 }
 
 hipError_t launch_sc_linear(const ScPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
@@ -649,6 +773,16 @@ hipError_t launch_sc_linear(const ScPlan& p, const uint16_t* x, int64_t M, int64
   uint8_t* xs = xc + p.xcode_bytes;
   float4v* partial = reinterpret_cast<float4v*>(xs + p.xscale_bytes);
   if (p.splits > 1 && p.groups > p.counter_bytes / 4) return hipErrorInvalidValue;
+  if (p.kind == 1 && p.fq) {
+#define FQL_X(F0, A, B, C, E)                                                                      \
+  if (p.fmt == F0 && p.wn == A && p.mtw == B && p.ntw == C && p.st == E)                           \
+    return launch_scv_fused_t<F0, A, B, C, E>(p, x, ldx, aligned, inv_scale, K, packed, w, M, N,    \
+                                              alpha, bias, y, ldy, st);
+    FQL_SCV_FUSED_CONFIGS(FQL_X, SC_MXFP4) FQL_SCV_FUSED_CONFIGS(FQL_X, SC_MXFP8)
+    FQL_SCV_FUSED_CONFIGS(FQL_X, SC_FP8) FQL_SCV_FUSED_CONFIGS(FQL_X, SC_FP8_BLOCK)
+#undef FQL_X
+    return hipErrorInvalidValue;
+  }
   hipError_t e = launch_sc_quant_operand(p.fmt, x, M, K, ldx, aligned, inv_scale, p.Mp, xc, xs, st);
   if (e != hipSuccess) return e;
   if (p.kind == 1) {

@@ -192,3 +192,16 @@ def test_dynamic_scalar_buffer_size_matches_header():
     text = open(os.path.join(ROOT, "include", "fql.h")).read()
     m = re.search(r"#define FQL_DYNAMIC_SCALARS (\d+)", text)
     assert m and int(m.group(1)) == fql.DYNAMIC_SCALARS
+
+
+def test_sibling_decode_plan_fuses_the_quantizer():
+    # M <= 16 runs one launch (the activation quantized inside the GEMV's
+    # workgroups) when the operand fits in LDS next to the weight ring
+    import fp8_quantized_linear_amd as fql
+
+    for fmt in ("mxfp4", "mxfp8", "fp8", "fp8_block"):
+        assert ",FQ=1>" in fql.linear_sc_plan(fmt, 1, 14336, 4096)
+        assert "sc_quant_operand_kernel" not in fql.linear_sc_plan(fmt, 16, 14336, 4096)
+        assert "sc_quant_operand_kernel" in fql.linear_sc_plan(fmt, 17, 14336, 4096)
+    # an operand too large for LDS keeps the two-launch path
+    assert "sc_quant_operand_kernel" in fql.linear_sc_plan("mxfp8", 1, 4096, 65536)

@@ -281,15 +281,54 @@ def test_every_sc_config(fmt, cfg, splits, monkeypatch):
 SCV_CONFIGS = [(4, 2, 4), (4, 2, 6), (8, 2, 3), (4, 4, 3), (8, 1, 4), (4, 2, 3), (8, 1, 3)]
 
 
+SCV_FUSED_CONFIGS = [(4, 4, 3), (4, 2, 3)]  # also built with the in-workgroup quantizer
+
+
+@pytest.mark.parametrize("fq", [0, 1])
 @pytest.mark.parametrize("M", [1, 16, 17, 32])
 @pytest.mark.parametrize("cfg", SCV_CONFIGS)
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8", "fp8", "fp8_block"])
-def test_every_gemv_config(fmt, cfg, M, monkeypatch):
+def test_every_gemv_config(fmt, cfg, M, fq, monkeypatch):
+    if fq and (M > 16 or cfg not in SCV_FUSED_CONFIGS):
+        pytest.skip("the fused GEMV is built for the decode defaults at M <= 16")
     K = 1152
     N = 384 if fmt == "fp8_block" else 400
     w, nt, d = cfg
-    monkeypatch.setenv("FQL_SC_GEMV", f"{w},{nt},{d}")
+    monkeypatch.setenv("FQL_SC_GEMV", f"{w},{nt},{d},{fq}")
     plan = fql.linear_sc_plan(fmt, M, N, K)
-    if f"gemv_sc_kernel<{fmt},W={w},MT={(M + 15) // 16},NT={nt},D={d}>" not in plan:
+    want = f"gemv_sc_kernel<{fmt},W={w},MT={(M + 15) // 16},NT={nt},D={d}" + (",FQ=1>" if fq else ">")
+    if want not in plan:
+        assert not fq, plan  # every fused configuration fits at this K
         pytest.skip(f"GEMV {cfg} not built for {fmt} at M={M}: {plan}")
-    _run(fmt, "tiny", M, K, N, True, alpha=None if fmt == "fp8" else 1.5, label=f"gemv {cfg}")
+    _run(fmt, "tiny", M, K, N, True, alpha=None if fmt == "fp8" else 1.5, label=f"gemv {cfg} fq={fq}")
+
+
+def _sc_weight(fmt, N, K):
+    W = f32_to_dev(synthetic.weight(N, K, config="siblings", seed=3))
+    if fmt == "fp8":
+        return fql.FP8Weight.from_float(W, input_scale=0.02)
+    return {"mxfp4": fql.MXFP4Weight, "mxfp8": fql.MXFP8Weight, "fp8_block": fql.FP8BlockWeight}[fmt].from_float(W)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8", "fp8", "fp8_block"])
+@pytest.mark.parametrize("M,K", [(1, 4096), (7, 1024), (16, 384), (3, 4096), (5, 1152)])
+def test_fused_gemv_equals_two_launch_path(fmt, M, K, monkeypatch):
+    # the in-workgroup quantizer produces the same operand bytes as the
+    # standalone quantizer, so the fused call is bit-identical to quantizer + GEMV
+    N = 2048 if fmt == "fp8_block" else 2000
+    w = _sc_weight(fmt, N, K)
+    fn = {"mxfp4": fql.linear_mxfp4, "mxfp8": fql.linear_mxfp8, "fp8": fql.linear_fp8,
+          "fp8_block": fql.linear_fp8_block}[fmt]
+    xb = cached_activations("normal", M, K, "siblings")
+    x = _dev_x(xb, pad=1 if M == 5 else 0)  # one unaligned case
+    nt = 4 if fmt == "mxfp4" else 2
+    outs = []
+    for fq in (1, 0):
+        monkeypatch.setenv("FQL_SC_GEMV", f"4,{nt},3,{fq}")
+        plan = fql.linear_sc_plan(fmt, M, N, K)
+        assert (",FQ=1>" in plan) == bool(fq), plan
+        announce(f"fused gemv {fmt} M={M} K={K} fq={fq}")
+        outs.append(fn(x, w))
+        torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
