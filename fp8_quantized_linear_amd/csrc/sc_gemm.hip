@@ -318,11 +318,12 @@ struct ScvStage<F, MT, NT, 1> {
 };
 
 // FQ = 1: the workgroup first quantizes rows 0 .. M-1 of x itself, with the
-// standalone quantizer's block arithmetic, into an LDS copy of the activation
-// operand for the whole K range (dynamic LDS: codes [MT][KC][H][64] x 16 B,
-// then the scales [KC][64] dwords or floats); rows >= M are left unwritten
-// (an output row depends only on its own activation row and rows >= M are
-// never stored), blocks past K are zero. The ring then carries only the
+// standalone quantizer's block arithmetic, into a compact LDS copy of the
+// activation operand for the whole K range (dynamic LDS, rows 0 .. M-1 only:
+// codes [KC][H][4 lane groups][M] x 16 B, then the scales: MX [KC][4][M]
+// dwords (byte 0), block FP8 [KC][M] floats); blocks past K are zero. Lanes
+// of rows >= M read row 0 (an output row depends only on its own activation
+// row and rows >= M are never stored). The ring then carries only the
 // weight. This removes the separate quantizer launch for decode sizes.
 template <int F, int W, int MT, int NT, int D, int FQ>
 __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
@@ -358,8 +359,7 @@ __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
   const int64_t nb = (tile0 * 16) / 128 < nbs ? (tile0 * 16) / 128 : (nbs > 0 ? nbs - 1 : 0);
 
   extern __shared__ __attribute__((aligned(16))) uint8_t sc_xop[];
-  const uint4v* xa = reinterpret_cast<const uint4v*>(sc_xop);
-  const uint32_t* xsd = reinterpret_cast<const uint32_t*>(sc_xop + MT * KC * H * 1024);
+  const uint32_t* xsd = reinterpret_cast<const uint32_t*>(sc_xop + KC * H * 4 * M * 16);
 
   // (called after the first weight chunks are issued, so they load meanwhile)
   auto quantize_activation = [&]() {
@@ -387,22 +387,23 @@ __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
           sbyte = 0;
           gs = 0.0f;
         }
-        const int64_t tile = m / 16, c = b / 4;
-        const int r = (int)(m % 16), kg = (int)(b % 4);
-        uint8_t* tb = sc_xop + (tile * KC + c) * (int64_t)(H * 1024);
+        const int64_t c = b / 4;
+        const int kg = (int)(b % 4);
+        // FP4: the 16-byte piece of row m is lane group kg; FP8: pieces h16 =
+        // 2kg + j go to half h16/4, lane group h16%4
         if (F == SC_MXFP4) {
-          *reinterpret_cast<uint4v*>(tb + (kg * 16 + r) * 16) = uint4v{w[0], w[1], w[2], w[3]};
+          *reinterpret_cast<uint4v*>(sc_xop + ((c * 4 + kg) * M + m) * 16) = uint4v{w[0], w[1], w[2], w[3]};
         } else {
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
             const int h16 = 2 * kg + j;
-            *reinterpret_cast<uint4v*>(tb + (h16 / 4) * 1024 + ((h16 % 4) * 16 + r) * 16) =
+            *reinterpret_cast<uint4v*>(sc_xop + (((c * H + h16 / 4) * 4 + h16 % 4) * M + m) * 16) =
                 uint4v{w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
           }
         }
-        uint8_t* sbase = sc_xop + MT * KC * H * 1024;
-        if (T::MX) sbase[((c * 64 + kg * 16 + r) * 4) + (int)tile] = (uint8_t)sbyte;
-        if (T::BLOCK && kg == 0) reinterpret_cast<float*>(sbase)[c * 64 + m % 64] = gs;
+        uint8_t* sbase = sc_xop + KC * H * 4 * M * 16;
+        if (T::MX) reinterpret_cast<uint32_t*>(sbase)[(c * 4 + kg) * M + m] = sbyte;
+        if (T::BLOCK && kg == 0) reinterpret_cast<float*>(sbase)[c * M + m] = gs;
       }
     }
     __syncthreads();
@@ -437,14 +438,28 @@ __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  // the activation's code words and scale dword of row tile mt, chunk c
+  // the lane's activation row of row tile mt in the compact copy (rows >= M
+  // read row 0)
+  auto fq_row = [&](int mt) -> int {
+    const int row = 16 * mt + (lane & 15);
+    return row < M ? row : 0;
+  };
+  // the activation's code words of row tile mt, half h, chunk c
   auto a_word = [&](const Stage& sg, int mt, int h, int64_t c) -> uint4v {
-    if constexpr (FQ) return xa[((mt * KC + c) * H + h) * 64 + lane];
+    if constexpr (FQ)
+      return *reinterpret_cast<const uint4v*>(sc_xop + (((c * H + h) * 4 + (lane >> 4)) * M + fq_row(mt)) * 16);
     else return sg.a[mt][h][lane];
   };
-  auto a_scales = [&](const Stage& sg, int64_t c) -> const uint32_t* {
-    if constexpr (FQ) return xsd + c * 64;
-    else return &sg.sa[0];
+  // MX: the E8M0 scale byte of row tile mt for this lane's row and block
+  auto a_scale_byte = [&](const Stage& sg, int mt, int64_t c) -> int {
+    if constexpr (FQ) return (int)(xsd[(c * 4 + (lane >> 4)) * M + fq_row(mt)] & 0xFFu);
+    else return (int)((sg.sa[lane] >> (8 * mt)) & 0xFFu);
+  };
+  // block FP8: the float32 scale of row 16mt + 4(lane/16) + i
+  auto a_row_scale = [&](const Stage& sg, int mt, int i, int64_t c) -> float {
+    const int row = 16 * mt + 4 * (lane >> 4) + i;
+    if constexpr (FQ) return reinterpret_cast<const float*>(xsd)[c * M + (row < M ? row : 0)];
+    else return reinterpret_cast<const float*>(&sg.sa[0])[row];
   };
   auto compute = [&](const Stage& sg, int64_t c) {
     int8v b[NT];
@@ -462,8 +477,6 @@ __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
       sb[nt] = T::MX ? (int)((sbw >> (8 * ((tile0 + nt) % 4))) & 0xFFu) : 127;
     }
     const float swv = T::BLOCK ? __uint_as_float(sbw) : 0.0f;
-    const uint32_t* asc = a_scales(sg, c);
-    const uint32_t saw = asc[lane];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const uint4v q0 = a_word(sg, mt, 0, c);
@@ -474,12 +487,11 @@ __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
         const uint4v q1 = a_word(sg, mt, H - 1, c);
         a = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
       }
-      const int sa = T::MX ? (int)((saw >> (8 * mt)) & 0xFFu) : 127;
+      const int sa = T::MX ? a_scale_byte(sg, mt, c) : 127;
       float4v s4 = float4v{0.f, 0.f, 0.f, 0.f};
-      if (T::BLOCK) {
-        const float* rs = reinterpret_cast<const float*>(asc) + 16 * mt + 4 * (lane >> 4);
-        s4 = float4v{rs[0] * swv, rs[1] * swv, rs[2] * swv, rs[3] * swv};
-      }
+      if (T::BLOCK)
+        s4 = float4v{a_row_scale(sg, mt, 0, c) * swv, a_row_scale(sg, mt, 1, c) * swv,
+                     a_row_scale(sg, mt, 2, c) * swv, a_row_scale(sg, mt, 3, c) * swv};
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         if (T::BLOCK) {
@@ -578,12 +590,12 @@ static bool scv_config_built(int fmt, int w, int mt, int nt, int d) {
   return false;
 }
 
-// Dynamic LDS of the fused GEMV (the whole activation operand of MT row
-// tiles), or 0 when the fused kernel is not built for this configuration or
-// the operand and the weight ring do not fit in 160 KiB together.
-static int64_t scv_fused_lds(int fmt, int w, int mt, int nt, int d, int64_t KC) {
+// Dynamic LDS of the fused GEMV (the compact activation operand, M rows), or
+// 0 when the fused kernel is not built for this configuration or the operand
+// and the weight ring do not fit in 160 KiB together.
+static int64_t scv_fused_lds(int fmt, int w, int mt, int nt, int d, int64_t KC, int64_t M) {
   const int H = fmt == SC_MXFP4 ? 1 : 2;
-  const int64_t dyn = (int64_t)mt * KC * H * 1024 + KC * 256;
+  const int64_t dyn = KC * M * (H * 64 + 16);  // codes, then scales, rows 0 .. M-1
 #define FQL_X(F0, A, B, C, E)                                                                     \
   if (fmt == F0 && w == A && mt == B && nt == C && d == E)                                         \
     return (int64_t)sizeof(ScvStage<F0, B, C, 1>) * A * E + dyn <= 160 * 1024 ? dyn : 0;
@@ -654,7 +666,7 @@ ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
       p.kind = 1;
       p.wm = 1; p.wn = gw; p.mtw = mt; p.ntw = gnt; p.st = gd;
       // decode sizes quantize the activation inside the workgroups (one launch)
-      const int64_t dyn = M <= 16 && fq != 0 ? scv_fused_lds(fmt, gw, mt, gnt, gd, KC) : 0;
+      const int64_t dyn = M <= 16 && fq != 0 ? scv_fused_lds(fmt, gw, mt, gnt, gd, KC, M) : 0;
       p.fq = dyn > 0 ? 1 : 0;
       p.dyn_lds = dyn;
       p.Mp = 16 * mt;

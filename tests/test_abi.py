@@ -204,4 +204,5 @@ def test_sibling_decode_plan_fuses_the_quantizer():
         assert "sc_quant_operand_kernel" not in fql.linear_sc_plan(fmt, 16, 14336, 4096)
         assert "sc_quant_operand_kernel" in fql.linear_sc_plan(fmt, 17, 14336, 4096)
     # an operand too large for LDS keeps the two-launch path
-    assert "sc_quant_operand_kernel" in fql.linear_sc_plan("mxfp8", 1, 4096, 65536)
+    assert ",FQ=1>" in fql.linear_sc_plan("mxfp8", 1, 4096, 65536)  # compact: M rows only
+    assert "sc_quant_operand_kernel" in fql.linear_sc_plan("mxfp8", 16, 4096, 65536)
