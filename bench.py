@@ -115,14 +115,16 @@ def _cases(workload, hb_override=None):
     return out
 
 
-def _kernel_of(M, N, K, fmt="nvfp4", xhat_only=False):
+def _kernel_of(M, N, K, fmt="nvfp4", general=False, dynamic=False):
     """The kernel that carries one linear call of this shape (the library's own plan;
-    the transform and dynamic-scale paths take the plan that writes x_hat)."""
+    the transform and dynamic-scale paths plan as unaligned calls, the transform's
+    with the x_hat operand)."""
     import fp8_quantized_linear_amd as fql
 
     if fmt != "nvfp4":
         return fql.linear_sc_plan(fmt, M, N, K).split(" grid=")[0].split(" + ")[-1]
-    return fql.linear_plan(M, N, K, aligned=not xhat_only).split(" grid=")[0].split(" + ")[-1]
+    plan = fql.linear_plan(M, N, K, aligned=not (general or dynamic), transform=general)
+    return plan.split(" grid=")[0].split(" + ")[-1]
 
 
 def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic=False):
@@ -191,7 +193,7 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic
         ws = fql.new_workspace(wsb, dev)
         setups.append(dict(M=M, N=N, K=K, name=name, hb=hbk, x=x, objs=objs, bias=bias, y=y,
                            ws=ws, flops=2.0 * M * N * K, bytes=_alg_bytes(M, N, K, with_bias, fmt),
-                           kernel=_kernel_of(M, N, K, fmt, xhat_only=general or dynamic)))
+                           kernel=_kernel_of(M, N, K, fmt, general=general, dynamic=dynamic)))
     torch.cuda.synchronize()
     n = len(setups)
 

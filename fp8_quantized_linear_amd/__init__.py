@@ -388,10 +388,12 @@ def linear_workspace_bytes(M, N, K):
     return n.value
 
 
-def linear_plan(M, N, K, aligned=True):
-    """One-line description of the kernel/launch plan a linear call of this shape uses."""
+def linear_plan(M, N, K, aligned=True, transform=False):
+    """One-line description of the kernel/launch plan a linear call of this shape uses
+    (`transform`: the plan of a call with a general transform matrix)."""
     buf = ctypes.create_string_buffer(256)
-    _check(lib().fql_linear_nvfp4_describe(int(M), int(N), int(K), int(bool(aligned)), buf, 256))
+    flags = int(bool(aligned)) | (2 if transform else 0)
+    _check(lib().fql_linear_nvfp4_describe(int(M), int(N), int(K), flags, buf, 256))
     return buf.value.decode()
 
 

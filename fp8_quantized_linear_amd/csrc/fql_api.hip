@@ -4,6 +4,7 @@
 // The availability / format-constraint split follows the write-ups' kernel
 // lifecycle: is_supported decides availability with a reason string,
 // can_implement checks format constraints, and the hot call only asserts.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -211,9 +212,12 @@ int fql_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* by
   if (!bytes) return fail(FQL_ERR_INVALID, "null pointer");
   if (M < 1 || N < 1 || K < 16 || K % 16 != 0)
     return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 16");
+  // every plan a call of this shape may take: aligned rows, unaligned rows, and
+  // the transform's x_hat-only operand
   const int64_t a = fql::plan_gemm_nvfp4(M, N, K, true).total_bytes;
   const int64_t u = fql::plan_gemm_nvfp4(M, N, K, false).total_bytes;
-  *bytes = (size_t)(a > u ? a : u);
+  const int64_t t = fql::plan_gemm_nvfp4(M, N, K, false, true).total_bytes;
+  *bytes = (size_t)std::max(a, std::max(u, t));
   return ok();
 }
 
@@ -221,7 +225,9 @@ int fql_linear_nvfp4_describe(int64_t M, int64_t N, int64_t K, int aligned, char
                               size_t buf_len) {
   if (M < 1 || N < 1 || K < 16 || K % 16 != 0)
     return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 16");
-  write_reason(buf, buf_len, fql::describe_plan(fql::plan_gemm_nvfp4(M, N, K, aligned != 0)));
+  const bool transform = (aligned & 2) != 0;
+  write_reason(buf, buf_len,
+               fql::describe_plan(fql::plan_gemm_nvfp4(M, N, K, !transform && (aligned & 1) != 0, transform)));
   return ok();
 }
 
@@ -382,8 +388,9 @@ int linear_nvfp4_extras(const void* x, int64_t M, int64_t K, int64_t ldx, float 
   if (reinterpret_cast<uintptr_t>(w_packed) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(FQL_ERR_INVALID, "packed weight must be 16-byte and workspace 256-byte aligned");
-  // a plan that writes x_hat (the fused small-M kernel quantizes with a host-side scale)
-  const fql::GemmPlan plan = fql::plan_gemm_nvfp4(M, N, K, false);
+  // a plan that writes x_hat or the packed activation (the fused small-M kernel
+  // quantizes with a host-side scale); the transform's quantizer writes x_hat only
+  const fql::GemmPlan plan = fql::plan_gemm_nvfp4(M, N, K, false, T != nullptr);
   if (workspace_bytes < (size_t)plan.total_bytes)
     return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
                 (long long)plan.total_bytes);

@@ -196,6 +196,14 @@ __device__ __forceinline__ void lds_load4(const void* sbase, uint32_t voff, uint
   __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
                    : "memory");
 }
+// A wave-uniform address the compiler cannot prove uniform (e.g. formed inside
+// a lane-dependent branch), moved to scalar registers for the loads above.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");

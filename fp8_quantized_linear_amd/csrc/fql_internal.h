@@ -44,6 +44,11 @@ hipError_t launch_quant_nvfp4_f32(const float* w, int64_t N, int64_t K, int64_t 
 hipError_t launch_quant_nvfp4_xhat(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
                                    int hb, bool aligned, int64_t Mp, int64_t Kp, _Float16* xhat,
                                    const float* g_dev, hipStream_t st);
+// The same quantization written as a packed operand (the packed weight layout
+// with Mp rows): codes [Mp/16][Kp/128][64][16 B], then scales; Mp % 16 == 0.
+hipError_t launch_quant_nvfp4_apack(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
+                                    int hb, bool aligned, int64_t Mp, int64_t Kp, uint8_t* apack,
+                                    const float* g_dev, hipStream_t st);
 // max |v| into out (one float, or nslots partial maxima that launch_dynamic_scale folds)
 hipError_t launch_amax_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int hb,
                             bool aligned, float* out, hipStream_t st, int nslots = 1);
@@ -83,19 +88,22 @@ struct GemmPlan {
   int ntw;            // kind 0: 16-column tiles per workgroup
   int64_t lds_bytes;  // kind 0: dynamic LDS (compact activation copy / reduction)
   int fq;             // kind 4: activation quantized inside the kernel (no x_hat pass)
+  int pa;             // kind 4: the quantizer pass writes the activation packed like a weight
   int64_t counter_bytes, xhat_bytes, partial_bytes, total_bytes;
 };
 // `aligned`: x rows are 16-byte aligned (pointer and row stride); the
 // fused small-M kernel needs it. Workspace sizes of both kinds are covered by
 // the aligned=false plan, which never needs less.
-GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned);
+// `xhat_only`: the activation operand comes from the transform's quantizer,
+// which writes x_hat only (no packed activation form).
+GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool xhat_only = false);
 
 // Whether gemm_tiled_kernel<mt, nt, wm> / gemm_lds_kernel<mt, nt, st> is built
 // into the library.
 bool tiled_config_built(int mt, int nt, int wm);
 bool lds_config_built(int mt, int nt, int st);
 bool lds32_config_built(int mt, int nt, int st);
-bool gemv_ring_config_built(int w, int mt, int nt, int d);
+bool gemv_ring_config_built(int w, int mt, int nt, int d, bool packed_a);
 
 // Kernel name and parameters of a plan (diagnostics).
 std::string describe_plan(const GemmPlan& p);

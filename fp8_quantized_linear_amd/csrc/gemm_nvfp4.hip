@@ -63,11 +63,19 @@ namespace fql {
 // instruction issues and the vmcnt counts hold. Weight fragments are dequantized to fp16
 // exactly as in the other kinds; the W partial sums are added in wave order
 // through LDS at the end (deterministic, no atomics).
-template <int MT, int NT>
+template <int MT, int NT, int PA>
 struct GemvStage {
   uint4v a[MT][4][64];  // x_hat fragments of the chunk's four 32-deep steps
   uint4v b[NT][64];     // weight codes (one 16-byte slot per lane and tile)
   uint32_t s[NT][64];   // the lane's scale dword of this chunk, per tile
+};
+// PA = 1: the activation in the packed weight layout (codes and scale dwords per row tile)
+template <int MT, int NT>
+struct GemvStage<MT, NT, 1> {
+  uint4v ac[MT][64];
+  uint32_t as[MT][64];
+  uint4v b[NT][64];
+  uint32_t s[NT][64];
 };
 
 template <int L, int K>
@@ -88,7 +96,11 @@ struct GemvWait<L, 0> {
 // the partner lane l^16 holds the other half of the 16-block, so one shuffle
 // gives the block maximum). Needs 16-byte aligned rows, K % 128 == 0 and no
 // rotation; rows >= M are read from row M-1 (in bounds) and zeroed.
-template <int W, int MT, int NT, int D, int FQ>
+// PA = 1 reads the activation packed like a weight (xhat then points at that
+// operand: codes of the 16·MT rows, then their scales) and dequantizes each A
+// fragment exactly like a B fragment: 1.25 KiB per row tile and chunk through
+// the ring instead of 4 KiB of x_hat, the same fp16 operand values.
+template <int W, int MT, int NT, int D, int FQ, int PA>
 __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
     const _Float16* __restrict__ xhat, const uint16_t* __restrict__ x, int64_t ldx, float g,
     const uint8_t* __restrict__ wcodes,
@@ -96,8 +108,9 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
     const float* __restrict__ alpha_dev,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t ldy) {
   if (alpha_dev != nullptr) alpha = *alpha_dev;  // per-call scale computed on the device
-  typedef GemvStage<MT, NT> Stage;
-  constexpr int L = MT * 4 + NT * 2;  // loads per chunk
+  static_assert(!(FQ && PA), "one activation form");
+  typedef GemvStage<MT, NT, PA> Stage;
+  constexpr int L = MT * (PA ? 2 : 4) + NT * 2;  // loads per chunk
   static_assert(L * (D - 1) <= 63, "vmcnt range");
   __shared__ Stage ring[W][D];
   static_assert(sizeof(ring) >= sizeof(float4v) * W * MT * NT * 64, "reduction buffer aliases the ring");
@@ -132,16 +145,29 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
 
   auto issue = [&](Stage& sg, int64_t c) {
     const uint32_t base = lds_offset(&sg);
+    if constexpr (PA) {
+      // rows >= M are never stored: skip their bytes (the instructions still issue)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (FQ)
-          lds_load16(xb + c * 256, x_voff[mt][ks], base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
-        else if (16 * mt + (lane & 15) < M || 16 * mt >= M)  // rows >= M are never stored: skip their bytes
-          lds_load16(xh + ((mt * KS + 4 * c + ks) * 64) * 16, lane * 16,
-                     base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint8_t* ac = uniform_ptr(xh + (mt * KC + c) * 1024);
+        const uint8_t* as = uniform_ptr(xh + 8 * MT * Kp + (mt * KC4 + c / 4) * 512);
+        if (16 * mt + (lane & 15) < M || 16 * mt >= M) {
+          lds_load16(ac, lane * 16, base + (uint32_t)offsetof(Stage, ac) + mt * 1024);
+          lds_load4(as, s_voff_lane + (uint32_t)(c & 3) * 4, base + (uint32_t)offsetof(Stage, as) + mt * 256);
+        }
       }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          if (FQ)
+            lds_load16(xb + c * 256, x_voff[mt][ks], base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
+          else if (16 * mt + (lane & 15) < M || 16 * mt >= M)  // rows >= M are never stored: skip their bytes
+            lds_load16(xh + ((mt * KS + 4 * c + ks) * 64) * 16, lane * 16,
+                       base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
+        }
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       lds_load16(wcodes + (bt[nt] * KC + c) * 1024, lane * 16,
@@ -162,6 +188,9 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
   // operations and rounding as the standalone quantizer
   auto quant_fragment = [&](const Stage& sg, int mt, int ks) -> half8 {
 #pragma clang fp contract(off)
+    if constexpr (PA) {
+      return half8{};
+    } else {
     const int r = lane & 15;
     const int c16 = 4 * ks + (lane >> 4);
     const uint4v raw = *reinterpret_cast<const uint4v*>(
@@ -190,6 +219,7 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
     uint32_t hw[4];
     dequant8_f16(q, half2v{sh, sh}, hw);
     return __builtin_bit_cast(half8, uint4v{hw[0], hw[1], hw[2], hw[3]});
+    }
   };
 
   auto compute = [&](const Stage& sg) {
@@ -200,6 +230,15 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
       codes[nt] = sg.b[nt][lane];
       sw[nt] = sg.s[nt][lane];
     }
+    uint4v acodes[PA ? MT : 1];
+    uint32_t asw[PA ? MT : 1];
+    if constexpr (PA) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acodes[mt] = sg.ac[mt][lane];
+        asw[mt] = sg.as[mt][lane];
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       half8 bf[NT];
@@ -208,7 +247,8 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         half8 a;
-        if (FQ) a = quant_fragment(sg, mt, ks);
+        if constexpr (PA) a = b_fragment(dword_of(acodes[mt], ks), ChunkScales(asw[mt])[ks]);
+        else if constexpr (FQ) a = quant_fragment(sg, mt, ks);
         else a = __builtin_bit_cast(half8, sg.a[mt][ks][lane]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
@@ -1028,7 +1068,7 @@ static constexpr int kCUs = 256;
 // Benchmarking aid: FQL_PLAN="kind=0,waves=8,ntw=2,rc=4" or "kind=1,mt=4,nt=1,splits=2"
 // overrides the launch-plan heuristics (no effect on results, only on speed).
 struct GemmOverride {
-  int kind = -1, waves = 0, ntw = 0, rc = 0, mt = 0, nt = 0, wm = 0, st = 0, splits = 0, fq = -1;
+  int kind = -1, waves = 0, ntw = 0, rc = 0, mt = 0, nt = 0, wm = 0, st = 0, splits = 0, fq = -1, pa = -1;
 };
 static GemmOverride gemm_override() {
   GemmOverride o;
@@ -1045,7 +1085,7 @@ static GemmOverride gemm_override() {
       const std::string k = kv.substr(0, eq);
       const int v = std::atoi(kv.c_str() + eq + 1);
       if (k == "kind") o.kind = v;
-      else if (k == "waves" && (v == 4 || v == 8)) o.waves = v;
+      else if (k == "waves" && (v == 4 || v == 8 || v == 16)) o.waves = v;
       else if (k == "ntw" && (v == 1 || v == 2 || v == 4)) o.ntw = v;
       else if (k == "rc" && (v == 4 || v == 8)) o.rc = v;
       else if (k == "mt" && (v == 1 || v == 2 || v == 4 || v == 8)) o.mt = v;
@@ -1054,6 +1094,7 @@ static GemmOverride gemm_override() {
       else if (k == "st" && v >= 2 && v <= 8) o.st = v;
       else if (k == "splits" && v >= 1 && v <= 64) o.splits = v;
       else if (k == "fq" && (v == 0 || v == 1)) o.fq = v;
+      else if (k == "pa" && (v == 0 || v == 1)) o.pa = v;
     }
     pos = end + 1;
   }
@@ -1063,7 +1104,7 @@ static constexpr int64_t kCounterBytes = kWorkspaceCounterBytes;
 static constexpr int64_t kGemvMaxLds = 64 * 1024;    // compact activation copy in LDS
 static constexpr int64_t kGemvMaxRedundantBlocks = 1 << 20;  // workgroups x 16-blocks quantized
 
-GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
+GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool xhat_only) {
   GemmPlan p{};
   const PackedDims d = packed_dims(N, K);
   p.Np = d.Np;
@@ -1090,7 +1131,7 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     p.Mp = M;
     p.waves = ntiles < 1024 ? 8 : 4;
     p.ntw = M > 1 && ntiles < 1024 ? 2 : 1;
-    if (ov.waves) p.waves = ov.waves;
+    if (ov.waves == 4 || ov.waves == 8) p.waves = ov.waves;  // the built kind-0 widths
     if (ov.ntw) p.ntw = ov.ntw;
     const int64_t cpw = (KC + p.waves - 1) / p.waves;
     p.kcmax = cpw <= 8 ? 4 : 8;  // register ring depth (chunks)
@@ -1104,10 +1145,13 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     p.lds_bytes = std::max<int64_t>(M * p.Kp * 2, (int64_t)p.waves * p.ntw * 1024);
   } else {
     // Workgroup tile (WM*MT*16) x ((4/WM)*NT*16); kind 2 always has WM = 1.
-    // Defaults (measured on the decode and prefill layer shapes): small M
-    // keeps the register-staged tiled kernel; from 33 rows on the LDS-ring
+    // Defaults (measured on the decode and prefill layer shapes): up to 32
+    // rows the per-wave-ring kernel, except wide layers with short K (gate_up)
+    // above 16 rows or without the packed activation, which stream better
+    // through the register-staged tiled kernel; from 33 rows on the LDS-ring
     // kernel on 32x32 MFMAs.
-    p.kind = M <= 32 ? ((N >= 16384 && p.Kp < 8192) ? 1 : 4) : 3;
+    const bool wide_short = N >= 16384 && p.Kp < 8192;
+    p.kind = M <= 32 ? (wide_short && (M > 16 || xhat_only) ? 1 : 4) : 3;
     if (ov.kind >= 1 && ov.kind <= 4) p.kind = ov.kind;
     if (p.kind == 4) {
       // per-wave rings: W waves split K, NT tiles per workgroup, D chunks in flight
@@ -1115,16 +1159,21 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
       p.waves = p.Kp >= 8192 ? 8 : 4;
       p.nt = p.Kp >= 8192 ? 1 : 2;
       p.st = 3;
-      if (M <= 16 && N >= 16384) { p.waves = 4; p.nt = 1; p.st = 4; }
+      if (M <= 16 && wide_short) p.nt = 4;
       if (ov.waves) p.waves = ov.waves;
       if (ov.nt) p.nt = ov.nt;
       if (ov.st) p.st = ov.st;
-      if (p.mt <= 2 && gemv_ring_config_built(p.waves, p.mt, p.nt, p.st)) {
+      // The fused quantizer repeats the activation's quantization in every
+      // workgroup; measured slower than the separate x_hat pass on the decode
+      // shapes (e.g. qkv M = 32: 15.9 vs 12.5 us), so it is opt-in.
+      const int fq = aligned && K % 128 == 0 && ov.fq == 1 ? 1 : 0;
+      // the quantizer pass writes the activation packed like a weight (not
+      // for the transform's quantizer, which writes x_hat)
+      const int pa = fq || xhat_only ? 0 : ov.pa >= 0 ? ov.pa : 1;
+      if (p.mt <= 2 && gemv_ring_config_built(p.waves, p.mt, p.nt, p.st, pa != 0)) {
         p.wm = 1;
-        // The fused quantizer repeats the activation's quantization in every
-        // workgroup; measured slower than the separate x_hat pass on the decode
-        // shapes (e.g. qkv M = 32: 15.9 vs 12.5 us), so it is opt-in.
-        p.fq = aligned && K % 128 == 0 && ov.fq == 1 ? 1 : 0;
+        p.fq = fq;
+        p.pa = pa;
         p.Mp = 16 * p.mt;
         p.groups = (ntiles + p.nt - 1) / p.nt;
         p.ngroups = p.groups;
@@ -1206,9 +1255,9 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
 std::string describe_plan(const GemmPlan& p) {
   char b[256];
   if (p.kind == 4) {
-    std::snprintf(b, sizeof(b), "%sgemv_ring_kernel<W=%d,MT=%d,NT=%d,D=%d,FQ=%d> grid=%lld splits=1",
-                  p.fq ? "" : "quant_nvfp4_xhat_kernel + ", p.waves, p.mt, p.nt, p.st, p.fq,
-                  (long long)p.groups);
+    std::snprintf(b, sizeof(b), "%sgemv_ring_kernel<W=%d,MT=%d,NT=%d,D=%d,FQ=%d,PA=%d> grid=%lld splits=1",
+                  p.fq ? "" : p.pa ? "quant_nvfp4_apack_kernel + " : "quant_nvfp4_xhat_kernel + ", p.waves,
+                  p.mt, p.nt, p.st, p.fq, p.pa, (long long)p.groups);
   } else if (p.kind == 3) {
     std::snprintf(b, sizeof(b),
                   "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d> grid=%lld splits=%d",
@@ -1347,9 +1396,18 @@ bool lds32_config_built(int mt, int nt, int st) {
 #define FQL_GEMV_RING_CONFIGS(X) \
   X(4, 1, 2, 3) X(4, 1, 2, 4) X(4, 1, 4, 3) X(8, 1, 1, 3) X(8, 1, 2, 3) X(4, 2, 2, 3) X(4, 2, 1, 4)
 
-bool gemv_ring_config_built(int w, int mt, int nt, int d) {
+// Further (W, MT, NT, D) configurations built only with the packed activation,
+// whose stages are small enough for more waves or deeper rings.
+#define FQL_GEMV_RING_PA_CONFIGS(X) \
+  X(8, 1, 1, 4) X(8, 1, 1, 6) X(16, 1, 1, 3) X(8, 1, 2, 4) X(4, 1, 4, 4) X(8, 2, 1, 3) X(8, 2, 1, 4) \
+  X(4, 2, 4, 3) X(8, 2, 2, 3)
+
+bool gemv_ring_config_built(int w, int mt, int nt, int d, bool packed_a) {
 #define FQL_X(A, B, C, E) if (w == A && mt == B && nt == C && d == E) return true;
   FQL_GEMV_RING_CONFIGS(FQL_X)
+  if (packed_a) {
+    FQL_GEMV_RING_PA_CONFIGS(FQL_X)
+  }
 #undef FQL_X
   return false;
 }
@@ -1385,7 +1443,15 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
   }
   if (p.kind == 0) return hipErrorInvalidValue;  // caller re-plans unaligned inputs as kind 1
   const bool fused = ex == nullptr && p.kind == 4 && p.fq && hb == 0 && aligned && K % 128 == 0;
-  if (!fused) {
+  // the packed activation comes from the x_hat quantizer's packed mode (not the transform's)
+  const bool packed_a = !fused && p.kind == 4 && p.pa && (ex == nullptr || ex->T == nullptr);
+  if (packed_a) {
+    if (p.Mp != 16 * p.mt) return hipErrorInvalidValue;
+    const hipError_t e = launch_quant_nvfp4_apack(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp,
+                                                  reinterpret_cast<uint8_t*>(xhat),
+                                                  ex != nullptr ? ex->g_dev : nullptr, st);
+    if (e != hipSuccess) return e;
+  } else if (!fused) {
     hipError_t e;
     if (ex != nullptr && ex->T != nullptr) {
       TransformArgs ta{};
@@ -1405,17 +1471,32 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
 #define FQL_X(A, B, C, E)                                                                             \
   if (p.waves == A && p.mt == B && p.nt == C && p.st == E) {                                          \
     if (fused)                                                                                        \
-      gemv_ring_kernel<A, B, C, E, 1><<<(unsigned)p.groups, 64 * A, 0, st>>>(                         \
+      gemv_ring_kernel<A, B, C, E, 1, 0><<<(unsigned)p.groups, 64 * A, 0, st>>>(                      \
+          xhat, x, ldx, g, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16),   \
+          alpha, alpha_dev, bias, y, ldy);                                                             \
+    else if (packed_a)                                                                                \
+      gemv_ring_kernel<A, B, C, E, 0, 1><<<(unsigned)p.groups, 64 * A, 0, st>>>(                      \
           xhat, x, ldx, g, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16),   \
           alpha, alpha_dev, bias, y, ldy);                                                             \
     else                                                                                              \
-      gemv_ring_kernel<A, B, C, E, 0><<<(unsigned)p.groups, 64 * A, 0, st>>>(                         \
+      gemv_ring_kernel<A, B, C, E, 0, 0><<<(unsigned)p.groups, 64 * A, 0, st>>>(                      \
           xhat, x, ldx, g, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16),   \
           alpha, alpha_dev, bias, y, ldy);                                                             \
     return hipGetLastError();                                                                          \
   }
     FQL_GEMV_RING_CONFIGS(FQL_X)
 #undef FQL_X
+    if (packed_a) {
+#define FQL_X(A, B, C, E)                                                                             \
+  if (p.waves == A && p.mt == B && p.nt == C && p.st == E) {                                          \
+    gemv_ring_kernel<A, B, C, E, 0, 1><<<(unsigned)p.groups, 64 * A, 0, st>>>(                        \
+        xhat, x, ldx, g, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16),     \
+        alpha, alpha_dev, bias, y, ldy);                                                               \
+    return hipGetLastError();                                                                          \
+  }
+      FQL_GEMV_RING_PA_CONFIGS(FQL_X)
+#undef FQL_X
+    }
     return hipErrorInvalidValue;
   }
   if (p.kind == 3) {

@@ -64,7 +64,13 @@ __global__ __launch_bounds__(256) void quant_nvfp4_canonical_kernel(
 // same block's stores for the wave's other rows: R * 16 contiguous bytes
 // per store instruction group (a wave writes 2 * J runs of 16 * R bytes).
 // R = 16 (J = 4) unless the rotation needs 8 blocks per chunk (b = 128: R = 8).
-template <int HB>
+//
+// PK = 1 writes the activation packed exactly like a weight (codes and scales
+// in the packed weight layout, rows padded to Mp): 0.5625 bytes per element
+// instead of x_hat's 2, and the small-M GEMV dequantizes its A fragments the
+// way it dequantizes the weight's. The same block arithmetic gives the same
+// codes and scales, so both forms hold the same operand values.
+template <int HB, int PK>
 __global__ __launch_bounds__(256) void quant_nvfp4_xhat_kernel(
     const uint16_t* __restrict__ x, int M, int K, int64_t ldx, float g, int aligned16, int Mp,
     int Kp, _Float16* __restrict__ xhat, const float* __restrict__ g_dev) {
@@ -90,6 +96,20 @@ __global__ __launch_bounds__(256) void quant_nvfp4_xhat_kernel(
   if constexpr (HB > 0) fwht_block<HB, (int)R>(v, kb);
   uint32_t lo, hi, s;
   quant_block(v, g, lo, hi, s);
+  if constexpr (PK) {
+    // tile t = m/16, row n = m%16, chunk c = kb/8, step j = (kb%8)/2, half h = kb%2:
+    // lo goes to lane (2h)*16 + n, hi to lane (2h+1)*16 + n, dword j of the chunk's
+    // 16-byte lane slot; the scale to slot 2n + h, byte 4(c%4) + j of the 4-chunk group
+    const uint32_t KC = (uint32_t)Kp / 128u, KC4 = (KC + 3u) / 4u;
+    const uint32_t t = m >> 4, n = m & 15u, c = kb >> 3, j = (kb >> 1) & 3u, h = kb & 1u;
+    uint8_t* out = reinterpret_cast<uint8_t*>(xhat);
+    uint32_t* cw = reinterpret_cast<uint32_t*>(out + ((size_t)(t * KC + c) * 64u + 2u * h * 16u + n) * 16u) + j;
+    cw[0] = lo;
+    cw[64] = hi;  // next 16-lane group: 256 bytes on
+    uint8_t* sc = out + (size_t)((uint32_t)Mp / 2u) * (uint32_t)Kp;
+    sc[((size_t)(t * KC4 + (c >> 2)) * 32u + 2u * n + h) * 16u + 4u * (c & 3u) + j] = (uint8_t)s;
+    return;
+  }
   const _Float16 sh = e4m3_to_f16(s);
   const half2v s2 = {sh, sh};
   uint32_t hw[8];
@@ -181,23 +201,37 @@ hipError_t launch_quant_nvfp4_f32(const float* w, int64_t N, int64_t K, int64_t 
   return launch_canonical<float>(w, N, K, ldw, g, hb, aligned, codes, scales, nullptr, st);
 }
 
-hipError_t launch_quant_nvfp4_xhat(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
-                                   int hb, bool aligned, int64_t Mp, int64_t Kp, _Float16* xhat,
-                                   const float* g_dev, hipStream_t st) {
+template <int PK>
+static hipError_t launch_xhat_t(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g, int hb,
+                                bool aligned, int64_t Mp, int64_t Kp, _Float16* xhat,
+                                const float* g_dev, hipStream_t st) {
   const int64_t total = Mp * (Kp / 16);
-  if (total >= ((int64_t)1 << 31) || Kp >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (total >= ((int64_t)1 << 31) || Kp >= ((int64_t)1 << 31) || Mp % 16 != 0) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((total + 255) / 256)), block(256);
   const int al = aligned ? 1 : 0;
   const int m = (int)M, k = (int)K, mp = (int)Mp, kp = (int)Kp;
   switch (hb) {
-    case 0: quant_nvfp4_xhat_kernel<0><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
-    case 16: quant_nvfp4_xhat_kernel<16><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
-    case 32: quant_nvfp4_xhat_kernel<32><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
-    case 64: quant_nvfp4_xhat_kernel<64><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
-    case 128: quant_nvfp4_xhat_kernel<128><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
+    case 0: quant_nvfp4_xhat_kernel<0, PK><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
+    case 16: quant_nvfp4_xhat_kernel<16, PK><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
+    case 32: quant_nvfp4_xhat_kernel<32, PK><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
+    case 64: quant_nvfp4_xhat_kernel<64, PK><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
+    case 128: quant_nvfp4_xhat_kernel<128, PK><<<grid, block, 0, st>>>(x, m, k, ldx, g, al, mp, kp, xhat, g_dev); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_quant_nvfp4_xhat(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
+                                   int hb, bool aligned, int64_t Mp, int64_t Kp, _Float16* xhat,
+                                   const float* g_dev, hipStream_t st) {
+  return launch_xhat_t<0>(x, M, K, ldx, g, hb, aligned, Mp, Kp, xhat, g_dev, st);
+}
+
+hipError_t launch_quant_nvfp4_apack(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
+                                    int hb, bool aligned, int64_t Mp, int64_t Kp, uint8_t* apack,
+                                    const float* g_dev, hipStream_t st) {
+  return launch_xhat_t<1>(x, M, K, ldx, g, hb, aligned, Mp, Kp, reinterpret_cast<_Float16*>(apack),
+                          g_dev, st);
 }
 
 template <typename TIn>

@@ -230,18 +230,61 @@ def test_linear_every_lds32_config(mt, nt, st, splits, monkeypatch):
 GEMV_RING_CONFIGS = [(4, 2, 3), (4, 2, 4), (4, 4, 3), (8, 1, 3), (8, 2, 3), (4, 1, 4)]
 
 
-@pytest.mark.parametrize("fq", [0, 1])
+@pytest.mark.parametrize("fq,pa", [(0, 0), (1, 0), (0, 1)])
 @pytest.mark.parametrize("M", [1, 16, 17, 32])
 @pytest.mark.parametrize("w,nt,d", GEMV_RING_CONFIGS)
-def test_linear_every_gemv_ring_config(w, nt, d, M, fq, monkeypatch):
-    # fq = 1: the activation is quantized inside the kernel (x rows through the ring)
+def test_linear_every_gemv_ring_config(w, nt, d, M, fq, pa, monkeypatch):
+    # fq = 1: the activation is quantized inside the kernel (x rows through the ring);
+    # pa = 1: the quantizer pass writes it packed like a weight
     K, N = 1152, 400
-    monkeypatch.setenv("FQL_PLAN", f"kind=4,waves={w},nt={nt},st={d},fq={fq}")
+    monkeypatch.setenv("FQL_PLAN", f"kind=4,waves={w},nt={nt},st={d},fq={fq},pa={pa}")
     plan = fql.linear_plan(M, N, K)
-    want = f"gemv_ring_kernel<W={w},MT={(M + 15) // 16},NT={nt},D={d},FQ={fq}>"
+    want = f"gemv_ring_kernel<W={w},MT={(M + 15) // 16},NT={nt},D={d},FQ={fq},PA={pa}>"
     if want not in plan:
         pytest.skip(f"{want} not built: {plan}")
-    _run_case("tiny", M, K, N, 0, True, label=f"gemv_ring<{w},{nt},{d},fq={fq}>")
+    _run_case("tiny", M, K, N, 0, True, label=f"gemv_ring<{w},{nt},{d},fq={fq},pa={pa}>")
+
+
+GEMV_RING_PA_CONFIGS = [(8, 1, 4), (8, 1, 6), (16, 1, 3), (8, 2, 4), (4, 4, 4), (8, 1, 3), (8, 2, 3),
+                        (4, 4, 3)]
+
+
+@pytest.mark.parametrize("M", [1, 16, 17, 32])
+@pytest.mark.parametrize("w,nt,d", GEMV_RING_PA_CONFIGS)
+def test_linear_every_packed_activation_ring_config(w, nt, d, M, monkeypatch):
+    # configurations built only for the packed activation (smaller ring stages)
+    K, N = 1920, 400
+    monkeypatch.setenv("FQL_PLAN", f"kind=4,waves={w},nt={nt},st={d},pa=1")
+    plan = fql.linear_plan(M, N, K)
+    want = f"gemv_ring_kernel<W={w},MT={(M + 15) // 16},NT={nt},D={d},FQ=0,PA=1>"
+    if want not in plan:
+        pytest.skip(f"{want} not built: {plan}")
+    _run_case("tiny", M, K, N, 0, True, label=f"gemv_ring<{w},{nt},{d},pa=1>")
+
+
+@pytest.mark.parametrize("M,K,hb", [(1, 1040, 0), (5, 4096, 0), (16, 1040, 16), (17, 2064, 0),
+                                    (32, 4096, 128), (8, 14336, 0), (24, 3072, 64)])
+def test_linear_packed_activation_equals_xhat(M, K, hb, monkeypatch):
+    # the packed activation holds the same codes and scales as x_hat's dequantized
+    # values, so the small-M ring gives bit-identical outputs either way (K with a
+    # ragged tail past the last 128-chunk; rotations go through the same quantizer)
+    N = 400
+    xb = synthetic.activations("normal", M, K, config="decode", seed=31)
+    x32 = synthetic.bf16_bits_to_f32(xb)
+    gx = Q.global_scale_from_amax(Q.amax_for_calibration(x32, hb))
+    W, gw, wc, ws = weight_case("decode", N, K, hb)
+    alpha = alpha_of(gx, gw)
+    announce(f"ring packed activation M={M} K={K} hb={hb}")
+    wobj, _, _ = _gpu_weight(W, gw, hb, gx)
+    xd = bf16_bits_to_dev(xb)
+    outs = {}
+    for pa in (0, 1):
+        monkeypatch.setenv("FQL_PLAN", f"kind=4,waves=4,nt=2,st=3,pa={pa}")
+        assert f"PA={pa}>" in fql.linear_plan(M, N, K), fql.linear_plan(M, N, K)
+        outs[pa] = dev_bf16_to_bits(fql.linear_nvfp4(xd, wobj, alpha=float(alpha)))
+    assert np.array_equal(outs[0], outs[1])
+    ref = Q.linear_nvfp4(*Q.quant_nvfp4(x32, gx, hb), wc, ws, alpha)
+    assert rel_frob(outs[1], ref) <= REL_FROB_TOL
 
 
 @pytest.mark.parametrize("M", [3, 24])

@@ -225,7 +225,7 @@ def test_linear_transform(M, b):
     ref = Q.linear_nvfp4(xc, xs, wc, ws, alpha)
     w = fql.NVFP4Weight.from_float(f32_to_dev(W), float(gx), weight_global_scale=float(gw),
                                    transform=_T_dev(Tb))
-    announce(f"linear transform M={M} b={b} plan={fql.linear_plan(M, N, K, aligned=False)}")
+    announce(f"linear transform M={M} b={b} plan={fql.linear_plan(M, N, K, aligned=False, transform=True)}")
     y = fql.linear_nvfp4(bf16_bits_to_dev(xb), w)
     torch.cuda.synchronize()
     err = rel_frob(dev_bf16_to_bits(y), ref)
@@ -325,6 +325,41 @@ def test_linear_dynamic(M, mode):
         torch.cuda.synchronize()
         if M > 16:  # both take x_hat plans (below, the static path may fuse the quantizer)
             assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("pa", [0, 1])
+@pytest.mark.parametrize("mode", ["none", "hadamard32", "transform64"])
+def test_linear_dynamic_small_m_ring(mode, pa, monkeypatch):
+    # the small-M ring with either activation form: the dynamic scale reaches the
+    # packed quantizer through the device scalar; a transform keeps the x_hat form
+    monkeypatch.setenv("FQL_PLAN", f"kind=4,waves=4,nt=2,st=3,pa={pa}")
+    M, K, N = 24, 2048, 640
+    xb = _x(M, K, seed=77)
+    x32 = synthetic.bf16_bits_to_f32(xb)
+    W = synthetic.weight(N, K, config="transform")
+    hb = 32 if mode == "hadamard32" else 0
+    gw = Q.global_scale_from_amax(Q.amax_for_calibration(W, hb))
+    wc, ws = Q.quant_nvfp4(W, gw, hb)
+    T = None
+    v = x32
+    if mode == "transform64":
+        Tb = _T_bits(64, seed=5)
+        v = TR.block_transform(x32, F.bf16_bits_to_f64(Tb))
+        T = _T_dev(Tb)
+    elif mode == "hadamard32":
+        v = fwht_fp32(x32, hb)
+    gx = TR.dynamic_global_scale(TR.tensor_amax(v))
+    ref = Q.linear_nvfp4(*Q.quant_nvfp4(v, gx), wc, ws, TR.dynamic_alpha(gx, gw))
+    w = fql.NVFP4Weight.from_float(f32_to_dev(W), 1.0, hadamard_block=hb,
+                                   weight_global_scale=float(gw), transform=T,
+                                   dynamic_input_scale=True)
+    announce(f"linear dynamic small-M ring {mode} pa={pa}")
+    plan = fql.linear_plan(M, N, K, aligned=False, transform=T is not None)
+    assert f"PA={pa if T is None else 0}>" in plan, plan
+    y = fql.linear_nvfp4(bf16_bits_to_dev(xb), w)
+    torch.cuda.synchronize()
+    err = rel_frob(dev_bf16_to_bits(y), ref)
+    assert err <= REL_FROB_TOL, err
 
 
 @pytest.mark.parametrize("mode", ["transform", "dynamic"])
@@ -432,7 +467,7 @@ def test_linear_transform_full_size_sampled(b, shape, M):
     gx = Q.global_scale_from_amax(TR.tensor_amax(TR.block_transform(x32s, T64)))
     xc, xs = TR.quant_nvfp4_transform(x32s, T64, gx)
     ref = Q.linear_nvfp4(xc, xs, wc, ws, alpha_of(gx, gw))
-    announce(f"linear transform full size {shape} M={M} b={b} plan={fql.linear_plan(M, N, K, aligned=False)}")
+    announce(f"linear transform full size {shape} M={M} b={b} plan={fql.linear_plan(M, N, K, aligned=False, transform=True)}")
     w = fql.NVFP4Weight.from_float(f32_to_dev(W), float(gx), weight_global_scale=float(gw),
                                    transform=_T_dev(Tb))
     y = fql.linear_nvfp4(bf16_bits_to_dev(xb), w)
