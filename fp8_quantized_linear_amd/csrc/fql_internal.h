@@ -89,6 +89,7 @@ struct GemmPlan {
   int64_t lds_bytes;  // kind 0: dynamic LDS (compact activation copy / reduction)
   int fq;             // kind 4: activation quantized inside the kernel (no x_hat pass)
   int pa;             // kind 4: the quantizer pass writes the activation packed like a weight
+  int ilv;            // kind 4: waves take interleaved chunks (wave, wave + W, ...)
   int64_t counter_bytes, xhat_bytes, partial_bytes, total_bytes;
 };
 // `aligned`: x rows are 16-byte aligned (pointer and row stride); the

@@ -262,6 +262,22 @@ def test_linear_every_packed_activation_ring_config(w, nt, d, M, monkeypatch):
     _run_case("tiny", M, K, N, 0, True, label=f"gemv_ring<{w},{nt},{d},pa=1>")
 
 
+@pytest.mark.parametrize("fq,pa", [(0, 0), (1, 0), (0, 1)])
+@pytest.mark.parametrize("M", [3, 17, 32])
+@pytest.mark.parametrize("w,nt,d", [(8, 1, 3), (4, 2, 3), (16, 1, 3)])
+def test_linear_ring_interleaved_chunks(w, nt, d, M, fq, pa, monkeypatch):
+    # waves taking chunks wave, wave + W, ... (K = 1664: 13 chunks, so some waves
+    # get one chunk fewer and with W = 16 some get none)
+    K, N = 1664, 272
+    monkeypatch.setenv("FQL_PLAN", f"kind=4,waves={w},nt={nt},st={d},fq={fq},pa={pa},il=1")
+    plan = fql.linear_plan(M, N, K)
+    want = f"gemv_ring_kernel<W={w},MT={(M + 15) // 16},NT={nt},D={d},FQ={fq},PA={pa}>"
+    if want not in plan:
+        pytest.skip(f"{want} not built: {plan}")
+    assert plan.endswith("chunks=interleaved"), plan
+    _run_case("tiny", M, K, N, 0, True, label=f"gemv_ring<{w},{nt},{d},fq={fq},pa={pa}> interleaved")
+
+
 @pytest.mark.parametrize("M,K,hb", [(1, 1040, 0), (5, 4096, 0), (16, 1040, 16), (17, 2064, 0),
                                     (32, 4096, 128), (8, 14336, 0), (24, 3072, 64)])
 def test_linear_packed_activation_equals_xhat(M, K, hb, monkeypatch):
