@@ -933,24 +933,42 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
     }
   }
 
-  // LDS load number e (0 <= e < L) of chunk c into stage sg; chunks past the
-  // range are clamped (a static number of loads per chunk)
-  auto issue_one = [&](LdsStage32<MT, NT>& sg, int64_t c, int e) {
+  // The scalar bases of chunk c's loads into stage sg, computed once per chunk
+  // (chunks past the range are clamped: a static number of loads per chunk).
+  struct Refill {
+    const uint8_t* a;  // activation row tile 0 of the chunk
+    const uint8_t* q;  // weight codes of the chunk
+    const uint8_t* s;  // the chunk's scale dword column
+    uint32_t la, lq, ls;  // this wave's LDS destinations in the stage
+  };
+  const int64_t a_tile_stride = (Kp / 32) * 1024;  // bytes between 16-row x_hat tiles
+  auto refill_of = [&](LdsStage32<MT, NT>& sg, int64_t c) -> Refill {
     c = c < c_end ? c : c_end - 1;
+    Refill r;
+    r.a = uniform_ptr(a_base + c * 4096);
+    r.q = uniform_ptr(wcodes + c * 1024);
+    r.s = uniform_ptr(wscales + (c >> 2) * 512 + (c & 3) * 4);
+    r.la = __builtin_amdgcn_readfirstlane(lds_offset(&sg.a[wave][0]));
+    r.lq = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bq[wave * NT * 2][0]));
+    r.ls = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bs[wave * NT * 2][0]));
+    return r;
+  };
+  // LDS load number e (0 <= e < L) of a chunk
+  auto issue_one = [&](const Refill& r, int e) {
     if (e < 2 * MT) {
-      lds_load16(a_base + ((int64_t)e * (Kp / 32) + c * 4) * 1024, a_voff, lds_offset(&sg.a[e * 4 + wave][0]));
+      lds_load16(r.a + e * a_tile_stride, a_voff, r.la + e * 4 * 1024);
     } else if (e < 2 * MT + 2 * NT) {
-      const int b = (e - 2 * MT) / 2, h = (e - 2 * MT) % 2;
-      lds_load16(wcodes + c * 1024, q_voff[b][h], lds_offset(&sg.bq[(wave * NT + b) * 2 + h][0]));
+      const int bh = e - 2 * MT;  // (b, h) = (bh / 2, bh % 2)
+      lds_load16(r.q, q_voff[bh / 2][bh % 2], r.lq + bh * 1024);
     } else {
-      const int b = (e - 2 * MT - 2 * NT) / 2, h = (e - 2 * MT - 2 * NT) % 2;
-      lds_load4(wscales + (c >> 2) * 512 + (c & 3) * 4, s_voff[b][h],
-                lds_offset(&sg.bs[(wave * NT + b) * 2 + h][0]));
+      const int bh = e - 2 * MT - 2 * NT;
+      lds_load4(r.s, s_voff[bh / 2][bh % 2], r.ls + bh * 256);
     }
   };
   auto issue = [&](LdsStage32<MT, NT>& sg, int64_t c) {
+    const Refill r = refill_of(sg, c);
 #pragma unroll
-    for (int e = 0; e < L; ++e) issue_one(sg, c, e);
+    for (int e = 0; e < L; ++e) issue_one(r, e);
   };
 
   float16v acc[MT][NT];
@@ -1009,13 +1027,14 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
   // refill (when given) receives chunk rc's loads, spread over the seven steps
   // so that the address unit works while the MFMAs run
   auto steps0to6 = [&](const LdsStage32<MT, NT>& sg, LdsStage32<MT, NT>& refill, int64_t rc) {
+    const Refill rf = refill_of(refill, rc);
 #pragma unroll
     for (int s = 0; s < 7; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
 #pragma unroll
       for (int a = 0; a < MT; ++a) af[nxt][a] = a_frag(sg, a, s + 1);
 #pragma unroll
-      for (int e = s * L / 7; e < (s + 1) * L / 7; ++e) issue_one(refill, rc, e);
+      for (int e = s * L / 7; e < (s + 1) * L / 7; ++e) issue_one(rf, e);
       __builtin_amdgcn_sched_barrier(0);
       dequant(nxt, s + 1);
       mfmas(cur);
