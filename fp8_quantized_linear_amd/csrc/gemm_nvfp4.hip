@@ -1433,8 +1433,7 @@ bool lds32_config_built(int mt, int nt, int st) {
 // Further (W, MT, NT, D) configurations built only with the packed activation,
 // whose stages are small enough for more waves or deeper rings.
 #define FQL_GEMV_RING_PA_CONFIGS(X) \
-  X(8, 1, 1, 4) X(8, 1, 1, 6) X(16, 1, 1, 3) X(8, 1, 2, 4) X(4, 1, 4, 4) X(8, 2, 1, 3) X(8, 2, 1, 4) \
-  X(4, 2, 4, 3) X(8, 2, 2, 3)
+  X(8, 1, 1, 4) X(16, 1, 1, 3) X(8, 2, 1, 3) X(8, 2, 1, 4) X(4, 2, 4, 3) X(8, 2, 2, 3)
 
 bool gemv_ring_config_built(int w, int mt, int nt, int d, bool packed_a) {
 #define FQL_X(A, B, C, E) if (w == A && mt == B && nt == C && d == E) return true;

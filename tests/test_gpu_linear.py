@@ -245,8 +245,7 @@ def test_linear_every_gemv_ring_config(w, nt, d, M, fq, pa, monkeypatch):
     _run_case("tiny", M, K, N, 0, True, label=f"gemv_ring<{w},{nt},{d},fq={fq},pa={pa}>")
 
 
-GEMV_RING_PA_CONFIGS = [(8, 1, 4), (8, 1, 6), (16, 1, 3), (8, 2, 4), (4, 4, 4), (8, 1, 3), (8, 2, 3),
-                        (4, 4, 3)]
+GEMV_RING_PA_CONFIGS = [(8, 1, 4), (16, 1, 3), (8, 1, 3), (8, 2, 3), (4, 4, 3)]
 
 
 @pytest.mark.parametrize("M", [1, 16, 17, 32])
