@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests fail loudly on a GPU machine if the library is missing; on a host
+    # GPU tests fail loudly on a machine with a GPU if the library is missing; on a host
     # without a GPU they are skipped (the CPU suite runs with -m "not gpu").
     try:
         import torch
