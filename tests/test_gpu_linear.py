@@ -277,6 +277,17 @@ def test_linear_ring_interleaved_chunks(w, nt, d, M, fq, pa, monkeypatch):
     _run_case("tiny", M, K, N, 0, True, label=f"gemv_ring<{w},{nt},{d},fq={fq},pa={pa}> interleaved")
 
 
+@pytest.mark.parametrize("cfg", ["waves=8,nt=1,st=3", "waves=4,nt=4,st=3", "waves=16,nt=1,st=3"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (8, 17, 16), (32, 33, 48), (17, 1, 112), (3, 200, 144)])
+def test_linear_ring_edge_shapes(M, N, K, cfg, monkeypatch):
+    # one chunk or less of K (most waves have no chunk), one or a few columns
+    monkeypatch.setenv("FQL_PLAN", f"kind=4,{cfg},pa=1")
+    plan = fql.linear_plan(M, N, K)
+    if "gemv_ring_kernel" not in plan:
+        pytest.skip(f"not built: {plan}")
+    _run_case("tiny", M, K, N, 0, True, label=f"ring edge {plan}")
+
+
 @pytest.mark.parametrize("M,K,hb", [(1, 1040, 0), (5, 4096, 0), (16, 1040, 16), (17, 2064, 0),
                                     (32, 4096, 128), (8, 14336, 0), (24, 3072, 64)])
 def test_linear_packed_activation_equals_xhat(M, K, hb, monkeypatch):
