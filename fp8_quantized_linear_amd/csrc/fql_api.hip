@@ -212,12 +212,11 @@ int fql_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* by
   if (!bytes) return fail(FQL_ERR_INVALID, "null pointer");
   if (M < 1 || N < 1 || K < 16 || K % 16 != 0)
     return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 16");
-  // every plan a call of this shape may take: aligned rows, unaligned rows, and
-  // the transform's x_hat-only operand
+  // either plan a call of this shape may take: aligned or unaligned rows (the
+  // transform and dynamic-scale calls take the unaligned one)
   const int64_t a = fql::plan_gemm_nvfp4(M, N, K, true).total_bytes;
   const int64_t u = fql::plan_gemm_nvfp4(M, N, K, false).total_bytes;
-  const int64_t t = fql::plan_gemm_nvfp4(M, N, K, false, true).total_bytes;
-  *bytes = (size_t)std::max(a, std::max(u, t));
+  *bytes = (size_t)std::max(a, u);
   return ok();
 }
 
@@ -225,9 +224,16 @@ int fql_linear_nvfp4_describe(int64_t M, int64_t N, int64_t K, int aligned, char
                               size_t buf_len) {
   if (M < 1 || N < 1 || K < 16 || K % 16 != 0)
     return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 16");
+  // a transform call plans as unaligned rows; its quantizer is the transform kernel
   const bool transform = (aligned & 2) != 0;
-  write_reason(buf, buf_len,
-               fql::describe_plan(fql::plan_gemm_nvfp4(M, N, K, !transform && (aligned & 1) != 0, transform)));
+  std::string d = fql::describe_plan(fql::plan_gemm_nvfp4(M, N, K, !transform && (aligned & 1) != 0));
+  if (transform) {
+    for (const char* q : {"quant_nvfp4_apack_kernel", "quant_nvfp4_xhat_kernel"}) {
+      const size_t at = d.find(q);
+      if (at != std::string::npos) d.replace(at, std::strlen(q), "transform_quant_kernel");
+    }
+  }
+  write_reason(buf, buf_len, d);
   return ok();
 }
 
@@ -388,9 +394,9 @@ int linear_nvfp4_extras(const void* x, int64_t M, int64_t K, int64_t ldx, float 
   if (reinterpret_cast<uintptr_t>(w_packed) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(FQL_ERR_INVALID, "packed weight must be 16-byte and workspace 256-byte aligned");
-  // a plan that writes x_hat or the packed activation (the fused small-M kernel
-  // quantizes with a host-side scale); the transform's quantizer writes x_hat only
-  const fql::GemmPlan plan = fql::plan_gemm_nvfp4(M, N, K, false, T != nullptr);
+  // a plan whose quantizer pass writes the GEMM's operand (x_hat or the packed
+  // activation), since the fused small-M kernel quantizes with a host-side scale
+  const fql::GemmPlan plan = fql::plan_gemm_nvfp4(M, N, K, false);
   if (workspace_bytes < (size_t)plan.total_bytes)
     return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
                 (long long)plan.total_bytes);

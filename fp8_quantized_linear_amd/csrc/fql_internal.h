@@ -95,9 +95,7 @@ struct GemmPlan {
 // `aligned`: x rows are 16-byte aligned (pointer and row stride); the
 // fused small-M kernel needs it. Workspace sizes of both kinds are covered by
 // the aligned=false plan, which never needs less.
-// `xhat_only`: the activation operand comes from the transform's quantizer,
-// which writes x_hat only (no packed activation form).
-GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool xhat_only = false);
+GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned);
 
 // Whether gemm_tiled_kernel<mt, nt, wm> / gemm_lds_kernel<mt, nt, st> is built
 // into the library.
@@ -124,7 +122,9 @@ constexpr int64_t kWorkspaceScalarOffset = kWorkspaceCounterBytes - kWorkspaceSc
 // One launch of the transform kernel. mode 0: canonical codes [M][K/2] and
 // scales [M][K/16]; 1: x_hat (float16, GEMM A-fragment order, rows_out = Mp
 // rows and Kp columns, zero padded); 2: max |v| into the kAmaxSlots partial
-// maxima at amax (zeroed first); 3: float32 values v [M][ldv].
+// maxima at amax (zeroed first); 3: float32 values v [M][ldv]; 4: the packed
+// activation (the packed weight layout with rows_out = Mp rows, a multiple of
+// 16, and Kp columns, zero padded) at xhat.
 struct TransformArgs {
   int mode;
   const uint16_t* x;

@@ -1137,7 +1137,7 @@ static constexpr int64_t kCounterBytes = kWorkspaceCounterBytes;
 static constexpr int64_t kGemvMaxLds = 64 * 1024;    // compact activation copy in LDS
 static constexpr int64_t kGemvMaxRedundantBlocks = 1 << 20;  // workgroups x 16-blocks quantized
 
-GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool xhat_only) {
+GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
   GemmPlan p{};
   const PackedDims d = packed_dims(N, K);
   p.Np = d.Np;
@@ -1180,11 +1180,10 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool xha
     // Workgroup tile (WM*MT*16) x ((4/WM)*NT*16); kind 2 always has WM = 1.
     // Defaults (measured on the decode and prefill layer shapes): up to 32
     // rows the per-wave-ring kernel, except wide layers with short K (gate_up)
-    // above 16 rows or without the packed activation, which stream better
-    // through the register-staged tiled kernel; from 33 rows on the LDS-ring
-    // kernel on 32x32 MFMAs.
+    // above 16 rows, which stream better through the register-staged tiled
+    // kernel; from 33 rows on the LDS-ring kernel on 32x32 MFMAs.
     const bool wide_short = N >= 16384 && p.Kp < 8192;
-    p.kind = M <= 32 ? (wide_short && (M > 16 || xhat_only) ? 1 : 4) : 3;
+    p.kind = M <= 32 ? (wide_short && M > 16 ? 1 : 4) : 3;
     if (ov.kind >= 1 && ov.kind <= 4) p.kind = ov.kind;
     if (p.kind == 4) {
       // per-wave rings: W waves split K, NT tiles per workgroup, D chunks in flight
@@ -1200,9 +1199,8 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool xha
       // workgroup; measured slower than the separate x_hat pass on the decode
       // shapes (e.g. qkv M = 32: 15.9 vs 12.5 us), so it is opt-in.
       const int fq = aligned && K % 128 == 0 && ov.fq == 1 ? 1 : 0;
-      // the quantizer pass writes the activation packed like a weight (not
-      // for the transform's quantizer, which writes x_hat)
-      const int pa = fq || xhat_only ? 0 : ov.pa >= 0 ? ov.pa : 1;
+      // the quantizer pass (or the transform's) writes the activation packed like a weight
+      const int pa = fq ? 0 : ov.pa >= 0 ? ov.pa : 1;
       if (p.mt <= 2 && gemv_ring_config_built(p.waves, p.mt, p.nt, p.st, pa != 0)) {
         p.wm = 1;
         p.fq = fq;
@@ -1476,13 +1474,22 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
   }
   if (p.kind == 0) return hipErrorInvalidValue;  // caller re-plans unaligned inputs as kind 1
   const bool fused = ex == nullptr && p.kind == 4 && p.fq && hb == 0 && aligned && K % 128 == 0;
-  // the packed activation comes from the x_hat quantizer's packed mode (not the transform's)
-  const bool packed_a = !fused && p.kind == 4 && p.pa && (ex == nullptr || ex->T == nullptr);
+  // the packed activation comes from the packed mode of the quantizer pass or of the transform
+  const bool packed_a = !fused && p.kind == 4 && p.pa;
   if (packed_a) {
     if (p.Mp != 16 * p.mt) return hipErrorInvalidValue;
-    const hipError_t e = launch_quant_nvfp4_apack(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp,
-                                                  reinterpret_cast<uint8_t*>(xhat),
-                                                  ex != nullptr ? ex->g_dev : nullptr, st);
+    hipError_t e;
+    if (ex != nullptr && ex->T != nullptr) {
+      TransformArgs ta{};
+      ta.mode = 4;  // packed activation
+      ta.x = x; ta.M = M; ta.K = K; ta.ldx = ldx; ta.aligned = ex->t_aligned;
+      ta.T = ex->T; ta.b = hb; ta.g = g; ta.g_dev = ex->g_dev;
+      ta.xhat = xhat; ta.rows_out = p.Mp; ta.Kp = p.Kp;
+      e = launch_transform_nvfp4(ta, st);
+    } else {
+      e = launch_quant_nvfp4_apack(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp, reinterpret_cast<uint8_t*>(xhat),
+                                   ex != nullptr ? ex->g_dev : nullptr, st);
+    }
     if (e != hipSuccess) return e;
   } else if (!fused) {
     hipError_t e;

@@ -41,7 +41,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t uint2v __attribute__((ext_vector_type(2)));
 
-enum TrMode { TR_CANON = 0, TR_XHAT = 1, TR_AMAX = 2, TR_VALUES = 3 };
+enum TrMode { TR_CANON = 0, TR_XHAT = 1, TR_AMAX = 2, TR_VALUES = 3, TR_PACKED = 4 };
 
 template <int B>
 struct TrShape {
@@ -139,6 +139,22 @@ __global__ __launch_bounds__(256) void transform_quant_kernel(
 
   const int nchunks = K / B;
   const uint16_t* xrow = x + (int64_t)(row_ok ? m : M - 1) * ldx + q * (S::KD / 4);
+  // TR_PACKED: 16-block kb of row r into the packed weight layout with
+  // mtiles * 16 rows (tile t = r/16, row n = r%16, chunk ch = kb/8, step
+  // j = (kb%8)/2, half h = kb%2: lo to lane (2h)*16 + n and hi to lane
+  // (2h+1)*16 + n, dword j of the chunk's 16-byte slot; the scale to slot
+  // 2n + h, byte 4(ch%4) + j of the 4-chunk scale group)
+  auto store_packed = [&](int r, int kb, uint32_t lo, uint32_t hi, uint32_t sb) {
+    const uint32_t KC = (uint32_t)Kp / 128u, KC4 = (KC + 3u) / 4u;
+    const uint32_t t = (uint32_t)r >> 4, n = (uint32_t)r & 15u, ch = (uint32_t)kb >> 3;
+    const uint32_t j = ((uint32_t)kb >> 1) & 3u, h = (uint32_t)kb & 1u;
+    uint8_t* out = reinterpret_cast<uint8_t*>(xhat);
+    uint32_t* cw32 = reinterpret_cast<uint32_t*>(out + ((size_t)(t * KC + ch) * 64u + 2u * h * 16u + n) * 16u) + j;
+    cw32[0] = lo;
+    cw32[64] = hi;  // next 16-lane group: 256 bytes on
+    out[(size_t)(mtiles * 8) * (uint32_t)Kp + ((size_t)(t * KC4 + (ch >> 2)) * 32u + 2u * n + h) * 16u +
+        4u * (ch & 3u) + j] = (uint8_t)sb;
+  };
   float wave_max = 0.0f;
 
   // ring slot n % D holds the chunk cw + n * cw_count (loads past the last
@@ -187,15 +203,19 @@ __global__ __launch_bounds__(256) void transform_quant_kernel(
         const float rcp = sd == 0.0f ? 0.0f : g / sd;
         uint32_t c16 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0] * rcp, v[1] * rcp, 1.0f, 0);
         c16 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(c16, v[2] * rcp, v[3] * rcp, 1.0f, 1);
-        if constexpr (MODE == TR_CANON) {
+        if constexpr (MODE == TR_CANON || MODE == TR_PACKED) {
           // gather the block's 8 code bytes into lane q == 0: words (q0 | q1 << 16), (q2 | q3 << 16)
           const uint32_t mine = c16 & 0xFFFFu;
           const uint32_t nb = __shfl_xor(mine, 16);
           const uint32_t lo = (q & 1) == 0 ? (mine | (nb << 16)) : 0u;
           const uint32_t hi = __shfl_xor(lo, 32);
-          if (q == 0 && row_ok) {
-            *reinterpret_cast<uint2v*>(codes + (int64_t)m * (K / 2) + (c * B + 16 * it) / 2) = uint2v{lo, hi};
-            scales[(int64_t)m * (K / 16) + c * (B / 16) + it] = (uint8_t)s;
+          if constexpr (MODE == TR_CANON) {
+            if (q == 0 && row_ok) {
+              *reinterpret_cast<uint2v*>(codes + (int64_t)m * (K / 2) + (c * B + 16 * it) / 2) = uint2v{lo, hi};
+              scales[(int64_t)m * (K / 16) + c * (B / 16) + it] = (uint8_t)s;
+            }
+          } else if (q == 0) {  // every row of the tile (rows >= M are zero)
+            store_packed(m, c * (B / 16) + it, lo, hi, s);
           }
         } else {  // TR_XHAT: e2m1(q) * s_d in float16 (exact), GEMM A-fragment order
           const _Float16 sh = (_Float16)sd;
@@ -223,6 +243,12 @@ __global__ __launch_bounds__(256) void transform_quant_kernel(
       const int nw = min(4, mtiles * cw_count - (int)blockIdx.x * 4);  // waves of this workgroup
       for (int w = 1; w < nw; ++w) b = __builtin_fmaxf(b, wg_max[w]);
       atomicMax(amax + blockIdx.x % kAmaxSlots, __float_as_uint(b));
+    }
+  }
+  if constexpr (MODE == TR_PACKED) {
+    // blocks K/16 .. Kp/16 of the tile are zero (codes and scales)
+    if (wave_live && cw == 0) {
+      for (int kb = K / 16 + q; kb < Kp / 16; kb += 4) store_packed(m, kb, 0u, 0u, 0u);
     }
   }
   if constexpr (MODE == TR_XHAT) {
@@ -312,6 +338,7 @@ hipError_t launch_transform_nvfp4(const TransformArgs& a, hipStream_t st) {
     case TR_XHAT: FQL_TRM(TR_XHAT);
     case TR_AMAX: FQL_TRM(TR_AMAX);
     case TR_VALUES: FQL_TRM(TR_VALUES);
+    case TR_PACKED: FQL_TRM(TR_PACKED);
     default: return hipErrorInvalidValue;
   }
 #undef FQL_TRM

@@ -327,11 +327,38 @@ def test_linear_dynamic(M, mode):
             assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
+@pytest.mark.parametrize("b,K", [(16, 1040), (32, 1056), (64, 1088), (128, 1152), (128, 5120)])
+@pytest.mark.parametrize("M", [1, 5, 17, 32])
+def test_linear_transform_packed_equals_xhat(b, K, M, monkeypatch):
+    # the transform kernel's packed activation and its x_hat hold the same
+    # quantized values, so the small-M ring gives identical bits with either
+    # (K not a multiple of 128: the packed blocks past K are zero)
+    N = 272
+    xb = _x(M, K, seed=M + b)
+    Tb = _T_bits(b, seed=b)
+    W = synthetic.weight(N, K, config="transform")
+    w = fql.NVFP4Weight.from_float(f32_to_dev(W), 5.0, transform=_T_dev(Tb))
+    announce(f"transform packed vs x_hat b={b} K={K} M={M}")
+    outs = []
+    for pa in (0, 1):
+        monkeypatch.setenv("FQL_PLAN", f"kind=4,waves=4,nt=2,st=3,pa={pa}")
+        assert f"PA={pa}>" in fql.linear_plan(M, N, K, aligned=False, transform=True)
+        outs.append(dev_bf16_to_bits(fql.linear_nvfp4(bf16_bits_to_dev(xb), w)))
+    assert np.array_equal(outs[0], outs[1])
+    v = TR.block_transform(synthetic.bf16_bits_to_f32(xb), F.bf16_bits_to_f64(Tb))
+    xc, xs = Q.quant_nvfp4(v, np.float32(5.0))
+    gw = np.float32(w.weight_global_scale)
+    wc, ws = Q.quant_nvfp4(W, gw)
+    ref = Q.linear_nvfp4(xc, xs, wc, ws, alpha_of(np.float32(5.0), gw))
+    assert rel_frob(outs[1], ref) <= REL_FROB_TOL
+
+
 @pytest.mark.parametrize("pa", [0, 1])
 @pytest.mark.parametrize("mode", ["none", "hadamard32", "transform64"])
 def test_linear_dynamic_small_m_ring(mode, pa, monkeypatch):
     # the small-M ring with either activation form: the dynamic scale reaches the
-    # packed quantizer through the device scalar; a transform keeps the x_hat form
+    # quantizer pass through the device scalar; under a transform the transform
+    # kernel writes the x_hat or the packed activation
     monkeypatch.setenv("FQL_PLAN", f"kind=4,waves=4,nt=2,st=3,pa={pa}")
     M, K, N = 24, 2048, 640
     xb = _x(M, K, seed=77)
@@ -355,7 +382,9 @@ def test_linear_dynamic_small_m_ring(mode, pa, monkeypatch):
                                    dynamic_input_scale=True)
     announce(f"linear dynamic small-M ring {mode} pa={pa}")
     plan = fql.linear_plan(M, N, K, aligned=False, transform=T is not None)
-    assert f"PA={pa if T is None else 0}>" in plan, plan
+    assert f"PA={pa}>" in plan, plan
+    if T is not None:
+        assert plan.startswith("transform_quant_kernel + "), plan
     y = fql.linear_nvfp4(bf16_bits_to_dev(xb), w)
     torch.cuda.synchronize()
     err = rel_frob(dev_bf16_to_bits(y), ref)
