@@ -1263,9 +1263,12 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     const int64_t groups = ngroups * mgroups;
     // Split K across workgroups only when there are too few output tiles to
     // occupy the GPU: the arrival counter of the split-K reduction costs
-    // about a microsecond plus ~0.35 us per split contending on it.
+    // about a microsecond plus ~0.35 us per split contending on it. Up to 4
+    // splits, or 6 for long K (at least 144 chunks: Qwen3-32B down at M = 256,
+    // 40 tiles, took 91 us with 6 splits against 101 us with 4).
     int64_t s = 1;
-    if (groups < 192) s = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(4, KC), 256 / groups));
+    const int64_t max_splits = KC >= 144 ? 6 : 4;
+    if (groups < 192) s = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(max_splits, KC), 256 / groups));
     if (ov.splits) s = std::min<int64_t>(ov.splits, KC);
     // the LDS ring runs deeper when a split-K tile has few chunks to hide latency in
     if (p.kind == 2 && !ov.st && s > 1 && lds_config_built(p.mt, p.nt, 4)) p.st = 4;
