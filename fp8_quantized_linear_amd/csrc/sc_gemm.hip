@@ -160,12 +160,21 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
   // Which kind of item slot j holds is known at compile time once the loops
   // are unrolled whenever all waves' item j are code tiles (or all MX scale
   // quads): then width and stride are constants and no branch is emitted.
-  auto issue_item = [&](Stage& sg, int64_t c, int j) {
+  // For those the chunk's offset rides in the per-lane offset (one vector add
+  // per chunk and stride, see ChunkOffsets) instead of a 64-bit scalar add per
+  // load; a tile's KC chunks stay far below 4 GiB.
+  struct ChunkOffsets {
+    uint32_t code, scale;  // lane*16 + c*CHUNK, lane*4 + c*256
+  };
+  auto offsets_of = [&](int64_t c) -> ChunkOffsets {
+    return ChunkOffsets{(uint32_t)lane * 16u + (uint32_t)c * (uint32_t)CHUNK, (uint32_t)lane * 4u + (uint32_t)c * 256u};
+  };
+  auto issue_item = [&](Stage& sg, int64_t c, const ChunkOffsets& o, int j) {
     const uint32_t lds = lds_offset(&sg) + it_lds[j];
     if (NW * j + NW <= NA + NB) {
-      lds_load16(it_src[j] + (uint32_t)c * (uint32_t)CHUNK, lane * 16, lds);
+      lds_load16(it_src[j], o.code, lds);
     } else if (NW * j >= NA + NB && T::MX) {
-      lds_load4(it_src[j] + (uint32_t)c * 256u, lane * 4, lds);
+      lds_load4(it_src[j], o.scale, lds);
     } else {
       const uint8_t* src = it_src[j] + (uint32_t)c * it_stride[j];
       if (it_wide[j]) lds_load16(src, it_voff[j], lds);
@@ -182,6 +191,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
   // one chunk: fragments from stage sg, MFMAs, and the refill loads of the
   // stage `refill` (chunk rc) spread between the MFMAs
   auto compute = [&](const Stage& sg, Stage& refill, int64_t rc) {
+    const ChunkOffsets ro = offsets_of(rc);
     int8v b[NTW];
     int sb[NTW];
 #pragma unroll
@@ -223,7 +233,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
       for (int nt = 0; nt < NTW; ++nt) {
 #pragma unroll
         for (int j = 0; j < L; ++j)
-          if ((j * P) / L == p) issue_item(refill, rc, j);
+          if ((j * P) / L == p) issue_item(refill, rc, ro, j);
         if (T::BLOCK) {
           const float4v z = float4v{0.f, 0.f, 0.f, 0.f};
           const float4v part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[nt], z, 0, 0, 0, 127, 0, 127);
@@ -245,8 +255,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
 #pragma unroll
   for (int p0 = 0; p0 < ST - 1; ++p0) {
     const int64_t c = c_begin + p0 < c_end ? c_begin + p0 : c_end - 1;
+    const ChunkOffsets o = offsets_of(c);
 #pragma unroll
-    for (int j = 0; j < L; ++j) issue_item(stage[p0], c, j);
+    for (int j = 0; j < L; ++j) issue_item(stage[p0], c, o, j);
   }
   for (int i0 = 0; i0 < nch; i0 += ST) {
 #pragma unroll
