@@ -150,9 +150,13 @@ def linear_nvfp4(x_codes, x_scales, w_codes, w_scales, alpha, bias=None):
 
 def linear_nvfp4_f64(x_codes, x_scales, w_codes, w_scales, alpha, bias=None):
     """The float64 value of the linear layer before the bfloat16 cast."""
-    xh = dequant_nvfp4(x_codes, x_scales)
-    wh = dequant_nvfp4(w_codes, w_scales)
-    y = np.float64(alpha) * (xh @ wh.T)
+    return linear_dequantized_f64(dequant_nvfp4(x_codes, x_scales),
+                                  dequant_nvfp4(w_codes, w_scales), alpha, bias)
+
+
+def linear_dequantized_f64(x_hat, w_hat, alpha, bias=None):
+    """G2 on operands already decoded by G1 (float64 x_hat [M, K], w_hat [N, K])."""
+    y = np.float64(alpha) * (np.asarray(x_hat, np.float64) @ np.asarray(w_hat, np.float64).T)
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float64)[None, :]
     return y

@@ -325,3 +325,58 @@ def test_hadamard_layer_invariance_through_quantization():
     assert np.allclose((x @ h.T) @ (w @ h.T).T, x.astype(np.float64) @ w.T, rtol=1e-5, atol=1e-6)
     ref = x.astype(np.float64) @ w.astype(np.float64).T
     assert np.linalg.norm(y - ref) / np.linalg.norm(ref) < 0.25
+
+
+# ---------------------------------------------------------------------------
+# calibration amax after the rotation ("QUTLASS NVFP4 online transforms",
+# Implementation: the block-diagonal rotation is applied before quantization,
+# so the global scale is calibrated on rotated values)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("b", [16, 32, 64, 128])
+def test_calibration_amax_is_that_of_the_dense_rotation(b):
+    # against the dense float64 product (H_b / sqrt(b)) v per chunk, within the
+    # FWHT's float32 error bound (log2(b) add stages and one multiply)
+    r = np.random.default_rng(700 + b)
+    K = 8 * b
+    x = synthetic.bf16_bits_to_f32(synthetic.f32_to_bf16_bits(
+        r.standard_t(3, size=(24, K)).astype(np.float32)))
+    h = sylvester(b).astype(np.float64) / np.sqrt(b)
+    dense = (x.astype(np.float64).reshape(24, K // b, b) @ h.T).reshape(24, K)
+    bound = (np.log2(b) + 2) * 2.0 ** -24 * np.abs(x.astype(np.float64)).reshape(
+        24, K // b, b).sum(-1).max()
+    got = float(Q.amax_for_calibration(x, b))
+    assert abs(got - np.abs(dense).max()) <= bound
+    # the rotation changes the answer for these inputs, so skipping it fails
+    assert abs(float(Q.amax_for_calibration(x, 0)) - np.abs(dense).max()) > 100 * bound
+
+
+@pytest.mark.parametrize("b", [16, 32, 64, 128])
+def test_calibration_amax_closed_form_constant_chunk(b):
+    # a chunk of equal values c rotates to (c * b, 0, ..., 0) / sqrt(b): the FWHT
+    # sums are exact, so the rotated amax is fl32(fl32(c * b) * fl32(1/sqrt(b)))
+    c = np.float32(0.75)
+    x = np.zeros((3, 4 * b), np.float32)
+    x[1, 2 * b:3 * b] = c
+    x[2, :b] = -c / 2
+    cb = np.float32(1.0 / np.sqrt(np.float64(b)))
+    expect = np.float32(np.float32(c * b) * cb)
+    assert Q.amax_for_calibration(x, b) == expect
+    if b in (16, 64):  # 1/sqrt(b) is a power of two: exactly c * sqrt(b)
+        assert float(expect) == 0.75 * math.sqrt(b)
+
+
+@pytest.mark.parametrize("b", [16, 32, 64, 128])
+def test_calibrated_rotated_scale_hits_the_format_maximum(b):
+    # global-scale invariant on rotated values: the block holding the rotated
+    # amax gets scale 448 (0x7E) and that element code +-6
+    r = np.random.default_rng(800 + b)
+    x = (r.standard_t(3, size=(16, 4 * b)) * 3).astype(np.float32)
+    g = Q.global_scale_from_amax(Q.amax_for_calibration(x, b))
+    codes, scales = Q.quant_nvfp4(x, g, b)
+    h = sylvester(b).astype(np.float64) / np.sqrt(b)
+    dense = (x.astype(np.float64).reshape(16, 4, b) @ h.T).reshape(16, 4 * b)
+    m, k = np.unravel_index(np.argmax(np.abs(dense)), dense.shape)
+    assert scales[m, k // 16] == 0x7E
+    assert Q.unpack_nibbles(codes)[m, k] & 7 == 7
+    assert np.all(scales <= 0x7E)
