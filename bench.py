@@ -1,21 +1,31 @@
 """Benchmark of the NVFP4 W4A4 linear layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode] [--format nvfp4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload serving] [--format nvfp4]
 
 A step is one pass of the whole hot path (activation quantize -> block-scaled
 GEMM -> alpha/bias/bf16 epilogue, i.e. one linear call) over every case of the
-workload. The default workload is the decode-shaped Llama-3.1-8B set: M in
-{1, 8, 32, 128} for qkv (K=4096, N=6144), gate_up (4096, 28672) and down
-(14336, 4096), with bias: 12 linear calls per step. Inputs are seeded
-synthetic tensors (the `synthetic` module); weights are quantized and packed
-on the GPU before timing and rotated through enough copies that every call
-reads its weight from HBM, not from the 256 MB last-level cache.
+workload. The default workload, `serving`, spans M = 1..8192:
+  * decode: Llama-3.1-8B qkv (K=4096, N=6144), gate_up (4096, 28672) and down
+    (14336, 4096) at M in {1, 8, 32, 128}, with bias (12 calls);
+  * prefill: the same shapes at M in {2048, 8192}, 1% outlier channels (6 calls);
+  * hadamard: Qwen3-32B gate_up (5120, 51200) and down (25600, 5120) at M in
+    {1, 256, 4096} with the block-diagonal Hadamard rotation, b in
+    {16, 32, 64, 128} (24 calls).
+Inputs are seeded synthetic tensors (the `synthetic` module); weights are
+quantized and packed on the GPU before timing and rotated through enough
+copies that every call reads its weight from HBM, not from the 256 MB
+last-level cache. Each step is one HIP graph replay.
 
 Prints one JSON line. `value` is whole-step TFLOP/s (2*M*N*K summed over the
-step / step time). `roofline` describes the GEMM calls against HBM bandwidth
-(algorithmic bytes: 0.5625 B per weight element + 2 B per activation and
-output element + bias), timed per call with HIP events on the launch stream.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+step / step time). `per_case` gives every call's time with its GB/s and HBM
+fraction (algorithmic bytes: 0.5625 B per weight element + 2 B per activation
+and output element + bias) and its TFLOP/s against the dense float16 MFMA
+peak (the exact NVFP4 path multiplies dequantized float16 operands) and the
+FP4 peak. `roofline` describes the kernel carrying the most time per step,
+timed alone with HIP events on its launch stream. `calibration` holds what a
+plain streaming read and MFMA loops reach on this GPU. `cpu_baseline` times
+the CPU oracle on a bounded sample of the same workload, on all host cores and
+on one thread.
 
 `--format mxfp4|mxfp8|fp8|fp8_block` runs one of the sibling layers (scaled
 FP4/FP8 MFMA) instead; their natural workload is `siblings` (K=4096,
@@ -24,9 +34,12 @@ MXFP8 1.03125, per-tensor FP8 1, block FP8 1 + 4/128^2.
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
+import statistics
+import subprocess
 import sys
 import time
 
@@ -34,17 +47,21 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 FP4_PEAK_TFLOPS = 10100.0
+FP8_PEAK_TFLOPS = 5000.0
 F16_PEAK_TFLOPS = 2500.0
 ROTATE_BYTES = 512 << 20
 
-WORKLOAD_KEYS = ("decode", "prefill", "hadamard", "tiny", "siblings", "transform")
+SINGLE_WORKLOADS = ("decode", "prefill", "hadamard", "tiny", "siblings", "transform")
+COMPOSITE_WORKLOADS = {"serving": ("decode", "prefill", "hadamard")}
+WORKLOAD_KEYS = tuple(COMPOSITE_WORKLOADS) + SINGLE_WORKLOADS
 FORMAT_KEYS = ("nvfp4", "mxfp4", "mxfp8", "fp8", "fp8_block")
 # algorithmic weight bytes per element: code + scale bytes per element
 WEIGHT_BYTES = {"nvfp4": 0.5 + 1.0 / 16, "mxfp4": 0.5 + 1.0 / 32, "mxfp8": 1.0 + 1.0 / 32,
                 "fp8": 1.0, "fp8_block": 1.0 + 4.0 / (128 * 128)}
 # dense MFMA peak the format runs on (TFLOP/s): NVFP4 multiplies exactly
 # dequantized float16 operands; the others run on the scaled FP4 / FP8 MFMA
-MFMA_PEAK = {"nvfp4": 2500.0, "mxfp4": 10100.0, "mxfp8": 5000.0, "fp8": 5000.0, "fp8_block": 5000.0}
+MFMA_PEAK = {"nvfp4": F16_PEAK_TFLOPS, "mxfp4": FP4_PEAK_TFLOPS, "mxfp8": FP8_PEAK_TFLOPS,
+             "fp8": FP8_PEAK_TFLOPS, "fp8_block": FP8_PEAK_TFLOPS}
 FORMAT_DTYPE = {
     "nvfp4": "nvfp4 (e2m1 x e4m3/16) -> f16 MFMA, f32 accumulate, bf16 out",
     "mxfp4": "mxfp4 (e2m1 x e8m0/32) -> scaled fp4 MFMA, f32 accumulate, bf16 out",
@@ -53,6 +70,9 @@ FORMAT_DTYPE = {
     "fp8_block": "fp8 e4m3, 1x128 / 128x128 f32 scales -> fp8 MFMA + f32 promotion, bf16 out",
 }
 WORKLOAD_NAMES = {
+    "serving": "serving: Llama-3.1-8B qkv/gate_up/down decode M=1,8,32,128 (bias) + prefill "
+               "M=2048,8192 (1% outlier channels) + Qwen3-32B gate_up/down M=1,256,4096 with "
+               "block-diagonal Hadamard b=16,32,64,128 (M=1..8192, 42 calls)",
     "decode": "decode: Llama-3.1-8B qkv/gate_up/down at M=1,8,32,128, bias",
     "prefill": "prefill: Llama-3.1-8B qkv/gate_up/down at M=2048,8192, 1% outlier channels",
     "hadamard": "hadamard: Qwen3-32B gate_up/down at M=1,256,4096, block-diagonal Hadamard",
@@ -64,7 +84,8 @@ WORKLOAD_NAMES = {
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_llama8b_hbm_traffic.md")
+TRAFFIC_SUMMARIES = [os.path.join(ROOT, "profiles", f) for f in
+                     ("prefill_llama8b_hbm_traffic.md", "decode_llama8b_hbm_traffic.md")]
 
 
 def source_digest():
@@ -78,24 +99,28 @@ def source_digest():
     return h.hexdigest()
 
 
-def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary.
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from a committed counter summary.
 
-    The summary records FETCH_SIZE + WRITE_SIZE per launch (scaled by the
-    plain-copy calibration) together with the digest of the kernel sources it
-    was taken on; once the sources differ, the figure no longer describes the
-    kernel and None is returned.
+    A summary records FETCH_SIZE + WRITE_SIZE per launch (scaled by the
+    plain-copy calibration) with the digest of the kernel sources it was taken
+    on; once the sources differ, the figure no longer describes the kernel and
+    None is returned.
     """
-    try:
-        text = open(TRAFFIC_SUMMARY).read()
-    except OSError:
-        return None
-    for line in text.splitlines():
-        if line.startswith("traffic-record: "):
-            rec = json.loads(line[len("traffic-record: "):])
-            if (rec.get("workload") == workload and rec.get("kernel") == kernel
-                    and rec.get("source_sha256") == source_digest()):
-                return rec["bytes_per_launch"]
+    digest = None
+    for path in TRAFFIC_SUMMARIES:
+        try:
+            text = open(path).read()
+        except OSError:
+            continue
+        for line in text.splitlines():
+            if line.startswith("traffic-record: "):
+                rec = json.loads(line[len("traffic-record: "):])
+                if rec.get("kernel") != kernel:
+                    continue
+                digest = digest or source_digest()
+                if rec.get("source_sha256") == digest:
+                    return rec["bytes_per_launch"]
     return None
 
 
@@ -104,21 +129,32 @@ def _alg_bytes(M, N, K, with_bias, fmt="nvfp4"):
             + (2.0 * N if with_bias else 0.0))
 
 
-def _cases(workload, hb_override=None):
+def _case_name(wl, name, M, hb):
+    tag = "b" if wl == "transform" else "hb"
+    return f"{wl}/{name}/M={M}" + (f"/{tag}={hb}" if hb else "")
+
+
+def _cases(workload, hb_override=None, only=None):
+    """(wl, M, name, K, N, hb, with_bias) of the workload's calls, optionally restricted
+    to one block size and to the case names in `only` (e.g. {"prefill/gate_up/M=8192"})."""
     import synthetic
 
     out = []
-    for M, name, K, N, hb, with_bias in synthetic.cases(workload):
-        if hb_override is not None and hb != hb_override:
-            continue
-        out.append((M, name, K, N, hb, with_bias))
+    for wl in COMPOSITE_WORKLOADS.get(workload, (workload,)):
+        for M, name, K, N, hb, with_bias in synthetic.cases(wl):
+            if hb_override is not None and hb != hb_override:
+                continue
+            if only and _case_name(wl, name, M, hb) not in only:
+                continue
+            out.append((wl, M, name, K, N, hb, with_bias))
+    if only and not out:
+        raise SystemExit(f"no case of the {workload} workload is named in {sorted(only)}")
     return out
 
 
 def _kernel_of(M, N, K, fmt="nvfp4", general=False, dynamic=False):
-    """The kernel that carries one linear call of this shape (the library's own plan;
-    the transform and dynamic-scale paths plan as unaligned calls, the transform's
-    with the x_hat operand)."""
+    """The GEMM kernel of one linear call of this shape (the library's own plan; the
+    transform and dynamic-scale paths plan as unaligned calls)."""
     import fp8_quantized_linear_amd as fql
 
     if fmt != "nvfp4":
@@ -127,13 +163,18 @@ def _kernel_of(M, N, K, fmt="nvfp4", general=False, dynamic=False):
     return plan.split(" grid=")[0].split(" + ")[-1]
 
 
-def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic=False):
+def _has_quant_pass(M, N, K):
+    import fp8_quantized_linear_amd as fql
+
+    return " + " in fql.linear_plan(M, N, K, aligned=True)
+
+
+def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic=False, only=None):
     import torch
 
     import fp8_quantized_linear_amd as fql
     import synthetic
 
-    general = workload == "transform"  # the block size is a general transform's, not a rotation's
     tmats = {}
 
     def tmat(b):
@@ -146,13 +187,15 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic
     if not ok:
         raise SystemExit(f"GPU path not supported here: {why}")
     dev = torch.device("cuda:0")
-    cases = _cases(workload, hb)
+    cases = _cases(workload, hb, only)
     setups = []
     weights = {}
-    for (M, name, K, N, hbk, with_bias) in cases:
-        key = (name, K, N, hbk)
+    xs = {}
+    for (wl, M, name, K, N, hbk, with_bias) in cases:
+        general = wl == "transform"  # the block size is a general transform's, not a rotation's
+        key = (wl, name, K, N, hbk)
         if key not in weights:
-            W = torch.from_numpy(synthetic.weight(N, K, config=workload)).to(dev)
+            W = torch.from_numpy(synthetic.weight(N, K, config=wl)).to(dev)
             if fmt == "nvfp4" and general:
                 w0 = fql.NVFP4Weight.from_float(W, input_global_scale=1.0, transform=tmat(hbk))
             elif fmt == "nvfp4":
@@ -168,8 +211,11 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic
             copies = [w0.packed] + [w0.packed.clone() for _ in range(ncopies - 1)]
             weights[key] = (w0, copies)
         w0, copies = weights[key]
-        xb = synthetic.activations(synthetic.WORKLOADS[workload]["x"], M, K, config=workload)
-        x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+        xkey = (wl, M, K)
+        if xkey not in xs:
+            xb = synthetic.activations(synthetic.WORKLOADS[wl]["x"], M, K, config=wl)
+            xs[xkey] = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+        x = xs[xkey]
         if fmt == "nvfp4":
             T = tmat(hbk) if general else None
             if general:  # calibration on the transformed activation (the library's amax kernel)
@@ -185,14 +231,16 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic
             objs = [type(w0)(p, N, K) for p in copies]
         bias = None
         if with_bias:
-            bias = torch.from_numpy(synthetic.bias(N, config=workload).view(np.int16)).view(
+            bias = torch.from_numpy(synthetic.bias(N, config=wl).view(np.int16)).view(
                 torch.bfloat16).to(dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         wsb = (fql.linear_workspace_bytes(M, N, K) if fmt == "nvfp4"
                else fql.linear_sc_workspace_bytes(fmt, M, N, K))
         ws = fql.new_workspace(wsb, dev)
-        setups.append(dict(M=M, N=N, K=K, name=name, hb=hbk, x=x, objs=objs, bias=bias, y=y,
-                           ws=ws, flops=2.0 * M * N * K, bytes=_alg_bytes(M, N, K, with_bias, fmt),
+        split = (fmt == "nvfp4" and not general and not dynamic and _has_quant_pass(M, N, K))
+        setups.append(dict(M=M, N=N, K=K, name=_case_name(wl, name, M, hbk), x=x, objs=objs,
+                           bias=bias, y=y, ws=ws, flops=2.0 * M * N * K,
+                           bytes=_alg_bytes(M, N, K, with_bias, fmt), split=split,
                            kernel=_kernel_of(M, N, K, fmt, general=general, dynamic=dynamic)))
     torch.cuda.synchronize()
     n = len(setups)
@@ -236,11 +284,10 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic
         t1 = time.perf_counter()
     ms_per_step = e0.elapsed_time(e1) / steps
     wall_ms_per_step = (t1 - t0) * 1e3 / steps
+    del graphs
 
-    # per-launch duration of each case: a graph of R back-to-back calls of that case
+    # per-call duration of each case: a graph of R back-to-back calls of that case
     # (rotating weight copies), timed with HIP events on the replay stream
-    detail = []
-    per_case_ms = []
     with torch.cuda.stream(stream):
         for s in setups:
             R = max(8, len(s["objs"]))
@@ -256,147 +303,276 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic
                 g.replay()
             b.record(stream)
             b.synchronize()
-            ms = a.elapsed_time(b) / (per_case_reps * R)
-            per_case_ms.append(ms)
-            tag = "b" if general else "hb"
-            detail.append(dict(case=f"{s['name']}/M={s['M']}" + (f"/{tag}={s['hb']}" if s["hb"] else ""),
-                               kernel=s["kernel"], us=round(ms * 1e3, 2),
-                               tflops=round(s["flops"] / (ms * 1e-3) / 1e12, 2),
-                               gbs=round(s["bytes"] / (ms * 1e-3) / 1e9, 1),
-                               hbm_frac=round(s["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 3)))
+            s["call_ms"] = a.elapsed_time(b) / (per_case_reps * R)
             del g
-    # dominant kernel: the one carrying the most time per step
+    # GEMM kernel alone: calls with a quantizer pass run as their two halves, and
+    # HIP events on the launch stream bracket each GEMM launch (rotating copies)
+    with torch.cuda.stream(stream):
+        for s in setups:
+            if not s["split"]:
+                s["kernel_ms"] = s["call_ms"]
+                continue
+            R = max(8, len(s["objs"]))
+            evs = []
+            for r in range(R + 1):
+                w = s["objs"][r % len(s["objs"])]
+                fql.linear_nvfp4_quantize(s["x"], w, s["ws"])
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fql.linear_nvfp4_gemm(s["M"], w, s["ws"], w.alpha, bias=s["bias"], out=s["y"])
+                b.record(stream)
+                if r > 0:  # the first round warms up
+                    evs.append((a, b))
+            stream.synchronize()
+            s["kernel_ms"] = statistics.mean(a.elapsed_time(b) for a, b in evs)
+
+    per_case = []
+    for s in setups:
+        ms = s["call_ms"]
+        tf = s["flops"] / (ms * 1e-3) / 1e12
+        gbs = s["bytes"] / (ms * 1e-3) / 1e9
+        d = dict(case=s["name"], kernel=s["kernel"], us=round(ms * 1e3, 2),
+                 gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 3), tflops=round(tf, 1),
+                 mfma_frac=round(tf / MFMA_PEAK[fmt], 3))
+        if fmt == "nvfp4":
+            d["fp4_frac"] = round(tf / FP4_PEAK_TFLOPS, 4)
+        if s["split"]:
+            d["gemm_us"] = round(s["kernel_ms"] * 1e3, 2)
+        per_case.append(d)
+    # dominant kernel: the GEMM kernel carrying the most time per step
     by_kernel = {}
-    for s, ms in zip(setups, per_case_ms):
-        k = by_kernel.setdefault(s["kernel"], dict(ms=0.0, bytes=0.0, flops=0.0, launches=0))
-        k["ms"] += ms
+    for s in setups:
+        k = by_kernel.setdefault(s["kernel"], dict(ms=0.0, bytes=0.0, flops=0.0, launches=0,
+                                                   cases=[]))
+        k["ms"] += s["kernel_ms"]
         k["bytes"] += s["bytes"]
         k["flops"] += s["flops"]
         k["launches"] += 1
+        k["cases"].append(s["name"])
     dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
     flops = sum(s["flops"] for s in setups)
     alg_bytes = sum(s["bytes"] for s in setups)
     return dict(ms_per_step=ms_per_step, wall_ms_per_step=wall_ms_per_step, flops=flops,
-                alg_bytes=alg_bytes, detail=detail, dominant=(dom_name, dom))
+                alg_bytes=alg_bytes, per_case=per_case, dominant=(dom_name, dom))
 
 
-def cpu_baseline_sc(workload, fmt, budget_s=12.0, n_rows=2048):
-    """The sibling format's oracle on a bounded sample of the workload (as cpu_baseline)."""
-    import oracle.fp8 as P
-    import oracle.mx as X
-    import synthetic
+# ---------------------------------------------------------------------------
+# calibration: what a plain streaming read and MFMA loops reach on this GPU
+# ---------------------------------------------------------------------------
 
+def calibration(stream_sizes_mb=(14.2, 33.1, 66.1, 147.5, 512.0), mfma_reps=3):
+    """Streaming-read GB/s per buffer size (cold: rotated over >= 512 MB, graph of
+    back-to-back reads, HIP events) and MFMA-loop TFLOP/s (f16 32x32x16 and the
+    scaled FP8 / FP4 16x16x128, one and two waves per SIMD)."""
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "fp8_quantized_linear_amd", "libfql_calib.so"))
+    lib.fql_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+    lib.fql_calib_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    sst = ctypes.c_void_p(stream.cuda_stream)
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+    out = {"stream_read_gbs": {}, "mfma_tflops": {}}
+    pool = torch.ones(1024 << 20, dtype=torch.uint8, device=dev)
+    for mb in stream_sizes_mb:
+        nb = int(mb * 1e6) // 4096 * 4096
+        bufs = max(2, (1024 << 20) // nb)
+        grid = int(min(1 << 16, max(1, nb // (16 * 1024))))
+        R = max(8, bufs)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(g, stream=stream):
+                for r in range(R):
+                    p = pool.data_ptr() + (r % bufs) * nb
+                    rc = lib.fql_calib_stream_read(ctypes.c_void_p(p), nb, grid,
+                                                   ctypes.c_void_p(sink.data_ptr()),
+                                                   ctypes.c_void_p(stream.cuda_stream))
+                    if rc != 0:
+                        raise RuntimeError(f"stream read calibration failed ({rc})")
+            g.replay()
+            stream.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(3):
+                g.replay()
+            b.record(stream)
+            b.synchronize()
+        ms = a.elapsed_time(b) / (3 * R)
+        out["stream_read_gbs"][f"{mb:g}MB"] = round(nb / (ms * 1e-3) / 1e9, 1)
+        del g
+    del pool
+    iters = 16000  # about a millisecond per launch, like the large GEMMs
+    for kind, name, flop in ((0, "f16_32x32x16", 32768), (1, "fp8_16x16x128", 65536),
+                             (2, "fp4_16x16x128", 65536)):
+        for wps in (1, 2):
+            grid = 256 * wps
+            with torch.cuda.stream(stream):
+                lib.fql_calib_mfma_loop(kind, grid, iters, ctypes.c_void_p(sink.data_ptr()), sst)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(mfma_reps):
+                    lib.fql_calib_mfma_loop(kind, grid, iters, ctypes.c_void_p(sink.data_ptr()), sst)
+                b.record(stream)
+                b.synchronize()
+            ms = a.elapsed_time(b) / mfma_reps
+            total = grid * 4 * iters * 4 * flop
+            out["mfma_tflops"][f"{name}_waves_per_simd={wps}"] = round(total / (ms * 1e-3) / 1e12, 1)
+    return out
+
+
+def environment():
+    """GPU, ROCm/HIP version and the GPU's clock limits (amd-smi), as far as available."""
+    import torch
+
+    env = {"hip": getattr(torch.version, "hip", None), "torch": torch.__version__}
+    try:
+        props = torch.cuda.get_device_properties(0)
+        env.update(device=props.name, gcn_arch=getattr(props, "gcnArchName", None),
+                   compute_units=props.multi_processor_count,
+                   hbm_gib=round(props.total_memory / 2 ** 30, 1))
+    except Exception:
+        pass
+    try:
+        env["rocm"] = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    try:
+        txt = subprocess.run(["amd-smi", "metric", "-c", "-p"], capture_output=True, text=True,
+                             timeout=20).stdout
+        for line in txt.splitlines():
+            t = line.strip()
+            if t.startswith("MAX_CLK:") and "gfx_max_clk_mhz" not in env:
+                env["gfx_max_clk_mhz"] = t.split(":", 1)[1].strip()
+            elif t.startswith("SOCKET_POWER:"):
+                env["socket_power_idle"] = t.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    env["host_cpus"] = os.cpu_count()
+    return env
+
+
+# ---------------------------------------------------------------------------
+# the oracle on the host (bounded sample)
+# ---------------------------------------------------------------------------
+
+def _threads():
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
-
-    def quant_w(W):
-        if fmt == "mxfp4":
-            return X.quant_mxfp4(W)
-        if fmt == "mxfp8":
-            return P.quant_mxfp8(W)
-        if fmt == "fp8_block":
-            return P.quant_fp8_block_weight(W)
-        s = P.scale_from_amax(np.abs(W).max())
-        return P.quant_fp8_tensor(W, s), s
-
-    def layer(x, wq):
-        if fmt == "mxfp4":
-            return X.linear_mxfp4(*X.quant_mxfp4(x), *wq)
-        if fmt == "mxfp8":
-            return P.linear_mxfp8(*P.quant_mxfp8(x), *wq)
-        if fmt == "fp8_block":
-            return P.linear_fp8_block(*P.quant_fp8_block_act(x), *wq)
-        sx = P.scale_from_amax(np.abs(x).max())
-        return P.linear_fp8_tensor(P.quant_fp8_tensor(x, sx), wq[0], P.output_scale(sx, wq[1]))
-
-    cases = _cases(workload)
-    wcache = {}
-    flops = t_total = 0.0
-    passes = 0
-    while t_total < budget_s and passes < 20:
-        for (M, name, K, N, hb, with_bias) in cases:
-            ns = min(N, n_rows)
-            if name not in wcache:
-                wcache[name] = quant_w(synthetic.weight(N, K, config=workload)[:ns])
-            Mr = min(M, 512)
-            xb = synthetic.activations(synthetic.WORKLOADS[workload]["x"], Mr, K, config=workload)
-            x = synthetic.bf16_bits_to_f32(xb)
-            t0 = time.perf_counter()
-            layer(x, wcache[name])
-            t_total += time.perf_counter() - t0
-            flops += 2.0 * Mr * ns * K
-        passes += 1
-    return dict(value=round(flops / t_total / 1e12, 6), unit="TFLOP/s", cores=int(threads),
-                kind="oracle",
-                sample=f"{passes} pass(es) over the {len(cases)} {workload} cases with the first "
-                       f"{n_rows} weight rows and at most 512 activation rows each "
-                       f"(x quantize + float64 GEMM + epilogue), {t_total:.1f} s of oracle time")
+        return os.cpu_count() or 1
 
 
-def cpu_baseline(workload, budget_s=12.0, n_rows=2048):
-    """The oracle, as it stands, on a bounded sample of the workload.
-
-    Every case runs with the first `n_rows` weight rows (weights quantized
-    once per shape, untimed); the timed part is the activation quantizer plus
-    the float64 GEMM and epilogue. Passes over the cases repeat until
-    `budget_s` seconds of oracle time have accumulated.
-    """
+def _oracle_runner(workload, fmt, n_rows, m_rows):
+    """A function running every case of the workload once through the oracle on a
+    bounded sample (first `n_rows` weight rows, at most `m_rows` activation rows;
+    weights quantized once, untimed); returns (seconds of oracle time, flops)."""
+    import oracle.fp8 as P
+    import oracle.mx as X
     import oracle.nvfp4 as Q
     import oracle.transform as TR
     import synthetic
     from oracle.formats import bf16_bits_to_f64
     from oracle.hadamard import fwht_fp32
 
-    general = workload == "transform"
-
-    try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
     cases = _cases(workload)
-    wcache = {}
-    flops = 0.0
-    t_total = 0.0
-    calls = 0
-    passes = 0
-    while t_total < budget_s and passes < 20:
-        for (M, name, K, N, hb, with_bias) in cases:
-            ns = min(N, n_rows)
-            if (name, hb) not in wcache:
-                W = synthetic.weight(N, K, config=workload)[:ns]
-                Wr = fwht_fp32(W, hb) if hb and not general else W
+    wcache, xcache = {}, {}
+
+    def weight(wl, name, K, N, hb):
+        key = (wl, name, hb)
+        if key not in wcache:
+            W = synthetic.weight(N, K, config=wl, rows=n_rows)
+            if fmt != "nvfp4":
+                if fmt == "mxfp4":
+                    wcache[key] = X.quant_mxfp4(W)
+                elif fmt == "mxfp8":
+                    wcache[key] = P.quant_mxfp8(W)
+                elif fmt == "fp8_block":
+                    wcache[key] = P.quant_fp8_block_weight(W)
+                else:
+                    s = P.scale_from_amax(np.abs(W).max())
+                    wcache[key] = (P.quant_fp8_tensor(W, s), s)
+            else:
+                Wr = fwht_fp32(W, hb) if hb and wl != "transform" else W
                 gw = Q.global_scale_from_amax(Q.amax_for_calibration(Wr))
-                wcache[(name, hb)] = (gw,) + Q.quant_nvfp4(Wr, gw)
-            gw, wc, wsc = wcache[(name, hb)]
-            Mr = min(M, 512)  # rows of x in the sample
-            xb = synthetic.activations(synthetic.WORKLOADS[workload]["x"], Mr, K, config=workload)
-            x = synthetic.bf16_bits_to_f32(xb)
-            if general:
-                T64 = bf16_bits_to_f64(synthetic.transform_matrix(hb))
-                gx = Q.global_scale_from_amax(TR.tensor_amax(TR.block_transform(x, T64)))
-            else:
-                gx = Q.global_scale_from_amax(Q.amax_for_calibration(x, hb))
+                wcache[key] = (gw,) + Q.quant_nvfp4(Wr, gw)
+        return wcache[key]
+
+    def act(wl, M, K):
+        key = (wl, min(M, m_rows), K)
+        if key not in xcache:
+            xb = synthetic.activations(synthetic.WORKLOADS[wl]["x"], min(M, m_rows), K, config=wl)
+            xcache[key] = synthetic.bf16_bits_to_f32(xb)
+        return xcache[key]
+
+    def layer(wl, x, hb, wq):
+        if fmt == "mxfp4":
+            return X.linear_mxfp4(*X.quant_mxfp4(x), *wq)
+        if fmt == "mxfp8":
+            return P.linear_mxfp8(*P.quant_mxfp8(x), *wq)
+        if fmt == "fp8_block":
+            return P.linear_fp8_block(*P.quant_fp8_block_act(x), *wq)
+        if fmt == "fp8":
+            sx = P.scale_from_amax(np.abs(x).max())
+            return P.linear_fp8_tensor(P.quant_fp8_tensor(x, sx), wq[0], P.output_scale(sx, wq[1]))
+        gw, wc, wsc = wq
+        if wl == "transform":
+            T64 = bf16_bits_to_f64(synthetic.transform_matrix(hb))
+            gx = Q.global_scale_from_amax(TR.tensor_amax(TR.block_transform(x, T64)))
+            xc, xs = TR.quant_nvfp4_transform(x, T64, gx)
+        else:
+            gx = Q.global_scale_from_amax(Q.amax_for_calibration(x, hb))
+            xc, xs = Q.quant_nvfp4(x, gx, hb)
+        return Q.linear_nvfp4(xc, xs, wc, wsc, TR.dynamic_alpha(gx, gw))
+
+    def run_once():
+        t_total = flops = 0.0
+        for (wl, M, name, K, N, hb, with_bias) in cases:
+            wq = weight(wl, name, K, N, hb)
+            x = act(wl, M, K)
             t0 = time.perf_counter()
-            if general:
-                xc, xs = TR.quant_nvfp4_transform(x, T64, gx)
-            else:
-                xc, xs = Q.quant_nvfp4(x, gx, hb)
-            Q.linear_nvfp4(xc, xs, wc, wsc, np.float32(1.0 / (float(gx) * float(gw))))
+            layer(wl, x, hb, wq)
             t_total += time.perf_counter() - t0
-            flops += 2.0 * Mr * ns * K
-            calls += 1
-        passes += 1
-    return dict(value=round(flops / t_total / 1e12, 6), unit="TFLOP/s", cores=int(threads),
-                kind="oracle",
-                sample=f"{passes} pass(es) over the {len(cases)} {workload} cases with the first "
-                       f"{n_rows} weight rows and at most 512 activation rows each "
-                       f"(x quantize + float64 GEMM + epilogue), {t_total:.1f} s of oracle time")
+            flops += 2.0 * x.shape[0] * min(N, n_rows) * K
+        return t_total, flops
+
+    return run_once, len(cases)
+
+
+def cpu_baseline(workload, fmt="nvfp4", n_rows=256, m_rows=64, runs=3):
+    """The oracle, as it stands, on a bounded sample of the workload: every case with
+    the first `n_rows` weight rows and at most `m_rows` activation rows (the
+    activation quantizer, the float64 GEMM and the epilogue are timed). Median of
+    `runs` passes on all host cores, and median of `runs` passes on one thread."""
+    run_once, ncases = _oracle_runner(workload, fmt, n_rows, m_rows)
+    run_once()  # quantizes the weights (untimed) and warms up
+    legs = {}
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        threadpool_limits = None
+    for leg in ("all", "one"):
+        res = []
+        for _ in range(runs):
+            if leg == "one" and threadpool_limits is not None:
+                with threadpool_limits(limits=1):
+                    res.append(run_once())
+            else:
+                res.append(run_once())
+        rates = sorted(f / t / 1e12 for t, f in res)
+        legs[leg] = dict(value=round(rates[len(rates) // 2], 6),
+                         seconds=round(sum(t for t, _ in res), 1))
+    sample = (f"median of {runs} passes over the {ncases} {workload} cases, each with the first "
+              f"{n_rows} weight rows and at most {m_rows} activation rows (activation quantize + "
+              f"float64 GEMM + epilogue); {legs['all']['seconds']} s of oracle time on all cores, "
+              f"{legs['one']['seconds']} s on one thread")
+    return dict(value=legs["all"]["value"], unit="TFLOP/s", cores=int(_threads()), kind="oracle",
+                sample=sample, one_thread=dict(value=legs["one"]["value"], unit="TFLOP/s",
+                                               cores=1))
 
 
 def main():
@@ -404,13 +580,16 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=WORKLOAD_KEYS)
+    ap.add_argument("--workload", default="serving", choices=WORKLOAD_KEYS)
     ap.add_argument("--format", default="nvfp4", choices=FORMAT_KEYS)
     ap.add_argument("--hadamard-block", type=int, default=None,
                     help="restrict the hadamard/transform workloads to one block size")
     ap.add_argument("--dynamic-scale", action="store_true",
                     help="NVFP4: compute the activation global scale per call on the device")
+    ap.add_argument("--cases", default=None,
+                    help="comma-separated case names to run (e.g. prefill/gate_up/M=8192)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true")
     ap.add_argument("--detail", action="store_true", help="print per-case timings to stderr")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="only run 5 plain device-to-device copies of MB MiB (counter calibration)")
@@ -434,12 +613,16 @@ def main():
         return
     if args.format != "nvfp4" and (args.dynamic_scale or args.workload == "transform"):
         raise SystemExit("--dynamic-scale and the transform workload are NVFP4 options")
+    only = set(args.cases.split(",")) if args.cases else None
+    print(f"[bench] {args.workload} {args.format}: setting up", file=sys.stderr, flush=True)
     r = gpu_bench(args.workload, args.steps, args.warmup, args.hadamard_block, fmt=args.format,
-                  dynamic=args.dynamic_scale)
+                  dynamic=args.dynamic_scale, only=only)
+    print(f"[bench] timed {args.steps} steps: {r['ms_per_step']:.4f} ms/step", file=sys.stderr,
+          flush=True)
     value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
     dom_name, dom = r["dominant"]
-    # binding bound of the dominant kernel: HBM bytes vs f16-MFMA flops (the exact
-    # NVFP4 path multiplies dequantized float16 operands), whichever needs more time
+    # binding bound of the dominant kernel: HBM bytes vs MFMA flops (the exact NVFP4
+    # path multiplies dequantized float16 operands), whichever needs more time
     mfma_peak = MFMA_PEAK[args.format]
     t_hbm = dom["bytes"] / (HBM_PEAK_GBS * 1e9)
     t_mfma = dom["flops"] / (mfma_peak * 1e12)
@@ -450,14 +633,16 @@ def main():
     else:
         ach = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": mfma_peak,
-                "unit": "TFLOP/s", "frac": round(ach / mfma_peak, 4),
-                "frac_of_fp4_peak": round(ach / FP4_PEAK_TFLOPS, 4)}
-    roof.update({"kernel": dom_name, "launches_per_step": dom["launches"],
-                 "alg_bytes_per_step": dom["bytes"], "flops_per_step": dom["flops"],
+                "unit": "TFLOP/s", "frac": round(ach / mfma_peak, 4)}
+        if args.format == "nvfp4":
+            roof["frac_of_fp4_peak"] = round(ach / FP4_PEAK_TFLOPS, 4)
+    roof.update({"traffic": measured_traffic(dom_name) if args.format == "nvfp4" else None,
+                 "kernel": dom_name, "launches_per_step": dom["launches"],
                  "avg_launch_us": round(dom["ms"] * 1e3 / dom["launches"], 2),
+                 "timing": "kernel alone, HIP events around each launch on its stream",
+                 "alg_flops_per_launch": round(dom["flops"] / dom["launches"]),
                  "alg_bytes_per_launch": round(dom["bytes"] / dom["launches"]),
-                 "traffic": measured_traffic(args.workload, dom_name)
-                 if args.format == "nvfp4" else None})
+                 "cases": dom["cases"]})
     out = {
         "metric": "NVFP4 W4A4 linear TFLOP/s (quant+GEMM), M=1..8192; % of HBM/FP4-MFMA roofline",
         "format": args.format,
@@ -474,15 +659,20 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.workload]
                    + (", dynamic activation global scale" if args.dynamic_scale else ""),
-                   "cases": len(r["detail"]),
+                   "cases": len(r["per_case"]),
                    "timing": "HIP graph replay per step, weights rotated over >= 512 MB"},
         "roofline": roof,
+        "per_case": r["per_case"],
     }
+    if not args.no_calibration:
+        print("[bench] calibration", file=sys.stderr, flush=True)
+        out["calibration"] = calibration()
+    out["env"] = environment()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = (cpu_baseline(args.workload) if args.format == "nvfp4"
-                               else cpu_baseline_sc(args.workload, args.format))
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.format)
     if args.detail:
-        for d in r["detail"]:
+        for d in r["per_case"]:
             print(json.dumps(d), file=sys.stderr)
     print(json.dumps(out), flush=True)
 

@@ -72,6 +72,12 @@ __all__ = [
     "transform_bf16",
     "quant_nvfp4_transform",
     "quant_nvfp4_dynamic",
+    "nvfp4_alpha",
+    "fp8_output_scale",
+    "set_plan_override",
+    "plan_override",
+    "linear_nvfp4_quantize",
+    "linear_nvfp4_gemm",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -147,7 +153,23 @@ SIGNATURES = {
     "fql_linear_mxfp4_describe": (_c_int, [_c_i64, _c_i64, _c_i64, ctypes.c_char_p, _c_sz]),
     "fql_linear_mxfp4": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_f32, _c_vp,
                                   _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fql_linear_nvfp4_dev_alpha": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_int, _c_vp,
+                                            _c_i64, _c_vp, _c_vp, _c_vp, _c_i64, _c_vp, _c_sz,
+                                            _c_vp]),
+    "fql_linear_fp8_dev_alpha": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_vp, _c_i64,
+                                          _c_vp, _c_vp, _c_vp, _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fql_linear_nvfp4_quantize": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_int, _c_i64,
+                                           _c_vp, _c_sz, _c_vp]),
+    "fql_linear_nvfp4_gemm": (_c_int, [_c_i64, _c_i64, _c_int, _c_vp, _c_i64, _c_f32, _c_vp, _c_vp,
+                                       _c_i64, _c_vp, _c_sz, _c_vp]),
+    "fql_nvfp4_global_scale": (_c_int, [_c_f32, ctypes.POINTER(_c_f32)]),
+    "fql_nvfp4_alpha": (_c_int, [_c_f32, _c_f32, ctypes.POINTER(_c_f32)]),
+    "fql_fp8_scale": (_c_int, [_c_f32, ctypes.POINTER(_c_f32)]),
+    "fql_fp8_output_scale": (_c_int, [_c_f32, _c_f32, ctypes.POINTER(_c_f32)]),
+    "fql_set_plan_override": (_c_int, [_c_int, ctypes.c_char_p]),
 }
+
+PLAN_OVERRIDES = {"nvfp4": 0, "sc_gemm": 1, "sc_gemv": 2}  # FQL_PLAN_NVFP4, _SC_GEMM, _SC_GEMV
 
 
 class FQLError(RuntimeError):
@@ -250,17 +272,50 @@ def amax(x, hadamard_block=0):
     return out
 
 
-def global_scale_from_amax(amax_value):
-    """g = 448 * 6 / amax rounded to float32 (1 when amax is 0, at most
-    2^118), on the host."""
-    import numpy as np
+def _host_scalar(name, *args):
+    out = _c_f32()
+    _check(getattr(lib(), name)(*[_c_f32(float(a)) for a in args], ctypes.byref(out)))
+    return out.value
 
-    a = np.float32(amax_value)
-    if a == 0:
-        return float(np.float32(1.0))
-    with np.errstate(over="ignore"):
-        g = np.float32(2688.0) / a
-    return float(min(g, np.float32(2.0 ** 118)))  # keeps g / (smallest E4M3 scale) finite
+
+def global_scale_from_amax(amax_value):
+    """The NVFP4 global scale g = fl32(448 * 6 / amax) of a calibration amax
+    (1 when amax is 0, at most 2^118), from the library (host-side)."""
+    return _host_scalar("fql_nvfp4_global_scale", amax_value)
+
+
+def nvfp4_alpha(input_global_scale, weight_global_scale):
+    """alpha = fl32((1/g_x) * (1/g_w)), the product of the two global dequant scales."""
+    return _host_scalar("fql_nvfp4_alpha", input_global_scale, weight_global_scale)
+
+
+def fp8_output_scale(input_scale, weight_scale):
+    """The per-tensor FP8 output scale fl32(s_x * s_w)."""
+    return _host_scalar("fql_fp8_output_scale", input_scale, weight_scale)
+
+
+def set_plan_override(spec, which="nvfp4"):
+    """Replace a launch-plan override (benchmarking and tests): `which` is "nvfp4"
+    (FQL_PLAN syntax), "sc_gemm" (FQL_SC_PLAN) or "sc_gemv" (FQL_SC_GEMV); None
+    or "" removes it. Results change at most in the float32 summation order."""
+    _check(lib().fql_set_plan_override(PLAN_OVERRIDES[which],
+                                       None if not spec else str(spec).encode()))
+
+
+class plan_override:
+    """Context manager: `with plan_override("kind=3,mt=4,nt=2,st=3"): ...` sets the
+    override on entry and removes it on exit."""
+
+    def __init__(self, spec, which="nvfp4"):
+        self.spec, self.which = spec, which
+
+    def __enter__(self):
+        set_plan_override(self.spec, self.which)
+        return self
+
+    def __exit__(self, *exc):
+        set_plan_override(None, self.which)
+        return False
 
 
 def quant_nvfp4(x, global_scale, hadamard_block=0, codes=None, scales=None):
@@ -340,6 +395,9 @@ class NVFP4Weight:
     the Hadamard rotation (the weight must have been transformed alike
     offline). dynamic_input_scale: g_x is computed from each call's
     activation (448 * 6 / amax) on the device instead of the static scale.
+    alpha_dev: alpha as a float32 device scalar, which linear_nvfp4 reads
+    when no alpha is passed, so repack_ with a new weight global scale keeps
+    captured graphs valid.
     """
 
     def __init__(self, packed, N, K, input_global_scale, weight_global_scale, hadamard_block=0,
@@ -355,10 +413,8 @@ class NVFP4Weight:
                 raise FQLError("a weight takes either a Hadamard block or a transform matrix")
         self.transform = transform
         self.dynamic_input_scale = bool(dynamic_input_scale)
-        import numpy as np
-
-        self.alpha = float(np.float32((1.0 / np.float64(np.float32(input_global_scale))) *
-                                      (1.0 / np.float64(np.float32(weight_global_scale)))))
+        self.alpha = nvfp4_alpha(self.input_global_scale, self.weight_global_scale)
+        self.alpha_dev = torch.full((1,), self.alpha, dtype=torch.float32, device=packed.device)
 
     @classmethod
     def from_float(cls, w, input_global_scale, hadamard_block=0, weight_global_scale=None,
@@ -372,9 +428,24 @@ class NVFP4Weight:
         return cls(packed, w.shape[0], w.shape[1], input_global_scale, weight_global_scale,
                    hadamard_block, transform=transform, dynamic_input_scale=dynamic_input_scale)
 
-    def repack_(self, codes, scales):
-        """Re-pack new canonical weights into the same storage (address kept)."""
+    def repack_(self, codes, scales, weight_global_scale=None):
+        """Re-pack new canonical weights into the same storage (address kept).
+
+        weight_global_scale: the new weight's g_w when it differs from the old
+        one; alpha is then recomputed and written to alpha_dev in stream order,
+        so graphs captured on calls without an explicit alpha replay with it.
+        Weights with a transform or a dynamic input scale pass g_w to the
+        library by value and reject a changed scale.
+        """
         pack_weight_nvfp4(codes, scales, out=self.packed)
+        if weight_global_scale is not None and float(weight_global_scale) != self.weight_global_scale:
+            if self.transform is not None or self.dynamic_input_scale:
+                raise FQLError("a weight with a transform or a dynamic input scale keeps its "
+                               "weight global scale across repack_")
+            alpha = nvfp4_alpha(self.input_global_scale, weight_global_scale)
+            self.weight_global_scale = float(weight_global_scale)
+            self.alpha = alpha
+            self.alpha_dev.fill_(alpha)
         return self
 
 
@@ -425,6 +496,7 @@ def linear_nvfp4(x, weight, alpha=None, bias=None, out=None, workspace=None):
     x2, ld = _rows_view(x, "x")
     M, K = x2.shape
     N = weight.N
+    alpha_dev = getattr(weight, "alpha_dev", None) if alpha is None else None
     if alpha is None:
         alpha = weight.alpha
     if bias is not None:
@@ -449,11 +521,42 @@ def linear_nvfp4(x, weight, alpha=None, bias=None, out=None, workspace=None):
                                                 float(alpha), _ptr(bias), _ptr(y2), ldy,
                                                 _ptr(workspace), workspace.numel(),
                                                 _stream(x.device)))
+    elif alpha_dev is not None:
+        _check(lib().fql_linear_nvfp4_dev_alpha(_ptr(x2), M, K, ld, weight.input_global_scale,
+                                                weight.hadamard_block, _ptr(weight.packed), N,
+                                                _ptr(alpha_dev), _ptr(bias), _ptr(y2), ldy,
+                                                _ptr(workspace), workspace.numel(),
+                                                _stream(x.device)))
     else:
         _check(lib().fql_linear_nvfp4(_ptr(x2), M, K, ld, weight.input_global_scale,
                                       weight.hadamard_block, _ptr(weight.packed), N, float(alpha),
                                       _ptr(bias), _ptr(y2), ldy, _ptr(workspace), workspace.numel(),
                                       _stream(x.device)))
+    return out
+
+
+def linear_nvfp4_quantize(x, weight, workspace):
+    """Diagnostics: the quantizer half of linear_nvfp4 (plain weights only): writes
+    the GEMM's activation operand into `workspace` exactly as the linear call does."""
+    _require_cuda(x, "x")
+    x2, ld = _rows_view(x, "x")
+    M, K = x2.shape
+    _check(lib().fql_linear_nvfp4_quantize(_ptr(x2), M, K, ld, weight.input_global_scale,
+                                           weight.hadamard_block, weight.N, _ptr(workspace),
+                                           workspace.numel(), _stream(x.device)))
+    return workspace
+
+
+def linear_nvfp4_gemm(M, weight, workspace, alpha, x_aligned=True, bias=None, out=None):
+    """Diagnostics: the GEMM half of linear_nvfp4 on the operand linear_nvfp4_quantize
+    left in `workspace`; returns y bf16 [M, N]."""
+    N = weight.N
+    if out is None:
+        out = torch.empty((int(M), N), dtype=torch.bfloat16, device=workspace.device)
+    y2, ldy = _rows_view(out, "out")
+    _check(lib().fql_linear_nvfp4_gemm(int(M), weight.K, int(bool(x_aligned)), _ptr(weight.packed), N,
+                                       float(alpha), _ptr(bias), _ptr(y2), ldy, _ptr(workspace),
+                                       workspace.numel(), _stream(workspace.device)))
     return out
 
 
@@ -609,11 +712,9 @@ def quant_fp8_block_weight(w):
 
 
 def fp8_scale_from_amax(amax_value):
-    """s = fl32(amax / 448) on the host (the FP8 calibration scale; 1 when amax is 0)."""
-    import numpy as np
-
-    a = np.float32(amax_value)
-    return float(np.float32(a / np.float32(448.0))) if a > 0 else 1.0
+    """The per-tensor FP8 calibration scale fl32(amax / 448) (1 when that is 0), from
+    the library (host-side)."""
+    return _host_scalar("fql_fp8_scale", amax_value)
 
 
 def packed_mxfp4_bytes(N, K):
@@ -707,16 +808,27 @@ class FP8BlockWeight(_ScWeight):
 
 class FP8Weight(_ScWeight):
     """A packed per-tensor FP8 weight [N, K] with its weight scale and the layer's
-    static input scale; alpha = fl32(input_scale * weight_scale)."""
+    static input scale; alpha = fl32(input_scale * weight_scale), also kept as a
+    float32 device scalar (alpha_dev) that linear_fp8 reads when no alpha is
+    passed, so repack_ with a new weight scale keeps captured graphs valid."""
     fmt = "fp8"
 
     def __init__(self, packed, N, K, weight_scale, input_scale):
         super().__init__(packed, N, K)
-        import numpy as np
+        self.weight_scale = _c_f32(float(weight_scale)).value
+        self.input_scale = _c_f32(float(input_scale)).value
+        self.alpha = fp8_output_scale(self.input_scale, self.weight_scale)
+        self.alpha_dev = torch.full((1,), self.alpha, dtype=torch.float32, device=packed.device)
 
-        self.weight_scale = float(np.float32(weight_scale))
-        self.input_scale = float(np.float32(input_scale))
-        self.alpha = float(np.float32(np.float64(self.input_scale) * np.float64(self.weight_scale)))
+    def repack_(self, codes, scales=None, weight_scale=None):
+        """Re-pack new FP8 weight codes into the same storage; a new weight_scale
+        updates alpha and alpha_dev (in stream order)."""
+        _pack_sc(self.fmt, codes, scales, self.packed)
+        if weight_scale is not None:
+            self.weight_scale = _c_f32(float(weight_scale)).value
+            self.alpha = fp8_output_scale(self.input_scale, self.weight_scale)
+            self.alpha_dev.fill_(self.alpha)
+        return self
 
     @classmethod
     def from_float(cls, w, input_scale, weight_scale=None):
@@ -766,10 +878,14 @@ def _linear_sc(fmt, x, weight, alpha, bias, out, workspace):
     if workspace is None:
         workspace = _workspace(x.device, linear_sc_workspace_bytes(fmt, M, N, K))
     st = _stream(x.device)
-    if fmt == "fp8":
-        a = weight.alpha if alpha is None else alpha
+    if fmt == "fp8" and alpha is None:
+        _check(_fn("fql_linear_fp8_dev_alpha")(_ptr(x2), M, K, ld, weight.input_scale,
+                                               _ptr(weight.packed), N, _ptr(weight.alpha_dev),
+                                               _ptr(bias), _ptr(y2), ldy, _ptr(workspace),
+                                               workspace.numel(), st))
+    elif fmt == "fp8":
         _check(_fn("fql_linear_fp8")(_ptr(x2), M, K, ld, weight.input_scale, _ptr(weight.packed), N,
-                                     float(a), _ptr(bias), _ptr(y2), ldy, _ptr(workspace),
+                                     float(alpha), _ptr(bias), _ptr(y2), ldy, _ptr(workspace),
                                      workspace.numel(), st))
     else:
         a = 1.0 if alpha is None else alpha

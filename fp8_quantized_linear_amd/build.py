@@ -1,4 +1,6 @@
-"""Build libfql.so (the gfx950 HIP library behind include/fql.h) in-tree.
+"""Build libfql.so (the gfx950 HIP library behind include/fql.h) in-tree, and
+libfql_calib.so, the measurement aids bench.py loads (streaming-read and
+MFMA-loop calibration kernels; not part of the layer).
 
 Usage: python -m fp8_quantized_linear_amd.build   (or call build()).
 
@@ -19,6 +21,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfql.so")
+CALIB_LIB = os.path.join(HERE, "libfql_calib.so")
+CALIB_SOURCES = ["calib.hip"]
 
 SOURCES = ["fql_api.hip", "quant_nvfp4.hip", "pack_nvfp4.hip", "gemm_nvfp4.hip", "sc_quant.hip",
            "sc_gemm.hip", "transform_nvfp4.hip"]
@@ -56,20 +60,26 @@ def _compile(src, obj, verbose):
     return obj
 
 
-def build(verbose=False):
-    """Compile all sources and link libfql.so. Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
-    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES]
-    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(SOURCES, objs)))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    """Compile all sources and link libfql.so and libfql_calib.so. Always rebuilds."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + CALIB_SOURCES
+    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in srcs]
+    with ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
+        list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(srcs, objs)))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], CALIB_LIB, verbose)
     return LIB
 
 

@@ -5,14 +5,93 @@
 // lifecycle: is_supported decides availability with a reason string,
 // can_implement checks format constraints, and the hot call only asserts.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/fql.h"
 #include "fql_internal.h"
+
+// ---- launch-plan overrides and per-thread plan caches ------------------------
+
+namespace fql {
+namespace {
+
+std::mutex g_override_mutex;
+std::string g_override[3];
+bool g_override_read = false;
+std::atomic<uint32_t> g_override_generation{1};
+
+void read_env_overrides_locked() {
+  if (g_override_read) return;
+  static const char* const names[3] = {"FQL_PLAN", "FQL_SC_PLAN", "FQL_SC_GEMV"};
+  for (int i = 0; i < 3; ++i) {
+    const char* e = std::getenv(names[i]);
+    g_override[i] = e ? e : "";
+  }
+  g_override_read = true;
+}
+
+// Direct-mapped cache of plans keyed by shape, a tag (alignment or format)
+// and the override generation.
+template <typename Plan>
+struct PlanCache {
+  struct Entry {
+    int64_t M = -1, N = -1, K = -1;
+    int tag = -1;
+    uint32_t gen = 0;
+    Plan plan{};
+  };
+  static constexpr int kEntries = 64;
+  Entry e[kEntries];
+  template <typename Make>
+  const Plan& get(int64_t M, int64_t N, int64_t K, int tag, Make make) {
+    const uint32_t gen = plan_generation();
+    const uint64_t h = (uint64_t)M * 0x9E3779B97F4A7C15ull ^ (uint64_t)N * 0xC2B2AE3D27D4EB4Full ^
+                       (uint64_t)K * 0x165667B19E3779F9ull ^ (uint64_t)tag;
+    Entry& x = e[(h >> 32) % kEntries];
+    if (x.M != M || x.N != N || x.K != K || x.tag != tag || x.gen != gen) {
+      x.plan = make();
+      x.M = M; x.N = N; x.K = K; x.tag = tag; x.gen = gen;
+    }
+    return x.plan;
+  }
+};
+
+}  // namespace
+
+std::string plan_override(int which) {
+  std::lock_guard<std::mutex> lock(g_override_mutex);
+  read_env_overrides_locked();
+  return which >= 0 && which < 3 ? g_override[which] : std::string();
+}
+
+void set_plan_override(int which, const char* spec) {
+  std::lock_guard<std::mutex> lock(g_override_mutex);
+  read_env_overrides_locked();
+  if (which < 0 || which >= 3) return;
+  g_override[which] = spec ? spec : "";
+  g_override_generation.fetch_add(1, std::memory_order_acq_rel);
+}
+
+uint32_t plan_generation() { return g_override_generation.load(std::memory_order_acquire); }
+
+GemmPlan cached_plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
+  thread_local PlanCache<GemmPlan> cache;
+  return cache.get(M, N, K, aligned ? 1 : 0, [&] { return plan_gemm_nvfp4(M, N, K, aligned); });
+}
+
+ScPlan cached_plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
+  thread_local PlanCache<ScPlan> cache;
+  return cache.get(M, N, K, fmt, [&] { return plan_sc_gemm(fmt, M, N, K); });
+}
+
+}  // namespace fql
 
 namespace {
 
@@ -214,8 +293,8 @@ int fql_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* by
     return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 16");
   // either plan a call of this shape may take: aligned or unaligned rows (the
   // transform and dynamic-scale calls take the unaligned one)
-  const int64_t a = fql::plan_gemm_nvfp4(M, N, K, true).total_bytes;
-  const int64_t u = fql::plan_gemm_nvfp4(M, N, K, false).total_bytes;
+  const int64_t a = fql::cached_plan_gemm_nvfp4(M, N, K, true).total_bytes;
+  const int64_t u = fql::cached_plan_gemm_nvfp4(M, N, K, false).total_bytes;
   *bytes = (size_t)std::max(a, u);
   return ok();
 }
@@ -237,31 +316,170 @@ int fql_linear_nvfp4_describe(int64_t M, int64_t N, int64_t K, int aligned, char
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the NVFP4 linear entry points (shape, scales, pointers).
+int check_linear_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float g, int hb,
+                       const void* w_packed, int64_t N, const void* y, int64_t ldy) {
+  if (int r = check_nvfp4_shape(M, K, ldx, hb, "M")) return r;
+  if (int r = check_scale(g, "input_global_scale")) return r;
+  if (N < 1 || N > (int64_t)1 << 24) return fail(FQL_ERR_INVALID, "N out of range");
+  if (ldy < N) return fail(FQL_ERR_INVALID, "ldy %lld is smaller than N %lld", (long long)ldy, (long long)N);
+  if (!x || !w_packed || !y) return fail(FQL_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(w_packed) % 16 != 0)
+    return fail(FQL_ERR_INVALID, "packed weight must be 16-byte aligned");
+  return FQL_OK;
+}
+
+int check_workspace(const void* workspace, size_t workspace_bytes, int64_t need) {
+  if (!workspace) return fail(FQL_ERR_INVALID, "null workspace");
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(FQL_ERR_INVALID, "workspace must be 256-byte aligned");
+  if (workspace_bytes < (size_t)need)
+    return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
+                (long long)need);
+  return FQL_OK;
+}
+
+// fql_linear_nvfp4 with alpha either a host value or (alpha_dev non-null) a
+// device scalar.
+int linear_nvfp4_plain(const void* x, int64_t M, int64_t K, int64_t ldx, float g, int hb,
+                       const void* w_packed, int64_t N, float alpha, const float* alpha_dev,
+                       const void* bias, void* y, int64_t ldy, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (int r = check_linear_nvfp4(x, M, K, ldx, g, hb, w_packed, N, y, ldy)) return r;
+  if (alpha_dev == nullptr && !std::isfinite(alpha)) return fail(FQL_ERR_INVALID, "alpha must be finite");
+  if (alpha_dev != nullptr && reinterpret_cast<uintptr_t>(alpha_dev) % 4 != 0)
+    return fail(FQL_ERR_INVALID, "alpha_dev must be 4-byte aligned");
+  const bool xal = aligned16(x, ldx, 2);
+  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, xal);
+  if (int r = check_workspace(workspace, workspace_bytes, plan.total_bytes)) return r;
+  fql::LinearExtras ex{};
+  ex.alpha_dev = alpha_dev;
+  hipError_t e = fql::launch_linear_nvfp4(
+      plan, static_cast<const uint16_t*>(x), M, K, ldx, g, hb, xal,
+      static_cast<const uint8_t*>(w_packed), N, alpha, static_cast<const uint16_t*>(bias),
+      static_cast<uint16_t*>(y), ldy, static_cast<uint8_t*>(workspace),
+      static_cast<hipStream_t>(stream), alpha_dev != nullptr ? &ex : nullptr);
+  return hip_status(e, "linear launch");
+}
+
+}  // namespace
+
+extern "C" {
+
 int fql_linear_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float input_global_scale,
                      int hadamard_block, const void* w_packed, int64_t N, float alpha,
                      const void* bias, void* y, int64_t ldy, void* workspace,
                      size_t workspace_bytes, void* stream) {
+  return linear_nvfp4_plain(x, M, K, ldx, input_global_scale, hadamard_block, w_packed, N, alpha,
+                            nullptr, bias, y, ldy, workspace, workspace_bytes, stream);
+}
+
+int fql_linear_nvfp4_dev_alpha(const void* x, int64_t M, int64_t K, int64_t ldx,
+                               float input_global_scale, int hadamard_block, const void* w_packed,
+                               int64_t N, const float* alpha_dev, const void* bias, void* y,
+                               int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!alpha_dev) return fail(FQL_ERR_INVALID, "null alpha_dev");
+  return linear_nvfp4_plain(x, M, K, ldx, input_global_scale, hadamard_block, w_packed, N, 0.0f,
+                            alpha_dev, bias, y, ldy, workspace, workspace_bytes, stream);
+}
+
+int fql_linear_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ldx,
+                              float input_global_scale, int hadamard_block, int64_t N,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   if (int r = check_nvfp4_shape(M, K, ldx, hadamard_block, "M")) return r;
   if (int r = check_scale(input_global_scale, "input_global_scale")) return r;
-  if (!std::isfinite(alpha)) return fail(FQL_ERR_INVALID, "alpha must be finite");
   if (N < 1 || N > (int64_t)1 << 24) return fail(FQL_ERR_INVALID, "N out of range");
-  if (ldy < N) return fail(FQL_ERR_INVALID, "ldy %lld is smaller than N %lld", (long long)ldy, (long long)N);
-  if (!x || !w_packed || !y || !workspace) return fail(FQL_ERR_INVALID, "null pointer");
-  if (reinterpret_cast<uintptr_t>(w_packed) % 16 != 0 ||
-      reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(FQL_ERR_INVALID, "packed weight must be 16-byte and workspace 256-byte aligned");
+  if (!x) return fail(FQL_ERR_INVALID, "null pointer");
   const bool xal = aligned16(x, ldx, 2);
-  const fql::GemmPlan plan = fql::plan_gemm_nvfp4(M, N, K, xal);
-  if (workspace_bytes < (size_t)plan.total_bytes)
-    return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
-                (long long)plan.total_bytes);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e = fql::launch_linear_nvfp4(
-      plan, static_cast<const uint16_t*>(x), M, K, ldx, input_global_scale, hadamard_block,
-      xal, static_cast<const uint8_t*>(w_packed), N, alpha,
-      static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), ldy,
-      static_cast<uint8_t*>(workspace), st);
-  return hip_status(e, "linear launch");
+  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, xal);
+  if (!fql::has_quant_pass(plan, hadamard_block, xal, K, nullptr))
+    return fail(FQL_ERR_UNSUPPORTED, "this call's plan quantizes inside the GEMM (%s)",
+                fql::describe_plan(plan).c_str());
+  if (int r = check_workspace(workspace, workspace_bytes, plan.total_bytes)) return r;
+  return hip_status(fql::launch_linear_quant(plan, static_cast<const uint16_t*>(x), M, K, ldx,
+                                             input_global_scale, hadamard_block, xal,
+                                             static_cast<uint8_t*>(workspace),
+                                             static_cast<hipStream_t>(stream)),
+                    "quantize launch");
+}
+
+int fql_linear_nvfp4_gemm(int64_t M, int64_t K, int x_aligned, const void* w_packed, int64_t N,
+                          float alpha, const void* bias, void* y, int64_t ldy, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (M < 1 || M > (int64_t)1 << 24 || K < 16 || K % 16 != 0 || K > (int64_t)1 << 24)
+    return fail(FQL_ERR_INVALID, "need 1 <= M <= 2^24 and K a positive multiple of 16");
+  if (N < 1 || N > (int64_t)1 << 24) return fail(FQL_ERR_INVALID, "N out of range");
+  if (!std::isfinite(alpha)) return fail(FQL_ERR_INVALID, "alpha must be finite");
+  if (ldy < N) return fail(FQL_ERR_INVALID, "ldy %lld is smaller than N %lld", (long long)ldy, (long long)N);
+  if (!w_packed || !y) return fail(FQL_ERR_INVALID, "null pointer");
+  if (reinterpret_cast<uintptr_t>(w_packed) % 16 != 0)
+    return fail(FQL_ERR_INVALID, "packed weight must be 16-byte aligned");
+  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, x_aligned != 0);
+  if (plan.kind == 0 || (plan.kind == 4 && plan.fq))
+    return fail(FQL_ERR_UNSUPPORTED, "this call's plan quantizes inside the GEMM (%s)",
+                fql::describe_plan(plan).c_str());
+  if (int r = check_workspace(workspace, workspace_bytes, plan.total_bytes)) return r;
+  return hip_status(fql::launch_linear_gemm(plan, static_cast<const uint8_t*>(w_packed), M, N, alpha,
+                                            static_cast<const uint16_t*>(bias),
+                                            static_cast<uint16_t*>(y), ldy,
+                                            static_cast<uint8_t*>(workspace),
+                                            static_cast<hipStream_t>(stream)),
+                    "gemm launch");
+}
+
+// ---- host-side scalars of the layer -------------------------------------------
+
+int fql_nvfp4_global_scale(float amax, float* global_scale) {
+  if (!global_scale) return fail(FQL_ERR_INVALID, "null pointer");
+  if (!std::isfinite(amax) || amax < 0.0f)
+    return fail(FQL_ERR_INVALID, "amax must be finite and >= 0 (got %g)", (double)amax);
+  if (amax == 0.0f) {
+    *global_scale = 1.0f;
+  } else {
+    const float g = 2688.0f / amax;  // fl32(448 * 6 / amax), a correctly rounded division
+    const float cap = 0x1p118f;      // keeps g / (smallest E4M3 scale 2^-9) finite
+    *global_scale = g < cap ? g : cap;
+  }
+  return ok();
+}
+
+int fql_nvfp4_alpha(float input_global_scale, float weight_global_scale, float* alpha) {
+  if (!alpha) return fail(FQL_ERR_INVALID, "null pointer");
+  if (int r = check_scale(input_global_scale, "input_global_scale")) return r;
+  if (int r = check_scale(weight_global_scale, "weight_global_scale")) return r;
+  *alpha = (float)((1.0 / (double)input_global_scale) * (1.0 / (double)weight_global_scale));
+  return ok();
+}
+
+int fql_fp8_scale(float amax, float* scale) {
+  if (!scale) return fail(FQL_ERR_INVALID, "null pointer");
+  if (!std::isfinite(amax) || amax < 0.0f)
+    return fail(FQL_ERR_INVALID, "amax must be finite and >= 0 (got %g)", (double)amax);
+  const float s = (float)((double)amax / 448.0);
+  *scale = s > 0.0f ? s : 1.0f;  // an all-zero tensor (or one whose amax / 448 underflows) takes 1
+  return ok();
+}
+
+int fql_fp8_output_scale(float input_scale, float weight_scale, float* alpha) {
+  if (!alpha) return fail(FQL_ERR_INVALID, "null pointer");
+  if (int r = check_scale(input_scale, "input_scale")) return r;
+  if (int r = check_scale(weight_scale, "weight_scale")) return r;
+  *alpha = (float)((double)input_scale * (double)weight_scale);
+  return ok();
+}
+
+int fql_set_plan_override(int which, const char* spec) {
+  if (which != FQL_PLAN_NVFP4 && which != FQL_PLAN_SC_GEMM && which != FQL_PLAN_SC_GEMV)
+    return fail(FQL_ERR_INVALID, "unknown plan override %d", which);
+  static_assert(FQL_PLAN_NVFP4 == fql::kOverrideNvfp4 && FQL_PLAN_SC_GEMM == fql::kOverrideScGemm &&
+                    FQL_PLAN_SC_GEMV == fql::kOverrideScGemv,
+                "override numbering");
+  fql::set_plan_override(which, spec);
+  return ok();
 }
 
 // ---- general block-diagonal transform, dynamic global scale ------------------
@@ -396,7 +614,7 @@ int linear_nvfp4_extras(const void* x, int64_t M, int64_t K, int64_t ldx, float 
     return fail(FQL_ERR_INVALID, "packed weight must be 16-byte and workspace 256-byte aligned");
   // a plan whose quantizer pass writes the GEMM's operand (x_hat or the packed
   // activation), since the fused small-M kernel quantizes with a host-side scale
-  const fql::GemmPlan plan = fql::plan_gemm_nvfp4(M, N, K, false);
+  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, false);
   if (workspace_bytes < (size_t)plan.total_bytes)
     return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
                 (long long)plan.total_bytes);
@@ -517,7 +735,7 @@ int sc_workspace_bytes(int fmt, int64_t M, int64_t N, int64_t K, size_t* bytes) 
   if (!bytes) return fail(FQL_ERR_INVALID, "null pointer");
   if (int r = check_sc_shape(fmt, N, K, K, "N", true)) return r;
   if (M < 1) return fail(FQL_ERR_INVALID, "M must be >= 1");
-  *bytes = (size_t)fql::plan_sc_gemm(fmt, M, N, K).total_bytes;
+  *bytes = (size_t)fql::cached_plan_sc_gemm(fmt, M, N, K).total_bytes;
   return ok();
 }
 
@@ -530,7 +748,8 @@ int sc_describe(int fmt, int64_t M, int64_t N, int64_t K, char* buf, size_t len)
 
 int sc_linear(int fmt, const void* x, int64_t M, int64_t K, int64_t ldx, float input_scale,
               const void* w_packed, int64_t N, float alpha, const void* bias, void* y, int64_t ldy,
-              void* workspace, size_t workspace_bytes, void* stream) {
+              void* workspace, size_t workspace_bytes, void* stream,
+              const float* alpha_dev = nullptr) {
   if (int r = check_sc_shape(fmt, M, K, ldx, "M", false)) return r;
   if (int r = check_sc_shape(fmt, N, K, K, "N", true)) return r;
   if (!std::isfinite(alpha)) return fail(FQL_ERR_INVALID, "alpha must be finite");
@@ -544,7 +763,7 @@ int sc_linear(int fmt, const void* x, int64_t M, int64_t K, int64_t ldx, float i
   if (reinterpret_cast<uintptr_t>(w_packed) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(FQL_ERR_INVALID, "packed weight must be 16-byte and workspace 256-byte aligned");
-  const fql::ScPlan plan = fql::plan_sc_gemm(fmt, M, N, K);
+  const fql::ScPlan plan = fql::cached_plan_sc_gemm(fmt, M, N, K);
   if (workspace_bytes < (size_t)plan.total_bytes)
     return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
                 (long long)plan.total_bytes);
@@ -554,7 +773,7 @@ int sc_linear(int fmt, const void* x, int64_t M, int64_t K, int64_t ldx, float i
     return fail(FQL_ERR_INVALID, "activation too large");
   hipError_t e = fql::launch_sc_linear(
       plan, static_cast<const uint16_t*>(x), M, K, ldx, aligned16(x, ldx, 2), inv,
-      static_cast<const uint8_t*>(w_packed), N, alpha, static_cast<const uint16_t*>(bias),
+      static_cast<const uint8_t*>(w_packed), N, alpha, alpha_dev, static_cast<const uint16_t*>(bias),
       static_cast<uint16_t*>(y), ldy, static_cast<uint8_t*>(workspace), static_cast<hipStream_t>(stream));
   return hip_status(e, "linear launch");
 }
@@ -648,6 +867,16 @@ int fql_linear_fp8(const void* x, int64_t M, int64_t K, int64_t ldx, float input
                    int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
   return sc_linear(fql::SC_FP8, x, M, K, ldx, input_scale, w_packed, N, alpha, bias, y, ldy,
                    workspace, workspace_bytes, stream);
+}
+
+int fql_linear_fp8_dev_alpha(const void* x, int64_t M, int64_t K, int64_t ldx, float input_scale,
+                             const void* w_packed, int64_t N, const float* alpha_dev,
+                             const void* bias, void* y, int64_t ldy, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!alpha_dev || reinterpret_cast<uintptr_t>(alpha_dev) % 4 != 0)
+    return fail(FQL_ERR_INVALID, "alpha_dev must be a 4-byte aligned device pointer");
+  return sc_linear(fql::SC_FP8, x, M, K, ldx, input_scale, w_packed, N, 0.0f, bias, y, ldy,
+                   workspace, workspace_bytes, stream, alpha_dev);
 }
 
 // block FP8

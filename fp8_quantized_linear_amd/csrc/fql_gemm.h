@@ -185,16 +185,16 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void_t*)(p);
 }
 // 16 (or 4) bytes per lane from sbase + voff into LDS at lds + lane * 16 (or 4).
-// sbase and lds must be wave-uniform.
+// sbase and lds must be wave-uniform. The LDS address travels in M0, passed
+// as the asm statement's "{m0}" operand: the compiler writes M0 itself and
+// knows the statement reads it, so no M0 value of its own can be disturbed.
 __device__ __forceinline__ void lds_load16(const void* sbase, uint32_t voff, uint32_t lds) {
   lds = __builtin_amdgcn_readfirstlane(lds);  // uniform by contract; keeps it in an SGPR
-  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
-                   : "memory");
+  __asm__ volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 __device__ __forceinline__ void lds_load4(const void* sbase, uint32_t voff, uint32_t lds) {
   lds = __builtin_amdgcn_readfirstlane(lds);
-  __asm__ volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
-                   : "memory");
+  __asm__ volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 // A wave-uniform address the compiler cannot prove uniform (e.g. formed inside
 // a lane-dependent branch), moved to scalar registers for the loads above.

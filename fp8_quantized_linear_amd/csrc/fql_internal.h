@@ -34,6 +34,17 @@ struct PackedDims {
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 inline PackedDims packed_dims(int64_t N, int64_t K) { return PackedDims{round_up(N, 16), round_up(K, 128)}; }
 
+// ---- launch-plan overrides -------------------------------------------------
+// Benchmarking aid: a spec that replaces the plan heuristics (results change
+// at most in the order of the float32 sum over K). Each starts as the
+// environment variable FQL_PLAN, FQL_SC_PLAN or FQL_SC_GEMV, read once, and
+// can be replaced at run time (fql_set_plan_override); every change bumps a
+// generation number that invalidates the plan caches.
+enum PlanOverrideKind { kOverrideNvfp4 = 0, kOverrideScGemm = 1, kOverrideScGemv = 2 };
+std::string plan_override(int which);  // "" when unset
+void set_plan_override(int which, const char* spec);
+uint32_t plan_generation();
+
 // ---- launchers (stream-ordered, return the launch status) -----------------
 hipError_t launch_quant_nvfp4_bf16(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float g,
                                    int hb, bool aligned, uint8_t* codes, uint8_t* scales,
@@ -65,8 +76,9 @@ hipError_t launch_unpack_nvfp4(const uint8_t* packed, int64_t N, int64_t K, uint
 //           workgroup quantizes the activation into LDS and computes one
 //           16-column tile over the full K, its waves splitting K.
 //   kind 1: quantizer kernel (x_hat in A-fragment order) + tiled GEMM.
-//   kind 2: quantizer kernel + LDS-ring tiled GEMM (direct global->LDS loads).
-//   kind 3: as kind 2 on 32x32x16 MFMAs (mt, nt count 32-row / 32-column tiles).
+//   kind 3: quantizer kernel + LDS-ring tiled GEMM on 32x32x16 MFMAs (direct
+//           global->LDS loads; mt, nt count 32-row / 32-column tiles).
+//   kind 4: quantizer kernel (packed activation) + per-wave-ring small-M GEMM.
 // Workspace layout: [arrival counters | x_hat | split-K partial slabs]. The
 // counters must be zero before the first call on a workspace; every call
 // leaves them zero again.
@@ -75,7 +87,7 @@ struct GemmPlan {
   int mt;             // kind 1: 16-row M tiles per wave
   int nt;             // kind 1: 16-column N tiles per wave
   int wm;             // kind 1: wave rows (the 4 waves form a wm x 4/wm grid)
-  int st;             // kind 2: LDS ring depth (chunks)
+  int st;             // kinds 3, 4: LDS ring depth (chunks)
   int64_t Mp;         // M padded to a whole number of M tiles
   int64_t Np, Kp;     // packed weight dims
   int64_t groups;     // output tiles (workgroups per split)
@@ -96,11 +108,13 @@ struct GemmPlan {
 // fused small-M kernel needs it. Workspace sizes of both kinds are covered by
 // the aligned=false plan, which never needs less.
 GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned);
+// The same plan from a small per-thread cache (keyed by the shape, the
+// alignment and the override generation), so a hot call plans once per shape.
+GemmPlan cached_plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned);
 
-// Whether gemm_tiled_kernel<mt, nt, wm> / gemm_lds_kernel<mt, nt, st> is built
-// into the library.
+// Whether gemm_tiled_kernel<mt, nt, wm> / gemm_lds32_kernel<mt, nt, st> is
+// built into the library.
 bool tiled_config_built(int mt, int nt, int wm);
-bool lds_config_built(int mt, int nt, int st);
 bool lds32_config_built(int mt, int nt, int st);
 bool gemv_ring_config_built(int w, int mt, int nt, int d, bool packed_a);
 
@@ -151,8 +165,8 @@ hipError_t launch_dynamic_scale(float* scal, float g_w, bool with_alpha, hipStre
 hipError_t launch_zero_words(uint32_t* p, int n, hipStream_t st);
 
 // Optional parts of a linear call: a general transform T (b = hb) in place
-// of the Hadamard rotation, and device-resident g / alpha. Needs a plan that
-// writes x_hat (the aligned = false plan).
+// of the Hadamard rotation (needs a plan with a quantizer pass: the
+// aligned = false plan), and device-resident g / alpha (any plan).
 struct LinearExtras {
   const uint16_t* T;
   bool t_aligned;
@@ -165,6 +179,16 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
                                int64_t N, float alpha, const uint16_t* bias, uint16_t* y,
                                int64_t ldy, uint8_t* workspace, hipStream_t st,
                                const LinearExtras* ex = nullptr);
+// The two halves of launch_linear_nvfp4 for plans with a quantizer pass
+// (has_quant_pass): the quantizer writes the activation operand into the
+// workspace, the GEMM reads it. Both together equal one launch_linear_nvfp4.
+bool has_quant_pass(const GemmPlan& p, int hb, bool aligned, int64_t K, const LinearExtras* ex);
+hipError_t launch_linear_quant(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K,
+                               int64_t ldx, float g, int hb, bool aligned, uint8_t* workspace,
+                               hipStream_t st, const LinearExtras* ex = nullptr);
+hipError_t launch_linear_gemm(const GemmPlan& p, const uint8_t* packed, int64_t M, int64_t N,
+                              float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
+                              uint8_t* workspace, hipStream_t st, const LinearExtras* ex = nullptr);
 
 // ---- scaled-MFMA formats: MXFP4, MXFP8, per-tensor FP8, block FP8 ---------
 // All four run on v_mfma_scale_f32_16x16x128_f8f6f4 (one instruction per
@@ -203,6 +227,7 @@ struct ScPlan {
   int64_t dyn_lds;  // GEMV with fq: dynamic LDS bytes (the activation operand)
 };
 ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K);
+ScPlan cached_plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K);
 std::string describe_sc_plan(const ScPlan& p);
 
 // Canonical quantizers: codes [rows][K/2] (FP4) or [rows][K] (FP8);
@@ -216,10 +241,11 @@ hipError_t launch_sc_quant(int fmt, bool f32_input, bool weight_tiles, const voi
 hipError_t launch_sc_pack(int fmt, const uint8_t* codes, const void* scales, int64_t N, int64_t K,
                           uint8_t* packed, hipStream_t st);
 // Activation quantize (straight into the operand layout) + GEMM + epilogue.
+// alpha_dev (nullable): the output scale read from device memory instead of alpha.
 hipError_t launch_sc_linear(const ScPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                             bool aligned, float inv_scale, const uint8_t* packed, int64_t N,
-                            float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
-                            uint8_t* workspace, hipStream_t st);
+                            float alpha, const float* alpha_dev, const uint16_t* bias, uint16_t* y,
+                            int64_t ldy, uint8_t* workspace, hipStream_t st);
 // Activation operand quantizer used by launch_sc_linear.
 hipError_t launch_sc_quant_operand(int fmt, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                    bool aligned, float inv_scale, int64_t Mp, uint8_t* codes,

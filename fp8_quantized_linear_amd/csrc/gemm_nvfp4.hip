@@ -336,10 +336,12 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
 //  compiler knows no asm statement can touch.)
 template <int W, int NTW, int HB, int RC, int QPRE>
 __global__ __launch_bounds__(64 * W) void linear_gemv_kernel(
-    const uint16_t* x, int M, int K, int64_t ldx, float g, int aligned16,
-    const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales, int N, int64_t Kp,
-    int ntiles, float alpha, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-    int64_t ldy) {
+    const uint16_t* x, int M, int K, int64_t ldx, float g, const float* __restrict__ g_dev,
+    int aligned16, const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales, int N,
+    int64_t Kp, int ntiles, float alpha, const float* __restrict__ alpha_dev,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t ldy) {
+  if (g_dev != nullptr) g = *g_dev;  // scales kept in device memory
+  if (alpha_dev != nullptr) alpha = *alpha_dev;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint4v* xs = reinterpret_cast<uint4v*>(smem);  // [M][Kp/8] 16-byte groups, swizzled
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -656,217 +658,24 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// LDS-ring tiled kernel (x_hat from the quantizer kernel)
-// ---------------------------------------------------------------------------
-//
-// Workgroup: 4 waves; tile (MT*16) rows x (4*NT*16) columns; wave w owns
-// columns [w*NT*16, (w+1)*NT*16) of the tile and all of its rows, so every
-// weight tile is dequantized by exactly one wave and the activation
-// fragments (read by all four waves) come from LDS.
-// Every global -> LDS transfer is a direct LDS load (global_load_lds_*), so
-// the data in flight holds no registers and an ST-deep ring of per-chunk
-// stages runs ST-1 chunks (128-deep K slices) ahead of the MFMAs:
-//   A  [MT][4 ks][64 lanes] x 16 B   x_hat fragments (wave w loads ks = w)
-//   Bq [4 waves][NT][64 lanes] x 16 B  weight code slots
-//   Bs [4 waves][NT][64 lanes] x 4 B   the lane's scale dword of the chunk
-// The loads are issued with inline assembly and waited for with explicit
-// s_waitcnt vmcnt(n): the compiler does not track LDS-DMA completion per
-// stage and would otherwise wait for the whole ring before every LDS read.
-template <int MT, int NT>
-struct LdsStage {
-  uint4v a[MT * 4][64];
-  uint4v bq[4 * NT][64];
-  uint32_t bs[4 * NT][64];
-};
-
-template <int MT, int NT, int ST, int OCC>
-__global__ __launch_bounds__(256, OCC) void gemm_lds_kernel(
-    const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
-    const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, int ngroups,
-    int kc_per_split, int splits, float alpha,
-    const float* __restrict__ alpha_dev, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ y, int64_t ldy, float4v* __restrict__ partial,
-    uint32_t* __restrict__ counters) {
-  if (alpha_dev != nullptr) alpha = *alpha_dev;  // per-call scale computed on the device
-  static_assert(ST >= 3 && ST <= 4, "ring depth (chunk i+1 must be issued a whole chunk ahead)");
-  constexpr int L = MT + 2 * NT;  // LDS loads per chunk per wave
-  static_assert(L * (ST - 2) <= 63, "vmcnt range");
-  __shared__ LdsStage<MT, NT> stage[ST];
-  __shared__ uint32_t s_flag;
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t KC = Kp / 128;
-  const int64_t KC4 = (KC + 3) / 4;
-  const int split = blockIdx.x % splits;
-  const int tilegrp = blockIdx.x / splits;
-  const int ngroup = tilegrp % ngroups;
-  const int mgroup = tilegrp / ngroups;
-  const int64_t c_begin = (int64_t)split * kc_per_split;
-  const int64_t c_end = c_begin + kc_per_split < KC ? c_begin + kc_per_split : KC;
-  const int nch = (int)(c_end - c_begin);
-  const int tile0 = (ngroup * 4 + wave) * NT;
-
-  // wave-uniform global bases; per-lane byte offsets
-  const uint8_t* a_base = reinterpret_cast<const uint8_t*>(xhat) +
-                          ((int64_t)mgroup * MT * (Kp / 32) + wave) * 1024;  // + f*KS*1024 + c*4096
-  const uint32_t a_voff = lane * 16;
-  const uint8_t* q_base[NT];
-  const uint8_t* s_base[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int64_t t = tile0 + nt < ntiles ? tile0 + nt : 0;  // invalid tiles read tile 0, never stored
-    q_base[nt] = wcodes + t * KC * 1024;                       // + c*1024
-    s_base[nt] = wscales + t * KC4 * 512;                      // + (c/4)*512 + (c%4)*4
-  }
-  const uint32_t q_voff = lane * 16;
-  const uint32_t s_voff = ((lane & 15) * 2 + (lane >> 5)) * 16;
-
-  // LDS load number e (0 <= e < L) of chunk c into stage sg; chunks past the
-  // range are clamped (a static number of loads per chunk)
-  auto issue_one = [&](LdsStage<MT, NT>& sg, int64_t c, int e) {
-    c = c < c_end ? c : c_end - 1;
-    if (e < MT) {
-      lds_load16(a_base + ((int64_t)e * (Kp / 32) + c * 4) * 1024, a_voff, lds_offset(&sg.a[e * 4 + wave][0]));
-    } else if (e < MT + NT) {
-      const int nt = e - MT;
-      lds_load16(q_base[nt] + c * 1024, q_voff, lds_offset(&sg.bq[wave * NT + nt][0]));
-    } else {
-      const int nt = e - MT - NT;
-      lds_load4(s_base[nt] + (c >> 2) * 512 + (c & 3) * 4, s_voff, lds_offset(&sg.bs[wave * NT + nt][0]));
-    }
-  };
-  auto issue = [&](LdsStage<MT, NT>& sg, int64_t c) {
-#pragma unroll
-    for (int e = 0; e < L; ++e) issue_one(sg, c, e);
-  };
-
-  float4v acc[MT][NT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = float4v{0.f, 0.f, 0.f, 0.f};
-
-  // Software pipeline. A chunk is four 32-deep K steps; step ks issues the
-  // LDS reads of step ks+1's activation fragments, then its own MFMAs
-  // interleaved with the dequantization of step ks+1's weight fragments (one
-  // wave per SIMD: VALU work only overlaps the matrix pipe when it is issued
-  // between the MFMAs, in program order). Between steps 2 and 3 the wave
-  // waits for the next chunk's stage, passes the workgroup barrier, refills
-  // the stage it has finished reading, and reads the next chunk's weight
-  // codes and first activation fragments, which step 3's MFMAs then hide.
-  constexpr int MFMAS = MT * NT;                    // per K step
-  constexpr int VPM = (8 * NT + MFMAS - 1) / MFMAS;  // dequantization VALU ops per MFMA
-  uint4v bq[NT];
-  uint32_t bsw[NT];
-  half8 bf[2][NT];
-  uint4v af[2][MT];
-  // the wave's own codes and scales (only its own loads must have landed)
-  auto read_head_b = [&](const LdsStage<MT, NT>& sg) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      bq[nt] = sg.bq[wave * NT + nt][lane];
-      bsw[nt] = sg.bs[wave * NT + nt][lane];
-    }
-  };
-  // the first step's activation fragments (loaded by all waves)
-  auto read_head_a = [&](const LdsStage<MT, NT>& sg) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) af[0][mt] = sg.a[mt * 4][lane];
-  };
-  auto read_head = [&](const LdsStage<MT, NT>& sg) {
-    read_head_b(sg);
-    read_head_a(sg);
-  };
-  auto dequant = [&](int buf, int ks) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) bf[buf][nt] = b_fragment(dword_of(bq[nt], ks), ChunkScales(bsw[nt])[ks]);
-  };
-  auto mfmas = [&](int buf) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const half8 a = __builtin_bit_cast(half8, af[buf][mt]);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[buf][nt], acc[mt][nt], 0, 0, 0);
-    }
-  };
-  // steps 0..2 of a chunk held in stage sg; refill receives chunk rc's loads,
-  // spread over the steps so that the address unit works while the MFMAs run
-  auto steps012 = [&](const LdsStage<MT, NT>& sg, LdsStage<MT, NT>& refill, int64_t rc) {
-#pragma unroll
-    for (int ks = 0; ks < 3; ++ks) {
-      const int cur = ks & 1, nxt = cur ^ 1;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) af[nxt][mt] = sg.a[mt * 4 + ks + 1][lane];
-#pragma unroll
-      for (int e = ks * L / 3; e < (ks + 1) * L / 3; ++e) issue_one(refill, rc, e);
-      __builtin_amdgcn_sched_barrier(0);
-      dequant(nxt, ks + 1);
-      mfmas(cur);
-#pragma unroll
-      for (int i = 0; i < MFMAS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // prologue: chunks 0 .. ST-2 in flight, chunk 0's head in registers
-#pragma unroll
-  for (int p = 0; p < ST - 1; ++p) issue(stage[p], c_begin + p);
-  wait_vmcnt<L * (ST - 2)>();
-  stage_barrier();
-  read_head(stage[0]);
-  dequant(0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // Ring protocol: chunk i lives in stage i % ST (the loop is unrolled by ST
-  // so that every stage index is a compile-time constant). While chunk i is
-  // computed, stage (i-1) % ST (chunk i-1's, freed by the previous mid-chunk
-  // barrier; for i = 0 the one stage the prologue left empty) receives chunk
-  // i+ST-1. At the mid-chunk barrier of chunk i, chunk i+1 has landed and
-  // everyone has finished reading chunk i's activation fragments.
-  for (int i0 = 0; i0 < nch; i0 += ST) {
-#pragma unroll
-    for (int j = 0; j < ST; ++j) {
-      if (i0 + j < nch) {
-        steps012(stage[j], stage[(j + ST - 1) % ST], c_begin + i0 + j + ST - 1);
-        const bool more = i0 + j + 1 < nch;
-        wait_vmcnt<L * (ST - 2)>();  // this wave's loads of chunk i+1 have landed
-        if (more) read_head_b(stage[(j + 1) % ST]);
-        stage_barrier();             // everyone's have, and stage j has been read by all
-        if (more) read_head_a(stage[(j + 1) % ST]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (more) dequant(0, 0);
-        mfmas(1);
-        // the head reads need time: the first MFMAs go out alone
-#pragma unroll
-        for (int i = 0; i < MFMAS; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i >= MFMAS / 4) __builtin_amdgcn_sched_group_barrier(0x002, VPM + 1, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-  wait_vmcnt<0>();  // no LDS load may still be in flight when the workgroup ends
-
-  float4v* slab = partial + (int64_t)tilegrp * splits * (4 * MT * NT * 64);
-  finish_tile<MT, NT, 1>(acc, M, N, mgroup * MT * 16, ngroup * 4 * NT * 16, split, splits, alpha,
-                         bias, y, ldy, slab, counters + tilegrp, &s_flag);
-}
-
-// ---------------------------------------------------------------------------
 // LDS-ring tiled kernel on 32x32x16 MFMAs
 // ---------------------------------------------------------------------------
 //
-// Same ring and pipeline as gemm_lds_kernel, with v_mfma_f32_32x32x16_f16:
-// each MFMA is twice the work of a 16x16x32 one for the same operand bytes,
-// so a wave spends half as many issue slots on MFMAs and the dequantization,
-// LDS reads and loads fit between them. One 16-deep K step is exactly one
-// NVFP4 block, so a weight fragment carries a single scale per lane.
+// Workgroup: 4 waves; wave w owns a column slice of the tile and all of its
+// rows, so every weight tile is dequantized by exactly one wave and the
+// activation fragments (read by all four waves) come from LDS. Every global
+// -> LDS transfer is a direct LDS load (global_load_lds_*), so the data in
+// flight holds no registers and an ST-deep ring of per-chunk stages runs
+// ST-1 chunks (128-deep K slices) ahead of the MFMAs. The loads are issued
+// with inline assembly and waited for with explicit s_waitcnt vmcnt(n): the
+// compiler does not track LDS-DMA completion per stage and would otherwise
+// wait for the whole ring before every LDS read.
+// The MFMA is v_mfma_f32_32x32x16_f16: twice the work of a 16x16x32 one for
+// the same operand bytes, so a wave spends half as many issue slots on MFMAs
+// and the dequantization, LDS reads and loads fit between them (one wave per
+// SIMD: VALU work only overlaps the matrix pipe when it is issued between the
+// MFMAs, in program order). One 16-deep K step is exactly one NVFP4 block, so
+// a weight fragment carries a single scale per lane.
 //   Workgroup tile (MT*32) rows x (4*NT*32) columns; wave w owns columns
 //   [w*NT*32, (w+1)*NT*32) and all rows.
 //   A fragment (32 rows x 16 k) of step s: lane l takes row l%32 and
@@ -977,10 +786,11 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[a][b] = float16v{};
 
-  // Software pipeline over the eight 16-deep steps of a chunk (see
-  // gemm_lds_kernel): step s issues the LDS reads of step s+1's activation
-  // fragments, then its MFMAs interleaved with step s+1's dequantization;
-  // between steps 6 and 7 the wave moves to the next chunk's stage.
+  // Software pipeline over the eight 16-deep steps of a chunk: step s issues
+  // the LDS reads of step s+1's activation fragments, then its MFMAs
+  // interleaved with step s+1's dequantization; between steps 6 and 7 the
+  // wave waits for the next chunk's stage, passes the workgroup barrier and
+  // reads the next chunk's weight codes and first activation fragments.
   constexpr int MFMAS = MT * NT;                              // per step
   constexpr int VPM = (8 * NT + MFMAS - 1) / MFMAS;           // dequantization VALU per MFMA
   const int a_lane = ((lane & 31) >> 4) * 4 * 64 + hh * 16 + (lane & 15);  // within a[][] of stage
@@ -1096,17 +906,18 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
 
 static constexpr int kCUs = 256;
 
-// Benchmarking aid: FQL_PLAN="kind=0,waves=8,ntw=2,rc=4" or "kind=1,mt=4,nt=1,splits=2"
-// overrides the launch-plan heuristics (no effect on results, only on speed).
+// Benchmarking aid: the override spec "kind=0,waves=8,ntw=2,rc=4" or
+// "kind=1,mt=4,nt=1,splits=2" (FQL_PLAN, or fql_set_plan_override) replaces
+// the launch-plan heuristics (results change at most in the order of the
+// float32 sum over K).
 struct GemmOverride {
   int kind = -1, waves = 0, ntw = 0, rc = 0, mt = 0, nt = 0, wm = 0, st = 0, splits = 0, fq = -1, pa = -1,
       il = -1;
 };
 static GemmOverride gemm_override() {
   GemmOverride o;
-  const char* e = std::getenv("FQL_PLAN");
-  if (!e) return o;
-  std::string s(e);
+  const std::string s = plan_override(kOverrideNvfp4);
+  if (s.empty()) return o;
   size_t pos = 0;
   while (pos < s.size()) {
     size_t end = s.find(',', pos);
@@ -1155,7 +966,7 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
   // narrow layers with K = 4096 (N < 16384), up to M = 16; long K (K = 14336)
   // and wide layers stream better through kinds 4 and 1 once M > 1.
   if (ov.kind < 0 && gemv_ok && M > 1 && (p.Kp >= 8192 || N >= 16384)) gemv_ok = false;
-  if (gemv_ok && ov.kind != 1 && ov.kind != 4) {
+  if (gemv_ok && ov.kind <= 0) {
     // one workgroup per NTW 16-column tiles over the full K (no cross-workgroup reduction)
     p.kind = 0;
     p.mt = 1;
@@ -1165,7 +976,7 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     p.waves = ntiles < 1024 ? 8 : 4;
     p.ntw = M > 1 && ntiles < 1024 ? 2 : 1;
     if (ov.waves == 4 || ov.waves == 8) p.waves = ov.waves;  // the built kind-0 widths
-    if (ov.ntw) p.ntw = ov.ntw;
+    if (ov.ntw == 1 || ov.ntw == 2) p.ntw = ov.ntw;
     const int64_t cpw = (KC + p.waves - 1) / p.waves;
     p.kcmax = cpw <= 8 ? 4 : 8;  // register ring depth (chunks)
     if (ov.rc) p.kcmax = ov.rc;
@@ -1177,14 +988,14 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     p.xhat_bytes = 0;
     p.lds_bytes = std::max<int64_t>(M * p.Kp * 2, (int64_t)p.waves * p.ntw * 1024);
   } else {
-    // Workgroup tile (WM*MT*16) x ((4/WM)*NT*16); kind 2 always has WM = 1.
+    // Workgroup tile (WM*MT*16) x ((4/WM)*NT*16) (kind 1) or (MT*32) x (4*NT*32) (kind 3).
     // Defaults (measured on the decode and prefill layer shapes): up to 32
     // rows the per-wave-ring kernel, except wide layers with short K (gate_up)
     // above 16 rows, which stream better through the register-staged tiled
     // kernel; from 33 rows on the LDS-ring kernel on 32x32 MFMAs.
     const bool wide_short = N >= 16384 && p.Kp < 8192;
     p.kind = M <= 32 ? (wide_short && M > 16 ? 1 : 4) : 3;
-    if (ov.kind >= 1 && ov.kind <= 4) p.kind = ov.kind;
+    if (ov.kind == 1 || ov.kind == 3 || ov.kind == 4) p.kind = ov.kind;
     if (p.kind == 4) {
       // per-wave rings: W waves split K, NT tiles per workgroup, D chunks in flight
       p.mt = (int)((M + 15) / 16);
@@ -1219,9 +1030,10 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
       }
       p.kind = 1;
     }
-    // kind 3 addresses the packed blob with 32-bit per-lane offsets
-    if (p.kind == 3 && d.total_bytes() >= ((int64_t)1 << 32)) p.kind = 2;
-    const bool lds_ring = p.kind >= 2;
+    // kind 3 addresses the packed blob with 32-bit per-lane offsets; the
+    // tiled kernel's 64-bit addresses take weights of 4 GiB and more
+    if (p.kind == 3 && d.total_bytes() >= ((int64_t)1 << 32)) p.kind = 1;
+    const bool lds_ring = p.kind == 3;
     p.wm = 1;
     p.st = 3;
     if (!lds_ring) {
@@ -1230,7 +1042,7 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
       else if (M <= 64) { p.mt = 2; p.nt = 2; p.wm = 2; }
       else if (M <= 128) { p.mt = 4; p.nt = 2; p.wm = 2; }
       else { p.mt = 8; p.nt = 4; }
-    } else if (p.kind == 3) {  // 32x32 tiles: MT x 32 rows, 4 x NT x 32 columns
+    } else {  // kind 3, 32x32 tiles: MT x 32 rows, 4 x NT x 32 columns
       if (M <= 128) {
         // 128 x 128 tiles when they alone fill the GPU, else 64 x 128 tiles
         // with a deeper ring and split K
@@ -1239,10 +1051,6 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
       } else {
         p.mt = 4; p.nt = 2; p.st = 3;
       }
-    } else if (M <= 128) {
-      p.mt = 4; p.nt = 2;
-    } else {
-      p.mt = 4; p.nt = 4;
     }
     if (ov.mt || ov.nt || ov.wm || ov.st) {
       if (ov.mt) p.mt = ov.mt;
@@ -1250,9 +1058,8 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
       if (ov.wm && !lds_ring) p.wm = ov.wm;
       if (ov.st) p.st = ov.st;
     }
-    const bool built = p.kind == 3   ? lds32_config_built(p.mt, p.nt, p.st)
-                       : p.kind == 2 ? lds_config_built(p.mt, p.nt, p.st)
-                                     : tiled_config_built(p.mt, p.nt, p.wm);
+    const bool built = p.kind == 3 ? lds32_config_built(p.mt, p.nt, p.st)
+                                   : tiled_config_built(p.mt, p.nt, p.wm);
     if (!built) { p.kind = 1; p.mt = 1; p.nt = 1; p.wm = 1; }
     // rows and 16-column tiles per workgroup
     const int tile_rows = p.kind == 3 ? 32 * p.mt : 16 * p.mt * p.wm;
@@ -1270,8 +1077,6 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     const int64_t max_splits = KC >= 144 ? 6 : 4;
     if (groups < 192) s = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(max_splits, KC), 256 / groups));
     if (ov.splits) s = std::min<int64_t>(ov.splits, KC);
-    // the LDS ring runs deeper when a split-K tile has few chunks to hide latency in
-    if (p.kind == 2 && !ov.st && s > 1 && lds_config_built(p.mt, p.nt, 4)) p.st = 4;
     p.kc_per_split = (int)((KC + s - 1) / s);
     p.splits = (int)((KC + p.kc_per_split - 1) / p.kc_per_split);
     p.groups = groups;
@@ -1297,10 +1102,6 @@ std::string describe_plan(const GemmPlan& p) {
     std::snprintf(b, sizeof(b),
                   "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d> grid=%lld splits=%d",
                   p.mt, p.nt, p.st, (long long)(p.groups * p.splits), p.splits);
-  } else if (p.kind == 2) {
-    std::snprintf(b, sizeof(b),
-                  "quant_nvfp4_xhat_kernel + gemm_lds_kernel<MT=%d,NT=%d,ST=%d> grid=%lld splits=%d",
-                  p.mt, p.nt, p.st, (long long)(p.groups * p.splits), p.splits);
   } else if (p.kind == 0) {
     std::snprintf(b, sizeof(b), "linear_gemv_kernel<W=%d,NTW=%d,RC=%d,QPRE=%d> grid=%lld lds=%lld",
                   p.waves, p.ntw, p.kcmax, p.qpre, (long long)p.groups, (long long)p.lds_bytes);
@@ -1312,47 +1113,63 @@ std::string describe_plan(const GemmPlan& p) {
   return std::string(b);
 }
 
+// Arguments of one fused small-M launch (kind 0).
+struct GemvLaunch {
+  const GemmPlan* p;
+  const uint16_t* x;
+  int64_t M, K, ldx;
+  float g;
+  bool aligned;
+  const uint8_t* packed;
+  int64_t N;
+  float alpha;
+  const float* g_dev;
+  const float* alpha_dev;
+  const uint16_t* bias;
+  uint16_t* y;
+  int64_t ldy;
+  hipStream_t st;
+};
+
 template <int W, int NTW, int HB, int RC, int QPRE>
-static void launch_gemv_t(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                          float g, bool aligned, const uint8_t* packed, int64_t N, float alpha,
-                          const uint16_t* bias, uint16_t* y, int64_t ldy, hipStream_t st) {
-  const uint8_t* wcodes = packed;
-  const uint8_t* wscales = packed + p.Np * p.Kp / 2;
-  linear_gemv_kernel<W, NTW, HB, RC, QPRE><<<(unsigned)p.groups, 64 * W, (size_t)p.lds_bytes, st>>>(
-      x, (int)M, (int)K, ldx, g, aligned ? 1 : 0, wcodes, wscales, (int)N, p.Kp,
-      (int)(p.Np / 16), alpha, bias, y, ldy);
+static void launch_gemv_t(const GemvLaunch& a) {
+  const GemmPlan& p = *a.p;
+  const uint8_t* wcodes = a.packed;
+  const uint8_t* wscales = a.packed + p.Np * p.Kp / 2;
+  linear_gemv_kernel<W, NTW, HB, RC, QPRE><<<(unsigned)p.groups, 64 * W, (size_t)p.lds_bytes, a.st>>>(
+      a.x, (int)a.M, (int)a.K, a.ldx, a.g, a.g_dev, a.aligned ? 1 : 0, wcodes, wscales, (int)a.N,
+      p.Kp, (int)(p.Np / 16), a.alpha, a.alpha_dev, a.bias, a.y, a.ldy);
 }
 
 template <int W, int NTW, int HB>
-static void launch_gemv_q(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                          float g, bool aligned, const uint8_t* packed, int64_t N, float alpha,
-                          const uint16_t* bias, uint16_t* y, int64_t ldy, hipStream_t st) {
-#define FQL_GEMV_ARGS p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st
+static void launch_gemv_q(const GemvLaunch& a) {
+  const GemmPlan& p = *a.p;
   if (p.kcmax == 4) {
-    if (p.qpre == 1) launch_gemv_t<W, NTW, HB, 4, 1>(FQL_GEMV_ARGS);
-    else if (p.qpre == 2) launch_gemv_t<W, NTW, HB, 4, 2>(FQL_GEMV_ARGS);
-    else launch_gemv_t<W, NTW, HB, 4, 4>(FQL_GEMV_ARGS);
+    if (p.qpre == 1) launch_gemv_t<W, NTW, HB, 4, 1>(a);
+    else if (p.qpre == 2) launch_gemv_t<W, NTW, HB, 4, 2>(a);
+    else launch_gemv_t<W, NTW, HB, 4, 4>(a);
   } else {
-    if (p.qpre == 1) launch_gemv_t<W, NTW, HB, 8, 1>(FQL_GEMV_ARGS);
-    else if (p.qpre == 2) launch_gemv_t<W, NTW, HB, 8, 2>(FQL_GEMV_ARGS);
-    else launch_gemv_t<W, NTW, HB, 8, 4>(FQL_GEMV_ARGS);
+    if (p.qpre == 1) launch_gemv_t<W, NTW, HB, 8, 1>(a);
+    else if (p.qpre == 2) launch_gemv_t<W, NTW, HB, 8, 2>(a);
+    else launch_gemv_t<W, NTW, HB, 8, 4>(a);
   }
 }
 
+// The built kind-0 shapes: 4 or 8 waves, one or two 16-column tiles per workgroup.
+static bool gemv_shape_built(int waves, int ntw) {
+  return (waves == 4 || waves == 8) && (ntw == 1 || ntw == 2);
+}
+
 template <int HB>
-static void launch_gemv_hb(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
-                           float g, bool aligned, const uint8_t* packed, int64_t N, float alpha,
-                           const uint16_t* bias, uint16_t* y, int64_t ldy, hipStream_t st) {
+static void launch_gemv_hb(const GemvLaunch& a) {
+  const GemmPlan& p = *a.p;
   if (p.waves == 8) {
-    if (p.ntw == 1) launch_gemv_q<8, 1, HB>(FQL_GEMV_ARGS);
-    else if (p.ntw == 2) launch_gemv_q<8, 2, HB>(FQL_GEMV_ARGS);
-    else launch_gemv_q<8, 4, HB>(FQL_GEMV_ARGS);
+    if (p.ntw == 1) launch_gemv_q<8, 1, HB>(a);
+    else launch_gemv_q<8, 2, HB>(a);
   } else {
-    if (p.ntw == 1) launch_gemv_q<4, 1, HB>(FQL_GEMV_ARGS);
-    else if (p.ntw == 2) launch_gemv_q<4, 2, HB>(FQL_GEMV_ARGS);
-    else launch_gemv_q<4, 4, HB>(FQL_GEMV_ARGS);
+    if (p.ntw == 1) launch_gemv_q<4, 1, HB>(a);
+    else launch_gemv_q<4, 2, HB>(a);
   }
-#undef FQL_GEMV_ARGS
 }
 
 template <int MT, int NT, int WM>
@@ -1370,36 +1187,9 @@ static hipError_t launch_tiled_t(const GemmPlan& p, const _Float16* xhat, const 
 }
 
 // The (MT, NT, WM) tiled configurations built into the library.
-#define FQL_TILED_CONFIGS(X) \
-  X(1, 1, 1) X(2, 1, 1) X(4, 1, 1) X(8, 1, 1) X(8, 2, 1) X(4, 4, 1) X(8, 4, 1) \
-  X(2, 2, 2) X(4, 2, 2) X(2, 4, 2) X(4, 4, 2) X(1, 4, 4) X(2, 4, 4) X(2, 2, 4)
-
-template <int MT, int NT, int ST, int OCC>
-static hipError_t launch_lds_t(const GemmPlan& p, const _Float16* xhat, const uint8_t* packed,
-                               int64_t M, int64_t N, float alpha, const float* alpha_dev,
-                                 const uint16_t* bias,
-                               uint16_t* y, int64_t ldy, float4v* partial, uint32_t* counters,
-                               hipStream_t st) {
-  const uint8_t* wcodes = packed;
-  const uint8_t* wscales = packed + p.Np * p.Kp / 2;
-  gemm_lds_kernel<MT, NT, ST, OCC><<<(unsigned)(p.groups * p.splits), 256, 0, st>>>(
-      xhat, wcodes, wscales, (int)M, (int)N, p.Kp, (int)(p.Np / 16), (int)p.ngroups,
-      p.kc_per_split, p.splits, alpha, alpha_dev, bias, y, ldy, partial, counters);
-  return hipGetLastError();
-}
-
-// The (MT, NT, ST, OCC) LDS-ring configurations built into the library
-// (OCC: workgroups per CU the register and LDS budgets are sized for).
-#define FQL_LDS_CONFIGS(X) \
-  X(1, 4, 4, 1) X(2, 4, 4, 1) X(4, 4, 3, 1) X(4, 4, 4, 1) X(8, 4, 3, 1) X(4, 2, 4, 1) X(8, 2, 3, 1) \
-  X(2, 2, 4, 1) X(4, 2, 3, 2) X(2, 4, 3, 1) X(2, 2, 3, 2)
-
-bool lds_config_built(int mt, int nt, int st) {
-#define FQL_X(A, B, C, D) if (mt == A && nt == B && st == C) return true;
-  FQL_LDS_CONFIGS(FQL_X)
-#undef FQL_X
-  return false;
-}
+// (the planner's choices: M <= 16, <= 32, <= 64, <= 128 and larger, the last
+// for weights of 4 GiB or more, whose offsets exceed the 32-bit ring kernel's)
+#define FQL_TILED_CONFIGS(X) X(1, 1, 1) X(2, 1, 1) X(2, 2, 2) X(4, 2, 2) X(8, 4, 1)
 
 template <int MT, int NT, int ST, int OCC>
 static hipError_t launch_lds32_t(const GemmPlan& p, const _Float16* xhat, const uint8_t* packed,
@@ -1427,14 +1217,14 @@ bool lds32_config_built(int mt, int nt, int st) {
   return false;
 }
 
-// The (W, MT, NT, D) per-wave-ring configurations built into the library.
-#define FQL_GEMV_RING_CONFIGS(X) \
-  X(4, 1, 2, 3) X(4, 1, 2, 4) X(4, 1, 4, 3) X(8, 1, 1, 3) X(8, 1, 2, 3) X(4, 2, 2, 3) X(4, 2, 1, 4)
+// The (W, MT, NT, D) per-wave-ring configurations built into the library
+// (the planner's choices: 4 waves with 2 tiles, wide short-K layers 4 tiles,
+// long K 8 waves with one tile, each for one or two row tiles).
+#define FQL_GEMV_RING_CONFIGS(X) X(4, 1, 2, 3) X(4, 1, 4, 3) X(8, 1, 1, 3) X(4, 2, 2, 3)
 
-// Further (W, MT, NT, D) configurations built only with the packed activation,
-// whose stages are small enough for more waves or deeper rings.
-#define FQL_GEMV_RING_PA_CONFIGS(X) \
-  X(8, 1, 1, 4) X(16, 1, 1, 3) X(8, 2, 1, 3) X(8, 2, 1, 4) X(4, 2, 4, 3) X(8, 2, 2, 3)
+// Configurations built only with the packed activation, whose stages are
+// small enough for 8 waves of two row tiles.
+#define FQL_GEMV_RING_PA_CONFIGS(X) X(8, 2, 1, 3)
 
 bool gemv_ring_config_built(int w, int mt, int nt, int d, bool packed_a) {
 #define FQL_X(A, B, C, E) if (w == A && mt == B && nt == C && d == E) return true;
@@ -1453,64 +1243,59 @@ bool tiled_config_built(int mt, int nt, int wm) {
   return false;
 }
 
-hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K,
-                               int64_t ldx, float g, int hb, bool aligned, const uint8_t* packed,
-                               int64_t N, float alpha, const uint16_t* bias, uint16_t* y,
-                               int64_t ldy, uint8_t* workspace, hipStream_t st,
-                               const LinearExtras* ex) {
-  uint32_t* counters = reinterpret_cast<uint32_t*>(workspace);
-  _Float16* xhat = reinterpret_cast<_Float16*>(workspace + p.counter_bytes);
-  float* partial = reinterpret_cast<float*>(workspace + p.counter_bytes + p.xhat_bytes);
+// Workspace regions of a plan: [arrival counters | activation operand | split-K slabs].
+static uint32_t* ws_counters(uint8_t* ws) { return reinterpret_cast<uint32_t*>(ws); }
+static uint8_t* ws_operand(const GemmPlan& p, uint8_t* ws) { return ws + p.counter_bytes; }
+static float4v* ws_partial(const GemmPlan& p, uint8_t* ws) {
+  return reinterpret_cast<float4v*>(ws + p.counter_bytes + p.xhat_bytes);
+}
+
+// kind 4 quantizing inside the GEMM (FQ = 1): no quantizer pass
+static bool fused_ring(const GemmPlan& p, int hb, bool aligned, int64_t K, const LinearExtras* ex) {
+  return ex == nullptr && p.kind == 4 && p.fq && hb == 0 && aligned && K % 128 == 0;
+}
+
+bool has_quant_pass(const GemmPlan& p, int hb, bool aligned, int64_t K, const LinearExtras* ex) {
+  return p.kind != 0 && !fused_ring(p, hb, aligned, K, ex);
+}
+
+hipError_t launch_linear_quant(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K,
+                               int64_t ldx, float g, int hb, bool aligned, uint8_t* workspace,
+                               hipStream_t st, const LinearExtras* ex) {
+  if (!has_quant_pass(p, hb, aligned, K, ex)) return hipErrorInvalidValue;
+  const bool transform = ex != nullptr && ex->T != nullptr;
+  const float* g_dev = ex != nullptr ? ex->g_dev : nullptr;
+  uint8_t* operand = ws_operand(p, workspace);
+  // the packed activation (kind 4 with pa) or x_hat, from the plain quantizer or the transform's
+  const bool packed_a = p.kind == 4 && p.pa;
+  if (packed_a && p.Mp != 16 * p.mt) return hipErrorInvalidValue;
+  if (transform) {
+    TransformArgs ta{};
+    ta.mode = packed_a ? 4 : 1;
+    ta.x = x; ta.M = M; ta.K = K; ta.ldx = ldx; ta.aligned = ex->t_aligned;
+    ta.T = ex->T; ta.b = hb; ta.g = g; ta.g_dev = g_dev;
+    ta.xhat = reinterpret_cast<_Float16*>(operand); ta.rows_out = p.Mp; ta.Kp = p.Kp;
+    return launch_transform_nvfp4(ta, st);
+  }
+  if (packed_a)
+    return launch_quant_nvfp4_apack(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp, operand, g_dev, st);
+  return launch_quant_nvfp4_xhat(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp,
+                                 reinterpret_cast<_Float16*>(operand), g_dev, st);
+}
+
+// The GEMM of kinds 1, 3 and 4 on the operand in the workspace (or, for the
+// fused kind 4, on x itself).
+static hipError_t launch_gemm_part(const GemmPlan& p, const uint16_t* x, int64_t ldx, float g,
+                                   bool fused, const uint8_t* packed, int64_t M, int64_t N,
+                                   float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
+                                   uint8_t* workspace, hipStream_t st, const LinearExtras* ex) {
   const float* alpha_dev = ex != nullptr ? ex->alpha_dev : nullptr;
+  uint32_t* counters = ws_counters(workspace);
+  _Float16* xhat = reinterpret_cast<_Float16*>(ws_operand(p, workspace));
+  float4v* partial4 = ws_partial(p, workspace);
   if (p.splits > 1 && p.groups > (p.counter_bytes - kWorkspaceScalarBytes) / 4) return hipErrorInvalidValue;
-  if (p.kind == 0 && ex != nullptr) return hipErrorInvalidValue;  // needs a plan that writes x_hat
-  if (p.kind == 0 && aligned) {  // the fused path reads x rows with 16-byte loads
-    switch (hb) {
-      case 0: launch_gemv_hb<0>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st); break;
-      case 16: launch_gemv_hb<16>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st); break;
-      case 32: launch_gemv_hb<32>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st); break;
-      case 64: launch_gemv_hb<64>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st); break;
-      case 128: launch_gemv_hb<128>(p, x, M, K, ldx, g, aligned, packed, N, alpha, bias, y, ldy, st); break;
-      default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-  }
-  if (p.kind == 0) return hipErrorInvalidValue;  // caller re-plans unaligned inputs as kind 1
-  const bool fused = ex == nullptr && p.kind == 4 && p.fq && hb == 0 && aligned && K % 128 == 0;
-  // the packed activation comes from the packed mode of the quantizer pass or of the transform
-  const bool packed_a = !fused && p.kind == 4 && p.pa;
-  if (packed_a) {
-    if (p.Mp != 16 * p.mt) return hipErrorInvalidValue;
-    hipError_t e;
-    if (ex != nullptr && ex->T != nullptr) {
-      TransformArgs ta{};
-      ta.mode = 4;  // packed activation
-      ta.x = x; ta.M = M; ta.K = K; ta.ldx = ldx; ta.aligned = ex->t_aligned;
-      ta.T = ex->T; ta.b = hb; ta.g = g; ta.g_dev = ex->g_dev;
-      ta.xhat = xhat; ta.rows_out = p.Mp; ta.Kp = p.Kp;
-      e = launch_transform_nvfp4(ta, st);
-    } else {
-      e = launch_quant_nvfp4_apack(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp, reinterpret_cast<uint8_t*>(xhat),
-                                   ex != nullptr ? ex->g_dev : nullptr, st);
-    }
-    if (e != hipSuccess) return e;
-  } else if (!fused) {
-    hipError_t e;
-    if (ex != nullptr && ex->T != nullptr) {
-      TransformArgs ta{};
-      ta.mode = 1;  // x_hat
-      ta.x = x; ta.M = M; ta.K = K; ta.ldx = ldx; ta.aligned = ex->t_aligned;
-      ta.T = ex->T; ta.b = hb; ta.g = g; ta.g_dev = ex->g_dev;
-      ta.xhat = xhat; ta.rows_out = p.Mp; ta.Kp = p.Kp;
-      e = launch_transform_nvfp4(ta, st);
-    } else {
-      e = launch_quant_nvfp4_xhat(x, M, K, ldx, g, hb, aligned, p.Mp, p.Kp, xhat,
-                                  ex != nullptr ? ex->g_dev : nullptr, st);
-    }
-    if (e != hipSuccess) return e;
-  }
-  float4v* partial4 = reinterpret_cast<float4v*>(partial);
   if (p.kind == 4) {
+    const bool packed_a = !fused && p.pa;
 #define FQL_X(A, B, C, E)                                                                             \
   if (p.waves == A && p.mt == B && p.nt == C && p.st == E) {                                          \
     if (fused)                                                                                        \
@@ -1550,20 +1335,51 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
 #undef FQL_X
     return hipErrorInvalidValue;
   }
-  if (p.kind == 2) {
-#define FQL_X(A, B, C, D)                                                                        \
-  if (p.mt == A && p.nt == B && p.st == C)                                                       \
-    return launch_lds_t<A, B, C, D>(p, xhat, packed, M, N, alpha, alpha_dev, bias, y, ldy, partial4, counters, st);
-    FQL_LDS_CONFIGS(FQL_X)
-#undef FQL_X
-    return hipErrorInvalidValue;
-  }
+  if (p.kind != 1) return hipErrorInvalidValue;
 #define FQL_X(A, B, C)                                                                           \
   if (p.mt == A && p.nt == B && p.wm == C)                                                       \
     return launch_tiled_t<A, B, C>(p, xhat, packed, M, N, alpha, alpha_dev, bias, y, ldy, partial4, counters, st);
   FQL_TILED_CONFIGS(FQL_X)
 #undef FQL_X
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_linear_gemm(const GemmPlan& p, const uint8_t* packed, int64_t M, int64_t N,
+                              float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
+                              uint8_t* workspace, hipStream_t st, const LinearExtras* ex) {
+  if (p.kind == 0 || (p.kind == 4 && p.fq)) return hipErrorInvalidValue;  // no separate operand
+  return launch_gemm_part(p, nullptr, 0, 0.0f, false, packed, M, N, alpha, bias, y, ldy, workspace,
+                          st, ex);
+}
+
+hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K,
+                               int64_t ldx, float g, int hb, bool aligned, const uint8_t* packed,
+                               int64_t N, float alpha, const uint16_t* bias, uint16_t* y,
+                               int64_t ldy, uint8_t* workspace, hipStream_t st,
+                               const LinearExtras* ex) {
+  if (p.kind == 0) {
+    // the fused path reads x rows with 16-byte loads and cannot apply a general transform
+    if (!aligned || (ex != nullptr && ex->T != nullptr)) return hipErrorInvalidValue;
+    if (!gemv_shape_built(p.waves, p.ntw)) return hipErrorInvalidValue;
+    const GemvLaunch a{&p, x, M, K, ldx, g, aligned, packed, N, alpha,
+                       ex != nullptr ? ex->g_dev : nullptr, ex != nullptr ? ex->alpha_dev : nullptr,
+                       bias, y, ldy, st};
+    switch (hb) {
+      case 0: launch_gemv_hb<0>(a); break;
+      case 16: launch_gemv_hb<16>(a); break;
+      case 32: launch_gemv_hb<32>(a); break;
+      case 64: launch_gemv_hb<64>(a); break;
+      case 128: launch_gemv_hb<128>(a); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
+  const bool fused = fused_ring(p, hb, aligned, K, ex);
+  if (!fused) {
+    const hipError_t e = launch_linear_quant(p, x, M, K, ldx, g, hb, aligned, workspace, st, ex);
+    if (e != hipSuccess) return e;
+  }
+  return launch_gemm_part(p, x, ldx, g, fused, packed, M, N, alpha, bias, y, ldy, workspace, st, ex);
 }
 
 }  // namespace fql

@@ -75,8 +75,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
     const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
     const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales, int M, int N,
     int64_t KC, int ntiles_w, int64_t quads_w, int ngroups, int kc_per_split, int splits,
-    float alpha, const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t ldy,
-    float4v* __restrict__ partial, uint32_t* __restrict__ counters) {
+    float alpha, const float* __restrict__ alpha_dev, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ y, int64_t ldy, float4v* __restrict__ partial,
+    uint32_t* __restrict__ counters) {
+  if (alpha_dev != nullptr) alpha = *alpha_dev;  // output scale kept in device memory
   typedef ScTraits<F> T;
   typedef ScStage<F, WM, WN, MTW, NTW> Stage;
   constexpr int NW = WM * WN, H = T::H, TA = Stage::TA, TB = Stage::TB;
@@ -340,9 +342,10 @@ template <int F, int W, int MT, int NT, int D, int FQ>
 __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
     const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
     const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales, int M, int N,
-    int64_t KC, int ntiles_w, int64_t quads_w, float alpha, const uint16_t* __restrict__ bias,
-    uint16_t* __restrict__ y, int64_t ldy, const uint16_t* __restrict__ x, int64_t ldx,
-    int aligned, float inv_scale, int64_t K) {
+    int64_t KC, int ntiles_w, int64_t quads_w, float alpha, const float* __restrict__ alpha_dev,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t ldy,
+    const uint16_t* __restrict__ x, int64_t ldx, int aligned, float inv_scale, int64_t K) {
+  if (alpha_dev != nullptr) alpha = *alpha_dev;  // output scale kept in device memory
   typedef ScTraits<F> T;
   typedef ScvStage<F, MT, NT, FQ> Stage;
   constexpr int H = T::H;
@@ -571,21 +574,29 @@ __global__ __launch_bounds__(64 * W) void gemv_sc_kernel(
 // configurations, plan, launcher
 // ---------------------------------------------------------------------------
 
-// (WM, WN, MTW, NTW, ST) built for every format; FP8 formats skip the ones
-// whose ring does not fit in LDS (see sc_config_fits).
-#define FQL_SC_CONFIGS(X, F)                                                                    \
-  X(F, 1, 4, 1, 4, 4) X(F, 1, 4, 2, 4, 4) X(F, 1, 4, 4, 2, 4) X(F, 2, 2, 4, 4, 3)              \
-  X(F, 2, 4, 4, 4, 3) X(F, 2, 4, 8, 4, 4) X(F, 4, 2, 4, 4, 3) X(F, 1, 4, 1, 2, 4)              \
-  X(F, 1, 4, 1, 2, 8) X(F, 1, 4, 4, 2, 6)
+// (WM, WN, MTW, NTW, ST) GEMM configurations built (the planner's choices:
+// 64 x 128 tiles up to M = 128, 128 x 128 for 8-bit formats up to M = 512,
+// then 256 x 128 for 8-bit formats and 256 x 256 for FP4, whose ring alone
+// fits in LDS; 16 x 128 tiles as the fallback).
+#define FQL_SC_CONFIGS_ANY(X, F) \
+  X(F, 1, 4, 4, 2, 4) X(F, 2, 2, 4, 4, 3) X(F, 4, 2, 4, 4, 3) X(F, 1, 4, 1, 2, 4)
+#define FQL_SC_CONFIGS_FP4(X, F) FQL_SC_CONFIGS_ANY(X, F) X(F, 2, 4, 8, 4, 4)
+#define FQL_SC_CONFIGS_ALL(X) \
+  FQL_SC_CONFIGS_FP4(X, SC_MXFP4) FQL_SC_CONFIGS_ANY(X, SC_MXFP8) FQL_SC_CONFIGS_ANY(X, SC_FP8) \
+  FQL_SC_CONFIGS_ANY(X, SC_FP8_BLOCK)
 
-// (W, MT, NT, D) GEMV configurations built for every format.
-#define FQL_SCV_CONFIGS(X, F)                                                                   \
-  X(F, 4, 1, 2, 4) X(F, 4, 1, 2, 6) X(F, 8, 1, 2, 3) X(F, 4, 1, 4, 3) X(F, 8, 1, 1, 4)          \
-  X(F, 4, 2, 2, 3) X(F, 8, 2, 1, 3) X(F, 4, 1, 2, 3) X(F, 8, 1, 1, 3)
+// (W, MT, NT, D) GEMV configurations built: 4 waves, one row tile with four
+// (FP4) or two (8-bit) column tiles, two row tiles with two column tiles.
+#define FQL_SCV_CONFIGS_FP4(X, F) X(F, 4, 1, 4, 3) X(F, 4, 2, 2, 3)
+#define FQL_SCV_CONFIGS_FP8(X, F) X(F, 4, 1, 2, 3) X(F, 4, 2, 2, 3)
+#define FQL_SCV_CONFIGS_ALL(X) \
+  FQL_SCV_CONFIGS_FP4(X, SC_MXFP4) FQL_SCV_CONFIGS_FP8(X, SC_MXFP8) FQL_SCV_CONFIGS_FP8(X, SC_FP8) \
+  FQL_SCV_CONFIGS_FP8(X, SC_FP8_BLOCK)
 
-// The (W, MT, NT, D) GEMV configurations also built with the activation
-// quantized in the workgroup (FQ = 1): the decode defaults.
-#define FQL_SCV_FUSED_CONFIGS(X, F) X(F, 4, 1, 4, 3) X(F, 4, 1, 2, 3)
+// The GEMV configurations also built with the activation quantized in the
+// workgroup (FQ = 1): the one-row-tile decode defaults.
+#define FQL_SCV_FUSED_CONFIGS_ALL(X) \
+  X(SC_MXFP4, 4, 1, 4, 3) X(SC_MXFP8, 4, 1, 2, 3) X(SC_FP8, 4, 1, 2, 3) X(SC_FP8_BLOCK, 4, 1, 2, 3)
 
 template <int F, int W, int MT, int NT, int D>
 static constexpr bool scv_config_fits() {
@@ -595,8 +606,7 @@ static constexpr bool scv_config_fits() {
 static bool scv_config_built(int fmt, int w, int mt, int nt, int d) {
 #define FQL_X(F0, A, B, C, E) \
   if (fmt == F0 && w == A && mt == B && nt == C && d == E) return scv_config_fits<F0, A, B, C, E>();
-  FQL_SCV_CONFIGS(FQL_X, SC_MXFP4) FQL_SCV_CONFIGS(FQL_X, SC_MXFP8) FQL_SCV_CONFIGS(FQL_X, SC_FP8)
-  FQL_SCV_CONFIGS(FQL_X, SC_FP8_BLOCK)
+  FQL_SCV_CONFIGS_ALL(FQL_X)
 #undef FQL_X
   return false;
 }
@@ -610,8 +620,7 @@ static int64_t scv_fused_lds(int fmt, int w, int mt, int nt, int d, int64_t KC, 
 #define FQL_X(F0, A, B, C, E)                                                                     \
   if (fmt == F0 && w == A && mt == B && nt == C && d == E)                                         \
     return (int64_t)sizeof(ScvStage<F0, B, C, 1>) * A * E + dyn <= 160 * 1024 ? dyn : 0;
-  FQL_SCV_FUSED_CONFIGS(FQL_X, SC_MXFP4) FQL_SCV_FUSED_CONFIGS(FQL_X, SC_MXFP8)
-  FQL_SCV_FUSED_CONFIGS(FQL_X, SC_FP8) FQL_SCV_FUSED_CONFIGS(FQL_X, SC_FP8_BLOCK)
+  FQL_SCV_FUSED_CONFIGS_ALL(FQL_X)
 #undef FQL_X
   return 0;
 }
@@ -627,8 +636,7 @@ static bool sc_config_built(int fmt, int wm, int wn, int mtw, int ntw, int st) {
 #define FQL_X(F0, A, B, C, D, E)                                                                 \
   if (fmt == F0 && wm == A && wn == B && mtw == C && ntw == D && st == E)                        \
     return sc_config_fits<F0, A, B, C, D, E>();
-  FQL_SC_CONFIGS(FQL_X, SC_MXFP4) FQL_SC_CONFIGS(FQL_X, SC_MXFP8) FQL_SC_CONFIGS(FQL_X, SC_FP8)
-  FQL_SC_CONFIGS(FQL_X, SC_FP8_BLOCK)
+  FQL_SC_CONFIGS_ALL(FQL_X)
 #undef FQL_X
   return false;
 }
@@ -663,16 +671,18 @@ ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
     else { gw = 4; gnt = 2; gd = 3; }
     bool forced = false;
     int fq = -1;  // -1: fused when built and it fits
-    if (const char* e = std::getenv("FQL_SC_GEMV")) {  // benchmarking aid: "W,NT,D[,FQ]" (0 = off)
+    const std::string gemv_spec = plan_override(kOverrideScGemv);
+    const std::string gemm_spec = plan_override(kOverrideScGemm);
+    if (!gemv_spec.empty()) {  // benchmarking aid: "W,NT,D[,FQ]" (0 = off)
       int a = 0, b = 0, c = 0, f = -1;
-      const int k = std::sscanf(e, "%d,%d,%d,%d", &a, &b, &c, &f);
+      const int k = std::sscanf(gemv_spec.c_str(), "%d,%d,%d,%d", &a, &b, &c, &f);
       if (k >= 1 && a == 0) gemv = false;
       else if (k >= 3 && M <= 64 && scv_config_built(fmt, a, mt, b, c)) {
         gemv = true; gw = a; gnt = b; gd = c; forced = true;
         if (k == 4) fq = f;
       }
     }
-    if (std::getenv("FQL_SC_PLAN")) gemv = forced;
+    if (!gemm_spec.empty()) gemv = forced;
     if (gemv && scv_config_built(fmt, gw, mt, gnt, gd)) {
       p.kind = 1;
       p.wm = 1; p.wn = gw; p.mtw = mt; p.ntw = gnt; p.st = gd;
@@ -695,15 +705,15 @@ ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
     }
   }
   int splits_override = 0;
-  if (const char* e = std::getenv("FQL_SC_PLAN")) {  // benchmarking aid: "wm,wn,mtw,ntw,st,splits"
+  const std::string gemm_spec = plan_override(kOverrideScGemm);
+  if (!gemm_spec.empty()) {  // benchmarking aid: "wm,wn,mtw,ntw,st,splits"
     int a = 0, b = 0, c = 0, d = 0, f = 0, s = 0;
-    if (std::sscanf(e, "%d,%d,%d,%d,%d,%d", &a, &b, &c, &d, &f, &s) >= 5 &&
+    if (std::sscanf(gemm_spec.c_str(), "%d,%d,%d,%d,%d,%d", &a, &b, &c, &d, &f, &s) >= 5 &&
         sc_config_built(fmt, a, b, c, d, f)) {
       wm = a; wn = b; mtw = c; ntw = d; st = f; splits_override = s;
     }
   }
-  if (!sc_config_built(fmt, wm, wn, mtw, ntw, st)) { wm = 1; wn = 4; mtw = 1; ntw = 4; st = fp4 ? 4 : 3; }
-  if (!sc_config_built(fmt, wm, wn, mtw, ntw, st)) { ntw = 2; st = 4; }
+  if (!sc_config_built(fmt, wm, wn, mtw, ntw, st)) { wm = 1; wn = 4; mtw = 1; ntw = 2; st = 4; }
   p.wm = wm; p.wn = wn; p.mtw = mtw; p.ntw = ntw; p.st = st;
   const int tile_rows = 16 * wm * mtw, tile_cols = 16 * wn * ntw;
   p.Mp = round_up(M, std::max(tile_rows, 16));
@@ -747,14 +757,14 @@ std::string describe_sc_plan(const ScPlan& p) {
 template <int F, int WM, int WN, int MTW, int NTW, int ST>
 static hipError_t launch_sc_t(const ScPlan& p, const uint8_t* xc, const uint8_t* xs,
                               const uint8_t* packed, const ScDims& w, int64_t M, int64_t N,
-                              float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
-                              float4v* partial, uint32_t* counters, hipStream_t st) {
+                              float alpha, const float* alpha_dev, const uint16_t* bias, uint16_t* y,
+                              int64_t ldy, float4v* partial, uint32_t* counters, hipStream_t st) {
   if constexpr (!sc_config_fits<F, WM, WN, MTW, NTW, ST>()) {
     return hipErrorInvalidValue;
   } else {
     gemm_sc_kernel<F, WM, WN, MTW, NTW, ST><<<(unsigned)(p.groups * p.splits), 64 * WM * WN, 0, st>>>(
         xc, xs, packed, packed + w.code_bytes, (int)M, (int)N, w.KC, (int)(w.rows_p / 16), w.quads,
-        (int)p.ngroups, p.kc_per_split, p.splits, alpha, bias, y, ldy, partial, counters);
+        (int)p.ngroups, p.kc_per_split, p.splits, alpha, alpha_dev, bias, y, ldy, partial, counters);
     return hipGetLastError();
   }
 }
@@ -762,14 +772,14 @@ static hipError_t launch_sc_t(const ScPlan& p, const uint8_t* xc, const uint8_t*
 template <int F, int W, int MT, int NT, int D>
 static hipError_t launch_scv_t(const ScPlan& p, const uint8_t* xc, const uint8_t* xs,
                                const uint8_t* packed, const ScDims& w, int64_t M, int64_t N,
-                               float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
-                               hipStream_t st) {
+                               float alpha, const float* alpha_dev, const uint16_t* bias,
+                               uint16_t* y, int64_t ldy, hipStream_t st) {
   if constexpr (!scv_config_fits<F, W, MT, NT, D>()) {
     return hipErrorInvalidValue;
   } else {
     gemv_sc_kernel<F, W, MT, NT, D, 0><<<(unsigned)p.groups, 64 * W, 0, st>>>(
         xc, xs, packed, packed + w.code_bytes, (int)M, (int)N, w.KC, (int)(w.rows_p / 16), w.quads,
-        alpha, bias, y, ldy, nullptr, 0, 0, 0.0f, 0);
+        alpha, alpha_dev, bias, y, ldy, nullptr, 0, 0, 0.0f, 0);
     return hipGetLastError();
   }
 }
@@ -778,18 +788,19 @@ template <int F, int W, int MT, int NT, int D>
 static hipError_t launch_scv_fused_t(const ScPlan& p, const uint16_t* x, int64_t ldx, bool aligned,
                                      float inv_scale, int64_t K, const uint8_t* packed,
                                      const ScDims& w, int64_t M, int64_t N, float alpha,
-                                     const uint16_t* bias, uint16_t* y, int64_t ldy, hipStream_t st) {
+                                     const float* alpha_dev, const uint16_t* bias, uint16_t* y,
+                                     int64_t ldy, hipStream_t st) {
   if (p.dyn_lds <= 0 || M > 16 * MT) return hipErrorInvalidValue;
   gemv_sc_kernel<F, W, MT, NT, D, 1><<<(unsigned)p.groups, 64 * W, (size_t)p.dyn_lds, st>>>(
       nullptr, nullptr, packed, packed + w.code_bytes, (int)M, (int)N, w.KC, (int)(w.rows_p / 16),
-      w.quads, alpha, bias, y, ldy, x, ldx, aligned ? 1 : 0, inv_scale, K);
+      w.quads, alpha, alpha_dev, bias, y, ldy, x, ldx, aligned ? 1 : 0, inv_scale, K);
   return hipGetLastError();
 }
 
 hipError_t launch_sc_linear(const ScPlan& p, const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                             bool aligned, float inv_scale, const uint8_t* packed, int64_t N,
-                            float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
-                            uint8_t* workspace, hipStream_t st) {
+                            float alpha, const float* alpha_dev, const uint16_t* bias, uint16_t* y,
+                            int64_t ldy, uint8_t* workspace, hipStream_t st) {
   const ScDims w = sc_dims(p.fmt, N, K, true);
   uint32_t* counters = reinterpret_cast<uint32_t*>(workspace);
   uint8_t* xc = workspace + p.counter_bytes;
@@ -800,9 +811,8 @@ hipError_t launch_sc_linear(const ScPlan& p, const uint16_t* x, int64_t M, int64
 #define FQL_X(F0, A, B, C, E)                                                                      \
   if (p.fmt == F0 && p.wn == A && p.mtw == B && p.ntw == C && p.st == E)                           \
     return launch_scv_fused_t<F0, A, B, C, E>(p, x, ldx, aligned, inv_scale, K, packed, w, M, N,    \
-                                              alpha, bias, y, ldy, st);
-    FQL_SCV_FUSED_CONFIGS(FQL_X, SC_MXFP4) FQL_SCV_FUSED_CONFIGS(FQL_X, SC_MXFP8)
-    FQL_SCV_FUSED_CONFIGS(FQL_X, SC_FP8) FQL_SCV_FUSED_CONFIGS(FQL_X, SC_FP8_BLOCK)
+                                              alpha, alpha_dev, bias, y, ldy, st);
+    FQL_SCV_FUSED_CONFIGS_ALL(FQL_X)
 #undef FQL_X
     return hipErrorInvalidValue;
   }
@@ -811,18 +821,17 @@ hipError_t launch_sc_linear(const ScPlan& p, const uint16_t* x, int64_t M, int64
   if (p.kind == 1) {
 #define FQL_X(F0, A, B, C, E)                                                                      \
   if (p.fmt == F0 && p.wn == A && p.mtw == B && p.ntw == C && p.st == E)                           \
-    return launch_scv_t<F0, A, B, C, E>(p, xc, xs, packed, w, M, N, alpha, bias, y, ldy, st);
-    FQL_SCV_CONFIGS(FQL_X, SC_MXFP4) FQL_SCV_CONFIGS(FQL_X, SC_MXFP8) FQL_SCV_CONFIGS(FQL_X, SC_FP8)
-    FQL_SCV_CONFIGS(FQL_X, SC_FP8_BLOCK)
+    return launch_scv_t<F0, A, B, C, E>(p, xc, xs, packed, w, M, N, alpha, alpha_dev, bias, y, ldy, \
+                                        st);
+    FQL_SCV_CONFIGS_ALL(FQL_X)
 #undef FQL_X
     return hipErrorInvalidValue;
   }
 #define FQL_X(F0, A, B, C, D, E)                                                                  \
   if (p.fmt == F0 && p.wm == A && p.wn == B && p.mtw == C && p.ntw == D && p.st == E)             \
-    return launch_sc_t<F0, A, B, C, D, E>(p, xc, xs, packed, w, M, N, alpha, bias, y, ldy, partial, \
-                                          counters, st);
-  FQL_SC_CONFIGS(FQL_X, SC_MXFP4) FQL_SC_CONFIGS(FQL_X, SC_MXFP8) FQL_SC_CONFIGS(FQL_X, SC_FP8)
-  FQL_SC_CONFIGS(FQL_X, SC_FP8_BLOCK)
+    return launch_sc_t<F0, A, B, C, D, E>(p, xc, xs, packed, w, M, N, alpha, alpha_dev, bias, y, ldy, \
+                                          partial, counters, st);
+  FQL_SC_CONFIGS_ALL(FQL_X)
 #undef FQL_X
   return hipErrorInvalidValue;
 }

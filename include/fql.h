@@ -183,6 +183,85 @@ int fql_linear_nvfp4(const void* x, int64_t M, int64_t K, int64_t ldx, float inp
                      const void* bias, void* y, int64_t ldy, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/*
+ * fql_linear_nvfp4 with alpha read from device memory (one float32 at
+ * alpha_dev, 4-byte aligned) instead of passed by value. A layer that keeps
+ * its alpha in device memory can re-pack new weights with a different
+ * weight global scale into the same storage, update that float in stream
+ * order, and replay HIP graphs captured before (the B12X write-up,
+ * Implementation: packed weight storage is reused in place so that captured
+ * graphs stay valid). Other arguments, the workspace and errors as
+ * fql_linear_nvfp4.
+ */
+int fql_linear_nvfp4_dev_alpha(const void* x, int64_t M, int64_t K, int64_t ldx,
+                               float input_global_scale, int hadamard_block, const void* w_packed,
+                               int64_t N, const float* alpha_dev, const void* bias, void* y,
+                               int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Diagnostics: the two halves of fql_linear_nvfp4, for launch plans that
+ * quantize the activation in a pass of their own (every plan but the
+ * one-launch small-M kernel and the opt-in in-GEMM quantization; those
+ * return FQL_ERR_UNSUPPORTED). fql_linear_nvfp4_quantize writes the GEMM's
+ * activation operand into the workspace exactly as fql_linear_nvfp4 does:
+ * at byte offset 65536 (after the arrival counters), either x_hat, the
+ * exactly dequantized values e2m1(q) * s as float16 in MFMA A-fragment order
+ * [Mp/16][Kp/32][64 lanes][8] (lane = kq*16 + m holds row m of the 16-row
+ * tile, k = 32*step + 8*kq + 0..7), or the packed activation (the packed
+ * weight layout of fql_pack_weight_nvfp4 with Mp rows); Mp and Kp are the
+ * row count and K padded with zeros (fql_linear_nvfp4_describe names the
+ * form: "xhat" or "apack"). fql_linear_nvfp4_gemm then runs the block-scaled
+ * GEMM and the epilogue on that operand; x_aligned says whether x had
+ * 16-byte aligned rows (pointer and stride), which selects the same plan.
+ * Called in this order on one stream and workspace, the pair computes
+ * exactly what one fql_linear_nvfp4 call computes.
+ */
+int fql_linear_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ldx,
+                              float input_global_scale, int hadamard_block, int64_t N,
+                              void* workspace, size_t workspace_bytes, void* stream);
+int fql_linear_nvfp4_gemm(int64_t M, int64_t K, int x_aligned, const void* w_packed, int64_t N,
+                          float alpha, const void* bias, void* y, int64_t ldy, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Host-side scalars of the layer (no device work, callable without a GPU).
+ * ------------------------------------------------------------------------- */
+
+/* NVFP4 activation or weight global scale from a calibration amax
+ * (TorchNvFp4LinearKernel: the input global scale is the inverse of the
+ * global dequant scale): g = fl32(448 * 6 / amax) (a correctly rounded
+ * float32 division), 1 when amax = 0, at most 2^118 (so g divided by the
+ * smallest nonzero E4M3 scale 2^-9 stays finite). amax must be finite and
+ * >= 0. */
+int fql_nvfp4_global_scale(float amax, float* global_scale);
+
+/* NVFP4 alpha, the product of the two global dequant scales
+ * (TorchNvFp4LinearKernel apply_weights): fl32((1/g_x) * (1/g_w)) evaluated
+ * in double precision and rounded once. Both scales finite and > 0. */
+int fql_nvfp4_alpha(float input_global_scale, float weight_global_scale, float* alpha);
+
+/* Per-tensor FP8 calibration scale: fl32(amax / 448), or 1 when that is 0
+ * (an all-zero tensor). amax finite and >= 0. */
+int fql_fp8_scale(float amax, float* scale);
+
+/* Per-tensor FP8 output scale (B12X write-up: the input and weight scales are
+ * merged into one output scale): fl32(input_scale * weight_scale), both
+ * finite and > 0. */
+int fql_fp8_output_scale(float input_scale, float weight_scale, float* alpha);
+
+/* Benchmarking aid: replace a launch-plan override. which: FQL_PLAN_NVFP4
+ * ("kind=K,waves=W,nt=N,st=S,splits=Z,..."), FQL_PLAN_SC_GEMM
+ * ("wm,wn,mtw,ntw,st[,splits]") or FQL_PLAN_SC_GEMV ("W,NT,D[,FQ]", or "0"
+ * for no GEMV); spec NULL or "" removes it. The initial values are the
+ * environment variables FQL_PLAN, FQL_SC_PLAN and FQL_SC_GEMV, read once.
+ * An override changes which kernel configuration runs, so results may differ
+ * in the float32 summation order over K, never otherwise; configurations
+ * that are not built are ignored. Host-side only. */
+#define FQL_PLAN_NVFP4 0
+#define FQL_PLAN_SC_GEMM 1
+#define FQL_PLAN_SC_GEMV 2
+int fql_set_plan_override(int which, const char* spec);
+
 /* ---------------------------------------------------------------------------
  * General block-diagonal transform and dynamic global scale ("QUTLASS NVFP4
  * online transforms" write-up: the fused quantizer accepts any
@@ -345,6 +424,13 @@ int fql_linear_fp8_describe(int64_t M, int64_t N, int64_t K, char* buf, size_t b
 int fql_linear_fp8(const void* x, int64_t M, int64_t K, int64_t ldx, float input_scale,
                    const void* w_packed, int64_t N, float alpha, const void* bias, void* y,
                    int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+/* fql_linear_fp8 with the output scale read from device memory (one float32
+ * at alpha_dev, 4-byte aligned), so a weight re-packed with a new weight
+ * scale only updates that float and captured graphs stay valid. */
+int fql_linear_fp8_dev_alpha(const void* x, int64_t M, int64_t K, int64_t ldx, float input_scale,
+                             const void* w_packed, int64_t N, const float* alpha_dev,
+                             const void* bias, void* y, int64_t ldy, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Block FP8 (B12X write-up, Implementation: the block FP8 kernel: activation

@@ -92,10 +92,12 @@ def activations(kind, M, K, config="decode", seed=0):
     return f32_to_bf16_bits(x)
 
 
-def weight(N, K, config="decode", seed=0, std=0.02):
-    """W [N, K] float32 ~ N(0, std^2)."""
+def weight(N, K, config="decode", seed=0, std=0.02, rows=None):
+    """W [N, K] float32 ~ N(0, std^2), or only its first `rows` rows (the same
+    values: the draws fill the matrix row by row)."""
     g = rng(STREAM_W, CONFIG_IDS[config], seed, N, K)
-    return (g.standard_normal((N, K), dtype=np.float32) * np.float32(std)).astype(np.float32)
+    n = N if rows is None else min(int(rows), N)
+    return (g.standard_normal((n, K), dtype=np.float32) * np.float32(std)).astype(np.float32)
 
 
 def bias(N, config="decode", seed=0, std=0.01):

@@ -28,3 +28,20 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture
+def plan_override():
+    """Set launch-plan overrides through the library (fql_set_plan_override) for
+    one test; every override the test set is removed afterwards."""
+    import fp8_quantized_linear_amd as fql
+
+    used = set()
+
+    def set_override(spec, which="nvfp4"):
+        fql.set_plan_override(spec, which)
+        used.add(which)
+
+    yield set_override
+    for which in used:
+        fql.set_plan_override(None, which)

@@ -67,8 +67,67 @@ def weight_case(config, N, K, hb, rows=None):
     """
     W = cached_weight(config, N, K)
     sel = W if rows is None else W[list(rows)]
-    amax = Q.amax_for_calibration(sel, hb)
-    gw = Q.global_scale_from_amax(amax)
     Wr = fwht_fp32(sel, hb) if hb else sel
+    gw = Q.global_scale_from_amax(Q.amax_for_calibration(Wr))  # amax of the rotated rows
     codes, scales = Q.quant_nvfp4(Wr, gw)
     return W, gw, codes, scales
+
+
+@functools.lru_cache(maxsize=8)
+def weight_hat(config, N, K, hb):
+    """The oracle's exactly decoded weight (G1, float64 [N, K]) of weight_case."""
+    _, _, codes, scales = weight_case(config, N, K, hb)
+    return Q.dequant_nvfp4(codes, scales)
+
+
+def full_rows_sample(M, n=256, seed=0):
+    """A seeded, sorted sample of n distinct rows of M (all rows when M <= n),
+    always holding the first and the last row."""
+    if M <= n:
+        return np.arange(M)
+    r = np.random.default_rng(seed)
+    rows = np.sort(r.choice(np.arange(1, M - 1), n - 2, replace=False))
+    return np.concatenate([[0], rows, [M - 1]])
+
+
+def plan_rows(plan, M):
+    """Rows Mp of the activation operand a launch plan writes (M padded to its row tile)."""
+    import re
+
+    m = re.search(r"gemm_lds32_kernel<MT=(\d+)", plan)
+    if m:
+        t = 32 * int(m.group(1))
+    elif "gemm_tiled_kernel" in plan:
+        m = re.search(r"gemm_tiled_kernel<MT=(\d+),NT=\d+,WM=(\d+)>", plan)
+        t = 16 * int(m.group(1)) * int(m.group(2))
+    else:
+        m = re.search(r"gemv_ring_kernel<W=\d+,MT=(\d+)", plan)
+        return 16 * int(m.group(1))
+    return -(-M // t) * t
+
+
+def decode_xhat(buf, Mp, Kp):
+    """x_hat operand (float16 in MFMA A-fragment order [Mp/16][Kp/32][64 lanes][8],
+    lane = kq*16 + m holding row m, k = 32*step + 8*kq + 0..7) -> float64 [Mp, Kp]."""
+    h = np.frombuffer(buf, dtype=np.float16, count=Mp * Kp)
+    h = h.reshape(Mp // 16, Kp // 32, 4, 16, 8).transpose(0, 3, 1, 2, 4)
+    return h.reshape(Mp, Kp).astype(np.float64)
+
+
+def decode_packed(buf, rows_p, Kp):
+    """Packed NVFP4 layout (the packed weight's, also the packed activation's)
+    -> canonical (codes uint8 [rows_p, Kp/2], scales uint8 [rows_p, Kp/16]).
+
+    codes [rows_p/16][KC][64 lanes][16 B]: lane = kq*16 + n, dword j holds the
+    eight codes of row n at k = 128c + 32j + 8kq + 0..7, element i in nibble i.
+    scales [rows_p/16][ceil(KC/4)][32 slots][16 B]: slot n*2 + h, byte 4q + j is
+    the scale of row n, 16-block 8c + 2j + h of chunk c = 4*group + q.
+    """
+    T, KC = rows_p // 16, Kp // 128
+    KC4 = -(-KC // 4)
+    b = np.frombuffer(buf, dtype=np.uint8)
+    c = b[:rows_p * Kp // 2].reshape(T, KC, 4, 16, 4, 4).transpose(0, 3, 1, 4, 2, 5)
+    codes = c.reshape(rows_p, Kp // 2)
+    s = b[rows_p * Kp // 2:rows_p * Kp // 2 + T * KC4 * 512].reshape(T, KC4, 16, 2, 4, 4)
+    scales = s.transpose(0, 2, 1, 4, 5, 3).reshape(rows_p, KC4 * 32)[:, :Kp // 16]
+    return np.ascontiguousarray(codes), np.ascontiguousarray(scales)

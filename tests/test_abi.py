@@ -221,3 +221,102 @@ def test_small_m_plans_pack_the_activation():
         assert tr.startswith("transform_quant_kernel + gemv_ring_kernel<") and ",PA=1>" in tr, tr
         assert "apack" in fql.linear_plan(M, N, K, aligned=False)  # dynamic scale, no transform
         assert fql.linear_workspace_bytes(M, N, K) >= 64 * 1024 + 16 * ((M + 15) // 16) * K * 2
+
+
+# ---------------------------------------------------------------------------
+# host-side scalars of the layer: the library's formulas against the oracle's
+# and against closed forms (no GPU needed)
+# ---------------------------------------------------------------------------
+
+def _amax_values():
+    import numpy as np
+
+    r = np.random.default_rng(31)
+    vals = np.concatenate([r.uniform(1e-3, 1e3, 2000), np.exp(r.uniform(-80, 80, 2000)),
+                           [1.0, 3.0, 6.0, 448.0, 2688.0, 1e-45, 1e-38, 3.4e38, 7.0 / 3.0]])
+    return vals.astype(np.float32)
+
+
+def test_global_scale_matches_oracle_and_closed_forms():
+    import numpy as np
+    from oracle import nvfp4 as Q
+
+    for a in _amax_values():
+        assert np.float32(fql.global_scale_from_amax(a)) == Q.global_scale_from_amax(a), a
+    assert fql.global_scale_from_amax(0.0) == 1.0
+    assert fql.global_scale_from_amax(2688.0) == 1.0
+    assert fql.global_scale_from_amax(1.0) == 2688.0
+    assert fql.global_scale_from_amax(6.0) == 448.0
+    assert fql.global_scale_from_amax(1e-40) == 2.0 ** 118      # the cap
+
+
+def test_alpha_matches_oracle_and_closed_forms():
+    import numpy as np
+    from oracle import transform as TR
+
+    r = np.random.default_rng(32)
+    for gx, gw in np.exp(r.uniform(-20, 20, (2000, 2))).astype(np.float32):
+        assert np.float32(fql.nvfp4_alpha(gx, gw)) == TR.dynamic_alpha(gx, gw)
+    assert fql.nvfp4_alpha(1.0, 1.0) == 1.0
+    assert fql.nvfp4_alpha(2.0, 0.25) == 2.0
+    assert fql.nvfp4_alpha(2688.0, 1.0) == float(np.float32(1.0 / 2688.0))
+
+
+def test_fp8_scales_match_oracle_and_closed_forms():
+    import numpy as np
+    from oracle import fp8 as P
+
+    for a in _amax_values():
+        s = P.scale_from_amax(a)
+        assert np.float32(fql.fp8_scale_from_amax(a)) == (s if s > 0 else np.float32(1.0)), a
+    assert fql.fp8_scale_from_amax(448.0) == 1.0
+    assert fql.fp8_scale_from_amax(0.0) == 1.0
+    assert fql.fp8_scale_from_amax(896.0) == 2.0
+    r = np.random.default_rng(33)
+    for sx, sw in np.exp(r.uniform(-30, 30, (2000, 2))).astype(np.float32):
+        assert np.float32(fql.fp8_output_scale(sx, sw)) == P.output_scale(sx, sw)
+    assert fql.fp8_output_scale(0.5, 0.25) == 0.125
+
+
+@pytest.mark.parametrize("name,args", [("fql_nvfp4_global_scale", (-1.0,)),
+                                       ("fql_nvfp4_global_scale", (float("inf"),)),
+                                       ("fql_nvfp4_global_scale", (float("nan"),)),
+                                       ("fql_nvfp4_alpha", (0.0, 1.0)),
+                                       ("fql_nvfp4_alpha", (1.0, float("inf"))),
+                                       ("fql_fp8_scale", (-2.0,)),
+                                       ("fql_fp8_output_scale", (1.0, -1.0))])
+def test_host_scalars_reject_invalid_inputs(name, args):
+    out = ctypes.c_float()
+    assert getattr(fql.lib(), name)(*[ctypes.c_float(a) for a in args], ctypes.byref(out)) == -1
+    assert fql.lib().fql_last_error().decode()
+
+
+def test_plan_override_set_and_cleared():
+    default = fql.linear_plan(100, 4096, 4096)
+    fql.set_plan_override("kind=1")
+    try:
+        assert "gemm_tiled_kernel<MT=4,NT=2,WM=2>" in fql.linear_plan(100, 4096, 4096)
+    finally:
+        fql.set_plan_override(None)
+    assert fql.linear_plan(100, 4096, 4096) == default
+    with fql.plan_override("8,1,3,0", which="sc_gemv"):
+        pass  # not a built GEMV: the default stays
+    assert fql.lib().fql_set_plan_override(7, None) == -1
+
+
+def test_binding_holds_no_numeric_formula():
+    # every scale and alpha of the layer comes from the library; the binding
+    # only marshals arguments: no numpy, no float literal but the unit alpha,
+    # no float division or power
+    import ast
+
+    src = open(os.path.join(ROOT, "fp8_quantized_linear_amd", "__init__.py")).read()
+    tree = ast.parse(src)
+    for node in ast.walk(tree):
+        if isinstance(node, (ast.Import, ast.ImportFrom)):
+            mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module]
+            assert not any(m and m.startswith("numpy") for m in mods)
+        if isinstance(node, ast.Constant) and isinstance(node.value, float):
+            assert node.value == 1.0, node.value
+        if isinstance(node, ast.BinOp):
+            assert not isinstance(node.op, (ast.Div, ast.Pow)), ast.unparse(node)

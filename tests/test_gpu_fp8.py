@@ -20,7 +20,7 @@ from oracle import fp8 as P
 from oracle import mx as X
 
 from gpu_helpers import (DEV, REL_FROB_TOL, announce, bf16_bits_to_dev, cached_activations,
-                         cached_weight, dev_bf16_to_bits, f32_to_dev, rel_frob)
+                         cached_weight, dev_bf16_to_bits, f32_to_dev, full_rows_sample, rel_frob)
 
 pytestmark = pytest.mark.gpu
 
@@ -120,6 +120,7 @@ def test_fp8_weight_quantizers_f32():
 # ---------------------------------------------------------------------------
 
 def _weight(fmt, W, input_scale=None):
+    """The GPU weight; per-tensor FP8 takes the oracle's calibration scales."""
     wd = f32_to_dev(W)
     if fmt == "mxfp4":
         return fql.MXFP4Weight.from_float(wd)
@@ -131,7 +132,14 @@ def _weight(fmt, W, input_scale=None):
     return fql.FP8Weight.from_float(wd, input_scale, weight_scale=float(sw))
 
 
-def _oracle(fmt, x32, W, wobj, alpha, bias64, cols=None):
+def _fp8_scales(x32, W):
+    """Oracle-side per-tensor FP8 scales (s_x, s_w) and output scale alpha."""
+    s_in = P.scale_from_amax(np.abs(x32).max())
+    s_w = P.scale_from_amax(np.abs(W).max())
+    return s_in, s_w, P.output_scale(s_in, s_w)
+
+
+def _oracle(fmt, x32, W, wobj, alpha, bias64, cols=None, s_in=None, s_w=None):
     """Oracle output [rows of x32, cols] (all columns when cols is None).
 
     Every weight scale covers whole rows of W except block FP8's 128 x 128
@@ -152,12 +160,15 @@ def _oracle(fmt, x32, W, wobj, alpha, bias64, cols=None):
         y = P.linear_fp8_block_f64(*P.quant_fp8_block_act(x32), wc, ws, None)[:, local]
         y = float(np.float32(alpha)) * y
         return F.bf16_round_bits(y if b is None else y + b[None, :])
-    xc = P.quant_fp8_tensor(x32, np.float32(wobj.input_scale))
-    wc = P.quant_fp8_tensor(W[cols], np.float32(wobj.weight_scale))
+    xc = P.quant_fp8_tensor(x32, s_in)
+    wc = P.quant_fp8_tensor(W[cols], s_w)
     return P.linear_fp8_tensor(xc, wc, np.float32(alpha), b)
 
 
 def _run(fmt, config, M, K, N, with_bias, rows=None, cols=None, alpha=None, label=""):
+    """One sibling linear call against the oracle on rows `rows` and columns `cols`
+    (all when None). Per-tensor FP8 without an explicit alpha runs on the
+    weight's device output scale and the oracle applies its own fl32(s_x s_w)."""
     xb = cached_activations("normal", M, K, config)
     x32 = synthetic.bf16_bits_to_f32(xb)
     W = cached_weight(config, N, K)
@@ -165,17 +176,21 @@ def _run(fmt, config, M, K, N, with_bias, rows=None, cols=None, alpha=None, labe
     c_sel = np.arange(N) if cols is None else np.asarray(cols)
     bias_bits = synthetic.bias(N, config=config) if with_bias else None
     announce(f"{fmt} linear {label} {config} M={M} K={K} N={N} bias={with_bias}")
-    s_in = float(P.scale_from_amax(np.abs(x32).max()))
-    wobj = _weight(fmt, W, s_in)
+    s_in, s_w, alpha_fp8 = _fp8_scales(x32, W)
+    wobj = _weight(fmt, W, float(s_in))
     bd = bf16_bits_to_dev(bias_bits) if with_bias else None
-    a = alpha if alpha is not None else (wobj.alpha if fmt == "fp8" else 1.0)
     fn = {"mxfp4": fql.linear_mxfp4, "mxfp8": fql.linear_mxfp8, "fp8": fql.linear_fp8,
           "fp8_block": fql.linear_fp8_block}[fmt]
-    y = fn(bf16_bits_to_dev(xb), wobj, alpha=a, bias=bd)
+    if alpha is None and fmt == "fp8":
+        y = fn(bf16_bits_to_dev(xb), wobj, bias=bd)  # device output scale of the weight
+        a = alpha_fp8
+    else:
+        a = 1.0 if alpha is None else alpha
+        y = fn(bf16_bits_to_dev(xb), wobj, alpha=a, bias=bd)
     torch.cuda.synchronize()
     yb = dev_bf16_to_bits(y)
     b64 = F.bf16_bits_to_f64(bias_bits) if with_bias else None
-    ref = _oracle(fmt, x32[r_sel], W, wobj, a, b64, c_sel)
+    ref = _oracle(fmt, x32[r_sel], W, wobj, a, b64, c_sel, s_in=s_in, s_w=s_w)
     err = rel_frob(yb[np.ix_(r_sel, c_sel)], ref)
     assert err <= REL_FROB_TOL, f"rel Frobenius {err:.3e}"
     return err
@@ -189,13 +204,9 @@ def test_linear_tiny(fmt):
 @pytest.mark.parametrize("M", [1, 64, 4096])
 @pytest.mark.parametrize("fmt", ["mxfp8", "fp8", "fp8_block"])
 def test_linear_siblings(fmt, M):
-    rows = None
-    if M == 4096:
-        rows = np.sort(np.random.default_rng(17).choice(M, 40, replace=False))
-        rows[-1] = M - 1
-    cols = np.sort(np.random.default_rng(M + 1).choice(14336, 128, replace=False))
-    cols[-1] = 14335
-    _run(fmt, "siblings", M, 4096, 14336, False, rows=rows, cols=cols, label="siblings")
+    # every output column; at M = 4096 a seeded sample of 256 whole rows
+    _run(fmt, "siblings", M, 4096, 14336, False, rows=full_rows_sample(M, seed=17),
+         label="siblings")
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 96, 100), (3, 160, 520), (17, 416, 33), (33, 2080, 200),
@@ -240,8 +251,10 @@ def test_fp8_strided_3d_and_deterministic():
         fn = {"mxfp8": fql.linear_mxfp8, "fp8": fql.linear_fp8, "fp8_block": fql.linear_fp8_block}[fmt]
         ybig = torch.zeros((M, N + 8), dtype=torch.bfloat16, device=DEV)
         fn(_dev_x(xb, 40), wobj, out=ybig[:, :N])
-        a = wobj.alpha if fmt == "fp8" else 1.0
-        ref = _oracle(fmt, x32, W, wobj, a, None)
+        s_x, s_w, a = _fp8_scales(x32, W)
+        if fmt != "fp8":
+            a = 1.0
+        ref = _oracle(fmt, x32, W, wobj, a, None, s_in=s_x, s_w=s_w)
         assert rel_frob(dev_bf16_to_bits(ybig[:, :N]), ref) <= REL_FROB_TOL, fmt
         assert torch.all(ybig[:, N:] == 0)
         y3 = fn(bf16_bits_to_dev(xb).view(2, 12, K), wobj)
@@ -251,55 +264,58 @@ def test_fp8_strided_3d_and_deterministic():
 
 
 # Every scaled-MFMA GEMM configuration built into the library (wave grid
-# WM x WN, MTW x NTW 16x16 tiles per wave, ring depth ST), with and without
-# split K, on a ragged shape: several row groups, 9 chunks of 128, a partial
-# column group.
-SC_CONFIGS = [(1, 4, 1, 4, 4), (1, 4, 2, 4, 4), (1, 4, 4, 2, 4), (2, 2, 4, 4, 3), (2, 4, 4, 4, 3),
-              (2, 4, 8, 4, 4), (4, 2, 4, 4, 3), (1, 4, 1, 2, 4)]
-FP8_SKIP = {(2, 4, 8, 4, 4)}  # its 8-bit ring does not fit in LDS
+# WM x WN, MTW x NTW 16x16 tiles per wave, ring depth ST: the planner's
+# choices), with and without split K, on a ragged shape: several row groups,
+# 9 chunks of 128, a partial column group.
+SC_CONFIGS = [(1, 4, 4, 2, 4), (2, 2, 4, 4, 3), (4, 2, 4, 4, 3), (1, 4, 1, 2, 4)]
+SC_CONFIGS_FP4 = SC_CONFIGS + [(2, 4, 8, 4, 4)]  # its 8-bit ring would not fit in LDS
 
 
-@pytest.mark.parametrize("splits", [1, 3])
-@pytest.mark.parametrize("cfg", SC_CONFIGS)
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8", "fp8", "fp8_block"])
-def test_every_sc_config(fmt, cfg, splits, monkeypatch):
-    if fmt != "mxfp4" and cfg in FP8_SKIP:
-        pytest.skip("configuration not built for 8-bit formats")
+def _sc_cases():
+    for fmt in ("mxfp4", "mxfp8", "fp8", "fp8_block"):
+        for cfg in (SC_CONFIGS_FP4 if fmt == "mxfp4" else SC_CONFIGS):
+            for splits in (1, 3):
+                yield pytest.param(fmt, cfg, splits, id=f"{fmt}-{cfg}-s{splits}")
+
+
+@pytest.mark.parametrize("fmt,cfg,splits", list(_sc_cases()))
+def test_every_sc_config(fmt, cfg, splits, plan_override):
     M, K = 150, 1152
     N = 384 if fmt == "fp8_block" else 400
     wm, wn, mtw, ntw, st = cfg
-    monkeypatch.setenv("FQL_SC_PLAN", f"{wm},{wn},{mtw},{ntw},{st},{splits}")
+    plan_override(f"{wm},{wn},{mtw},{ntw},{st},{splits}", "sc_gemm")
     plan = fql.linear_sc_plan(fmt, M, N, K)
     want = f"gemm_sc_kernel<{fmt},WM={wm},WN={wn},MTW={mtw},NTW={ntw},ST={st}>"
     assert want in plan and f"splits={splits}" in plan, plan
     _run(fmt, "tiny", M, K, N, True, alpha=None if fmt == "fp8" else 1.5, label=f"{cfg} splits={splits}")
 
 
-# Every small-M GEMV configuration (W waves splitting K, NT column tiles per
-# workgroup, D chunks in flight per wave) at M = 1, 16 (one row tile) and
-# 17, 32 (two), on a ragged shape: 9 chunks of 128, a partial column tile.
-SCV_CONFIGS = [(4, 2, 4), (4, 2, 6), (8, 2, 3), (4, 4, 3), (8, 1, 4), (4, 2, 3), (8, 1, 3)]
+# Every small-M GEMV configuration built (W waves splitting K, NT column tiles
+# per workgroup, D chunks in flight per wave) at M = 1, 16 (one row tile) and
+# 17, 32 (two), on a ragged shape: 9 chunks of 128, a partial column tile; the
+# one-row-tile configuration also with the in-workgroup quantizer (fq = 1).
+SCV_ONE_TILE = {"mxfp4": (4, 4, 3), "mxfp8": (4, 2, 3), "fp8": (4, 2, 3), "fp8_block": (4, 2, 3)}
+SCV_TWO_TILES = (4, 2, 3)
 
 
-SCV_FUSED_CONFIGS = [(4, 4, 3), (4, 2, 3)]  # also built with the in-workgroup quantizer
+def _scv_cases():
+    for fmt, one in SCV_ONE_TILE.items():
+        for M in (1, 16):
+            for fq in (0, 1):
+                yield pytest.param(fmt, one, M, fq, id=f"{fmt}-{one}-M{M}-fq{fq}")
+        for M in (17, 32):
+            yield pytest.param(fmt, SCV_TWO_TILES, M, 0, id=f"{fmt}-{SCV_TWO_TILES}-M{M}")
 
 
-@pytest.mark.parametrize("fq", [0, 1])
-@pytest.mark.parametrize("M", [1, 16, 17, 32])
-@pytest.mark.parametrize("cfg", SCV_CONFIGS)
-@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8", "fp8", "fp8_block"])
-def test_every_gemv_config(fmt, cfg, M, fq, monkeypatch):
-    if fq and (M > 16 or cfg not in SCV_FUSED_CONFIGS):
-        pytest.skip("the fused GEMV is built for the decode defaults at M <= 16")
+@pytest.mark.parametrize("fmt,cfg,M,fq", list(_scv_cases()))
+def test_every_gemv_config(fmt, cfg, M, fq, plan_override):
     K = 1152
     N = 384 if fmt == "fp8_block" else 400
     w, nt, d = cfg
-    monkeypatch.setenv("FQL_SC_GEMV", f"{w},{nt},{d},{fq}")
+    plan_override(f"{w},{nt},{d},{fq}", "sc_gemv")
     plan = fql.linear_sc_plan(fmt, M, N, K)
     want = f"gemv_sc_kernel<{fmt},W={w},MT={(M + 15) // 16},NT={nt},D={d}" + (",FQ=1>" if fq else ">")
-    if want not in plan:
-        assert not fq, plan  # every fused configuration fits at this K
-        pytest.skip(f"GEMV {cfg} not built for {fmt} at M={M}: {plan}")
+    assert want in plan, plan
     _run(fmt, "tiny", M, K, N, True, alpha=None if fmt == "fp8" else 1.5, label=f"gemv {cfg} fq={fq}")
 
 
@@ -312,7 +328,7 @@ def _sc_weight(fmt, N, K):
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8", "fp8", "fp8_block"])
 @pytest.mark.parametrize("M,K", [(1, 4096), (7, 1024), (16, 384), (3, 4096), (5, 1152)])
-def test_fused_gemv_equals_two_launch_path(fmt, M, K, monkeypatch):
+def test_fused_gemv_equals_two_launch_path(fmt, M, K, plan_override):
     # the in-workgroup quantizer produces the same operand bytes as the
     # standalone quantizer, so the fused call is bit-identical to quantizer + GEMV
     N = 2048 if fmt == "fp8_block" else 2000
@@ -324,7 +340,7 @@ def test_fused_gemv_equals_two_launch_path(fmt, M, K, monkeypatch):
     nt = 4 if fmt == "mxfp4" else 2
     outs = []
     for fq in (1, 0):
-        monkeypatch.setenv("FQL_SC_GEMV", f"4,{nt},3,{fq}")
+        plan_override(f"4,{nt},3,{fq}", "sc_gemv")
         plan = fql.linear_sc_plan(fmt, M, N, K)
         assert (",FQ=1>" in plan) == bool(fq), plan
         announce(f"fused gemv {fmt} M={M} K={K} fq={fq}")

@@ -3,8 +3,10 @@
 The HIP path quantizes the activation, runs the block-scaled GEMM and the
 fused epilogue; the oracle quantizes independently and evaluates the float64
 product of the decoded operands, rounded to bf16. Outputs must agree within a
-relative Frobenius error of 1e-3 (bf16 vs bf16). Large configurations compare
-a seeded sample of rows and columns, each computed in full by the oracle.
+relative Frobenius error of 1e-3 (bf16 vs bf16). The activation global scale
+is calibrated on the whole activation; large configurations compare a seeded
+sample of at least 256 whole rows (every output column, the first and the
+last row included) with the oracle.
 """
 
 import numpy as np
@@ -18,7 +20,8 @@ from oracle import nvfp4 as Q
 from oracle.hadamard import fwht_fp32
 
 from gpu_helpers import (DEV, REL_FROB_TOL, alpha_of, announce, bf16_bits_to_dev,
-                         cached_activations, dev_bf16_to_bits, f32_to_dev, rel_frob, weight_case)
+                         cached_activations, dev_bf16_to_bits, f32_to_dev, full_rows_sample,
+                         rel_frob, weight_case, weight_hat)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,38 +33,39 @@ def _gpu_weight(W, gw, hb, gx):
     return fql.NVFP4Weight(packed, W.shape[0], W.shape[1], float(gx), float(gw), hb), codes, scales
 
 
-def _run_case(config, M, K, N, hb, with_bias, rows=None, cols=None, xkind=None, label=""):
+def _run_case(config, M, K, N, hb, with_bias, rows=None, xkind=None, label=""):
+    """One linear call against the oracle: the GPU weight codes and scales bit for
+    bit, then y on the rows `rows` (all rows when None), every column. The call
+    runs twice, with alpha passed by value and with the weight's device alpha
+    (from the library's alpha formula), which must agree bit for bit."""
     xkind = xkind or synthetic.WORKLOADS[config]["x"]
     xb = cached_activations(xkind, M, K, config)
     x32 = synthetic.bf16_bits_to_f32(xb)
     r_sel = np.arange(M) if rows is None else np.asarray(rows)
-    c_sel = None if cols is None else tuple(int(c) for c in cols)
-    gx = Q.global_scale_from_amax(Q.amax_for_calibration(x32[r_sel], hb))
-    W, gw, wc_ref, ws_ref = weight_case(config, N, K, hb, c_sel)
+    gx = Q.global_scale_from_amax(Q.amax_for_calibration(x32, hb))
+    W, gw, wc_ref, ws_ref = weight_case(config, N, K, hb)
     bias_bits = synthetic.bias(N, config=config) if with_bias else None
     alpha = alpha_of(gx, gw)
 
     announce(f"linear {label} {config} M={M} K={K} N={N} hb={hb} bias={with_bias}")
     wobj, wcodes, wscales = _gpu_weight(W, gw, hb, gx)
-    if c_sel is None:
-        assert np.array_equal(wcodes.cpu().numpy(), wc_ref)
-        assert np.array_equal(wscales.cpu().numpy(), ws_ref)
-    else:
-        assert np.array_equal(wcodes.cpu().numpy()[list(c_sel)], wc_ref)
-        assert np.array_equal(wscales.cpu().numpy()[list(c_sel)], ws_ref)
+    assert np.array_equal(wcodes.cpu().numpy(), wc_ref)
+    assert np.array_equal(wscales.cpu().numpy(), ws_ref)
+    del wcodes, wscales
     xd = bf16_bits_to_dev(xb)
     bd = bf16_bits_to_dev(bias_bits) if with_bias else None
     y = fql.linear_nvfp4(xd, wobj, alpha=float(alpha), bias=bd)
+    y_dev_alpha = fql.linear_nvfp4(xd, wobj, bias=bd)  # alpha from the weight's device scalar
     torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_dev_alpha.view(torch.int16))
     yb = dev_bf16_to_bits(y)
 
     xc, xs = Q.quant_nvfp4(x32[r_sel], gx, hb)
-    bias64 = None
-    if with_bias:
-        bias64 = F.bf16_bits_to_f64(bias_bits if c_sel is None else bias_bits[list(c_sel)])
-    ref = Q.linear_nvfp4(xc, xs, wc_ref, ws_ref, alpha, bias64)
-    got = yb[r_sel] if c_sel is None else yb[np.ix_(r_sel, list(c_sel))]
-    err = rel_frob(got, ref)
+    bias64 = F.bf16_bits_to_f64(bias_bits) if with_bias else None
+    # G1 of the weight decoded once per weight and kept for the other cases
+    ref = F.bf16_round_bits(Q.linear_dequantized_f64(Q.dequant_nvfp4(xc, xs),
+                                                     weight_hat(config, N, K, hb), alpha, bias64))
+    err = rel_frob(yb[r_sel], ref)
     assert err <= REL_FROB_TOL, f"rel Frobenius {err:.3e}"
     return err
 
@@ -79,27 +83,18 @@ def test_linear_decode(M, shape):
 
 @pytest.mark.parametrize("M", [2048, 8192])
 @pytest.mark.parametrize("shape", ["qkv", "gate_up", "down"])
-def test_linear_prefill_sampled(M, shape):
+def test_linear_prefill_full_rows(M, shape):
     K, N = synthetic.LLAMA_SHAPES[shape]
-    r = np.random.default_rng(M + K + N)
-    rows = np.sort(r.choice(M, 48, replace=False))
-    rows[-1] = M - 1
-    cols = np.sort(r.choice(N, 96, replace=False))
-    cols[-1] = N - 1
-    _run_case("prefill", M, K, N, 0, False, rows=rows, cols=cols, label=shape)
+    _run_case("prefill", M, K, N, 0, False, rows=full_rows_sample(M, seed=M + K + N), label=shape)
 
 
 @pytest.mark.parametrize("hb", [16, 32, 64, 128])
 @pytest.mark.parametrize("shape", ["gate_up", "down"])
 @pytest.mark.parametrize("M", [1, 256, 4096])
-def test_linear_hadamard_sampled(hb, shape, M):
+def test_linear_hadamard_full_rows(hb, shape, M):
     K, N = synthetic.QWEN_SHAPES[shape]
-    r = np.random.default_rng(hb + M + K)
-    rows = None if M <= 256 else np.sort(r.choice(M, 24, replace=False))
-    if M == 256:
-        rows = np.sort(r.choice(M, 64, replace=False))
-    cols = np.sort(r.choice(N, 64, replace=False))
-    _run_case("hadamard", M, K, N, hb, False, rows=rows, cols=cols, label=f"qwen-{shape}")
+    _run_case("hadamard", M, K, N, hb, False, rows=full_rows_sample(M, seed=hb + M + K),
+              label=f"qwen-{shape}")
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 272, 100), (3, 144, 520), (17, 400, 33), (33, 2064, 200),
@@ -179,34 +174,17 @@ def test_linear_identity_weight_closed_form():
 # Every tiled GEMM configuration built into the library (workgroup tile of
 # (WM*MT*16) rows x ((4/WM)*NT*16) columns), with and without split K, on a
 # ragged shape: several row groups, an odd chunk count, a partial column tile.
-TILED_CONFIGS = [(1, 1, 1), (2, 1, 1), (4, 1, 1), (8, 1, 1), (8, 2, 1), (4, 4, 1), (8, 4, 1),
-                 (2, 2, 2), (4, 2, 2), (2, 4, 2), (4, 4, 2), (1, 4, 4), (2, 4, 4), (2, 2, 4)]
+TILED_CONFIGS = [(1, 1, 1), (2, 1, 1), (2, 2, 2), (4, 2, 2), (8, 4, 1)]
 
 
 @pytest.mark.parametrize("splits", [1, 3])
 @pytest.mark.parametrize("mt,nt,wm", TILED_CONFIGS)
-def test_linear_every_tiled_config(mt, nt, wm, splits, monkeypatch):
+def test_linear_every_tiled_config(mt, nt, wm, splits, plan_override):
     M, K, N = 150, 1152, 400
-    monkeypatch.setenv("FQL_PLAN", f"kind=1,mt={mt},nt={nt},wm={wm},splits={splits}")
+    plan_override(f"kind=1,mt={mt},nt={nt},wm={wm},splits={splits}")
     plan = fql.linear_plan(M, N, K)
     assert f"MT={mt},NT={nt},WM={wm}>" in plan and f"splits={splits}" in plan, plan
     _run_case("tiny", M, K, N, 0, True, label=f"tiled<{mt},{nt},{wm}> splits={splits}")
-
-
-# Every LDS-ring GEMM configuration built into the library (workgroup tile of
-# (MT*16) rows x (4*NT*16) columns, ring depth ST), same ragged shape.
-LDS_CONFIGS = [(1, 4, 4), (2, 4, 4), (4, 4, 3), (4, 4, 4), (8, 4, 3), (4, 2, 4), (8, 2, 3),
-               (2, 2, 4), (4, 2, 3), (2, 4, 3), (2, 2, 3)]
-
-
-@pytest.mark.parametrize("splits", [1, 3])
-@pytest.mark.parametrize("mt,nt,st", LDS_CONFIGS)
-def test_linear_every_lds_config(mt, nt, st, splits, monkeypatch):
-    M, K, N = 150, 1152, 400
-    monkeypatch.setenv("FQL_PLAN", f"kind=2,mt={mt},nt={nt},st={st},splits={splits}")
-    plan = fql.linear_plan(M, N, K)
-    assert f"gemm_lds_kernel<MT={mt},NT={nt},ST={st}>" in plan and f"splits={splits}" in plan, plan
-    _run_case("tiny", M, K, N, 0, True, label=f"lds<{mt},{nt},{st}> splits={splits}")
 
 
 # Every 32x32-MFMA LDS-ring configuration (workgroup tile (MT*32) rows x
@@ -216,81 +194,76 @@ LDS32_CONFIGS = [(4, 2, 3), (4, 1, 3), (2, 2, 4), (2, 2, 3), (2, 1, 4), (2, 1, 3
 
 @pytest.mark.parametrize("splits", [1, 3])
 @pytest.mark.parametrize("mt,nt,st", LDS32_CONFIGS)
-def test_linear_every_lds32_config(mt, nt, st, splits, monkeypatch):
+def test_linear_every_lds32_config(mt, nt, st, splits, plan_override):
     M, K, N = 150, 1152, 400
-    monkeypatch.setenv("FQL_PLAN", f"kind=3,mt={mt},nt={nt},st={st},splits={splits}")
+    plan_override(f"kind=3,mt={mt},nt={nt},st={st},splits={splits}")
     plan = fql.linear_plan(M, N, K)
     assert f"gemm_lds32_kernel<MT={mt},NT={nt},ST={st}>" in plan and f"splits={splits}" in plan, plan
     _run_case("tiny", M, K, N, 0, True, label=f"lds32<{mt},{nt},{st}> splits={splits}")
 
 
-# Every per-wave-ring small-M configuration (W waves splitting K, MT row
-# tiles, NT column tiles per workgroup, D chunks in flight per wave), same
-# ragged shape at M = 1, 16 (one row tile), 17 and 32 (two).
-GEMV_RING_CONFIGS = [(4, 2, 3), (4, 2, 4), (4, 4, 3), (8, 1, 3), (8, 2, 3), (4, 1, 4)]
+# Every per-wave-ring small-M configuration built into the library (W waves
+# splitting K, MT row tiles, NT column tiles per workgroup, D chunks in flight
+# per wave: the planner's choices), on a ragged shape, in every activation form
+# built for it: fq = 1 quantizes inside the kernel, pa = 1 reads the packed
+# activation, pa = 0 x_hat. M = 1 and 16 fill one row tile, 17 and 32 two.
+GEMV_RING_BUILT = [(4, 1, 2, 3), (4, 1, 4, 3), (8, 1, 1, 3), (4, 2, 2, 3)]
+GEMV_RING_PA_BUILT = [(8, 2, 1, 3)]  # built for the packed activation only
+RING_FORMS = [(0, 0), (1, 0), (0, 1)]
 
 
-@pytest.mark.parametrize("fq,pa", [(0, 0), (1, 0), (0, 1)])
-@pytest.mark.parametrize("M", [1, 16, 17, 32])
-@pytest.mark.parametrize("w,nt,d", GEMV_RING_CONFIGS)
-def test_linear_every_gemv_ring_config(w, nt, d, M, fq, pa, monkeypatch):
-    # fq = 1: the activation is quantized inside the kernel (x rows through the ring);
-    # pa = 1: the quantizer pass writes it packed like a weight
+def _ring_cases():
+    for w, mt, nt, d in GEMV_RING_BUILT:
+        for fq, pa in RING_FORMS:
+            for M in ((1, 16) if mt == 1 else (17, 32)):
+                yield pytest.param(w, nt, d, M, fq, pa, id=f"W{w}-NT{nt}-D{d}-M{M}-fq{fq}-pa{pa}")
+    for w, mt, nt, d in GEMV_RING_PA_BUILT:
+        for M in ((1, 16) if mt == 1 else (17, 32)):
+            yield pytest.param(w, nt, d, M, 0, 1, id=f"W{w}-NT{nt}-D{d}-M{M}-pa1")
+
+
+@pytest.mark.parametrize("w,nt,d,M,fq,pa", list(_ring_cases()))
+def test_linear_every_gemv_ring_config(w, nt, d, M, fq, pa, plan_override):
     K, N = 1152, 400
-    monkeypatch.setenv("FQL_PLAN", f"kind=4,waves={w},nt={nt},st={d},fq={fq},pa={pa}")
+    plan_override(f"kind=4,waves={w},nt={nt},st={d},fq={fq},pa={pa}")
     plan = fql.linear_plan(M, N, K)
     want = f"gemv_ring_kernel<W={w},MT={(M + 15) // 16},NT={nt},D={d},FQ={fq},PA={pa}>"
-    if want not in plan:
-        pytest.skip(f"{want} not built: {plan}")
+    assert want in plan, plan
     _run_case("tiny", M, K, N, 0, True, label=f"gemv_ring<{w},{nt},{d},fq={fq},pa={pa}>")
 
 
-GEMV_RING_PA_CONFIGS = [(8, 1, 4), (16, 1, 3), (8, 1, 3), (8, 2, 3), (4, 4, 3)]
-
-
-@pytest.mark.parametrize("M", [1, 16, 17, 32])
-@pytest.mark.parametrize("w,nt,d", GEMV_RING_PA_CONFIGS)
-def test_linear_every_packed_activation_ring_config(w, nt, d, M, monkeypatch):
-    # configurations built only for the packed activation (smaller ring stages)
-    K, N = 1920, 400
-    monkeypatch.setenv("FQL_PLAN", f"kind=4,waves={w},nt={nt},st={d},pa=1")
-    plan = fql.linear_plan(M, N, K)
-    want = f"gemv_ring_kernel<W={w},MT={(M + 15) // 16},NT={nt},D={d},FQ=0,PA=1>"
-    if want not in plan:
-        pytest.skip(f"{want} not built: {plan}")
-    _run_case("tiny", M, K, N, 0, True, label=f"gemv_ring<{w},{nt},{d},pa=1>")
-
-
-@pytest.mark.parametrize("fq,pa", [(0, 0), (1, 0), (0, 1)])
-@pytest.mark.parametrize("M", [3, 17, 32])
-@pytest.mark.parametrize("w,nt,d", [(8, 1, 3), (4, 2, 3), (16, 1, 3)])
-def test_linear_ring_interleaved_chunks(w, nt, d, M, fq, pa, monkeypatch):
+@pytest.mark.parametrize("w,nt,d,M,fq,pa", [(4, 2, 3, 3, 0, 1), (4, 2, 3, 3, 1, 0), (4, 2, 3, 17, 0, 0),
+                                            (4, 2, 3, 32, 0, 1), (8, 1, 3, 5, 0, 1), (8, 1, 3, 24, 0, 1),
+                                            (4, 4, 3, 9, 0, 0)])
+def test_linear_ring_interleaved_chunks(w, nt, d, M, fq, pa, plan_override):
     # waves taking chunks wave, wave + W, ... (K = 1664: 13 chunks, so some waves
-    # get one chunk fewer and with W = 16 some get none)
+    # get one chunk fewer)
     K, N = 1664, 272
-    monkeypatch.setenv("FQL_PLAN", f"kind=4,waves={w},nt={nt},st={d},fq={fq},pa={pa},il=1")
+    plan_override(f"kind=4,waves={w},nt={nt},st={d},fq={fq},pa={pa},il=1")
     plan = fql.linear_plan(M, N, K)
     want = f"gemv_ring_kernel<W={w},MT={(M + 15) // 16},NT={nt},D={d},FQ={fq},PA={pa}>"
-    if want not in plan:
-        pytest.skip(f"{want} not built: {plan}")
-    assert plan.endswith("chunks=interleaved"), plan
+    assert want in plan and plan.endswith("chunks=interleaved"), plan
     _run_case("tiny", M, K, N, 0, True, label=f"gemv_ring<{w},{nt},{d},fq={fq},pa={pa}> interleaved")
 
 
-@pytest.mark.parametrize("cfg", ["waves=8,nt=1,st=3", "waves=4,nt=4,st=3", "waves=16,nt=1,st=3"])
-@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (8, 17, 16), (32, 33, 48), (17, 1, 112), (3, 200, 144)])
-def test_linear_ring_edge_shapes(M, N, K, cfg, monkeypatch):
+@pytest.mark.parametrize("cfg,M,N,K", [("waves=8,nt=1,st=3", 1, 1, 16), ("waves=8,nt=1,st=3", 8, 17, 16),
+                                        ("waves=8,nt=1,st=3", 32, 33, 48),
+                                        ("waves=8,nt=1,st=3", 17, 1, 112),
+                                        ("waves=4,nt=4,st=3", 3, 200, 144),
+                                        ("waves=4,nt=4,st=3", 16, 1, 16),
+                                        ("waves=4,nt=2,st=3", 32, 33, 48),
+                                        ("waves=4,nt=2,st=3", 1, 17, 112)])
+def test_linear_ring_edge_shapes(cfg, M, N, K, plan_override):
     # one chunk or less of K (most waves have no chunk), one or a few columns
-    monkeypatch.setenv("FQL_PLAN", f"kind=4,{cfg},pa=1")
+    plan_override(f"kind=4,{cfg},pa=1")
     plan = fql.linear_plan(M, N, K)
-    if "gemv_ring_kernel" not in plan:
-        pytest.skip(f"not built: {plan}")
+    assert "gemv_ring_kernel" in plan, plan
     _run_case("tiny", M, K, N, 0, True, label=f"ring edge {plan}")
 
 
 @pytest.mark.parametrize("M,K,hb", [(1, 1040, 0), (5, 4096, 0), (16, 1040, 16), (17, 2064, 0),
                                     (32, 4096, 128), (8, 14336, 0), (24, 3072, 64)])
-def test_linear_packed_activation_equals_xhat(M, K, hb, monkeypatch):
+def test_linear_packed_activation_equals_xhat(M, K, hb, plan_override):
     # the packed activation holds the same codes and scales as x_hat's dequantized
     # values, so the small-M ring gives bit-identical outputs either way (K with a
     # ragged tail past the last 128-chunk; rotations go through the same quantizer)
@@ -305,7 +278,7 @@ def test_linear_packed_activation_equals_xhat(M, K, hb, monkeypatch):
     xd = bf16_bits_to_dev(xb)
     outs = {}
     for pa in (0, 1):
-        monkeypatch.setenv("FQL_PLAN", f"kind=4,waves=4,nt=2,st=3,pa={pa}")
+        plan_override(f"kind=4,waves=4,nt=2,st=3,pa={pa}")
         assert f"PA={pa}>" in fql.linear_plan(M, N, K), fql.linear_plan(M, N, K)
         outs[pa] = dev_bf16_to_bits(fql.linear_nvfp4(xd, wobj, alpha=float(alpha)))
     assert np.array_equal(outs[0], outs[1])
@@ -314,10 +287,10 @@ def test_linear_packed_activation_equals_xhat(M, K, hb, monkeypatch):
 
 
 @pytest.mark.parametrize("M", [3, 24])
-def test_linear_fused_ring_strided_rows(M, monkeypatch):
+def test_linear_fused_ring_strided_rows(M, plan_override):
     # fused quantization reads x rows with the caller's stride (rows >= M clamped)
     K, N = 2048, 272
-    monkeypatch.setenv("FQL_PLAN", "kind=4,waves=4,nt=2,st=3,fq=1")
+    plan_override("kind=4,waves=4,nt=2,st=3,fq=1")
     xb = synthetic.activations("normal", M, K, config="decode", seed=9)
     x32 = synthetic.bf16_bits_to_f32(xb)
     gx = Q.global_scale_from_amax(Q.amax_for_calibration(x32))

@@ -17,7 +17,7 @@ from oracle import formats as F
 from oracle import mx as X
 
 from gpu_helpers import (DEV, REL_FROB_TOL, announce, bf16_bits_to_dev, cached_activations,
-                         cached_weight, dev_bf16_to_bits, f32_to_dev, rel_frob)
+                         cached_weight, dev_bf16_to_bits, f32_to_dev, full_rows_sample, rel_frob)
 
 pytestmark = pytest.mark.gpu
 
@@ -132,14 +132,9 @@ def test_mx_linear_tiny():
 
 @pytest.mark.parametrize("M", [1, 4, 64, 4096])
 def test_mx_linear_siblings(M):
-    rows = None
-    if M == 4096:
-        r = np.random.default_rng(17)
-        rows = np.sort(r.choice(M, 48, replace=False))
-        rows[-1] = M - 1
-    cols = np.sort(np.random.default_rng(M).choice(14336, 128, replace=False))
-    cols[-1] = 14335
-    _run_linear("siblings", M, 4096, 14336, False, rows=rows, cols=cols, label="siblings")
+    # every output column; at M = 4096 a seeded sample of 256 whole rows
+    _run_linear("siblings", M, 4096, 14336, False, rows=full_rows_sample(M, seed=17),
+                label="siblings")
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 96, 100), (3, 160, 520), (17, 416, 33), (33, 2080, 200),

@@ -329,7 +329,7 @@ def test_linear_dynamic(M, mode):
 
 @pytest.mark.parametrize("b,K", [(16, 1040), (32, 1056), (64, 1088), (128, 1152), (128, 5120)])
 @pytest.mark.parametrize("M", [1, 5, 17, 32])
-def test_linear_transform_packed_equals_xhat(b, K, M, monkeypatch):
+def test_linear_transform_packed_equals_xhat(b, K, M, plan_override):
     # the transform kernel's packed activation and its x_hat hold the same
     # quantized values, so the small-M ring gives identical bits with either
     # (K not a multiple of 128: the packed blocks past K are zero)
@@ -341,7 +341,7 @@ def test_linear_transform_packed_equals_xhat(b, K, M, monkeypatch):
     announce(f"transform packed vs x_hat b={b} K={K} M={M}")
     outs = []
     for pa in (0, 1):
-        monkeypatch.setenv("FQL_PLAN", f"kind=4,waves=4,nt=2,st=3,pa={pa}")
+        plan_override(f"kind=4,waves=4,nt=2,st=3,pa={pa}")
         assert f"PA={pa}>" in fql.linear_plan(M, N, K, aligned=False, transform=True)
         outs.append(dev_bf16_to_bits(fql.linear_nvfp4(bf16_bits_to_dev(xb), w)))
     assert np.array_equal(outs[0], outs[1])
@@ -355,11 +355,11 @@ def test_linear_transform_packed_equals_xhat(b, K, M, monkeypatch):
 
 @pytest.mark.parametrize("pa", [0, 1])
 @pytest.mark.parametrize("mode", ["none", "hadamard32", "transform64"])
-def test_linear_dynamic_small_m_ring(mode, pa, monkeypatch):
+def test_linear_dynamic_small_m_ring(mode, pa, plan_override):
     # the small-M ring with either activation form: the dynamic scale reaches the
     # quantizer pass through the device scalar; under a transform the transform
     # kernel writes the x_hat or the packed activation
-    monkeypatch.setenv("FQL_PLAN", f"kind=4,waves=4,nt=2,st=3,pa={pa}")
+    plan_override(f"kind=4,waves=4,nt=2,st=3,pa={pa}")
     M, K, N = 24, 2048, 640
     xb = _x(M, K, seed=77)
     x32 = synthetic.bf16_bits_to_f32(xb)
