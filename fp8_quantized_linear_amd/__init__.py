@@ -78,6 +78,7 @@ __all__ = [
     "plan_override",
     "linear_nvfp4_quantize",
     "linear_nvfp4_gemm",
+    "linear_nvfp4_noalloc",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -167,6 +168,8 @@ SIGNATURES = {
     "fql_fp8_scale": (_c_int, [_c_f32, ctypes.POINTER(_c_f32)]),
     "fql_fp8_output_scale": (_c_int, [_c_f32, _c_f32, ctypes.POINTER(_c_f32)]),
     "fql_set_plan_override": (_c_int, [_c_int, ctypes.c_char_p]),
+    "fql_linear_nvfp4_noalloc": (_c_int, [_c_vp, _c_i64, _c_i64, _c_i64, _c_f32, _c_int, _c_vp,
+                                          _c_i64, _c_f32, _c_vp, _c_vp, _c_i64, _c_vp]),
 }
 
 PLAN_OVERRIDES = {"nvfp4": 0, "sc_gemm": 1, "sc_gemv": 2}  # FQL_PLAN_NVFP4, _SC_GEMM, _SC_GEMV
@@ -532,6 +535,32 @@ def linear_nvfp4(x, weight, alpha=None, bias=None, out=None, workspace=None):
                                       weight.hadamard_block, _ptr(weight.packed), N, float(alpha),
                                       _ptr(bias), _ptr(y2), ldy, _ptr(workspace), workspace.numel(),
                                       _stream(x.device)))
+    return out
+
+
+def linear_nvfp4_noalloc(x, weight, out, alpha=None, bias=None):
+    """linear_nvfp4 for callers that cannot allocate: no workspace, the library's
+    static per-device scratch instead (FQL_NOALLOC_SCRATCH_BYTES; larger calls
+    raise). `out` (bf16 [..., N]) must be given; calls that overlap in time on
+    one device race on the shared scratch."""
+    _require_cuda(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise FQLError("linear_nvfp4_noalloc takes bfloat16 activations")
+    if x.shape[-1] != weight.K:
+        raise FQLError(f"x has K={x.shape[-1]}, weight has K={weight.K}")
+    if getattr(weight, "transform", None) is not None or getattr(weight, "dynamic_input_scale", False):
+        raise FQLError("linear_nvfp4_noalloc takes plain (optionally Hadamard-rotated) weights")
+    x2, ld = _rows_view(x, "x")
+    M, K = x2.shape
+    if bias is not None:
+        _require_cuda(bias, "bias")
+        if bias.dtype != torch.bfloat16 or bias.numel() != weight.N or not bias.is_contiguous():
+            raise FQLError("bias must be a contiguous bf16 tensor of N elements")
+    y2, ldy = _rows_view(out, "out")
+    a = weight.alpha if alpha is None else alpha
+    _check(lib().fql_linear_nvfp4_noalloc(_ptr(x2), M, K, ld, weight.input_global_scale,
+                                          weight.hadamard_block, _ptr(weight.packed), weight.N,
+                                          float(a), _ptr(bias), _ptr(y2), ldy, _stream(x.device)))
     return out
 
 

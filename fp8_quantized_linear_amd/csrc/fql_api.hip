@@ -909,3 +909,79 @@ int fql_linear_fp8_block(const void* x, int64_t M, int64_t K, int64_t ldx, const
 }
 
 }  // extern "C"
+// ---- linear call without allocation: a static scratch buffer per device ------
+//
+// For callers that cannot allocate (code under HIP graph capture, tight
+// serving loops): fql_linear_nvfp4_noalloc runs the same plan and kernels as
+// fql_linear_nvfp4 with the workspace in a file-scope device array. In host
+// code `scratch` names a host-side stand-in, never the device memory; its
+// device address comes from hipGetSymbolAddress, once per device (each GPU
+// holds its own copy), and only that address reaches kernels.
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = FQL_NOALLOC_SCRATCH_BYTES;
+static_assert(fql::kWorkspaceCounterBytes % 4 == 0, "counter words");
+
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this device's scratch, set up on the first call on
+// the device: the address is looked up and the arrival counters at its start
+// are cleared in stream order (every linear call leaves them zero again).
+int scratch_for_current_device(hipStream_t st, uint8_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FQL_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    const int words = (int)(fql::kWorkspaceCounterBytes / 4);
+    clear_words_kernel<<<(words + 255) / 256, 256, 0, st>>>(static_cast<uint32_t*>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, "scratch clear launch");
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return FQL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fql_linear_nvfp4_noalloc(const void* x, int64_t M, int64_t K, int64_t ldx,
+                             float input_global_scale, int hadamard_block, const void* w_packed,
+                             int64_t N, float alpha, const void* bias, void* y, int64_t ldy,
+                             void* stream) {
+  if (int r = check_linear_nvfp4(x, M, K, ldx, input_global_scale, hadamard_block, w_packed, N, y, ldy))
+    return r;
+  if (!std::isfinite(alpha)) return fail(FQL_ERR_INVALID, "alpha must be finite");
+  const bool xal = aligned16(x, ldx, 2);
+  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, xal);
+  if ((size_t)plan.total_bytes > kNoAllocScratchBytes)
+    return fail(FQL_ERR_WORKSPACE,
+                "this call needs %lld bytes of scratch, more than the %zu bytes the "
+                "allocation-free entry point holds per device; use fql_linear_nvfp4 with a workspace",
+                (long long)plan.total_bytes, kNoAllocScratchBytes);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = nullptr;
+  if (int r = scratch_for_current_device(st, &ws)) return r;
+  hipError_t e = fql::launch_linear_nvfp4(
+      plan, static_cast<const uint16_t*>(x), M, K, ldx, input_global_scale, hadamard_block, xal,
+      static_cast<const uint8_t*>(w_packed), N, alpha, static_cast<const uint16_t*>(bias),
+      static_cast<uint16_t*>(y), ldy, ws, st);
+  return hip_status(e, "linear launch");
+}
+
+}  // extern "C"

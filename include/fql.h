@@ -223,6 +223,26 @@ int fql_linear_nvfp4_gemm(int64_t M, int64_t K, int x_aligned, const void* w_pac
                           float alpha, const void* bias, void* y, int64_t ldy, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/*
+ * The NVFP4 linear layer for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): fql_linear_nvfp4 without a workspace argument. The scratch the
+ * call needs (arrival counters, the quantized activation operand, split-K
+ * partial sums) lives in a file-scope device array of
+ * FQL_NOALLOC_SCRATCH_BYTES bytes on each device, held until the process
+ * ends; a call whose launch plan needs more returns FQL_ERR_WORKSPACE and
+ * launches nothing. The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine). Every call on a device shares that device's
+ * array: calls that overlap in time on one device (other streams, other
+ * threads) race; calls in order on one stream do not. Same arguments,
+ * launch plan, numerics and errors as fql_linear_nvfp4 otherwise.
+ */
+#define FQL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fql_linear_nvfp4_noalloc(const void* x, int64_t M, int64_t K, int64_t ldx,
+                             float input_global_scale, int hadamard_block, const void* w_packed,
+                             int64_t N, float alpha, const void* bias, void* y, int64_t ldy,
+                             void* stream);
+
 /* ---------------------------------------------------------------------------
  * Host-side scalars of the layer (no device work, callable without a GPU).
  * ------------------------------------------------------------------------- */
