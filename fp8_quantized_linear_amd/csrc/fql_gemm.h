@@ -150,17 +150,18 @@ __device__ __forceinline__ void finish_tile(float4v (&acc)[MT][NT], int M, int N
                         slab, counter, s_flag);
 }
 
-// 32x32 accumulator tiles (v_mfma_f32_32x32x16_f16 layout): wave w holds MT x
-// NT tiles; register r of tile (a, b) is row m0 + a*32 + 8*(r/4) + 4*(lane/32)
-// + r%4, column n0 + (w*NT + b)*32 + lane%32.
-template <int MT, int NT>
+// 32x32 accumulator tiles (v_mfma_f32_32x32x16_f16 layout): the wave of
+// column slice wn holds MT x NT tiles; register r of tile (a, b) is row m0 +
+// a*32 + 8*(r/4) + 4*(lane/32) + r%4, column n0 + (wn*NT + b)*32 + lane%32.
+// The workgroup has 4 * WM waves (m0 is the wave's own first row).
+template <int MT, int NT, int WM = 1>
 __device__ __forceinline__ void finish_tile32(float16v (&acc)[MT][NT], int M, int N, int m0, int n0,
-                                              int split, int splits, float alpha,
+                                              int wn, int split, int splits, float alpha,
                                               const uint16_t* __restrict__ bias,
                                               uint16_t* __restrict__ y, int64_t ldy,
                                               float4v* __restrict__ slab, uint32_t* counter,
                                               uint32_t* s_flag) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   float4v frag[MT * NT * 4];
 #pragma unroll
   for (int a = 0; a < MT; ++a)
@@ -171,9 +172,9 @@ __device__ __forceinline__ void finish_tile32(float16v (&acc)[MT][NT], int M, in
         frag[(a * NT + b) * 4 + r4] = float4v{acc[a][b][4 * r4], acc[a][b][4 * r4 + 1],
                                               acc[a][b][4 * r4 + 2], acc[a][b][4 * r4 + 3]};
   auto row_of = [&](int f, int i) { return (f / (NT * 4)) * 32 + 8 * (f % 4) + 4 * (lane >> 5) + i; };
-  auto col_of = [&](int f) { return (wave * NT + (f / 4) % NT) * 32 + (lane & 31); };
-  finish_frags<MT * NT * 4>(frag, row_of, col_of, M, N, m0, n0, split, splits, alpha, bias, y, ldy,
-                            slab, counter, s_flag);
+  auto col_of = [&](int f) { return (wn * NT + (f / 4) % NT) * 32 + (lane & 31); };
+  finish_frags<MT * NT * 4, decltype(row_of), decltype(col_of), 4 * WM>(
+      frag, row_of, col_of, M, N, m0, n0, split, splits, alpha, bias, y, ldy, slab, counter, s_flag);
 }
 
 // Direct global -> LDS loads. The loads are issued with inline assembly and

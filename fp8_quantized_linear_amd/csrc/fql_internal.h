@@ -86,7 +86,8 @@ struct GemmPlan {
   int kind;
   int mt;             // kind 1: 16-row M tiles per wave
   int nt;             // kind 1: 16-column N tiles per wave
-  int wm;             // kind 1: wave rows (the 4 waves form a wm x 4/wm grid)
+  int wm;             // kind 1: wave rows (the 4 waves form a wm x 4/wm grid);
+                      // kind 3: row halves (4 * wm waves, wm of them per SIMD)
   int st;             // kinds 3, 4: LDS ring depth (chunks)
   int64_t Mp;         // M padded to a whole number of M tiles
   int64_t Np, Kp;     // packed weight dims
@@ -115,7 +116,7 @@ GemmPlan cached_plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned);
 // Whether gemm_tiled_kernel<mt, nt, wm> / gemm_lds32_kernel<mt, nt, st> is
 // built into the library.
 bool tiled_config_built(int mt, int nt, int wm);
-bool lds32_config_built(int mt, int nt, int st);
+bool lds32_config_built(int mt, int nt, int st, int wm);
 bool gemv_ring_config_built(int w, int mt, int nt, int d, bool packed_a);
 
 // Kernel name and parameters of a plan (diagnostics).

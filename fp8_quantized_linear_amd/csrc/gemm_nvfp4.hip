@@ -687,15 +687,20 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 //   s/2 of the slot's scale dword (l%16)*2 + s%2 for the chunk.
 // Per chunk and 32-column tile a lane therefore loads two code slots (even
 // and odd steps) and two scale dwords.
-template <int MT, int NT>
+template <int MT, int NT, int WM>
 struct LdsStage32 {
-  uint4v a[MT * 2 * 4][64];     // [16-row tile][32-deep step][lane] x_hat fragments
-  uint4v bq[4 * NT * 2][64];    // [wave][32-col tile][even/odd steps][lane] codes
-  uint32_t bs[4 * NT * 2][64];  // [wave][32-col tile][even/odd steps][lane] scales
+  uint4v a[WM * MT * 2 * 4][64];  // [16-row tile][32-deep step][lane] x_hat fragments
+  uint4v bq[4 * NT * 2][64];      // [column wave][32-col tile][even/odd steps][lane] codes
+  uint32_t bs[4 * NT * 2][64];    // [column wave][32-col tile][even/odd steps][lane] scales
 };
 
-template <int MT, int NT, int ST, int OCC>
-__global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
+// WM = 2 doubles the waves (two per SIMD): the 4 column waves of each of two
+// row halves; a wave owns MT 32-row tiles of its half and NT 32-column tiles,
+// and the two waves of a column slice load one of its two code and scale
+// slots each and dequantize the slice both. A stalled wave (a barrier, a
+// wait) then leaves the matrix pipe to the other wave of its SIMD.
+template <int MT, int NT, int ST, int OCC, int WM = 1>
+__global__ __launch_bounds__(256 * WM, OCC) void gemm_lds32_kernel(
     const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
     const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, int ngroups,
     int kc_per_split, int splits, float alpha,
@@ -704,13 +709,17 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
     uint32_t* __restrict__ counters) {
   if (alpha_dev != nullptr) alpha = *alpha_dev;  // per-call scale computed on the device
   static_assert(ST >= 3 && ST <= 4, "ring depth (chunk i+1 must be issued a whole chunk ahead)");
-  constexpr int L = 2 * MT + 4 * NT;  // LDS loads per chunk per wave
+  static_assert(WM == 1 || WM == 2, "one or two row halves");
+  constexpr int NLB = 2 * NT / WM;    // code (and scale) slot loads per chunk per wave
+  constexpr int L = 2 * MT + 2 * NLB;  // LDS loads per chunk per wave
   static_assert(L * (ST - 2) <= 63, "vmcnt range");
-  __shared__ LdsStage32<MT, NT> stage[ST];
+  typedef LdsStage32<MT, NT, WM> Stage;
+  __shared__ Stage stage[ST];
   __shared__ uint32_t s_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;  // row half, column slice
   const int64_t KC = Kp / 128;
   const int64_t KC4 = (KC + 3) / 4;
   const int split = blockIdx.x % splits;
@@ -720,26 +729,28 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
   const int64_t c_begin = (int64_t)split * kc_per_split;
   const int64_t c_end = c_begin + kc_per_split < KC ? c_begin + kc_per_split : KC;
   const int nch = (int)(c_end - c_begin);
-  const int tile16_0 = (ngroup * 4 + wave) * NT * 2;  // first packed 16-column tile of the wave
+  const int tile16_0 = (ngroup * 4 + wn) * NT * 2;  // first packed 16-column tile of the wave
 
-  // wave-uniform global bases; per-lane byte offsets
+  // wave-uniform global bases; per-lane byte offsets. A wave loads the
+  // 32-deep step wn of each 16-row tile of its row half.
   const uint8_t* a_base = reinterpret_cast<const uint8_t*>(xhat) +
-                          ((int64_t)mgroup * MT * 2 * (Kp / 32) + wave) * 1024;
+                          (((int64_t)mgroup * WM + wm) * MT * 2 * (Kp / 32) + wn) * 1024;
   const uint32_t a_voff = lane * 16;
   const int jc = lane & 31, hh = lane >> 5;  // column in the 32-column tile, k half
-  // per-lane offsets of the lane's 16-column packed tile (a tile past the end
-  // is clamped to the last one: read, never stored); the host keeps the
-  // packed blob below 4 GiB so that these 32-bit offsets cannot wrap
-  uint32_t q_voff[NT][2], s_voff[NT][2];
+  // Per-lane offsets of the code and scale slots this wave loads: slot (b, e)
+  // of 32-column tile b holds the even (e = 0) or odd (e = 1) steps; with
+  // WM = 2 the wave of row half wm loads e = wm. A 16-column tile past the
+  // end is clamped to the last one (read, never stored); the host keeps the
+  // packed blob below 4 GiB so that these 32-bit offsets cannot wrap.
+  uint32_t q_voff[NLB], s_voff[NLB];
 #pragma unroll
-  for (int b = 0; b < NT; ++b) {
+  for (int i = 0; i < NLB; ++i) {
+    const int b = WM == 1 ? i / 2 : i;
+    const int e = WM == 1 ? i % 2 : wm;
     int64_t tl = tile16_0 + 2 * b + (jc >> 4);
     tl = tl < ntiles ? tl : ntiles - 1;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      q_voff[b][e] = (uint32_t)(tl * KC * 1024 + ((2 * e + hh) * 16 + (jc & 15)) * 16);
-      s_voff[b][e] = (uint32_t)(tl * KC4 * 512 + ((jc & 15) * 2 + e) * 16);
-    }
+    q_voff[i] = (uint32_t)(tl * KC * 1024 + ((2 * e + hh) * 16 + (jc & 15)) * 16);
+    s_voff[i] = (uint32_t)(tl * KC4 * 512 + ((jc & 15) * 2 + e) * 16);
   }
 
   // The scalar bases of chunk c's loads into stage sg, computed once per chunk
@@ -751,30 +762,32 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
     uint32_t la, lq, ls;  // this wave's LDS destinations in the stage
   };
   const int64_t a_tile_stride = (Kp / 32) * 1024;  // bytes between 16-row x_hat tiles
-  auto refill_of = [&](LdsStage32<MT, NT>& sg, int64_t c) -> Refill {
+  // the wave's slot i sits at slot index (wn*NT + b)*2 + e of the stage
+  constexpr int SLOT_STEP = WM == 1 ? 1 : 2;
+  auto refill_of = [&](Stage& sg, int64_t c) -> Refill {
     c = c < c_end ? c : c_end - 1;
     Refill r;
     r.a = uniform_ptr(a_base + c * 4096);
     r.q = uniform_ptr(wcodes + c * 1024);
     r.s = uniform_ptr(wscales + (c >> 2) * 512 + (c & 3) * 4);
-    r.la = __builtin_amdgcn_readfirstlane(lds_offset(&sg.a[wave][0]));
-    r.lq = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bq[wave * NT * 2][0]));
-    r.ls = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bs[wave * NT * 2][0]));
+    r.la = __builtin_amdgcn_readfirstlane(lds_offset(&sg.a[wm * MT * 2 * 4 + wn][0]));
+    r.lq = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bq[wn * NT * 2 + (WM == 1 ? 0 : wm)][0]));
+    r.ls = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bs[wn * NT * 2 + (WM == 1 ? 0 : wm)][0]));
     return r;
   };
   // LDS load number e (0 <= e < L) of a chunk
   auto issue_one = [&](const Refill& r, int e) {
     if (e < 2 * MT) {
       lds_load16(r.a + e * a_tile_stride, a_voff, r.la + e * 4 * 1024);
-    } else if (e < 2 * MT + 2 * NT) {
-      const int bh = e - 2 * MT;  // (b, h) = (bh / 2, bh % 2)
-      lds_load16(r.q, q_voff[bh / 2][bh % 2], r.lq + bh * 1024);
+    } else if (e < 2 * MT + NLB) {
+      const int i = e - 2 * MT;
+      lds_load16(r.q, q_voff[i], r.lq + i * SLOT_STEP * 1024);
     } else {
-      const int bh = e - 2 * MT - 2 * NT;
-      lds_load4(r.s, s_voff[bh / 2][bh % 2], r.ls + bh * 256);
+      const int i = e - 2 * MT - NLB;
+      lds_load4(r.s, s_voff[i], r.ls + i * SLOT_STEP * 256);
     }
   };
-  auto issue = [&](LdsStage32<MT, NT>& sg, int64_t c) {
+  auto issue = [&](Stage& sg, int64_t c) {
     const Refill r = refill_of(sg, c);
 #pragma unroll
     for (int e = 0; e < L; ++e) issue_one(r, e);
@@ -798,25 +811,25 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
   uint32_t bsw[NT][2];
   half8 bf[2][NT];
   uint4v af[2][MT];
-  auto a_frag = [&](const LdsStage32<MT, NT>& sg, int a, int s) -> uint4v {
-    return (&sg.a[0][0])[a_lane + ((2 * a) * 4 + (s >> 1)) * 64 + 2 * (s & 1) * 16];
+  auto a_frag = [&](const Stage& sg, int a, int s) -> uint4v {
+    return (&sg.a[0][0])[a_lane + ((2 * (wm * MT + a)) * 4 + (s >> 1)) * 64 + 2 * (s & 1) * 16];
   };
-  // the wave's own codes and scales (only its own loads must have landed)
-  auto read_head_b = [&](const LdsStage32<MT, NT>& sg) {
+  // the column slice's codes and scales (with WM = 1 the wave's own loads)
+  auto read_head_b = [&](const Stage& sg) {
 #pragma unroll
     for (int b = 0; b < NT; ++b)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        bq[b][e] = sg.bq[(wave * NT + b) * 2 + e][lane];
-        bsw[b][e] = sg.bs[(wave * NT + b) * 2 + e][lane];
+        bq[b][e] = sg.bq[(wn * NT + b) * 2 + e][lane];
+        bsw[b][e] = sg.bs[(wn * NT + b) * 2 + e][lane];
       }
   };
   // the first step's activation fragments (loaded by all waves)
-  auto read_head_a = [&](const LdsStage32<MT, NT>& sg) {
+  auto read_head_a = [&](const Stage& sg) {
 #pragma unroll
     for (int a = 0; a < MT; ++a) af[0][a] = a_frag(sg, a, 0);
   };
-  auto read_head = [&](const LdsStage32<MT, NT>& sg) {
+  auto read_head = [&](const Stage& sg) {
     read_head_b(sg);
     read_head_a(sg);
   };
@@ -836,7 +849,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
   };
   // refill (when given) receives chunk rc's loads, spread over the seven steps
   // so that the address unit works while the MFMAs run
-  auto steps0to6 = [&](const LdsStage32<MT, NT>& sg, LdsStage32<MT, NT>& refill, int64_t rc) {
+  auto steps0to6 = [&](const Stage& sg, Stage& refill, int64_t rc) {
     const Refill rf = refill_of(refill, rc);
 #pragma unroll
     for (int s = 0; s < 7; ++s) {
@@ -878,8 +891,9 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
         steps0to6(stage[j], stage[(j + ST - 1) % ST], c_begin + i0 + j + ST - 1);
         const bool more = i0 + j + 1 < nch;
         wait_vmcnt<L * (ST - 2)>();  // this wave's loads of chunk i+1 have landed
-        if (more) read_head_b(stage[(j + 1) % ST]);
+        if (WM == 1 && more) read_head_b(stage[(j + 1) % ST]);  // its own loads
         stage_barrier();             // everyone's have, and stage j has been read by all
+        if (WM == 2 && more) read_head_b(stage[(j + 1) % ST]);
         if (more) read_head_a(stage[(j + 1) % ST]);
         __builtin_amdgcn_sched_barrier(0);
         if (more) dequant(0, 0);
@@ -895,9 +909,9 @@ __global__ __launch_bounds__(256, OCC) void gemm_lds32_kernel(
   }
   wait_vmcnt<0>();  // no LDS load may still be in flight when the workgroup ends
 
-  float4v* slab = partial + (int64_t)tilegrp * splits * (4 * MT * NT * 4 * 64);
-  finish_tile32<MT, NT>(acc, M, N, mgroup * MT * 32, ngroup * 4 * NT * 32, split, splits, alpha,
-                        bias, y, ldy, slab, counters + tilegrp, &s_flag);
+  float4v* slab = partial + (int64_t)tilegrp * splits * (4 * WM * MT * NT * 4 * 64);
+  finish_tile32<MT, NT, WM>(acc, M, N, (mgroup * WM + wm) * MT * 32, ngroup * 4 * NT * 32, wn,
+                            split, splits, alpha, bias, y, ldy, slab, counters + tilegrp, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -1035,7 +1049,7 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     if (p.kind == 3 && d.total_bytes() >= ((int64_t)1 << 32)) p.kind = 1;
     const bool lds_ring = p.kind == 3;
     p.wm = 1;
-    p.st = 3;
+    p.st = 3;  // (the tables below may change wm for kind 3)
     if (!lds_ring) {
       if (M <= 16) { p.mt = 1; p.nt = 1; }
       else if (M <= 32) { p.mt = 2; p.nt = 1; }
@@ -1049,20 +1063,22 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
         p.mt = 4; p.nt = 1; p.st = 3;
         if ((M + 127) / 128 * ((ntiles + 7) / 8) < 192) { p.mt = 2; p.st = 4; }
       } else {
-        p.mt = 4; p.nt = 2; p.st = 3;
+        // 128 x 256 tiles on 8 waves, two per SIMD (measured 3-8% faster than
+        // one wave per SIMD with 128-row waves on the prefill shapes)
+        p.mt = 2; p.nt = 2; p.st = 3; p.wm = 2;
       }
     }
     if (ov.mt || ov.nt || ov.wm || ov.st) {
       if (ov.mt) p.mt = ov.mt;
       if (ov.nt) p.nt = ov.nt;
-      if (ov.wm && !lds_ring) p.wm = ov.wm;
+      if (ov.wm && (!lds_ring || ov.wm <= 2)) p.wm = ov.wm;
       if (ov.st) p.st = ov.st;
     }
-    const bool built = p.kind == 3 ? lds32_config_built(p.mt, p.nt, p.st)
+    const bool built = p.kind == 3 ? lds32_config_built(p.mt, p.nt, p.st, p.wm)
                                    : tiled_config_built(p.mt, p.nt, p.wm);
     if (!built) { p.kind = 1; p.mt = 1; p.nt = 1; p.wm = 1; }
     // rows and 16-column tiles per workgroup
-    const int tile_rows = p.kind == 3 ? 32 * p.mt : 16 * p.mt * p.wm;
+    const int tile_rows = p.kind == 3 ? 32 * p.mt * p.wm : 16 * p.mt * p.wm;
     const int tile_cols16 = p.kind == 3 ? 8 * p.nt : (4 / p.wm) * p.nt;
     p.Mp = round_up(M, tile_rows);
     const int64_t ngroups = (ntiles + tile_cols16 - 1) / tile_cols16;
@@ -1083,9 +1099,9 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     p.ngroups = ngroups;
     p.xhat_bytes = round_up(p.Mp * p.Kp * 2, 256);
   }
-  // [splits][4 waves][fragments][64 lanes] float4 per output tile
+  // [splits][waves][fragments][64 lanes] float4 per output tile
   const int64_t frags = (int64_t)p.mt * p.nt * (p.kind == 3 ? 4 : 1);
-  const int64_t slab = (int64_t)p.splits * 4 * frags * 64 * 16;
+  const int64_t slab = (int64_t)p.splits * (p.kind == 3 ? 4 * p.wm : 4) * frags * 64 * 16;
   p.partial_bytes = p.splits > 1 ? round_up(p.groups * slab, 256) : 0;
   p.counter_bytes = kCounterBytes;
   p.total_bytes = p.counter_bytes + p.xhat_bytes + p.partial_bytes;
@@ -1098,6 +1114,10 @@ std::string describe_plan(const GemmPlan& p) {
     std::snprintf(b, sizeof(b), "%sgemv_ring_kernel<W=%d,MT=%d,NT=%d,D=%d,FQ=%d,PA=%d> grid=%lld splits=1%s",
                   p.fq ? "" : p.pa ? "quant_nvfp4_apack_kernel + " : "quant_nvfp4_xhat_kernel + ", p.waves,
                   p.mt, p.nt, p.st, p.fq, p.pa, (long long)p.groups, p.ilv ? " chunks=interleaved" : "");
+  } else if (p.kind == 3 && p.wm > 1) {
+    std::snprintf(b, sizeof(b),
+                  "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d,WM=%d> grid=%lld splits=%d",
+                  p.mt, p.nt, p.st, p.wm, (long long)(p.groups * p.splits), p.splits);
   } else if (p.kind == 3) {
     std::snprintf(b, sizeof(b),
                   "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d> grid=%lld splits=%d",
@@ -1191,7 +1211,7 @@ static hipError_t launch_tiled_t(const GemmPlan& p, const _Float16* xhat, const 
 // for weights of 4 GiB or more, whose offsets exceed the 32-bit ring kernel's)
 #define FQL_TILED_CONFIGS(X) X(1, 1, 1) X(2, 1, 1) X(2, 2, 2) X(4, 2, 2) X(8, 4, 1)
 
-template <int MT, int NT, int ST, int OCC>
+template <int MT, int NT, int ST, int OCC, int WM>
 static hipError_t launch_lds32_t(const GemmPlan& p, const _Float16* xhat, const uint8_t* packed,
                                  int64_t M, int64_t N, float alpha, const float* alpha_dev,
                                  const uint16_t* bias,
@@ -1199,19 +1219,19 @@ static hipError_t launch_lds32_t(const GemmPlan& p, const _Float16* xhat, const 
                                  hipStream_t st) {
   const uint8_t* wcodes = packed;
   const uint8_t* wscales = packed + p.Np * p.Kp / 2;
-  gemm_lds32_kernel<MT, NT, ST, OCC><<<(unsigned)(p.groups * p.splits), 256, 0, st>>>(
+  gemm_lds32_kernel<MT, NT, ST, OCC, WM><<<(unsigned)(p.groups * p.splits), 256 * WM, 0, st>>>(
       xhat, wcodes, wscales, (int)M, (int)N, p.Kp, (int)(p.Np / 16), (int)p.ngroups,
       p.kc_per_split, p.splits, alpha, alpha_dev, bias, y, ldy, partial, counters);
   return hipGetLastError();
 }
 
-// The (MT, NT, ST, OCC) 32x32 LDS-ring configurations built into the library.
+// The (MT, NT, ST, OCC, WM) 32x32 LDS-ring configurations built into the library.
 #define FQL_LDS32_CONFIGS(X) \
-  X(4, 2, 3, 1) X(4, 1, 3, 1) X(2, 2, 4, 1) X(2, 2, 3, 2) X(2, 1, 4, 2) X(2, 1, 3, 2) X(1, 2, 4, 2) \
-  X(1, 2, 3, 2)
+  X(4, 2, 3, 1, 1) X(4, 1, 3, 1, 1) X(2, 2, 4, 1, 1) X(2, 2, 3, 2, 1) X(2, 1, 4, 2, 1) \
+  X(2, 1, 3, 2, 1) X(1, 2, 4, 2, 1) X(1, 2, 3, 2, 1) X(2, 2, 3, 1, 2)
 
-bool lds32_config_built(int mt, int nt, int st) {
-#define FQL_X(A, B, C, D) if (mt == A && nt == B && st == C) return true;
+bool lds32_config_built(int mt, int nt, int st, int wm) {
+#define FQL_X(A, B, C, D, E) if (mt == A && nt == B && st == C && wm == E) return true;
   FQL_LDS32_CONFIGS(FQL_X)
 #undef FQL_X
   return false;
@@ -1328,9 +1348,9 @@ static hipError_t launch_gemm_part(const GemmPlan& p, const uint16_t* x, int64_t
     return hipErrorInvalidValue;
   }
   if (p.kind == 3) {
-#define FQL_X(A, B, C, D)                                                                        \
-  if (p.mt == A && p.nt == B && p.st == C)                                                       \
-    return launch_lds32_t<A, B, C, D>(p, xhat, packed, M, N, alpha, alpha_dev, bias, y, ldy, partial4, counters, st);
+#define FQL_X(A, B, C, D, E)                                                                     \
+  if (p.mt == A && p.nt == B && p.st == C && p.wm == E)                                          \
+    return launch_lds32_t<A, B, C, D, E>(p, xhat, packed, M, N, alpha, alpha_dev, bias, y, ldy, partial4, counters, st);
     FQL_LDS32_CONFIGS(FQL_X)
 #undef FQL_X
     return hipErrorInvalidValue;

@@ -189,17 +189,20 @@ def test_linear_every_tiled_config(mt, nt, wm, splits, plan_override):
 
 # Every 32x32-MFMA LDS-ring configuration (workgroup tile (MT*32) rows x
 # (4*NT*32) columns), same ragged shape (N = 400 leaves half a 32-column tile).
-LDS32_CONFIGS = [(4, 2, 3), (4, 1, 3), (2, 2, 4), (2, 2, 3), (2, 1, 4), (2, 1, 3), (1, 2, 4), (1, 2, 3)]
+# (WM = 2: two row halves of 4 waves each, two waves per SIMD.)
+LDS32_CONFIGS = [(4, 2, 3, 1), (4, 1, 3, 1), (2, 2, 4, 1), (2, 2, 3, 1), (2, 1, 4, 1), (2, 1, 3, 1),
+                 (1, 2, 4, 1), (1, 2, 3, 1), (2, 2, 3, 2)]
 
 
 @pytest.mark.parametrize("splits", [1, 3])
-@pytest.mark.parametrize("mt,nt,st", LDS32_CONFIGS)
-def test_linear_every_lds32_config(mt, nt, st, splits, plan_override):
+@pytest.mark.parametrize("mt,nt,st,wm", LDS32_CONFIGS)
+def test_linear_every_lds32_config(mt, nt, st, wm, splits, plan_override):
     M, K, N = 150, 1152, 400
-    plan_override(f"kind=3,mt={mt},nt={nt},st={st},splits={splits}")
+    plan_override(f"kind=3,mt={mt},nt={nt},st={st},wm={wm},splits={splits}")
     plan = fql.linear_plan(M, N, K)
-    assert f"gemm_lds32_kernel<MT={mt},NT={nt},ST={st}>" in plan and f"splits={splits}" in plan, plan
-    _run_case("tiny", M, K, N, 0, True, label=f"lds32<{mt},{nt},{st}> splits={splits}")
+    want = f"gemm_lds32_kernel<MT={mt},NT={nt},ST={st}" + (f",WM={wm}>" if wm > 1 else ">")
+    assert want in plan and f"splits={splits}" in plan, plan
+    _run_case("tiny", M, K, N, 0, True, label=f"lds32<{mt},{nt},{st},{wm}> splits={splits}")
 
 
 # Every per-wave-ring small-M configuration built into the library (W waves
