@@ -84,18 +84,17 @@ WORKLOAD_NAMES = {
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_SUMMARIES = [os.path.join(ROOT, "profiles", f) for f in
-                     ("prefill_llama8b_hbm_traffic.md", "decode_llama8b_hbm_traffic.md")]
+TRAFFIC_SUMMARIES = [os.path.join(ROOT, "profiles", "serving_hbm_traffic.md")]
 
 
 def source_digest():
-    """sha256 over the library's kernel sources (names and bytes, sorted)."""
+    """sha256 over the sources of the NVFP4 GEMM translation unit (gemm_nvfp4.hip and
+    the headers it includes: names and bytes, in this order)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "fp8_quantized_linear_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in ("gemm_nvfp4.hip", "fql_device.h", "fql_gemm.h", "fql_internal.h", "fql_quant.h"):
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()
 
 
@@ -362,8 +361,9 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic
 
 def calibration(stream_sizes_mb=(14.2, 33.1, 66.1, 147.5, 512.0), mfma_reps=3):
     """Streaming-read GB/s per buffer size (cold: rotated over >= 512 MB, graph of
-    back-to-back reads, HIP events) and MFMA-loop TFLOP/s (f16 32x32x16 and the
-    scaled FP8 / FP4 16x16x128, one and two waves per SIMD)."""
+    back-to-back reads, HIP events), MFMA-loop TFLOP/s (f16 32x32x16 and the
+    scaled FP8 / FP4 16x16x128, one and two waves per SIMD) and the vendor
+    library's float16 GEMM on the large layer shapes."""
     import torch
 
     lib = ctypes.CDLL(os.path.join(ROOT, "fp8_quantized_linear_amd", "libfql_calib.so"))
@@ -404,7 +404,7 @@ def calibration(stream_sizes_mb=(14.2, 33.1, 66.1, 147.5, 512.0), mfma_reps=3):
         out["stream_read_gbs"][f"{mb:g}MB"] = round(nb / (ms * 1e-3) / 1e9, 1)
         del g
     del pool
-    iters = 16000  # about a millisecond per launch, like the large GEMMs
+    iters = 8000  # about a millisecond per launch, like the large GEMMs
     for kind, name, flop in ((0, "f16_32x32x16", 32768), (1, "fp8_16x16x128", 65536),
                              (2, "fp4_16x16x128", 65536)):
         for wps in (1, 2):
@@ -418,8 +418,27 @@ def calibration(stream_sizes_mb=(14.2, 33.1, 66.1, 147.5, 512.0), mfma_reps=3):
                 b.record(stream)
                 b.synchronize()
             ms = a.elapsed_time(b) / mfma_reps
-            total = grid * 4 * iters * 4 * flop
+            total = grid * 4 * iters * 8 * flop
             out["mfma_tflops"][f"{name}_waves_per_simd={wps}"] = round(total / (ms * 1e-3) / 1e12, 1)
+    # the vendor library's dense float16 GEMM (torch.matmul -> hipBLASLt) on the
+    # layer shapes of the largest calls, as a practical reference for an f16-MFMA GEMM
+    out["library_f16_gemm_tflops"] = {}
+    for (M, N, K) in ((8192, 28672, 4096), (8192, 4096, 14336), (4096, 51200, 5120),
+                      (4096, 5120, 25600), (2048, 6144, 4096)):
+        a = torch.randn(M, K, device=dev, dtype=torch.float16)
+        b = torch.randn(N, K, device=dev, dtype=torch.float16)
+        with torch.cuda.stream(stream):
+            for _ in range(2):
+                c = a @ b.T
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                c = a @ b.T
+            e1.record(stream)
+            e1.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        out["library_f16_gemm_tflops"][f"M={M},N={N},K={K}"] = round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)
+        del a, b, c
     return out
 
 

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4v* __restri
 
 // KIND 0: v_mfma_f32_32x32x16_f16 (32768 flops); 1: the scaled
 // 16x16x128 MFMA on FP8 (E4M3) operands; 2: the same on FP4 (E2M1) operands
-// (16x16x128: 65536 flops). Four independent accumulators per wave, `iters`
+// (16x16x128: 65536 flops). Eight independent accumulators per wave, `iters`
 // rounds; the operands depend on the lane so nothing folds away.
 template <int KIND>
 __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __restrict__ sink) {
@@ -57,18 +57,16 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __rest
       a[i] = (_Float16)(0.001f * (float)(lane + i));
       b[i] = (_Float16)(0.002f * (float)(lane - i));
     }
-    // distinct starting values keep the four chains from being merged
-    float16v c0 = {}, c1 = {}, c2 = {}, c3 = {};
-    c1[0] = 1.0f;
-    c2[0] = 2.0f;
-    c3[0] = 3.0f;
-    for (int it = 0; it < iters; ++it) {
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c1, 0, 0, 0);
-      c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c2, 0, 0, 0);
-      c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c3, 0, 0, 0);
+    // distinct starting values keep the chains from being merged
+    float16v c[8];
+    for (int j = 0; j < 8; ++j) {
+      c[j] = float16v{};
+      c[j][0] = (float)j;
     }
-    acc_sum = c0[0] + c1[1] + c2[2] + c3[3];
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c[j], 0, 0, 0);
+    for (int j = 0; j < 8; ++j) acc_sum += c[j][j];
   } else {
     constexpr int F = KIND == 1 ? 0 : 4;  // operand format: 0 = E4M3, 4 = E2M1
     int8v a, b;
@@ -76,15 +74,13 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __rest
       a[i] = 0x01010101 * ((lane + i) & 7);
       b[i] = 0x02020202 * ((lane + 3 * i) & 3);
     }
-    float4v c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {1.f, 0.f, 0.f, 0.f}, c2 = {2.f, 0.f, 0.f, 0.f},
-            c3 = {3.f, 0.f, 0.f, 0.f};
-    for (int it = 0; it < iters; ++it) {
-      c0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c0, F, F, 0, 127, 0, 127);
-      c1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c1, F, F, 0, 127, 0, 127);
-      c2 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c2, F, F, 0, 127, 0, 127);
-      c3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c3, F, F, 0, 127, 0, 127);
-    }
-    acc_sum = c0[0] + c1[1] + c2[2] + c3[3];
+    float4v c[8];
+    for (int j = 0; j < 8; ++j) c[j] = float4v{(float)j, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        c[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c[j], F, F, 0, 127, 0, 127);
+    for (int j = 0; j < 8; ++j) acc_sum += c[j][j & 3];
   }
   if (acc_sum == 12345.678f) sink[blockIdx.x] = acc_sum;  // keeps the loop; never true in practice
 }
@@ -104,9 +100,9 @@ int fql_calib_stream_read(const void* buf, int64_t bytes, int grid, uint32_t* si
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-// `grid` workgroups of 4 waves, each wave `iters` rounds of 4 MFMAs of kind
+// `grid` workgroups of 4 waves, each wave `iters` rounds of 8 MFMAs of kind
 // `kind` (0: float16 32x32x16, 1: scaled FP8 16x16x128, 2: scaled FP4
-// 16x16x128). Flops = grid * 4 * iters * 4 * (32768 for kind 0, 65536 else).
+// 16x16x128). Flops = grid * 4 * iters * 8 * (32768 for kind 0, 65536 else).
 int fql_calib_mfma_loop(int kind, int grid, int iters, float* sink, void* stream) {
   if (!sink || grid < 1 || iters < 1) return -1;
   hipStream_t st = static_cast<hipStream_t>(stream);

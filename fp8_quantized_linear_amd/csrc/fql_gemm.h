@@ -199,6 +199,25 @@ __device__ __forceinline__ void lds_load4(const void* sbase, uint32_t voff, uint
 }
 // A wave-uniform address the compiler cannot prove uniform (e.g. formed inside
 // a lane-dependent branch), moved to scalar registers for the loads above.
+// Output tile of workgroup `bid` (of `n`, one K split) in an XCD-grouped order.
+// The workgroups of a launch are handed to the 8 XCDs round-robin (bid % 8),
+// and each XCD has its own L2. Renumbering makes every XCD run a contiguous
+// range of a band-major order: bands of `xg` row groups, walked column group
+// by column group and row group by row group within a column, so the
+// workgroups resident on one XCD at a time form an xg-row block that shares
+// its activation rows and weight columns through that XCD's L2.
+// Returns mgroup * ngroups + ngroup.
+__device__ __forceinline__ int xcd_grouped_tile(int bid, int n, int ngroups, int xg) {
+  const int q = n >> 3, r = n & 7, x = bid & 7;
+  const int logical = x * q + (x < r ? x : r) + (bid >> 3);
+  const int mgroups = n / ngroups;
+  const int band = logical / (xg * ngroups);
+  const int first_m = band * xg;
+  const int gsize = mgroups - first_m < xg ? mgroups - first_m : xg;
+  const int within = logical - first_m * ngroups;
+  return (first_m + within % gsize) * ngroups + within / gsize;
+}
+
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);

@@ -103,6 +103,8 @@ struct GemmPlan {
   int fq;             // kind 4: activation quantized inside the kernel (no x_hat pass)
   int pa;             // kind 4: the quantizer pass writes the activation packed like a weight
   int ilv;            // kind 4: waves take interleaved chunks (wave, wave + W, ...)
+  int xg;             // kind 3, one K split: XCD-grouped tile order in bands of xg
+                      // row groups (0: row-major order of the output tiles)
   int64_t counter_bytes, xhat_bytes, partial_bytes, total_bytes;
 };
 // `aligned`: x rows are 16-byte aligned (pointer and row stride); the

@@ -205,6 +205,29 @@ def test_linear_every_lds32_config(mt, nt, st, wm, splits, plan_override):
     _run_case("tiny", M, K, N, 0, True, label=f"lds32<{mt},{nt},{st},{wm}> splits={splits}")
 
 
+# The XCD-grouped tile order (bands of xg row groups per XCD) only renumbers
+# the output tiles: on a grid that is not a multiple of 8 workgroups, with a
+# ragged last row group and a last band shorter than xg, every order matches
+# the oracle and all orders agree bit for bit (xg = 0: row-major order).
+@pytest.mark.parametrize("xg", [0, 1, 3, 4, 9])
+def test_linear_xcd_tile_order(xg, plan_override):
+    M, K, N = 1100, 1152, 2100
+    plan_override(f"kind=3,mt=2,nt=2,st=3,wm=2,splits=1,xg={xg}")
+    plan = fql.linear_plan(M, N, K)
+    assert "grid=81 " in plan and (f"xcd_bands={xg}" in plan if xg else "xcd_bands" not in plan), plan
+    _run_case("tiny", M, K, N, 0, True, label=f"xcd bands {xg}")
+    xb = cached_activations(synthetic.WORKLOADS["tiny"]["x"], M, K, "tiny")
+    W, gw, _, _ = weight_case("tiny", N, K, 0)
+    gx = Q.global_scale_from_amax(Q.amax_for_calibration(synthetic.bf16_bits_to_f32(xb), 0))
+    wobj, _, _ = _gpu_weight(W, gw, 0, gx)
+    xd = bf16_bits_to_dev(xb)
+    y = fql.linear_nvfp4(xd, wobj)
+    plan_override("kind=3,mt=2,nt=2,st=3,wm=2,splits=1,xg=0")
+    y0 = fql.linear_nvfp4(xd, wobj)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
+
+
 # Every per-wave-ring small-M configuration built into the library (W waves
 # splitting K, MT row tiles, NT column tiles per workgroup, D chunks in flight
 # per wave: the planner's choices), on a ragged shape, in every activation form
