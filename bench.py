@@ -562,7 +562,7 @@ def _oracle_runner(workload, fmt, n_rows, m_rows):
     return run_once, len(cases)
 
 
-def cpu_baseline(workload, fmt="nvfp4", n_rows=256, m_rows=64, runs=3):
+def cpu_baseline(workload, fmt="nvfp4", n_rows=384, m_rows=96, runs=3):
     """The oracle, as it stands, on a bounded sample of the workload: every case with
     the first `n_rows` weight rows and at most `m_rows` activation rows (the
     activation quantizer, the float64 GEMM and the epilogue are timed). Median of
