@@ -153,8 +153,8 @@ __device__ __forceinline__ void finish_tile(float4v (&acc)[MT][NT], int M, int N
 // 32x32 accumulator tiles (v_mfma_f32_32x32x16_f16 layout): the wave of
 // column slice wn holds MT x NT tiles; register r of tile (a, b) is row m0 +
 // a*32 + 8*(r/4) + 4*(lane/32) + r%4, column n0 + (wn*NT + b)*32 + lane%32.
-// The workgroup has 4 * WM waves (m0 is the wave's own first row).
-template <int MT, int NT, int WM = 1>
+// The workgroup has NW waves (m0 is the wave's own first row).
+template <int MT, int NT, int NW = 4>
 __device__ __forceinline__ void finish_tile32(float16v (&acc)[MT][NT], int M, int N, int m0, int n0,
                                               int wn, int split, int splits, float alpha,
                                               const uint16_t* __restrict__ bias,
@@ -173,7 +173,7 @@ __device__ __forceinline__ void finish_tile32(float16v (&acc)[MT][NT], int M, in
                                               acc[a][b][4 * r4 + 2], acc[a][b][4 * r4 + 3]};
   auto row_of = [&](int f, int i) { return (f / (NT * 4)) * 32 + 8 * (f % 4) + 4 * (lane >> 5) + i; };
   auto col_of = [&](int f) { return (wn * NT + (f / 4) % NT) * 32 + (lane & 31); };
-  finish_frags<MT * NT * 4, decltype(row_of), decltype(col_of), 4 * WM>(
+  finish_frags<MT * NT * 4, decltype(row_of), decltype(col_of), NW>(
       frag, row_of, col_of, M, N, m0, n0, split, splits, alpha, bias, y, ldy, slab, counter, s_flag);
 }
 
@@ -197,8 +197,6 @@ __device__ __forceinline__ void lds_load4(const void* sbase, uint32_t voff, uint
   lds = __builtin_amdgcn_readfirstlane(lds);
   __asm__ volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
-// A wave-uniform address the compiler cannot prove uniform (e.g. formed inside
-// a lane-dependent branch), moved to scalar registers for the loads above.
 // Output tile of workgroup `bid` (of `n`, one K split) in an XCD-grouped order.
 // The workgroups of a launch are handed to the 8 XCDs round-robin (bid % 8),
 // and each XCD has its own L2. Renumbering makes every XCD run a contiguous
@@ -218,6 +216,8 @@ __device__ __forceinline__ int xcd_grouped_tile(int bid, int n, int ngroups, int
   return (first_m + within % gsize) * ngroups + within / gsize;
 }
 
+// A wave-uniform address the compiler cannot prove uniform (e.g. formed inside
+// a lane-dependent branch), moved to scalar registers for the loads above.
 __device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);

@@ -103,6 +103,7 @@ struct GemmPlan {
   int fq;             // kind 4: activation quantized inside the kernel (no x_hat pass)
   int pa;             // kind 4: the quantizer pass writes the activation packed like a weight
   int ilv;            // kind 4: waves take interleaved chunks (wave, wave + W, ...)
+  int cw;             // kind 3: column waves (4, or 8 with wm = 1)
   int xg;             // kind 3, one K split: XCD-grouped tile order in bands of xg
                       // row groups (0: row-major order of the output tiles)
   int64_t counter_bytes, xhat_bytes, partial_bytes, total_bytes;
@@ -118,7 +119,7 @@ GemmPlan cached_plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned);
 // Whether gemm_tiled_kernel<mt, nt, wm> / gemm_lds32_kernel<mt, nt, st> is
 // built into the library.
 bool tiled_config_built(int mt, int nt, int wm);
-bool lds32_config_built(int mt, int nt, int st, int wm);
+bool lds32_config_built(int mt, int nt, int st, int wm, int cw);
 bool gemv_ring_config_built(int w, int mt, int nt, int d, bool packed_a);
 
 // Kernel name and parameters of a plan (diagnostics).

@@ -687,11 +687,11 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 //   s/2 of the slot's scale dword (l%16)*2 + s%2 for the chunk.
 // Per chunk and 32-column tile a lane therefore loads two code slots (even
 // and odd steps) and two scale dwords.
-template <int MT, int NT, int WM>
+template <int MT, int NT, int WM, int WN>
 struct LdsStage32 {
   uint4v a[WM * MT * 2 * 4][64];  // [16-row tile][32-deep step][lane] x_hat fragments
-  uint4v bq[4 * NT * 2][64];      // [column wave][32-col tile][even/odd steps][lane] codes
-  uint32_t bs[4 * NT * 2][64];    // [column wave][32-col tile][even/odd steps][lane] scales
+  uint4v bq[WN * NT * 2][64];     // [column wave][32-col tile][even/odd steps][lane] codes
+  uint32_t bs[WN * NT * 2][64];   // [column wave][32-col tile][even/odd steps][lane] scales
 };
 
 // WM = 2 doubles the waves (two per SIMD): the 4 column waves of each of two
@@ -699,8 +699,13 @@ struct LdsStage32 {
 // and the two waves of a column slice load one of its two code and scale
 // slots each and dequantize the slice both. A stalled wave (a barrier, a
 // wait) then leaves the matrix pipe to the other wave of its SIMD.
-template <int MT, int NT, int ST, int OCC, int WM = 1>
-__global__ __launch_bounds__(256 * WM, OCC) void gemm_lds32_kernel(
+// WN = 8 (with WM = 1) doubles the column waves instead: two per SIMD again,
+// each owning all MT row tiles and its own NT column tiles, so every weight
+// fragment is dequantized once and feeds MT MFMAs (MT = 4: half the
+// dequantization per MFMA of the WM = 2 layout); each wave then loads half
+// as many activation pieces per chunk (every other 16-row tile).
+template <int MT, int NT, int ST, int OCC, int WM = 1, int WN = 4>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_lds32_kernel(
     const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
     const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, int ngroups,
     int kc_per_split, int splits, int xg, float alpha,
@@ -710,16 +715,20 @@ __global__ __launch_bounds__(256 * WM, OCC) void gemm_lds32_kernel(
   if (alpha_dev != nullptr) alpha = *alpha_dev;  // per-call scale computed on the device
   static_assert(ST >= 3 && ST <= 4, "ring depth (chunk i+1 must be issued a whole chunk ahead)");
   static_assert(WM == 1 || WM == 2, "one or two row halves");
-  constexpr int NLB = 2 * NT / WM;    // code (and scale) slot loads per chunk per wave
-  constexpr int L = 2 * MT + 2 * NLB;  // LDS loads per chunk per wave
+  static_assert((WN == 4 || WN == 8) && WM * WN <= 8, "4 or 8 column waves, at most 8 waves");
+  constexpr int TS = WN / 4;             // 16-row tile stride of a wave's activation pieces
+  constexpr int NA = 2 * MT / TS;        // activation piece loads per chunk per wave
+  static_assert(NA >= 1, "every wave loads activation pieces");
+  constexpr int NLB = 2 * NT / WM;       // code (and scale) slot loads per chunk per wave
+  constexpr int L = NA + 2 * NLB;        // LDS loads per chunk per wave
   static_assert(L * (ST - 2) <= 63, "vmcnt range");
-  typedef LdsStage32<MT, NT, WM> Stage;
+  typedef LdsStage32<MT, NT, WM, WN> Stage;
   __shared__ Stage stage[ST];
   __shared__ uint32_t s_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;  // row half, column slice
+  const int wm = wave / WN, wn = wave % WN;  // row half, column slice
   const int64_t KC = Kp / 128;
   const int64_t KC4 = (KC + 3) / 4;
   // one K split: tiles in the XCD-grouped order when xg > 0; else
@@ -731,12 +740,15 @@ __global__ __launch_bounds__(256 * WM, OCC) void gemm_lds32_kernel(
   const int64_t c_begin = (int64_t)split * kc_per_split;
   const int64_t c_end = c_begin + kc_per_split < KC ? c_begin + kc_per_split : KC;
   const int nch = (int)(c_end - c_begin);
-  const int tile16_0 = (ngroup * 4 + wn) * NT * 2;  // first packed 16-column tile of the wave
+  const int tile16_0 = (ngroup * WN + wn) * NT * 2;  // first packed 16-column tile of the wave
 
   // wave-uniform global bases; per-lane byte offsets. A wave loads the
-  // 32-deep step wn of each 16-row tile of its row half.
+  // 32-deep step wn % 4 of every TS-th 16-row tile of its row half, from tile
+  // wn / 4 on.
+  const int64_t a_tile_stride = (Kp / 32) * 1024;  // bytes between 16-row x_hat tiles
   const uint8_t* a_base = reinterpret_cast<const uint8_t*>(xhat) +
-                          (((int64_t)mgroup * WM + wm) * MT * 2 * (Kp / 32) + wn) * 1024;
+                          (((int64_t)mgroup * WM + wm) * MT * 2 * (Kp / 32) + wn % 4) * 1024 +
+                          (wn / 4) * a_tile_stride;
   const uint32_t a_voff = lane * 16;
   const int jc = lane & 31, hh = lane >> 5;  // column in the 32-column tile, k half
   // Per-lane offsets of the code and scale slots this wave loads: slot (b, e)
@@ -763,7 +775,6 @@ __global__ __launch_bounds__(256 * WM, OCC) void gemm_lds32_kernel(
     const uint8_t* s;  // the chunk's scale dword column
     uint32_t la, lq, ls;  // this wave's LDS destinations in the stage
   };
-  const int64_t a_tile_stride = (Kp / 32) * 1024;  // bytes between 16-row x_hat tiles
   // the wave's slot i sits at slot index (wn*NT + b)*2 + e of the stage
   constexpr int SLOT_STEP = WM == 1 ? 1 : 2;
   auto refill_of = [&](Stage& sg, int64_t c) -> Refill {
@@ -772,20 +783,20 @@ __global__ __launch_bounds__(256 * WM, OCC) void gemm_lds32_kernel(
     r.a = uniform_ptr(a_base + c * 4096);
     r.q = uniform_ptr(wcodes + c * 1024);
     r.s = uniform_ptr(wscales + (c >> 2) * 512 + (c & 3) * 4);
-    r.la = __builtin_amdgcn_readfirstlane(lds_offset(&sg.a[wm * MT * 2 * 4 + wn][0]));
+    r.la = __builtin_amdgcn_readfirstlane(lds_offset(&sg.a[(wm * MT * 2 + wn / 4) * 4 + wn % 4][0]));
     r.lq = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bq[wn * NT * 2 + (WM == 1 ? 0 : wm)][0]));
     r.ls = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bs[wn * NT * 2 + (WM == 1 ? 0 : wm)][0]));
     return r;
   };
   // LDS load number e (0 <= e < L) of a chunk
   auto issue_one = [&](const Refill& r, int e) {
-    if (e < 2 * MT) {
-      lds_load16(r.a + e * a_tile_stride, a_voff, r.la + e * 4 * 1024);
-    } else if (e < 2 * MT + NLB) {
-      const int i = e - 2 * MT;
+    if (e < NA) {
+      lds_load16(r.a + e * TS * a_tile_stride, a_voff, r.la + e * TS * 4 * 1024);
+    } else if (e < NA + NLB) {
+      const int i = e - NA;
       lds_load16(r.q, q_voff[i], r.lq + i * SLOT_STEP * 1024);
     } else {
-      const int i = e - 2 * MT - NLB;
+      const int i = e - NA - NLB;
       lds_load4(r.s, s_voff[i], r.ls + i * SLOT_STEP * 256);
     }
   };
@@ -911,9 +922,9 @@ __global__ __launch_bounds__(256 * WM, OCC) void gemm_lds32_kernel(
   }
   wait_vmcnt<0>();  // no LDS load may still be in flight when the workgroup ends
 
-  float4v* slab = partial + (int64_t)tilegrp * splits * (4 * WM * MT * NT * 4 * 64);
-  finish_tile32<MT, NT, WM>(acc, M, N, (mgroup * WM + wm) * MT * 32, ngroup * 4 * NT * 32, wn,
-                            split, splits, alpha, bias, y, ldy, slab, counters + tilegrp, &s_flag);
+  float4v* slab = partial + (int64_t)tilegrp * splits * (WN * WM * MT * NT * 4 * 64);
+  finish_tile32<MT, NT, WM * WN>(acc, M, N, (mgroup * WM + wm) * MT * 32, ngroup * WN * NT * 32, wn,
+                                 split, splits, alpha, bias, y, ldy, slab, counters + tilegrp, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -928,7 +939,7 @@ static constexpr int kCUs = 256;
 // float32 sum over K).
 struct GemmOverride {
   int kind = -1, waves = 0, ntw = 0, rc = 0, mt = 0, nt = 0, wm = 0, st = 0, splits = 0, fq = -1, pa = -1,
-      il = -1, xg = -1;
+      il = -1, xg = -1, cw = 0;
 };
 static GemmOverride gemm_override() {
   GemmOverride o;
@@ -956,6 +967,7 @@ static GemmOverride gemm_override() {
       else if (k == "pa" && (v == 0 || v == 1)) o.pa = v;
       else if (k == "il" && (v == 0 || v == 1)) o.il = v;
       else if (k == "xg" && v >= 0 && v <= 64) o.xg = v;
+      else if (k == "cw" && (v == 4 || v == 8)) o.cw = v;
     }
     pos = end + 1;
   }
@@ -1052,6 +1064,7 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     if (p.kind == 3 && d.total_bytes() >= ((int64_t)1 << 32)) p.kind = 1;
     const bool lds_ring = p.kind == 3;
     p.wm = 1;
+    p.cw = 4;
     p.st = 3;  // (the tables below may change wm for kind 3)
     if (!lds_ring) {
       if (M <= 16) { p.mt = 1; p.nt = 1; }
@@ -1067,22 +1080,26 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
         if ((M + 127) / 128 * ((ntiles + 7) / 8) < 192) { p.mt = 2; p.st = 4; }
       } else {
         // 128 x 256 tiles on 8 waves, two per SIMD (measured 3-8% faster than
-        // one wave per SIMD with 128-row waves on the prefill shapes)
-        p.mt = 2; p.nt = 2; p.st = 3; p.wm = 2;
+        // one wave per SIMD with 128-row waves on the prefill shapes), each
+        // wave 128 x 32 so that a weight fragment feeds 4 MFMAs (about 1%
+        // faster again than 64 x 64 waves)
+        p.mt = 4; p.nt = 1; p.st = 3; p.cw = 8;
       }
     }
-    if (ov.mt || ov.nt || ov.wm || ov.st) {
+    if (ov.mt || ov.nt || ov.wm || ov.st || ov.cw) {
       if (ov.mt) p.mt = ov.mt;
       if (ov.nt) p.nt = ov.nt;
       if (ov.wm && (!lds_ring || ov.wm <= 2)) p.wm = ov.wm;
       if (ov.st) p.st = ov.st;
+      if (lds_ring && ov.wm == 2) p.cw = 4;  // at most 8 waves
+      if (lds_ring && ov.cw) p.cw = ov.cw;
     }
-    const bool built = p.kind == 3 ? lds32_config_built(p.mt, p.nt, p.st, p.wm)
+    const bool built = p.kind == 3 ? lds32_config_built(p.mt, p.nt, p.st, p.wm, p.cw)
                                    : tiled_config_built(p.mt, p.nt, p.wm);
-    if (!built) { p.kind = 1; p.mt = 1; p.nt = 1; p.wm = 1; }
+    if (!built) { p.kind = 1; p.mt = 1; p.nt = 1; p.wm = 1; p.cw = 4; }
     // rows and 16-column tiles per workgroup
     const int tile_rows = p.kind == 3 ? 32 * p.mt * p.wm : 16 * p.mt * p.wm;
-    const int tile_cols16 = p.kind == 3 ? 8 * p.nt : (4 / p.wm) * p.nt;
+    const int tile_cols16 = p.kind == 3 ? 2 * p.cw * p.nt : (4 / p.wm) * p.nt;
     p.Mp = round_up(M, tile_rows);
     const int64_t ngroups = (ntiles + tile_cols16 - 1) / tile_cols16;
     const int64_t mgroups = p.Mp / tile_rows;
@@ -1112,7 +1129,7 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
   }
   // [splits][waves][fragments][64 lanes] float4 per output tile
   const int64_t frags = (int64_t)p.mt * p.nt * (p.kind == 3 ? 4 : 1);
-  const int64_t slab = (int64_t)p.splits * (p.kind == 3 ? 4 * p.wm : 4) * frags * 64 * 16;
+  const int64_t slab = (int64_t)p.splits * (p.kind == 3 ? p.cw * p.wm : 4) * frags * 64 * 16;
   p.partial_bytes = p.splits > 1 ? round_up(p.groups * slab, 256) : 0;
   p.counter_bytes = kCounterBytes;
   p.total_bytes = p.counter_bytes + p.xhat_bytes + p.partial_bytes;
@@ -1125,10 +1142,11 @@ std::string describe_plan(const GemmPlan& p) {
     std::snprintf(b, sizeof(b), "%sgemv_ring_kernel<W=%d,MT=%d,NT=%d,D=%d,FQ=%d,PA=%d> grid=%lld splits=1%s",
                   p.fq ? "" : p.pa ? "quant_nvfp4_apack_kernel + " : "quant_nvfp4_xhat_kernel + ", p.waves,
                   p.mt, p.nt, p.st, p.fq, p.pa, (long long)p.groups, p.ilv ? " chunks=interleaved" : "");
-  } else if (p.kind == 3 && p.wm > 1) {
+  } else if (p.kind == 3 && (p.wm > 1 || p.cw != 4)) {
     std::snprintf(b, sizeof(b),
-                  "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d,WM=%d> grid=%lld splits=%d%s",
-                  p.mt, p.nt, p.st, p.wm, (long long)(p.groups * p.splits), p.splits,
+                  "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d,%s=%d> grid=%lld splits=%d%s",
+                  p.mt, p.nt, p.st, p.wm > 1 ? "WM" : "WN", p.wm > 1 ? p.wm : p.cw,
+                  (long long)(p.groups * p.splits), p.splits,
                   p.xg > 0 ? (" xcd_bands=" + std::to_string(p.xg)).c_str() : "");
   } else if (p.kind == 3) {
     std::snprintf(b, sizeof(b),
@@ -1224,7 +1242,7 @@ static hipError_t launch_tiled_t(const GemmPlan& p, const _Float16* xhat, const 
 // for weights of 4 GiB or more, whose offsets exceed the 32-bit ring kernel's)
 #define FQL_TILED_CONFIGS(X) X(1, 1, 1) X(2, 1, 1) X(2, 2, 2) X(4, 2, 2) X(8, 4, 1)
 
-template <int MT, int NT, int ST, int OCC, int WM>
+template <int MT, int NT, int ST, int OCC, int WM, int WN>
 static hipError_t launch_lds32_t(const GemmPlan& p, const _Float16* xhat, const uint8_t* packed,
                                  int64_t M, int64_t N, float alpha, const float* alpha_dev,
                                  const uint16_t* bias,
@@ -1232,19 +1250,20 @@ static hipError_t launch_lds32_t(const GemmPlan& p, const _Float16* xhat, const 
                                  hipStream_t st) {
   const uint8_t* wcodes = packed;
   const uint8_t* wscales = packed + p.Np * p.Kp / 2;
-  gemm_lds32_kernel<MT, NT, ST, OCC, WM><<<(unsigned)(p.groups * p.splits), 256 * WM, 0, st>>>(
+  gemm_lds32_kernel<MT, NT, ST, OCC, WM, WN><<<(unsigned)(p.groups * p.splits), 64 * WM * WN, 0, st>>>(
       xhat, wcodes, wscales, (int)M, (int)N, p.Kp, (int)(p.Np / 16), (int)p.ngroups,
       p.kc_per_split, p.splits, p.xg, alpha, alpha_dev, bias, y, ldy, partial, counters);
   return hipGetLastError();
 }
 
-// The (MT, NT, ST, OCC, WM) 32x32 LDS-ring configurations built into the library.
+// The (MT, NT, ST, OCC, WM, WN) 32x32 LDS-ring configurations built into the library.
 #define FQL_LDS32_CONFIGS(X) \
-  X(4, 2, 3, 1, 1) X(4, 1, 3, 1, 1) X(2, 2, 4, 1, 1) X(2, 2, 3, 2, 1) X(2, 1, 4, 2, 1) \
-  X(2, 1, 3, 2, 1) X(1, 2, 4, 2, 1) X(1, 2, 3, 2, 1) X(2, 2, 3, 1, 2)
+  X(4, 2, 3, 1, 1, 4) X(4, 1, 3, 1, 1, 4) X(2, 2, 4, 1, 1, 4) X(2, 2, 3, 2, 1, 4) \
+  X(2, 1, 4, 2, 1, 4) X(2, 1, 3, 2, 1, 4) X(1, 2, 4, 2, 1, 4) X(1, 2, 3, 2, 1, 4) \
+  X(2, 2, 3, 1, 2, 4) X(4, 1, 3, 1, 1, 8)
 
-bool lds32_config_built(int mt, int nt, int st, int wm) {
-#define FQL_X(A, B, C, D, E) if (mt == A && nt == B && st == C && wm == E) return true;
+bool lds32_config_built(int mt, int nt, int st, int wm, int cw) {
+#define FQL_X(A, B, C, D, E, F) if (mt == A && nt == B && st == C && wm == E && cw == F) return true;
   FQL_LDS32_CONFIGS(FQL_X)
 #undef FQL_X
   return false;
@@ -1361,9 +1380,9 @@ static hipError_t launch_gemm_part(const GemmPlan& p, const uint16_t* x, int64_t
     return hipErrorInvalidValue;
   }
   if (p.kind == 3) {
-#define FQL_X(A, B, C, D, E)                                                                     \
-  if (p.mt == A && p.nt == B && p.st == C && p.wm == E)                                          \
-    return launch_lds32_t<A, B, C, D, E>(p, xhat, packed, M, N, alpha, alpha_dev, bias, y, ldy, partial4, counters, st);
+#define FQL_X(A, B, C, D, E, F)                                                                  \
+  if (p.mt == A && p.nt == B && p.st == C && p.wm == E && p.cw == F)                             \
+    return launch_lds32_t<A, B, C, D, E, F>(p, xhat, packed, M, N, alpha, alpha_dev, bias, y, ldy, partial4, counters, st);
     FQL_LDS32_CONFIGS(FQL_X)
 #undef FQL_X
     return hipErrorInvalidValue;

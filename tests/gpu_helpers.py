@@ -94,9 +94,9 @@ def plan_rows(plan, M):
     """Rows Mp of the activation operand a launch plan writes (M padded to its row tile)."""
     import re
 
-    m = re.search(r"gemm_lds32_kernel<MT=(\d+),NT=\d+,ST=\d+(?:,WM=(\d+))?>", plan)
+    m = re.search(r"gemm_lds32_kernel<MT=(\d+),NT=\d+,ST=\d+(?:,(WM|WN)=(\d+))?>", plan)
     if m:
-        t = 32 * int(m.group(1)) * int(m.group(2) or 1)
+        t = 32 * int(m.group(1)) * (int(m.group(3)) if m.group(2) == "WM" else 1)
     elif "gemm_tiled_kernel" in plan:
         m = re.search(r"gemm_tiled_kernel<MT=(\d+),NT=\d+,WM=(\d+)>", plan)
         t = 16 * int(m.group(1)) * int(m.group(2))

@@ -304,6 +304,21 @@ def test_plan_override_set_and_cleared():
     assert fql.lib().fql_set_plan_override(7, None) == -1
 
 
+def test_lds32_layouts_and_tile_order_in_the_plan():
+    # above 128 rows: 128 x 256 tiles on 8 column waves in XCD bands of 4 row
+    # groups (clamped to the row groups there are); up to 128 rows 4 waves
+    assert ("gemm_lds32_kernel<MT=4,NT=1,ST=3,WN=8> grid=7168 splits=1 xcd_bands=4"
+            in fql.linear_plan(8192, 28672, 4096))
+    assert "xcd_bands=2" in fql.linear_plan(256, 51200, 5120)
+    assert "gemm_lds32_kernel<MT=2,NT=1,ST=4> grid=192 splits=2" in fql.linear_plan(128, 6144, 4096)
+    # a two-row-half override implies four column waves; the band is selectable
+    with fql.plan_override("kind=3,mt=2,nt=2,st=3,wm=2,splits=1,xg=0"):
+        plan = fql.linear_plan(1100, 2100, 1152)
+        assert "gemm_lds32_kernel<MT=2,NT=2,ST=3,WM=2> grid=81 splits=1" in plan and "xcd" not in plan
+    with fql.plan_override("kind=3,mt=4,nt=1,st=3,wm=1,cw=8,splits=1,xg=3"):
+        assert "WN=8> grid=81 splits=1 xcd_bands=3" in fql.linear_plan(1100, 2100, 1152)
+
+
 def test_binding_holds_no_numeric_formula():
     # every scale and alpha of the layer comes from the library; the binding
     # only marshals arguments: no numpy, no float literal but the unit alpha,

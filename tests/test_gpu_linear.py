@@ -190,19 +190,21 @@ def test_linear_every_tiled_config(mt, nt, wm, splits, plan_override):
 # Every 32x32-MFMA LDS-ring configuration (workgroup tile (MT*32) rows x
 # (4*NT*32) columns), same ragged shape (N = 400 leaves half a 32-column tile).
 # (WM = 2: two row halves of 4 waves each, two waves per SIMD.)
-LDS32_CONFIGS = [(4, 2, 3, 1), (4, 1, 3, 1), (2, 2, 4, 1), (2, 2, 3, 1), (2, 1, 4, 1), (2, 1, 3, 1),
-                 (1, 2, 4, 1), (1, 2, 3, 1), (2, 2, 3, 2)]
+# (WN = 8: eight column waves of one row half, two per SIMD.)
+LDS32_CONFIGS = [(4, 2, 3, 1, 4), (4, 1, 3, 1, 4), (2, 2, 4, 1, 4), (2, 2, 3, 1, 4), (2, 1, 4, 1, 4),
+                 (2, 1, 3, 1, 4), (1, 2, 4, 1, 4), (1, 2, 3, 1, 4), (2, 2, 3, 2, 4), (4, 1, 3, 1, 8)]
 
 
 @pytest.mark.parametrize("splits", [1, 3])
-@pytest.mark.parametrize("mt,nt,st,wm", LDS32_CONFIGS)
-def test_linear_every_lds32_config(mt, nt, st, wm, splits, plan_override):
+@pytest.mark.parametrize("mt,nt,st,wm,cw", LDS32_CONFIGS)
+def test_linear_every_lds32_config(mt, nt, st, wm, cw, splits, plan_override):
     M, K, N = 150, 1152, 400
-    plan_override(f"kind=3,mt={mt},nt={nt},st={st},wm={wm},splits={splits}")
+    plan_override(f"kind=3,mt={mt},nt={nt},st={st},wm={wm},cw={cw},splits={splits}")
     plan = fql.linear_plan(M, N, K)
-    want = f"gemm_lds32_kernel<MT={mt},NT={nt},ST={st}" + (f",WM={wm}>" if wm > 1 else ">")
+    want = f"gemm_lds32_kernel<MT={mt},NT={nt},ST={st}" + (
+        f",WM={wm}>" if wm > 1 else f",WN={cw}>" if cw != 4 else ">")
     assert want in plan and f"splits={splits}" in plan, plan
-    _run_case("tiny", M, K, N, 0, True, label=f"lds32<{mt},{nt},{st},{wm}> splits={splits}")
+    _run_case("tiny", M, K, N, 0, True, label=f"lds32<{mt},{nt},{st},{wm},{cw}> splits={splits}")
 
 
 # The XCD-grouped tile order (bands of xg row groups per XCD) only renumbers
