@@ -406,7 +406,8 @@ def calibration(stream_sizes_mb=(14.2, 33.1, 66.1, 147.5, 512.0), mfma_reps=3):
     del pool
     iters = 8000  # about a millisecond per launch, like the large GEMMs
     for kind, name, flop in ((0, "f16_32x32x16", 32768), (1, "fp8_16x16x128", 65536),
-                             (2, "fp4_16x16x128", 65536)):
+                             (2, "fp4_16x16x128", 65536), (4, "fp8_32x32x64", 131072),
+                             (3, "fp4_32x32x64", 131072)):
         for wps in (1, 2):
             grid = 256 * wps
             with torch.cuda.stream(stream):

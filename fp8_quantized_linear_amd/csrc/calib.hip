@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4v* __restri
 
 // KIND 0: v_mfma_f32_32x32x16_f16 (32768 flops); 1: the scaled
 // 16x16x128 MFMA on FP8 (E4M3) operands; 2: the same on FP4 (E2M1) operands
-// (16x16x128: 65536 flops). Eight independent accumulators per wave, `iters`
+// (16x16x128: 65536 flops); 3 and 4: the scaled 32x32x64 MFMA on FP4 and on
+// FP8 operands (131072 flops). Eight independent accumulators per wave, `iters`
 // rounds; the operands depend on the lane so nothing folds away.
 template <int KIND>
 __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __restrict__ sink) {
@@ -66,6 +67,23 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, float* __rest
     for (int it = 0; it < iters; ++it)
 #pragma unroll
       for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c[j], 0, 0, 0);
+    for (int j = 0; j < 8; ++j) acc_sum += c[j][j];
+  } else if constexpr (KIND >= 3) {
+    constexpr int F = KIND == 4 ? 0 : 4;  // operand format: 0 = E4M3, 4 = E2M1
+    int8v a, b;
+    for (int i = 0; i < 8; ++i) {
+      a[i] = 0x01010101 * ((lane + i) & 7);
+      b[i] = 0x02020202 * ((lane + 3 * i) & 3);
+    }
+    float16v c[8];
+    for (int j = 0; j < 8; ++j) {
+      c[j] = float16v{};
+      c[j][0] = (float)j;
+    }
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        c[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c[j], F, F, 0, 127, 0, 127);
     for (int j = 0; j < 8; ++j) acc_sum += c[j][j];
   } else {
     constexpr int F = KIND == 1 ? 0 : 4;  // operand format: 0 = E4M3, 4 = E2M1
@@ -102,13 +120,16 @@ int fql_calib_stream_read(const void* buf, int64_t bytes, int grid, uint32_t* si
 
 // `grid` workgroups of 4 waves, each wave `iters` rounds of 8 MFMAs of kind
 // `kind` (0: float16 32x32x16, 1: scaled FP8 16x16x128, 2: scaled FP4
-// 16x16x128). Flops = grid * 4 * iters * 8 * (32768 for kind 0, 65536 else).
+// 16x16x128, 3: scaled FP4 32x32x64, 4: scaled FP8 32x32x64). Flops =
+// grid * 4 * iters * 8 * (32768 for kind 0, 65536 for 1 and 2, 131072 for 3 and 4).
 int fql_calib_mfma_loop(int kind, int grid, int iters, float* sink, void* stream) {
   if (!sink || grid < 1 || iters < 1) return -1;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (kind == 0) mfma_loop_kernel<0><<<grid, 256, 0, st>>>(iters, sink);
   else if (kind == 1) mfma_loop_kernel<1><<<grid, 256, 0, st>>>(iters, sink);
   else if (kind == 2) mfma_loop_kernel<2><<<grid, 256, 0, st>>>(iters, sink);
+  else if (kind == 3) mfma_loop_kernel<3><<<grid, 256, 0, st>>>(iters, sink);
+  else if (kind == 4) mfma_loop_kernel<4><<<grid, 256, 0, st>>>(iters, sink);
   else return -1;
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
