@@ -168,7 +168,7 @@ def _has_quant_pass(M, N, K):
     return " + " in fql.linear_plan(M, N, K, aligned=True)
 
 
-def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic=False, only=None):
+def gpu_bench(workload, steps, warmup, hb, per_case_reps=11, fmt="nvfp4", dynamic=False, only=None):
     import torch
 
     import fp8_quantized_linear_amd as fql
@@ -286,7 +286,8 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic
     del graphs
 
     # per-call duration of each case: a graph of R back-to-back calls of that case
-    # (rotating weight copies), timed with HIP events on the replay stream
+    # (rotating weight copies), each replay timed with HIP events on the replay
+    # stream; the median replay gives the per-call time, p10 and p90 its spread
     with torch.cuda.stream(stream):
         for s in setups:
             R = max(8, len(s["objs"]))
@@ -296,13 +297,16 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic
                     call(s, r)
             g.replay()
             stream.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(per_case_reps):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(per_case_reps + 1)]
+            evs[0].record(stream)
+            for i in range(per_case_reps):
                 g.replay()
-            b.record(stream)
-            b.synchronize()
-            s["call_ms"] = a.elapsed_time(b) / (per_case_reps * R)
+                evs[i + 1].record(stream)
+            evs[-1].synchronize()
+            per = sorted(evs[i].elapsed_time(evs[i + 1]) / R for i in range(per_case_reps))
+            s["call_ms"] = per[len(per) // 2]
+            s["call_ms_p10"] = per[int(0.1 * (len(per) - 1))]
+            s["call_ms_p90"] = per[int(round(0.9 * (len(per) - 1)))]
             del g
     # GEMM kernel alone: calls with a quantizer pass run as their two halves, and
     # HIP events on the launch stream bracket each GEMM launch (rotating copies)
@@ -331,6 +335,7 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=3, fmt="nvfp4", dynamic
         tf = s["flops"] / (ms * 1e-3) / 1e12
         gbs = s["bytes"] / (ms * 1e-3) / 1e9
         d = dict(case=s["name"], kernel=s["kernel"], us=round(ms * 1e3, 2),
+                 us_p10=round(s["call_ms_p10"] * 1e3, 2), us_p90=round(s["call_ms_p90"] * 1e3, 2),
                  gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 3), tflops=round(tf, 1),
                  mfma_frac=round(tf / MFMA_PEAK[fmt], 3))
         if fmt == "nvfp4":
@@ -529,36 +534,53 @@ def _oracle_runner(workload, fmt, n_rows, m_rows):
             xcache[key] = synthetic.bf16_bits_to_f32(xb)
         return xcache[key]
 
-    def layer(wl, x, hb, wq):
+    def quantize(wl, x, hb, wq):
+        """the activation side: (operands for the GEMM step)"""
         if fmt == "mxfp4":
-            return X.linear_mxfp4(*X.quant_mxfp4(x), *wq)
+            return X.quant_mxfp4(x)
         if fmt == "mxfp8":
-            return P.linear_mxfp8(*P.quant_mxfp8(x), *wq)
+            return P.quant_mxfp8(x)
         if fmt == "fp8_block":
-            return P.linear_fp8_block(*P.quant_fp8_block_act(x), *wq)
+            return P.quant_fp8_block_act(x)
         if fmt == "fp8":
             sx = P.scale_from_amax(np.abs(x).max())
-            return P.linear_fp8_tensor(P.quant_fp8_tensor(x, sx), wq[0], P.output_scale(sx, wq[1]))
-        gw, wc, wsc = wq
+            return P.quant_fp8_tensor(x, sx), sx
         if wl == "transform":
             T64 = bf16_bits_to_f64(synthetic.transform_matrix(hb))
             gx = Q.global_scale_from_amax(TR.tensor_amax(TR.block_transform(x, T64)))
-            xc, xs = TR.quant_nvfp4_transform(x, T64, gx)
-        else:
-            gx = Q.global_scale_from_amax(Q.amax_for_calibration(x, hb))
-            xc, xs = Q.quant_nvfp4(x, gx, hb)
+            return TR.quant_nvfp4_transform(x, T64, gx) + (gx,)
+        gx = Q.global_scale_from_amax(Q.amax_for_calibration(x, hb))
+        return Q.quant_nvfp4(x, gx, hb) + (gx,)
+
+    def gemm(xq, wq):
+        """the float64 GEMM and the epilogue"""
+        if fmt == "mxfp4":
+            return X.linear_mxfp4(*xq, *wq)
+        if fmt == "mxfp8":
+            return P.linear_mxfp8(*xq, *wq)
+        if fmt == "fp8_block":
+            return P.linear_fp8_block(*xq, *wq)
+        if fmt == "fp8":
+            return P.linear_fp8_tensor(xq[0], wq[0], P.output_scale(xq[1], wq[1]))
+        gw, wc, wsc = wq
+        xc, xs, gx = xq
         return Q.linear_nvfp4(xc, xs, wc, wsc, TR.dynamic_alpha(gx, gw))
 
     def run_once():
-        t_total = flops = 0.0
+        """one pass: (seconds, flops, seconds in the activation quantizer)"""
+        t_total = t_quant = flops = 0.0
         for (wl, M, name, K, N, hb, with_bias) in cases:
             wq = weight(wl, name, K, N, hb)
             x = act(wl, M, K)
             t0 = time.perf_counter()
-            layer(wl, x, hb, wq)
-            t_total += time.perf_counter() - t0
+            xq = quantize(wl, x, hb, wq)
+            t1 = time.perf_counter()
+            gemm(xq, wq)
+            t2 = time.perf_counter()
+            t_total += t2 - t0
+            t_quant += t1 - t0
             flops += 2.0 * x.shape[0] * min(N, n_rows) * K
-        return t_total, flops
+        return t_total, flops, t_quant
 
     return run_once, len(cases)
 
@@ -583,16 +605,20 @@ def cpu_baseline(workload, fmt="nvfp4", n_rows=384, m_rows=96, runs=3):
                     res.append(run_once())
             else:
                 res.append(run_once())
-        rates = sorted(f / t / 1e12 for t, f in res)
-        legs[leg] = dict(value=round(rates[len(rates) // 2], 6),
-                         seconds=round(sum(t for t, _ in res), 1))
+        res.sort(key=lambda r: r[1] / r[0])
+        t, f, tq = res[len(res) // 2]  # the median pass
+        legs[leg] = dict(value=round(f / t / 1e12, 6), seconds=round(sum(r[0] for r in res), 1),
+                         quant_s=round(tq, 3), gemm_s=round(t - tq, 3))
     sample = (f"median of {runs} passes over the {ncases} {workload} cases, each with the first "
               f"{n_rows} weight rows and at most {m_rows} activation rows (activation quantize + "
               f"float64 GEMM + epilogue); {legs['all']['seconds']} s of oracle time on all cores, "
               f"{legs['one']['seconds']} s on one thread")
     return dict(value=legs["all"]["value"], unit="TFLOP/s", cores=int(_threads()), kind="oracle",
-                sample=sample, one_thread=dict(value=legs["one"]["value"], unit="TFLOP/s",
-                                               cores=1))
+                sample=sample,
+                pass_seconds=dict(quantize=legs["all"]["quant_s"], gemm=legs["all"]["gemm_s"]),
+                one_thread=dict(value=legs["one"]["value"], unit="TFLOP/s", cores=1,
+                                pass_seconds=dict(quantize=legs["one"]["quant_s"],
+                                                  gemm=legs["one"]["gemm_s"])))
 
 
 def main():
