@@ -1074,10 +1074,16 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
       else { p.mt = 8; p.nt = 4; }
     } else {  // kind 3, 32x32 tiles: MT x 32 rows, 4 x NT x 32 columns
       if (M <= 128) {
-        // 128 x 128 tiles when they alone fill the GPU, else 64 x 128 tiles
-        // with a deeper ring and split K
+        // 64 x 256 tiles on 8 column waves (two per SIMD) when they alone
+        // fill the GPU (gate_up at M = 128: 41.7 against 44.3 us for 128 x 128
+        // tiles on 4 waves); else 128 x 128 tiles when those fill it, else
+        // 64 x 128 tiles with a deeper ring and split K
         p.mt = 4; p.nt = 1; p.st = 3;
-        if ((M + 127) / 128 * ((ntiles + 7) / 8) < 192) { p.mt = 2; p.st = 4; }
+        if ((M + 63) / 64 * ((ntiles + 15) / 16) >= 192) {
+          p.mt = 2; p.st = 4; p.cw = 8;
+        } else if ((M + 127) / 128 * ((ntiles + 7) / 8) < 192) {
+          p.mt = 2; p.st = 4;
+        }
       } else {
         // 128 x 256 tiles on 8 waves, two per SIMD (measured 3-8% faster than
         // one wave per SIMD with 128-row waves on the prefill shapes), each
@@ -1260,7 +1266,7 @@ static hipError_t launch_lds32_t(const GemmPlan& p, const _Float16* xhat, const 
 #define FQL_LDS32_CONFIGS(X) \
   X(4, 2, 3, 1, 1, 4) X(4, 1, 3, 1, 1, 4) X(2, 2, 4, 1, 1, 4) X(2, 2, 3, 2, 1, 4) \
   X(2, 1, 4, 2, 1, 4) X(2, 1, 3, 2, 1, 4) X(1, 2, 4, 2, 1, 4) X(1, 2, 3, 2, 1, 4) \
-  X(2, 2, 3, 1, 2, 4) X(4, 1, 3, 1, 1, 8)
+  X(2, 2, 3, 1, 2, 4) X(4, 1, 3, 1, 1, 8) X(2, 1, 4, 1, 1, 8)
 
 bool lds32_config_built(int mt, int nt, int st, int wm, int cw) {
 #define FQL_X(A, B, C, D, E, F) if (mt == A && nt == B && st == C && wm == E && cw == F) return true;

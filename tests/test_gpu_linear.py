@@ -192,7 +192,8 @@ def test_linear_every_tiled_config(mt, nt, wm, splits, plan_override):
 # (WM = 2: two row halves of 4 waves each, two waves per SIMD.)
 # (WN = 8: eight column waves of one row half, two per SIMD.)
 LDS32_CONFIGS = [(4, 2, 3, 1, 4), (4, 1, 3, 1, 4), (2, 2, 4, 1, 4), (2, 2, 3, 1, 4), (2, 1, 4, 1, 4),
-                 (2, 1, 3, 1, 4), (1, 2, 4, 1, 4), (1, 2, 3, 1, 4), (2, 2, 3, 2, 4), (4, 1, 3, 1, 8)]
+                 (2, 1, 3, 1, 4), (1, 2, 4, 1, 4), (1, 2, 3, 1, 4), (2, 2, 3, 2, 4), (4, 1, 3, 1, 8),
+                 (2, 1, 4, 1, 8)]
 
 
 @pytest.mark.parametrize("splits", [1, 3])
