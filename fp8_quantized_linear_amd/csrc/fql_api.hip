@@ -396,7 +396,7 @@ int fql_linear_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ldx,
   if (!x) return fail(FQL_ERR_INVALID, "null pointer");
   const bool xal = aligned16(x, ldx, 2);
   const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, xal);
-  if (!fql::has_quant_pass(plan, hadamard_block, xal, K, nullptr))
+  if (!fql::has_quant_pass(plan))
     return fail(FQL_ERR_UNSUPPORTED, "this call's plan quantizes inside the GEMM (%s)",
                 fql::describe_plan(plan).c_str());
   if (int r = check_workspace(workspace, workspace_bytes, plan.total_bytes)) return r;
@@ -419,7 +419,7 @@ int fql_linear_nvfp4_gemm(int64_t M, int64_t K, int x_aligned, const void* w_pac
   if (reinterpret_cast<uintptr_t>(w_packed) % 16 != 0)
     return fail(FQL_ERR_INVALID, "packed weight must be 16-byte aligned");
   const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, x_aligned != 0);
-  if (plan.kind == 0 || (plan.kind == 4 && plan.fq))
+  if (plan.kind == 0)
     return fail(FQL_ERR_UNSUPPORTED, "this call's plan quantizes inside the GEMM (%s)",
                 fql::describe_plan(plan).c_str());
   if (int r = check_workspace(workspace, workspace_bytes, plan.total_bytes)) return r;

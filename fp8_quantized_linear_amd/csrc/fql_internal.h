@@ -86,8 +86,7 @@ struct GemmPlan {
   int kind;
   int mt;             // kind 1: 16-row M tiles per wave
   int nt;             // kind 1: 16-column N tiles per wave
-  int wm;             // kind 1: wave rows (the 4 waves form a wm x 4/wm grid);
-                      // kind 3: row halves (4 * wm waves, wm of them per SIMD)
+  int wm;             // kind 1: wave rows (the 4 waves form a wm x 4/wm grid)
   int st;             // kinds 3, 4: LDS ring depth (chunks)
   int64_t Mp;         // M padded to a whole number of M tiles
   int64_t Np, Kp;     // packed weight dims
@@ -100,10 +99,7 @@ struct GemmPlan {
   int qpre;           // kind 0: activation blocks per thread loaded ahead of the weights
   int ntw;            // kind 0: 16-column tiles per workgroup
   int64_t lds_bytes;  // kind 0: dynamic LDS (compact activation copy / reduction)
-  int fq;             // kind 4: activation quantized inside the kernel (no x_hat pass)
-  int pa;             // kind 4: the quantizer pass writes the activation packed like a weight
-  int ilv;            // kind 4: waves take interleaved chunks (wave, wave + W, ...)
-  int cw;             // kind 3: column waves (4, or 8 with wm = 1)
+  int cw;             // kind 3: column waves (4 or 8)
   int xg;             // kind 3, one K split: XCD-grouped tile order in bands of xg
                       // row groups (0: row-major order of the output tiles)
   int64_t counter_bytes, xhat_bytes, partial_bytes, total_bytes;
@@ -119,8 +115,8 @@ GemmPlan cached_plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned);
 // Whether gemm_tiled_kernel<mt, nt, wm> / gemm_lds32_kernel<mt, nt, st> is
 // built into the library.
 bool tiled_config_built(int mt, int nt, int wm);
-bool lds32_config_built(int mt, int nt, int st, int wm, int cw);
-bool gemv_ring_config_built(int w, int mt, int nt, int d, bool packed_a);
+bool lds32_config_built(int mt, int nt, int st, int cw);
+bool gemv_ring_config_built(int w, int mt, int nt, int d);
 
 // Kernel name and parameters of a plan (diagnostics).
 std::string describe_plan(const GemmPlan& p);
@@ -186,7 +182,7 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
 // The two halves of launch_linear_nvfp4 for plans with a quantizer pass
 // (has_quant_pass): the quantizer writes the activation operand into the
 // workspace, the GEMM reads it. Both together equal one launch_linear_nvfp4.
-bool has_quant_pass(const GemmPlan& p, int hb, bool aligned, int64_t K, const LinearExtras* ex);
+bool has_quant_pass(const GemmPlan& p);
 hipError_t launch_linear_quant(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K,
                                int64_t ldx, float g, int hb, bool aligned, uint8_t* workspace,
                                hipStream_t st, const LinearExtras* ex = nullptr);

@@ -53,31 +53,26 @@ namespace fql {
 // ---------------------------------------------------------------------------
 //
 // A linear call with M <= 32 is a stream over the weight. W waves of a
-// workgroup share NT 16-column tiles and split the K chunks (by default
-// interleaved: wave w takes chunks w, w + W, ..., so a workgroup's waves read
-// neighbouring chunks at any time); each wave
-// streams its own chunks (activation, weight codes, scale dwords) into a
-// private D-stage LDS ring with direct global->LDS loads and waits only for
-// its own loads (explicit vmcnt, no workgroup barrier in the loop), so D
-// chunks per wave stay in flight. Lanes of x_hat rows >= M skip their loads
-// (an output row depends only on its own A row and rows >= M are never
+// workgroup share NT 16-column tiles and split the K chunks, interleaved (wave
+// w takes chunks w, w + W, ..., so a workgroup's waves read neighbouring
+// chunks at any time); each wave streams its own chunks (activation, weight
+// codes, scale dwords) into a private D-stage LDS ring with direct
+// global->LDS loads and waits only for its own loads (explicit vmcnt, no
+// workgroup barrier in the loop), so D chunks per wave stay in flight. The
+// activation arrives packed like a weight (the quantizer pass writes the MT
+// row tiles' codes, then their scales) and each A fragment is dequantized
+// exactly like a B fragment: 1.25 KiB per row tile and chunk through the
+// ring, the same fp16 operand values as x_hat. Lanes of rows >= M skip their
+// loads (an output row depends only on its own A row and rows >= M are never
 // stored); a row tile with no row below M loads whole, so every load
-// instruction issues and the vmcnt counts hold. Weight fragments are dequantized to fp16
-// exactly as in the other kinds; the W partial sums are added in wave order
-// through LDS at the end (deterministic, no atomics).
-template <int MT, int NT, int PA>
-struct GemvStage {
-  uint4v a[MT][4][64];  // x_hat fragments of the chunk's four 32-deep steps
-  uint4v b[NT][64];     // weight codes (one 16-byte slot per lane and tile)
-  uint32_t s[NT][64];   // the lane's scale dword of this chunk, per tile
-};
-// PA = 1: the activation in the packed weight layout (codes and scale dwords per row tile)
+// instruction issues and the vmcnt counts hold. The W partial sums are added
+// in wave order through LDS at the end (deterministic, no atomics).
 template <int MT, int NT>
-struct GemvStage<MT, NT, 1> {
-  uint4v ac[MT][64];
-  uint32_t as[MT][64];
-  uint4v b[NT][64];
-  uint32_t s[NT][64];
+struct GemvStage {
+  uint4v ac[MT][64];   // activation codes of the chunk, per row tile
+  uint32_t as[MT][64];  // the lane's activation scale dword, per row tile
+  uint4v b[NT][64];     // weight codes (one 16-byte slot per lane and tile)
+  uint32_t s[NT][64];   // the lane's weight scale dword of this chunk, per tile
 };
 
 template <int L, int K>
@@ -92,93 +87,43 @@ struct GemvWait<L, 0> {
   static __device__ __forceinline__ void run(int) { wait_vmcnt<0>(); }
 };
 
-// FQ = 1 fuses the activation quantizer: the ring carries bf16 x rows (16-byte
-// columns XOR-swizzled by row, so a fragment read hits 16 distinct bank groups)
-// instead of x_hat, and each lane quantizes its own A fragment (8 elements;
-// the partner lane l^16 holds the other half of the 16-block, so one shuffle
-// gives the block maximum). Needs 16-byte aligned rows, K % 128 == 0 and no
-// rotation; rows >= M are read from row M-1 (in bounds) and zeroed.
-// PA = 1 reads the activation packed like a weight (xhat then points at that
-// operand: codes of the 16·MT rows, then their scales) and dequantizes each A
-// fragment exactly like a B fragment: 1.25 KiB per row tile and chunk through
-// the ring instead of 4 KiB of x_hat, the same fp16 operand values.
-template <int W, int MT, int NT, int D, int FQ, int PA>
+// xa: the packed activation (codes of the 16·MT rows, then their scales).
+template <int W, int MT, int NT, int D>
 __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
-    const _Float16* __restrict__ xhat, const uint16_t* __restrict__ x, int64_t ldx, float g,
-    const uint8_t* __restrict__ wcodes,
+    const uint8_t* __restrict__ xa, const uint8_t* __restrict__ wcodes,
     const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, float alpha,
-    const float* __restrict__ alpha_dev,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int64_t ldy, int interleave) {
+    const float* __restrict__ alpha_dev, const uint16_t* __restrict__ bias,
+    uint16_t* __restrict__ y, int64_t ldy) {
   if (alpha_dev != nullptr) alpha = *alpha_dev;  // per-call scale computed on the device
-  static_assert(!(FQ && PA), "one activation form");
-  typedef GemvStage<MT, NT, PA> Stage;
-  constexpr int L = MT * (PA ? 2 : 4) + NT * 2;  // loads per chunk
+  typedef GemvStage<MT, NT> Stage;
+  constexpr int L = MT * 2 + NT * 2;  // loads per chunk
   static_assert(L * (D - 1) <= 63, "vmcnt range");
   __shared__ Stage ring[W][D];
   static_assert(sizeof(ring) >= sizeof(float4v) * W * MT * NT * 64, "reduction buffer aliases the ring");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t KC = Kp / 128, KC4 = (KC + 3) / 4, KS = Kp / 32;
+  const int64_t KC = Kp / 128, KC4 = (KC + 3) / 4;
   const int64_t tile0 = (int64_t)blockIdx.x * NT;
-  // chunk idx of this wave is c0 + idx * cs: a contiguous K range per wave, or
-  // (interleave) chunks wave, wave + W, ... so the waves read neighbouring chunks
-  const int64_t cpw = (KC + W - 1) / W;
-  int64_t c0, cs;
-  int n;
-  if (interleave) {
-    c0 = wave;
-    cs = W;
-    n = wave < KC ? (int)((KC - wave + W - 1) / W) : 0;
-  } else {
-    c0 = (int64_t)wave * cpw < KC ? (int64_t)wave * cpw : KC;
-    cs = 1;
-    n = (int)((c0 + cpw < KC ? c0 + cpw : KC) - c0);
-  }
+  // chunk idx of this wave is wave + idx * W
+  const int64_t c0 = wave, cs = W;
+  const int n = wave < KC ? (int)((KC - wave + W - 1) / W) : 0;
   int64_t bt[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) bt[nt] = tile0 + nt < ntiles ? tile0 + nt : ntiles - 1;  // never stored
-  const uint8_t* xh = reinterpret_cast<const uint8_t*>(xhat);
-  const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
   // this lane's scale dword within a tile's 512-byte group of four chunks
   const uint32_t s_voff_lane = (uint32_t)(((lane & 15) * 2 + (lane >> 5)) * 16);
-  // fused: load j of row tile mt brings rows 16mt + 4j + lane/16, 16-byte
-  // column (lane%16) ^ (row%16) of the chunk
-  uint32_t x_voff[FQ ? MT : 1][4];
-  if (FQ) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 16 * mt + 4 * j + (lane >> 4);
-        const int rc = row < M ? row : M - 1;
-        x_voff[mt][j] = (uint32_t)((int64_t)rc * ldx * 2 + (((lane & 15) ^ (row & 15)) * 16));
-      }
-  }
 
   auto issue = [&](Stage& sg, int64_t c) {
     const uint32_t base = lds_offset(&sg);
-    if constexpr (PA) {
-      // rows >= M are never stored: skip their bytes (the instructions still issue)
+    // rows >= M are never stored: skip their bytes (the instructions still issue)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint8_t* ac = uniform_ptr(xh + (mt * KC + c) * 1024);
-        const uint8_t* as = uniform_ptr(xh + 8 * MT * Kp + (mt * KC4 + c / 4) * 512);
-        if (16 * mt + (lane & 15) < M || 16 * mt >= M) {
-          lds_load16(ac, lane * 16, base + (uint32_t)offsetof(Stage, ac) + mt * 1024);
-          lds_load4(as, s_voff_lane + (uint32_t)(c & 3) * 4, base + (uint32_t)offsetof(Stage, as) + mt * 256);
-        }
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint8_t* ac = uniform_ptr(xa + (mt * KC + c) * 1024);
+      const uint8_t* as = uniform_ptr(xa + 8 * MT * Kp + (mt * KC4 + c / 4) * 512);
+      if (16 * mt + (lane & 15) < M || 16 * mt >= M) {
+        lds_load16(ac, lane * 16, base + (uint32_t)offsetof(Stage, ac) + mt * 1024);
+        lds_load4(as, s_voff_lane + (uint32_t)(c & 3) * 4, base + (uint32_t)offsetof(Stage, as) + mt * 256);
       }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          if (FQ)
-            lds_load16(xb + c * 256, x_voff[mt][ks], base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
-          else if (16 * mt + (lane & 15) < M || 16 * mt >= M)  // rows >= M are never stored: skip their bytes
-            lds_load16(xh + ((mt * KS + 4 * c + ks) * 64) * 16, lane * 16,
-                       base + (uint32_t)offsetof(Stage, a) + (mt * 4 + ks) * 1024);
-        }
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -195,45 +140,6 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  // fused quantizer: this lane's A fragment (row 16mt + lane%16, k = 32ks +
-  // 8(lane/16) + 0..7) as exactly dequantized NVFP4 in fp16, with the same
-  // operations and rounding as the standalone quantizer
-  auto quant_fragment = [&](const Stage& sg, int mt, int ks) -> half8 {
-#pragma clang fp contract(off)
-    if constexpr (PA) {
-      return half8{};
-    } else {
-    const int r = lane & 15;
-    const int c16 = 4 * ks + (lane >> 4);
-    const uint4v raw = *reinterpret_cast<const uint4v*>(
-        reinterpret_cast<const uint8_t*>(&sg.a[0][0][0]) + (mt * 16 + r) * 256 + ((c16 ^ r) * 16));
-    const bool live = 16 * mt + r < M;
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-    float v[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[2 * j] = live ? __uint_as_float(w[j] << 16) : 0.0f;
-      v[2 * j + 1] = live ? __uint_as_float(w[j] & 0xFFFF0000u) : 0.0f;
-    }
-    float a8 = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a8 = __builtin_fmaxf(a8, __builtin_fabsf(v[e]));
-    const float a16 = __builtin_fmaxf(a8, __shfl_xor(a8, 16));
-    const float sf = (a16 / 6.0f) * g;
-    const uint32_t sc = e4m3_encode_nonneg(sf);
-    const float sd = e4m3_decode_nonneg(sc);
-    const float rr = sd == 0.0f ? 0.0f : g / sd;
-    uint32_t q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0] * rr, v[1] * rr, 1.0f, 0);
-    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, v[2] * rr, v[3] * rr, 1.0f, 1);
-    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, v[4] * rr, v[5] * rr, 1.0f, 2);
-    q = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(q, v[6] * rr, v[7] * rr, 1.0f, 3);
-    const _Float16 sh = (_Float16)sd;
-    uint32_t hw[4];
-    dequant8_f16(q, half2v{sh, sh}, hw);
-    return __builtin_bit_cast(half8, uint4v{hw[0], hw[1], hw[2], hw[3]});
-    }
-  };
-
   auto compute = [&](const Stage& sg) {
     uint4v codes[NT];
     uint32_t sw[NT];
@@ -242,14 +148,12 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
       codes[nt] = sg.b[nt][lane];
       sw[nt] = sg.s[nt][lane];
     }
-    uint4v acodes[PA ? MT : 1];
-    uint32_t asw[PA ? MT : 1];
-    if constexpr (PA) {
+    uint4v acodes[MT];
+    uint32_t asw[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        acodes[mt] = sg.ac[mt][lane];
-        asw[mt] = sg.as[mt][lane];
-      }
+    for (int mt = 0; mt < MT; ++mt) {
+      acodes[mt] = sg.ac[mt][lane];
+      asw[mt] = sg.as[mt][lane];
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -258,10 +162,7 @@ __global__ __launch_bounds__(64 * W) void gemv_ring_kernel(
       for (int nt = 0; nt < NT; ++nt) bf[nt] = b_fragment(dword_of(codes[nt], ks), ChunkScales(sw[nt])[ks]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        half8 a;
-        if constexpr (PA) a = b_fragment(dword_of(acodes[mt], ks), ChunkScales(asw[mt])[ks]);
-        else if constexpr (FQ) a = quant_fragment(sg, mt, ks);
-        else a = __builtin_bit_cast(half8, sg.a[mt][ks][lane]);
+        const half8 a = b_fragment(dword_of(acodes[mt], ks), ChunkScales(asw[mt])[ks]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[nt], acc[mt][nt], 0, 0, 0);
@@ -687,25 +588,20 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(
 //   s/2 of the slot's scale dword (l%16)*2 + s%2 for the chunk.
 // Per chunk and 32-column tile a lane therefore loads two code slots (even
 // and odd steps) and two scale dwords.
-template <int MT, int NT, int WM, int WN>
+template <int MT, int NT, int WN>
 struct LdsStage32 {
-  uint4v a[WM * MT * 2 * 4][64];  // [16-row tile][32-deep step][lane] x_hat fragments
+  uint4v a[MT * 2 * 4][64];       // [16-row tile][32-deep step][lane] x_hat fragments
   uint4v bq[WN * NT * 2][64];     // [column wave][32-col tile][even/odd steps][lane] codes
   uint32_t bs[WN * NT * 2][64];   // [column wave][32-col tile][even/odd steps][lane] scales
 };
 
-// WM = 2 doubles the waves (two per SIMD): the 4 column waves of each of two
-// row halves; a wave owns MT 32-row tiles of its half and NT 32-column tiles,
-// and the two waves of a column slice load one of its two code and scale
-// slots each and dequantize the slice both. A stalled wave (a barrier, a
-// wait) then leaves the matrix pipe to the other wave of its SIMD.
-// WN = 8 (with WM = 1) doubles the column waves instead: two per SIMD again,
-// each owning all MT row tiles and its own NT column tiles, so every weight
-// fragment is dequantized once and feeds MT MFMAs (MT = 4: half the
-// dequantization per MFMA of the WM = 2 layout); each wave then loads half
-// as many activation pieces per chunk (every other 16-row tile).
-template <int MT, int NT, int ST, int OCC, int WM = 1, int WN = 4>
-__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_lds32_kernel(
+// WN = 8 doubles the column waves: two per SIMD, so a stalled wave (a
+// barrier, a wait) leaves the matrix pipe to the other wave of its SIMD; each
+// owns all MT row tiles and its own NT column tiles, so every weight fragment
+// is dequantized once and feeds MT MFMAs, and loads half as many activation
+// pieces per chunk (every other 16-row tile).
+template <int MT, int NT, int ST, int OCC, int WN = 4>
+__global__ __launch_bounds__(64 * WN, OCC) void gemm_lds32_kernel(
     const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
     const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, int ngroups,
     int kc_per_split, int splits, int xg, float alpha,
@@ -714,21 +610,20 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_lds32_kernel(
     uint32_t* __restrict__ counters) {
   if (alpha_dev != nullptr) alpha = *alpha_dev;  // per-call scale computed on the device
   static_assert(ST >= 3 && ST <= 4, "ring depth (chunk i+1 must be issued a whole chunk ahead)");
-  static_assert(WM == 1 || WM == 2, "one or two row halves");
-  static_assert((WN == 4 || WN == 8) && WM * WN <= 8, "4 or 8 column waves, at most 8 waves");
+  static_assert(WN == 4 || WN == 8, "4 or 8 column waves");
   constexpr int TS = WN / 4;             // 16-row tile stride of a wave's activation pieces
   constexpr int NA = 2 * MT / TS;        // activation piece loads per chunk per wave
   static_assert(NA >= 1, "every wave loads activation pieces");
-  constexpr int NLB = 2 * NT / WM;       // code (and scale) slot loads per chunk per wave
+  constexpr int NLB = 2 * NT;            // code (and scale) slot loads per chunk per wave
   constexpr int L = NA + 2 * NLB;        // LDS loads per chunk per wave
   static_assert(L * (ST - 2) <= 63, "vmcnt range");
-  typedef LdsStage32<MT, NT, WM, WN> Stage;
+  typedef LdsStage32<MT, NT, WN> Stage;
   __shared__ Stage stage[ST];
   __shared__ uint32_t s_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN, wn = wave % WN;  // row half, column slice
+  const int wn = wave;  // column slice
   const int64_t KC = Kp / 128;
   const int64_t KC4 = (KC + 3) / 4;
   // one K split: tiles in the XCD-grouped order when xg > 0; else
@@ -743,24 +638,23 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_lds32_kernel(
   const int tile16_0 = (ngroup * WN + wn) * NT * 2;  // first packed 16-column tile of the wave
 
   // wave-uniform global bases; per-lane byte offsets. A wave loads the
-  // 32-deep step wn % 4 of every TS-th 16-row tile of its row half, from tile
-  // wn / 4 on.
+  // 32-deep step wn % 4 of every TS-th 16-row tile, from tile wn / 4 on.
   const int64_t a_tile_stride = (Kp / 32) * 1024;  // bytes between 16-row x_hat tiles
   const uint8_t* a_base = reinterpret_cast<const uint8_t*>(xhat) +
-                          (((int64_t)mgroup * WM + wm) * MT * 2 * (Kp / 32) + wn % 4) * 1024 +
+                          ((int64_t)mgroup * MT * 2 * (Kp / 32) + wn % 4) * 1024 +
                           (wn / 4) * a_tile_stride;
   const uint32_t a_voff = lane * 16;
   const int jc = lane & 31, hh = lane >> 5;  // column in the 32-column tile, k half
   // Per-lane offsets of the code and scale slots this wave loads: slot (b, e)
-  // of 32-column tile b holds the even (e = 0) or odd (e = 1) steps; with
-  // WM = 2 the wave of row half wm loads e = wm. A 16-column tile past the
-  // end is clamped to the last one (read, never stored); the host keeps the
-  // packed blob below 4 GiB so that these 32-bit offsets cannot wrap.
+  // of 32-column tile b holds the even (e = 0) or odd (e = 1) steps. A
+  // 16-column tile past the end is clamped to the last one (read, never
+  // stored); the host keeps the packed blob below 4 GiB so that these 32-bit
+  // offsets cannot wrap.
   uint32_t q_voff[NLB], s_voff[NLB];
 #pragma unroll
   for (int i = 0; i < NLB; ++i) {
-    const int b = WM == 1 ? i / 2 : i;
-    const int e = WM == 1 ? i % 2 : wm;
+    const int b = i / 2;
+    const int e = i % 2;
     int64_t tl = tile16_0 + 2 * b + (jc >> 4);
     tl = tl < ntiles ? tl : ntiles - 1;
     q_voff[i] = (uint32_t)(tl * KC * 1024 + ((2 * e + hh) * 16 + (jc & 15)) * 16);
@@ -775,17 +669,16 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_lds32_kernel(
     const uint8_t* s;  // the chunk's scale dword column
     uint32_t la, lq, ls;  // this wave's LDS destinations in the stage
   };
-  // the wave's slot i sits at slot index (wn*NT + b)*2 + e of the stage
-  constexpr int SLOT_STEP = WM == 1 ? 1 : 2;
+  // the wave's slot i sits at slot index (wn*NT + b)*2 + e = wn*NT*2 + i of the stage
   auto refill_of = [&](Stage& sg, int64_t c) -> Refill {
     c = c < c_end ? c : c_end - 1;
     Refill r;
     r.a = uniform_ptr(a_base + c * 4096);
     r.q = uniform_ptr(wcodes + c * 1024);
     r.s = uniform_ptr(wscales + (c >> 2) * 512 + (c & 3) * 4);
-    r.la = __builtin_amdgcn_readfirstlane(lds_offset(&sg.a[(wm * MT * 2 + wn / 4) * 4 + wn % 4][0]));
-    r.lq = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bq[wn * NT * 2 + (WM == 1 ? 0 : wm)][0]));
-    r.ls = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bs[wn * NT * 2 + (WM == 1 ? 0 : wm)][0]));
+    r.la = __builtin_amdgcn_readfirstlane(lds_offset(&sg.a[(wn / 4) * 4 + wn % 4][0]));
+    r.lq = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bq[wn * NT * 2][0]));
+    r.ls = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bs[wn * NT * 2][0]));
     return r;
   };
   // LDS load number e (0 <= e < L) of a chunk
@@ -794,10 +687,10 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_lds32_kernel(
       lds_load16(r.a + e * TS * a_tile_stride, a_voff, r.la + e * TS * 4 * 1024);
     } else if (e < NA + NLB) {
       const int i = e - NA;
-      lds_load16(r.q, q_voff[i], r.lq + i * SLOT_STEP * 1024);
+      lds_load16(r.q, q_voff[i], r.lq + i * 1024);
     } else {
       const int i = e - NA - NLB;
-      lds_load4(r.s, s_voff[i], r.ls + i * SLOT_STEP * 256);
+      lds_load4(r.s, s_voff[i], r.ls + i * 256);
     }
   };
   auto issue = [&](Stage& sg, int64_t c) {
@@ -825,9 +718,9 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_lds32_kernel(
   half8 bf[2][NT];
   uint4v af[2][MT];
   auto a_frag = [&](const Stage& sg, int a, int s) -> uint4v {
-    return (&sg.a[0][0])[a_lane + ((2 * (wm * MT + a)) * 4 + (s >> 1)) * 64 + 2 * (s & 1) * 16];
+    return (&sg.a[0][0])[a_lane + ((2 * a) * 4 + (s >> 1)) * 64 + 2 * (s & 1) * 16];
   };
-  // the column slice's codes and scales (with WM = 1 the wave's own loads)
+  // the column slice's codes and scales (the wave's own loads)
   auto read_head_b = [&](const Stage& sg) {
 #pragma unroll
     for (int b = 0; b < NT; ++b)
@@ -904,9 +797,8 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_lds32_kernel(
         steps0to6(stage[j], stage[(j + ST - 1) % ST], c_begin + i0 + j + ST - 1);
         const bool more = i0 + j + 1 < nch;
         wait_vmcnt<L * (ST - 2)>();  // this wave's loads of chunk i+1 have landed
-        if (WM == 1 && more) read_head_b(stage[(j + 1) % ST]);  // its own loads
+        if (more) read_head_b(stage[(j + 1) % ST]);  // its own loads
         stage_barrier();             // everyone's have, and stage j has been read by all
-        if (WM == 2 && more) read_head_b(stage[(j + 1) % ST]);
         if (more) read_head_a(stage[(j + 1) % ST]);
         __builtin_amdgcn_sched_barrier(0);
         if (more) dequant(0, 0);
@@ -922,9 +814,9 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_lds32_kernel(
   }
   wait_vmcnt<0>();  // no LDS load may still be in flight when the workgroup ends
 
-  float4v* slab = partial + (int64_t)tilegrp * splits * (WN * WM * MT * NT * 4 * 64);
-  finish_tile32<MT, NT, WM * WN>(acc, M, N, (mgroup * WM + wm) * MT * 32, ngroup * WN * NT * 32, wn,
-                                 split, splits, alpha, bias, y, ldy, slab, counters + tilegrp, &s_flag);
+  float4v* slab = partial + (int64_t)tilegrp * splits * (WN * MT * NT * 4 * 64);
+  finish_tile32<MT, NT, WN>(acc, M, N, mgroup * MT * 32, ngroup * WN * NT * 32, wn, split, splits,
+                            alpha, bias, y, ldy, slab, counters + tilegrp, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -938,8 +830,7 @@ static constexpr int kCUs = 256;
 // the launch-plan heuristics (results change at most in the order of the
 // float32 sum over K).
 struct GemmOverride {
-  int kind = -1, waves = 0, ntw = 0, rc = 0, mt = 0, nt = 0, wm = 0, st = 0, splits = 0, fq = -1, pa = -1,
-      il = -1, xg = -1, cw = 0;
+  int kind = -1, waves = 0, ntw = 0, rc = 0, mt = 0, nt = 0, wm = 0, st = 0, splits = 0, xg = -1, cw = 0;
 };
 static GemmOverride gemm_override() {
   GemmOverride o;
@@ -963,9 +854,6 @@ static GemmOverride gemm_override() {
       else if (k == "wm" && (v == 1 || v == 2 || v == 4)) o.wm = v;
       else if (k == "st" && v >= 2 && v <= 8) o.st = v;
       else if (k == "splits" && v >= 1 && v <= 64) o.splits = v;
-      else if (k == "fq" && (v == 0 || v == 1)) o.fq = v;
-      else if (k == "pa" && (v == 0 || v == 1)) o.pa = v;
-      else if (k == "il" && (v == 0 || v == 1)) o.il = v;
       else if (k == "xg" && v >= 0 && v <= 64) o.xg = v;
       else if (k == "cw" && (v == 4 || v == 8)) o.cw = v;
     }
@@ -1035,17 +923,9 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
       if (ov.waves) p.waves = ov.waves;
       if (ov.nt) p.nt = ov.nt;
       if (ov.st) p.st = ov.st;
-      // The fused quantizer repeats the activation's quantization in every
-      // workgroup; measured slower than the separate x_hat pass on the decode
-      // shapes (e.g. qkv M = 32: 15.9 vs 12.5 us), so it is opt-in.
-      const int fq = aligned && K % 128 == 0 && ov.fq == 1 ? 1 : 0;
       // the quantizer pass (or the transform's) writes the activation packed like a weight
-      const int pa = fq ? 0 : ov.pa >= 0 ? ov.pa : 1;
-      if (p.mt <= 2 && gemv_ring_config_built(p.waves, p.mt, p.nt, p.st, pa != 0)) {
+      if (p.mt <= 2 && gemv_ring_config_built(p.waves, p.mt, p.nt, p.st)) {
         p.wm = 1;
-        p.fq = fq;
-        p.pa = pa;
-        p.ilv = ov.il >= 0 ? ov.il : 1;  // measured 0.2-0.9 us faster on the decode shapes
         p.Mp = 16 * p.mt;
         p.groups = (ntiles + p.nt - 1) / p.nt;
         p.ngroups = p.groups;
@@ -1063,9 +943,9 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     // tiled kernel's 64-bit addresses take weights of 4 GiB and more
     if (p.kind == 3 && d.total_bytes() >= ((int64_t)1 << 32)) p.kind = 1;
     const bool lds_ring = p.kind == 3;
-    p.wm = 1;
+    p.wm = 1;  // kind 1's wave grid; kind 3 has one row of 4 or 8 column waves
     p.cw = 4;
-    p.st = 3;  // (the tables below may change wm for kind 3)
+    p.st = 3;
     if (!lds_ring) {
       if (M <= 16) { p.mt = 1; p.nt = 1; }
       else if (M <= 32) { p.mt = 2; p.nt = 1; }
@@ -1095,16 +975,15 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     if (ov.mt || ov.nt || ov.wm || ov.st || ov.cw) {
       if (ov.mt) p.mt = ov.mt;
       if (ov.nt) p.nt = ov.nt;
-      if (ov.wm && (!lds_ring || ov.wm <= 2)) p.wm = ov.wm;
+      if (ov.wm && !lds_ring) p.wm = ov.wm;
       if (ov.st) p.st = ov.st;
-      if (lds_ring && ov.wm == 2) p.cw = 4;  // at most 8 waves
       if (lds_ring && ov.cw) p.cw = ov.cw;
     }
-    const bool built = p.kind == 3 ? lds32_config_built(p.mt, p.nt, p.st, p.wm, p.cw)
+    const bool built = p.kind == 3 ? lds32_config_built(p.mt, p.nt, p.st, p.cw)
                                    : tiled_config_built(p.mt, p.nt, p.wm);
     if (!built) { p.kind = 1; p.mt = 1; p.nt = 1; p.wm = 1; p.cw = 4; }
     // rows and 16-column tiles per workgroup
-    const int tile_rows = p.kind == 3 ? 32 * p.mt * p.wm : 16 * p.mt * p.wm;
+    const int tile_rows = p.kind == 3 ? 32 * p.mt : 16 * p.mt * p.wm;
     const int tile_cols16 = p.kind == 3 ? 2 * p.cw * p.nt : (4 / p.wm) * p.nt;
     p.Mp = round_up(M, tile_rows);
     const int64_t ngroups = (ntiles + tile_cols16 - 1) / tile_cols16;
@@ -1135,7 +1014,7 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
   }
   // [splits][waves][fragments][64 lanes] float4 per output tile
   const int64_t frags = (int64_t)p.mt * p.nt * (p.kind == 3 ? 4 : 1);
-  const int64_t slab = (int64_t)p.splits * (p.kind == 3 ? p.cw * p.wm : 4) * frags * 64 * 16;
+  const int64_t slab = (int64_t)p.splits * (p.kind == 3 ? p.cw : 4) * frags * 64 * 16;
   p.partial_bytes = p.splits > 1 ? round_up(p.groups * slab, 256) : 0;
   p.counter_bytes = kCounterBytes;
   p.total_bytes = p.counter_bytes + p.xhat_bytes + p.partial_bytes;
@@ -1145,14 +1024,12 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
 std::string describe_plan(const GemmPlan& p) {
   char b[256];
   if (p.kind == 4) {
-    std::snprintf(b, sizeof(b), "%sgemv_ring_kernel<W=%d,MT=%d,NT=%d,D=%d,FQ=%d,PA=%d> grid=%lld splits=1%s",
-                  p.fq ? "" : p.pa ? "quant_nvfp4_apack_kernel + " : "quant_nvfp4_xhat_kernel + ", p.waves,
-                  p.mt, p.nt, p.st, p.fq, p.pa, (long long)p.groups, p.ilv ? " chunks=interleaved" : "");
-  } else if (p.kind == 3 && (p.wm > 1 || p.cw != 4)) {
+    std::snprintf(b, sizeof(b), "quant_nvfp4_apack_kernel + gemv_ring_kernel<W=%d,MT=%d,NT=%d,D=%d> grid=%lld splits=1",
+                  p.waves, p.mt, p.nt, p.st, (long long)p.groups);
+  } else if (p.kind == 3 && p.cw != 4) {
     std::snprintf(b, sizeof(b),
-                  "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d,%s=%d> grid=%lld splits=%d%s",
-                  p.mt, p.nt, p.st, p.wm > 1 ? "WM" : "WN", p.wm > 1 ? p.wm : p.cw,
-                  (long long)(p.groups * p.splits), p.splits,
+                  "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d,WN=%d> grid=%lld splits=%d%s",
+                  p.mt, p.nt, p.st, p.cw, (long long)(p.groups * p.splits), p.splits,
                   p.xg > 0 ? (" xcd_bands=" + std::to_string(p.xg)).c_str() : "");
   } else if (p.kind == 3) {
     std::snprintf(b, sizeof(b),
@@ -1248,7 +1125,7 @@ static hipError_t launch_tiled_t(const GemmPlan& p, const _Float16* xhat, const 
 // for weights of 4 GiB or more, whose offsets exceed the 32-bit ring kernel's)
 #define FQL_TILED_CONFIGS(X) X(1, 1, 1) X(2, 1, 1) X(2, 2, 2) X(4, 2, 2) X(8, 4, 1)
 
-template <int MT, int NT, int ST, int OCC, int WM, int WN>
+template <int MT, int NT, int ST, int OCC, int WN>
 static hipError_t launch_lds32_t(const GemmPlan& p, const _Float16* xhat, const uint8_t* packed,
                                  int64_t M, int64_t N, float alpha, const float* alpha_dev,
                                  const uint16_t* bias,
@@ -1256,20 +1133,20 @@ static hipError_t launch_lds32_t(const GemmPlan& p, const _Float16* xhat, const 
                                  hipStream_t st) {
   const uint8_t* wcodes = packed;
   const uint8_t* wscales = packed + p.Np * p.Kp / 2;
-  gemm_lds32_kernel<MT, NT, ST, OCC, WM, WN><<<(unsigned)(p.groups * p.splits), 64 * WM * WN, 0, st>>>(
+  gemm_lds32_kernel<MT, NT, ST, OCC, WN><<<(unsigned)(p.groups * p.splits), 64 * WN, 0, st>>>(
       xhat, wcodes, wscales, (int)M, (int)N, p.Kp, (int)(p.Np / 16), (int)p.ngroups,
       p.kc_per_split, p.splits, p.xg, alpha, alpha_dev, bias, y, ldy, partial, counters);
   return hipGetLastError();
 }
 
-// The (MT, NT, ST, OCC, WM, WN) 32x32 LDS-ring configurations built into the library.
-#define FQL_LDS32_CONFIGS(X) \
-  X(4, 2, 3, 1, 1, 4) X(4, 1, 3, 1, 1, 4) X(2, 2, 4, 1, 1, 4) X(2, 2, 3, 2, 1, 4) \
-  X(2, 1, 4, 2, 1, 4) X(2, 1, 3, 2, 1, 4) X(1, 2, 4, 2, 1, 4) X(1, 2, 3, 2, 1, 4) \
-  X(2, 2, 3, 1, 2, 4) X(4, 1, 3, 1, 1, 8) X(2, 1, 4, 1, 1, 8)
+// The (MT, NT, ST, OCC, WN) 32x32 LDS-ring configurations built into the
+// library, the planner's choices: 128 x 128 tiles (4 waves), 64 x 128 tiles
+// with a 4-deep ring (split K at M <= 128), 128 x 256 and 64 x 256 tiles on 8
+// column waves.
+#define FQL_LDS32_CONFIGS(X) X(4, 1, 3, 1, 4) X(2, 1, 4, 2, 4) X(4, 1, 3, 1, 8) X(2, 1, 4, 1, 8)
 
-bool lds32_config_built(int mt, int nt, int st, int wm, int cw) {
-#define FQL_X(A, B, C, D, E, F) if (mt == A && nt == B && st == C && wm == E && cw == F) return true;
+bool lds32_config_built(int mt, int nt, int st, int cw) {
+#define FQL_X(A, B, C, D, F) if (mt == A && nt == B && st == C && cw == F) return true;
   FQL_LDS32_CONFIGS(FQL_X)
 #undef FQL_X
   return false;
@@ -1278,18 +1155,11 @@ bool lds32_config_built(int mt, int nt, int st, int wm, int cw) {
 // The (W, MT, NT, D) per-wave-ring configurations built into the library
 // (the planner's choices: 4 waves with 2 tiles, wide short-K layers 4 tiles,
 // long K 8 waves with one tile, each for one or two row tiles).
-#define FQL_GEMV_RING_CONFIGS(X) X(4, 1, 2, 3) X(4, 1, 4, 3) X(8, 1, 1, 3) X(4, 2, 2, 3)
+#define FQL_GEMV_RING_CONFIGS(X) X(4, 1, 2, 3) X(4, 1, 4, 3) X(8, 1, 1, 3) X(4, 2, 2, 3) X(8, 2, 1, 3)
 
-// Configurations built only with the packed activation, whose stages are
-// small enough for 8 waves of two row tiles.
-#define FQL_GEMV_RING_PA_CONFIGS(X) X(8, 2, 1, 3)
-
-bool gemv_ring_config_built(int w, int mt, int nt, int d, bool packed_a) {
+bool gemv_ring_config_built(int w, int mt, int nt, int d) {
 #define FQL_X(A, B, C, E) if (w == A && mt == B && nt == C && d == E) return true;
   FQL_GEMV_RING_CONFIGS(FQL_X)
-  if (packed_a) {
-    FQL_GEMV_RING_PA_CONFIGS(FQL_X)
-  }
 #undef FQL_X
   return false;
 }
@@ -1308,24 +1178,17 @@ static float4v* ws_partial(const GemmPlan& p, uint8_t* ws) {
   return reinterpret_cast<float4v*>(ws + p.counter_bytes + p.xhat_bytes);
 }
 
-// kind 4 quantizing inside the GEMM (FQ = 1): no quantizer pass
-static bool fused_ring(const GemmPlan& p, int hb, bool aligned, int64_t K, const LinearExtras* ex) {
-  return ex == nullptr && p.kind == 4 && p.fq && hb == 0 && aligned && K % 128 == 0;
-}
-
-bool has_quant_pass(const GemmPlan& p, int hb, bool aligned, int64_t K, const LinearExtras* ex) {
-  return p.kind != 0 && !fused_ring(p, hb, aligned, K, ex);
-}
+bool has_quant_pass(const GemmPlan& p) { return p.kind != 0; }
 
 hipError_t launch_linear_quant(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K,
                                int64_t ldx, float g, int hb, bool aligned, uint8_t* workspace,
                                hipStream_t st, const LinearExtras* ex) {
-  if (!has_quant_pass(p, hb, aligned, K, ex)) return hipErrorInvalidValue;
+  if (!has_quant_pass(p)) return hipErrorInvalidValue;
   const bool transform = ex != nullptr && ex->T != nullptr;
   const float* g_dev = ex != nullptr ? ex->g_dev : nullptr;
   uint8_t* operand = ws_operand(p, workspace);
-  // the packed activation (kind 4 with pa) or x_hat, from the plain quantizer or the transform's
-  const bool packed_a = p.kind == 4 && p.pa;
+  // the packed activation (kind 4) or x_hat, from the plain quantizer or the transform's
+  const bool packed_a = p.kind == 4;
   if (packed_a && p.Mp != 16 * p.mt) return hipErrorInvalidValue;
   if (transform) {
     TransformArgs ta{};
@@ -1341,10 +1204,8 @@ hipError_t launch_linear_quant(const GemmPlan& p, const uint16_t* x, int64_t M, 
                                  reinterpret_cast<_Float16*>(operand), g_dev, st);
 }
 
-// The GEMM of kinds 1, 3 and 4 on the operand in the workspace (or, for the
-// fused kind 4, on x itself).
-static hipError_t launch_gemm_part(const GemmPlan& p, const uint16_t* x, int64_t ldx, float g,
-                                   bool fused, const uint8_t* packed, int64_t M, int64_t N,
+// The GEMM of kinds 1, 3 and 4 on the operand in the workspace.
+static hipError_t launch_gemm_part(const GemmPlan& p, const uint8_t* packed, int64_t M, int64_t N,
                                    float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
                                    uint8_t* workspace, hipStream_t st, const LinearExtras* ex) {
   const float* alpha_dev = ex != nullptr ? ex->alpha_dev : nullptr;
@@ -1353,42 +1214,21 @@ static hipError_t launch_gemm_part(const GemmPlan& p, const uint16_t* x, int64_t
   float4v* partial4 = ws_partial(p, workspace);
   if (p.splits > 1 && p.groups > (p.counter_bytes - kWorkspaceScalarBytes) / 4) return hipErrorInvalidValue;
   if (p.kind == 4) {
-    const bool packed_a = !fused && p.pa;
 #define FQL_X(A, B, C, E)                                                                             \
   if (p.waves == A && p.mt == B && p.nt == C && p.st == E) {                                          \
-    if (fused)                                                                                        \
-      gemv_ring_kernel<A, B, C, E, 1, 0><<<(unsigned)p.groups, 64 * A, 0, st>>>(                      \
-          xhat, x, ldx, g, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16),   \
-          alpha, alpha_dev, bias, y, ldy, p.ilv);                                                      \
-    else if (packed_a)                                                                                \
-      gemv_ring_kernel<A, B, C, E, 0, 1><<<(unsigned)p.groups, 64 * A, 0, st>>>(                      \
-          xhat, x, ldx, g, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16),   \
-          alpha, alpha_dev, bias, y, ldy, p.ilv);                                                      \
-    else                                                                                              \
-      gemv_ring_kernel<A, B, C, E, 0, 0><<<(unsigned)p.groups, 64 * A, 0, st>>>(                      \
-          xhat, x, ldx, g, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16),   \
-          alpha, alpha_dev, bias, y, ldy, p.ilv);                                                      \
+    gemv_ring_kernel<A, B, C, E><<<(unsigned)p.groups, 64 * A, 0, st>>>(                              \
+        ws_operand(p, workspace), packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp,              \
+        (int)(p.Np / 16), alpha, alpha_dev, bias, y, ldy);                                             \
     return hipGetLastError();                                                                          \
   }
     FQL_GEMV_RING_CONFIGS(FQL_X)
 #undef FQL_X
-    if (packed_a) {
-#define FQL_X(A, B, C, E)                                                                             \
-  if (p.waves == A && p.mt == B && p.nt == C && p.st == E) {                                          \
-    gemv_ring_kernel<A, B, C, E, 0, 1><<<(unsigned)p.groups, 64 * A, 0, st>>>(                        \
-        xhat, x, ldx, g, packed, packed + p.Np * p.Kp / 2, (int)M, (int)N, p.Kp, (int)(p.Np / 16),     \
-        alpha, alpha_dev, bias, y, ldy, p.ilv);                                                        \
-    return hipGetLastError();                                                                          \
-  }
-      FQL_GEMV_RING_PA_CONFIGS(FQL_X)
-#undef FQL_X
-    }
     return hipErrorInvalidValue;
   }
   if (p.kind == 3) {
-#define FQL_X(A, B, C, D, E, F)                                                                  \
-  if (p.mt == A && p.nt == B && p.st == C && p.wm == E && p.cw == F)                             \
-    return launch_lds32_t<A, B, C, D, E, F>(p, xhat, packed, M, N, alpha, alpha_dev, bias, y, ldy, partial4, counters, st);
+#define FQL_X(A, B, C, D, F)                                                                     \
+  if (p.mt == A && p.nt == B && p.st == C && p.cw == F)                                          \
+    return launch_lds32_t<A, B, C, D, F>(p, xhat, packed, M, N, alpha, alpha_dev, bias, y, ldy, partial4, counters, st);
     FQL_LDS32_CONFIGS(FQL_X)
 #undef FQL_X
     return hipErrorInvalidValue;
@@ -1405,9 +1245,8 @@ static hipError_t launch_gemm_part(const GemmPlan& p, const uint16_t* x, int64_t
 hipError_t launch_linear_gemm(const GemmPlan& p, const uint8_t* packed, int64_t M, int64_t N,
                               float alpha, const uint16_t* bias, uint16_t* y, int64_t ldy,
                               uint8_t* workspace, hipStream_t st, const LinearExtras* ex) {
-  if (p.kind == 0 || (p.kind == 4 && p.fq)) return hipErrorInvalidValue;  // no separate operand
-  return launch_gemm_part(p, nullptr, 0, 0.0f, false, packed, M, N, alpha, bias, y, ldy, workspace,
-                          st, ex);
+  if (p.kind == 0) return hipErrorInvalidValue;  // no separate operand
+  return launch_gemm_part(p, packed, M, N, alpha, bias, y, ldy, workspace, st, ex);
 }
 
 hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, int64_t K,
@@ -1432,12 +1271,9 @@ hipError_t launch_linear_nvfp4(const GemmPlan& p, const uint16_t* x, int64_t M, 
     }
     return hipGetLastError();
   }
-  const bool fused = fused_ring(p, hb, aligned, K, ex);
-  if (!fused) {
-    const hipError_t e = launch_linear_quant(p, x, M, K, ldx, g, hb, aligned, workspace, st, ex);
-    if (e != hipSuccess) return e;
-  }
-  return launch_gemm_part(p, x, ldx, g, fused, packed, M, N, alpha, bias, y, ldy, workspace, st, ex);
+  const hipError_t e = launch_linear_quant(p, x, M, K, ldx, g, hb, aligned, workspace, st, ex);
+  if (e != hipSuccess) return e;
+  return launch_gemm_part(p, packed, M, N, alpha, bias, y, ldy, workspace, st, ex);
 }
 
 }  // namespace fql

@@ -216,9 +216,9 @@ def test_small_m_plans_pack_the_activation():
 
     for M, N, K in ((8, 4096, 14336), (32, 4096, 14336), (32, 6144, 4096), (8, 28672, 4096)):
         plain = fql.linear_plan(M, N, K)
-        assert plain.startswith("quant_nvfp4_apack_kernel + gemv_ring_kernel<") and ",PA=1>" in plain
+        assert plain.startswith("quant_nvfp4_apack_kernel + gemv_ring_kernel<"), plain
         tr = fql.linear_plan(M, N, K, aligned=False, transform=True)
-        assert tr.startswith("transform_quant_kernel + gemv_ring_kernel<") and ",PA=1>" in tr, tr
+        assert tr.startswith("transform_quant_kernel + gemv_ring_kernel<"), tr
         assert "apack" in fql.linear_plan(M, N, K, aligned=False)  # dynamic scale, no transform
         assert fql.linear_workspace_bytes(M, N, K) >= 64 * 1024 + 16 * ((M + 15) // 16) * K * 2
 
@@ -311,10 +311,12 @@ def test_lds32_layouts_and_tile_order_in_the_plan():
             in fql.linear_plan(8192, 28672, 4096))
     assert "xcd_bands=2" in fql.linear_plan(256, 51200, 5120)
     assert "gemm_lds32_kernel<MT=2,NT=1,ST=4> grid=192 splits=2" in fql.linear_plan(128, 6144, 4096)
-    # a two-row-half override implies four column waves; the band is selectable
-    with fql.plan_override("kind=3,mt=2,nt=2,st=3,wm=2,splits=1,xg=0"):
+    # the band is selectable; a configuration that is not built falls back to kind 1
+    with fql.plan_override("kind=3,mt=4,nt=1,st=3,cw=4,splits=1,xg=0"):
         plan = fql.linear_plan(1100, 2100, 1152)
-        assert "gemm_lds32_kernel<MT=2,NT=2,ST=3,WM=2> grid=81 splits=1" in plan and "xcd" not in plan
+        assert "gemm_lds32_kernel<MT=4,NT=1,ST=3> grid=153 splits=1" in plan and "xcd" not in plan
+    with fql.plan_override("kind=3,mt=2,nt=2,st=3,splits=1"):
+        assert "gemm_tiled_kernel" in fql.linear_plan(1100, 2100, 1152)
     with fql.plan_override("kind=3,mt=4,nt=1,st=3,wm=1,cw=8,splits=1,xg=3"):
         assert "WN=8> grid=81 splits=1 xcd_bands=3" in fql.linear_plan(1100, 2100, 1152)
 

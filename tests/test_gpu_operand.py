@@ -2,11 +2,10 @@
 
 A linear call quantizes x into one of three forms before (or inside) its GEMM:
 * x_hat, the dequantized values e2m1(q) * s as float16 in MFMA A-fragment
-  order, written by a quantizer pass (kinds 1 and 3, and kind 4 with pa=0);
+  order, written by a quantizer pass (kinds 1 and 3);
 * the packed activation, codes and E4M3 scales in the packed weight layout,
-  written by a quantizer pass (kind 4 with pa=1, the small-M default);
-* no stored form: the one-launch small-M kernel (kind 0) quantizes into LDS
-  and kind 4 with fq=1 inside its ring.
+  written by a quantizer pass (kind 4, the small-M ring);
+* no stored form: the one-launch small-M kernel (kind 0) quantizes into LDS.
 The stored forms are read back from the workspace after the diagnostic
 quantizer half of the call (fql_linear_nvfp4_quantize) and decoded on the
 host: x_hat must equal the oracle's dequantized values exactly, and the
@@ -74,14 +73,21 @@ def _check_operand(config, M, K, hb, N, rows=None, xkind=None):
     return plan
 
 
-@pytest.mark.parametrize("pa", [0, 1])
 @pytest.mark.parametrize("M", [1, 17, 32])
 @pytest.mark.parametrize("K,hb", [(4096, 0), (14336, 0), (1040, 16), (3072, 64), (4096, 128)])
-def test_small_m_operand_forms(M, K, hb, pa, plan_override):
-    # the per-wave-ring GEMM's operand, packed (pa=1) or as x_hat (pa=0)
-    plan_override(f"kind=4,waves=4,nt=2,st=3,pa={pa}")
+def test_small_m_packed_operand(M, K, hb, plan_override):
+    # the per-wave-ring GEMM's operand: the activation packed like a weight
+    plan_override("kind=4,waves=4,nt=2,st=3")
     plan = _check_operand("decode", M, K, hb, 4096)
-    assert ("apack" in plan) == bool(pa), plan
+    assert "apack" in plan, plan
+
+
+@pytest.mark.parametrize("M,K,hb", [(1, 4096, 0), (17, 1040, 16), (32, 3072, 64)])
+def test_small_m_xhat_operand(M, K, hb, plan_override):
+    # the same activations as x_hat, the operand of the LDS-ring GEMM
+    plan_override("kind=3,mt=2,nt=1,st=4,cw=4")
+    plan = _check_operand("decode", M, K, hb, 4096)
+    assert "xhat" in plan and "gemm_lds32_kernel" in plan, plan
 
 
 @pytest.mark.parametrize("M,K", [(128, 4096), (128, 14336), (300, 1152), (2048, 4096),
@@ -136,9 +142,7 @@ IDENTITY_KINDS = {
     "kind0": "kind=0",
     "kind1": "kind=1",
     "kind3": "kind=3",
-    "kind4_xhat": "kind=4,waves=4,nt=2,st=3,pa=0",
-    "kind4_packed": "kind=4,waves=4,nt=2,st=3,pa=1",
-    "kind4_fused": "kind=4,waves=4,nt=2,st=3,fq=1",
+    "kind4": "kind=4,waves=4,nt=2,st=3",
 }
 
 
@@ -147,11 +151,9 @@ def _identity_cases():
         for M in (1, 16, 17, 32, 128, 300):
             if kind == "kind0" and M > 16:
                 continue
-            if kind.startswith("kind4") and M > 32:
+            if kind == "kind4" and M > 32:
                 continue
             for K, hb in ((1152, 0), (1040, 16), (1152, 32), (2048, 64), (1152, 128)):
-                if kind == "kind4_fused" and (hb or K % 128):
-                    continue
                 if kind == "kind0" and M * K * 2 > 64 * 1024:
                     continue
                 yield pytest.param(kind, M, K, hb, id=f"{kind}-M{M}-K{K}-hb{hb}")
@@ -163,8 +165,7 @@ def test_identity_weight_exposes_operand_every_kind(kind, M, K, hb, plan_overrid
     plan_override(spec)
     plan = fql.linear_plan(M, K, K)
     want = {"kind0": "linear_gemv_kernel<", "kind1": "gemm_tiled_kernel<",
-            "kind3": "gemm_lds32_kernel<", "kind4_xhat": "PA=0>", "kind4_packed": "PA=1>",
-            "kind4_fused": "FQ=1,PA=0>"}[kind]
+            "kind3": "gemm_lds32_kernel<", "kind4": "gemv_ring_kernel<"}[kind]
     assert want in plan, plan
     xb = synthetic.activations("student_t3", M, K, config="hadamard", seed=M + hb)
     x32 = synthetic.bf16_bits_to_f32(xb)

@@ -329,10 +329,11 @@ def test_linear_dynamic(M, mode):
 
 @pytest.mark.parametrize("b,K", [(16, 1040), (32, 1056), (64, 1088), (128, 1152), (128, 5120)])
 @pytest.mark.parametrize("M", [1, 5, 17, 32])
-def test_linear_transform_packed_equals_xhat(b, K, M, plan_override):
-    # the transform kernel's packed activation and its x_hat hold the same
-    # quantized values, so the small-M ring gives identical bits with either
-    # (K not a multiple of 128: the packed blocks past K are zero)
+def test_linear_transform_packed_ring_and_xhat_gemm(b, K, M, plan_override):
+    # the transform kernel's packed activation (small-M ring) and its x_hat
+    # (LDS-ring GEMM) hold the same quantized values; the kernels sum in
+    # different orders, so both are held to the oracle and to each other within
+    # the output bar (K not a multiple of 128: the packed blocks past K are zero)
     N = 272
     xb = _x(M, K, seed=M + b)
     Tb = _T_bits(b, seed=b)
@@ -340,26 +341,27 @@ def test_linear_transform_packed_equals_xhat(b, K, M, plan_override):
     w = fql.NVFP4Weight.from_float(f32_to_dev(W), 5.0, transform=_T_dev(Tb))
     announce(f"transform packed vs x_hat b={b} K={K} M={M}")
     outs = []
-    for pa in (0, 1):
-        plan_override(f"kind=4,waves=4,nt=2,st=3,pa={pa}")
-        assert f"PA={pa}>" in fql.linear_plan(M, N, K, aligned=False, transform=True)
+    for spec, kernel in (("kind=4,waves=4,nt=2,st=3", "gemv_ring_kernel"),
+                         ("kind=3,mt=2,nt=1,st=4,cw=4", "gemm_lds32_kernel")):
+        plan_override(spec)
+        assert kernel in fql.linear_plan(M, N, K, aligned=False, transform=True)
         outs.append(dev_bf16_to_bits(fql.linear_nvfp4(bf16_bits_to_dev(xb), w)))
-    assert np.array_equal(outs[0], outs[1])
+    assert rel_frob(outs[0], outs[1]) <= REL_FROB_TOL
     v = TR.block_transform(synthetic.bf16_bits_to_f32(xb), F.bf16_bits_to_f64(Tb))
     xc, xs = Q.quant_nvfp4(v, np.float32(5.0))
     gw = np.float32(w.weight_global_scale)
     wc, ws = Q.quant_nvfp4(W, gw)
     ref = Q.linear_nvfp4(xc, xs, wc, ws, alpha_of(np.float32(5.0), gw))
-    assert rel_frob(outs[1], ref) <= REL_FROB_TOL
+    for y in outs:
+        assert rel_frob(y, ref) <= REL_FROB_TOL
 
 
-@pytest.mark.parametrize("pa", [0, 1])
 @pytest.mark.parametrize("mode", ["none", "hadamard32", "transform64"])
-def test_linear_dynamic_small_m_ring(mode, pa, plan_override):
-    # the small-M ring with either activation form: the dynamic scale reaches the
-    # quantizer pass through the device scalar; under a transform the transform
-    # kernel writes the x_hat or the packed activation
-    plan_override(f"kind=4,waves=4,nt=2,st=3,pa={pa}")
+def test_linear_dynamic_small_m_ring(mode, plan_override):
+    # the small-M ring: the dynamic scale reaches the quantizer pass through the
+    # device scalar; under a transform the transform kernel writes the packed
+    # activation
+    plan_override("kind=4,waves=4,nt=2,st=3")
     M, K, N = 24, 2048, 640
     xb = _x(M, K, seed=77)
     x32 = synthetic.bf16_bits_to_f32(xb)
@@ -380,9 +382,9 @@ def test_linear_dynamic_small_m_ring(mode, pa, plan_override):
     w = fql.NVFP4Weight.from_float(f32_to_dev(W), 1.0, hadamard_block=hb,
                                    weight_global_scale=float(gw), transform=T,
                                    dynamic_input_scale=True)
-    announce(f"linear dynamic small-M ring {mode} pa={pa}")
+    announce(f"linear dynamic small-M ring {mode}")
     plan = fql.linear_plan(M, N, K, aligned=False, transform=T is not None)
-    assert f"PA={pa}>" in plan, plan
+    assert "gemv_ring_kernel" in plan, plan
     if T is not None:
         assert plan.startswith("transform_quant_kernel + "), plan
     y = fql.linear_nvfp4(bf16_bits_to_dev(xb), w)
