@@ -151,14 +151,15 @@ def _cases(workload, hb_override=None, only=None):
     return out
 
 
-def _kernel_of(M, N, K, fmt="nvfp4", general=False, dynamic=False):
+def _kernel_of(M, N, K, fmt="nvfp4", general=False, dynamic=False, hb=0):
     """The GEMM kernel of one linear call of this shape (the library's own plan; the
     transform and dynamic-scale paths plan as unaligned calls)."""
     import fp8_quantized_linear_amd as fql
 
     if fmt != "nvfp4":
         return fql.linear_sc_plan(fmt, M, N, K).split(" grid=")[0].split(" + ")[-1]
-    plan = fql.linear_plan(M, N, K, aligned=not (general or dynamic), transform=general)
+    plan = fql.linear_plan(M, N, K, aligned=not (general or dynamic), transform=general,
+                           hadamard_block=hb)
     return plan.split(" grid=")[0].split(" + ")[-1]
 
 
@@ -240,7 +241,8 @@ def gpu_bench(workload, steps, warmup, hb, per_case_reps=11, fmt="nvfp4", dynami
         setups.append(dict(M=M, N=N, K=K, name=_case_name(wl, name, M, hbk), x=x, objs=objs,
                            bias=bias, y=y, ws=ws, flops=2.0 * M * N * K,
                            bytes=_alg_bytes(M, N, K, with_bias, fmt), split=split,
-                           kernel=_kernel_of(M, N, K, fmt, general=general, dynamic=dynamic)))
+                           kernel=_kernel_of(M, N, K, fmt, general=general, dynamic=dynamic,
+                                             hb=0 if general else (hbk or 0))))
     torch.cuda.synchronize()
     n = len(setups)
 

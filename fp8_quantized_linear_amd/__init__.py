@@ -462,11 +462,12 @@ def linear_workspace_bytes(M, N, K):
     return n.value
 
 
-def linear_plan(M, N, K, aligned=True, transform=False):
+def linear_plan(M, N, K, aligned=True, transform=False, hadamard_block=0):
     """One-line description of the kernel/launch plan a linear call of this shape uses
-    (`transform`: the plan of a call with a general transform matrix)."""
+    (`transform`: the plan of a call with a general transform matrix; `hadamard_block`:
+    that of a call with this block Hadamard rotation, 0 for none)."""
     buf = ctypes.create_string_buffer(256)
-    flags = int(bool(aligned)) | (2 if transform else 0)
+    flags = int(bool(aligned)) | (2 if transform else 0) | (4 if hadamard_block else 0)
     _check(lib().fql_linear_nvfp4_describe(int(M), int(N), int(K), flags, buf, 256))
     return buf.value.decode()
 

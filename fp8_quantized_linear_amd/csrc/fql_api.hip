@@ -81,9 +81,10 @@ void set_plan_override(int which, const char* spec) {
 
 uint32_t plan_generation() { return g_override_generation.load(std::memory_order_acquire); }
 
-GemmPlan cached_plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
+GemmPlan cached_plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool rotated) {
   thread_local PlanCache<GemmPlan> cache;
-  return cache.get(M, N, K, aligned ? 1 : 0, [&] { return plan_gemm_nvfp4(M, N, K, aligned); });
+  return cache.get(M, N, K, (aligned ? 1 : 0) | (rotated ? 2 : 0),
+                   [&] { return plan_gemm_nvfp4(M, N, K, aligned, rotated); });
 }
 
 ScPlan cached_plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
@@ -292,9 +293,10 @@ int fql_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* by
   if (M < 1 || N < 1 || K < 16 || K % 16 != 0)
     return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 16");
   // either plan a call of this shape may take: aligned or unaligned rows (the
-  // transform and dynamic-scale calls take the unaligned one)
-  const int64_t a = fql::cached_plan_gemm_nvfp4(M, N, K, true).total_bytes;
-  const int64_t u = fql::cached_plan_gemm_nvfp4(M, N, K, false).total_bytes;
+  // transform and dynamic-scale calls take the unaligned one); the rotation
+  // changes no plan's workspace
+  const int64_t a = fql::cached_plan_gemm_nvfp4(M, N, K, true, false).total_bytes;
+  const int64_t u = fql::cached_plan_gemm_nvfp4(M, N, K, false, false).total_bytes;
   *bytes = (size_t)std::max(a, u);
   return ok();
 }
@@ -305,7 +307,9 @@ int fql_linear_nvfp4_describe(int64_t M, int64_t N, int64_t K, int aligned, char
     return fail(FQL_ERR_INVALID, "need M, N >= 1 and K a positive multiple of 16");
   // a transform call plans as unaligned rows; its quantizer is the transform kernel
   const bool transform = (aligned & 2) != 0;
-  std::string d = fql::describe_plan(fql::plan_gemm_nvfp4(M, N, K, !transform && (aligned & 1) != 0));
+  const bool rotated = (aligned & 4) != 0;
+  std::string d = fql::describe_plan(
+      fql::plan_gemm_nvfp4(M, N, K, !transform && (aligned & 1) != 0, rotated && !transform));
   if (transform) {
     for (const char* q : {"quant_nvfp4_apack_kernel", "quant_nvfp4_xhat_kernel"}) {
       const size_t at = d.find(q);
@@ -354,7 +358,7 @@ int linear_nvfp4_plain(const void* x, int64_t M, int64_t K, int64_t ldx, float g
   if (alpha_dev != nullptr && reinterpret_cast<uintptr_t>(alpha_dev) % 4 != 0)
     return fail(FQL_ERR_INVALID, "alpha_dev must be 4-byte aligned");
   const bool xal = aligned16(x, ldx, 2);
-  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, xal);
+  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, xal, hb > 0);
   if (int r = check_workspace(workspace, workspace_bytes, plan.total_bytes)) return r;
   fql::LinearExtras ex{};
   ex.alpha_dev = alpha_dev;
@@ -395,7 +399,7 @@ int fql_linear_nvfp4_quantize(const void* x, int64_t M, int64_t K, int64_t ldx,
   if (N < 1 || N > (int64_t)1 << 24) return fail(FQL_ERR_INVALID, "N out of range");
   if (!x) return fail(FQL_ERR_INVALID, "null pointer");
   const bool xal = aligned16(x, ldx, 2);
-  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, xal);
+  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, xal, hadamard_block > 0);
   if (!fql::has_quant_pass(plan))
     return fail(FQL_ERR_UNSUPPORTED, "this call's plan quantizes inside the GEMM (%s)",
                 fql::describe_plan(plan).c_str());
@@ -418,7 +422,8 @@ int fql_linear_nvfp4_gemm(int64_t M, int64_t K, int x_aligned, const void* w_pac
   if (!w_packed || !y) return fail(FQL_ERR_INVALID, "null pointer");
   if (reinterpret_cast<uintptr_t>(w_packed) % 16 != 0)
     return fail(FQL_ERR_INVALID, "packed weight must be 16-byte aligned");
-  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, x_aligned != 0);
+  // the rotation never changes a plan with a quantizer pass
+  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, x_aligned != 0, false);
   if (plan.kind == 0)
     return fail(FQL_ERR_UNSUPPORTED, "this call's plan quantizes inside the GEMM (%s)",
                 fql::describe_plan(plan).c_str());
@@ -614,7 +619,7 @@ int linear_nvfp4_extras(const void* x, int64_t M, int64_t K, int64_t ldx, float 
     return fail(FQL_ERR_INVALID, "packed weight must be 16-byte and workspace 256-byte aligned");
   // a plan whose quantizer pass writes the GEMM's operand (x_hat or the packed
   // activation), since the fused small-M kernel quantizes with a host-side scale
-  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, false);
+  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, false, false);
   if (workspace_bytes < (size_t)plan.total_bytes)
     return fail(FQL_ERR_WORKSPACE, "workspace holds %zu bytes, %lld needed", workspace_bytes,
                 (long long)plan.total_bytes);
@@ -968,7 +973,7 @@ int fql_linear_nvfp4_noalloc(const void* x, int64_t M, int64_t K, int64_t ldx,
     return r;
   if (!std::isfinite(alpha)) return fail(FQL_ERR_INVALID, "alpha must be finite");
   const bool xal = aligned16(x, ldx, 2);
-  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, xal);
+  const fql::GemmPlan plan = fql::cached_plan_gemm_nvfp4(M, N, K, xal, hadamard_block > 0);
   if ((size_t)plan.total_bytes > kNoAllocScratchBytes)
     return fail(FQL_ERR_WORKSPACE,
                 "this call needs %lld bytes of scratch, more than the %zu bytes the "

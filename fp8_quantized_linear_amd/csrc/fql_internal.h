@@ -106,11 +106,15 @@ struct GemmPlan {
 };
 // `aligned`: x rows are 16-byte aligned (pointer and row stride); the
 // fused small-M kernel needs it. Workspace sizes of both kinds are covered by
-// the aligned=false plan, which never needs less.
-GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned);
+// the aligned=false plan, which never needs less. `rotated`: the call applies
+// a block Hadamard transform to the activation (hadamard_block > 0); it only
+// changes the column tiles per workgroup of the fused kernel, never the kind
+// or the workspace.
+GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool rotated);
 // The same plan from a small per-thread cache (keyed by the shape, the
-// alignment and the override generation), so a hot call plans once per shape.
-GemmPlan cached_plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned);
+// alignment, the rotation and the override generation), so a hot call plans
+// once per shape.
+GemmPlan cached_plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool rotated);
 
 // Whether gemm_tiled_kernel<mt, nt, wm> / gemm_lds32_kernel<mt, nt, st> is
 // built into the library.

@@ -865,7 +865,7 @@ static constexpr int64_t kCounterBytes = kWorkspaceCounterBytes;
 static constexpr int64_t kGemvMaxLds = 64 * 1024;    // compact activation copy in LDS
 static constexpr int64_t kGemvMaxRedundantBlocks = 1 << 20;  // workgroups x 16-blocks quantized
 
-GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
+GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool rotated) {
   GemmPlan p{};
   const PackedDims d = packed_dims(N, K);
   p.Np = d.Np;
@@ -891,7 +891,13 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned) {
     p.wm = 1;
     p.Mp = M;
     p.waves = ntiles < 1024 ? 8 : 4;
-    p.ntw = M > 1 && ntiles < 1024 ? 2 : 1;
+    // Two column tiles per workgroup halve the workgroups that each quantize
+    // (and, with a rotation, transform) the whole activation. Measured: a win
+    // from M = 2 on, and at M = 1 with a rotation on the narrow layers
+    // (Qwen3-32B down, 320 tiles: ~10%); at M = 1 without one they lose
+    // (Llama-3.1-8B down 11.0 -> 14.7 us), and the wide layers (>= 1024
+    // tiles) keep one.
+    p.ntw = (M > 1 || rotated) && ntiles < 1024 ? 2 : 1;
     if (ov.waves == 4 || ov.waves == 8) p.waves = ov.waves;  // the built kind-0 widths
     if (ov.ntw == 1 || ov.ntw == 2) p.ntw = ov.ntw;
     const int64_t cpw = (KC + p.waves - 1) / p.waves;

@@ -158,7 +158,9 @@ int fql_linear_nvfp4_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* by
  * is a bit set: bit 0 says whether x rows will be 16-byte aligned; bit 1
  * describes the plan of fql_linear_nvfp4_transform instead (the unaligned
  * plan, with the transform kernel as its quantizer; the dynamic-scale call
- * without a transform plans like an unaligned plain call). Host-side only.
+ * without a transform plans like an unaligned plain call); bit 2 says that
+ * the call rotates the activation (hadamard_block > 0), which can change the
+ * column tiles per workgroup of the fused small-M kernel. Host-side only.
  */
 int fql_linear_nvfp4_describe(int64_t M, int64_t N, int64_t K, int aligned, char* buf,
                               size_t buf_len);

@@ -321,6 +321,20 @@ def test_lds32_layouts_and_tile_order_in_the_plan():
         assert "WN=8> grid=81 splits=1 xcd_bands=3" in fql.linear_plan(1100, 2100, 1152)
 
 
+def test_rotation_widens_the_fused_kernels_workgroups_at_m1():
+    # with a Hadamard rotation every workgroup of the fused kernel also rotates
+    # the activation: two column tiles per workgroup on the narrow layers
+    assert "NTW=1" in fql.linear_plan(1, 5120, 25600)
+    assert "linear_gemv_kernel<W=8,NTW=2," in fql.linear_plan(1, 5120, 25600, hadamard_block=64)
+    assert "NTW=1" in fql.linear_plan(1, 51200, 5120, hadamard_block=64)  # >= 1024 column tiles
+    assert "NTW=1" in fql.linear_plan(1, 4096, 14336)
+    # plans with a quantizer pass, and the transform's plan, do not depend on it
+    for M, N, K in [(32, 5120, 25600), (256, 5120, 25600), (4096, 51200, 5120)]:
+        assert fql.linear_plan(M, N, K) == fql.linear_plan(M, N, K, hadamard_block=128)
+    assert (fql.linear_plan(1, 5120, 25600, aligned=False, transform=True)
+            == fql.linear_plan(1, 5120, 25600, aligned=False, transform=True, hadamard_block=64))
+
+
 def test_binding_holds_no_numeric_formula():
     # every scale and alpha of the layer comes from the library; the binding
     # only marshals arguments: no numpy, no float literal but the unit alpha,

@@ -104,6 +104,13 @@ def test_linear_ragged(M, K, N, with_bias):
     _run_case("decode", M, K, N, 0, with_bias, label="ragged")
 
 
+@pytest.mark.parametrize("M,K,N,hb", [(1, 288, 100, 32), (1, 2048, 5000, 128), (1, 1024, 48, 16)])
+def test_linear_rotated_single_row_ragged(M, K, N, hb):
+    # the fused kernel at M = 1 with a rotation takes two column tiles per
+    # workgroup; odd tile counts leave the last workgroup one
+    _run_case("hadamard", M, K, N, hb, True, label="rotated-ragged")
+
+
 def test_linear_strided_3d_input_and_output_stride():
     M, K, N = 24, 1024, 320
     xb = synthetic.activations("normal", M, K, config="decode", seed=4)
