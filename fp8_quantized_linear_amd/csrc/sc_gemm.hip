@@ -70,6 +70,29 @@ struct ScStage {
   uint32_t bs[SB > 0 ? SB : 1][64];
 };
 
+// One scaled MFMA whose E8M0 scales are byte `BA` of `sa` and byte `BB` of
+// `sb` (the instruction's scale byte select; it must be an immediate).
+template <int FMT, int BA, int BB>
+__device__ __forceinline__ float4v mfma_scale_bytes(const int8v& a, const int8v& b, const float4v& c, int sa,
+                                                    int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, FMT, BA, sa, BB, sb);
+}
+// The same with the bytes given as values that are constants once the
+// caller's loops are unrolled (the switch folds to one call).
+template <int FMT>
+__device__ __forceinline__ float4v mfma_scale_sel(const int8v& a, const int8v& b, const float4v& c, int sa, int ba,
+                                                  int sb, int bb) {
+  switch (ba * 4 + bb) {
+#define FQL_SC_SEL(I) \
+  case I: return mfma_scale_bytes<FMT, I / 4, I % 4>(a, b, c, sa, sb);
+    FQL_SC_SEL(0) FQL_SC_SEL(1) FQL_SC_SEL(2) FQL_SC_SEL(3) FQL_SC_SEL(4) FQL_SC_SEL(5) FQL_SC_SEL(6)
+    FQL_SC_SEL(7) FQL_SC_SEL(8) FQL_SC_SEL(9) FQL_SC_SEL(10) FQL_SC_SEL(11) FQL_SC_SEL(12) FQL_SC_SEL(13)
+    FQL_SC_SEL(14)
+#undef FQL_SC_SEL
+    default: return mfma_scale_bytes<FMT, 3, 3>(a, b, c, sa, sb);
+  }
+}
+
 template <int F, int WM, int WN, int MTW, int NTW, int ST>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
     const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
@@ -87,8 +110,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
   constexpr int L = (ITEMS + NW - 1) / NW;  // loads per wave per chunk
   constexpr int P = MTW * NTW;              // MFMAs per wave per chunk
   constexpr int CHUNK = 64 * 16 * H;        // bytes of one tile-chunk
+  // Fragment prefetch (the MFMAs of a chunk read registers filled during the
+  // previous chunk) for MXFP4 and block FP8; per-tensor FP8 and MXFP8 read
+  // their fragments just before the MFMAs, which measured faster for them
+  // (their 3-stage rings lose a chunk of load lead time to the prefetch, and
+  // they have no per-chunk VALU work for it to hide).
+  constexpr bool PF = F == SC_MXFP4 || F == SC_FP8_BLOCK;
   static_assert(ST >= 3 && ST <= 8, "ring depth");
-  static_assert(L * (ST - 2) <= 63, "vmcnt range");
+  static_assert(L * (PF ? ST - 1 : ST - 2) <= 63, "vmcnt range");
   static_assert(TB % 4 == 0, "weight tiles come in quads");
   static_assert(!T::BLOCK || (NTW * 16 <= 128 && 128 % (NTW * 16) == 0), "a wave's columns in one block");
   __shared__ Stage stage[ST];
@@ -190,86 +219,210 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  // one chunk: fragments from stage sg, MFMAs, and the refill loads of the
-  // stage `refill` (chunk rc) spread between the MFMAs
-  auto compute = [&](const Stage& sg, Stage& refill, int64_t rc) {
-    const ChunkOffsets ro = offsets_of(rc);
-    int8v b[NTW];
-    int sb[NTW];
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
+  if constexpr (PF) {
+    // This wave's operand fragments of one chunk, in two register sets: the
+    // MFMAs of chunk i read set i % 2 while the LDS reads of chunk i+1 fill the
+    // other, so no MFMA waits on an LDS read issued just before it. Each
+    // fragment of chunk i+1 is read once the last MFMA of chunk i that reads
+    // the same slot is issued, so only about one set is live at a time.
+    // Fragments are kept as 16-byte halves: an FP4 operand fills only the
+    // first half of the MFMA's 32-byte operand, so no zero half is held across
+    // the loop. The E8M0 scales stay packed as loaded, four tiles' bytes per dword: the
+    // wave's row tiles start at tile a_first of the loaded quads and its column
+    // tiles at b_first (MTW and NTW divide 4 or are multiples of it, so the
+    // first tile's byte offset is the only runtime part: the words are shifted
+    // by it once, and tile mt's byte is mt % 4 of word mt / 4).
+    constexpr int AW = (MTW + 3) / 4, BW = (NTW + 3) / 4;
+    static_assert((MTW % 4 == 0 || 4 % MTW == 0) && (NTW % 4 == 0 || 4 % NTW == 0), "tiles per wave");
+    const int a_first = a_qoff + wm * MTW, b_first = wn * NTW;
+    const int a_shift = 8 * (a_first % 4), b_shift = 8 * (b_first % 4);
+    uint4v fa[2][MTW][H];  // activation tiles
+    int fsa[2][AW];        // their E8M0 scale words (MX)
+    float4v fs4[2][MTW];   // block FP8: row scales x the column block's scale
+    uint4v fb[2][NTW][H];  // weight tiles
+    int fsb[2][BW];        // their E8M0 scale words (MX)
+    float fsw[2];          // block FP8: the wave's column block scale
+    auto operand = [&](const uint4v (&f)[H]) -> int8v {
+      const uint4v q0 = f[0];
+      if (H == 1) return int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, 0, 0, 0, 0};
+      const uint4v q1 = f[H - 1];
+      return int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+    };
+    auto read_sw = [&](const Stage& sg, int q) {
+      fsw[q] = T::BLOCK ? __uint_as_float(sg.bs[(wn * NTW * 16) / 128][0]) : 0.0f;
+    };
+    auto read_b = [&](const Stage& sg, int q, int nt) {
       const int t = wn * NTW + nt;
-      const uint4v q0 = sg.b[t][0][lane];
-      if (H == 1) {
-        b[nt] = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, 0, 0, 0, 0};
-      } else {
-        const uint4v q1 = sg.b[t][H - 1][lane];
-        b[nt] = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
-      }
-      sb[nt] = T::MX ? (int)((sg.bs[t / 4][lane] >> (8 * (t % 4))) & 0xFFu) : 127;
-    }
-    float swv = 0.0f;
-    if (T::BLOCK) swv = __uint_as_float(sg.bs[(wn * NTW * 16) / 128][0]);
-    int p = 0;
 #pragma unroll
-    for (int mt = 0; mt < MTW; ++mt) {
+      for (int h = 0; h < H; ++h) fb[q][nt][h] = sg.b[t][h][lane];
+      if (T::MX && nt % 4 == 0) fsb[q][nt / 4] = (int)(sg.bs[(b_first + nt) / 4][lane] >> b_shift);
+    };
+    auto read_a = [&](const Stage& sg, int q, int mt) {
       const int t = wm * MTW + mt;
-      const uint4v q0 = sg.a[t][0][lane];
-      int8v a;
-      if (H == 1) {
-        a = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, 0, 0, 0, 0};
-      } else {
-        const uint4v q1 = sg.a[t][H - 1][lane];
-        a = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
-      }
+#pragma unroll
+      for (int h = 0; h < H; ++h) fa[q][mt][h] = sg.a[t][h][lane];
       const int at = a_qoff + t;  // tile index within the loaded scale quads
-      int sa = 127;
-      if (T::MX) sa = (int)((sg.as[at / 4][lane] >> (8 * (at % 4))) & 0xFFu);
-      float4v s4 = float4v{0.f, 0.f, 0.f, 0.f};
+      if (T::MX && mt % 4 == 0) fsa[q][mt / 4] = (int)(sg.as[(a_first + mt) / 4][lane] >> a_shift);
       if (T::BLOCK) {
         // row scales of the lane's four accumulator rows 16*at + 4*(lane/16) + i
         const float* rs = reinterpret_cast<const float*>(&sg.as[at / 4][0]) + 16 * (at % 4) + 4 * (lane >> 4);
-        s4 = float4v{rs[0] * swv, rs[1] * swv, rs[2] * swv, rs[3] * swv};
+        fs4[q][mt] = float4v{rs[0] * fsw[q], rs[1] * fsw[q], rs[2] * fsw[q], rs[3] * fsw[q]};
       }
+    };
+    auto mfma = [&](int q, int mt, int nt) {
+      if (T::BLOCK) {
+        const float4v z = float4v{0.f, 0.f, 0.f, 0.f};
+        const float4v part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(fa[q][mt]), operand(fb[q][nt]), z,
+                                                                              0, 0, 0, 127, 0, 127);
+        acc[mt][nt] += part * fs4[q][mt];
+      } else if (T::MX) {
+        acc[mt][nt] = mfma_scale_sel<T::FMT>(operand(fa[q][mt]), operand(fb[q][nt]), acc[mt][nt], fsa[q][mt / 4], mt % 4,
+                                             fsb[q][nt / 4], nt % 4);
+      } else {
+        acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(operand(fa[q][mt]), operand(fb[q][nt]), acc[mt][nt],
+                                                                       T::FMT, T::FMT, 0, 127, 0, 127);
+      }
+    };
+
+    // Ring: chunk i lives in stage i % ST. The first ST chunks are loaded up
+    // front and chunk 0's fragments read. Chunk i then waits for the wave's
+    // own loads of chunk i+1, passes the barrier (every
+    // wave's loads of chunk i+1 have landed, and every wave has read chunk i's
+    // fragments out of stage i % ST) and issues its MFMAs from registers; after
+    // each row tile's MFMAs it reads that row tile of chunk i+1, during the last
+    // row tile's the weight tiles of chunk i+1, and it refills stage i % ST with
+    // chunk i+ST between the MFMAs. Chunk indices past the end are clamped to
+    // the last chunk, so every chunk issues the same loads, reads and barrier
+    // (the last chunk's reads of a "next" chunk are in-bounds and unused).
+#pragma unroll
+    for (int p0 = 0; p0 < ST; ++p0) {
+      const int64_t c = c_begin + p0 < c_end ? c_begin + p0 : c_end - 1;
+      const ChunkOffsets o = offsets_of(c);
+#pragma unroll
+      for (int j = 0; j < L; ++j) issue_item(stage[p0], c, o, j);
+    }
+    wait_vmcnt<L * (ST - 1)>();  // this wave's loads of chunk 0
+    stage_barrier();
+    read_sw(stage[0], 0);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) read_b(stage[0], 0, nt);
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt) read_a(stage[0], 0, mt);
+
+    auto chunk = [&](int i, int s, int q) {
+      wait_vmcnt<L * (ST - 2)>();  // this wave's loads of chunk i+1
+      stage_barrier();
+      const Stage& next = stage[(s + 1) % ST];
+      read_sw(next, q ^ 1);
+      int64_t rc = c_begin + i + ST;
+      rc = rc < c_end ? rc : c_end - 1;
+      const ChunkOffsets ro = offsets_of(rc);
+      int p = 0;
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt) {
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+          for (int j = 0; j < L; ++j)
+            if ((j * P) / L == p) issue_item(stage[s], rc, ro, j);
+          mfma(q, mt, nt);
+          ++p;
+          if (mt == MTW - 1) read_b(next, q ^ 1, nt);  // the tile's last MFMA of this chunk is issued
+        }
+        read_a(next, q ^ 1, mt);
+        // keep the reads behind the MFMAs that free their registers
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // unrolled so that the stage and the fragment set of every chunk are static
+    constexpr int U = ST % 2 == 0 ? ST : 2 * ST;
+    for (int i0 = 0; i0 < nch; i0 += U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i0 + u < nch) chunk(i0 + u, u % ST, u % 2);
+    }
+  } else {
+    // one chunk: fragments from stage sg, MFMAs, and the refill loads of the
+    // stage `refill` (chunk rc) spread between the MFMAs
+    auto compute = [&](const Stage& sg, Stage& refill, int64_t rc) {
+      const ChunkOffsets ro = offsets_of(rc);
+      int8v b[NTW];
+      int sb[NTW];
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
-#pragma unroll
-        for (int j = 0; j < L; ++j)
-          if ((j * P) / L == p) issue_item(refill, rc, ro, j);
-        if (T::BLOCK) {
-          const float4v z = float4v{0.f, 0.f, 0.f, 0.f};
-          const float4v part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[nt], z, 0, 0, 0, 127, 0, 127);
-          acc[mt][nt] += part * s4;
+        const int t = wn * NTW + nt;
+        const uint4v q0 = sg.b[t][0][lane];
+        if (H == 1) {
+          b[nt] = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, 0, 0, 0, 0};
         } else {
-          acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[nt], acc[mt][nt], T::FMT,
-                                                                         T::FMT, 0, sa, 0, sb[nt]);
+          const uint4v q1 = sg.b[t][H - 1][lane];
+          b[nt] = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
         }
-        ++p;
+        sb[nt] = T::MX ? (int)((sg.bs[t / 4][lane] >> (8 * (t % 4))) & 0xFFu) : 127;
       }
-    }
-  };
+      float swv = 0.0f;
+      if (T::BLOCK) swv = __uint_as_float(sg.bs[(wn * NTW * 16) / 128][0]);
+      int p = 0;
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt) {
+        const int t = wm * MTW + mt;
+        const uint4v q0 = sg.a[t][0][lane];
+        int8v a;
+        if (H == 1) {
+          a = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, 0, 0, 0, 0};
+        } else {
+          const uint4v q1 = sg.a[t][H - 1][lane];
+          a = int8v{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w};
+        }
+        const int at = a_qoff + t;  // tile index within the loaded scale quads
+        int sa = 127;
+        if (T::MX) sa = (int)((sg.as[at / 4][lane] >> (8 * (at % 4))) & 0xFFu);
+        float4v s4 = float4v{0.f, 0.f, 0.f, 0.f};
+        if (T::BLOCK) {
+          // row scales of the lane's four accumulator rows 16*at + 4*(lane/16) + i
+          const float* rs = reinterpret_cast<const float*>(&sg.as[at / 4][0]) + 16 * (at % 4) + 4 * (lane >> 4);
+          s4 = float4v{rs[0] * swv, rs[1] * swv, rs[2] * swv, rs[3] * swv};
+        }
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+          for (int j = 0; j < L; ++j)
+            if ((j * P) / L == p) issue_item(refill, rc, ro, j);
+          if (T::BLOCK) {
+            const float4v z = float4v{0.f, 0.f, 0.f, 0.f};
+            const float4v part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[nt], z, 0, 0, 0, 127, 0, 127);
+            acc[mt][nt] += part * s4;
+          } else {
+            acc[mt][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b[nt], acc[mt][nt], T::FMT,
+                                                                           T::FMT, 0, sa, 0, sb[nt]);
+          }
+          ++p;
+        }
+      }
+    };
 
-  // Ring: chunk i lives in stage i % ST. Before computing chunk i a wave
-  // waits for its own loads of chunk i, passes the barrier (everyone's have
-  // landed and everyone has finished chunk i-1), then refills stage
-  // (i-1) % ST with chunk i+ST-1 while computing (clamped chunk index past
-  // the end: a static number of loads per chunk).
+    // Ring: chunk i lives in stage i % ST. Before computing chunk i a wave
+    // waits for its own loads of chunk i, passes the barrier (everyone's have
+    // landed and everyone has finished chunk i-1), then refills stage
+    // (i-1) % ST with chunk i+ST-1 while computing (clamped chunk index past
+    // the end: a static number of loads per chunk).
 #pragma unroll
-  for (int p0 = 0; p0 < ST - 1; ++p0) {
-    const int64_t c = c_begin + p0 < c_end ? c_begin + p0 : c_end - 1;
-    const ChunkOffsets o = offsets_of(c);
+    for (int p0 = 0; p0 < ST - 1; ++p0) {
+      const int64_t c = c_begin + p0 < c_end ? c_begin + p0 : c_end - 1;
+      const ChunkOffsets o = offsets_of(c);
 #pragma unroll
-    for (int j = 0; j < L; ++j) issue_item(stage[p0], c, o, j);
-  }
-  for (int i0 = 0; i0 < nch; i0 += ST) {
+      for (int j = 0; j < L; ++j) issue_item(stage[p0], c, o, j);
+    }
+    for (int i0 = 0; i0 < nch; i0 += ST) {
 #pragma unroll
-    for (int j = 0; j < ST; ++j) {
-      if (i0 + j < nch) {
-        wait_vmcnt<L * (ST - 2)>();
-        stage_barrier();
-        int64_t rc = c_begin + i0 + j + ST - 1;
-        rc = rc < c_end ? rc : c_end - 1;
-        compute(stage[j], stage[(j + ST - 1) % ST], rc);
+      for (int j = 0; j < ST; ++j) {
+        if (i0 + j < nch) {
+          wait_vmcnt<L * (ST - 2)>();
+          stage_barrier();
+          int64_t rc = c_begin + i0 + j + ST - 1;
+          rc = rc < c_end ? rc : c_end - 1;
+          compute(stage[j], stage[(j + ST - 1) % ST], rc);
+        }
       }
     }
   }
