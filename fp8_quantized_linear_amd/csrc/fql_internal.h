@@ -90,10 +90,13 @@ struct GemmPlan {
   int st;             // kinds 3, 4: LDS ring depth (chunks)
   int64_t Mp;         // M padded to a whole number of M tiles
   int64_t Np, Kp;     // packed weight dims
-  int64_t groups;     // output tiles (workgroups per split)
+  int64_t groups;     // output tiles
   int64_t ngroups;    // column groups (kind 1)
-  int splits;         // K splits (1 = epilogue directly in the GEMM)
+  int splits;         // K splits of the split tiles (1 = epilogue directly in the GEMM)
   int kc_per_split;   // 128-deep K chunks per split
+  int64_t dp_groups;  // kind 3: tiles computed whole, one workgroup each (the first
+                      // dp_groups workgroups); the other groups - dp_groups tiles
+                      // take `splits` consecutive workgroups each
   int kcmax;          // kind 0: weight register ring depth in chunks (4 or 8)
   int waves;          // kind 0: waves per workgroup (split of K inside the workgroup)
   int qpre;           // kind 0: activation blocks per thread loaded ahead of the weights

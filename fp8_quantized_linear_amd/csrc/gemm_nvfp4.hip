@@ -604,7 +604,7 @@ template <int MT, int NT, int ST, int OCC, int WN = 4>
 __global__ __launch_bounds__(64 * WN, OCC) void gemm_lds32_kernel(
     const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
     const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, int ngroups,
-    int kc_per_split, int splits, int xg, float alpha,
+    int kc_per_split, int dp, int splits, int xg, float alpha,
     const float* __restrict__ alpha_dev, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ y, int64_t ldy, float4v* __restrict__ partial,
     uint32_t* __restrict__ counters) {
@@ -626,14 +626,24 @@ __global__ __launch_bounds__(64 * WN, OCC) void gemm_lds32_kernel(
   const int wn = wave;  // column slice
   const int64_t KC = Kp / 128;
   const int64_t KC4 = (KC + 3) / 4;
-  // one K split: tiles in the XCD-grouped order when xg > 0; else
-  // blockIdx.x = (mgroup * ngroups + ngroup) * splits + split
-  const int split = xg > 0 ? 0 : blockIdx.x % splits;
-  const int tilegrp = xg > 0 ? xcd_grouped_tile(blockIdx.x, gridDim.x, ngroups, xg) : blockIdx.x / splits;
+  // Workgroups [0, dp) compute whole tiles; after them each remaining tile
+  // takes `splits` consecutive workgroups, one K range each. Tile slot v
+  // (v < dp: workgroup v itself) maps to a tile in the XCD-grouped order when
+  // xg > 0 (a bijection over all slots, and for v < dp the order of the
+  // hardware's XCD assignment), else row-major: mgroup * ngroups + ngroup.
+  const int b = blockIdx.x;
+  const bool whole = b < dp;
+  const int vslot = whole ? b : dp + (b - dp) / splits;
+  const int split = whole ? 0 : (b - dp) % splits;
+  const int nsplit = whole ? 1 : splits;
+  const int ntile = dp + ((int)gridDim.x - dp) / splits;
+  const int tilegrp = xg > 0 ? xcd_grouped_tile(vslot, ntile, ngroups, xg) : vslot;
+  const int sslot = whole ? 0 : vslot - dp;  // partial slab and counter of a split tile
   const int ngroup = tilegrp % ngroups;
   const int mgroup = tilegrp / ngroups;
-  const int64_t c_begin = (int64_t)split * kc_per_split;
-  const int64_t c_end = c_begin + kc_per_split < KC ? c_begin + kc_per_split : KC;
+  const int64_t c_begin = whole ? 0 : (int64_t)split * kc_per_split;
+  const int64_t c_last = whole ? KC : c_begin + kc_per_split;
+  const int64_t c_end = c_last < KC ? c_last : KC;
   const int nch = (int)(c_end - c_begin);
   const int tile16_0 = (ngroup * WN + wn) * NT * 2;  // first packed 16-column tile of the wave
 
@@ -814,9 +824,9 @@ __global__ __launch_bounds__(64 * WN, OCC) void gemm_lds32_kernel(
   }
   wait_vmcnt<0>();  // no LDS load may still be in flight when the workgroup ends
 
-  float4v* slab = partial + (int64_t)tilegrp * splits * (WN * MT * NT * 4 * 64);
-  finish_tile32<MT, NT, WN>(acc, M, N, mgroup * MT * 32, ngroup * WN * NT * 32, wn, split, splits,
-                            alpha, bias, y, ldy, slab, counters + tilegrp, &s_flag);
+  float4v* slab = partial + (int64_t)sslot * splits * (WN * MT * NT * 4 * 64);
+  finish_tile32<MT, NT, WN>(acc, M, N, mgroup * MT * 32, ngroup * WN * NT * 32, wn, split, nsplit,
+                            alpha, bias, y, ldy, slab, counters + sslot, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -831,6 +841,7 @@ static constexpr int kCUs = 256;
 // float32 sum over K).
 struct GemmOverride {
   int kind = -1, waves = 0, ntw = 0, rc = 0, mt = 0, nt = 0, wm = 0, st = 0, splits = 0, xg = -1, cw = 0;
+  int tail = 0;  // kind 3: 1 = never split the last round's tiles, 2..4 = split them that many ways
 };
 static GemmOverride gemm_override() {
   GemmOverride o;
@@ -856,6 +867,7 @@ static GemmOverride gemm_override() {
       else if (k == "splits" && v >= 1 && v <= 64) o.splits = v;
       else if (k == "xg" && v >= 0 && v <= 64) o.xg = v;
       else if (k == "cw" && (v == 4 || v == 8)) o.cw = v;
+      else if (k == "tail" && v >= 1 && v <= 4) o.tail = v;
     }
     pos = end + 1;
   }
@@ -1016,12 +1028,29 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool rot
       p.xg = ov.xg >= 0 ? ov.xg : 4;
       if (p.xg > mgroups) p.xg = (int)mgroups;
     }
+    // Whole tiles use one workgroup each. When the tiles leave the last round
+    // of the GPU's 256 workgroup slots (one per CU) at most half full, the
+    // tiles of that round are split along K instead (up to 4 ways, through
+    // the split-K partial sums), so that round takes a fraction of a tile's
+    // time: Qwen3-32B down at M = 4096 has 640 tiles, 2.5 rounds.
+    p.dp_groups = p.splits > 1 ? 0 : groups;
+    if (p.kind == 3 && p.splits == 1 && ov.tail != 1 && groups >= kCUs) {
+      const int64_t r = groups % kCUs;
+      int64_t ts = r > 0 && r <= kCUs / 2 ? std::min<int64_t>(4, kCUs / r) : 1;
+      if (ov.tail >= 2 && r > 0) ts = ov.tail;
+      if (ts > 1 && KC >= 4 * ts && r <= (kCounterBytes - kWorkspaceScalarBytes) / 4) {
+        p.dp_groups = groups - r;
+        p.splits = (int)ts;
+        p.kc_per_split = (int)((KC + ts - 1) / ts);
+        p.splits = (int)((KC + p.kc_per_split - 1) / p.kc_per_split);
+      }
+    }
     p.xhat_bytes = round_up(p.Mp * p.Kp * 2, 256);
   }
   // [splits][waves][fragments][64 lanes] float4 per output tile
   const int64_t frags = (int64_t)p.mt * p.nt * (p.kind == 3 ? 4 : 1);
   const int64_t slab = (int64_t)p.splits * (p.kind == 3 ? p.cw : 4) * frags * 64 * 16;
-  p.partial_bytes = p.splits > 1 ? round_up(p.groups * slab, 256) : 0;
+  p.partial_bytes = p.splits > 1 ? round_up((p.groups - p.dp_groups) * slab, 256) : 0;
   p.counter_bytes = kCounterBytes;
   p.total_bytes = p.counter_bytes + p.xhat_bytes + p.partial_bytes;
   return p;
@@ -1032,16 +1061,16 @@ std::string describe_plan(const GemmPlan& p) {
   if (p.kind == 4) {
     std::snprintf(b, sizeof(b), "quant_nvfp4_apack_kernel + gemv_ring_kernel<W=%d,MT=%d,NT=%d,D=%d> grid=%lld splits=1",
                   p.waves, p.mt, p.nt, p.st, (long long)p.groups);
-  } else if (p.kind == 3 && p.cw != 4) {
-    std::snprintf(b, sizeof(b),
-                  "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d,WN=%d> grid=%lld splits=%d%s",
-                  p.mt, p.nt, p.st, p.cw, (long long)(p.groups * p.splits), p.splits,
-                  p.xg > 0 ? (" xcd_bands=" + std::to_string(p.xg)).c_str() : "");
   } else if (p.kind == 3) {
+    // whole tiles first; a split tail reads "tail=<tiles>x<splits>"
+    const bool tail = p.dp_groups > 0 && p.splits > 1;
+    std::string extra = p.xg > 0 ? " xcd_bands=" + std::to_string(p.xg) : "";
+    if (tail) extra += " tail=" + std::to_string(p.groups - p.dp_groups) + "x" + std::to_string(p.splits);
+    const std::string wn = p.cw != 4 ? ",WN=" + std::to_string(p.cw) : "";
     std::snprintf(b, sizeof(b),
-                  "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d> grid=%lld splits=%d%s",
-                  p.mt, p.nt, p.st, (long long)(p.groups * p.splits), p.splits,
-                  p.xg > 0 ? (" xcd_bands=" + std::to_string(p.xg)).c_str() : "");
+                  "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d%s> grid=%lld splits=%d%s",
+                  p.mt, p.nt, p.st, wn.c_str(), (long long)(p.dp_groups + (p.groups - p.dp_groups) * p.splits),
+                  tail ? 1 : p.splits, extra.c_str());
   } else if (p.kind == 0) {
     std::snprintf(b, sizeof(b), "linear_gemv_kernel<W=%d,NTW=%d,RC=%d,QPRE=%d> grid=%lld lds=%lld",
                   p.waves, p.ntw, p.kcmax, p.qpre, (long long)p.groups, (long long)p.lds_bytes);
@@ -1139,9 +1168,11 @@ static hipError_t launch_lds32_t(const GemmPlan& p, const _Float16* xhat, const 
                                  hipStream_t st) {
   const uint8_t* wcodes = packed;
   const uint8_t* wscales = packed + p.Np * p.Kp / 2;
-  gemm_lds32_kernel<MT, NT, ST, OCC, WN><<<(unsigned)(p.groups * p.splits), 64 * WN, 0, st>>>(
+  const int64_t grid = p.dp_groups + (p.groups - p.dp_groups) * p.splits;
+  gemm_lds32_kernel<MT, NT, ST, OCC, WN><<<(unsigned)grid, 64 * WN, 0, st>>>(
       xhat, wcodes, wscales, (int)M, (int)N, p.Kp, (int)(p.Np / 16), (int)p.ngroups,
-      p.kc_per_split, p.splits, p.xg, alpha, alpha_dev, bias, y, ldy, partial, counters);
+      p.kc_per_split, (int)p.dp_groups, p.splits, p.xg, alpha, alpha_dev, bias, y, ldy, partial,
+      counters);
   return hipGetLastError();
 }
 
@@ -1218,7 +1249,9 @@ static hipError_t launch_gemm_part(const GemmPlan& p, const uint8_t* packed, int
   uint32_t* counters = ws_counters(workspace);
   _Float16* xhat = reinterpret_cast<_Float16*>(ws_operand(p, workspace));
   float4v* partial4 = ws_partial(p, workspace);
-  if (p.splits > 1 && p.groups > (p.counter_bytes - kWorkspaceScalarBytes) / 4) return hipErrorInvalidValue;
+  // one arrival counter per split tile
+  if (p.splits > 1 && p.groups - (p.kind == 3 ? p.dp_groups : 0) > (p.counter_bytes - kWorkspaceScalarBytes) / 4)
+    return hipErrorInvalidValue;
   if (p.kind == 4) {
 #define FQL_X(A, B, C, E)                                                                             \
   if (p.waves == A && p.mt == B && p.nt == C && p.st == E) {                                          \

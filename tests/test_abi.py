@@ -321,6 +321,25 @@ def test_lds32_layouts_and_tile_order_in_the_plan():
         assert "WN=8> grid=81 splits=1 xcd_bands=3" in fql.linear_plan(1100, 2100, 1152)
 
 
+def test_last_round_tiles_split_along_k():
+    # 640 tiles of 128 x 256 leave the third round of 256 half full: its 128
+    # tiles take two workgroups each; full rounds and short K stay whole
+    assert "grid=768 splits=1 xcd_bands=4 tail=128x2" in fql.linear_plan(4096, 5120, 25600)
+    assert "grid=512 splits=1 xcd_bands=4 tail=128x2" in fql.linear_plan(2048, 6144, 4096)
+    assert "grid=272 splits=1 xcd_bands=4 tail=4x4" in fql.linear_plan(1650, 5120, 2048)
+    assert "tail" not in fql.linear_plan(8192, 28672, 4096)   # 7168 tiles: 28 full rounds
+    assert "tail" not in fql.linear_plan(256, 51200, 5120)    # 400 tiles: last round 56% full
+    assert "tail" not in fql.linear_plan(2048, 6144, 512)     # 4 chunks of K
+    with fql.plan_override("tail=1"):
+        assert "grid=640 splits=1 xcd_bands=4" in fql.linear_plan(4096, 5120, 25600)
+    with fql.plan_override("tail=3"):
+        assert "grid=896 splits=1 xcd_bands=4 tail=128x3" in fql.linear_plan(4096, 5120, 25600)
+    # the split tiles' partial sums are part of the workspace
+    with fql.plan_override("tail=1"):
+        whole = fql.linear_workspace_bytes(4096, 5120, 25600)
+    assert fql.linear_workspace_bytes(4096, 5120, 25600) == whole + 128 * 2 * 8 * 16 * 64 * 16
+
+
 def test_rotation_widens_the_fused_kernels_workgroups_at_m1():
     # with a Hadamard rotation every workgroup of the fused kernel also rotates
     # the activation: two column tiles per workgroup on the narrow layers

@@ -111,6 +111,21 @@ def test_linear_rotated_single_row_ragged(M, K, N, hb):
     _run_case("hadamard", M, K, N, hb, True, label="rotated-ragged")
 
 
+@pytest.mark.parametrize("M,K,N,spec", [(2048, 1024, 6144, None), (1650, 2048, 5120, None),
+                                        (2048, 2048, 6144, "tail=3")])
+def test_linear_last_round_split_every_row(M, K, N, spec):
+    # tiles of the last, part-filled round of workgroups are split along K
+    # (2048 x 6144: 384 tiles, the last 128 in two halves; 1650 x 5120: 260
+    # tiles, the last 4 in quarters; ragged rows); every row is compared
+    if spec:
+        with fql.plan_override(spec):
+            assert "tail=" in fql.linear_plan(M, N, K)
+            _run_case("prefill", M, K, N, 0, True, label=f"tail-split {spec}")
+    else:
+        assert "tail=" in fql.linear_plan(M, N, K)
+        _run_case("prefill", M, K, N, 0, True, label="tail-split")
+
+
 def test_linear_strided_3d_input_and_output_stride():
     M, K, N = 24, 1024, 320
     xb = synthetic.activations("normal", M, K, config="decode", seed=4)
