@@ -228,7 +228,9 @@ struct ScPlan {
                              // GEMV: wn = waves splitting K, mtw = row tiles,
                              //       ntw = column tiles per workgroup, st = chunks in flight
   int64_t Mp, groups, ngroups;
-  int splits, kc_per_split;
+  int splits, kc_per_split;  // K splits of the split tiles, chunks per split
+  int64_t dp_groups;         // GEMM: tiles computed whole (the first dp_groups workgroups);
+                             // the others take `splits` consecutive workgroups each
   int64_t counter_bytes, xcode_bytes, xscale_bytes, partial_bytes, total_bytes;
   int fq;           // GEMV: activation quantized inside the workgroups (one launch)
   int64_t dyn_lds;  // GEMV with fq: dynamic LDS bytes (the activation operand)

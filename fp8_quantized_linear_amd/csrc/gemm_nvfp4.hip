@@ -1029,14 +1029,18 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool rot
       if (p.xg > mgroups) p.xg = (int)mgroups;
     }
     // Whole tiles use one workgroup each. When the tiles leave the last round
-    // of the GPU's 256 workgroup slots (one per CU) at most half full, the
-    // tiles of that round are split along K instead (up to 4 ways, through
-    // the split-K partial sums), so that round takes a fraction of a tile's
-    // time: Qwen3-32B down at M = 4096 has 640 tiles, 2.5 rounds.
+    // of the GPU's 256 workgroup slots (one per CU) at most half full and K
+    // is long, the tiles of that round are split along K instead (up to 4
+    // ways, through the split-K partial sums), so that round takes a fraction
+    // of a tile's time. Measured: Qwen3-32B down at M = 4096 (640 tiles, 2.5
+    // rounds, 200 chunks of K) 940 -> 875 us; with 32 chunks the saving is
+    // gone (prefill qkv at M = 2048: 111 us either way), as the half-empty
+    // round already runs at a higher clock and the partial sums cost a few
+    // microseconds per tile.
     p.dp_groups = p.splits > 1 ? 0 : groups;
     if (p.kind == 3 && p.splits == 1 && ov.tail != 1 && groups >= kCUs) {
       const int64_t r = groups % kCUs;
-      int64_t ts = r > 0 && r <= kCUs / 2 ? std::min<int64_t>(4, kCUs / r) : 1;
+      int64_t ts = r > 0 && r <= kCUs / 2 && KC >= 64 ? std::min<int64_t>(4, kCUs / r) : 1;
       if (ov.tail >= 2 && r > 0) ts = ov.tail;
       if (ts > 1 && KC >= 4 * ts && r <= (kCounterBytes - kWorkspaceScalarBytes) / 4) {
         p.dp_groups = groups - r;

@@ -97,7 +97,7 @@ template <int F, int WM, int WN, int MTW, int NTW, int ST>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
     const uint8_t* __restrict__ xcodes, const uint8_t* __restrict__ xscales,
     const uint8_t* __restrict__ wcodes, const uint8_t* __restrict__ wscales, int M, int N,
-    int64_t KC, int ntiles_w, int64_t quads_w, int ngroups, int kc_per_split, int splits,
+    int64_t KC, int ntiles_w, int64_t quads_w, int ngroups, int kc_per_split, int dp, int splits,
     float alpha, const float* __restrict__ alpha_dev, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ y, int64_t ldy, float4v* __restrict__ partial,
     uint32_t* __restrict__ counters) {
@@ -126,12 +126,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
-  const int split = blockIdx.x % splits;
-  const int tilegrp = blockIdx.x / splits;
+  // Workgroups [0, dp) compute whole tiles (tile = workgroup); after them
+  // each remaining tile takes `splits` consecutive workgroups, one K range
+  // each. Tiles are numbered row-major: mgroup * ngroups + ngroup.
+  const int b = blockIdx.x;
+  const bool whole = b < dp;
+  const int tilegrp = whole ? b : dp + (b - dp) / splits;
+  const int split = whole ? 0 : (b - dp) % splits;
+  const int nsplit = whole ? 1 : splits;
+  const int sslot = whole ? 0 : tilegrp - dp;  // partial slab and counter of a split tile
   const int ngroup = tilegrp % ngroups;
   const int mgroup = tilegrp / ngroups;
-  const int64_t c_begin = (int64_t)split * kc_per_split;
-  const int64_t c_end = c_begin + kc_per_split < KC ? c_begin + kc_per_split : KC;
+  const int64_t c_begin = whole ? 0 : (int64_t)split * kc_per_split;
+  const int64_t c_last = whole ? KC : c_begin + kc_per_split;
+  const int64_t c_end = c_last < KC ? c_last : KC;
   const int nch = (int)(c_end - c_begin);
   const int64_t a_tile0 = (int64_t)mgroup * TA;
   const int64_t a_quad0 = a_tile0 / 4;
@@ -435,10 +443,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
     for (int nt = 0; nt < NTW; ++nt) frag[mt * NTW + nt] = acc[mt][nt];
   auto row_of = [&](int f, int i) { return (wm * MTW + f / NTW) * 16 + 4 * (lane >> 4) + i; };
   auto col_of = [&](int f) { return (wn * NTW + f % NTW) * 16 + (lane & 15); };
-  float4v* slab = partial + (int64_t)tilegrp * splits * (NW * P * 64);
+  float4v* slab = partial + (int64_t)sslot * splits * (NW * P * 64);
   finish_frags<P, decltype(row_of), decltype(col_of), NW>(
-      frag, row_of, col_of, M, N, mgroup * TA * 16, ngroup * TB * 16, split, splits, alpha, bias, y,
-      ldy, slab, counters + tilegrp, &s_flag);
+      frag, row_of, col_of, M, N, mgroup * TA * 16, ngroup * TB * 16, split, nsplit, alpha, bias, y,
+      ldy, slab, counters + sslot, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -857,13 +865,13 @@ ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
       return p;
     }
   }
-  int splits_override = 0;
+  int splits_override = 0, tail_override = 0;
   const std::string gemm_spec = plan_override(kOverrideScGemm);
-  if (!gemm_spec.empty()) {  // benchmarking aid: "wm,wn,mtw,ntw,st,splits"
-    int a = 0, b = 0, c = 0, d = 0, f = 0, s = 0;
-    if (std::sscanf(gemm_spec.c_str(), "%d,%d,%d,%d,%d,%d", &a, &b, &c, &d, &f, &s) >= 5 &&
+  if (!gemm_spec.empty()) {  // benchmarking aid: "wm,wn,mtw,ntw,st,splits[,tail]"
+    int a = 0, b = 0, c = 0, d = 0, f = 0, s = 0, t = 0;
+    if (std::sscanf(gemm_spec.c_str(), "%d,%d,%d,%d,%d,%d,%d", &a, &b, &c, &d, &f, &s, &t) >= 5 &&
         sc_config_built(fmt, a, b, c, d, f)) {
-      wm = a; wn = b; mtw = c; ntw = d; st = f; splits_override = s;
+      wm = a; wn = b; mtw = c; ntw = d; st = f; splits_override = s; tail_override = t;
     }
   }
   if (!sc_config_built(fmt, wm, wn, mtw, ntw, st)) { wm = 1; wn = 4; mtw = 1; ntw = 2; st = 4; }
@@ -878,11 +886,29 @@ ScPlan plan_sc_gemm(int fmt, int64_t M, int64_t N, int64_t K) {
   p.kc_per_split = (int)((KC + s - 1) / s);
   p.splits = (int)((KC + p.kc_per_split - 1) / p.kc_per_split);
   p.groups = groups;
+  // The 8-wave tiles hold one workgroup per CU (their rings fill the LDS).
+  // When their tiles leave the last round of the 256 CUs at most half full
+  // and K is long (at least 64 chunks), that round's tiles are split along K
+  // (up to 4 ways, through the split-K partial sums) instead. With short K
+  // the partial sums cost more than the round saves: MXFP4 at M = 4096,
+  // N = 14336, K = 4096 (896 tiles, 3.5 rounds, 32 chunks) took 180 us split
+  // against 163 us whole. tail_override: 1 = never, 2..4 = that many ways.
+  p.dp_groups = p.splits > 1 ? 0 : groups;
+  if (p.splits == 1 && wm * wn == 8 && tail_override != 1 && groups >= 256) {
+    const int64_t r = groups % 256;
+    int64_t ts = r > 0 && r <= 128 && KC >= 64 ? std::min<int64_t>(4, 256 / r) : 1;
+    if (tail_override >= 2 && tail_override <= 4 && r > 0) ts = tail_override;
+    if (ts > 1 && KC >= 4 * ts) {
+      p.dp_groups = groups - r;
+      p.kc_per_split = (int)((KC + ts - 1) / ts);
+      p.splits = (int)((KC + p.kc_per_split - 1) / p.kc_per_split);
+    }
+  }
   const ScDims x = sc_dims(fmt, p.Mp, K, false);
   p.xcode_bytes = round_up(x.code_bytes, 256);
   p.xscale_bytes = round_up(std::max<int64_t>(x.scale_bytes, 0), 256);
   const int64_t slab = (int64_t)p.splits * wm * wn * mtw * ntw * 64 * 16;
-  p.partial_bytes = p.splits > 1 ? round_up(groups * slab, 256) : 0;
+  p.partial_bytes = p.splits > 1 ? round_up((groups - p.dp_groups) * slab, 256) : 0;
   p.counter_bytes = 64 * 1024;
   p.total_bytes = p.counter_bytes + p.xcode_bytes + p.xscale_bytes + p.partial_bytes;
   return p;
@@ -900,10 +926,15 @@ std::string describe_sc_plan(const ScPlan& p) {
                   sc_fmt_name(p.fmt), sc_fmt_name(p.fmt), p.wn, p.mtw, p.ntw, p.st, (long long)p.groups);
     return std::string(b);
   }
+  // whole tiles first; a split tail reads "tail=<tiles>x<splits>"
+  const bool tail = p.dp_groups > 0 && p.splits > 1;
+  const std::string extra =
+      tail ? " tail=" + std::to_string(p.groups - p.dp_groups) + "x" + std::to_string(p.splits) : "";
   std::snprintf(b, sizeof(b),
-                "sc_quant_operand_kernel<%s> + gemm_sc_kernel<%s,WM=%d,WN=%d,MTW=%d,NTW=%d,ST=%d> grid=%lld splits=%d",
+                "sc_quant_operand_kernel<%s> + gemm_sc_kernel<%s,WM=%d,WN=%d,MTW=%d,NTW=%d,ST=%d> grid=%lld splits=%d%s",
                 sc_fmt_name(p.fmt), sc_fmt_name(p.fmt), p.wm, p.wn, p.mtw, p.ntw, p.st,
-                (long long)(p.groups * p.splits), p.splits);
+                (long long)(p.dp_groups + (p.groups - p.dp_groups) * p.splits), tail ? 1 : p.splits,
+                extra.c_str());
   return std::string(b);
 }
 
@@ -915,9 +946,11 @@ static hipError_t launch_sc_t(const ScPlan& p, const uint8_t* xc, const uint8_t*
   if constexpr (!sc_config_fits<F, WM, WN, MTW, NTW, ST>()) {
     return hipErrorInvalidValue;
   } else {
-    gemm_sc_kernel<F, WM, WN, MTW, NTW, ST><<<(unsigned)(p.groups * p.splits), 64 * WM * WN, 0, st>>>(
+    const int64_t grid = p.dp_groups + (p.groups - p.dp_groups) * p.splits;
+    gemm_sc_kernel<F, WM, WN, MTW, NTW, ST><<<(unsigned)grid, 64 * WM * WN, 0, st>>>(
         xc, xs, packed, packed + w.code_bytes, (int)M, (int)N, w.KC, (int)(w.rows_p / 16), w.quads,
-        (int)p.ngroups, p.kc_per_split, p.splits, alpha, alpha_dev, bias, y, ldy, partial, counters);
+        (int)p.ngroups, p.kc_per_split, (int)p.dp_groups, p.splits, alpha, alpha_dev, bias, y, ldy,
+        partial, counters);
     return hipGetLastError();
   }
 }
@@ -959,7 +992,7 @@ hipError_t launch_sc_linear(const ScPlan& p, const uint16_t* x, int64_t M, int64
   uint8_t* xc = workspace + p.counter_bytes;
   uint8_t* xs = xc + p.xcode_bytes;
   float4v* partial = reinterpret_cast<float4v*>(xs + p.xscale_bytes);
-  if (p.splits > 1 && p.groups > p.counter_bytes / 4) return hipErrorInvalidValue;
+  if (p.splits > 1 && p.groups - p.dp_groups > p.counter_bytes / 4) return hipErrorInvalidValue;  // counter per split tile
   if (p.kind == 1 && p.fq) {
 #define FQL_X(F0, A, B, C, E)                                                                      \
   if (p.fmt == F0 && p.wn == A && p.mtw == B && p.ntw == C && p.st == E)                           \

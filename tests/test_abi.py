@@ -325,11 +325,14 @@ def test_last_round_tiles_split_along_k():
     # 640 tiles of 128 x 256 leave the third round of 256 half full: its 128
     # tiles take two workgroups each; full rounds and short K stay whole
     assert "grid=768 splits=1 xcd_bands=4 tail=128x2" in fql.linear_plan(4096, 5120, 25600)
-    assert "grid=512 splits=1 xcd_bands=4 tail=128x2" in fql.linear_plan(2048, 6144, 4096)
-    assert "grid=272 splits=1 xcd_bands=4 tail=4x4" in fql.linear_plan(1650, 5120, 2048)
+    assert "tail" not in fql.linear_plan(2048, 6144, 4096)    # 32 chunks of K: kept whole
     assert "tail" not in fql.linear_plan(8192, 28672, 4096)   # 7168 tiles: 28 full rounds
     assert "tail" not in fql.linear_plan(256, 51200, 5120)    # 400 tiles: last round 56% full
-    assert "tail" not in fql.linear_plan(2048, 6144, 512)     # 4 chunks of K
+    with fql.plan_override("tail=2"):
+        assert "grid=512 splits=1 xcd_bands=4 tail=128x2" in fql.linear_plan(2048, 6144, 4096)
+        assert "tail" not in fql.linear_plan(2048, 6144, 512)  # 4 chunks of K: too short to split
+    with fql.plan_override("tail=4"):
+        assert "grid=272 splits=1 xcd_bands=4 tail=4x4" in fql.linear_plan(1650, 5120, 2048)
     with fql.plan_override("tail=1"):
         assert "grid=640 splits=1 xcd_bands=4" in fql.linear_plan(4096, 5120, 25600)
     with fql.plan_override("tail=3"):
@@ -338,6 +341,20 @@ def test_last_round_tiles_split_along_k():
     with fql.plan_override("tail=1"):
         whole = fql.linear_workspace_bytes(4096, 5120, 25600)
     assert fql.linear_workspace_bytes(4096, 5120, 25600) == whole + 128 * 2 * 8 * 16 * 64 * 16
+
+
+def test_sibling_last_round_tiles_split_along_k():
+    # MXFP4 at M = 4096: 896 tiles of 256 x 256, the last 128 in two halves
+    # MXFP4 at M = 4096: 896 tiles of 256 x 256, the last 128 split in two
+    # along K when K is long; at K = 4096 (32 chunks) they stay whole
+    assert "grid=1024 splits=1 tail=128x2" in fql.linear_sc_plan("mxfp4", 4096, 14336, 8192)
+    assert "grid=896 splits=1" in fql.linear_sc_plan("mxfp4", 4096, 14336, 4096)
+    assert "tail" not in fql.linear_sc_plan("fp8", 4096, 14336, 8192)  # 1792 tiles: 7 rounds
+    assert "tail" not in fql.linear_sc_plan("mxfp4", 2048, 14336, 8192)  # last round 75% full
+    with fql.plan_override("2,4,8,4,4,0,2", which="sc_gemm"):
+        assert "grid=1024 splits=1 tail=128x2" in fql.linear_sc_plan("mxfp4", 4096, 14336, 4096)
+    with fql.plan_override("2,4,8,4,4,0,1", which="sc_gemm"):
+        assert "grid=896 splits=1" in fql.linear_sc_plan("mxfp4", 4096, 14336, 8192)
 
 
 def test_rotation_widens_the_fused_kernels_workgroups_at_m1():

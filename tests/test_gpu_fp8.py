@@ -209,6 +209,18 @@ def test_linear_siblings(fmt, M):
          label="siblings")
 
 
+@pytest.mark.parametrize("fmt,N", [("mxfp4", 24576), ("mxfp8", 12288), ("fp8", 12288), ("fp8_block", 12288)])
+def test_linear_last_round_split_every_row(fmt, N):
+    # 4 row groups x 96 column groups = 384 tiles: the last 128 are split in
+    # two along K; 1000 rows (ragged), every row and column compared
+    # (forced: the plan splits the last round itself only for long K)
+    M, K = 1000, 1024
+    spec = "2,4,8,4,4,0,2" if fmt == "mxfp4" else "4,2,4,4,3,0,2"
+    with fql.plan_override(spec, which="sc_gemm"):
+        assert "grid=512 splits=1 tail=128x2" in fql.linear_sc_plan(fmt, M, N, K)
+        _run(fmt, "siblings", M, K, N, True, label="tail-split")
+
+
 @pytest.mark.parametrize("M,K,N", [(1, 96, 100), (3, 160, 520), (17, 416, 33), (33, 2080, 200),
                                    (130, 4096, 48)])
 @pytest.mark.parametrize("fmt", ["mxfp8", "fp8"])

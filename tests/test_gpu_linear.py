@@ -111,19 +111,16 @@ def test_linear_rotated_single_row_ragged(M, K, N, hb):
     _run_case("hadamard", M, K, N, hb, True, label="rotated-ragged")
 
 
-@pytest.mark.parametrize("M,K,N,spec", [(2048, 1024, 6144, None), (1650, 2048, 5120, None),
-                                        (2048, 2048, 6144, "tail=3")])
+@pytest.mark.parametrize("M,K,N,spec", [(2048, 1024, 6144, "tail=2"), (1650, 2048, 5120, "tail=4"),
+                                        (2048, 2048, 6144, "tail=3"), (1650, 8192, 5120, None)])
 def test_linear_last_round_split_every_row(M, K, N, spec):
-    # tiles of the last, part-filled round of workgroups are split along K
-    # (2048 x 6144: 384 tiles, the last 128 in two halves; 1650 x 5120: 260
-    # tiles, the last 4 in quarters; ragged rows); every row is compared
-    if spec:
-        with fql.plan_override(spec):
-            assert "tail=" in fql.linear_plan(M, N, K)
-            _run_case("prefill", M, K, N, 0, True, label=f"tail-split {spec}")
-    else:
+    # tiles of the last, part-filled round of workgroups split along K (the
+    # plan's own choice for long K, here 64 chunks; forced at shorter K):
+    # 2048 x 6144 has 384 tiles, the last 128 in halves or thirds; 1650 x 5120
+    # has 260, the last 4 in quarters (ragged rows). Every row is compared.
+    with fql.plan_override(spec or ""):
         assert "tail=" in fql.linear_plan(M, N, K)
-        _run_case("prefill", M, K, N, 0, True, label="tail-split")
+        _run_case("prefill", M, K, N, 0, True, label=f"tail-split {spec}")
 
 
 def test_linear_strided_3d_input_and_output_stride():
