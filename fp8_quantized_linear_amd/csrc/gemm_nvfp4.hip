@@ -839,42 +839,42 @@ __global__ __launch_bounds__(64 * WN, OCC) void gemm_lds32_kernel(
   // landed and everyone has finished reading chunk g's activation fragments.
   // After an item's last chunk its tile is written out and the accumulators
   // start over for the next item, whose first chunks are already in flight.
-  // (The stage is a runtime index: one copy of the chunk body, the tile
-  // write-out included, instead of one per stage.)
   const int total = T * nch;
-  int sj = 0;  // stage of chunk g
-  for (int g = 0; g < total; ++g) {
-    const int sp = sj == 0 ? ST - 1 : sj - 1, sn = sj == ST - 1 ? 0 : sj + 1;
-    steps0to6(stage[sj], stage[sp]);
-    const bool more = g + 1 < total;
-    wait_vmcnt<L * (ST - 2)>();  // this wave's loads of chunk g+1 have landed
-    if (more) read_head_b(stage[sn]);  // its own loads
-    stage_barrier();             // everyone's have, and stage sj has been read by all
-    if (more) read_head_a(stage[sn]);
-    __builtin_amdgcn_sched_barrier(0);
-    if (more) dequant(0, 0);
-    mfmas(1);
+  for (int g0 = 0; g0 < total; g0 += ST) {
 #pragma unroll
-    for (int i = 0; i < MFMAS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i >= MFMAS / 4) __builtin_amdgcn_sched_group_barrier(0x002, VPM + 1, 0);
+    for (int j = 0; j < ST; ++j) {
+      if (g0 + j < total) {
+        steps0to6(stage[j], stage[(j + ST - 1) % ST]);
+        const bool more = g0 + j + 1 < total;
+        wait_vmcnt<L * (ST - 2)>();  // this wave's loads of chunk g+1 have landed
+        if (more) read_head_b(stage[(j + 1) % ST]);  // its own loads
+        stage_barrier();             // everyone's have, and stage j has been read by all
+        if (more) read_head_a(stage[(j + 1) % ST]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) dequant(0, 0);
+        mfmas(1);
+#pragma unroll
+        for (int i = 0; i < MFMAS; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i >= MFMAS / 4) __builtin_amdgcn_sched_group_barrier(0x002, VPM + 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (cc == nch - 1 && nsplit == 1) {
+          // a whole tile is done: write it out (the plain path, splits = 1)
+          // and start the next item's sums
+          finish_tile32<MT, NT, WN>(acc, M, N, cur.m0, cur.n0, wn, 0, 1, alpha, bias, y, ldy, nullptr,
+                                    nullptr, &s_flag);
+#pragma unroll
+          for (int a2 = 0; a2 < MT; ++a2)
+#pragma unroll
+            for (int b2 = 0; b2 < NT; ++b2) acc[a2][b2] = float16v{};
+          cc = 0;
+          if (++cj < T) cur = nxt;
+        } else {
+          ++cc;
+        }
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (cc == nch - 1 && nsplit == 1) {
-      // a whole tile is done: write it out (the plain path, splits = 1) and
-      // start the next item's sums
-      finish_tile32<MT, NT, WN>(acc, M, N, cur.m0, cur.n0, wn, 0, 1, alpha, bias, y, ldy, nullptr,
-                                nullptr, &s_flag);
-#pragma unroll
-      for (int a2 = 0; a2 < MT; ++a2)
-#pragma unroll
-        for (int b2 = 0; b2 < NT; ++b2) acc[a2][b2] = float16v{};
-      cc = 0;
-      if (++cj < T) cur = nxt;
-    } else {
-      ++cc;
-    }
-    sj = sn;
   }
   wait_vmcnt<0>();  // no LDS load may still be in flight when the workgroup ends
   if (nsplit > 1) {
