@@ -94,10 +94,9 @@ struct GemmPlan {
   int64_t ngroups;    // column groups (kind 1)
   int splits;         // K splits of the split tiles (1 = epilogue directly in the GEMM)
   int kc_per_split;   // 128-deep K chunks per split
-  int64_t dp_groups;  // kind 3: tiles computed whole; the other groups - dp_groups
-                      // tiles take `splits` consecutive workgroups each
-  int64_t pw;         // kind 3: workgroups sharing the whole tiles (pw = dp_groups: one
-                      // tile each; fewer: persistent, pw per round of tiles)
+  int64_t dp_groups;  // kind 3: tiles computed whole, one workgroup each (the first
+                      // dp_groups workgroups); the other groups - dp_groups tiles
+                      // take `splits` consecutive workgroups each
   int kcmax;          // kind 0: weight register ring depth in chunks (4 or 8)
   int waves;          // kind 0: waves per workgroup (split of K inside the workgroup)
   int qpre;           // kind 0: activation blocks per thread loaded ahead of the weights

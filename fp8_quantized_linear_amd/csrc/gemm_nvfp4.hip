@@ -604,7 +604,7 @@ template <int MT, int NT, int ST, int OCC, int WN = 4>
 __global__ __launch_bounds__(64 * WN, OCC) void gemm_lds32_kernel(
     const _Float16* __restrict__ xhat, const uint8_t* __restrict__ wcodes,
     const uint8_t* __restrict__ wscales, int M, int N, int64_t Kp, int ntiles, int ngroups,
-    int kc_per_split, int dp, int pw, int splits, int xg, float alpha,
+    int kc_per_split, int dp, int splits, int xg, float alpha,
     const float* __restrict__ alpha_dev, const uint16_t* __restrict__ bias,
     uint16_t* __restrict__ y, int64_t ldy, float4v* __restrict__ partial,
     uint32_t* __restrict__ counters) {
@@ -626,105 +626,70 @@ __global__ __launch_bounds__(64 * WN, OCC) void gemm_lds32_kernel(
   const int wn = wave;  // column slice
   const int64_t KC = Kp / 128;
   const int64_t KC4 = (KC + 3) / 4;
-  // Work items. The dp whole tiles are shared by the first pw workgroups:
-  // workgroup b < pw computes tile slots b, b + pw, b + 2 pw, ... below dp
-  // (pw = dp: one each; pw < dp: persistent workgroups, one per CU, whose
-  // ring runs on from one tile into the next). After them each remaining
-  // tile takes `splits` consecutive workgroups, one K range each. Tile slot v
-  // maps to a tile in the XCD-grouped order when xg > 0 (a bijection over all
-  // slots which, as pw is a multiple of 8, keeps every slot of a workgroup on
-  // the workgroup's XCD), else row-major: mgroup * ngroups + ngroup.
+  // Workgroups [0, dp) compute whole tiles; after them each remaining tile
+  // takes `splits` consecutive workgroups, one K range each. Tile slot v
+  // (v < dp: workgroup v itself) maps to a tile in the XCD-grouped order when
+  // xg > 0 (a bijection over all slots, and for v < dp the order of the
+  // hardware's XCD assignment), else row-major: mgroup * ngroups + ngroup.
   const int b = blockIdx.x;
-  const bool whole = b < pw;
-  const int ntile = dp + ((int)gridDim.x - pw) / splits;
-  const int T = whole ? (dp - b + pw - 1) / pw : 1;  // work items of this workgroup
-  const int split = whole ? 0 : (b - pw) % splits;
+  const bool whole = b < dp;
+  const int vslot = whole ? b : dp + (b - dp) / splits;
+  const int split = whole ? 0 : (b - dp) % splits;
   const int nsplit = whole ? 1 : splits;
-  const int sslot = whole ? 0 : (b - pw) / splits;  // partial slab and counter of a split tile
+  const int ntile = dp + ((int)gridDim.x - dp) / splits;
+  const int tilegrp = xg > 0 ? xcd_grouped_tile(vslot, ntile, ngroups, xg) : vslot;
+  const int sslot = whole ? 0 : vslot - dp;  // partial slab and counter of a split tile
+  const int ngroup = tilegrp % ngroups;
+  const int mgroup = tilegrp / ngroups;
   const int64_t c_begin = whole ? 0 : (int64_t)split * kc_per_split;
   const int64_t c_last = whole ? KC : c_begin + kc_per_split;
   const int64_t c_end = c_last < KC ? c_last : KC;
   const int nch = (int)(c_end - c_begin);
+  const int tile16_0 = (ngroup * WN + wn) * NT * 2;  // first packed 16-column tile of the wave
 
   // wave-uniform global bases; per-lane byte offsets. A wave loads the
   // 32-deep step wn % 4 of every TS-th 16-row tile, from tile wn / 4 on.
   const int64_t a_tile_stride = (Kp / 32) * 1024;  // bytes between 16-row x_hat tiles
+  const uint8_t* a_base = reinterpret_cast<const uint8_t*>(xhat) +
+                          ((int64_t)mgroup * MT * 2 * (Kp / 32) + wn % 4) * 1024 +
+                          (wn / 4) * a_tile_stride;
   const uint32_t a_voff = lane * 16;
   const int jc = lane & 31, hh = lane >> 5;  // column in the 32-column tile, k half
-  // One work item's tile: its output origin, its x_hat row tiles and the
-  // per-lane offsets of the code and scale slots this wave loads (slot (b, e)
-  // of 32-column tile b holds the even (e = 0) or odd (e = 1) steps; a
-  // 16-column tile past the end is clamped to the last one, read and never
-  // stored; the host keeps the packed blob below 4 GiB so that these 32-bit
-  // offsets cannot wrap).
-  struct Item {
-    const uint8_t* a_base;
-    uint32_t q_voff[NLB], s_voff[NLB];
-    int m0, n0;
-  };
-  auto item_of = [&](int j) -> Item {
-    const int v = whole ? b + j * pw : dp + sslot;
-    const int tilegrp = xg > 0 ? xcd_grouped_tile(v, ntile, ngroups, xg) : v;
-    const int ngroup = tilegrp % ngroups;
-    const int mgroup = tilegrp / ngroups;
-    const int tile16_0 = (ngroup * WN + wn) * NT * 2;  // first packed 16-column tile of the wave
-    Item it;
-    it.a_base = uniform_ptr(reinterpret_cast<const uint8_t*>(xhat) +
-                            ((int64_t)mgroup * MT * 2 * (Kp / 32) + wn % 4) * 1024 +
-                            (wn / 4) * a_tile_stride);
+  // Per-lane offsets of the code and scale slots this wave loads: slot (b, e)
+  // of 32-column tile b holds the even (e = 0) or odd (e = 1) steps. A
+  // 16-column tile past the end is clamped to the last one (read, never
+  // stored); the host keeps the packed blob below 4 GiB so that these 32-bit
+  // offsets cannot wrap.
+  uint32_t q_voff[NLB], s_voff[NLB];
 #pragma unroll
-    for (int i = 0; i < NLB; ++i) {
-      const int bt = i / 2;
-      const int e = i % 2;
-      int64_t tl = tile16_0 + 2 * bt + (jc >> 4);
-      tl = tl < ntiles ? tl : ntiles - 1;
-      it.q_voff[i] = (uint32_t)(tl * KC * 1024 + ((2 * e + hh) * 16 + (jc & 15)) * 16);
-      it.s_voff[i] = (uint32_t)(tl * KC4 * 512 + ((jc & 15) * 2 + e) * 16);
-    }
-    it.m0 = mgroup * MT * 32;
-    it.n0 = ngroup * WN * NT * 32;
-    return it;
-  };
-  // The computation is at chunk cc of item cj (state cur); the refills walk
-  // the same chunk stream ST-1 chunks ahead, at chunk rc of item rj (state
-  // cur while rj == cj, nxt once they have moved on to the next item; nch >=
-  // ST whenever T > 1, so they are never two items ahead). Past the end of
-  // the stream they repeat the last chunk: a static number of loads per chunk.
-  int cj = 0, cc = 0, rj = 0, rc = 0;
-  Item cur = item_of(0);
-  Item nxt = cur;
+  for (int i = 0; i < NLB; ++i) {
+    const int b = i / 2;
+    const int e = i % 2;
+    int64_t tl = tile16_0 + 2 * b + (jc >> 4);
+    tl = tl < ntiles ? tl : ntiles - 1;
+    q_voff[i] = (uint32_t)(tl * KC * 1024 + ((2 * e + hh) * 16 + (jc & 15)) * 16);
+    s_voff[i] = (uint32_t)(tl * KC4 * 512 + ((jc & 15) * 2 + e) * 16);
+  }
 
+  // The scalar bases of chunk c's loads into stage sg, computed once per chunk
+  // (chunks past the range are clamped: a static number of loads per chunk).
   struct Refill {
     const uint8_t* a;  // activation row tile 0 of the chunk
     const uint8_t* q;  // weight codes of the chunk
     const uint8_t* s;  // the chunk's scale dword column
     uint32_t la, lq, ls;  // this wave's LDS destinations in the stage
-    uint32_t qv[NLB], sv[NLB];  // the item's per-lane code and scale offsets
   };
   // the wave's slot i sits at slot index (wn*NT + b)*2 + e = wn*NT*2 + i of the stage
-  auto refill_of = [&](Stage& sg) -> Refill {
-    const bool past = rj >= T;
-    const bool from_nxt = !past && rj != cj;
-    const int64_t c = past ? c_end - 1 : c_begin + rc;
+  auto refill_of = [&](Stage& sg, int64_t c) -> Refill {
+    c = c < c_end ? c : c_end - 1;
     Refill r;
-    r.a = uniform_ptr((from_nxt ? nxt.a_base : cur.a_base) + c * 4096);
+    r.a = uniform_ptr(a_base + c * 4096);
     r.q = uniform_ptr(wcodes + c * 1024);
     r.s = uniform_ptr(wscales + (c >> 2) * 512 + (c & 3) * 4);
     r.la = __builtin_amdgcn_readfirstlane(lds_offset(&sg.a[(wn / 4) * 4 + wn % 4][0]));
     r.lq = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bq[wn * NT * 2][0]));
     r.ls = __builtin_amdgcn_readfirstlane(lds_offset(&sg.bs[wn * NT * 2][0]));
-#pragma unroll
-    for (int i = 0; i < NLB; ++i) {
-      r.qv[i] = from_nxt ? nxt.q_voff[i] : cur.q_voff[i];
-      r.sv[i] = from_nxt ? nxt.s_voff[i] : cur.s_voff[i];
-    }
     return r;
-  };
-  auto advance_refill = [&]() {
-    if (++rc == nch) {
-      rc = 0;
-      if (++rj < T) nxt = item_of(rj);
-    }
   };
   // LDS load number e (0 <= e < L) of a chunk
   auto issue_one = [&](const Refill& r, int e) {
@@ -732,15 +697,14 @@ __global__ __launch_bounds__(64 * WN, OCC) void gemm_lds32_kernel(
       lds_load16(r.a + e * TS * a_tile_stride, a_voff, r.la + e * TS * 4 * 1024);
     } else if (e < NA + NLB) {
       const int i = e - NA;
-      lds_load16(r.q, r.qv[i], r.lq + i * 1024);
+      lds_load16(r.q, q_voff[i], r.lq + i * 1024);
     } else {
       const int i = e - NA - NLB;
-      lds_load4(r.s, r.sv[i], r.ls + i * 256);
+      lds_load4(r.s, s_voff[i], r.ls + i * 256);
     }
   };
-  auto issue = [&](Stage& sg) {
-    const Refill r = refill_of(sg);
-    advance_refill();
+  auto issue = [&](Stage& sg, int64_t c) {
+    const Refill r = refill_of(sg, c);
 #pragma unroll
     for (int e = 0; e < L; ++e) issue_one(r, e);
   };
@@ -801,9 +765,8 @@ __global__ __launch_bounds__(64 * WN, OCC) void gemm_lds32_kernel(
   };
   // refill (when given) receives chunk rc's loads, spread over the seven steps
   // so that the address unit works while the MFMAs run
-  auto steps0to6 = [&](const Stage& sg, Stage& refill) {
-    const Refill rf = refill_of(refill);
-    advance_refill();
+  auto steps0to6 = [&](const Stage& sg, Stage& refill, int64_t rc) {
+    const Refill rf = refill_of(refill, rc);
 #pragma unroll
     for (int s = 0; s < 7; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
@@ -823,30 +786,27 @@ __global__ __launch_bounds__(64 * WN, OCC) void gemm_lds32_kernel(
     }
   };
 
-  // prologue: stream chunks 0 .. ST-2 in flight, chunk 0's head in registers
+  // prologue: chunks 0 .. ST-2 in flight, chunk 0's head in registers
 #pragma unroll
-  for (int p = 0; p < ST - 1; ++p) issue(stage[p]);
+  for (int p = 0; p < ST - 1; ++p) issue(stage[p], c_begin + p);
   wait_vmcnt<L * (ST - 2)>();
   stage_barrier();
   read_head(stage[0]);
   dequant(0, 0);
   __builtin_amdgcn_sched_barrier(0);
 
-  // Ring protocol over the chunk stream: chunk g lives in stage g % ST. While
-  // chunk g is computed, stage (g-1) % ST (chunk g-1's, freed by the previous
-  // mid-chunk barrier; for g = 0 the one stage the prologue left empty)
-  // receives chunk g+ST-1. At the mid-chunk barrier of chunk g, chunk g+1 has
-  // landed and everyone has finished reading chunk g's activation fragments.
-  // After an item's last chunk its tile is written out and the accumulators
-  // start over for the next item, whose first chunks are already in flight.
-  const int total = T * nch;
-  for (int g0 = 0; g0 < total; g0 += ST) {
+  // Ring protocol: chunk i lives in stage i % ST. While chunk i is computed,
+  // stage (i-1) % ST (chunk i-1's, freed by the previous mid-chunk barrier;
+  // for i = 0 the one stage the prologue left empty) receives chunk i+ST-1.
+  // At the mid-chunk barrier of chunk i, chunk i+1 has landed and everyone
+  // has finished reading chunk i's activation fragments.
+  for (int i0 = 0; i0 < nch; i0 += ST) {
 #pragma unroll
     for (int j = 0; j < ST; ++j) {
-      if (g0 + j < total) {
-        steps0to6(stage[j], stage[(j + ST - 1) % ST]);
-        const bool more = g0 + j + 1 < total;
-        wait_vmcnt<L * (ST - 2)>();  // this wave's loads of chunk g+1 have landed
+      if (i0 + j < nch) {
+        steps0to6(stage[j], stage[(j + ST - 1) % ST], c_begin + i0 + j + ST - 1);
+        const bool more = i0 + j + 1 < nch;
+        wait_vmcnt<L * (ST - 2)>();  // this wave's loads of chunk i+1 have landed
         if (more) read_head_b(stage[(j + 1) % ST]);  // its own loads
         stage_barrier();             // everyone's have, and stage j has been read by all
         if (more) read_head_a(stage[(j + 1) % ST]);
@@ -859,30 +819,14 @@ __global__ __launch_bounds__(64 * WN, OCC) void gemm_lds32_kernel(
           if (i >= MFMAS / 4) __builtin_amdgcn_sched_group_barrier(0x002, VPM + 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (cc == nch - 1 && nsplit == 1) {
-          // a whole tile is done: write it out (the plain path, splits = 1)
-          // and start the next item's sums
-          finish_tile32<MT, NT, WN>(acc, M, N, cur.m0, cur.n0, wn, 0, 1, alpha, bias, y, ldy, nullptr,
-                                    nullptr, &s_flag);
-#pragma unroll
-          for (int a2 = 0; a2 < MT; ++a2)
-#pragma unroll
-            for (int b2 = 0; b2 < NT; ++b2) acc[a2][b2] = float16v{};
-          cc = 0;
-          if (++cj < T) cur = nxt;
-        } else {
-          ++cc;
-        }
       }
     }
   }
   wait_vmcnt<0>();  // no LDS load may still be in flight when the workgroup ends
-  if (nsplit > 1) {
-    // a split tile (its workgroup's only item): the split-K reduction
-    float4v* slab = partial + (int64_t)sslot * splits * (WN * MT * NT * 4 * 64);
-    finish_tile32<MT, NT, WN>(acc, M, N, cur.m0, cur.n0, wn, split, nsplit, alpha, bias, y, ldy, slab,
-                              counters + sslot, &s_flag);
-  }
+
+  float4v* slab = partial + (int64_t)sslot * splits * (WN * MT * NT * 4 * 64);
+  finish_tile32<MT, NT, WN>(acc, M, N, mgroup * MT * 32, ngroup * WN * NT * 32, wn, split, nsplit,
+                            alpha, bias, y, ldy, slab, counters + sslot, &s_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -898,7 +842,6 @@ static constexpr int kCUs = 256;
 struct GemmOverride {
   int kind = -1, waves = 0, ntw = 0, rc = 0, mt = 0, nt = 0, wm = 0, st = 0, splits = 0, xg = -1, cw = 0;
   int tail = 0;  // kind 3: 1 = never split the last round's tiles, 2..4 = split them that many ways
-  int pers = -1;  // kind 3: 0 = one workgroup per whole tile, 1 = persistent workgroups
 };
 static GemmOverride gemm_override() {
   GemmOverride o;
@@ -925,7 +868,6 @@ static GemmOverride gemm_override() {
       else if (k == "xg" && v >= 0 && v <= 64) o.xg = v;
       else if (k == "cw" && (v == 4 || v == 8)) o.cw = v;
       else if (k == "tail" && v >= 1 && v <= 4) o.tail = v;
-      else if (k == "pers" && (v == 0 || v == 1)) o.pers = v;
     }
     pos = end + 1;
   }
@@ -1107,14 +1049,6 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool rot
         p.splits = (int)((KC + p.kc_per_split - 1) / p.kc_per_split);
       }
     }
-    // Persistent workgroups: with more whole tiles than CUs, one workgroup per
-    // CU walks its tiles in the same XCD-grouped order and its ring runs on
-    // from one tile into the next, so a tile's first chunks load while the
-    // previous tile computes and is written out, and no workgroup is
-    // relaunched per tile. (A round of 128 x 256 tiles at M = 8192, N = 28672
-    // costs about 8 us on top of 1.55 us per 128-deep chunk.)
-    p.pw = p.dp_groups;
-    if (p.kind == 3 && p.dp_groups > kCUs && KC >= 8 && ov.pers != 0) p.pw = kCUs;
     p.xhat_bytes = round_up(p.Mp * p.Kp * 2, 256);
   }
   // [splits][waves][fragments][64 lanes] float4 per output tile
@@ -1135,12 +1069,11 @@ std::string describe_plan(const GemmPlan& p) {
     // whole tiles first; a split tail reads "tail=<tiles>x<splits>"
     const bool tail = p.dp_groups > 0 && p.splits > 1;
     std::string extra = p.xg > 0 ? " xcd_bands=" + std::to_string(p.xg) : "";
-    if (p.pw < p.dp_groups) extra += " persistent=" + std::to_string(p.pw);
     if (tail) extra += " tail=" + std::to_string(p.groups - p.dp_groups) + "x" + std::to_string(p.splits);
     const std::string wn = p.cw != 4 ? ",WN=" + std::to_string(p.cw) : "";
     std::snprintf(b, sizeof(b),
                   "quant_nvfp4_xhat_kernel + gemm_lds32_kernel<MT=%d,NT=%d,ST=%d%s> grid=%lld splits=%d%s",
-                  p.mt, p.nt, p.st, wn.c_str(), (long long)(p.pw + (p.groups - p.dp_groups) * p.splits),
+                  p.mt, p.nt, p.st, wn.c_str(), (long long)(p.dp_groups + (p.groups - p.dp_groups) * p.splits),
                   tail ? 1 : p.splits, extra.c_str());
   } else if (p.kind == 0) {
     std::snprintf(b, sizeof(b), "linear_gemv_kernel<W=%d,NTW=%d,RC=%d,QPRE=%d> grid=%lld lds=%lld",
@@ -1239,17 +1172,11 @@ static hipError_t launch_lds32_t(const GemmPlan& p, const _Float16* xhat, const 
                                  hipStream_t st) {
   const uint8_t* wcodes = packed;
   const uint8_t* wscales = packed + p.Np * p.Kp / 2;
-  // whole tiles go to pw workgroups (all of them, or a multiple of 8 sharing
-  // them, at least ring-depth chunks each), split tiles to `splits` each
-  const int64_t KC = p.Kp / 128;
-  if (p.pw > p.dp_groups || (p.dp_groups > 0 && p.pw <= 0) ||
-      (p.pw < p.dp_groups && (p.pw % 8 != 0 || KC < ST)))
-    return hipErrorInvalidValue;
-  const int64_t grid = p.pw + (p.groups - p.dp_groups) * p.splits;
+  const int64_t grid = p.dp_groups + (p.groups - p.dp_groups) * p.splits;
   gemm_lds32_kernel<MT, NT, ST, OCC, WN><<<(unsigned)grid, 64 * WN, 0, st>>>(
       xhat, wcodes, wscales, (int)M, (int)N, p.Kp, (int)(p.Np / 16), (int)p.ngroups,
-      p.kc_per_split, (int)p.dp_groups, (int)p.pw, p.splits, p.xg, alpha, alpha_dev, bias, y, ldy,
-      partial, counters);
+      p.kc_per_split, (int)p.dp_groups, p.splits, p.xg, alpha, alpha_dev, bias, y, ldy, partial,
+      counters);
   return hipGetLastError();
 }
 

@@ -272,14 +272,11 @@ int fql_fp8_scale(float amax, float* scale);
 int fql_fp8_output_scale(float input_scale, float weight_scale, float* alpha);
 
 /* Benchmarking aid: replace a launch-plan override. which: FQL_PLAN_NVFP4
- * ("kind=K,waves=W,nt=N,st=S,splits=Z,tail=T,pers=P,..."), FQL_PLAN_SC_GEMM
+ * ("kind=K,waves=W,nt=N,st=S,splits=Z,tail=T,..."), FQL_PLAN_SC_GEMM
  * ("wm,wn,mtw,ntw,st[,splits[,tail]]") or FQL_PLAN_SC_GEMV ("W,NT,D[,FQ]",
  * or "0" for no GEMV); spec NULL or "" removes it. tail: 1 keeps the last
- * round of tiles whole, 2..4 splits its tiles that many ways along K; pers: 0
- * gives every whole tile a workgroup of its own, 1 (the default when there
- * are more whole tiles than CUs) shares them among persistent workgroups.
- * The initial values are the environment variables FQL_PLAN, FQL_SC_PLAN and
- * FQL_SC_GEMV, read once.
+ * round of tiles whole, 2..4 splits its tiles that many ways along K. The initial values are the
+ * environment variables FQL_PLAN, FQL_SC_PLAN and FQL_SC_GEMV, read once.
  * An override changes which kernel configuration runs, so results may differ
  * in the float32 summation order over K, never otherwise; configurations
  * that are not built are ignored. Host-side only. */

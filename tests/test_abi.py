@@ -307,7 +307,7 @@ def test_plan_override_set_and_cleared():
 def test_lds32_layouts_and_tile_order_in_the_plan():
     # above 128 rows: 128 x 256 tiles on 8 column waves in XCD bands of 4 row
     # groups (clamped to the row groups there are); up to 128 rows 4 waves
-    assert ("gemm_lds32_kernel<MT=4,NT=1,ST=3,WN=8> grid=256 splits=1 xcd_bands=4 persistent=256"
+    assert ("gemm_lds32_kernel<MT=4,NT=1,ST=3,WN=8> grid=7168 splits=1 xcd_bands=4"
             in fql.linear_plan(8192, 28672, 4096))
     assert "xcd_bands=2" in fql.linear_plan(256, 51200, 5120)
     assert "gemm_lds32_kernel<MT=2,NT=1,ST=4> grid=192 splits=2" in fql.linear_plan(128, 6144, 4096)
@@ -324,7 +324,7 @@ def test_lds32_layouts_and_tile_order_in_the_plan():
 def test_last_round_tiles_split_along_k():
     # 640 tiles of 128 x 256 leave the third round of 256 half full: its 128
     # tiles take two workgroups each; full rounds and short K stay whole
-    assert "grid=512 splits=1 xcd_bands=4 persistent=256 tail=128x2" in fql.linear_plan(4096, 5120, 25600)
+    assert "grid=768 splits=1 xcd_bands=4 tail=128x2" in fql.linear_plan(4096, 5120, 25600)
     assert "tail" not in fql.linear_plan(2048, 6144, 4096)    # 32 chunks of K: kept whole
     assert "tail" not in fql.linear_plan(8192, 28672, 4096)   # 7168 tiles: 28 full rounds
     assert "tail" not in fql.linear_plan(256, 51200, 5120)    # 400 tiles: last round 56% full
@@ -334,33 +334,13 @@ def test_last_round_tiles_split_along_k():
     with fql.plan_override("tail=4"):
         assert "grid=272 splits=1 xcd_bands=4 tail=4x4" in fql.linear_plan(1650, 5120, 2048)
     with fql.plan_override("tail=1"):
-        assert "grid=256 splits=1 xcd_bands=4 persistent=256" in fql.linear_plan(4096, 5120, 25600)
-    with fql.plan_override("tail=1,pers=0"):
         assert "grid=640 splits=1 xcd_bands=4" in fql.linear_plan(4096, 5120, 25600)
-    with fql.plan_override("tail=3,pers=0"):
-        assert "grid=896 splits=1 xcd_bands=4 tail=128x3" in fql.linear_plan(4096, 5120, 25600)
     with fql.plan_override("tail=3"):
-        assert "grid=640 splits=1 xcd_bands=4 persistent=256 tail=128x3" in fql.linear_plan(4096, 5120, 25600)
+        assert "grid=896 splits=1 xcd_bands=4 tail=128x3" in fql.linear_plan(4096, 5120, 25600)
     # the split tiles' partial sums are part of the workspace
     with fql.plan_override("tail=1"):
         whole = fql.linear_workspace_bytes(4096, 5120, 25600)
     assert fql.linear_workspace_bytes(4096, 5120, 25600) == whole + 128 * 2 * 8 * 16 * 64 * 16
-
-
-def test_persistent_workgroups_for_more_tiles_than_cus():
-    # one workgroup per CU walks its tiles when there are more whole tiles
-    # than CUs and K has at least 8 chunks; otherwise one tile per workgroup
-    assert "grid=256 splits=1 xcd_bands=4 persistent=256" in fql.linear_plan(4096, 51200, 5120)
-    assert "persistent=256" in fql.linear_plan(2048, 6144, 4096)          # 384 tiles
-    assert "persistent" not in fql.linear_plan(2048, 4096, 14336)         # 256 tiles: one round
-    assert "persistent" not in fql.linear_plan(2048, 6144, 512)           # 4 chunks of K
-    assert "persistent" not in fql.linear_plan(256, 5120, 25600)          # split K
-    with fql.plan_override("pers=0"):
-        assert "grid=6400 splits=1 xcd_bands=4" in fql.linear_plan(4096, 51200, 5120)
-    # the workspace does not depend on it
-    with fql.plan_override("pers=0"):
-        ws0 = fql.linear_workspace_bytes(4096, 51200, 5120)
-    assert fql.linear_workspace_bytes(4096, 51200, 5120) == ws0
 
 
 def test_sibling_last_round_tiles_split_along_k():

@@ -123,27 +123,6 @@ def test_linear_last_round_split_every_row(M, K, N, spec):
         _run_case("prefill", M, K, N, 0, True, label=f"tail-split {spec}")
 
 
-@pytest.mark.parametrize("M,K,N,spec", [(2048, 4096, 6144, ""), (2500, 1040, 4000, ""),
-                                        (2500, 1040, 4000, "xg=0"), (4096, 2048, 5120, "tail=2")])
-def test_linear_persistent_bitwise_equals_one_tile_per_workgroup(M, K, N, spec):
-    # persistent workgroups compute every tile exactly as a workgroup of its
-    # own would (same K order), so the outputs agree bit for bit: 384 tiles
-    # (workgroups with two tiles and with one), 320 tiles with ragged M and K
-    # in the banded and the row-major order, and whole tiles with a split tail
-    xb = synthetic.activations("normal", M, K, config="prefill", seed=5)
-    W, gw, _, _ = weight_case("prefill", N, K, 0)
-    announce(f"persistent vs one tile per workgroup M={M} K={K} N={N} {spec}")
-    wobj, _, _ = _gpu_weight(W, gw, 0, 1.0)
-    xd = bf16_bits_to_dev(xb)
-    with fql.plan_override(spec):
-        assert "persistent=256" in fql.linear_plan(M, N, K)
-        y1 = fql.linear_nvfp4(xd, wobj).clone()
-    with fql.plan_override(",".join(s for s in (spec, "pers=0") if s)):
-        assert "persistent" not in fql.linear_plan(M, N, K)
-        y0 = fql.linear_nvfp4(xd, wobj).clone()
-    assert torch.equal(y1.view(torch.int16), y0.view(torch.int16))
-
-
 def test_linear_strided_3d_input_and_output_stride():
     M, K, N = 24, 1024, 320
     xb = synthetic.activations("normal", M, K, config="decode", seed=4)
