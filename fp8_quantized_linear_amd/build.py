@@ -9,6 +9,9 @@ Every HIP source is compiled for gfx950 only, with:
     codes and scales must equal an IEEE reference bit for bit);
   * packed-FP32 instructions disabled (-packed-fp32-ops);
   * no fast-math.
+The sources that issue direct global->LDS loads are also compiled to
+assembly, and the library is not linked if any of those loads reads an SGPR
+sooner after its VALU write than the hardware allows (lds_dma_check).
 """
 
 import os
@@ -16,6 +19,11 @@ import shutil
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
+
+try:
+    from . import lds_dma_check
+except ImportError:  # run as a script
+    import lds_dma_check
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -71,13 +79,29 @@ def _link(objs, lib, verbose):
     os.replace(tmp, lib)
 
 
+def lds_dma_violations(src):
+    """Wait-state violations before the LDS-DMA loads of one source's kernels."""
+    asm = lds_dma_check.device_asm(_hipcc(), HIPCC_FLAGS, CSRC, src,
+                                   os.path.join(BUILD, src.replace(".hip", ".s")))
+    bad, loads = lds_dma_check.hazards(asm)
+    if loads == 0:
+        bad.append(f"{src}: no LDS-DMA load found in the assembly")
+    return [f"{src}: {b}" for b in bad]
+
+
 def build(verbose=False):
     """Compile all sources and link libfql.so and libfql_calib.so. Always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = SOURCES + CALIB_SOURCES
     objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in srcs]
+    checked = lds_dma_check.sources_with_lds_dma(CSRC, SOURCES)
     with ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
+        checks = [ex.submit(lds_dma_violations, s) for s in checked]
         list(ex.map(lambda so: _compile(so[0], so[1], verbose), zip(srcs, objs)))
+        bad = [b for c in checks for b in c.result()]
+    if bad:
+        raise RuntimeError("LDS-DMA loads without their wait states (library not linked):\n" +
+                           "\n".join(bad[:20]))
     _link(objs[:len(SOURCES)], LIB, verbose)
     _link(objs[len(SOURCES):], CALIB_LIB, verbose)
     return LIB

@@ -190,20 +190,22 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // as the asm statement's "{m0}" operand: the compiler writes M0 itself and
 // knows the statement reads it, so no M0 value of its own can be disturbed.
 // The compiler inserts no hazard wait states around inline assembly, and two
-// GFX9 rules apply to these loads: a vector memory instruction may read an
-// SGPR only five wait states after a VALU instruction (v_readfirstlane, a
-// 64-bit compare) wrote it, and an LDS-DMA load may read M0 only one wait
-// state after a SALU write. Each statement therefore opens with s_nop 4, five
-// wait states after whatever the compiler placed before it (a few issue
-// cycles per load; the other waves of the SIMD issue meanwhile).
+// GFX9 rules apply to these loads: an LDS-DMA load may read M0 only one wait
+// state after a SALU write, and a vector memory instruction may read an SGPR
+// (the base, M0) only five wait states after a VALU instruction (a
+// v_readfirstlane, a 64-bit compare) wrote it. The statement's s_nop 0 keeps
+// the first rule in any schedule; the second depends on the compiler's
+// placement of those VALU instructions, and the build checks it on the
+// generated assembly of every kernel that uses these loads (five wait states
+// on every load cost 2% on the large GEMMs).
 __device__ __forceinline__ void lds_load16(const void* sbase, uint32_t voff, uint32_t lds) {
   lds = __builtin_amdgcn_readfirstlane(lds);  // uniform by contract; keeps it in an SGPR
-  __asm__ volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds)
+  __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds)
                    : "memory");
 }
 __device__ __forceinline__ void lds_load4(const void* sbase, uint32_t voff, uint32_t lds) {
   lds = __builtin_amdgcn_readfirstlane(lds);
-  __asm__ volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds)
+  __asm__ volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(lds)
                    : "memory");
 }
 // Output tile of workgroup `bid` (of `n`, one K split) in an XCD-grouped order.

@@ -1,109 +1,69 @@
-"""Wait states around the direct global->LDS loads, checked on the generated
+"""Wait states before the direct global->LDS loads, checked on the generated
 gfx950 assembly (CPU only: hipcc cross-compiles the kernel sources to text).
 
-The loads are written as inline assembly, and the compiler inserts no hazard
-wait states around inline assembly. Two GFX9 rules apply to them: a vector
-memory instruction may read an SGPR (its scalar base address, M0) only five
-wait states after a VALU instruction wrote it, and an LDS-DMA load may read
-M0 only one wait state after a SALU write. A load that reads a base address
-still being written takes a stale one and can fault. Every LDS-DMA load of
-every kernel must keep both rules, whatever schedule the compiler picked.
+The loads are inline assembly, around which the compiler inserts no hazard
+wait states. Two GFX9 rules apply: a vector memory instruction may read an
+SGPR (its scalar base address, M0) only five wait states after a VALU
+instruction wrote it, and an LDS-DMA load may read M0 only one wait state
+after a SALU write. A load that reads a base address still being written
+takes a stale one and can fault. build() runs the same check and refuses to
+link a library that breaks either rule; here the checker itself is tested on
+small listings, then run on every kernel source that issues such loads.
 """
 
 import os
-import re
-import subprocess
 from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
 from fp8_quantized_linear_amd import build as B
-
-VMEM_SGPR_WAIT = 5  # VALU writes an SGPR -> vector memory instruction reads it
-M0_LDS_DMA_WAIT = 1  # SALU writes M0 -> LDS-DMA load reads it
+from fp8_quantized_linear_amd.lds_dma_check import device_asm, hazards, sources_with_lds_dma
 
 
-def _sources_with_lds_dma():
-    out = []
-    for s in B.SOURCES:
-        text = open(os.path.join(B.CSRC, s)).read()
-        if "lds_load16(" in text or "lds_load4(" in text:
-            out.append(s)
-    return out
+def _listing(*lines):
+    return "_Zk:\n" + "".join(f"{l}\n" if l.endswith(":") else f"\t{l}\n" for l in lines) + ".Lfunc_end0:"
 
 
-def _sgprs(tok):
-    m = re.fullmatch(r"s\[(\d+):(\d+)\]", tok)
-    if m:
-        return {f"s{i}" for i in range(int(m.group(1)), int(m.group(2)) + 1)}
-    if re.fullmatch(r"s\d+|m0", tok):
-        return {tok}
-    return set()
-
-
-def _wait_states(ins):
-    parts = ins.split()
-    return int(parts[1], 0) + 1 if parts[0] == "s_nop" else 1
-
-
-def _functions(asm):
-    """(name, [instruction text or None for a label]) per kernel."""
-    for m in re.finditer(r"^(_Z\S+):", asm, re.M):
-        end = asm.find(".Lfunc_end", m.start())
-        body = []
-        for line in asm[m.start():end].splitlines()[1:]:
-            line = line.split(";")[0].strip()
-            if not line or line.startswith("."):
-                continue
-            body.append(None if line.endswith(":") else line)
-        yield m.group(1), body
-
-
-def hazards(asm):
-    """Violations of the two rules in one assembly listing, and the number of
-    LDS-DMA loads seen. The look-back is linear and steps over labels, so a
-    write in a block that falls or branches into the load's block is seen as
-    long as it is the linear predecessor; the loads checked here are preceded
-    by an s_nop inside their own asm statement, which no label can split."""
-    bad, loads = [], 0
-    for name, body in _functions(asm):
-        for i, ins in enumerate(body):
-            if ins is None:
-                continue
-            op, *args = ins.replace(",", " ").split()
-            if op.startswith("v_") and args and args[0] == "m0":
-                bad.append(f"{name}: VALU writes M0: {ins}")
-            if not op.startswith("global_load_lds"):
-                continue
-            loads += 1
-            reads = _sgprs(args[1]) | {"m0"}
-            waited, j = 0, i - 1
-            while j >= 0 and waited < VMEM_SGPR_WAIT:
-                prev = body[j]
-                j -= 1
-                if prev is None:
-                    continue
-                pop, *pargs = prev.replace(",", " ").split()
-                written = _sgprs(pargs[0]) if pargs else set()
-                if pop.startswith("v_") and written & reads:
-                    bad.append(f"{name}: {prev} {waited} wait states before {ins}")
-                if pop.startswith("s_") and "m0" in written and waited < M0_LDS_DMA_WAIT:
-                    bad.append(f"{name}: {prev} {waited} wait states before {ins}")
-                waited += _wait_states(prev)
-    return bad, loads
-
-
-def test_rules_flag_a_load_right_after_its_base_is_written():
-    # the checker itself: a v_readfirstlane into the load's base, and an M0
-    # write with no wait state, are both flagged; five wait states clear them
-    k = "_Zk:\n"
-    bad, n = hazards(k + "\tv_readfirstlane_b32 s53, v3\n\tglobal_load_lds_dword v70, s[52:53]\n.Lfunc_end0:")
+def test_a_load_right_after_its_base_or_m0_is_written_is_flagged():
+    bad, n = hazards(_listing("v_readfirstlane_b32 s53, v3", "global_load_lds_dword v70, s[52:53]"))
     assert n == 1 and len(bad) == 1
-    bad, _ = hazards(k + "\ts_mov_b32 m0, s2\n\tglobal_load_lds_dwordx4 v68, s[42:43]\n.Lfunc_end0:")
+    bad, _ = hazards(_listing("s_mov_b32 m0, s2", "global_load_lds_dwordx4 v68, s[42:43]"))
     assert len(bad) == 1
-    bad, _ = hazards(k + "\tv_readfirstlane_b32 s53, v3\n\ts_mov_b32 m0, s2\n\ts_nop 4\n"
-                     "\tglobal_load_lds_dword v70, s[52:53]\n.Lfunc_end0:")
-    assert bad == []
+    bad, _ = hazards(_listing("v_readfirstlane_b32 m0, v1", "s_nop 3", "global_load_lds_dword v1, s[2:3]"))
+    assert len(bad) == 2  # a VALU write of M0, four wait states before the load
+
+
+def test_enough_wait_states_clear_both_rules():
+    assert hazards(_listing("v_readfirstlane_b32 s53, v3", "s_mov_b32 m0, s2", "s_nop 3",
+                            "global_load_lds_dword v70, s[52:53]"))[0] == []
+    assert hazards(_listing("s_mov_b32 m0, s2", "s_nop 0", "global_load_lds_dword v70, s[52:53]"))[0] == []
+    # a VALU that only reads the SGPR is no hazard
+    assert hazards(_listing("v_add_u32_e32 v1, s52, v2", "s_nop 0", "global_load_lds_dword v70, s[52:53]"))[0] == []
+
+
+def test_carry_outputs_count_as_sgpr_writes():
+    bad, _ = hazards(_listing("v_add_co_u32_e64 v1, s[52:53], v2, v3", "s_nop 1",
+                              "global_load_lds_dword v70, s[52:53]"))
+    assert len(bad) == 1
+    bad, _ = hazards(_listing("v_cmp_lt_i64_e32 vcc, v[2:3], v[4:5]", "s_nop 0",
+                              "global_load_lds_dword v70, vcc"))
+    assert len(bad) == 1
+
+
+def test_the_look_back_follows_branches_into_the_load_block():
+    # the linear predecessor has waited long enough, the branch source has not
+    listing = _listing("v_readfirstlane_b32 s53, v3", "s_cbranch_scc1 .LBB0_2", "s_nop 7", "s_nop 7",
+                       ".LBB0_2:", "s_nop 0", "global_load_lds_dword v70, s[52:53]")
+    bad, _ = hazards(listing)
+    assert len(bad) == 1 and "v_readfirstlane_b32 s53" in bad[0]
+    # after an unconditional branch the label is not reached by falling through
+    listing = _listing("v_readfirstlane_b32 s53, v3", "s_branch .LBB0_3", ".LBB0_2:", "s_nop 0",
+                       "global_load_lds_dword v70, s[52:53]", ".LBB0_3:", "s_endpgm")
+    assert hazards(listing)[0] == []
+    # a loop back-edge: the write at the loop's end reaches the load at its head
+    listing = _listing("s_nop 7", ".LBB0_1:", "s_nop 0", "global_load_lds_dword v70, s[52:53]", "s_nop 7",
+                       "v_readfirstlane_b32 s52, v3", "s_cbranch_scc1 .LBB0_1")
+    assert len(hazards(listing)[0]) == 1
 
 
 def _have_hipcc():
@@ -116,16 +76,11 @@ def _have_hipcc():
 
 @pytest.mark.skipif(not _have_hipcc(), reason="hipcc not installed")
 def test_every_lds_dma_load_keeps_its_wait_states(tmp_path):
-    sources = _sources_with_lds_dma()
+    sources = sources_with_lds_dma(B.CSRC, B.SOURCES)
     assert sources, "no kernel source uses the direct global->LDS loads"
 
     def compile_asm(src):
-        out = tmp_path / (src + ".s")
-        cmd = [B._hipcc(), *B.HIPCC_FLAGS, "-I", B.CSRC, "--cuda-device-only", "-S",
-               os.path.join(B.CSRC, src), "-o", str(out)]
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        assert r.returncode == 0, r.stderr[-2000:]
-        return src, out.read_text()
+        return src, device_asm(B._hipcc(), B.HIPCC_FLAGS, B.CSRC, src, str(tmp_path / (src + ".s")))
 
     with ThreadPoolExecutor(len(sources)) as ex:
         listings = list(ex.map(compile_asm, sources))
