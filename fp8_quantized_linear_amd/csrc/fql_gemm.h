@@ -177,44 +177,34 @@ __device__ __forceinline__ void finish_tile32(float16v (&acc)[MT][NT], int M, in
       frag, row_of, col_of, M, N, m0, n0, split, splits, alpha, bias, y, ldy, slab, counter, s_flag);
 }
 
-// Whole-tile write-out (one K split) of 32x32 accumulator tiles through LDS.
-// In the accumulator layout a lane holds one column and 4-row runs of it, so
-// direct stores are 2-byte scatters, 64 per lane for a 128-row wave. Here each
-// wave writes its bf16 results into a row-major copy of the workgroup tile in
-// LDS (`lds`, at least R x P halves, free of other use), and after a barrier
-// every thread stores 16-byte row pieces: whole rows of consecutive addresses,
-// an eighth of the store instructions. The value of each element is the
-// direct path's (alpha * sum + bias, rounded to bf16 once). Rows at or past M
-// and columns at or past N are not stored; y needs 16-byte alignment and ldy a
-// multiple of 8 for the 16-byte stores, else the pieces go out element by
-// element. The caller has made sure that no LDS access or LDS-bound load of
-// the workgroup is still in flight on `lds` (a wait and a barrier).
-template <int MT, int NT, int NW>
-__device__ __forceinline__ void write_tile32_staged(const float16v (&acc)[MT][NT], int M, int N, int m0,
-                                                    int n0, int wn, float alpha,
-                                                    const uint16_t* __restrict__ bias,
-                                                    uint16_t* __restrict__ y, int64_t ldy,
-                                                    uint16_t* lds) {
-  constexpr int R = MT * 32, C = NW * NT * 32;
-  constexpr int P = C + 8;  // row pitch in halves: 16 bytes of padding keep the two half-waves' rows apart in the banks
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int b = 0; b < NT; ++b) {
-    const int c = (wn * NT + b) * 32 + (lane & 31);
-    const int n = n0 + c;
-    const float bv = bias != nullptr && n < N ? bf16_bits_to_f32(bias[n]) : 0.0f;
-#pragma unroll
-    for (int a = 0; a < MT; ++a)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = a * 32 + 8 * (r / 4) + 4 * (lane >> 5) + r % 4;
-        lds[row * P + c] = (uint16_t)f32_to_bf16_bits(alpha * acc[a][b][r] + bv);
-      }
-  }
-  __syncthreads();
+// Whole-tile write-out (one K split) through LDS. In the MFMA accumulator
+// layouts a lane holds one column and 4-row runs of it, so direct stores are
+// 2-byte scatters (64 per lane for a 128-row wave of 32x32 tiles). Instead
+// each wave writes its bf16 results into a row-major copy of the workgroup's
+// R x C tile in LDS (`lds`, at least R x (C + 8) halves, free of other use),
+// and after a barrier every thread stores 16-byte row pieces: whole rows of
+// consecutive addresses, an eighth of the store instructions. The value of
+// each element is the direct path's (alpha * sum + bias, rounded to bf16
+// once). Rows at or past M and columns at or past N are not stored; y needs
+// 16-byte alignment and ldy a multiple of 8 for the 16-byte stores, else the
+// pieces go out element by element. The caller has made sure that no LDS
+// access or LDS-bound load of the workgroup is still in flight on `lds` (a
+// wait and a barrier).
+template <int C>
+struct StagedPitch {
+  // row pitch in halves: 16 bytes of padding keep the rows written by one
+  // instruction's lane groups apart in the banks, and rows 16-byte aligned
+  static constexpr int P = C + 8;
+};
+
+// the store half: 16-byte row pieces of the staged R x C tile, NW waves
+template <int R, int C, int NW>
+__device__ __forceinline__ void store_staged_tile(const uint16_t* lds, int M, int N, int m0, int n0,
+                                                  uint16_t* __restrict__ y, int64_t ldy) {
+  constexpr int P = StagedPitch<C>::P;
   const bool vec = (ldy & 7) == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0;
-  constexpr int PIECES = R * C / 8;  // 16-byte pieces of the tile
-  static_assert(PIECES % (64 * NW) == 0, "whole pieces per thread");
+  constexpr int PIECES = R * C / 8;
+  static_assert(C % 8 == 0 && PIECES % (64 * NW) == 0, "whole pieces per thread");
 #pragma unroll
   for (int q0 = 0; q0 < PIECES; q0 += 64 * NW) {
     const int q = q0 + threadIdx.x;
@@ -231,6 +221,60 @@ __device__ __forceinline__ void write_tile32_staged(const float16v (&acc)[MT][NT
         if (n + i < N) dst[i] = (uint16_t)(v[i / 2] >> (16 * (i % 2)));
     }
   }
+}
+
+// 32x32 accumulator tiles (the layout of finish_tile32): one row of NW
+// column waves, each MT x NT tiles; R = 32 MT, C = 32 NW NT.
+template <int MT, int NT, int NW>
+__device__ __forceinline__ void write_tile32_staged(const float16v (&acc)[MT][NT], int M, int N, int m0,
+                                                    int n0, int wn, float alpha,
+                                                    const uint16_t* __restrict__ bias,
+                                                    uint16_t* __restrict__ y, int64_t ldy,
+                                                    uint16_t* lds) {
+  constexpr int R = MT * 32, C = NW * NT * 32, P = StagedPitch<C>::P;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int b = 0; b < NT; ++b) {
+    const int c = (wn * NT + b) * 32 + (lane & 31);
+    const int n = n0 + c;
+    const float bv = bias != nullptr && n < N ? bf16_bits_to_f32(bias[n]) : 0.0f;
+#pragma unroll
+    for (int a = 0; a < MT; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = a * 32 + 8 * (r / 4) + 4 * (lane >> 5) + r % 4;
+        lds[row * P + c] = (uint16_t)f32_to_bf16_bits(alpha * acc[a][b][r] + bv);
+      }
+  }
+  __syncthreads();
+  store_staged_tile<R, C, NW>(lds, M, N, m0, n0, y, ldy);
+}
+
+// 16x16 accumulator tiles (the layout of finish_tile): a WM x WN wave grid,
+// each wave MT x NT tiles; R = 16 WM MT, C = 16 WN NT.
+template <int MT, int NT, int WM, int WN>
+__device__ __forceinline__ void write_tile16_staged(const float4v (&acc)[MT][NT], int M, int N, int m0,
+                                                    int n0, int wm, int wn, float alpha,
+                                                    const uint16_t* __restrict__ bias,
+                                                    uint16_t* __restrict__ y, int64_t ldy,
+                                                    uint16_t* lds) {
+  constexpr int R = WM * MT * 16, C = WN * NT * 16, P = StagedPitch<C>::P;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int c = (wn * NT + nt) * 16 + (lane & 15);
+    const int n = n0 + c;
+    const float bv = bias != nullptr && n < N ? bf16_bits_to_f32(bias[n]) : 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = (wm * MT + mt) * 16 + 4 * (lane >> 4) + i;
+        lds[row * P + c] = (uint16_t)f32_to_bf16_bits(alpha * acc[mt][nt][i] + bv);
+      }
+  }
+  __syncthreads();
+  store_staged_tile<R, C, WM * WN>(lds, M, N, m0, n0, y, ldy);
 }
 
 // Direct global -> LDS loads. The loads are issued with inline assembly and

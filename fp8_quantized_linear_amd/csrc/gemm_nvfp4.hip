@@ -827,7 +827,7 @@ __global__ __launch_bounds__(64 * WN, OCC) void gemm_lds32_kernel(
   const int m0 = mgroup * MT * 32, n0 = ngroup * WN * NT * 32;
   if (nsplit == 1) {
     // a whole tile: through the ring's LDS, once every wave's loads have landed
-    static_assert(sizeof(stage) >= (size_t)MT * 32 * (WN * NT * 32 + 8) * 2, "staged tile fits the ring");
+    static_assert(sizeof(stage) >= (size_t)MT * 32 * StagedPitch<WN * NT * 32>::P * 2, "staged tile fits the ring");
     __syncthreads();
     write_tile32_staged<MT, NT, WN>(acc, M, N, m0, n0, wn, alpha, bias, y, ldy,
                                     reinterpret_cast<uint16_t*>(&stage[0]));

@@ -436,6 +436,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
   }
   wait_vmcnt<0>();  // no LDS load may still be in flight when the workgroup ends
 
+  const int m0 = mgroup * TA * 16, n0 = ngroup * TB * 16;
+  // a whole tile goes out through the ring's LDS when the staged tile fits it
+  // (and its 16-byte pieces divide evenly among the threads)
+  constexpr bool kStaged = sizeof(stage) >= (size_t)TA * 16 * StagedPitch<TB * 16>::P * 2 &&
+                           (TA * 16 * TB * 16 / 8) % (64 * NW) == 0;
+  if constexpr (kStaged) {
+    if (nsplit == 1) {
+      __syncthreads();  // every wave's loads have landed: the ring is free
+      write_tile16_staged<MTW, NTW, WM, WN>(acc, M, N, m0, n0, wm, wn, alpha, bias, y, ldy,
+                                            reinterpret_cast<uint16_t*>(&stage[0]));
+      return;
+    }
+  }
   float4v frag[P];
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt)
@@ -445,8 +458,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_sc_kernel(
   auto col_of = [&](int f) { return (wn * NTW + f % NTW) * 16 + (lane & 15); };
   float4v* slab = partial + (int64_t)sslot * splits * (NW * P * 64);
   finish_frags<P, decltype(row_of), decltype(col_of), NW>(
-      frag, row_of, col_of, M, N, mgroup * TA * 16, ngroup * TB * 16, split, nsplit, alpha, bias, y,
-      ldy, slab, counters + sslot, &s_flag);
+      frag, row_of, col_of, M, N, m0, n0, split, nsplit, alpha, bias, y, ldy, slab, counters + sslot,
+      &s_flag);
 }
 
 // ---------------------------------------------------------------------------
