@@ -131,3 +131,17 @@ def decode_packed(buf, rows_p, Kp):
     s = b[rows_p * Kp // 2:rows_p * Kp // 2 + T * KC4 * 512].reshape(T, KC4, 16, 2, 4, 4)
     scales = s.transpose(0, 2, 1, 4, 5, 3).reshape(rows_p, KC4 * 32)[:, :Kp // 16]
     return np.ascontiguousarray(codes), np.ascontiguousarray(scales)
+
+
+def strided_output(M, N, ld, off, fill=-7.0):
+    """An M x N bf16 output view with row stride ld starting `off` elements into
+    a flat buffer filled with `fill` (odd ld or off give a view whose rows are
+    not 16-byte aligned), the flat buffer, and the mask of the elements the
+    view covers."""
+    import torch
+    flat = torch.full((off + M * ld + 8,), fill, dtype=torch.bfloat16, device=DEV)
+    y = torch.as_strided(flat, (M, N), (ld, 1), off)
+    covered = torch.zeros(flat.numel(), dtype=torch.bool)
+    idx = off + torch.arange(M).unsqueeze(1) * ld + torch.arange(N).unsqueeze(0)
+    covered[idx.reshape(-1)] = True
+    return y, flat, covered.to(DEV)

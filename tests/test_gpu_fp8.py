@@ -20,7 +20,8 @@ from oracle import fp8 as P
 from oracle import mx as X
 
 from gpu_helpers import (DEV, REL_FROB_TOL, announce, bf16_bits_to_dev, cached_activations,
-                         cached_weight, dev_bf16_to_bits, f32_to_dev, full_rows_sample, rel_frob)
+                         cached_weight, dev_bf16_to_bits, f32_to_dev, full_rows_sample, rel_frob,
+                         strided_output)
 
 pytestmark = pytest.mark.gpu
 
@@ -273,6 +274,31 @@ def test_fp8_strided_3d_and_deterministic():
         y4 = fn(bf16_bits_to_dev(xb).view(2, 12, K), wobj)
         assert tuple(y3.shape) == (2, 12, N)
         assert torch.equal(y3.view(torch.int16), y4.view(torch.int16))
+
+
+@pytest.mark.parametrize("pad,off", [(1, 5), (8, 8)])
+def test_sibling_tile_writeout_any_output_stride(pad, off):
+    # whole tiles of the scaled-MFMA GEMM leave as 16-byte row pieces when y
+    # is 16-byte aligned with ldy a multiple of 8, element by element
+    # otherwise; either way the values equal a contiguous output's bit for bit
+    # and nothing outside the view is written
+    M, K, N = 2100, 1024, 6144
+    xb = synthetic.activations("normal", M, K, config="prefill", seed=9)
+    x32 = synthetic.bf16_bits_to_f32(xb)
+    W = cached_weight("prefill", N, K)
+    xd = bf16_bits_to_dev(xb)
+    for fmt in ("mxfp4", "mxfp8", "fp8", "fp8_block"):
+        announce(f"{fmt} tile write-out M={M} N={N} K={K} ldy=N+{pad} offset={off}")
+        assert "splits=1" in fql.linear_sc_plan(fmt, M, N, K)
+        wobj = _weight(fmt, W, float(P.scale_from_amax(np.abs(x32).max())))
+        fn = {"mxfp4": fql.linear_mxfp4, "mxfp8": fql.linear_mxfp8, "fp8": fql.linear_fp8,
+              "fp8_block": fql.linear_fp8_block}[fmt]
+        y0 = fn(xd, wobj).clone()
+        y, flat, covered = strided_output(M, N, N + pad, off)
+        fn(xd, wobj, out=y)
+        torch.cuda.synchronize()
+        assert torch.equal(y.contiguous().view(torch.int16), y0.view(torch.int16)), fmt
+        assert torch.all(flat[~covered] == -7.0), fmt
 
 
 # Every scaled-MFMA GEMM configuration built into the library (wave grid

@@ -21,7 +21,7 @@ from oracle.hadamard import fwht_fp32
 
 from gpu_helpers import (DEV, REL_FROB_TOL, alpha_of, announce, bf16_bits_to_dev,
                          cached_activations, dev_bf16_to_bits, f32_to_dev, full_rows_sample,
-                         rel_frob, weight_case, weight_hat)
+                         rel_frob, strided_output, weight_case, weight_hat)
 
 pytestmark = pytest.mark.gpu
 
@@ -145,6 +145,31 @@ def test_linear_strided_3d_input_and_output_stride():
     y3 = fql.linear_nvfp4(x3, wobj, alpha=float(alpha))
     assert tuple(y3.shape) == (2, 12, N) and y3.dtype == torch.bfloat16
     assert rel_frob(dev_bf16_to_bits(y3).reshape(M, N), ref) <= REL_FROB_TOL
+
+
+@pytest.mark.parametrize("M,N,K,pad,off,spec", [(300, 517, 1024, 3, 1, "splits=1"),
+                                                (300, 512, 1024, 8, 0, "splits=1"),
+                                                (2100, 6144, 1024, 1, 5, None),
+                                                (2100, 6144, 1024, 8, 8, None)])
+def test_linear_tile_writeout_any_output_stride(M, N, K, pad, off, spec):
+    # whole tiles of the LDS-ring GEMM leave as 16-byte row pieces when y is
+    # 16-byte aligned with ldy a multiple of 8, element by element otherwise
+    # (odd ldy or start, ragged last piece); either way the values equal a
+    # contiguous output's bit for bit and nothing outside the view is written
+    xb = synthetic.activations("normal", M, K, config="prefill", seed=9)
+    W, gw, _, _ = weight_case("prefill", N, K, 0)
+    announce(f"tile write-out M={M} N={N} K={K} ldy=N+{pad} offset={off}")
+    wobj, _, _ = _gpu_weight(W, gw, 0, 1.0)
+    xd = bf16_bits_to_dev(xb)
+    bd = bf16_bits_to_dev(synthetic.bias(N, config="prefill"))
+    with fql.plan_override(spec):
+        assert "gemm_lds32_kernel" in fql.linear_plan(M, N, K) and "splits=1" in fql.linear_plan(M, N, K)
+        y0 = fql.linear_nvfp4(xd, wobj, bias=bd).clone()
+        y, flat, covered = strided_output(M, N, N + pad, off)
+        fql.linear_nvfp4(xd, wobj, bias=bd, out=y)
+    torch.cuda.synchronize()
+    assert torch.equal(y.contiguous().view(torch.int16), y0.view(torch.int16))
+    assert torch.all(flat[~covered] == -7.0)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 6144, 4096), (128, 4096, 14336), (300, 256, 512)])
