@@ -904,6 +904,12 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool rot
   // narrow layers with K = 4096 (N < 16384), up to M = 16; long K (K = 14336)
   // and wide layers stream better through kinds 4 and 1 once M > 1.
   if (ov.kind < 0 && gemv_ok && M > 1 && (p.Kp >= 8192 || N >= 16384)) gemv_ok = false;
+  // With a rotation, every workgroup of the fused kernel also rotates the
+  // whole activation; on the wide layers (>= 1024 column tiles, one per
+  // workgroup) quantizing and rotating once, then the per-wave-ring GEMV, is
+  // faster (Qwen3-32B gate_up at M = 1: 37-40 against 42-50 us for b = 32..128,
+  // a tie at b = 16).
+  if (ov.kind < 0 && gemv_ok && rotated && ntiles >= 1024) gemv_ok = false;
   if (gemv_ok && ov.kind <= 0) {
     // one workgroup per NTW 16-column tiles over the full K (no cross-workgroup reduction)
     p.kind = 0;
@@ -917,7 +923,7 @@ GemmPlan plan_gemm_nvfp4(int64_t M, int64_t N, int64_t K, bool aligned, bool rot
     // from M = 2 on, and at M = 1 with a rotation on the narrow layers
     // (Qwen3-32B down, 320 tiles: ~10%); at M = 1 without one they lose
     // (Llama-3.1-8B down 11.0 -> 14.7 us), and the wide layers (>= 1024
-    // tiles) keep one.
+    // tiles, without a rotation: with one they leave the fused kernel) keep one.
     p.ntw = (M > 1 || rotated) && ntiles < 1024 ? 2 : 1;
     if (ov.waves == 4 || ov.waves == 8) p.waves = ov.waves;  // the built kind-0 widths
     if (ov.ntw == 1 || ov.ntw == 2) p.ntw = ov.ntw;

@@ -359,10 +359,14 @@ def test_sibling_last_round_tiles_split_along_k():
 
 def test_rotation_widens_the_fused_kernels_workgroups_at_m1():
     # with a Hadamard rotation every workgroup of the fused kernel also rotates
-    # the activation: two column tiles per workgroup on the narrow layers
+    # the activation: two column tiles per workgroup on the narrow layers, and
+    # the wide layers (>= 1024 column tiles) quantize and rotate once instead
     assert "NTW=1" in fql.linear_plan(1, 5120, 25600)
     assert "linear_gemv_kernel<W=8,NTW=2," in fql.linear_plan(1, 5120, 25600, hadamard_block=64)
-    assert "NTW=1" in fql.linear_plan(1, 51200, 5120, hadamard_block=64)  # >= 1024 column tiles
+    assert "linear_gemv_kernel<W=4,NTW=1," in fql.linear_plan(1, 51200, 5120)
+    for hb in (16, 32, 64, 128):
+        assert ("quant_nvfp4_apack_kernel + gemv_ring_kernel<W=4,MT=1,NT=4,D=3>"
+                in fql.linear_plan(1, 51200, 5120, hadamard_block=hb))
     assert "NTW=1" in fql.linear_plan(1, 4096, 14336)
     # plans with a quantizer pass, and the transform's plan, do not depend on it
     for M, N, K in [(32, 5120, 25600), (256, 5120, 25600), (4096, 51200, 5120)]:
